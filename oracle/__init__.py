@@ -1,0 +1,320 @@
+"""TEST INFRASTRUCTURE -- the fp64 CPU oracle of the TTT layer forward pass.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  It shares no code with the HIP library
+(``test_sequence_layer_amd``) and neither imports the other; the only module
+both sides use is ``ttt_inputs`` (seeded random inputs, no method arithmetic).
+
+Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，一夜推翻Transformer"
+(aharts.cn / itmax.cn).  Sections cited: 03 §1 (hidden state = weights W_t,
+output with the updated W_t, update = one GD step), 03 §5 (multi-view
+reconstruction loss |f(theta_K x; W) - theta_V x|^2, output f(theta_Q x; W)),
+03 §6 (mini-batch GD: gradients at the state before the mini-batch), 03 §7
+(dual form), 03 §8 (linear f + batch GD equals linear attention), 03 §9
+(TTT-Linear f = W x, TTT-MLP with hidden width 4x and GELU).
+
+Contents
+  linear_primal / mlp_primal   fp64 primal form in C (OpenMP over chains) --
+                               THE oracle the HIP path is compared with.
+  linear_primal_exact          the same primal loop in pure Python over any
+                               number type (fractions.Fraction for exact runs).
+  linear_dual_exact            the dual form written out from 03 §7, pure
+                               Python, any number type (self-check only).
+  linear_dual_f64, mlp_dual_f64, linear_naive_f64, mlp_primal_np
+                               numpy fp64 forms used only to check the oracle.
+  gelu, gelu_prime             exact-erf GELU and its derivative (numpy).
+
+Parity pins: every function above is checked in tests/test_oracle_*.py
+against closed forms, invariants and exact-rational arithmetic.  The absolute
+values at full workload size are not printed on the pages (every formula and
+plot there was an image) -- beyond the pins, parity is unpinned by the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from fractions import Fraction  # noqa: F401  (re-exported for tests)
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ttt_oracle.c")
+_LIB = os.path.join(_HERE, "libttt_oracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the C oracle into oracle/libttt_oracle.so (gcc, OpenMP)."""
+    cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-Wall", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i = ctypes.c_int
+    lib.oracle_linear_primal.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
+    lib.oracle_linear_primal.restype = None
+    lib.oracle_mlp_primal.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp, i]
+    lib.oracle_mlp_primal.restype = None
+    lib.oracle_max_threads.restype = i
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def linear_primal(q, k, v, w0, eta, b: int, threads: int = 0):
+    """TTT-Linear, primal form, fp64, for n independent chains.
+
+    q, k, v : [n, T, d];  w0 : [n, d, d] (z = W q);  eta : [n, T]
+    returns (z [n, T, d], w_final [n, d, d]) in fp64.
+    """
+    q, k, v, w0, eta = map(_f64, (q, k, v, w0, eta))
+    n, T, d = q.shape
+    assert k.shape == v.shape == (n, T, d) and w0.shape == (n, d, d) and eta.shape == (n, T)
+    assert b >= 1
+    z = np.empty((n, T, d))
+    wf = np.empty((n, d, d))
+    if n:
+        _load().oracle_linear_primal(n, T, d, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta),
+                                     _ptr(z), _ptr(wf), int(threads))
+    return z, wf
+
+
+def mlp_primal(q, k, v, w1, w2, eta, b: int, threads: int = 0):
+    """TTT-MLP (f = W2 GELU(W1 x)), primal form, fp64.
+
+    q, k, v : [n, T, d];  w1 : [n, dh, d];  w2 : [n, d, dh];  eta : [n, T]
+    returns (z, w1_final, w2_final).
+    """
+    q, k, v, w1, w2, eta = map(_f64, (q, k, v, w1, w2, eta))
+    n, T, d = q.shape
+    dh = w1.shape[1]
+    assert w1.shape == (n, dh, d) and w2.shape == (n, d, dh) and eta.shape == (n, T)
+    z = np.empty((n, T, d))
+    w1f = np.empty((n, dh, d))
+    w2f = np.empty((n, d, dh))
+    if n:
+        _load().oracle_mlp_primal(n, T, d, dh, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2),
+                                  _ptr(eta), _ptr(z), _ptr(w1f), _ptr(w2f), int(threads))
+    return z, w1f, w2f
+
+
+def run_inputs(inp, threads: int = 0):
+    """Run the oracle on a ``ttt_inputs.Inputs`` (its selected chains)."""
+    cfg = inp.cfg
+    eta = inp.eta_rows()
+    if cfg.is_mlp:
+        return mlp_primal(inp.q, inp.k, inp.v, inp.w_rows(1), inp.w_rows(2), eta, cfg.b, threads)
+    return linear_primal(inp.q, inp.k, inp.v, inp.w_rows(1), eta, cfg.b, threads)
+
+
+# ----------------------------------------------------------------------------
+# Pure-Python forms over any number type (exact with fractions.Fraction).
+# Vectors are lists, matrices are lists of rows; tokens are indexed 0..T-1.
+# ----------------------------------------------------------------------------
+
+def _mv(M, x):
+    return [sum((m * xi for m, xi in zip(row, x)), 0) for row in M]
+
+
+def _dot(x, y):
+    return sum((a * c for a, c in zip(x, y)), 0)
+
+
+def linear_primal_exact(q, k, v, w0, eta, b):
+    """Primal TTT-Linear for one chain (03 §1, §5, §6): lists in, lists out."""
+    d = len(w0)
+    W = [list(r) for r in w0]
+    z = []
+    T = len(q)
+    for t0 in range(0, T, b):
+        Wb = [list(r) for r in W]           # state before the mini-batch
+        for t in range(t0, min(t0 + b, T)):
+            e = [a - c for a, c in zip(_mv(Wb, k[t]), v[t])]
+            for i in range(d):
+                for j in range(d):
+                    W[i][j] -= eta[t] * 2 * e[i] * k[t][j]
+            z.append(_mv(W, q[t]))          # output with the updated W_t
+    return z, W
+
+
+def linear_dual_exact(q, k, v, w0, eta, b):
+    """Dual form of 03 §7 for one chain, pure Python, any number type.
+
+    Per mini-batch with start state W (columns = tokens of the mini-batch):
+      E = W K - V,  A[s][t] = eta_s (k_s . q_t) for s <= t (else 0),
+      Z = W Q - 2 E A,  W_next = W - 2 E diag(eta) K^T.
+    """
+    d = len(w0)
+    W = [list(r) for r in w0]
+    T = len(q)
+    z = []
+    for t0 in range(0, T, b):
+        ts = list(range(t0, min(t0 + b, T)))
+        E = {s: [a - c for a, c in zip(_mv(W, k[s]), v[s])] for s in ts}
+        for t in ts:
+            wq = _mv(W, q[t])
+            corr = [0] * d
+            for s in ts:
+                if s <= t:
+                    a = eta[s] * _dot(k[s], q[t])
+                    corr = [c + a * e for c, e in zip(corr, E[s])]
+            z.append([x - 2 * c for x, c in zip(wq, corr)])
+        Wn = [list(r) for r in W]
+        for s in ts:
+            for i in range(d):
+                for j in range(d):
+                    Wn[i][j] -= 2 * eta[s] * E[s][i] * k[s][j]
+        W = Wn
+    return z, W
+
+
+# ----------------------------------------------------------------------------
+# numpy fp64 forms (self-checks of the C oracle only)
+# ----------------------------------------------------------------------------
+
+def linear_dual_f64(q, k, v, w0, eta, b):
+    """Dual form (03 §7) per chain in fp64, column notation.  Shapes as linear_primal."""
+    q, k, v, w0, eta = map(_f64, (q, k, v, w0, eta))
+    n, T, d = q.shape
+    z = np.empty((n, T, d))
+    wf = np.empty((n, d, d))
+    for c in range(n):
+        W = w0[c].copy()
+        for t0 in range(0, T, b):
+            sl = slice(t0, min(t0 + b, T))
+            K, V, Q = k[c, sl].T, v[c, sl].T, q[c, sl].T      # d x b columns
+            et = eta[c, sl]
+            E = W @ K - V
+            A = np.triu(K.T @ Q) * et[:, None]               # A[s,t] = eta_s k_s.q_t [s<=t]
+            z[c, sl] = (W @ Q - 2.0 * E @ A).T
+            W = W - 2.0 * (E * et[None, :]) @ K.T
+        wf[c] = W
+    return z, wf
+
+
+def linear_naive_f64(q, k, v, w0, eta, b):
+    """The 'naive' form of 03 §7: materialise every d x d gradient G_t."""
+    q, k, v, w0, eta = map(_f64, (q, k, v, w0, eta))
+    n, T, d = q.shape
+    z = np.empty((n, T, d))
+    wf = np.empty((n, d, d))
+    for c in range(n):
+        W = w0[c].copy()
+        for t0 in range(0, T, b):
+            ts = range(t0, min(t0 + b, T))
+            G = [2.0 * np.outer(W @ k[c, t] - v[c, t], k[c, t]) for t in ts]
+            for j, t in enumerate(ts):
+                Wt = W - sum(eta[c, s] * G[i] for i, s in enumerate(ts) if s <= t)
+                z[c, t] = Wt @ q[c, t]
+            W = W - sum(eta[c, s] * G[i] for i, s in enumerate(ts))
+        wf[c] = W
+    return z, wf
+
+
+def gelu(x):
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def gelu_prime(x):
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + erf(x / np.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+
+
+def mlp_primal_np(q, k, v, w1, w2, eta, b):
+    """numpy fp64 primal TTT-MLP (same rule as mlp_primal), for cross-checks."""
+    q, k, v, w1, w2, eta = map(_f64, (q, k, v, w1, w2, eta))
+    n, T, d = q.shape
+    z = np.empty((n, T, d))
+    W1f = np.empty_like(w1)
+    W2f = np.empty_like(w2)
+    for c in range(n):
+        W1, W2 = w1[c].copy(), w2[c].copy()
+        for t0 in range(0, T, b):
+            W1b, W2b = W1.copy(), W2.copy()
+            for t in range(t0, min(t0 + b, T)):
+                h = W1b @ k[c, t]
+                a = gelu(h)
+                e2 = 2.0 * (W2b @ a - v[c, t])
+                g1 = (W2b.T @ e2) * gelu_prime(h)
+                W2 = W2 - eta[c, t] * np.outer(e2, a)
+                W1 = W1 - eta[c, t] * np.outer(g1, k[c, t])
+                z[c, t] = W2 @ gelu(W1 @ q[c, t])
+        W1f[c], W2f[c] = W1, W2
+    return z, W1f, W2f
+
+
+def mlp_dual_f64(q, k, v, w1, w2, eta, b):
+    """Dual form of TTT-MLP, fp64 (the 03 §7 identity applied layer by layer).
+
+    Column notation per mini-batch (start weights W1, W2):
+      H_K = W1 K, A_K = gelu(H_K), E = 2 (W2 A_K - V),
+      D1 = (W2^T E) * gelu'(H_K),
+      H_Q = W1 Q - D1 (diag(eta) triu(K^T Q)),  A_Q = gelu(H_Q),
+      Z = W2 A_Q - E (diag(eta) triu(A_K^T A_Q)),
+      W1 -= D1 diag(eta) K^T,  W2 -= E diag(eta) A_K^T.
+    """
+    q, k, v, w1, w2, eta = map(_f64, (q, k, v, w1, w2, eta))
+    n, T, d = q.shape
+    z = np.empty((n, T, d))
+    W1f = np.empty_like(w1)
+    W2f = np.empty_like(w2)
+    for c in range(n):
+        W1, W2 = w1[c].copy(), w2[c].copy()
+        for t0 in range(0, T, b):
+            sl = slice(t0, min(t0 + b, T))
+            K, V, Q = k[c, sl].T, v[c, sl].T, q[c, sl].T
+            et = eta[c, sl]
+            HK = W1 @ K
+            AK = gelu(HK)
+            E = 2.0 * (W2 @ AK - V)
+            D1 = (W2.T @ E) * gelu_prime(HK)
+            HQ = W1 @ Q - D1 @ (np.triu(K.T @ Q) * et[:, None])
+            AQ = gelu(HQ)
+            z[c, sl] = (W2 @ AQ - E @ (np.triu(AK.T @ AQ) * et[:, None])).T
+            W1 = W1 - (D1 * et[None, :]) @ K.T
+            W2 = W2 - (E * et[None, :]) @ AK.T
+        W1f[c], W2f[c] = W1, W2
+    return z, W1f, W2f
+
+
+def max_rel_err(x, ref, axis_slices: Optional[int] = None) -> float:
+    """max over slices of max|x - ref| / max|ref|, slices along the leading axis."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    if x.size == 0:
+        return 0.0
+    xs = x.reshape(x.shape[0], -1)
+    rs = ref.reshape(ref.shape[0], -1)
+    num = np.abs(xs - rs).max(axis=1)
+    den = np.abs(rs).max(axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return float((num / den).max())

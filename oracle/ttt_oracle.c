@@ -1,0 +1,160 @@
+/*
+ * TEST INFRASTRUCTURE -- fp64 CPU oracle of the TTT layer forward pass.
+ * Only tests/, the smoke check and the benchmark's CPU-baseline leg use it.
+ * It shares no code with the HIP library and is never on the product path.
+ *
+ * Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，
+ * 一夜推翻Transformer" (aharts.cn / itmax.cn).
+ *
+ * What it computes is the *primal* form, token by token, in fp64:
+ *   - the hidden state is the weight W of a model f; the output for token t is
+ *     f applied to x_t with the already-updated W_t, and the update is one
+ *     gradient step of size eta on a self-supervised loss
+ *     ([TTT] 03 §1 "TTT hidden state");
+ *   - the loss is the multi-view reconstruction |f(k_t; W) - v_t|^2 and the
+ *     output uses the query view q_t ([TTT] 03 §5 "self-supervised task");
+ *   - mini-batch GD: every gradient of mini-batch n is taken at the W held
+ *     just before the first token of that mini-batch ([TTT] 03 §6);
+ *   - TTT-Linear: f(x) = W x with W square; TTT-MLP: two layers, hidden width
+ *     dh, GELU in between ([TTT] 03 §9 "two variants").
+ * The gradient of |W k - v|^2 with respect to W is 2 (W k - v) k^T (summed
+ * squared error, no 1/2, no 1/d).  GELU is the exact form x * Phi(x).
+ *
+ * Layouts (all fp64, caller-expanded per chain, row-major):
+ *   q, k, v, z : [n, T, d]        eta : [n, T]
+ *   linear: w0, wf : [n, d, d]    (z = W q)
+ *   mlp:    w1 : [n, dh, d]  w2 : [n, d, dh]
+ * A final mini-batch shorter than b (T % b != 0) is handled by the same rule.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_abi_version(void) { return 1; }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* y = M x, M is rows x cols row-major */
+static void matvec(const double* M, const double* x, double* y, int rows, int cols) {
+  for (int i = 0; i < rows; ++i) {
+    double s = 0.0;
+    const double* m = M + (size_t)i * cols;
+    for (int c = 0; c < cols; ++c) s += m[c] * x[c];
+    y[i] = s;
+  }
+}
+
+/* y = M^T x, M is rows x cols row-major, y has cols entries */
+static void matvec_t(const double* M, const double* x, double* y, int rows, int cols) {
+  for (int c = 0; c < cols; ++c) y[c] = 0.0;
+  for (int i = 0; i < rows; ++i) {
+    const double* m = M + (size_t)i * cols;
+    for (int c = 0; c < cols; ++c) y[c] += m[c] * x[i];
+  }
+}
+
+/* M -= a * u v^T  (rank one), M rows x cols */
+static void rank1_sub(double* M, double a, const double* u, const double* v, int rows, int cols) {
+  for (int i = 0; i < rows; ++i) {
+    double ai = a * u[i];
+    double* m = M + (size_t)i * cols;
+    for (int c = 0; c < cols; ++c) m[c] -= ai * v[c];
+  }
+}
+
+static double gelu(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
+static double gelu_prime(double x) {
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * inv_sqrt_2pi * exp(-0.5 * x * x);
+}
+
+/* TTT-Linear primal form for n independent chains. */
+void oracle_linear_primal(int n, int T, int d, int b,
+                          const double* q, const double* k, const double* v,
+                          const double* w0, const double* eta,
+                          double* z, double* wf, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int c = 0; c < n; ++c) {
+    const size_t dd = (size_t)d * d;
+    double* W = (double*)malloc(dd * sizeof(double));
+    double* Wb = (double*)malloc(dd * sizeof(double));
+    double* e = (double*)malloc((size_t)d * sizeof(double));
+    memcpy(W, w0 + c * dd, dd * sizeof(double));
+    for (int t0 = 0; t0 < T; t0 += b) {
+      memcpy(Wb, W, dd * sizeof(double)); /* state at the start of the mini-batch */
+      int t1 = t0 + b < T ? t0 + b : T;
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        matvec(Wb, k + o, e, d, d);                      /* e = Wb k_t - v_t */
+        for (int i = 0; i < d; ++i) e[i] -= v[o + i];
+        rank1_sub(W, 2.0 * eta[(size_t)c * T + t], e, k + o, d, d); /* W -= eta * 2 e k^T */
+        matvec(W, q + o, z + o, d, d);                   /* z_t = W_t q_t */
+      }
+    }
+    memcpy(wf + c * dd, W, dd * sizeof(double));
+    free(W); free(Wb); free(e);
+  }
+}
+
+/* TTT-MLP primal form: f(x) = W2 GELU(W1 x), W1 dh x d, W2 d x dh. */
+void oracle_mlp_primal(int n, int T, int d, int dh, int b,
+                       const double* q, const double* k, const double* v,
+                       const double* w1_0, const double* w2_0, const double* eta,
+                       double* z, double* w1f, double* w2f, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int c = 0; c < n; ++c) {
+    const size_t sz = (size_t)dh * d;
+    double* W1 = (double*)malloc(sz * sizeof(double));
+    double* W2 = (double*)malloc(sz * sizeof(double));
+    double* W1b = (double*)malloc(sz * sizeof(double));
+    double* W2b = (double*)malloc(sz * sizeof(double));
+    double* h = (double*)malloc((size_t)dh * sizeof(double));
+    double* a = (double*)malloc((size_t)dh * sizeof(double));
+    double* g1 = (double*)malloc((size_t)dh * sizeof(double));
+    double* e = (double*)malloc((size_t)d * sizeof(double));
+    memcpy(W1, w1_0 + c * sz, sz * sizeof(double));
+    memcpy(W2, w2_0 + c * sz, sz * sizeof(double));
+    for (int t0 = 0; t0 < T; t0 += b) {
+      memcpy(W1b, W1, sz * sizeof(double));
+      memcpy(W2b, W2, sz * sizeof(double));
+      int t1 = t0 + b < T ? t0 + b : T;
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        const double et = eta[(size_t)c * T + t];
+        /* forward of the reconstruction at the mini-batch-start weights */
+        matvec(W1b, k + o, h, dh, d);
+        for (int j = 0; j < dh; ++j) a[j] = gelu(h[j]);
+        matvec(W2b, a, e, d, dh);
+        for (int i = 0; i < d; ++i) e[i] = 2.0 * (e[i] - v[o + i]); /* dl/d(out) */
+        /* back-propagate to the hidden pre-activation */
+        matvec_t(W2b, e, g1, d, dh);
+        for (int j = 0; j < dh; ++j) g1[j] *= gelu_prime(h[j]);
+        /* one gradient step on both layers */
+        rank1_sub(W2, et, e, a, d, dh);
+        rank1_sub(W1, et, g1, k + o, dh, d);
+        /* output with the updated weights */
+        matvec(W1, q + o, h, dh, d);
+        for (int j = 0; j < dh; ++j) a[j] = gelu(h[j]);
+        matvec(W2, a, z + o, d, dh);
+      }
+    }
+    memcpy(w1f + c * sz, W1, sz * sizeof(double));
+    memcpy(w2f + c * sz, W2, sz * sizeof(double));
+    free(W1); free(W2); free(W1b); free(W2b); free(h); free(a); free(g1); free(e);
+  }
+}
