@@ -1,0 +1,137 @@
+/*
+ * ttt.h -- C ABI of libttt.so, the MI355X (gfx950) forward pass of the TTT
+ * (test-time training) sequence layer: TTT-Linear and TTT-MLP, mini-batch
+ * dual form.
+ *
+ * Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，
+ * 一夜推翻Transformer" (aharts.cn / itmax.cn).
+ *
+ * The layer ([TTT] 03 §1, §5, §6, §7, §9).  Per (sequence bi, head h) the
+ * hidden state is the weight W of a small model f.  For token t with key,
+ * value and query views k_t, v_t, q_t (the caller applies the projections
+ * theta_K, theta_V, theta_Q):
+ *     W_t = W_{t-1} - eta_t * grad_W |f(k_t; W) - v_t|^2  evaluated at W_{t'}
+ *     z_t = f(q_t; W_t)                         (the UPDATED state)
+ * where t' is the last token before t's mini-batch of b tokens (mini-batch GD,
+ * 03 §6; mini-batch n holds tokens [n*b, (n+1)*b), 0-based).  The library
+ * computes this with the dual form of 03 §7, one mini-batch at a time:
+ *     E = W K - V,   Z = W Q - 2 E (diag(eta) triu(K^T Q)),
+ *     W <- W - 2 E diag(eta) K^T          (K, V, Q: d x b, one column per token)
+ * TTT-Linear: f(x) = W x, W square d x d.  TTT-MLP: f(x) = W2 GELU(W1 x),
+ * W1 dh x d, W2 d x dh, GELU(x) = x * Phi(x) (exact erf form).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (HIP global memory) allocated by
+ *    the caller; the library allocates nothing, keeps no global mutable state,
+ *    and is re-entrant.  Nothing is read or written on the host.
+ *  - Layouts are row-major and contiguous:
+ *      Q, K, V, Z : [B, H, T, d]   (token-major: one row of d per token)
+ *      W0, W_final: [B or 1, H, d, d] with z = W q  (row i = output i)
+ *  - eta is read as eta[bi*eta_stride_b + h*eta_stride_h + t*eta_stride_t]
+ *    (elements, fp32): (0,0,0) = one scalar, (0,1,0) = per head,
+ *    (H*T, T, 1) = per token.  Strides must be >= 0.
+ *  - The call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Argument errors are detected on the host BEFORE any launch and
+ *    nothing is written.  Faults during execution surface at the caller's next
+ *    synchronisation.
+ *  - Alignment: Q, K, V, Z, W0, W_final 16-byte aligned; eta 4-byte aligned.
+ *  - Outputs (Z, W_final) must not overlap any input, except that W_final may
+ *    be exactly W0 when W0 is per sequence (w0_batch_stride == H*d*d): the
+ *    in-place state carry used for streaming / resume.
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_NULL = 1,        /* a required pointer (or desc) is NULL               */
+  TTT_ERR_SHAPE = 2,       /* negative size, b < 1, T % b != 0, size overflow    */
+  TTT_ERR_DTYPE = 3,       /* dtype code is not a ttt_dtype                      */
+  TTT_ERR_UNSUPPORTED = 4, /* valid request, but no kernel built for it          */
+  TTT_ERR_ALIAS = 5,       /* an output overlaps an input in a forbidden way     */
+  TTT_ERR_ALIGN = 6,       /* a pointer is not aligned as required               */
+  TTT_ERR_HIP = 7,         /* the HIP runtime rejected the launch                */
+  TTT_ERR_STRIDE = 8,      /* negative eta stride, or w0 stride not 0 / H*d*d    */
+  TTT_ERR_FLAGS = 9        /* unknown bit set in flags                           */
+} ttt_status;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/* flags */
+#define TTT_FLAG_GENERIC 1u /* force the portable fp32 kernel (testing / cross-check) */
+
+/* TTT-Linear problem description. */
+typedef struct {
+  int32_t B, H, T, d, b;    /* batch, heads, tokens, head dim, mini-batch size      */
+  int32_t in_dtype;         /* ttt_dtype of Q, K, V                                  */
+  int32_t out_dtype;        /* ttt_dtype of Z (W_final is always fp32)               */
+  uint32_t flags;           /* TTT_FLAG_*                                            */
+  int64_t w0_batch_stride;  /* elements between sequences' W0: 0 (shared, [H,d,d])   */
+                            /* or H*d*d (per sequence, [B,H,d,d])                     */
+  int64_t eta_stride_b, eta_stride_h, eta_stride_t; /* elements, see above          */
+} ttt_linear_desc;
+
+/*
+ * TTT-Linear forward ([TTT] 03 §7 dual form, 03 §9 f(x) = W x).
+ *   Q, K, V : [B,H,T,d] of in_dtype       W0 : fp32, see w0_batch_stride
+ *   eta     : fp32, strided as above      Z  : [B,H,T,d] of out_dtype
+ *   W_final : [B,H,d,d] fp32, the state after the last token.
+ * Supported: d in {16, 32, 64}, fp32 or bf16 inputs, b <= 64 (b <= 32 for
+ * d = 64); d = 64, b = 16, bf16 inputs run the MFMA kernel.  B*H == 0 or
+ * T == 0 is valid (T == 0 copies W0 to W_final; Q/K/V/Z may then be NULL).
+ */
+ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                          const float* W0, const float* eta, void* Z, float* W_final, void* stream);
+
+/* Runs every host-side check of ttt_linear_fwd and launches nothing. */
+ttt_status ttt_linear_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                               const float* W0, const float* eta, const void* Z, const float* W_final);
+
+/* Name of the kernel ttt_linear_fwd would launch for desc, or NULL if unsupported. */
+const char* ttt_linear_kernel_name(const ttt_linear_desc* desc);
+
+/* TTT-MLP problem description ([TTT] 03 §9: two layers, GELU). */
+typedef struct {
+  int32_t B, H, T, d, dh, b; /* dh = hidden width (4*d on the pages)                */
+  int32_t in_dtype, out_dtype;
+  uint32_t flags;
+  int32_t reserved;          /* must be 0                                            */
+  int64_t w_batch_stride;    /* 0 (W1, W2 shared over the batch) or per sequence:   */
+                             /* H*dh*d (the same element count for W1 and W2)        */
+  int64_t eta_stride_b, eta_stride_h, eta_stride_t;
+} ttt_mlp_desc;
+
+/*
+ * TTT-MLP forward.  Q, K, V, Z as for TTT-Linear.
+ *   W1_0 : [B or 1, H, dh, d] fp32     W2_0 : [B or 1, H, d, dh] fp32
+ *   W1_final : [B,H,dh,d] fp32         W2_final : [B,H,d,dh] fp32
+ * Supported: d = 64, dh = 256, b = 16, bf16 inputs.
+ */
+ttt_status ttt_mlp_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                       const float* W1_0, const float* W2_0, const float* eta, void* Z,
+                       float* W1_final, float* W2_final, void* stream);
+
+ttt_status ttt_mlp_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                            const float* W1_0, const float* W2_0, const float* eta, const void* Z,
+                            const float* W1_final, const float* W2_final);
+
+const char* ttt_mlp_kernel_name(const ttt_mlp_desc* desc);
+
+/* Human-readable text of a status code (never NULL). */
+const char* ttt_status_str(int status);
+
+/* TTT_ABI_VERSION of the built library. */
+int ttt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_H_ */

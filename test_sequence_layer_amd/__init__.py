@@ -1,0 +1,262 @@
+"""MI355X (gfx950) forward pass of the TTT sequence layer -- Python binding.
+
+Thin ctypes layer over libttt.so (C ABI in include/ttt.h).  It only checks and
+marshals arguments: torch supplies device memory and the current HIP stream,
+and every step of the computation runs in the library's HIP kernels.  There is
+no CPU or PyTorch fallback: if libttt.so is missing, importing the ops raises.
+
+    import test_sequence_layer_amd as ttt
+    z, w_final = ttt.linear_fwd(q, k, v, w0, eta, b=16)
+    z, w1_final, w2_final = ttt.mlp_fwd(q, k, v, w1, w2, eta, b=16)
+
+Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，一夜推翻Transformer"
+(aharts.cn / itmax.cn), part 03 §1-§9 (the TTT layer, mini-batch GD, the dual
+form, TTT-Linear and TTT-MLP).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libttt.so")
+
+TTT_OK = 0
+TTT_F32, TTT_BF16 = 0, 1
+TTT_FLAG_GENERIC = 1
+
+STATUS_NAMES = {
+    0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE", 4: "TTT_ERR_UNSUPPORTED",
+    5: "TTT_ERR_ALIAS", 6: "TTT_ERR_ALIGN", 7: "TTT_ERR_HIP", 8: "TTT_ERR_STRIDE", 9: "TTT_ERR_FLAGS",
+}
+
+# Every symbol include/ttt.h declares.
+EXPORTS = (
+    "ttt_linear_fwd", "ttt_linear_validate", "ttt_linear_kernel_name",
+    "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name",
+    "ttt_status_str", "ttt_abi_version",
+)
+
+
+class LinearDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("b", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("w0_batch_stride", ctypes.c_int64),
+        ("eta_stride_b", ctypes.c_int64), ("eta_stride_h", ctypes.c_int64), ("eta_stride_t", ctypes.c_int64),
+    ]
+
+
+class MlpDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("dh", ctypes.c_int32), ("b", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+        ("w_batch_stride", ctypes.c_int64),
+        ("eta_stride_b", ctypes.c_int64), ("eta_stride_h", ctypes.c_int64), ("eta_stride_t", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libttt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    L.ttt_linear_fwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, vp, fp, vp]
+    L.ttt_linear_fwd.restype = ctypes.c_int
+    L.ttt_linear_validate.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, vp, fp]
+    L.ttt_linear_validate.restype = ctypes.c_int
+    L.ttt_linear_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
+    L.ttt_linear_kernel_name.restype = ctypes.c_char_p
+    L.ttt_mlp_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp, vp]
+    L.ttt_mlp_fwd.restype = ctypes.c_int
+    L.ttt_mlp_validate.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp]
+    L.ttt_mlp_validate.restype = ctypes.c_int
+    L.ttt_mlp_kernel_name.argtypes = [ctypes.POINTER(MlpDesc)]
+    L.ttt_mlp_kernel_name.restype = ctypes.c_char_p
+    L.ttt_status_str.argtypes = [ctypes.c_int]
+    L.ttt_status_str.restype = ctypes.c_char_p
+    L.ttt_abi_version.argtypes = []
+    L.ttt_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().ttt_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().ttt_abi_version())
+
+
+# ----------------------------------------------------------------- helpers --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return TTT_F32
+    if dt == torch.bfloat16:
+        return TTT_BF16
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("every tensor must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("every tensor must be contiguous")
+
+
+def eta_layout(eta, B: int, H: int, T: int, device):
+    """eta as (device fp32 tensor, (stride_b, stride_h, stride_t)).
+
+    float / 1-element tensor -> scalar; [H] -> per head; [B, H, T] -> per token.
+    """
+    torch = _torch()
+    if not torch.is_tensor(eta):
+        return torch.tensor([float(eta)], dtype=torch.float32, device=device), (0, 0, 0)
+    if eta.dtype != torch.float32:
+        raise TypeError("eta must be float32")
+    if eta.numel() == 1:
+        return eta.reshape(1), (0, 0, 0)
+    if tuple(eta.shape) == (H,):
+        return eta, (0, 1, 0)
+    if tuple(eta.shape) == (B, H, T):
+        return eta, (H * T, T, 1)
+    raise ValueError(f"eta shape {tuple(eta.shape)}: expected scalar, [H] or [B, H, T]")
+
+
+# ------------------------------------------------------------- TTT-Linear --
+
+def linear_desc(B, H, T, d, b, in_dtype, out_dtype, w0_batch_stride, eta_strides, flags=0) -> LinearDesc:
+    return LinearDesc(B, H, T, d, b, in_dtype, out_dtype, flags, w0_batch_stride, *eta_strides)
+
+
+def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
+               generic: bool = False, stream=None) -> Tuple["object", "object"]:
+    """TTT-Linear forward (dual form) on the GPU.
+
+    q, k, v : [B, H, T, d] bfloat16 or float32 (same dtype), contiguous, on the GPU
+    w0      : [H, d, d] (shared over the batch) or [B, H, d, d] float32; z = W q
+    eta     : float, [H] or [B, H, T] float32
+    b       : mini-batch size (T % b == 0)
+    returns (Z [B, H, T, d] of out_dtype (default float32), W_final [B, H, d, d] float32).
+    ``w_final`` may be ``w0`` itself (in-place carry) when w0 is [B, H, d, d].
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    if w0.dtype != torch.float32:
+        raise TypeError("w0 must be float32")
+    if tuple(w0.shape) == (H, d, d):
+        wstride = 0
+    elif tuple(w0.shape) == (B, H, d, d):
+        wstride = H * d * d
+    else:
+        raise ValueError(f"w0 shape {tuple(w0.shape)}: expected [H,d,d] or [B,H,d,d]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    if w_final is None:
+        w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    _check_dev(q, k, v, w0, eta_t, z, w_final)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est,
+                       TTT_FLAG_GENERIC if generic else 0)
+    st = lib().ttt_linear_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta_t),
+                              _ptr(z), _ptr(w_final), _stream_handle(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_fwd")
+    return z, w_final
+
+
+def linear_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),
+                       generic=False) -> Optional[str]:
+    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_GENERIC if generic else 0)
+    name = lib().ttt_linear_kernel_name(ctypes.byref(desc))
+    return None if name is None else name.decode()
+
+
+# ---------------------------------------------------------------- TTT-MLP --
+
+def mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, w_batch_stride, eta_strides) -> MlpDesc:
+    return MlpDesc(B, H, T, d, dh, b, in_dtype, out_dtype, 0, 0, w_batch_stride, *eta_strides)
+
+
+def mlp_fwd(q, k, v, w1, w2, eta, b: int, out_dtype=None, w1_final=None, w2_final=None, z=None,
+            stream=None):
+    """TTT-MLP forward: f(x) = W2 GELU(W1 x).
+
+    w1 : [H, dh, d] or [B, H, dh, d] float32;  w2 : [H, d, dh] or [B, H, d, dh] float32
+    returns (Z, W1_final [B,H,dh,d], W2_final [B,H,d,dh]).
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    dh = w1.shape[-2]
+    if w1.dtype != torch.float32 or w2.dtype != torch.float32:
+        raise TypeError("w1, w2 must be float32")
+    if tuple(w1.shape) == (H, dh, d) and tuple(w2.shape) == (H, d, dh):
+        wstride = 0
+    elif tuple(w1.shape) == (B, H, dh, d) and tuple(w2.shape) == (B, H, d, dh):
+        wstride = H * dh * d
+    else:
+        raise ValueError("w1/w2 shapes: expected [H,dh,d]/[H,d,dh] or [B,H,dh,d]/[B,H,d,dh]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    if w1_final is None:
+        w1_final = torch.empty((B, H, dh, d), dtype=torch.float32, device=q.device)
+    if w2_final is None:
+        w2_final = torch.empty((B, H, d, dh), dtype=torch.float32, device=q.device)
+    _check_dev(q, k, v, w1, w2, eta_t, z, w1_final, w2_final)
+    desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est)
+    st = lib().ttt_mlp_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(eta_t),
+                           _ptr(z), _ptr(w1_final), _ptr(w2_final), _stream_handle(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_mlp_fwd")
+    return z, w1_final, w2_final
+
+
+def mlp_kernel_name(B, H, T, d, dh, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0)):
+    desc = mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, 0, eta_strides)
+    name = lib().ttt_mlp_kernel_name(ctypes.byref(desc))
+    return None if name is None else name.decode()

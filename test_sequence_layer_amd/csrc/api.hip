@@ -1,0 +1,258 @@
+// C ABI of libttt.so: argument validation and kernel dispatch.
+// The entry points and their contracts are documented in include/ttt.h.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/ttt.h"
+#include "ttt_internal.h"
+
+namespace {
+
+struct Range {
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlaps(Range a, Range b) {
+  if (a.bytes <= 0 || b.bytes <= 0 || a.p == nullptr || b.p == nullptr) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// a*b*c*... <= limit without overflow (all factors >= 0)
+bool mul_ok(int64_t& acc, int64_t f, int64_t limit = (int64_t(1) << 46)) {
+  if (f < 0) return false;
+  if (f != 0 && acc > limit / f) return false;
+  acc *= f;
+  return true;
+}
+
+int64_t dtype_size(int32_t dt) { return dt == TTT_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dt) { return dt == TTT_F32 || dt == TTT_BF16; }
+
+// element extent of eta (last index + 1) for B, H, T >= 1
+int64_t eta_extent(int64_t B, int64_t H, int64_t T, int64_t sb, int64_t sh, int64_t st) {
+  return (B - 1) * sb + (H - 1) * sh + (T - 1) * st + 1;
+}
+
+enum Kernel { K_NONE, K_GENERIC, K_MFMA };
+
+Kernel pick_linear(const ttt::LinearArgs& a, uint32_t flags) {
+  if (flags & TTT_FLAG_GENERIC) return ttt::linear_generic_supported(a.d, a.b) ? K_GENERIC : K_NONE;
+  if (ttt::linear_mfma_supported(a)) return K_MFMA;
+  if (ttt::linear_generic_supported(a.d, a.b)) return K_GENERIC;
+  return K_NONE;
+}
+
+ttt::LinearArgs make_linear_args(const ttt_linear_desc* d, const void* Q, const void* K, const void* V,
+                                 const float* W0, const float* eta, const void* Z, const float* Wf) {
+  ttt::LinearArgs a;
+  a.B = d->B; a.H = d->H; a.T = d->T; a.d = d->d; a.b = d->b;
+  a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype;
+  a.Q = Q; a.K = K; a.V = V; a.W0 = W0; a.w0_bstride = d->w0_batch_stride;
+  a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
+  a.Z = const_cast<void*>(Z); a.Wf = const_cast<float*>(Wf);
+  return a;
+}
+
+ttt_status validate_linear(const ttt_linear_desc* d, const void* Q, const void* K, const void* V,
+                           const float* W0, const float* eta, const void* Z, const float* Wf,
+                           Kernel* which) {
+  if (which) *which = K_NONE;
+  if (!d) return TTT_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->b < 1) return TTT_ERR_SHAPE;
+  if (d->T % d->b != 0) return TTT_ERR_SHAPE;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
+  if (d->flags & ~static_cast<uint32_t>(TTT_FLAG_GENERIC)) return TTT_ERR_FLAGS;
+  int64_t chains = 1, tok = 1, wel = 1;
+  if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
+  tok = chains;
+  if (!mul_ok(tok, d->T) || !mul_ok(tok, d->d)) return TTT_ERR_SHAPE;
+  wel = chains;
+  if (!mul_ok(wel, d->d) || !mul_ok(wel, d->d)) return TTT_ERR_SHAPE;
+  const int64_t hdd = static_cast<int64_t>(d->H) * d->d * d->d;
+  if (d->w0_batch_stride != 0 && d->w0_batch_stride != hdd) return TTT_ERR_STRIDE;
+  if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
+
+  ttt::LinearArgs a = make_linear_args(d, Q, K, V, W0, eta, Z, Wf);
+  const Kernel k = pick_linear(a, d->flags);
+  if (k == K_NONE) return TTT_ERR_UNSUPPORTED;
+  if (chains == 0) {
+    if (which) *which = k;
+    return TTT_OK;
+  }
+
+  // pointers
+  if (!W0 || !Wf) return TTT_ERR_NULL;
+  if (tok > 0 && (!Q || !K || !V || !Z || !eta)) return TTT_ERR_NULL;
+  if (!aligned(W0, 16) || !aligned(Wf, 16)) return TTT_ERR_ALIGN;
+  if (tok > 0 && (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Z, 16) || !aligned(eta, 4)))
+    return TTT_ERR_ALIGN;
+
+  // extents and aliasing
+  const int64_t in_b = tok * dtype_size(d->in_dtype);
+  const int64_t z_b = tok * dtype_size(d->out_dtype);
+  const int64_t wf_b = wel * 4;
+  const int64_t w0_b = (d->w0_batch_stride == 0 ? hdd : wel) * 4;
+  const int64_t eta_b =
+      tok > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const Range rq{Q, in_b}, rk{K, in_b}, rv{V, in_b}, re{eta, eta_b}, rw0{W0, w0_b};
+  const Range rz{Z, z_b}, rwf{Wf, wf_b};
+  for (Range in : {rq, rk, rv, re, rw0})
+    if (overlaps(rz, in)) return TTT_ERR_ALIAS;
+  if (overlaps(rz, rwf)) return TTT_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, re})
+    if (overlaps(rwf, in)) return TTT_ERR_ALIAS;
+  if (overlaps(rwf, rw0)) {
+    const bool inplace = static_cast<const void*>(Wf) == static_cast<const void*>(W0) && d->w0_batch_stride == hdd;
+    if (!inplace) return TTT_ERR_ALIAS;
+  }
+  if (which) *which = k;
+  return TTT_OK;
+}
+
+// ---------------------------------------------------------------- MLP --
+
+ttt::MlpArgs make_mlp_args(const ttt_mlp_desc* d, const void* Q, const void* K, const void* V, const float* W1,
+                           const float* W2, const float* eta, const void* Z, const float* W1f, const float* W2f) {
+  ttt::MlpArgs a;
+  a.B = d->B; a.H = d->H; a.T = d->T; a.d = d->d; a.dh = d->dh; a.b = d->b;
+  a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype;
+  a.Q = Q; a.K = K; a.V = V; a.W1 = W1; a.W2 = W2; a.w_bstride = d->w_batch_stride;
+  a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
+  a.Z = const_cast<void*>(Z); a.W1f = const_cast<float*>(W1f); a.W2f = const_cast<float*>(W2f);
+  return a;
+}
+
+ttt_status validate_mlp(const ttt_mlp_desc* d, const void* Q, const void* K, const void* V, const float* W1,
+                        const float* W2, const float* eta, const void* Z, const float* W1f, const float* W2f,
+                        bool* ok_kernel) {
+  if (ok_kernel) *ok_kernel = false;
+  if (!d) return TTT_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->dh < 1 || d->b < 1) return TTT_ERR_SHAPE;
+  if (d->T % d->b != 0) return TTT_ERR_SHAPE;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
+  if (d->flags != 0 || d->reserved != 0) return TTT_ERR_FLAGS;
+  int64_t chains = 1, tok = 1, wel = 1;
+  if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
+  tok = chains;
+  if (!mul_ok(tok, d->T) || !mul_ok(tok, d->d)) return TTT_ERR_SHAPE;
+  wel = chains;
+  if (!mul_ok(wel, d->d) || !mul_ok(wel, d->dh)) return TTT_ERR_SHAPE;
+  const int64_t hw = static_cast<int64_t>(d->H) * d->d * d->dh;
+  if (d->w_batch_stride != 0 && d->w_batch_stride != hw) return TTT_ERR_STRIDE;
+  if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
+  ttt::MlpArgs a = make_mlp_args(d, Q, K, V, W1, W2, eta, Z, W1f, W2f);
+  if (!ttt::mlp_supported(a)) return TTT_ERR_UNSUPPORTED;
+  if (chains == 0) {
+    if (ok_kernel) *ok_kernel = true;
+    return TTT_OK;
+  }
+  if (!W1 || !W2 || !W1f || !W2f) return TTT_ERR_NULL;
+  if (tok > 0 && (!Q || !K || !V || !Z || !eta)) return TTT_ERR_NULL;
+  for (const void* p : {static_cast<const void*>(W1), static_cast<const void*>(W2),
+                        static_cast<const void*>(W1f), static_cast<const void*>(W2f)})
+    if (!aligned(p, 16)) return TTT_ERR_ALIGN;
+  if (tok > 0 && (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Z, 16) || !aligned(eta, 4)))
+    return TTT_ERR_ALIGN;
+  const int64_t in_b = tok * dtype_size(d->in_dtype);
+  const int64_t z_b = tok * dtype_size(d->out_dtype);
+  const int64_t wf_b = wel * 4;
+  const int64_t w0_b = (d->w_batch_stride == 0 ? hw : wel) * 4;
+  const int64_t eta_b =
+      tok > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const Range rq{Q, in_b}, rk{K, in_b}, rv{V, in_b}, re{eta, eta_b}, rw1{W1, w0_b}, rw2{W2, w0_b};
+  const Range rz{Z, z_b}, rf1{W1f, wf_b}, rf2{W2f, wf_b};
+  for (Range out : {rz, rf1, rf2}) {
+    for (Range in : {rq, rk, rv, re})
+      if (overlaps(out, in)) return TTT_ERR_ALIAS;
+  }
+  if (overlaps(rz, rf1) || overlaps(rz, rf2) || overlaps(rf1, rf2)) return TTT_ERR_ALIAS;
+  if (overlaps(rz, rw1) || overlaps(rz, rw2)) return TTT_ERR_ALIAS;
+  const bool per_seq = d->w_batch_stride == hw;
+  if (overlaps(rf1, rw1) && !(per_seq && static_cast<const void*>(W1f) == static_cast<const void*>(W1)))
+    return TTT_ERR_ALIAS;
+  if (overlaps(rf2, rw2) && !(per_seq && static_cast<const void*>(W2f) == static_cast<const void*>(W2)))
+    return TTT_ERR_ALIAS;
+  if (overlaps(rf1, rw2) || overlaps(rf2, rw1)) return TTT_ERR_ALIAS;
+  if (ok_kernel) *ok_kernel = true;
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_abi_version(void) { return TTT_ABI_VERSION; }
+
+const char* ttt_status_str(int s) {
+  switch (s) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_NULL: return "a required pointer is NULL";
+    case TTT_ERR_SHAPE: return "invalid shape (negative size, b < 1, T % b != 0 or size overflow)";
+    case TTT_ERR_DTYPE: return "invalid dtype code";
+    case TTT_ERR_UNSUPPORTED: return "no kernel is built for this (d, b, dtype) combination";
+    case TTT_ERR_ALIAS: return "an output overlaps an input";
+    case TTT_ERR_ALIGN: return "a pointer is misaligned (16 bytes for tensors, 4 for eta)";
+    case TTT_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case TTT_ERR_STRIDE: return "invalid stride";
+    case TTT_ERR_FLAGS: return "unknown flag or non-zero reserved field";
+    default: return "unknown status";
+  }
+}
+
+ttt_status ttt_linear_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                               const float* W0, const float* eta, const void* Z, const float* W_final) {
+  return validate_linear(desc, Q, K, V, W0, eta, Z, W_final, nullptr);
+}
+
+const char* ttt_linear_kernel_name(const ttt_linear_desc* d) {
+  if (!d) return nullptr;
+  ttt::LinearArgs a = make_linear_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  switch (pick_linear(a, d->flags)) {
+    case K_MFMA: return ttt::linear_mfma_name(a);
+    case K_GENERIC: return ttt::linear_generic_name(a.d);
+    default: return nullptr;
+  }
+}
+
+ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                          const float* W0, const float* eta, void* Z, float* W_final, void* stream) {
+  Kernel k;
+  const ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  const ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (k == K_MFMA) ? ttt::launch_linear_mfma(a, s) : ttt::launch_linear_generic(a, s);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_mlp_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                            const float* W1_0, const float* W2_0, const float* eta, const void* Z,
+                            const float* W1_final, const float* W2_final) {
+  return validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, nullptr);
+}
+
+const char* ttt_mlp_kernel_name(const ttt_mlp_desc* d) {
+  if (!d) return nullptr;
+  ttt::MlpArgs a = make_mlp_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr);
+  return ttt::mlp_supported(a) ? ttt::mlp_name(a) : nullptr;
+}
+
+ttt_status ttt_mlp_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* W1_0,
+                       const float* W2_0, const float* eta, void* Z, float* W1_final, float* W2_final,
+                       void* stream) {
+  bool ok;
+  const ttt_status st = validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, &ok);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  const ttt::MlpArgs a = make_mlp_args(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final);
+  const hipError_t e = ttt::launch_mlp(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+}  // extern "C"

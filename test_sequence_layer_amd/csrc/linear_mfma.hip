@@ -1,0 +1,313 @@
+// TTT-Linear dual-form forward on CDNA4 matrix cores: d = 64, b = 16, bf16 Q/K/V.
+//
+// Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，一夜推翻Transformer"
+// (aharts.cn / itmax.cn), part 03 §6 (mini-batch GD: every gradient of a
+// mini-batch is taken at the state before it), §7 (dual form: never build the
+// b per-token d x d gradients; get the mini-batch-end state and the b outputs
+// from matrix products), §9 (TTT-Linear, f(x) = W x).
+//
+// Work decomposition
+//   One workgroup (4 waves) per (sequence, head) walks the T/16 mini-batches
+//   in order.  Rows of W are independent (row i of the next state and of Z
+//   needs only row i of W, column i of V and all of K, Q, eta), so wave w
+//   owns rows [16w, 16w+16) of W and never talks to the other waves except
+//   through the shared input tiles.
+//
+// State layout (the key trick)
+//   Wave w keeps W^T[c][i] (c = 0..63, i = 16w..16w+15) as four 16x16 fp32
+//   MFMA accumulator tiles: lane l holds W[16w + l%16][16a + 4(l/16) + r] in
+//   wt[a][r].  That is exactly the B-operand layout (k = c, n = i) the
+//   projections K W^T and Q W^T need, so the state is fed back into the
+//   matrix cores with no transpose and no LDS round trip, and the rank-16
+//   update accumulates straight into it.
+//
+// Per mini-batch, per wave (M = 16 tokens, N = 16 rows of W):
+//   P_K = K W^T, P_Q = Q W^T    v_mfma_f32_16x16x32_bf16, W split hi+lo bf16
+//   S   = K Q^T (s x t)         v_mfma_f32_16x16x32_bf16, exact bf16 products
+//   E   = P_K - V               registers (E^T layout: lane = (t = 4g+r, i))
+//   Z   = P_Q - L E,  L[t][s] = 2 eta_s S[s][t] [s <= t]
+//                               v_mfma_f32_16x16x16_bf16, 3-pass split
+//   W^T += K^T (-2 diag(eta) E) v_mfma_f32_16x16x16_bf16, E split hi+lo
+//   The S accumulator layout (s = 4g+r, t = l%16) is the A-operand layout of
+//   L, and the E accumulator layout is the B-operand layout of both the Z
+//   correction and the update: the mask and the eta scaling are applied in
+//   registers between the products.
+//
+// Precision: fp32 operands enter the bf16 matrix cores as hi + lo bf16 pairs
+// (|x - hi - lo| <= 2^-18 |x|); bf16 x bf16 products are exact and every sum
+// is fp32, so the result tracks an fp32 computation.
+//
+// Streaming: a 16-token tile of Q, K, V is 3 x 2 KB contiguous.  Each step
+// loads the tile PF steps ahead into registers (coalesced 16-byte loads),
+// stores the tile one step ahead into a double-buffered LDS slot (plus a
+// transposed copy of K for the update's A operand), and issues one barrier.
+#include "ttt_internal.h"
+
+namespace ttt {
+namespace {
+
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short short4v __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float float4v __attribute__((__vector_size__(4 * sizeof(float))));
+
+constexpr int D = 64;       // head dim
+constexpr int BT = 16;      // mini-batch (tokens)
+constexpr int ROW = 72;     // padded LDS row of a token tile (bf16 elements, 144 B)
+constexpr int KTROW = 20;   // padded LDS row of the transposed K tile (bf16, 40 B)
+constexpr int kThreads = 256;
+
+struct __align__(16) Slot {
+  uint16_t q[BT * ROW];
+  uint16_t k[BT * ROW];
+  uint16_t v[BT * ROW];
+  uint16_t kt[D * KTROW];
+  float eta[BT];
+};
+static_assert(sizeof(Slot) % 16 == 0, "slot size");
+
+__device__ __forceinline__ float4v mfma32(bf16x8 a, bf16x8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4v mfma16(bf16x4 a, bf16x4 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                   __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split4(const float x[4], bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 h = static_cast<__bf16>(x[j]);
+    hi[j] = h;
+    lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+  }
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store_z(OutT* p, float x);
+template <>
+__device__ __forceinline__ void store_z<float>(float* p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store_z<uint16_t>(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
+
+template <int PF, bool ETA_TOKEN, typename OutT>
+__global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a) {
+  __shared__ Slot slots[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int li = lane & 15;
+  const int g = lane >> 4;
+
+  const int chain = blockIdx.x;
+  const int bi = chain / a.H;
+  const int h = chain - bi * a.H;
+  const int nb = a.T / BT;
+
+  const size_t tok0 = static_cast<size_t>(chain) * a.T;
+  const uint4* Qg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + tok0 * D);
+  const uint4* Kg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.K) + tok0 * D);
+  const uint4* Vg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + tok0 * D);
+  OutT* Zg = static_cast<OutT*>(a.Z) + tok0 * D;
+  const float* eg = a.eta + bi * a.esb + h * a.esh;
+
+  // staging roles (every load unconditional, so the ring stays in registers):
+  //   16 B of Q (tid < 128) or K (tid >= 128): row srow, columns scol..scol+7
+  //   8 B of V: row vrow, columns vcol..vcol+3;  eta of token (tid & 15)
+  const int within = tid & 127;
+  const uint4* srcA = (tid < 128 ? Qg : Kg) + within;
+  const uint2* srcB = reinterpret_cast<const uint2*>(Vg) + tid;
+  const int srow = within >> 3;
+  const int scol = (within & 7) * 8;
+  const int vrow = tid >> 4;
+  const int vcol = (tid & 15) * 4;
+  const float* srcE = eg + static_cast<int64_t>(tid & 15) * a.est;
+
+  uint4 ra[PF];
+  uint2 rb[PF];
+  float re[PF];
+
+  auto load_step = [&](int n, uint4& xa, uint2& xb, float& xe) {
+    xa = srcA[static_cast<size_t>(n) * (BT * D / 8)];  // 128 uint4 per tile
+    xb = srcB[static_cast<size_t>(n) * (BT * D / 4)];  // 256 uint2 per tile
+    xe = ETA_TOKEN ? srcE[static_cast<int64_t>(n) * BT * a.est] : 0.f;
+  };
+  auto stage = [&](int slot, const uint4& xa, const uint2& xb, float xe) {
+    Slot& S = slots[slot];
+    *reinterpret_cast<uint2*>(&S.v[vrow * ROW + vcol]) = xb;
+    if (tid < 128) {
+      *reinterpret_cast<uint4*>(&S.q[srow * ROW + scol]) = xa;
+    } else {
+      *reinterpret_cast<uint4*>(&S.k[srow * ROW + scol]) = xa;
+      const uint32_t wv[4] = {xa.x, xa.y, xa.z, xa.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        S.kt[(scol + 2 * j) * KTROW + srow] = static_cast<uint16_t>(wv[j] & 0xffffu);
+        S.kt[(scol + 2 * j + 1) * KTROW + srow] = static_cast<uint16_t>(wv[j] >> 16);
+      }
+    }
+    if (ETA_TOKEN && tid < BT) S.eta[tid] = xe;
+  };
+
+  // constant eta (scalar or per head)
+  float eta_c = 0.f;
+  if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
+
+  // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
+  float4v wt[4];
+  {
+    const float* w0 = a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D +
+                      static_cast<int64_t>(16 * w + li) * D + 4 * g;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4 x = *reinterpret_cast<const float4*>(w0 + 16 * t);
+      wt[t] = float4v{x.x, x.y, x.z, x.w};
+    }
+  }
+
+  // Drain the state / eta loads before the ring prologue: otherwise the
+  // compiler's wait analysis sees them pending at the loop header and makes
+  // every step wait for all outstanding loads (vmcnt(0)), which serialises the
+  // prefetch ring.  (s_waitcnt immediate: vmcnt = 0, expcnt = 7, lgkmcnt = 15.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  if (nb > 0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load_step(min(j, nb - 1), ra[j], rb[j], re[j]);
+    stage(0, ra[0], rb[0], re[0]);
+  }
+  __syncthreads();
+
+  // One mini-batch: stage step n+1 (ring slot jn) into LDS, prefetch step
+  // min(n+PF, nb-1) into ring slot j, compute step n, barrier.  The prefetch
+  // index is clamped instead of guarded so every step issues the same memory
+  // operations and the compiler's wait counts stay exact.
+  auto step = [&](const int n, uint4& xa, uint2& xb, float& xe, const uint4& ya, const uint2& yb,
+                  const float ye) {
+    stage((n + 1) & 1, ya, yb, ye);
+    load_step(min(n + PF, nb - 1), xa, xb, xe);
+    const Slot& S = slots[n & 1];
+    // ---- operands: token rows li, column groups {16a + 4g .. +3} ----
+    bf16x4 kx[4], qx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      kx[t] = *reinterpret_cast<const bf16x4*>(&S.k[li * ROW + 16 * t + 4 * g]);
+      qx[t] = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * t + 4 * g]);
+    }
+    float et[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) et[r] = ETA_TOKEN ? S.eta[4 * g + r] : eta_c;
+
+    // ---- P_K = K W^T, P_Q = Q W^T, S = K Q^T ----
+    float4v pk = {0.f, 0.f, 0.f, 0.f}, pq = pk, sc = pk;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float w8[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        w8[r] = wt[2 * m][r];
+        w8[4 + r] = wt[2 * m + 1][r];
+      }
+      bf16x4 h0, l0, h1, l1;
+      split4(w8, h0, l0);
+      split4(w8 + 4, h1, l1);
+      const bf16x8 whi = cat(h0, h1), wlo = cat(l0, l1);
+      const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
+      const bf16x8 aq = cat(qx[2 * m], qx[2 * m + 1]);
+      pk = mfma32(ak, whi, pk);
+      pq = mfma32(aq, whi, pq);
+      sc = mfma32(ak, aq, sc);
+      pk = mfma32(ak, wlo, pk);
+      pq = mfma32(aq, wlo, pq);
+    }
+
+    // ---- E^T[t = 4g+r][i = 16w+li] = P_K - V ----
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      e[r] = pk[r] - bf16_bits_to_f32(S.v[(4 * g + r) * ROW + 16 * w + li]);
+
+    // ---- Z = P_Q - L E, L[t][s] = 2 eta_s S[s][t] (s <= t) ----
+    float lv[4], bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = 4 * g + r;
+      lv[r] = (s <= li) ? -2.f * et[r] * sc[r] : 0.f;
+      bv[r] = -2.f * et[r] * e[r];
+    }
+    bf16x4 lhi, llo, ehi, elo, bhi, blo;
+    split4(lv, lhi, llo);
+    split4(e, ehi, elo);
+    split4(bv, bhi, blo);
+    float4v z = pq;
+    z = mfma16(lhi, ehi, z);
+    z = mfma16(lhi, elo, z);
+    z = mfma16(llo, ehi, z);
+
+    // ---- W^T[c][i] += sum_s K[s][c] (-2 eta_s E[i][s]) ----
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x4 kt = *reinterpret_cast<const bf16x4*>(&S.kt[(16 * t + li) * KTROW + 4 * g]);
+      wt[t] = mfma16(kt, bhi, wt[t]);
+      wt[t] = mfma16(kt, blo, wt[t]);
+    }
+
+    // ---- store Z rows t = 4g + r, columns 16w + li ----
+    OutT* zp = Zg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_z<OutT>(zp + r * D, z[r]);
+
+    __syncthreads();
+  };
+
+  const int nfull = nb / PF * PF;
+  for (int n0 = 0; n0 < nfull; n0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int jn = (j + 1) % PF;
+      step(n0 + j, ra[j], rb[j], re[j], ra[jn], rb[jn], re[jn]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int jn = (j + 1) % PF;
+    if (nfull + j < nb) step(nfull + j, ra[j], rb[j], re[j], ra[jn], rb[jn], re[jn]);
+  }
+
+  float* wf = a.Wf + static_cast<int64_t>(chain) * D * D + static_cast<int64_t>(16 * w + li) * D + 4 * g;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    *reinterpret_cast<float4*>(wf + 16 * t) = make_float4(wt[t][0], wt[t][1], wt[t][2], wt[t][3]);
+}
+
+constexpr int kPF = 4;
+
+template <bool TOK>
+hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.H), block(kThreads);
+  if (a.out_dtype == 0)
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool linear_mfma_supported(const LinearArgs& a) { return a.d == 64 && a.b == 16 && a.in_dtype == 1; }
+
+const char* linear_mfma_name(const LinearArgs& a) {
+  (void)a;
+  return "ttt_linear_mfma_d64b16";
+}
+
+hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
+  return a.est != 0 ? launch_eta<true>(a, s) : launch_eta<false>(a, s);
+}
+
+}  // namespace ttt

@@ -1,0 +1,66 @@
+// Internal declarations of libttt.so (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+// Everything a TTT-Linear launch needs, validated on the host.
+struct LinearArgs {
+  int B, H, T, d, b;
+  int in_dtype, out_dtype;  // 0 = fp32, 1 = bf16
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* W0;
+  int64_t w0_bstride;  // elements between sequences' W0 (0 = shared)
+  const float* eta;
+  int64_t esb, esh, est;  // eta strides (elements)
+  void* Z;
+  float* Wf;
+};
+
+struct MlpArgs {
+  int B, H, T, d, dh, b;
+  int in_dtype, out_dtype;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* W1;
+  const float* W2;
+  int64_t w_bstride;
+  const float* eta;
+  int64_t esb, esh, est;
+  void* Z;
+  float* W1f;
+  float* W2f;
+};
+
+// Portable fp32 kernel (any supported d/b/dtype).
+bool linear_generic_supported(int d, int b);
+const char* linear_generic_name(int d);
+hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
+
+// MFMA kernel: d = 64, b = 16, bf16 Q/K/V.
+bool linear_mfma_supported(const LinearArgs& a);
+const char* linear_mfma_name(const LinearArgs& a);
+hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
+
+// TTT-MLP kernel: d = 64, dh = 256, b = 16, bf16 Q/K/V.
+bool mlp_supported(const MlpArgs& a);
+const char* mlp_name(const MlpArgs& a);
+hipError_t launch_mlp(const MlpArgs& a, hipStream_t s);
+
+// bf16 <-> fp32 on raw bits (the library stores bf16 as uint16_t).
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = static_cast<__bf16>(x);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+}  // namespace ttt

@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: libttt.so loads, exports every symbol include/ttt.h
+declares, and its host-side validation returns the documented status codes.
+
+Validation runs entirely on the host before any HIP call, so it is exercised
+here through ttt_*_validate with fake (never dereferenced) device addresses.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import test_sequence_layer_amd as ttt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, ALIGN, HIP, STRIDE, FLAGS = range(10)
+GB = 1 << 30
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(ttt_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(ttt.EXPORTS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    L = ttt.lib()
+    for sym in _declared():
+        assert hasattr(L, sym), sym
+    out = subprocess.run(["nm", "-D", "--defined-only", ttt.LIB_PATH], capture_output=True, text=True).stdout
+    for sym in _declared():
+        assert re.search(rf"\bT {sym}$", out, re.M), sym
+
+
+def test_version_and_status_strings():
+    assert ttt.abi_version() == 1
+    for s in range(10):
+        assert ttt.status_str(s) and ttt.status_str(s) != "unknown status"
+    assert ttt.status_str(99) == "unknown status"
+
+
+# ---- TTT-Linear validation -----------------------------------------------------
+
+class Bufs:
+    """Fake, well-separated, aligned device addresses for one problem."""
+
+    def __init__(self):
+        self.q, self.k, self.v = 1 * GB, 2 * GB, 3 * GB
+        self.w0, self.eta, self.z, self.wf = 4 * GB, 5 * GB, 6 * GB, 7 * GB
+
+    def args(self):
+        return (self.q, self.k, self.v, self.w0, self.eta, self.z, self.wf)
+
+
+def _desc(B=2, H=4, T=64, d=64, b=16, ind=1, outd=0, flags=0, wstride=0, est=(0, 0, 0)):
+    return ttt.linear_desc(B, H, T, d, b, ind, outd, wstride, est, flags)
+
+
+def _val(desc, bufs=None, **over):
+    bufs = bufs or Bufs()
+    for k, v in over.items():
+        setattr(bufs, k, v)
+    return ttt.lib().ttt_linear_validate(ctypes.byref(desc), *bufs.args())
+
+
+def test_linear_ok():
+    assert _val(_desc()) == OK
+    assert _val(_desc(est=(4 * 64, 64, 1))) == OK
+    assert _val(_desc(ind=0, d=16, b=4)) == OK
+
+
+def test_linear_null():
+    assert ttt.lib().ttt_linear_validate(None, *Bufs().args()) == NULL
+    for name in ("q", "k", "v", "w0", "eta", "z", "wf"):
+        assert _val(_desc(), **{name: None}) == NULL, name
+
+
+def test_linear_empty_allows_null_tensors():
+    assert _val(_desc(B=0), q=None, k=None, v=None, z=None, w0=None, wf=None, eta=None) == OK
+    assert _val(_desc(T=0), q=None, k=None, v=None, z=None, eta=None) == OK
+    assert _val(_desc(T=0), w0=None) == NULL
+
+
+@pytest.mark.parametrize("kw", [dict(T=60), dict(b=0), dict(B=-1), dict(d=0), dict(T=-16)])
+def test_linear_shape(kw):
+    assert _val(_desc(**kw)) == SHAPE
+
+
+def test_linear_dtype_flags_stride():
+    assert _val(_desc(ind=2)) == DTYPE
+    assert _val(_desc(outd=-1)) == DTYPE
+    assert _val(_desc(flags=4)) == FLAGS
+    assert _val(_desc(wstride=5)) == STRIDE
+    assert _val(_desc(est=(0, -1, 0))) == STRIDE
+    assert _val(_desc(wstride=4 * 64 * 64)) == OK
+
+
+@pytest.mark.parametrize("kw", [dict(d=48), dict(d=128), dict(d=64, b=64), dict(d=16, b=65, T=130)])
+def test_linear_unsupported(kw):
+    assert _val(_desc(**kw)) == UNSUP
+
+
+def test_linear_align():
+    assert _val(_desc(), q=1 * GB + 8) == ALIGN
+    assert _val(_desc(), wf=7 * GB + 4) == ALIGN
+    assert _val(_desc(), eta=5 * GB + 2) == ALIGN
+    assert _val(_desc(), eta=5 * GB + 4) == OK
+
+
+def test_linear_alias():
+    d = _desc()
+    assert _val(d, z=1 * GB) == ALIAS                       # Z == Q
+    assert _val(d, z=2 * GB + 4096) == ALIAS                # Z inside K
+    assert _val(d, wf=3 * GB) == ALIAS                      # W_final == V
+    assert _val(d, wf=4 * GB) == ALIAS                      # in place with a shared W0
+    assert _val(_desc(wstride=4 * 64 * 64), wf=4 * GB) == OK      # in place, per-sequence W0
+    assert _val(_desc(wstride=4 * 64 * 64), wf=4 * GB + 256) == ALIAS
+    # Z directly after Q (no overlap) is fine: Q is 2*4*64*64*2 bytes
+    assert _val(d, z=1 * GB + 2 * 4 * 64 * 64 * 2) == OK
+    assert _val(d, z=1 * GB + 2 * 4 * 64 * 64 * 2 - 16) == ALIAS
+
+
+def test_linear_kernel_selection():
+    assert ttt.linear_kernel_name(16, 32, 8192, 64, 16) == "ttt_linear_mfma_d64b16"
+    assert ttt.linear_kernel_name(16, 32, 8192, 64, 16, generic=True) == "ttt_linear_generic_kernel<64>"
+    assert ttt.linear_kernel_name(1, 1, 64, 16, 4, in_dtype=0) == "ttt_linear_generic_kernel<16>"
+    assert ttt.linear_kernel_name(1, 1, 64, 64, 16, in_dtype=0) == "ttt_linear_generic_kernel<64>"
+    assert ttt.linear_kernel_name(1, 1, 64, 48, 16) is None
+
+
+# ---- TTT-MLP validation ----------------------------------------------------------
+
+def _mdesc(B=2, H=4, T=64, d=64, dh=256, b=16, wstride=0, est=(0, 0, 0)):
+    return ttt.mlp_desc(B, H, T, d, dh, b, 1, 0, wstride, est)
+
+
+def _mval(desc, **over):
+    p = dict(q=1 * GB, k=2 * GB, v=3 * GB, w1=4 * GB, w2=5 * GB, eta=6 * GB, z=7 * GB, f1=8 * GB, f2=9 * GB)
+    p.update(over)
+    return ttt.lib().ttt_mlp_validate(ctypes.byref(desc), p["q"], p["k"], p["v"], p["w1"], p["w2"], p["eta"],
+                                      p["z"], p["f1"], p["f2"])
+
+
+def test_mlp_validation():
+    if ttt.mlp_kernel_name(2, 4, 64, 64, 256, 16) is None:
+        assert _mval(_mdesc()) == UNSUP
+        pytest.skip("MLP kernel not built")
+    assert _mval(_mdesc()) == OK
+    assert _mval(_mdesc(T=40)) == SHAPE
+    assert _mval(_mdesc(dh=128)) == UNSUP
+    assert _mval(_mdesc(), f1=None) == NULL
+    assert _mval(_mdesc(), z=1 * GB) == ALIAS
+    assert _mval(_mdesc(), f1=4 * GB) == ALIAS
+    assert _mval(_mdesc(wstride=4 * 64 * 256), f1=4 * GB, f2=5 * GB) == OK
+    assert _mval(_mdesc(), f2=9 * GB + 8) == ALIGN
