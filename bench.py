@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: TTT-Linear dual-form forward on one MI355X.
+
+One step = one call of the whole hot path (ttt_linear_fwd: every mini-batch of
+every (sequence, head) chain) on inputs already resident in HBM.  Prints one
+JSON line (rank 0) with tokens/s, the HBM roofline of the kernel (live HIP
+event timing) and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--config l1p3b|l125m|long|mlp]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import ttt_inputs as ti  # noqa: E402
+
+METRIC = "TTT-Linear fwd tokens/sec at B16 H32 d64 T8192 b16; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # fp32 matrix
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg: ti.Config, eta_strides):
+    """Algorithmic bytes and flops of one forward call (the unavoidable work).
+
+    Bytes: read Q, K, V once (bf16 or fp32), write Z once (fp32), read eta
+    (per token: 4 B per token-head; otherwise negligible), read W0, write W_final.
+    Flops per token-head: TTT-Linear 6 d^2 + 4 d b (W K, W Q, the b x b scores
+    and their product with E, and the rank-b state update); TTT-MLP: see DESIGN.
+    """
+    th = cfg.B * cfg.H * cfg.T
+    in_sz = 2 if cfg.dtype == "bf16" else 4
+    eta_b = 4 * th if eta_strides[2] != 0 else 4 * (cfg.H if eta_strides[1] else 1)
+    d, b = cfg.d, cfg.b
+    if cfg.is_mlp:
+        dh = cfg.dh
+        w = cfg.H * d * dh * 4 * 2
+        wf = cfg.B * cfg.H * d * dh * 4 * 2
+        flops_mb = 7 * 2 * d * dh * b + 2 * 2 * d * b * b + 2 * 2 * dh * b * b
+        flops = flops_mb * th // b
+    else:
+        w = cfg.H * d * d * 4
+        wf = cfg.B * cfg.H * d * d * 4
+        flops = th * (6 * d * d + 4 * d * b)
+    bytes_ = th * d * (3 * in_sz + 4) + eta_b + w + wf
+    return bytes_, flops
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "test_sequence_layer_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        db = json.load(fh)
+    rec = db.get(f"{kernel}|{workload}")
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int):
+    import oracle
+
+    chains = ti.sample_chains(cfg, sample_chains)
+    sub = ti.Inputs(cfg, chains, inp_full.q[chains], inp_full.k[chains], inp_full.v[chains],
+                    inp_full.w1, inp_full.w2, inp_full.eta_buf, inp_full.eta_strides)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.run_inputs(sub, threads=threads)
+    dt = time.perf_counter() - t0
+    tokens = len(chains) * cfg.T / cfg.H           # token = all H heads of one position
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(chains)} of {cfg.chains} (sequence, head) chains at full T={cfg.T}, "
+                      f"fp64 primal form, {dt:.2f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="l1p3b", choices=sorted(ti.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-chains", type=int, default=128)
+    ap.add_argument("--generic", action="store_true", help="time the portable fp32 kernel instead")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the (sequence, head) chains are independent, so N GPUs would each run this same kernel on "
+              "1/N of them with no communication", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import test_sequence_layer_amd as ttt
+
+    cfg = ti.CONFIGS[args.config]
+    log(f"bench: generating {cfg.name} inputs ...")
+    t0 = time.perf_counter()
+    inp = ti.generate(cfg)
+    t = ti.to_device(inp, "cuda:0")
+    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    z = torch.empty((B, H, T, d), dtype=torch.float32, device="cuda:0")
+    if cfg.is_mlp:
+        f1 = torch.empty((B, H, cfg.dh, d), dtype=torch.float32, device="cuda:0")
+        f2 = torch.empty((B, H, d, cfg.dh), dtype=torch.float32, device="cuda:0")
+        kname = ttt.mlp_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides)
+
+        def step():
+            ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1, w2_final=f2)
+    else:
+        wf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda:0")
+        kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
+                                       inp.eta_strides, args.generic)
+
+        def step():
+            ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf,
+                           generic=args.generic)
+    log(f"bench: kernel {kname}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps      # one launch per step
+    ms_per_step = max(wall * 1e3 / args.steps, kernel_ms)
+    tokens = B * T
+    value = tokens / (ms_per_step / 1e3)
+
+    bytes_, flops = algorithmic(cfg, inp.eta_strides)
+    achieved = bytes_ / (kernel_ms / 1e3) / 1e9
+    traffic = measured_traffic(kname, cfg.name)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes": bytes_, "kernel": kname, "kernel_ms": round(kernel_ms, 4)}
+    tflops = flops / (kernel_ms / 1e3) / 1e12
+    mfma = {"algorithmic_flops": flops, "achieved_tflops": round(tflops, 2),
+            "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "frac_of_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
+    log(f"bench: {kname}: {kernel_ms:.3f} ms/launch, {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM), "
+        f"{tflops:.1f} TFLOP/s algorithmic")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on a sample ...")
+        cpu = cpu_baseline(cfg, inp, args.cpu_sample_chains)
+        log(f"bench: cpu baseline {cpu['value']:.3e} tokens/s ({cpu['sample']})")
+
+    eta_desc = {(0, 0, 0): "scalar", (0, 1, 0): "per head"}.get(tuple(inp.eta_strides), "per token")
+    model = "TTT-MLP" if cfg.is_mlp else "TTT-Linear"
+    rec = {
+        "metric": METRIC if cfg.name == "l1p3b" else f"{model} fwd tokens/sec ({cfg.name})",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" and not args.generic else "fp32",
+        "data": "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) weights)",
+        "config": {"workload": f"{model} dual-form forward B{B} H{H} d{d}"
+                               f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
+                               f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta",
+                   "B": B, "H": H, "d": d, "T": T, "b": cfg.b, "global_batch": B, "seq_len": T,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "mfma": mfma,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,6 +19,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the state and the accumulators feed VALU
+    # work every step, and AGPR destinations would add a copy for each value
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

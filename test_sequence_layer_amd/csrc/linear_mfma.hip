@@ -25,17 +25,21 @@
 //   P_K = K W^T, P_Q = Q W^T    v_mfma_f32_16x16x32_bf16, W split hi+lo bf16
 //   S   = K Q^T (s x t)         v_mfma_f32_16x16x32_bf16, exact bf16 products
 //   E   = P_K - V               registers (E^T layout: lane = (t = 4g+r, i))
-//   Z   = P_Q - L E,  L[t][s] = 2 eta_s S[s][t] [s <= t]
-//                               v_mfma_f32_16x16x16_bf16, 3-pass split
-//   W^T += K^T (-2 diag(eta) E) v_mfma_f32_16x16x16_bf16, E split hi+lo
+//   G   = -2 diag(eta) E        registers (same layout as E)
+//   Z   = P_Q + M G,  M[t][s] = S[s][t] [s <= t]
+//                               v_mfma_f32_16x16x32_bf16 x2 (3 split passes)
+//   W^T += K^T G                v_mfma_f32_16x16x32_bf16, [K^T K^T] x [G_hi G_lo]
+//   Only the native gfx950 K=32 bf16 MFMA is used: a 16-token contraction
+//   puts two split passes into its 8 k-slots per lane group.
 //   The S accumulator layout (s = 4g+r, t = l%16) is the A-operand layout of
-//   L, and the E accumulator layout is the B-operand layout of both the Z
-//   correction and the update: the mask and the eta scaling are applied in
-//   registers between the products.
+//   M, and the E accumulator layout is the B-operand layout of both the Z
+//   correction and the update: the causal mask and the eta scaling are
+//   applied in registers between the products, and G is split once for both.
 //
-// Precision: fp32 operands enter the bf16 matrix cores as hi + lo bf16 pairs
-// (|x - hi - lo| <= 2^-18 |x|); bf16 x bf16 products are exact and every sum
-// is fp32, so the result tracks an fp32 computation.
+// Precision: fp32 operands enter the bf16 matrix cores as hi + lo bf16 pairs,
+// each rounded to nearest (bf16 keeps 8 significant bits, so |x - hi| <= 2^-8 |x|
+// and |x - hi - lo| <= 2^-16 |x|); bf16 x bf16 products are exact and every
+// sum is fp32, so the result tracks an fp32 computation to ~1e-5.
 //
 // Streaming: a 16-token tile of Q, K, V is 3 x 2 KB contiguous.  Each step
 // loads the tile PF steps ahead into registers (coalesced 16-byte loads),
@@ -48,8 +52,9 @@ namespace {
 
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef short short4v __attribute__((__vector_size__(4 * sizeof(short))));
 typedef float float4v __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 64;       // head dim
 constexpr int BT = 16;      // mini-batch (tokens)
@@ -69,30 +74,61 @@ static_assert(sizeof(Slot) % 16 == 0, "slot size");
 __device__ __forceinline__ float4v mfma32(bf16x8 a, bf16x8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float4v mfma16(bf16x4 a, bf16x4 b, float4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
-                                                   __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float float2v __attribute__((__vector_size__(2 * sizeof(float))));
+
+// Two fp32 values -> packed bf16 hi pair and lo pair, x ~= hi + lo.  One
+// v_cvt_pk_bf16_f32 rounds both hi values (nearest even); they are widened back
+// with a shift and a mask, and the exact residuals are rounded into lo.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector(float2v{x0, x1}, bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float h0 = __uint_as_float(hi << 16);
+  const float h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{x0 - h0, x1 - h1}, bf16x2));
 }
 
 __device__ __forceinline__ void split4(const float x[4], bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const __bf16 h = static_cast<__bf16>(x[j]);
-    hi[j] = h;
-    lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-  }
+  uint32_t h[2], l[2];
+  split2(x[0], x[1], h[0], l[0]);
+  split2(x[2], x[3], h[1], l[1]);
+  hi = __builtin_bit_cast(bf16x4, h);
+  lo = __builtin_bit_cast(bf16x4, l);
 }
 
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+#ifndef TTT_LINEAR_NT
+#define TTT_LINEAR_NT 1
+#endif
+// Q/K/V and Z are touched exactly once: mark them as streaming (non-temporal)
+// so they do not evict each other from the caches (about 15% at the 1.3B shape).
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+  if constexpr (TTT_LINEAR_NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T x) {
+  if constexpr (TTT_LINEAR_NT) {
+    __builtin_nontemporal_store(x, p);
+  } else {
+    *p = x;
+  }
+}
+
 template <typename OutT>
 __device__ __forceinline__ void store_z(OutT* p, float x);
 template <>
-__device__ __forceinline__ void store_z<float>(float* p, float x) { *p = x; }
+__device__ __forceinline__ void store_z<float>(float* p, float x) { st_stream(p, x); }
 template <>
-__device__ __forceinline__ void store_z<uint16_t>(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
+__device__ __forceinline__ void store_z<uint16_t>(uint16_t* p, float x) { st_stream(p, f32_to_bf16_bits(x)); }
 
 template <int PF, bool ETA_TOKEN, typename OutT>
 __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a) {
@@ -110,9 +146,9 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   const int nb = a.T / BT;
 
   const size_t tok0 = static_cast<size_t>(chain) * a.T;
-  const uint4* Qg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + tok0 * D);
-  const uint4* Kg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.K) + tok0 * D);
-  const uint4* Vg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + tok0 * D);
+  const u32x4* Qg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.Q) + tok0 * D);
+  const u32x4* Kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.K) + tok0 * D);
+  const u32x4* Vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.V) + tok0 * D);
   OutT* Zg = static_cast<OutT*>(a.Z) + tok0 * D;
   const float* eg = a.eta + bi * a.esb + h * a.esh;
 
@@ -120,30 +156,30 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   //   16 B of Q (tid < 128) or K (tid >= 128): row srow, columns scol..scol+7
   //   8 B of V: row vrow, columns vcol..vcol+3;  eta of token (tid & 15)
   const int within = tid & 127;
-  const uint4* srcA = (tid < 128 ? Qg : Kg) + within;
-  const uint2* srcB = reinterpret_cast<const uint2*>(Vg) + tid;
+  const u32x4* srcA = (tid < 128 ? Qg : Kg) + within;
+  const u32x2* srcB = reinterpret_cast<const u32x2*>(Vg) + tid;
   const int srow = within >> 3;
   const int scol = (within & 7) * 8;
   const int vrow = tid >> 4;
   const int vcol = (tid & 15) * 4;
   const float* srcE = eg + static_cast<int64_t>(tid & 15) * a.est;
 
-  uint4 ra[PF];
-  uint2 rb[PF];
+  u32x4 ra[PF];
+  u32x2 rb[PF];
   float re[PF];
 
-  auto load_step = [&](int n, uint4& xa, uint2& xb, float& xe) {
-    xa = srcA[static_cast<size_t>(n) * (BT * D / 8)];  // 128 uint4 per tile
-    xb = srcB[static_cast<size_t>(n) * (BT * D / 4)];  // 256 uint2 per tile
+  auto load_step = [&](int n, u32x4& xa, u32x2& xb, float& xe) {
+    xa = ld_stream(srcA + static_cast<size_t>(n) * (BT * D / 8));  // 128 uint4 per tile
+    xb = ld_stream(srcB + static_cast<size_t>(n) * (BT * D / 4));  // 256 uint2 per tile
     xe = ETA_TOKEN ? srcE[static_cast<int64_t>(n) * BT * a.est] : 0.f;
   };
-  auto stage = [&](int slot, const uint4& xa, const uint2& xb, float xe) {
+  auto stage = [&](int slot, const u32x4& xa, const u32x2& xb, float xe) {
     Slot& S = slots[slot];
-    *reinterpret_cast<uint2*>(&S.v[vrow * ROW + vcol]) = xb;
+    *reinterpret_cast<u32x2*>(&S.v[vrow * ROW + vcol]) = xb;
     if (tid < 128) {
-      *reinterpret_cast<uint4*>(&S.q[srow * ROW + scol]) = xa;
+      *reinterpret_cast<u32x4*>(&S.q[srow * ROW + scol]) = xa;
     } else {
-      *reinterpret_cast<uint4*>(&S.k[srow * ROW + scol]) = xa;
+      *reinterpret_cast<u32x4*>(&S.k[srow * ROW + scol]) = xa;
       const uint32_t wv[4] = {xa.x, xa.y, xa.z, xa.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -187,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // min(n+PF, nb-1) into ring slot j, compute step n, barrier.  The prefetch
   // index is clamped instead of guarded so every step issues the same memory
   // operations and the compiler's wait counts stay exact.
-  auto step = [&](const int n, uint4& xa, uint2& xb, float& xe, const uint4& ya, const uint2& yb,
+  auto step = [&](const int n, u32x4& xa, u32x2& xb, float& xe, const u32x4& ya, const u32x2& yb,
                   const float ye) {
     stage((n + 1) & 1, ya, yb, ye);
     load_step(min(n + PF, nb - 1), xa, xb, xe);
@@ -232,29 +268,30 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     for (int r = 0; r < 4; ++r)
       e[r] = pk[r] - bf16_bits_to_f32(S.v[(4 * g + r) * ROW + 16 * w + li]);
 
-    // ---- Z = P_Q - L E, L[t][s] = 2 eta_s S[s][t] (s <= t) ----
-    float lv[4], bv[4];
+    // ---- Z = P_Q + M G, with M[t][s] = S[s][t] [s <= t] (causal mask, diagonal
+    // included) and G[s][i] = -2 eta_s E^T[s][i], the operand the update uses too ----
+    float mv[4], gv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int s = 4 * g + r;
-      lv[r] = (s <= li) ? -2.f * et[r] * sc[r] : 0.f;
-      bv[r] = -2.f * et[r] * e[r];
+      mv[r] = (4 * g + r <= li) ? sc[r] : 0.f;
+      gv[r] = -2.f * et[r] * e[r];
     }
-    bf16x4 lhi, llo, ehi, elo, bhi, blo;
-    split4(lv, lhi, llo);
-    split4(e, ehi, elo);
-    split4(bv, bhi, blo);
+    bf16x4 mhi, mlo, bhi, blo;
+    split4(mv, mhi, mlo);
+    split4(gv, bhi, blo);
+    // The 16x16x32 MFMA sums 8 k-slots per lane group; a 16-token contraction
+    // uses slots 0-3 and 4-7 for two passes at once: [hi, hi] x [hi, lo].
+    const bf16x4 zero4 = {};
     float4v z = pq;
-    z = mfma16(lhi, ehi, z);
-    z = mfma16(lhi, elo, z);
-    z = mfma16(llo, ehi, z);
+    z = mfma32(cat(mhi, mhi), cat(bhi, blo), z);
+    z = mfma32(cat(mlo, zero4), cat(bhi, zero4), z);
 
-    // ---- W^T[c][i] += sum_s K[s][c] (-2 eta_s E[i][s]) ----
+    // ---- W^T[c][i] += sum_s K[s][c] G[s][i] ----
+    const bf16x8 gb = cat(bhi, blo);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bf16x4 kt = *reinterpret_cast<const bf16x4*>(&S.kt[(16 * t + li) * KTROW + 4 * g]);
-      wt[t] = mfma16(kt, bhi, wt[t]);
-      wt[t] = mfma16(kt, blo, wt[t]);
+      wt[t] = mfma32(cat(kt, kt), gb, wt[t]);
     }
 
     // ---- store Z rows t = 4g + r, columns 16w + li ----
@@ -285,7 +322,10 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     *reinterpret_cast<float4*>(wf + 16 * t) = make_float4(wt[t][0], wt[t][1], wt[t][2], wt[t][3]);
 }
 
-constexpr int kPF = 4;
+#ifndef TTT_LINEAR_PF
+#define TTT_LINEAR_PF 8
+#endif
+constexpr int kPF = TTT_LINEAR_PF;  // prefetch distance (mini-batches in flight per thread)
 
 template <bool TOK>
 hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {

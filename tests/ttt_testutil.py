@@ -6,36 +6,8 @@ import numpy as np
 import ttt_inputs as ti
 
 
-def to_device(inp: ti.Inputs, device="cuda:0", dtype=None):
-    """Q, K, V, W1 (and W2), eta of a full-chain Inputs as device tensors.
-
-    Returns dict(q, k, v, w1, w2, eta) with Q/K/V shaped [B, H, T, d] in the
-    config's storage dtype (the exact bits the oracle reads).
-    """
-    import torch
-
-    cfg = inp.cfg
-    assert len(inp.chains) == cfg.chains and np.all(inp.chains == np.arange(cfg.chains))
-    shape = (cfg.B, cfg.H, cfg.T, cfg.d)
-    dtype = dtype or cfg.dtype
-
-    def qkv(x):
-        if dtype == "bf16":
-            bits = ti.bf16_round(x)[1]
-            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).reshape(shape).to(device)
-        return torch.from_numpy(np.ascontiguousarray(x)).reshape(shape).to(device)
-
-    out = dict(q=qkv(inp.q), k=qkv(inp.k), v=qkv(inp.v),
-               w1=torch.from_numpy(inp.w1).to(device),
-               w2=None if inp.w2 is None else torch.from_numpy(inp.w2).to(device))
-    sb, sh, st = inp.eta_strides
-    if (sb, sh, st) == (0, 0, 0):
-        out["eta"] = torch.from_numpy(inp.eta_buf[:1].copy()).to(device)
-    elif (sb, sh, st) == (0, 1, 0):
-        out["eta"] = torch.from_numpy(inp.eta_buf.copy()).to(device)
-    else:
-        out["eta"] = torch.from_numpy(inp.eta_buf.reshape(cfg.B, cfg.H, cfg.T).copy()).to(device)
-    return out
+def to_device(inp, device="cuda:0", dtype=None):
+    return ti.to_device(inp, device, dtype)
 
 
 def rows(t, chains=None):

@@ -196,3 +196,35 @@ def sample_chains(cfg: Config, count: int, seed: int = 7) -> np.ndarray:
     pick = set(rng.choice(n, size=max(count - 2, 0), replace=False).tolist())
     pick.update({0, n - 1})
     return np.array(sorted(pick), dtype=np.int64)
+
+
+def to_device(inp: Inputs, device="cuda:0", dtype: Optional[str] = None) -> dict:
+    """Upload a full-chain Inputs: dict(q, k, v, w1, w2, eta) of torch tensors.
+
+    Q, K, V are [B, H, T, d] in the storage dtype (the exact bits the oracle
+    reads); eta is shaped to match its strides: [1], [H] or [B, H, T].
+    """
+    import torch
+
+    cfg = inp.cfg
+    assert len(inp.chains) == cfg.chains and np.all(inp.chains == np.arange(cfg.chains))
+    shape = (cfg.B, cfg.H, cfg.T, cfg.d)
+    dtype = dtype or cfg.dtype
+
+    def qkv(x):
+        if dtype == "bf16":
+            bits = bf16_round(x)[1]
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).reshape(shape).to(device)
+        return torch.from_numpy(np.ascontiguousarray(x)).reshape(shape).to(device)
+
+    out = dict(q=qkv(inp.q), k=qkv(inp.k), v=qkv(inp.v),
+               w1=torch.from_numpy(inp.w1).to(device),
+               w2=None if inp.w2 is None else torch.from_numpy(inp.w2).to(device))
+    strides = tuple(inp.eta_strides)
+    if strides == (0, 0, 0):
+        out["eta"] = torch.from_numpy(inp.eta_buf[:1].copy()).to(device)
+    elif strides == (0, 1, 0):
+        out["eta"] = torch.from_numpy(inp.eta_buf.copy()).to(device)
+    else:
+        out["eta"] = torch.from_numpy(inp.eta_buf.reshape(cfg.B, cfg.H, cfg.T).copy()).to(device)
+    return out
