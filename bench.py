@@ -11,7 +11,6 @@ event timing) and the fp64 CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,6 +29,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # fp32 matrix
 PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30           # size of the calibration copy (read and written once each)
 
 
 def log(*a):
@@ -62,15 +62,6 @@ def algorithmic(cfg: ti.Config, eta_strides):
     return bytes_, flops
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "test_sequence_layer_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when the summary is missing or was taken on a different kernel source."""
@@ -79,8 +70,10 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as fh:
         db = json.load(fh)
+    from test_sequence_layer_amd.profiling import source_hash
+
     rec = db.get(f"{kernel}|{workload}")
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -110,6 +103,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-chains", type=int, default=128)
     ap.add_argument("--generic", action="store_true", help="time the portable fp32 kernel instead")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) so profiler "
+                         "HBM counters can be scaled to bytes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -177,6 +173,15 @@ def main():
             "frac_of_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
     log(f"bench: {kname}: {kernel_ms:.3f} ms/launch, {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM), "
         f"{tflops:.1f} TFLOP/s algorithmic")
+
+    if args.copy_calibration:
+        n = COPY_BYTES // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

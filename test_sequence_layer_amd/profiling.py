@@ -1,0 +1,136 @@
+"""Summarise rocprofv3 output for one kernel into profiles/.
+
+Given the CSV directories of three rocprofv3 runs of the same benchmark command
+(kernel trace with --stats, then --pmc FETCH_SIZE, then --pmc WRITE_SIZE), each
+run also executing a plain device copy of known size (bench.py
+--copy-calibration: 1 GiB read + 1 GiB written), this writes
+
+  profiles/<kernel>__<workload>.md   average launch time, HBM bytes per launch
+  profiles/traffic.json              bytes per launch, keyed by kernel|workload,
+                                     with a hash of the kernel's source files so
+                                     a stale figure is never reported.
+
+The HBM byte counters are scaled by what they read for the copy kernel:
+factor = known bytes / counter bytes (per counter).
+
+    python -m test_sequence_layer_amd.profiling --stats D1 --fetch D2 --write D3 \
+        --kernel ttt_linear_mfma_d64b16 --workload l1p3b --algorithmic-bytes N \
+        --command "..."
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+# source files that define each kernel (a change to any of them invalidates its counters)
+KERNEL_SOURCES = {
+    "ttt_linear_mfma_d64b16": ["linear_mfma.hip", "ttt_internal.h"],
+    "ttt_linear_generic_kernel": ["linear_generic.hip", "ttt_internal.h"],
+    "ttt_mlp_fwd_d64h256b16": ["mlp.hip", "ttt_internal.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel.split("<")[0], []):
+        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _one(d: str, pattern: str) -> str:
+    files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if len(files) != 1:
+        raise FileNotFoundError(f"expected one {pattern} under {d}, found {files}")
+    return files[0]
+
+
+def kernel_stats(stats_dir: str, kernel: str):
+    """(calls, average ns, min ns) of the kernel from *_kernel_stats.csv."""
+    for r in csv.DictReader(open(_one(stats_dir, "*_kernel_stats.csv"))):
+        if kernel in r["Name"]:
+            return int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), r["Name"]
+    raise KeyError(kernel)
+
+
+def counter_kib(pmc_dir: str, name_substr: str, counter: str):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(_one(pmc_dir, "*_counter_collection.csv")))
+            if name_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise KeyError((name_substr, counter))
+    return vals
+
+
+def summarize(stats_dir, fetch_dir, write_dir, kernel, workload, algorithmic_bytes, command, out_dir=PROFILES):
+    calls, avg_ns, min_ns, full_name = kernel_stats(stats_dir, kernel)
+    fetch = counter_kib(fetch_dir, kernel, "FETCH_SIZE")
+    write = counter_kib(write_dir, kernel, "WRITE_SIZE")
+    cf = counter_kib(fetch_dir, COPY_KERNEL, "FETCH_SIZE")
+    cw = counter_kib(write_dir, COPY_KERNEL, "WRITE_SIZE")
+    f_fetch = COPY_BYTES / (statistics.median(cf) * 1024)
+    f_write = COPY_BYTES / (statistics.median(cw) * 1024)
+    rd = statistics.median(fetch) * 1024 * f_fetch
+    wr = statistics.median(write) * 1024 * f_write
+    total = rd + wr
+    os.makedirs(out_dir, exist_ok=True)
+    base = f"{kernel}__{workload}"
+    md = os.path.join(out_dir, base + ".md")
+    with open(md, "w") as fh:
+        fh.write(f"# {kernel} -- {workload}\n\n")
+        fh.write(f"Kernel symbol: `{full_name}`\n\n")
+        fh.write("Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root):\n\n")
+        for c in command:
+            fh.write(f"    {c}\n")
+        fh.write("\n| quantity | value |\n|---|---|\n")
+        fh.write(f"| launches traced | {calls} |\n")
+        fh.write(f"| average launch duration | {avg_ns / 1e3:.1f} us |\n")
+        fh.write(f"| fastest launch | {min_ns / 1e3:.1f} us |\n")
+        fh.write(f"| FETCH_SIZE per launch (median, raw) | {statistics.median(fetch):.0f} KiB |\n")
+        fh.write(f"| WRITE_SIZE per launch (median, raw) | {statistics.median(write):.0f} KiB |\n")
+        fh.write(f"| copy calibration (1 GiB copy) FETCH / WRITE raw | "
+                 f"{statistics.median(cf):.0f} / {statistics.median(cw):.0f} KiB |\n")
+        fh.write(f"| scale factors FETCH / WRITE | {f_fetch:.4f} / {f_write:.4f} |\n")
+        fh.write(f"| HBM bytes read per launch | {rd:.4e} |\n")
+        fh.write(f"| HBM bytes written per launch | {wr:.4e} |\n")
+        fh.write(f"| HBM traffic per launch | {total:.4e} B |\n")
+        fh.write(f"| algorithmic bytes per launch | {algorithmic_bytes:.4e} B |\n")
+        fh.write(f"| traffic / algorithmic | {total / algorithmic_bytes:.4f} |\n")
+        fh.write(f"| achieved (algorithmic bytes / average duration) | "
+                 f"{algorithmic_bytes / avg_ns:.1f} GB/s |\n")
+        fh.write(f"| kernel source hash | {source_hash(kernel)} |\n")
+    tj = os.path.join(out_dir, "traffic.json")
+    db = json.load(open(tj)) if os.path.exists(tj) else {}
+    db[f"{kernel}|{workload}"] = {"bytes_per_launch": round(total), "read": round(rd), "write": round(wr),
+                                  "avg_launch_us": round(avg_ns / 1e3, 2),
+                                  "source_hash": source_hash(kernel)}
+    with open(tj, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+    return md
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--algorithmic-bytes", type=float, required=True)
+    ap.add_argument("--command", action="append", default=[])
+    a = ap.parse_args()
+    print(summarize(a.stats, a.fetch, a.write, a.kernel, a.workload, a.algorithmic_bytes, a.command))
+
+
+if __name__ == "__main__":
+    main()
