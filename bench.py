@@ -42,7 +42,10 @@ def algorithmic(cfg: ti.Config, eta_strides):
     Bytes: read Q, K, V once (bf16 or fp32), write Z once (fp32), read eta
     (per token: 4 B per token-head; otherwise negligible), read W0, write W_final.
     Flops per token-head: TTT-Linear 6 d^2 + 4 d b (W K, W Q, the b x b scores
-    and their product with E, and the rank-b state update); TTT-MLP: see DESIGN.
+    and their product with E, and the rank-b state update).  TTT-MLP per
+    mini-batch: seven d x dh x b products (W1 K, W1 Q, W2 A_K, W2^T E, W2 A_Q
+    and the two rank-b updates), two b x b x d ones (K^T Q and E L2) and two
+    b x b x dh ones (D L1 and A_K^T A_Q), at 2 flops per multiply-add.
     """
     th = cfg.B * cfg.H * cfg.T
     in_sz = 2 if cfg.dtype == "bf16" else 4
@@ -164,10 +167,17 @@ def main():
     bytes_, flops = algorithmic(cfg, inp.eta_strides)
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
     traffic = measured_traffic(kname, cfg.name)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "algorithmic_bytes": bytes_, "kernel": kname, "kernel_ms": round(kernel_ms, 4)}
     tflops = flops / (kernel_ms / 1e3) / 1e12
+    # the binding roofline: bytes / 8 TB/s vs flops / 2.5 PF/s (bf16 MFMA, which every
+    # contraction runs on); TTT-Linear is HBM-bound, TTT-MLP MFMA-bound
+    if bytes_ / HBM_PEAK_GBS >= flops / BF16_PEAK_TFLOPS / 1e3:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof.update({"algorithmic_bytes": bytes_, "algorithmic_flops": flops, "achieved_gbs": round(achieved, 1),
+                 "kernel": kname, "kernel_ms": round(kernel_ms, 4)})
     mfma = {"algorithmic_flops": flops, "achieved_tflops": round(tflops, 2),
             "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
             "frac_of_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
