@@ -100,11 +100,13 @@ def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU clock settles only after ~50 back-to-back launches (~30 ms at the
+    # 1.3B shape: the first launches run up to 40% slower), so warm up with 100.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="l1p3b", choices=sorted(ti.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-chains", type=int, default=128)
+    ap.add_argument("--cpu-sample-chains", type=int, default=512)
     ap.add_argument("--generic", action="store_true", help="time the portable fp32 kernel instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) so profiler "

@@ -43,8 +43,9 @@
 //
 // Streaming: a 16-token tile of Q, K, V is 3 x 2 KB contiguous.  Each step
 // loads the tile PF steps ahead into registers (coalesced 16-byte loads),
-// stores the tile one step ahead into a double-buffered LDS slot (plus a
-// transposed copy of K for the update's A operand), and issues one barrier.
+// stores the tile one step ahead into a double-buffered LDS slot, and issues
+// one barrier.  The update's K^T operand and E's V values are column reads of
+// the row-major tiles with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -59,20 +60,32 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = 64;       // head dim
 constexpr int BT = 16;      // mini-batch (tokens)
 constexpr int ROW = 72;     // padded LDS row of a token tile (bf16 elements, 144 B)
-constexpr int KTROW = 20;   // padded LDS row of the transposed K tile (bf16, 40 B)
 constexpr int kThreads = 256;
 
 struct __align__(16) Slot {
   uint16_t q[BT * ROW];
   uint16_t k[BT * ROW];
   uint16_t v[BT * ROW];
-  uint16_t kt[D * KTROW];
   float eta[BT];
 };
 static_assert(sizeof(Slot) % 16 == 0, "slot size");
 
 __device__ __forceinline__ float4v mfma32(bf16x8 a, bf16x8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef short short4v __attribute__((__vector_size__(4 * sizeof(short))));
+
+// Column read of a row-major bf16 tile (row stride ROW): lane l gets
+// X[row0 + 4(l/16) + r][col0 + l%16] for r = 0..3.  ds_read_b64_tr_b16 works on
+// blocks of 16 lanes: output lane i receives element r from the 8-byte chunk
+// addressed by lane 4r + i/4 of its block, position i%4; so lane j of block g
+// addresses row row0 + 4g + j/4, columns col0 + 4(j%4) .. +3.
+__device__ __forceinline__ bf16x4 read_cols(const uint16_t* tile, int row0, int col0, int li, int g) {
+  const uint16_t* p = tile + (row0 + 4 * g + (li >> 2)) * ROW + col0 + 4 * (li & 3);
+  typedef short4v __attribute__((address_space(3))) * lds_short4v_ptr;
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_ptr)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
@@ -176,17 +189,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   auto stage = [&](int slot, const u32x4& xa, const u32x2& xb, float xe) {
     Slot& S = slots[slot];
     *reinterpret_cast<u32x2*>(&S.v[vrow * ROW + vcol]) = xb;
-    if (tid < 128) {
-      *reinterpret_cast<u32x4*>(&S.q[srow * ROW + scol]) = xa;
-    } else {
-      *reinterpret_cast<u32x4*>(&S.k[srow * ROW + scol]) = xa;
-      const uint32_t wv[4] = {xa.x, xa.y, xa.z, xa.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        S.kt[(scol + 2 * j) * KTROW + srow] = static_cast<uint16_t>(wv[j] & 0xffffu);
-        S.kt[(scol + 2 * j + 1) * KTROW + srow] = static_cast<uint16_t>(wv[j] >> 16);
-      }
-    }
+    *reinterpret_cast<u32x4*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
     if (ETA_TOKEN && tid < BT) S.eta[tid] = xe;
   };
 
@@ -264,9 +267,11 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 
     // ---- E^T[t = 4g+r][i = 16w+li] = P_K - V ----
     float e[4];
+    {
+      const bf16x4 vc = read_cols(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      e[r] = pk[r] - bf16_bits_to_f32(S.v[(4 * g + r) * ROW + 16 * w + li]);
+      for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
+    }
 
     // ---- Z = P_Q + M G, with M[t][s] = S[s][t] [s <= t] (causal mask, diagonal
     // included) and G[s][i] = -2 eta_s E^T[s][i], the operand the update uses too ----
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     const bf16x8 gb = cat(bhi, blo);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x4 kt = *reinterpret_cast<const bf16x4*>(&S.kt[(16 * t + li) * KTROW + 4 * g]);
+      const bf16x4 kt = read_cols(S.k, 0, 16 * t, li, g);  // K[4g + r][16t + li]
       wt[t] = mfma32(cat(kt, kt), gb, wt[t]);
     }
 
