@@ -108,6 +108,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-chains", type=int, default=512)
     ap.add_argument("--generic", action="store_true", help="time the portable fp32 kernel instead")
+    ap.add_argument("--primal", action="store_true",
+                    help="time the primal (token-by-token) form instead of the dual form")
+    ap.add_argument("--decode", action="store_true",
+                    help="time decoding: one token per call for every sequence, state carried in place")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) so profiler "
                          "HBM counters can be scaled to bytes")
@@ -138,14 +142,30 @@ def main():
 
         def step():
             ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1, w2_final=f2)
+    elif args.decode:
+        # one call = one new token for all B*H sequences (T=1), positions advancing
+        kname = ttt.linear_kernel_name(B, H, 1, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0, (0, 0, 0),
+                                       primal=True)
+        w = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
+        wb = w.clone()
+        zt = torch.empty((B, H, 1, d), dtype=torch.float32, device="cuda:0")
+        tok = [(t["q"][:, :, i:i + 1].contiguous(), t["k"][:, :, i:i + 1].contiguous(),
+                t["v"][:, :, i:i + 1].contiguous(),
+                t["eta"][:, :, i:i + 1].contiguous() if t["eta"].dim() == 3 else t["eta"]) for i in range(64)]
+        pos = [0]
+
+        def step():
+            q1, k1, v1, e1 = tok[pos[0] % 64]
+            ttt.linear_decode(q1, k1, v1, e1, w, wb, pos[0], cfg.b, z=zt)
+            pos[0] += 1
     else:
         wf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda:0")
         kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
-                                       inp.eta_strides, args.generic)
+                                       inp.eta_strides, args.generic, args.primal)
 
         def step():
             ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf,
-                           generic=args.generic)
+                           generic=args.generic, primal=args.primal)
     log(f"bench: kernel {kname}")
 
     for _ in range(args.warmup):
@@ -163,10 +183,14 @@ def main():
     wall = time.perf_counter() - w0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps      # one launch per step
     ms_per_step = max(wall * 1e3 / args.steps, kernel_ms)
-    tokens = B * T
+    tokens = B * (1 if args.decode else T)
     value = tokens / (ms_per_step / 1e3)
 
     bytes_, flops = algorithmic(cfg, inp.eta_strides)
+    if args.decode:
+        # per call: read every state twice (W and Wb) and write them, one token of Q/K/V in, Z out
+        bytes_ = B * H * (4 * d * d * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
+        flops = B * H * 6 * d * d
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
     traffic = measured_traffic(kname, cfg.name)
     tflops = flops / (kernel_ms / 1e3) / 1e12
@@ -186,6 +210,10 @@ def main():
     log(f"bench: {kname}: {kernel_ms:.3f} ms/launch, {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM), "
         f"{tflops:.1f} TFLOP/s algorithmic")
 
+    if args.decode or args.primal:
+        roof["note"] = ("decode: one token per call, latency-bound" if args.decode
+                        else "primal (token-by-token) form: the baseline the dual form replaces")
+
     if args.copy_calibration:
         n = COPY_BYTES // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -196,15 +224,17 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.decode:
         log("bench: timing the fp64 oracle on a sample ...")
         cpu = cpu_baseline(cfg, inp, args.cpu_sample_chains)
         log(f"bench: cpu baseline {cpu['value']:.3e} tokens/s ({cpu['sample']})")
 
     eta_desc = {(0, 0, 0): "scalar", (0, 1, 0): "per head"}.get(tuple(inp.eta_strides), "per token")
     model = "TTT-MLP" if cfg.is_mlp else "TTT-Linear"
+    form = "decode" if args.decode else ("primal" if args.primal else ("generic" if args.generic else ""))
+    headline = cfg.name == "l1p3b" and not form
     rec = {
-        "metric": METRIC if cfg.name == "l1p3b" else f"{model} fwd tokens/sec ({cfg.name})",
+        "metric": METRIC if headline else f"{model} {form + ' ' if form else ''}fwd tokens/sec ({cfg.name})",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,

@@ -60,13 +60,16 @@ typedef enum {
   TTT_ERR_ALIGN = 6,       /* a pointer is not aligned as required               */
   TTT_ERR_HIP = 7,         /* the HIP runtime rejected the launch                */
   TTT_ERR_STRIDE = 8,      /* negative eta stride, or w0 stride not 0 / H*d*d    */
-  TTT_ERR_FLAGS = 9        /* unknown bit set in flags                           */
+  TTT_ERR_FLAGS = 9,       /* unknown bit set in flags                           */
+  TTT_ERR_POS = 10         /* negative decode position                           */
 } ttt_status;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
 
 /* flags */
-#define TTT_FLAG_GENERIC 1u /* force the portable fp32 kernel (testing / cross-check) */
+#define TTT_FLAG_GENERIC 1u /* force the portable fp32 kernel (testing / cross-check)          */
+#define TTT_FLAG_PRIMAL 2u  /* compute token by token (primal form, [TTT] 03 §7's naive form):  */
+                            /* the same result, no dual form; d in {16, 32, 64}, any b          */
 
 /* TTT-Linear problem description. */
 typedef struct {
@@ -85,15 +88,38 @@ typedef struct {
  *   eta     : fp32, strided as above      Z  : [B,H,T,d] of out_dtype
  *   W_final : [B,H,d,d] fp32, the state after the last token.
  * Supported: d in {16, 32, 64}, fp32 or bf16 inputs, b <= 64 (b <= 32 for
- * d = 64); d = 64, b = 16, bf16 inputs run the MFMA kernel.  B*H == 0 or
- * T == 0 is valid (T == 0 copies W0 to W_final; Q/K/V/Z may then be NULL).
+ * d = 64); d = 64, b = 16, bf16 inputs run the MFMA kernel; with
+ * TTT_FLAG_PRIMAL any b >= 1.  B*H == 0 or T == 0 is valid (T == 0 copies W0
+ * to W_final; Q/K/V/Z may then be NULL).
  */
 ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                           const float* W0, const float* eta, void* Z, float* W_final, void* stream);
 
+/*
+ * TTT-Linear decode ([TTT] 04 §3: generation is sequential and uses the primal
+ * form).  Continues B*H sequences by desc->T new tokens (often 1), all at
+ * absolute positions pos, pos+1, ..., carrying the state in place:
+ *   W  : [B,H,d,d] fp32, the state after the pos tokens seen so far (read, then
+ *        overwritten with the state after the new tokens)
+ *   Wb : [B,H,d,d] fp32, the state at the start of the current mini-batch (read
+ *        and overwritten likewise).  A token at position p with p % b == 0
+ *        starts a mini-batch: Wb <- W before its gradient is taken.
+ *   Q, K, V, Z : [B,H,T,d]; eta strides index the new tokens (t = 0..T-1).
+ * desc->w0_batch_stride and desc->flags must be 0; T need not be a multiple of
+ * b.  Decoding T tokens from pos = 0 with W = Wb = W0 gives the same Z and W as
+ * ttt_linear_fwd (to rounding).  Supported: d in {16, 32, 64}, fp32/bf16 inputs.
+ */
+ttt_status ttt_linear_decode(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* eta, void* Z, float* W, float* Wb, int64_t pos, void* stream);
+
 /* Runs every host-side check of ttt_linear_fwd and launches nothing. */
 ttt_status ttt_linear_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                                const float* W0, const float* eta, const void* Z, const float* W_final);
+
+/* Runs every host-side check of ttt_linear_decode and launches nothing. */
+ttt_status ttt_linear_decode_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                      const float* eta, const void* Z, const float* W, const float* Wb,
+                                      int64_t pos);
 
 /* Name of the kernel ttt_linear_fwd would launch for desc, or NULL if unsupported. */
 const char* ttt_linear_kernel_name(const ttt_linear_desc* desc);

@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence, Tuple, Union
+from typing import Optional, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libttt.so")
@@ -25,15 +25,18 @@ LIB_PATH = os.path.join(_PKG, "libttt.so")
 TTT_OK = 0
 TTT_F32, TTT_BF16 = 0, 1
 TTT_FLAG_GENERIC = 1
+TTT_FLAG_PRIMAL = 2
 
 STATUS_NAMES = {
     0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE", 4: "TTT_ERR_UNSUPPORTED",
     5: "TTT_ERR_ALIAS", 6: "TTT_ERR_ALIGN", 7: "TTT_ERR_HIP", 8: "TTT_ERR_STRIDE", 9: "TTT_ERR_FLAGS",
+    10: "TTT_ERR_POS",
 }
 
 # Every symbol include/ttt.h declares.
 EXPORTS = (
     "ttt_linear_fwd", "ttt_linear_validate", "ttt_linear_kernel_name",
+    "ttt_linear_decode", "ttt_linear_decode_validate",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name",
     "ttt_status_str", "ttt_abi_version",
 )
@@ -83,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_fwd.restype = ctypes.c_int
     L.ttt_linear_validate.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, vp, fp]
     L.ttt_linear_validate.restype = ctypes.c_int
+    L.ttt_linear_decode.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, vp, fp, fp, ctypes.c_int64, vp]
+    L.ttt_linear_decode.restype = ctypes.c_int
+    L.ttt_linear_decode_validate.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, vp, fp, fp, ctypes.c_int64]
+    L.ttt_linear_decode_validate.restype = ctypes.c_int
     L.ttt_linear_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
     L.ttt_linear_kernel_name.restype = ctypes.c_char_p
     L.ttt_mlp_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp, vp]
@@ -168,7 +175,7 @@ def linear_desc(B, H, T, d, b, in_dtype, out_dtype, w0_batch_stride, eta_strides
 
 
 def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
-               generic: bool = False, stream=None) -> Tuple["object", "object"]:
+               generic: bool = False, primal: bool = False, stream=None) -> Tuple["object", "object"]:
     """TTT-Linear forward (dual form) on the GPU.
 
     q, k, v : [B, H, T, d] bfloat16 or float32 (same dtype), contiguous, on the GPU
@@ -177,6 +184,8 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
     b       : mini-batch size (T % b == 0)
     returns (Z [B, H, T, d] of out_dtype (default float32), W_final [B, H, d, d] float32).
     ``w_final`` may be ``w0`` itself (in-place carry) when w0 is [B, H, d, d].
+    ``generic`` forces the portable fp32 kernel; ``primal`` computes token by
+    token (the primal form) instead of with the dual form.
     """
     torch = _torch()
     B, H, T, d = q.shape
@@ -197,8 +206,8 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
     if w_final is None:
         w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
     _check_dev(q, k, v, w0, eta_t, z, w_final)
-    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est,
-                       TTT_FLAG_GENERIC if generic else 0)
+    flags = (TTT_FLAG_GENERIC if generic else 0) | (TTT_FLAG_PRIMAL if primal else 0)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, flags)
     st = lib().ttt_linear_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta_t),
                               _ptr(z), _ptr(w_final), _stream_handle(stream))
     if st != TTT_OK:
@@ -207,10 +216,40 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
 
 
 def linear_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),
-                       generic=False) -> Optional[str]:
-    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_GENERIC if generic else 0)
+                       generic=False, primal=False) -> Optional[str]:
+    flags = (TTT_FLAG_GENERIC if generic else 0) | (TTT_FLAG_PRIMAL if primal else 0)
+    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, flags)
     name = lib().ttt_linear_kernel_name(ctypes.byref(desc))
     return None if name is None else name.decode()
+
+
+def linear_decode(q, k, v, eta, w, wb, pos: int, b: int, out_dtype=None, z=None, stream=None):
+    """Continue B*H sequences by T new tokens (primal form), state carried in place.
+
+    q, k, v : [B, H, T, d];  w, wb : [B, H, d, d] float32 -- the state and the
+    mini-batch-start state after ``pos`` tokens, both updated in place.
+    eta     : float, [H] or [B, H, T] (indexed by the new tokens).
+    returns Z [B, H, T, d].
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    if tuple(w.shape) != (B, H, d, d) or tuple(wb.shape) != (B, H, d, d):
+        raise ValueError("w and wb must be [B, H, d, d]")
+    if w.dtype != torch.float32 or wb.dtype != torch.float32:
+        raise TypeError("w and wb must be float32")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    _check_dev(q, k, v, eta_t, z, w, wb)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), 0, est, 0)
+    st = lib().ttt_linear_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(z),
+                                 _ptr(w), _ptr(wb), int(pos), _stream_handle(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_decode")
+    return z
 
 
 # ---------------------------------------------------------------- TTT-MLP --

@@ -37,9 +37,10 @@ int64_t eta_extent(int64_t B, int64_t H, int64_t T, int64_t sb, int64_t sh, int6
   return (B - 1) * sb + (H - 1) * sh + (T - 1) * st + 1;
 }
 
-enum Kernel { K_NONE, K_GENERIC, K_MFMA };
+enum Kernel { K_NONE, K_GENERIC, K_MFMA, K_PRIMAL };
 
 Kernel pick_linear(const ttt::LinearArgs& a, uint32_t flags) {
+  if (flags & TTT_FLAG_PRIMAL) return ttt::linear_primal_supported(a.d) ? K_PRIMAL : K_NONE;
   if (flags & TTT_FLAG_GENERIC) return ttt::linear_generic_supported(a.d, a.b) ? K_GENERIC : K_NONE;
   if (ttt::linear_mfma_supported(a)) return K_MFMA;
   if (ttt::linear_generic_supported(a.d, a.b)) return K_GENERIC;
@@ -65,7 +66,8 @@ ttt_status validate_linear(const ttt_linear_desc* d, const void* Q, const void* 
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->b < 1) return TTT_ERR_SHAPE;
   if (d->T % d->b != 0) return TTT_ERR_SHAPE;
   if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
-  if (d->flags & ~static_cast<uint32_t>(TTT_FLAG_GENERIC)) return TTT_ERR_FLAGS;
+  if (d->flags & ~static_cast<uint32_t>(TTT_FLAG_GENERIC | TTT_FLAG_PRIMAL)) return TTT_ERR_FLAGS;
+  if ((d->flags & TTT_FLAG_GENERIC) && (d->flags & TTT_FLAG_PRIMAL)) return TTT_ERR_FLAGS;
   int64_t chains = 1, tok = 1, wel = 1;
   if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
   tok = chains;
@@ -110,6 +112,53 @@ ttt_status validate_linear(const ttt_linear_desc* d, const void* Q, const void* 
     if (!inplace) return TTT_ERR_ALIAS;
   }
   if (which) *which = k;
+  return TTT_OK;
+}
+
+ttt::PrimalArgs make_primal_args_fwd(const ttt_linear_desc* d, const void* Q, const void* K, const void* V,
+                                     const float* W0, const float* eta, void* Z, float* Wf) {
+  ttt::PrimalArgs a;
+  a.B = d->B; a.H = d->H; a.T = d->T; a.d = d->d; a.b = d->b;
+  a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype;
+  a.Q = Q; a.K = K; a.V = V;
+  a.W_in = W0; a.Wb_in = W0; a.w_in_bstride = d->w0_batch_stride;
+  a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
+  a.Z = Z; a.W_out = Wf; a.Wb_out = nullptr; a.pos = 0;
+  return a;
+}
+
+ttt_status validate_decode(const ttt_linear_desc* d, const void* Q, const void* K, const void* V, const float* eta,
+                           const void* Z, const float* W, const float* Wb, int64_t pos) {
+  if (!d) return TTT_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->b < 1) return TTT_ERR_SHAPE;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
+  if (d->flags != 0) return TTT_ERR_FLAGS;
+  if (pos < 0) return TTT_ERR_POS;
+  if (d->w0_batch_stride != 0) return TTT_ERR_STRIDE;
+  if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
+  int64_t chains = 1, tok = 1, wel = 1;
+  if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
+  tok = chains;
+  if (!mul_ok(tok, d->T) || !mul_ok(tok, d->d)) return TTT_ERR_SHAPE;
+  wel = chains;
+  if (!mul_ok(wel, d->d) || !mul_ok(wel, d->d)) return TTT_ERR_SHAPE;
+  if (!ttt::linear_primal_supported(d->d)) return TTT_ERR_UNSUPPORTED;
+  if (chains == 0) return TTT_OK;
+  if (!W || !Wb) return TTT_ERR_NULL;
+  if (tok > 0 && (!Q || !K || !V || !Z || !eta)) return TTT_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(Wb, 16)) return TTT_ERR_ALIGN;
+  if (tok > 0 && (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Z, 16) || !aligned(eta, 4)))
+    return TTT_ERR_ALIGN;
+  const int64_t in_b = tok * dtype_size(d->in_dtype);
+  const int64_t z_b = tok * dtype_size(d->out_dtype);
+  const int64_t w_b = wel * 4;
+  const int64_t eta_b =
+      tok > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const Range rq{Q, in_b}, rk{K, in_b}, rv{V, in_b}, re{eta, eta_b}, rz{Z, z_b}, rw{W, w_b}, rwb{Wb, w_b};
+  for (Range out : {rz, rw, rwb})
+    for (Range in : {rq, rk, rv, re})
+      if (overlaps(out, in)) return TTT_ERR_ALIAS;
+  if (overlaps(rz, rw) || overlaps(rz, rwb) || overlaps(rw, rwb)) return TTT_ERR_ALIAS;
   return TTT_OK;
 }
 
@@ -199,6 +248,7 @@ const char* ttt_status_str(int s) {
     case TTT_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case TTT_ERR_STRIDE: return "invalid stride";
     case TTT_ERR_FLAGS: return "unknown flag or non-zero reserved field";
+    case TTT_ERR_POS: return "negative decode position";
     default: return "unknown status";
   }
 }
@@ -214,6 +264,7 @@ const char* ttt_linear_kernel_name(const ttt_linear_desc* d) {
   switch (pick_linear(a, d->flags)) {
     case K_MFMA: return ttt::linear_mfma_name(a);
     case K_GENERIC: return ttt::linear_generic_name(a.d);
+    case K_PRIMAL: return ttt::linear_primal_name(a.d);
     default: return nullptr;
   }
 }
@@ -226,7 +277,35 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
   if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
   const ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = (k == K_MFMA) ? ttt::launch_linear_mfma(a, s) : ttt::launch_linear_generic(a, s);
+  hipError_t e;
+  if (k == K_MFMA)
+    e = ttt::launch_linear_mfma(a, s);
+  else if (k == K_PRIMAL)
+    e = ttt::launch_linear_primal(make_primal_args_fwd(desc, Q, K, V, W0, eta, Z, W_final), s);
+  else
+    e = ttt::launch_linear_generic(a, s);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_linear_decode_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                      const float* eta, const void* Z, const float* W, const float* Wb,
+                                      int64_t pos) {
+  return validate_decode(desc, Q, K, V, eta, Z, W, Wb, pos);
+}
+
+ttt_status ttt_linear_decode(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* eta, void* Z, float* W, float* Wb, int64_t pos, void* stream) {
+  const ttt_status st = validate_decode(desc, Q, K, V, eta, Z, W, Wb, pos);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  ttt::PrimalArgs a;
+  a.B = desc->B; a.H = desc->H; a.T = desc->T; a.d = desc->d; a.b = desc->b;
+  a.in_dtype = desc->in_dtype; a.out_dtype = desc->out_dtype;
+  a.Q = Q; a.K = K; a.V = V;
+  a.W_in = W; a.Wb_in = Wb; a.w_in_bstride = static_cast<int64_t>(desc->H) * desc->d * desc->d;
+  a.eta = eta; a.esb = desc->eta_stride_b; a.esh = desc->eta_stride_h; a.est = desc->eta_stride_t;
+  a.Z = Z; a.W_out = W; a.Wb_out = Wb; a.pos = pos;
+  const hipError_t e = ttt::launch_linear_primal(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

@@ -37,6 +37,27 @@ struct MlpArgs {
   float* W2f;
 };
 
+// Primal form (token by token): full forward and decode.
+struct PrimalArgs {
+  int B, H, T, d, b;
+  int in_dtype, out_dtype;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* W_in;   // state at position pos
+  const float* Wb_in;  // mini-batch-start state at position pos
+  int64_t w_in_bstride;
+  const float* eta;
+  int64_t esb, esh, est;
+  void* Z;
+  float* W_out;        // [B, H, d, d]
+  float* Wb_out;       // [B, H, d, d] or nullptr
+  int64_t pos;         // tokens already processed
+};
+bool linear_primal_supported(int d);
+const char* linear_primal_name(int d);
+hipError_t launch_linear_primal(const PrimalArgs& a, hipStream_t s);
+
 // Portable fp32 kernel (any supported d/b/dtype).
 bool linear_generic_supported(int d, int b);
 const char* linear_generic_name(int d);

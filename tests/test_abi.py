@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert ttt.abi_version() == 1
-    for s in range(10):
+    for s in range(11):
         assert ttt.status_str(s) and ttt.status_str(s) != "unknown status"
     assert ttt.status_str(99) == "unknown status"
 
@@ -159,3 +159,32 @@ def test_mlp_validation():
     assert _mval(_mdesc(), f1=4 * GB) == ALIAS
     assert _mval(_mdesc(wstride=4 * 64 * 256), f1=4 * GB, f2=5 * GB) == OK
     assert _mval(_mdesc(), f2=9 * GB + 8) == ALIGN
+
+
+# ---- decode validation -------------------------------------------------------------
+
+def _dval(desc, pos=0, **over):
+    p = dict(q=1 * GB, k=2 * GB, v=3 * GB, eta=5 * GB, z=6 * GB, w=7 * GB, wb=8 * GB)
+    p.update(over)
+    return ttt.lib().ttt_linear_decode_validate(ctypes.byref(desc), p["q"], p["k"], p["v"], p["eta"], p["z"],
+                                                p["w"], p["wb"], pos)
+
+
+def test_decode_validation():
+    POS = 10
+    assert _dval(_desc(T=1)) == OK
+    assert _dval(_desc(T=37)) == OK                # T need not be a multiple of b
+    assert _dval(_desc(T=1), pos=-1) == POS
+    assert _dval(_desc(T=1, flags=1)) == FLAGS
+    assert _dval(_desc(T=1, wstride=4 * 64 * 64)) == STRIDE
+    assert _dval(_desc(T=1, d=48)) == UNSUP
+    assert _dval(_desc(T=1), wb=7 * GB) == ALIAS   # W and Wb alias
+    assert _dval(_desc(T=1), w=1 * GB) == ALIAS    # W over Q
+    assert _dval(_desc(T=1), z=None) == NULL
+    assert _dval(_desc(T=0), q=None, k=None, v=None, z=None, eta=None) == OK
+
+
+def test_primal_flag():
+    assert _val(_desc(flags=2, b=7, T=63)) == OK   # any b with the primal form
+    assert _val(_desc(flags=3)) == FLAGS            # generic and primal together
+    assert ttt.linear_kernel_name(2, 4, 64, 64, 16, primal=True) == "ttt_linear_primal_kernel<64>"
