@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--generic", action="store_true", help="time the portable fp32 kernel instead")
     ap.add_argument("--primal", action="store_true",
                     help="time the primal (token-by-token) form instead of the dual form")
+    ap.add_argument("--chunks", type=int, default=1,
+                    help="split each sequence into this many chunks run in parallel (chunked forward)")
     ap.add_argument("--decode", action="store_true",
                     help="time decoding: one token per call for every sequence, state carried in place")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -163,9 +165,18 @@ def main():
         kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
                                        inp.eta_strides, args.generic, args.primal)
 
-        def step():
-            ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf,
-                           generic=args.generic, primal=args.primal)
+        if args.chunks > 1:
+            kname = "ttt_linear_mfma_d64b16"
+            ws = torch.empty(ttt.linear_chunked_workspace_bytes(B, H, T, d, cfg.b, args.chunks),
+                             dtype=torch.uint8, device="cuda:0")
+
+            def step():
+                ttt.linear_fwd_chunked(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, args.chunks,
+                                       workspace=ws, z=z, w_final=wf)
+        else:
+            def step():
+                ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf,
+                               generic=args.generic, primal=args.primal)
     log(f"bench: kernel {kname}")
 
     for _ in range(args.warmup):
@@ -181,7 +192,7 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps      # one launch per step
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps      # one call per step (the chunked form: 4 launches)
     ms_per_step = max(wall * 1e3 / args.steps, kernel_ms)
     tokens = B * (1 if args.decode else T)
     value = tokens / (ms_per_step / 1e3)
@@ -232,6 +243,9 @@ def main():
     eta_desc = {(0, 0, 0): "scalar", (0, 1, 0): "per head"}.get(tuple(inp.eta_strides), "per token")
     model = "TTT-MLP" if cfg.is_mlp else "TTT-Linear"
     form = "decode" if args.decode else ("primal" if args.primal else ("generic" if args.generic else ""))
+    if args.chunks > 1:
+        form = f"chunked({args.chunks})"
+        roof["note"] = "chunked forward: chunk maps + scan + parallel chunks (4 launches per call)"
     headline = cfg.name == "l1p3b" and not form
     rec = {
         "metric": METRIC if headline else f"{model} {form + ' ' if form else ''}fwd tokens/sec ({cfg.name})",

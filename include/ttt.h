@@ -61,7 +61,8 @@ typedef enum {
   TTT_ERR_HIP = 7,         /* the HIP runtime rejected the launch                */
   TTT_ERR_STRIDE = 8,      /* negative eta stride, or w0 stride not 0 / H*d*d    */
   TTT_ERR_FLAGS = 9,       /* unknown bit set in flags                           */
-  TTT_ERR_POS = 10         /* negative decode position                           */
+  TTT_ERR_POS = 10,        /* negative decode position                           */
+  TTT_ERR_WORKSPACE = 11   /* workspace missing, misaligned or too small         */
 } ttt_status;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
@@ -94,6 +95,27 @@ typedef struct {
  */
 ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                           const float* W0, const float* eta, void* Z, float* W_final, void* stream);
+
+/*
+ * TTT-Linear forward with the sequence split into nchunks chunks processed in
+ * parallel: the same result as ttt_linear_fwd (to rounding), for shapes with
+ * few (sequence, head) chains and long sequences.  Each mini-batch maps the
+ * state affinely (W -> W P_n + R_n, P_n = I - 2 K diag(eta) K^T,
+ * R_n = 2 V diag(eta) K^T; [TTT] 03 §7), so the library (1) composes the map of
+ * every chunk but the last in parallel, (2) scans them to get each chunk's
+ * start state, (3) runs every chunk's forward in parallel from its start state.
+ * Requires the MFMA path (d = 64, b = 16, bf16 inputs, flags = 0) and
+ * T % (16 * nchunks) == 0.  workspace: device memory of at least
+ * ttt_linear_chunked_workspace_bytes(desc, nchunks) bytes, 16-byte aligned,
+ * overlapping no argument; contents on return are unspecified.  nchunks = 1
+ * is ttt_linear_fwd (the workspace may then be NULL).
+ */
+ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K,
+                                  const void* V, const float* W0, const float* eta, void* Z, float* W_final,
+                                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes ttt_linear_fwd_chunked needs (0 for nchunks = 1; -1 if desc is NULL or nchunks < 1). */
+int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t nchunks);
 
 /*
  * TTT-Linear decode ([TTT] 04 §3: generation is sequential and uses the primal

@@ -30,13 +30,14 @@ TTT_FLAG_PRIMAL = 2
 STATUS_NAMES = {
     0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE", 4: "TTT_ERR_UNSUPPORTED",
     5: "TTT_ERR_ALIAS", 6: "TTT_ERR_ALIGN", 7: "TTT_ERR_HIP", 8: "TTT_ERR_STRIDE", 9: "TTT_ERR_FLAGS",
-    10: "TTT_ERR_POS",
+    10: "TTT_ERR_POS", 11: "TTT_ERR_WORKSPACE",
 }
 
 # Every symbol include/ttt.h declares.
 EXPORTS = (
     "ttt_linear_fwd", "ttt_linear_validate", "ttt_linear_kernel_name",
     "ttt_linear_decode", "ttt_linear_decode_validate",
+    "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name",
     "ttt_status_str", "ttt_abi_version",
 )
@@ -90,6 +91,11 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_decode.restype = ctypes.c_int
     L.ttt_linear_decode_validate.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, vp, fp, fp, ctypes.c_int64]
     L.ttt_linear_decode_validate.restype = ctypes.c_int
+    L.ttt_linear_fwd_chunked.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int32, vp, vp, vp, fp, fp, vp, fp,
+                                         vp, ctypes.c_int64, vp]
+    L.ttt_linear_fwd_chunked.restype = ctypes.c_int
+    L.ttt_linear_chunked_workspace_bytes.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int32]
+    L.ttt_linear_chunked_workspace_bytes.restype = ctypes.c_int64
     L.ttt_linear_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
     L.ttt_linear_kernel_name.restype = ctypes.c_char_p
     L.ttt_mlp_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp, vp]
@@ -221,6 +227,47 @@ def linear_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_
     desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, flags)
     name = lib().ttt_linear_kernel_name(ctypes.byref(desc))
     return None if name is None else name.decode()
+
+
+def linear_fwd_chunked(q, k, v, w0, eta, b: int, nchunks: int, workspace=None, out_dtype=None,
+                       w_final=None, z=None, stream=None):
+    """TTT-Linear forward with the sequence split into ``nchunks`` chunks run in parallel.
+
+    Same arguments and result as :func:`linear_fwd` (to rounding).  ``workspace``
+    is a uint8 device tensor of at least :func:`linear_chunked_workspace_bytes`
+    bytes; one is allocated when omitted.
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if tuple(w0.shape) == (H, d, d):
+        wstride = 0
+    elif tuple(w0.shape) == (B, H, d, d):
+        wstride = H * d * d
+    else:
+        raise ValueError(f"w0 shape {tuple(w0.shape)}: expected [H,d,d] or [B,H,d,d]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    if w_final is None:
+        w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, 0)
+    need = int(lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(desc), int(nchunks)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_dev(q, k, v, w0, eta_t, z, w_final, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ttt_linear_fwd_chunked(ctypes.byref(desc), int(nchunks), _ptr(q), _ptr(k), _ptr(v), _ptr(w0),
+                                      _ptr(eta_t), _ptr(z), _ptr(w_final), _ptr(workspace), wbytes,
+                                      _stream_handle(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_fwd_chunked")
+    return z, w_final
+
+
+def linear_chunked_workspace_bytes(B, H, T, d, b, nchunks) -> int:
+    desc = linear_desc(B, H, T, d, b, TTT_BF16, TTT_F32, 0, (0, 0, 0), 0)
+    return int(lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(desc), int(nchunks)))
 
 
 def linear_decode(q, k, v, eta, w, wb, pos: int, b: int, out_dtype=None, z=None, stream=None):

@@ -55,6 +55,7 @@ ttt::LinearArgs make_linear_args(const ttt_linear_desc* d, const void* Q, const 
   a.Q = Q; a.K = K; a.V = V; a.W0 = W0; a.w0_bstride = d->w0_batch_stride;
   a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
   a.Z = const_cast<void*>(Z); a.Wf = const_cast<float*>(Wf);
+  a.nchunk = 1; a.Tc = d->T; a.Wstart = nullptr; a.maps = nullptr;
   return a;
 }
 
@@ -249,6 +250,7 @@ const char* ttt_status_str(int s) {
     case TTT_ERR_STRIDE: return "invalid stride";
     case TTT_ERR_FLAGS: return "unknown flag or non-zero reserved field";
     case TTT_ERR_POS: return "negative decode position";
+    case TTT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     default: return "unknown status";
   }
 }
@@ -284,6 +286,50 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
     e = ttt::launch_linear_primal(make_primal_args_fwd(desc, Q, K, V, W0, eta, Z, W_final), s);
   else
     e = ttt::launch_linear_generic(a, s);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t nchunks) {
+  if (!desc || nchunks < 1 || desc->B < 0 || desc->H < 0 || desc->d < 1) return -1;
+  if (nchunks == 1) return 0;
+  const int64_t per_chain = (static_cast<int64_t>(nchunks - 1) * 2 + nchunks) * desc->d * desc->d * 4;
+  return static_cast<int64_t>(desc->B) * desc->H * per_chain;
+}
+
+ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K,
+                                  const void* V, const float* W0, const float* eta, void* Z, float* W_final,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+  Kernel k;
+  ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
+  if (st != TTT_OK) return st;
+  if (nchunks < 1 || desc->T % (16 * nchunks) != 0) return TTT_ERR_SHAPE;
+  if (desc->flags != 0 || k != K_MFMA) return TTT_ERR_UNSUPPORTED;
+  if (nchunks == 1) return ttt_linear_fwd(desc, Q, K, V, W0, eta, Z, W_final, stream);
+  const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
+  if (chains == 0) return TTT_OK;
+  const int64_t need = ttt_linear_chunked_workspace_bytes(desc, nchunks);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TTT_ERR_WORKSPACE;
+  {
+    const int64_t tok = chains * desc->T * desc->d;
+    const int64_t in_b = tok * dtype_size(desc->in_dtype), z_b = tok * dtype_size(desc->out_dtype);
+    const int64_t hdd = static_cast<int64_t>(desc->H) * desc->d * desc->d;
+    const int64_t w0_b = (desc->w0_batch_stride == 0 ? hdd : chains * desc->d * desc->d) * 4;
+    const int64_t eta_b = tok > 0 ? eta_extent(desc->B, desc->H, desc->T, desc->eta_stride_b, desc->eta_stride_h,
+                                               desc->eta_stride_t) * 4 : 0;
+    const Range rw{workspace, need};
+    for (Range r : {Range{Q, in_b}, Range{K, in_b}, Range{V, in_b}, Range{eta, eta_b}, Range{W0, w0_b},
+                    Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
+      if (overlaps(rw, r)) return TTT_ERR_ALIAS;
+  }
+  ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
+  a.nchunk = nchunks;
+  a.Tc = desc->T / nchunks;
+  a.maps = static_cast<float*>(workspace);
+  a.Wstart = a.maps + chains * (nchunks - 1) * 2 * desc->d * desc->d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = ttt::launch_linear_mfma_maps(a, s);
+  if (e == hipSuccess) e = ttt::launch_linear_chunk_scan(a, s);
+  if (e == hipSuccess) e = ttt::launch_linear_mfma(a, s);
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

@@ -143,7 +143,10 @@ __device__ __forceinline__ void store_z<float>(float* p, float x) { st_stream(p,
 template <>
 __device__ __forceinline__ void store_z<uint16_t>(uint16_t* p, float x) { st_stream(p, f32_to_bf16_bits(x)); }
 
-template <int PF, bool ETA_TOKEN, typename OutT>
+// MODE 0: forward (Z and the final state).  MODE 1 / 2: chunk map P / R of a
+// chunked forward -- the state recurrence from I with V = 0 / from 0 with V,
+// over one chunk, with no query path and no Z.
+template <int PF, bool ETA_TOKEN, typename OutT, int MODE>
 __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a) {
   __shared__ Slot slots[2];
 
@@ -153,17 +156,20 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   const int li = lane & 15;
   const int g = lane >> 4;
 
-  const int chain = blockIdx.x;
+  // workgroup -> (chain, chunk); a plain forward has one chunk of T tokens
+  const int per_chain = MODE == 0 ? a.nchunk : a.nchunk - 1;
+  const int chain = blockIdx.x / per_chain;
+  const int chunk = blockIdx.x - chain * per_chain;
   const int bi = chain / a.H;
   const int h = chain - bi * a.H;
-  const int nb = a.T / BT;
+  const int nb = a.Tc / BT;
 
-  const size_t tok0 = static_cast<size_t>(chain) * a.T;
+  const size_t tok0 = static_cast<size_t>(chain) * a.T + static_cast<size_t>(chunk) * a.Tc;
   const u32x4* Qg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.Q) + tok0 * D);
   const u32x4* Kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.K) + tok0 * D);
   const u32x4* Vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.V) + tok0 * D);
   OutT* Zg = static_cast<OutT*>(a.Z) + tok0 * D;
-  const float* eg = a.eta + bi * a.esb + h * a.esh;
+  const float* eg = a.eta + bi * a.esb + h * a.esh + static_cast<int64_t>(chunk) * a.Tc * a.est;
 
   // staging roles (every load unconditional, so the ring stays in registers):
   //   16 B of Q (tid < 128) or K (tid >= 128): row srow, columns scol..scol+7
@@ -199,14 +205,22 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 
   // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
   float4v wt[4];
-  {
-    const float* w0 = a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D +
+  if constexpr (MODE == 0) {
+    const float* w0 = (a.Wstart ? a.Wstart + (static_cast<int64_t>(chain) * a.nchunk + chunk) * D * D
+                                : a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D) +
                       static_cast<int64_t>(16 * w + li) * D + 4 * g;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float4 x = *reinterpret_cast<const float4*>(w0 + 16 * t);
       wt[t] = float4v{x.x, x.y, x.z, x.w};
     }
+  } else {
+    // P map starts from the identity, R map from zero
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        wt[t][r] = (MODE == 1 && 16 * w + li == 16 * t + 4 * g + r) ? 1.f : 0.f;
   }
 
   // Drain the state / eta loads before the ring prologue: otherwise the
@@ -246,6 +260,21 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     float4v pk = {0.f, 0.f, 0.f, 0.f}, pq = pk, sc = pk;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
+      if constexpr (MODE != 0) {
+        float w8[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          w8[r] = wt[2 * m][r];
+          w8[4 + r] = wt[2 * m + 1][r];
+        }
+        bf16x4 h0, l0, h1, l1;
+        split4(w8, h0, l0);
+        split4(w8 + 4, h1, l1);
+        const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
+        pk = mfma32(ak, cat(h0, h1), pk);
+        pk = mfma32(ak, cat(l0, l1), pk);
+        continue;
+      }
       float w8[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -267,7 +296,10 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 
     // ---- E^T[t = 4g+r][i = 16w+li] = P_K - V ----
     float e[4];
-    {
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e[r] = pk[r];  // V = 0
+    } else {
       const bf16x4 vc = read_cols(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
@@ -275,21 +307,24 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 
     // ---- Z = P_Q + M G, with M[t][s] = S[s][t] [s <= t] (causal mask, diagonal
     // included) and G[s][i] = -2 eta_s E^T[s][i], the operand the update uses too ----
-    float mv[4], gv[4];
+    float gv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      mv[r] = (4 * g + r <= li) ? sc[r] : 0.f;
-      gv[r] = -2.f * et[r] * e[r];
-    }
-    bf16x4 mhi, mlo, bhi, blo;
-    split4(mv, mhi, mlo);
+    for (int r = 0; r < 4; ++r) gv[r] = -2.f * et[r] * e[r];
+    bf16x4 bhi, blo;
     split4(gv, bhi, blo);
-    // The 16x16x32 MFMA sums 8 k-slots per lane group; a 16-token contraction
-    // uses slots 0-3 and 4-7 for two passes at once: [hi, hi] x [hi, lo].
-    const bf16x4 zero4 = {};
     float4v z = pq;
-    z = mfma32(cat(mhi, mhi), cat(bhi, blo), z);
-    z = mfma32(cat(mlo, zero4), cat(bhi, zero4), z);
+    if constexpr (MODE == 0) {
+      float mv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mv[r] = (4 * g + r <= li) ? sc[r] : 0.f;
+      bf16x4 mhi, mlo;
+      split4(mv, mhi, mlo);
+      // The 16x16x32 MFMA sums 8 k-slots per lane group; a 16-token contraction
+      // uses slots 0-3 and 4-7 for two passes at once: [hi, hi] x [hi, lo].
+      const bf16x4 zero4 = {};
+      z = mfma32(cat(mhi, mhi), cat(bhi, blo), z);
+      z = mfma32(cat(mlo, zero4), cat(bhi, zero4), z);
+    }
 
     // ---- W^T[c][i] += sum_s K[s][c] G[s][i] ----
     const bf16x8 gb = cat(bhi, blo);
@@ -300,9 +335,11 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     }
 
     // ---- store Z rows t = 4g + r, columns 16w + li ----
-    OutT* zp = Zg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
+    if constexpr (MODE == 0) {
+      OutT* zp = Zg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) store_z<OutT>(zp + r * D, z[r]);
+      for (int r = 0; r < 4; ++r) store_z<OutT>(zp + r * D, z[r]);
+    }
 
     __syncthreads();
   };
@@ -321,7 +358,14 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     if (nfull + j < nb) step(nfull + j, ra[j], rb[j], re[j], ra[jn], rb[jn], re[jn]);
   }
 
-  float* wf = a.Wf + static_cast<int64_t>(chain) * D * D + static_cast<int64_t>(16 * w + li) * D + 4 * g;
+  float* wf;
+  if constexpr (MODE == 0) {
+    if (chunk != a.nchunk - 1) return;  // only the last chunk holds the final state
+    wf = a.Wf + static_cast<int64_t>(chain) * D * D;
+  } else {
+    wf = a.maps + ((static_cast<int64_t>(chain) * (a.nchunk - 1) + chunk) * 2 + (MODE - 1)) * D * D;
+  }
+  wf += static_cast<int64_t>(16 * w + li) * D + 4 * g;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     *reinterpret_cast<float4*>(wf + 16 * t) = make_float4(wt[t][0], wt[t][1], wt[t][2], wt[t][3]);
@@ -334,11 +378,19 @@ constexpr int kPF = TTT_LINEAR_PF;  // prefetch distance (mini-batches in flight
 
 template <bool TOK>
 hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
-  dim3 grid(a.B * a.H), block(kThreads);
+  dim3 grid(a.B * a.H * a.nchunk), block(kThreads);
   if (a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 0>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t, 0>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool TOK>
+hipError_t launch_maps_eta(const LinearArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.H * (a.nchunk - 1)), block(kThreads);
+  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 1>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 2>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -353,6 +405,10 @@ const char* linear_mfma_name(const LinearArgs& a) {
 
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
   return a.est != 0 ? launch_eta<true>(a, s) : launch_eta<false>(a, s);
+}
+
+hipError_t launch_linear_mfma_maps(const LinearArgs& a, hipStream_t s) {
+  return a.est != 0 ? launch_maps_eta<true>(a, s) : launch_maps_eta<false>(a, s);
 }
 
 }  // namespace ttt

@@ -19,6 +19,11 @@ struct LinearArgs {
   int64_t esb, esh, est;  // eta strides (elements)
   void* Z;
   float* Wf;
+  // Chunked execution: the sequence is split into nchunk chunks of Tc tokens
+  // (nchunk = 1, Tc = T, Wstart = maps = nullptr for a plain forward).
+  int nchunk, Tc;
+  float* Wstart;        // [chains][nchunk][d][d] start state of every chunk
+  float* maps;          // [chains][nchunk-1][2][d][d] chunk maps (P, R)
 };
 
 struct MlpArgs {
@@ -67,6 +72,12 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(const LinearArgs& a);
 const char* linear_mfma_name(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
+// The chunk maps of a chunked forward: for every chain and every chunk but the
+// last, P = the product of the chunk's (I - 2 K diag(eta) K^T) and R = the
+// state the chunk reaches from zero, so that W_end = W_start P + R.
+hipError_t launch_linear_mfma_maps(const LinearArgs& a, hipStream_t s);
+// Chunk start states: Wstart[c+1] = Wstart[c] P_c + R_c, Wstart[0] = W0.
+hipError_t launch_linear_chunk_scan(const LinearArgs& a, hipStream_t s);
 
 // TTT-MLP kernel: d = 64, dh = 256, b = 16, bf16 Q/K/V.
 bool mlp_supported(const MlpArgs& a);

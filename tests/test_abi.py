@@ -16,13 +16,13 @@ import test_sequence_layer_amd as ttt
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ttt.h")
 
-OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, ALIGN, HIP, STRIDE, FLAGS = range(10)
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, ALIGN, HIP, STRIDE, FLAGS, POS, WORKSPACE = range(12)
 GB = 1 << 30
 
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(ttt_[a-z_0-9]+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ttt_[a-z_0-9]+)\s*\(", src, re.M)))
 
 
 def test_header_and_binding_agree():
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert ttt.abi_version() == 1
-    for s in range(11):
+    for s in range(12):
         assert ttt.status_str(s) and ttt.status_str(s) != "unknown status"
     assert ttt.status_str(99) == "unknown status"
 
@@ -188,3 +188,11 @@ def test_primal_flag():
     assert _val(_desc(flags=2, b=7, T=63)) == OK   # any b with the primal form
     assert _val(_desc(flags=3)) == FLAGS            # generic and primal together
     assert ttt.linear_kernel_name(2, 4, 64, 64, 16, primal=True) == "ttt_linear_primal_kernel<64>"
+
+
+def test_chunked_workspace_bytes():
+    d = _desc(B=2, H=32, T=32768)
+    assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 1) == 0
+    assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 8) == 64 * (7 * 2 + 8) * 64 * 64 * 4
+    assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 0) == -1
+    assert ttt.lib().ttt_linear_chunked_workspace_bytes(None, 4) == -1
