@@ -20,7 +20,10 @@ Contents
                                number type (fractions.Fraction for exact runs).
   linear_dual_exact            the dual form written out from 03 §7, pure
                                Python, any number type (self-check only).
-  linear_dual_f64, mlp_dual_f64, linear_naive_f64, mlp_primal_np
+  linear_ln_primal             fp64 primal form of TTT-Linear with layer norm
+                               and residual inside f (03 §9), in C.
+  linear_dual_f64, mlp_dual_f64, linear_naive_f64, mlp_primal_np,
+  linear_ln_dual_f64
                                numpy fp64 forms used only to check the oracle.
   gelu, gelu_prime             exact-erf GELU and its derivative (numpy).
 
@@ -69,6 +72,8 @@ def _load():
     lib.oracle_linear_primal.restype = None
     lib.oracle_mlp_primal.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp, i]
     lib.oracle_mlp_primal.restype = None
+    lib.oracle_linear_ln_primal.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, dp, i]
+    lib.oracle_linear_ln_primal.restype = None
     lib.oracle_max_threads.restype = i
     _lib = lib
     return lib
@@ -121,6 +126,23 @@ def mlp_primal(q, k, v, w1, w2, eta, b: int, threads: int = 0):
         _load().oracle_mlp_primal(n, T, d, dh, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2),
                                   _ptr(eta), _ptr(z), _ptr(w1f), _ptr(w2f), int(threads))
     return z, w1f, w2f
+
+
+def linear_ln_primal(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, threads: int = 0):
+    """TTT-Linear with LN + residual, f(x) = x + LN(W x), primal form, fp64.
+
+    q, k, v : [n, T, d];  w0 : [n, d, d];  gamma, beta : [n, d];  eta : [n, T]
+    returns (z, w_final).
+    """
+    q, k, v, w0, gamma, beta, eta = map(_f64, (q, k, v, w0, gamma, beta, eta))
+    n, T, d = q.shape
+    assert w0.shape == (n, d, d) and gamma.shape == (n, d) and beta.shape == (n, d) and eta.shape == (n, T)
+    z = np.empty((n, T, d))
+    wf = np.empty((n, d, d))
+    if n:
+        _load().oracle_linear_ln_primal(n, T, d, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
+                                        _ptr(beta), float(eps), _ptr(eta), _ptr(z), _ptr(wf), int(threads))
+    return z, wf
 
 
 def run_inputs(inp, threads: int = 0):
@@ -232,6 +254,43 @@ def linear_naive_f64(q, k, v, w0, eta, b):
                 Wt = W - sum(eta[c, s] * G[i] for i, s in enumerate(ts) if s <= t)
                 z[c, t] = Wt @ q[c, t]
             W = W - sum(eta[c, s] * G[i] for i, s in enumerate(ts))
+        wf[c] = W
+    return z, wf
+
+
+def _ln_cols(Y, gamma, beta, eps):
+    """Layer norm of every column of Y (d x b): (normalised, std) with per-row gamma, beta."""
+    mu = Y.mean(axis=0, keepdims=True)
+    s = np.sqrt(((Y - mu) ** 2).mean(axis=0, keepdims=True) + eps)
+    Yh = (Y - mu) / s
+    return gamma[:, None] * Yh + beta[:, None], Yh, s
+
+
+def linear_ln_dual_f64(q, k, v, w0, gamma, beta, eta, b, eps=1e-6):
+    """Dual form of TTT-Linear with LN + residual, fp64 (self-check only).
+
+    Per mini-batch (columns = tokens, start state W): Y = W K, LN statistics per
+    column, G = 2 (K + LN(Y) - V) * gamma, D = (G - mean(G) - Yh mean(G Yh)) / s
+    (column means over the d rows), Z = Q + LN(W Q - D (diag(eta) triu(K^T Q))),
+    W <- W - D diag(eta) K^T.
+    """
+    q, k, v, w0, gamma, beta, eta = map(_f64, (q, k, v, w0, gamma, beta, eta))
+    n, T, d = q.shape
+    z = np.empty((n, T, d))
+    wf = np.empty((n, d, d))
+    for c in range(n):
+        W = w0[c].copy()
+        for t0 in range(0, T, b):
+            sl = slice(t0, min(t0 + b, T))
+            K, V, Q = k[c, sl].T, v[c, sl].T, q[c, sl].T
+            et = eta[c, sl]
+            Y = W @ K
+            L, Yh, s = _ln_cols(Y, gamma[c], beta[c], eps)
+            G = 2.0 * (K + L - V) * gamma[c][:, None]
+            Dl = (G - G.mean(axis=0, keepdims=True) - Yh * (G * Yh).mean(axis=0, keepdims=True)) / s
+            YQ = W @ Q - Dl @ (np.triu(K.T @ Q) * et[:, None])
+            z[c, sl] = (Q + _ln_cols(YQ, gamma[c], beta[c], eps)[0]).T
+            W = W - (Dl * et[None, :]) @ K.T
         wf[c] = W
     return z, wf
 

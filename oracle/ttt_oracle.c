@@ -16,7 +16,10 @@
  *   - mini-batch GD: every gradient of mini-batch n is taken at the W held
  *     just before the first token of that mini-batch ([TTT] 03 §6);
  *   - TTT-Linear: f(x) = W x with W square; TTT-MLP: two layers, hidden width
- *     dh, GELU in between ([TTT] 03 §9 "two variants").
+ *     dh, GELU in between ([TTT] 03 §9 "two variants");
+ *   - with layer norm and residual (03 §9: f always has them for stability):
+ *     f(x) = x + LN(W x), LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps) + beta
+ *     over the d outputs (var the biased mean of squares), gamma/beta per head.
  * The gradient of |W k - v|^2 with respect to W is 2 (W k - v) k^T (summed
  * squared error, no 1/2, no 1/d).  GELU is the exact form x * Phi(x).
  *
@@ -156,5 +159,71 @@ void oracle_mlp_primal(int n, int T, int d, int dh, int b,
     memcpy(w1f + c * sz, W1, sz * sizeof(double));
     memcpy(w2f + c * sz, W2, sz * sizeof(double));
     free(W1); free(W2); free(W1b); free(W2b); free(h); free(a); free(g1); free(e);
+  }
+}
+
+/* LN over d values: yhat = (y - mu) / s, s = sqrt(var + eps); returns s. */
+static double ln_normalize(const double* y, double* yhat, int d, double eps) {
+  double mu = 0.0;
+  for (int i = 0; i < d; ++i) mu += y[i];
+  mu /= d;
+  double var = 0.0;
+  for (int i = 0; i < d; ++i) var += (y[i] - mu) * (y[i] - mu);
+  var /= d;
+  const double s = sqrt(var + eps);
+  for (int i = 0; i < d; ++i) yhat[i] = (y[i] - mu) / s;
+  return s;
+}
+
+/* TTT-Linear with LN and residual, f(x) = x + LN(W x), primal form.
+ * gamma, beta : [n, d] (per chain).  The gradient of |f(k) - v|^2 with respect
+ * to W is delta k^T, where delta is the loss gradient back-propagated through
+ * LN to y = W k:  g = 2 (f(k) - v) * gamma,
+ * delta = (g - mean(g) - yhat * mean(g * yhat)) / s. */
+void oracle_linear_ln_primal(int n, int T, int d, int b,
+                             const double* q, const double* k, const double* v,
+                             const double* w0, const double* gamma, const double* beta, double eps,
+                             const double* eta, double* z, double* wf, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int c = 0; c < n; ++c) {
+    const size_t dd = (size_t)d * d;
+    const double* gm = gamma + (size_t)c * d;
+    const double* bt = beta + (size_t)c * d;
+    double* W = (double*)malloc(dd * sizeof(double));
+    double* Wb = (double*)malloc(dd * sizeof(double));
+    double* y = (double*)malloc((size_t)d * sizeof(double));
+    double* yh = (double*)malloc((size_t)d * sizeof(double));
+    double* g = (double*)malloc((size_t)d * sizeof(double));
+    memcpy(W, w0 + c * dd, dd * sizeof(double));
+    for (int t0 = 0; t0 < T; t0 += b) {
+      memcpy(Wb, W, dd * sizeof(double));
+      int t1 = t0 + b < T ? t0 + b : T;
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        /* reconstruction of v_t from k_t at the mini-batch-start state */
+        matvec(Wb, k + o, y, d, d);
+        const double s = ln_normalize(y, yh, d, eps);
+        double mg = 0.0, mgy = 0.0;
+        for (int i = 0; i < d; ++i) {
+          const double r = k[o + i] + gm[i] * yh[i] + bt[i] - v[o + i];
+          g[i] = 2.0 * r * gm[i];
+          mg += g[i];
+          mgy += g[i] * yh[i];
+        }
+        mg /= d;
+        mgy /= d;
+        for (int i = 0; i < d; ++i) g[i] = (g[i] - mg - yh[i] * mgy) / s; /* delta */
+        rank1_sub(W, eta[(size_t)c * T + t], g, k + o, d, d);
+        /* output with the updated state */
+        matvec(W, q + o, y, d, d);
+        ln_normalize(y, yh, d, eps);
+        for (int i = 0; i < d; ++i) z[o + i] = q[o + i] + gm[i] * yh[i] + bt[i];
+      }
+    }
+    memcpy(wf + c * dd, W, dd * sizeof(double));
+    free(W); free(Wb); free(y); free(yh); free(g);
   }
 }

@@ -1,0 +1,125 @@
+"""Pins of the oracle of TTT-Linear with layer norm and residual inside f.
+
+Pages: [TTT] news article, part 03 §9: f always contains layer normalization
+and a residual connection, f(x) = x + LN(f_res(x)); here f_res(x) = W x and LN
+normalises the d outputs with per-head gamma, beta and a small eps.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _ln(y, gamma, beta, eps):
+    mu = y.mean()
+    s = np.sqrt(((y - mu) ** 2).mean() + eps)
+    return gamma * (y - mu) / s + beta
+
+
+def _rand(seed, n, T, d, eta_scale=0.05):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((n, T, d)) / np.sqrt(d)
+    k = r.standard_normal((n, T, d)) / np.sqrt(d)
+    v = r.standard_normal((n, T, d)) / np.sqrt(d)
+    w0 = r.standard_normal((n, d, d)) * 0.2
+    gamma = 1.0 + 0.3 * r.standard_normal((n, d))
+    beta = 0.1 * r.standard_normal((n, d))
+    eta = eta_scale / (1.0 + np.exp(-r.standard_normal((n, T))))
+    return q, k, v, w0, gamma, beta, eta
+
+
+def test_step_is_gradient_fd():
+    """T = b = 1: W_final = W0 - eta * grad |k + LN(W0 k) - v|^2 (central differences)."""
+    q, k, v, w0, gamma, beta, _ = _rand(1, 1, 1, 6)
+    eta = 0.01
+    eps = 1e-6
+    _, wf = oracle.linear_ln_primal(q, k, v, w0, gamma, beta, np.array([[eta]]), 1, eps)
+    grad = (w0[0] - wf[0]) / eta
+    loss = lambda W: float(np.sum((k[0, 0] + _ln(W @ k[0, 0], gamma[0], beta[0], eps) - v[0, 0]) ** 2))  # noqa
+    fd = np.zeros_like(grad)
+    h = 1e-6
+    for i in range(6):
+        for j in range(6):
+            P, M = w0[0].copy(), w0[0].copy()
+            P[i, j] += h
+            M[i, j] -= h
+            fd[i, j] = (loss(P) - loss(M)) / (2 * h)
+    np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7)
+
+
+def test_eta_zero_closed_form():
+    q, k, v, w0, gamma, beta, eta = _rand(2, 2, 20, 8)
+    z, wf = oracle.linear_ln_primal(q, k, v, w0, gamma, beta, np.zeros_like(eta), 4)
+    np.testing.assert_array_equal(wf, w0)
+    for c in range(2):
+        for t in range(20):
+            np.testing.assert_allclose(z[c, t], q[c, t] + _ln(w0[c] @ q[c, t], gamma[c], beta[c], 1e-6),
+                                       rtol=0, atol=1e-14)
+
+
+def test_zero_gamma_freezes_state():
+    """gamma = 0: f(x) = x + beta does not depend on W, the gradient vanishes,
+    W never moves and Z = Q + beta -- a dropped gamma in the backward fails this."""
+    q, k, v, w0, gamma, beta, eta = _rand(3, 2, 32, 8)
+    z, wf = oracle.linear_ln_primal(q, k, v, w0, np.zeros_like(gamma), beta, eta, 16)
+    np.testing.assert_array_equal(wf, w0)
+    np.testing.assert_allclose(z, q + beta[:, None, :], rtol=0, atol=1e-15)
+
+
+def test_output_rows_are_normalised():
+    """gamma = 1, beta = 0: every z_t - q_t has zero mean and mean square
+    var / (var + eps) < 1 over the d outputs, whatever the state."""
+    q, k, v, w0, _, _, eta = _rand(4, 2, 32, 16)
+    z, _ = oracle.linear_ln_primal(q, k, v, w0, np.ones((2, 16)), np.zeros((2, 16)), eta, 8)
+    dz = z - q
+    np.testing.assert_allclose(dz.mean(axis=2), 0.0, atol=1e-14)
+    ms = (dz ** 2).mean(axis=2)
+    assert np.all(ms < 1.0) and np.all(ms > 0.99)
+
+
+def test_constant_row_shift_invariance():
+    """LN removes the mean over the outputs, so adding 1 u^T to the state (the same
+    u^T added to every row) changes neither the outputs nor the gradients: Z is
+    unchanged and W_final shifts by exactly 1 u^T."""
+    q, k, v, w0, gamma, beta, eta = _rand(5, 1, 48, 8)
+    u = np.random.default_rng(9).standard_normal(8)
+    z1, f1 = oracle.linear_ln_primal(q, k, v, w0, gamma, beta, eta, 16)
+    z2, f2 = oracle.linear_ln_primal(q, k, v, w0 + np.outer(np.ones(8), u)[None], gamma, beta, eta, 16)
+    np.testing.assert_allclose(z2, z1, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(f2 - f1, np.outer(np.ones(8), u)[None], rtol=0, atol=1e-11)
+
+
+def test_b1_is_online_gd():
+    q, k, v, w0, gamma, beta, eta = _rand(6, 1, 12, 6)
+    eps = 1e-6
+    z, wf = oracle.linear_ln_primal(q, k, v, w0, gamma, beta, eta, 1, eps)
+    W = w0[0].copy()
+    g0, b0 = gamma[0], beta[0]
+    for t in range(12):
+        y = W @ k[0, t]
+        mu = y.mean()
+        s = np.sqrt(((y - mu) ** 2).mean() + eps)
+        yh = (y - mu) / s
+        gr = 2 * (k[0, t] + g0 * yh + b0 - v[0, t]) * g0
+        delta = (gr - gr.mean() - yh * (gr * yh).mean()) / s
+        W = W - eta[0, t] * np.outer(delta, k[0, t])
+        np.testing.assert_allclose(z[0, t], q[0, t] + _ln(W @ q[0, t], g0, b0, eps), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(wf[0], W, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,T,d,b", [(2, 48, 16, 16), (1, 37, 8, 5), (3, 64, 64, 16)])
+def test_dual_equals_primal(n, T, d, b):
+    q, k, v, w0, gamma, beta, eta = _rand(7 + T, n, T, d)
+    z, wf = oracle.linear_ln_primal(q, k, v, w0, gamma, beta, eta, b)
+    zd, wd = oracle.linear_ln_dual_f64(q, k, v, w0, gamma, beta, eta, b)
+    assert oracle.max_rel_err(z, zd) < 1e-12
+    assert oracle.max_rel_err(wf, wd) < 1e-12
+
+
+def test_state_passing_bitwise():
+    q, k, v, w0, gamma, beta, eta = _rand(8, 2, 64, 8)
+    z, wf = oracle.linear_ln_primal(q, k, v, w0, gamma, beta, eta, 16)
+    za, wa = oracle.linear_ln_primal(q[:, :32], k[:, :32], v[:, :32], w0, gamma, beta, eta[:, :32], 16)
+    zb, wb = oracle.linear_ln_primal(q[:, 32:], k[:, 32:], v[:, 32:], wa, gamma, beta, eta[:, 32:], 16)
+    np.testing.assert_array_equal(z, np.concatenate([za, zb], axis=1))
+    np.testing.assert_array_equal(wf, wb)
