@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--generic", action="store_true", help="time the portable fp32 kernel instead")
     ap.add_argument("--primal", action="store_true",
                     help="time the primal (token-by-token) form instead of the dual form")
+    ap.add_argument("--ln", action="store_true",
+                    help="layer norm and residual inside f (gamma = 1, beta = 0)")
     ap.add_argument("--chunks", type=int, default=1,
                     help="split each sequence into this many chunks run in parallel (chunked forward)")
     ap.add_argument("--decode", action="store_true",
@@ -165,7 +167,13 @@ def main():
         kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
                                        inp.eta_strides, args.generic, args.primal)
 
-        if args.chunks > 1:
+        if args.ln:
+            gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
+            bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
+
+            def step():
+                ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], gam, bet, t["eta"], cfg.b, z=z, w_final=wf)
+        elif args.chunks > 1:
             kname = "ttt_linear_mfma_d64b16"
             ws = torch.empty(ttt.linear_chunked_workspace_bytes(B, H, T, d, cfg.b, args.chunks),
                              dtype=torch.uint8, device="cuda:0")
@@ -243,6 +251,9 @@ def main():
     eta_desc = {(0, 0, 0): "scalar", (0, 1, 0): "per head"}.get(tuple(inp.eta_strides), "per token")
     model = "TTT-MLP" if cfg.is_mlp else "TTT-Linear"
     form = "decode" if args.decode else ("primal" if args.primal else ("generic" if args.generic else ""))
+    if args.ln:
+        form = "layer-norm"
+        roof["note"] = "f(x) = x + LN(W x): layer norm and residual inside f"
     if args.chunks > 1:
         form = f"chunked({args.chunks})"
         roof["note"] = "chunked forward: chunk maps + scan + parallel chunks (4 launches per call)"

@@ -118,6 +118,21 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
 int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t nchunks);
 
 /*
+ * TTT-Linear with layer norm and residual inside f ([TTT] 03 §9: "for
+ * stability, f always contains LN and a residual connection"):
+ *     f(x) = x + LN(W x),  LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps) + beta
+ * over the d outputs (var = mean of squared deviations), gamma and beta fp32
+ * [H, d] per head.  The gradient of |f(k) - v|^2 stays rank one per token,
+ * delta k^T with delta the loss gradient back-propagated through LN to W k, so
+ * the dual form carries over: Y = W Q - Delta (diag(eta) triu(K^T Q)),
+ * Z = Q + LN(Y), W <- W - Delta diag(eta) K^T.  Other arguments as for
+ * ttt_linear_fwd.  Supported: d = 64, b = 16, bf16 inputs, flags = 0, eps >= 0.
+ */
+ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* W0, const float* gamma, const float* beta, float eps, const float* eta,
+                             void* Z, float* W_final, void* stream);
+
+/*
  * TTT-Linear decode ([TTT] 04 §3: generation is sequential and uses the primal
  * form).  Continues B*H sequences by desc->T new tokens (often 1), all at
  * absolute positions pos, pos+1, ..., carrying the state in place:

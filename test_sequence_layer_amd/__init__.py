@@ -37,7 +37,7 @@ STATUS_NAMES = {
 EXPORTS = (
     "ttt_linear_fwd", "ttt_linear_validate", "ttt_linear_kernel_name",
     "ttt_linear_decode", "ttt_linear_decode_validate",
-    "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes",
+    "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes", "ttt_linear_ln_fwd",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name",
     "ttt_status_str", "ttt_abi_version",
 )
@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_fwd_chunked.restype = ctypes.c_int
     L.ttt_linear_chunked_workspace_bytes.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int32]
     L.ttt_linear_chunked_workspace_bytes.restype = ctypes.c_int64
+    L.ttt_linear_ln_fwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, fp, vp, fp,
+                                    vp]
+    L.ttt_linear_ln_fwd.restype = ctypes.c_int
     L.ttt_linear_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
     L.ttt_linear_kernel_name.restype = ctypes.c_char_p
     L.ttt_mlp_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp, vp]
@@ -262,6 +265,37 @@ def linear_fwd_chunked(q, k, v, w0, eta, b: int, nchunks: int, workspace=None, o
                                       _stream_handle(stream))
     if st != TTT_OK:
         raise TTTError(st, "ttt_linear_fwd_chunked")
+    return z, w_final
+
+
+def linear_ln_fwd(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, out_dtype=None, w_final=None,
+                  z=None, stream=None):
+    """TTT-Linear with layer norm and residual inside f: f(x) = x + LN(W x).
+
+    gamma, beta : [H, d] float32 (per head).  Other arguments as :func:`linear_fwd`.
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
+        raise ValueError("gamma and beta must be [H, d]")
+    if tuple(w0.shape) == (H, d, d):
+        wstride = 0
+    elif tuple(w0.shape) == (B, H, d, d):
+        wstride = H * d * d
+    else:
+        raise ValueError(f"w0 shape {tuple(w0.shape)}: expected [H,d,d] or [B,H,d,d]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    if w_final is None:
+        w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    _check_dev(q, k, v, w0, gamma, beta, eta_t, z, w_final)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, 0)
+    st = lib().ttt_linear_ln_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
+                                 _ptr(beta), float(eps), _ptr(eta_t), _ptr(z), _ptr(w_final), _stream_handle(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_ln_fwd")
     return z, w_final
 
 

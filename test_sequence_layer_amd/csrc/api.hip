@@ -56,6 +56,7 @@ ttt::LinearArgs make_linear_args(const ttt_linear_desc* d, const void* Q, const 
   a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
   a.Z = const_cast<void*>(Z); a.Wf = const_cast<float*>(Wf);
   a.nchunk = 1; a.Tc = d->T; a.Wstart = nullptr; a.maps = nullptr;
+  a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
   return a;
 }
 
@@ -286,6 +287,31 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
     e = ttt::launch_linear_primal(make_primal_args_fwd(desc, Q, K, V, W0, eta, Z, W_final), s);
   else
     e = ttt::launch_linear_generic(a, s);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* W0, const float* gamma, const float* beta, float eps, const float* eta,
+                             void* Z, float* W_final, void* stream) {
+  Kernel k;
+  const ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
+  if (st != TTT_OK) return st;
+  if (desc->flags != 0 || k != K_MFMA) return TTT_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
+  const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
+  if (chains == 0) return TTT_OK;
+  if (!gamma || !beta) return TTT_ERR_NULL;
+  if (!aligned(gamma, 4) || !aligned(beta, 4)) return TTT_ERR_ALIGN;
+  const int64_t hd_b = static_cast<int64_t>(desc->H) * desc->d * 4;
+  const int64_t z_b = chains * desc->T * desc->d * dtype_size(desc->out_dtype);
+  for (Range out : {Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
+    for (Range in : {Range{gamma, hd_b}, Range{beta, hd_b}})
+      if (overlaps(out, in)) return TTT_ERR_ALIAS;
+  ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
+  a.gamma = gamma;
+  a.beta = beta;
+  a.eps = eps;
+  const hipError_t e = ttt::launch_linear_mfma(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

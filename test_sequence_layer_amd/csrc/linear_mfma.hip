@@ -143,12 +143,70 @@ __device__ __forceinline__ void store_z<float>(float* p, float x) { st_stream(p,
 template <>
 __device__ __forceinline__ void store_z<uint16_t>(uint16_t* p, float x) { st_stream(p, f32_to_bf16_bits(x)); }
 
+// ---- layer norm across the row-split waves --------------------------------
+// A token's 64 outputs are spread over the 4 waves (16 each, at lanes l%16 of
+// lane group l/16 = token / 4).  Sums over a wave's 16 outputs use xor
+// shuffles inside the 16-lane group; the 4 wave partials meet in LDS.
+// Data-parallel-primitive (DPP) lane moves inside a 16-lane row: quad_perm
+// [1,0,3,2] and [2,3,0,1] exchange neighbours 1 and 2 apart; row_half_mirror
+// (lane i <-> 7 - i within 8) and row_mirror (i <-> 15 - i) then fold the
+// quads, so after four adds every lane of the row holds the row's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
+struct LnShared {
+  float2 part[3][4][BT];  // [exchange][wave][token]
+};
+
+// Mean and 1/sqrt(var + eps) over the 64 outputs of the 4 tokens 4g + r this
+// lane holds (x[r] = output 16w + l%16 of token 4g + r).  Each wave's
+// (mean, M2) over its 16 outputs are combined exactly (equal counts), which
+// avoids the cancellation of raw power sums.
+__device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs[4], float2 (*part)[BT], int w,
+                                         int li, int g, float eps) {
+  float mw[4], m2[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mw[r] = sum16(x[r]) * (1.f / 16.f);
+    const float dv = x[r] - mw[r];
+    m2[r] = sum16(dv * dv);
+  }
+  if (li == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[w][4 * g + r] = make_float2(mw[r], m2[r]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float2 p[4];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) p[ww] = part[ww][4 * g + r];
+    const float m = 0.25f * (p[0].x + p[1].x + p[2].x + p[3].x);
+    float M2 = p[0].y + p[1].y + p[2].y + p[3].y;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M2 += 16.f * (p[ww].x - m) * (p[ww].x - m);
+    mu[r] = m;
+    rs[r] = rsqrtf(M2 * (1.f / 64.f) + eps);
+  }
+}
+
 // MODE 0: forward (Z and the final state).  MODE 1 / 2: chunk map P / R of a
 // chunked forward -- the state recurrence from I with V = 0 / from 0 with V,
 // over one chunk, with no query path and no Z.
-template <int PF, bool ETA_TOKEN, typename OutT, int MODE>
+// LN: f(x) = x + LN(W x) (layer norm and residual inside f; MODE 0 only).
+template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN>
 __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a) {
   __shared__ Slot slots[2];
+  __shared__ LnShared lns;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -202,6 +260,12 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // constant eta (scalar or per head)
   float eta_c = 0.f;
   if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
+  // LN scale and shift of output 16w + l%16
+  float ln_g = 0.f, ln_b = 0.f;
+  if constexpr (LN) {
+    ln_g = a.gamma[h * D + 16 * w + li];
+    ln_b = a.beta[h * D + 16 * w + li];
+  }
 
   // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
   float4v wt[4];
@@ -295,21 +359,56 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     }
 
     // ---- E^T[t = 4g+r][i = 16w+li] = P_K - V ----
-    float e[4];
-    if constexpr (MODE == 1) {
+    // ---- G[s][i] = -eta_s (dl/dy)[s][i]: the gradient factor of the rank-16
+    // update, also the operand of the Z correction ----
+    float gv[4];
+    if constexpr (LN) {
+      // y = W k (pk), f(k) = k + LN(y); dl/dy through LN (mini-batch-start state)
+      float mu[4], rs[4], yh[4], gr[4], s1[4], s2[4];
+      const float yk[4] = {pk[0], pk[1], pk[2], pk[3]};
+      ln_stats(yk, mu, rs, lns.part[0], w, li, g, a.eps);
+      const bf16x4 vc = read_cols(S.v, 0, 16 * w, li, g);   // V[4g + r][16w + li]
+      const bf16x4 kc = read_cols(S.k, 0, 16 * w, li, g);   // K[4g + r][16w + li]
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e[r] = pk[r];  // V = 0
+      for (int r = 0; r < 4; ++r) {
+        yh[r] = (pk[r] - mu[r]) * rs[r];
+        const float res = static_cast<float>(kc[r]) + ln_g * yh[r] + ln_b - static_cast<float>(vc[r]);
+        gr[r] = 2.f * res * ln_g;
+        s1[r] = sum16(gr[r]);
+        s2[r] = sum16(gr[r] * yh[r]);
+      }
+      if (li == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lns.part[1][w][4 * g + r] = make_float2(s1[r], s2[r]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mg = 0.f, mgy = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float2 p = lns.part[1][ww][4 * g + r];
+          mg += p.x;
+          mgy += p.y;
+        }
+        gv[r] = -et[r] * (gr[r] - mg * (1.f / 64.f) - yh[r] * mgy * (1.f / 64.f)) * rs[r];
+      }
     } else {
-      const bf16x4 vc = read_cols(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
+      float e[4];
+      if constexpr (MODE == 1) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
+        for (int r = 0; r < 4; ++r) e[r] = pk[r];  // V = 0
+      } else {
+        const bf16x4 vc = read_cols(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gv[r] = -2.f * et[r] * e[r];
     }
 
     // ---- Z = P_Q + M G, with M[t][s] = S[s][t] [s <= t] (causal mask, diagonal
-    // included) and G[s][i] = -2 eta_s E^T[s][i], the operand the update uses too ----
-    float gv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) gv[r] = -2.f * et[r] * e[r];
+    // included), G the operand the update uses too ----
     bf16x4 bhi, blo;
     split4(gv, bhi, blo);
     float4v z = pq;
@@ -335,6 +434,16 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     }
 
     // ---- store Z rows t = 4g + r, columns 16w + li ----
+    if constexpr (LN) {
+      // z = q + LN(W_t q): normalise the pre-norm output over its 64 entries
+      float zz[4], mu[4], rs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) zz[r] = z[r];
+      ln_stats(zz, mu, rs, lns.part[2], w, li, g, a.eps);
+      const bf16x4 qc = read_cols(S.q, 0, 16 * w, li, g);  // Q[4g + r][16w + li]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qc[r]) + ln_g * (zz[r] - mu[r]) * rs[r] + ln_b;
+    }
     if constexpr (MODE == 0) {
       OutT* zp = Zg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
 #pragma unroll
@@ -376,21 +485,21 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 #endif
 constexpr int kPF = TTT_LINEAR_PF;  // prefetch distance (mini-batches in flight per thread)
 
-template <bool TOK>
+template <bool TOK, bool LN>
 hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
   dim3 grid(a.B * a.H * a.nchunk), block(kThreads);
   if (a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 0>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 0, LN>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t, 0>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t, 0, LN>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <bool TOK>
 hipError_t launch_maps_eta(const LinearArgs& a, hipStream_t s) {
   dim3 grid(a.B * a.H * (a.nchunk - 1)), block(kThreads);
-  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 1>), grid, block, 0, s, a);
-  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 2>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 1, false>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 2, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -399,12 +508,12 @@ hipError_t launch_maps_eta(const LinearArgs& a, hipStream_t s) {
 bool linear_mfma_supported(const LinearArgs& a) { return a.d == 64 && a.b == 16 && a.in_dtype == 1; }
 
 const char* linear_mfma_name(const LinearArgs& a) {
-  (void)a;
-  return "ttt_linear_mfma_d64b16";
+  return a.gamma ? "ttt_linear_mfma_d64b16 (layer norm)" : "ttt_linear_mfma_d64b16";
 }
 
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
-  return a.est != 0 ? launch_eta<true>(a, s) : launch_eta<false>(a, s);
+  if (a.gamma) return a.est != 0 ? launch_eta<true, true>(a, s) : launch_eta<false, true>(a, s);
+  return a.est != 0 ? launch_eta<true, false>(a, s) : launch_eta<false, false>(a, s);
 }
 
 hipError_t launch_linear_mfma_maps(const LinearArgs& a, hipStream_t s) {

@@ -24,6 +24,10 @@ struct LinearArgs {
   int nchunk, Tc;
   float* Wstart;        // [chains][nchunk][d][d] start state of every chunk
   float* maps;          // [chains][nchunk-1][2][d][d] chunk maps (P, R)
+  // Layer norm and residual inside f (f(x) = x + LN(W x)); gamma == nullptr: plain f(x) = W x.
+  const float* gamma;   // [H][d]
+  const float* beta;    // [H][d]
+  float eps;
 };
 
 struct MlpArgs {

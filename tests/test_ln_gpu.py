@@ -1,0 +1,99 @@
+"""GPU parity of TTT-Linear with layer norm and residual inside f (f(x) = x + LN(W x)).
+
+Pages: [TTT] news article, part 03 §9 (f always contains LN and a residual
+connection).  Compared with the fp64 oracle; tolerance 2e-3 (bf16 inputs).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import ttt_inputs as ti
+from ttt_testutil import max_rel, rows, to_device
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ttt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import test_sequence_layer_amd as m
+    m.lib()
+    return m
+
+
+def _ln_params(H, d, seed, kind="random"):
+    r = np.random.default_rng(seed)
+    if kind == "unit":
+        return np.ones((H, d), np.float32), np.zeros((H, d), np.float32)
+    return ((1.0 + 0.3 * r.standard_normal((H, d))).astype(np.float32),
+            (0.1 * r.standard_normal((H, d))).astype(np.float32))
+
+
+def _check(ttt, cfg, gamma, beta, chains=None, eps=1e-6, tol=2e-3, label=""):
+    full = ti.generate(cfg)
+    t = to_device(full)
+    dev = "cuda:0"
+    z, wf = ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], torch.from_numpy(gamma).to(dev),
+                              torch.from_numpy(beta).to(dev), t["eta"], cfg.b, eps)
+    torch.cuda.synchronize()
+    chains = np.arange(cfg.chains) if chains is None else np.asarray(chains)
+    sub = ti.generate(cfg, chains=chains)
+    heads = chains % cfg.H
+    zr, wr = oracle.linear_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(), gamma[heads], beta[heads],
+                                     sub.eta_rows(), cfg.b, eps)
+    ez, ew = max_rel(rows(z, chains), zr), max_rel(rows(wf, chains), wr)
+    print(f"[LN {label or cfg.name}] err Z={ez:.3e} W_final={ew:.3e}", flush=True)
+    assert ez < tol and ew < tol, (ez, ew)
+    return z, wf, t
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 1, 16), (2, 3, 112), (1, 2, 256)])
+@pytest.mark.parametrize("eta_kind", ["scalar", "token"])
+def test_ln_small(ttt, B, H, T, eta_kind):
+    cfg = ti.CONFIGS["l1p3b"].with_(B=B, H=H, T=T, eta_kind=eta_kind, eta_value=1.0 / 64, seed=60 + T)
+    g, b = _ln_params(H, 64, T)
+    _check(ttt, cfg, g, b, label=f"B{B} H{H} T{T} {eta_kind}")
+
+
+def test_ln_large_step(ttt):
+    """A large step size drives the state (and the LN statistics) far from W0."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=1, H=2, T=256, eta_kind="scalar", eta_value=0.5, seed=62)
+    g, b = _ln_params(2, 64, 5)
+    _check(ttt, cfg, g, b, label="eta=0.5")
+
+
+def test_ln_full_shape_sampled(ttt):
+    cfg = ti.CONFIGS["l1p3b"]
+    g, b = _ln_params(cfg.H, 64, 7, "unit")
+    z, _, t = _check(ttt, cfg, g, b, chains=ti.sample_chains(cfg, 16), label="1.3B shape, gamma=1 beta=0")
+    # with gamma = 1, beta = 0 every z_t - q_t is normalised over its 64 entries
+    dz = (z.float() - t["q"].float()).reshape(-1, 64)
+    assert float(dz.mean(dim=1).abs().max()) < 1e-5
+
+
+def test_ln_zero_gamma_freezes_state(ttt):
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=2, T=64, seed=63)
+    inp = ti.generate(cfg)
+    t = to_device(inp)
+    beta = torch.randn((2, 64), device="cuda:0")
+    z, wf = ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], torch.zeros((2, 64), device="cuda:0"), beta,
+                              t["eta"], 16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(rows(wf), inp.w_rows())
+    ref = t["q"].float() + beta[None, :, None, :]
+    assert float((z - ref).abs().max()) < 1e-6
+
+
+def test_ln_errors(ttt):
+    x = torch.zeros((1, 1, 32, 64), dtype=torch.bfloat16, device="cuda:0")
+    w0 = torch.zeros((1, 64, 64), device="cuda:0")
+    g = torch.ones((1, 64), device="cuda:0")
+    xf = torch.zeros((1, 1, 32, 64), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ttt.TTTError) as ei:
+        ttt.linear_ln_fwd(xf, xf, xf, w0, g, g, 0.1, 16)      # fp32 inputs: no LN kernel
+    assert ei.value.status == 4
+    with pytest.raises(ttt.TTTError) as ei:
+        ttt.linear_ln_fwd(x, x, x, w0, g, g, 0.1, 16, eps=-1.0)
+    assert ei.value.status == 2
