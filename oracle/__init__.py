@@ -22,6 +22,8 @@ Contents
                                Python, any number type (self-check only).
   linear_ln_primal             fp64 primal form of TTT-Linear with layer norm
                                and residual inside f (03 §9), in C.
+  linear_grads                 gradients of TTT-Linear: torch fp64 autograd
+                               through the primal loop (linear_primal_torch).
   linear_dual_f64, mlp_dual_f64, linear_naive_f64, mlp_primal_np,
   linear_ln_dual_f64
                                numpy fp64 forms used only to check the oracle.
@@ -293,6 +295,46 @@ def linear_ln_dual_f64(q, k, v, w0, gamma, beta, eta, b, eps=1e-6):
             W = W - (Dl * et[None, :]) @ K.T
         wf[c] = W
     return z, wf
+
+
+def linear_primal_torch(q, k, v, w0, eta, b):
+    """The primal TTT-Linear loop (03 §1, §5, §6) on torch CPU tensors, any dtype.
+
+    Shapes as linear_primal; differentiable, so torch autograd of this loop is
+    the reference gradient of the layer.
+    """
+    import torch
+
+    n, T, d = q.shape
+    W = w0.clone()
+    zs = []
+    for t0 in range(0, T, b):
+        Wb = W
+        for t in range(t0, min(t0 + b, T)):
+            e = torch.einsum("nij,nj->ni", Wb, k[:, t]) - v[:, t]
+            W = W - (2.0 * eta[:, t])[:, None, None] * e[:, :, None] * k[:, t][:, None, :]
+            zs.append(torch.einsum("nij,nj->ni", W, q[:, t]))
+    return torch.stack(zs, dim=1), W
+
+
+def linear_grads(q, k, v, w0, eta, b, dz, dwf=None):
+    """Gradients of  sum(dz * Z) + sum(dwf * W_final)  of TTT-Linear, fp64 autograd
+    through the primal loop.  w0 : [n, d, d] (per chain), eta : [n, T].
+
+    returns (dq, dk, dv, deta [n, T], dw0 [n, d, d]) as numpy fp64.
+    """
+    import torch
+
+    def t(x):
+        return torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True)
+
+    q_, k_, v_, w_, e_ = t(q), t(k), t(v), t(w0), t(eta)
+    z, wf = linear_primal_torch(q_, k_, v_, w_, e_, b)
+    loss = (z * torch.tensor(np.asarray(dz, np.float64))).sum()
+    if dwf is not None:
+        loss = loss + (wf * torch.tensor(np.asarray(dwf, np.float64))).sum()
+    loss.backward()
+    return tuple(x.grad.numpy() for x in (q_, k_, v_, e_, w_))
 
 
 def gelu(x):
