@@ -1,7 +1,7 @@
 /*
- * ttt.h -- C ABI of libttt.so, the MI355X (gfx950) forward pass of the TTT
- * (test-time training) sequence layer: TTT-Linear and TTT-MLP, mini-batch
- * dual form.
+ * ttt.h -- C ABI of libttt.so, the MI355X (gfx950) TTT (test-time training)
+ * sequence layer: the forward of TTT-Linear and TTT-MLP and the backward of
+ * TTT-Linear, mini-batch dual form.
  *
  * Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，
  * 一夜推翻Transformer" (aharts.cn / itmax.cn).
@@ -148,6 +148,54 @@ ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const v
  */
 ttt_status ttt_linear_decode(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                              const float* eta, void* Z, float* W, float* Wb, int64_t pos, void* stream);
+
+/*
+ * TTT-Linear forward for training: ttt_linear_fwd, and also
+ *   E_saved : [B,H,T,d] fp32, e_t = W k_t - v_t with W the state at the start
+ *             of t's mini-batch (the reconstruction error the gradient step
+ *             uses), which is all ttt_linear_bwd needs besides the inputs and
+ *             W_final.  Must overlap no other argument.
+ * Same support as ttt_linear_fwd; TTT_FLAG_PRIMAL is rejected (TTT_ERR_FLAGS).
+ */
+ttt_status ttt_linear_fwd_save(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                               const float* W0, const float* eta, void* Z, float* W_final, float* E_saved,
+                               void* stream);
+
+/*
+ * TTT-Linear backward ([TTT] 03 §4: the layer is trained end to end, so the
+ * gradient flows through the inner gradient steps; 03 §7: the dual form is
+ * used for the backward as well).  With L any scalar whose gradients with
+ * respect to Z and W_final are dZ and dW_final, it returns the gradients of L
+ * with respect to every input of the forward:
+ *   in : Q, K     [B,H,T,d] in_dtype (as given to the forward; V is not needed)
+ *        eta      strided as for the forward
+ *        W_final  [B,H,d,d] fp32 from ttt_linear_fwd_save
+ *        E_saved  [B,H,T,d] fp32 from ttt_linear_fwd_save
+ *        dZ       [B,H,T,d] out_dtype
+ *        dW_final [B,H,d,d] fp32, or NULL for zero
+ *   out: dQ, dK, dV [B,H,T,d] out_dtype
+ *        deta     [B,H,T] fp32, the gradient for every token's step size (sum
+ *                 it over the tokens / sequences that share an eta)
+ *        dW0      [B,H,d,d] fp32, per sequence (sum over B for a shared W0)
+ * The mini-batch-start states are rebuilt backward from W_final and E_saved
+ * (W = W' + 2 E diag(eta) K^T), so nothing else is kept from the forward.
+ * Outputs overlap no input and no other output.  flags: 0 or
+ * TTT_FLAG_GENERIC; w0_batch_stride is ignored (dW0 is always per sequence).
+ * Supported: d = 64, b = 16, bf16 Q/K on the MFMA kernel; the portable fp32
+ * kernel for d = 16 (b <= 64), d = 32 (b <= 32), d = 64 (b <= 16).
+ */
+ttt_status ttt_linear_bwd(const ttt_linear_desc* desc, const void* Q, const void* K, const float* eta,
+                          const float* W_final, const float* E_saved, const void* dZ, const float* dW_final,
+                          void* dQ, void* dK, void* dV, float* deta, float* dW0, void* stream);
+
+/* Runs every host-side check of ttt_linear_bwd and launches nothing. */
+ttt_status ttt_linear_bwd_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const float* eta,
+                                   const float* W_final, const float* E_saved, const void* dZ,
+                                   const float* dW_final, const void* dQ, const void* dK, const void* dV,
+                                   const float* deta, const float* dW0);
+
+/* Name of the kernel ttt_linear_bwd would launch for desc, or NULL if unsupported. */
+const char* ttt_linear_bwd_kernel_name(const ttt_linear_desc* desc);
 
 /* Runs every host-side check of ttt_linear_fwd and launches nothing. */
 ttt_status ttt_linear_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,

@@ -24,6 +24,9 @@ Contents
                                and residual inside f (03 §9), in C.
   linear_grads                 gradients of TTT-Linear: torch fp64 autograd
                                through the primal loop (linear_primal_torch).
+  linear_primal_grads          the same gradients by a hand-written reverse
+                               pass of the primal loop in C (fast; pinned by
+                               finite differences and against linear_grads).
   linear_dual_f64, mlp_dual_f64, linear_naive_f64, mlp_primal_np,
   linear_ln_dual_f64
                                numpy fp64 forms used only to check the oracle.
@@ -65,7 +68,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build()
     lib = ctypes.CDLL(_LIB)
     dp = ctypes.POINTER(ctypes.c_double)
@@ -76,6 +79,8 @@ def _load():
     lib.oracle_mlp_primal.restype = None
     lib.oracle_linear_ln_primal.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, dp, i]
     lib.oracle_linear_ln_primal.restype = None
+    lib.oracle_linear_primal_grads.argtypes = [i, i, i, i] + [dp] * 12 + [i]
+    lib.oracle_linear_primal_grads.restype = None
     lib.oracle_max_threads.restype = i
     _lib = lib
     return lib
@@ -109,6 +114,32 @@ def linear_primal(q, k, v, w0, eta, b: int, threads: int = 0):
         _load().oracle_linear_primal(n, T, d, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta),
                                      _ptr(z), _ptr(wf), int(threads))
     return z, wf
+
+
+def linear_primal_grads(q, k, v, w0, eta, b: int, dz, dwf=None, threads: int = 0):
+    """Gradients of  sum(dz * Z) + sum(dwf * W_final)  of TTT-Linear, by
+    reverse-mode differentiation of the primal token loop, fp64, in C.
+
+    Shapes as linear_primal; dz : [n, T, d], dwf : [n, d, d] or None.
+    returns (dq, dk, dv, deta [n, T], dw0 [n, d, d]).
+    """
+    q, k, v, w0, eta, dz = map(_f64, (q, k, v, w0, eta, dz))
+    n, T, d = q.shape
+    assert k.shape == v.shape == dz.shape == (n, T, d) and w0.shape == (n, d, d) and eta.shape == (n, T)
+    assert b >= 1
+    dwf_p = None
+    if dwf is not None:
+        dwf = _f64(dwf)
+        assert dwf.shape == (n, d, d)
+        dwf_p = _ptr(dwf)
+    dq, dk, dv = (np.empty((n, T, d)) for _ in range(3))
+    deta = np.empty((n, T))
+    dw0 = np.empty((n, d, d))
+    if n:
+        _load().oracle_linear_primal_grads(n, T, d, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta),
+                                           _ptr(dz), dwf_p, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0),
+                                           int(threads))
+    return dq, dk, dv, deta, dw0
 
 
 def mlp_primal(q, k, v, w1, w2, eta, b: int, threads: int = 0):

@@ -227,3 +227,98 @@ void oracle_linear_ln_primal(int n, int T, int d, int b,
     free(W); free(Wb); free(y); free(yh); free(g);
   }
 }
+
+/* Gradients of TTT-Linear by reverse-mode differentiation of the primal token
+ * loop above (fp64), for L = sum(dz * Z) + sum(dwf * W_final):
+ *   dq, dk, dv : [n, T, d]   deta : [n, T]   dw0 : [n, d, d]   (dwf may be NULL).
+ * The loop's states are recomputed per mini-batch from stored mini-batch-start
+ * states.  Token t of the loop does  e_t = Wb k_t - v_t,
+ * W_t = W_{t-1} - 2 eta_t e_t k_t^T,  z_t = W_t q_t  (Wb: state at the start of
+ * t's mini-batch, which is also W_{t-1} for its first token), so walking back
+ * with A = dL/dW_t:
+ *   A += dz_t q_t^T;  dq_t = W_t^T dz_t
+ *   de_t = -2 eta_t A k_t;  dk_t = -2 eta_t A^T e_t + Wb^T de_t
+ *   deta_t = -2 e_t . (A k_t);  dv_t = -de_t;  dWb += de_t k_t^T
+ * and A_{t-1} = A_t; at the mini-batch start A += dWb. */
+void oracle_linear_primal_grads(int n, int T, int d, int b,
+                                const double* q, const double* k, const double* v,
+                                const double* w0, const double* eta,
+                                const double* dz, const double* dwf,
+                                double* dq, double* dk, double* dv, double* deta, double* dw0,
+                                int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int c = 0; c < n; ++c) {
+    const size_t dd = (size_t)d * d;
+    const int nb = (T + b - 1) / b;
+    double* Wst = (double*)malloc((size_t)(nb > 0 ? nb : 1) * dd * sizeof(double));
+    double* W = (double*)malloc(dd * sizeof(double));
+    double* Wt = (double*)malloc((size_t)b * dd * sizeof(double));
+    double* E = (double*)malloc((size_t)b * d * sizeof(double));
+    double* A = (double*)malloc(dd * sizeof(double));
+    double* dWb = (double*)malloc(dd * sizeof(double));
+    double* ak = (double*)malloc((size_t)d * sizeof(double));
+    double* de = (double*)malloc((size_t)d * sizeof(double));
+    double* tmp = (double*)malloc((size_t)d * sizeof(double));
+    const double* et = eta + (size_t)c * T;
+
+    /* forward: the state at every mini-batch start */
+    memcpy(W, w0 + c * dd, dd * sizeof(double));
+    for (int mb = 0; mb < nb; ++mb) {
+      double* Wb = Wst + (size_t)mb * dd;
+      memcpy(Wb, W, dd * sizeof(double));
+      const int t0 = mb * b, t1 = t0 + b < T ? t0 + b : T;
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        matvec(Wb, k + o, tmp, d, d);
+        for (int i = 0; i < d; ++i) tmp[i] -= v[o + i];
+        rank1_sub(W, 2.0 * et[t], tmp, k + o, d, d);
+      }
+    }
+
+    /* backward */
+    if (dwf) memcpy(A, dwf + c * dd, dd * sizeof(double));
+    else memset(A, 0, dd * sizeof(double));
+    for (int mb = nb - 1; mb >= 0; --mb) {
+      const double* Wb = Wst + (size_t)mb * dd;
+      const int t0 = mb * b, t1 = t0 + b < T ? t0 + b : T;
+      /* recompute the mini-batch: e_t and W_t */
+      memcpy(W, Wb, dd * sizeof(double));
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        double* e = E + (size_t)(t - t0) * d;
+        matvec(Wb, k + o, e, d, d);
+        for (int i = 0; i < d; ++i) e[i] -= v[o + i];
+        rank1_sub(W, 2.0 * et[t], e, k + o, d, d);
+        memcpy(Wt + (size_t)(t - t0) * dd, W, dd * sizeof(double));
+      }
+      memset(dWb, 0, dd * sizeof(double));
+      for (int t = t1 - 1; t >= t0; --t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        const double* e = E + (size_t)(t - t0) * d;
+        const double* Wc = Wt + (size_t)(t - t0) * dd;
+        matvec_t(Wc, dz + o, dq + o, d, d);               /* dq_t = W_t^T dz_t */
+        rank1_sub(A, -1.0, dz + o, q + o, d, d);          /* A += dz_t q_t^T   */
+        matvec(A, k + o, ak, d, d);                       /* A k_t             */
+        double s = 0.0;
+        for (int i = 0; i < d; ++i) {
+          de[i] = -2.0 * et[t] * ak[i];
+          s += e[i] * ak[i];
+        }
+        deta[(size_t)c * T + t] = -2.0 * s;
+        matvec_t(A, e, dk + o, d, d);                     /* A^T e_t           */
+        matvec_t(Wb, de, tmp, d, d);                      /* Wb^T de_t         */
+        for (int i = 0; i < d; ++i) {
+          dk[o + i] = -2.0 * et[t] * dk[o + i] + tmp[i];
+          dv[o + i] = -de[i];
+        }
+        rank1_sub(dWb, -1.0, de, k + o, d, d);            /* dWb += de_t k_t^T */
+      }
+      for (size_t x = 0; x < dd; ++x) A[x] += dWb[x];
+    }
+    memcpy(dw0 + c * dd, A, dd * sizeof(double));
+    free(Wst); free(W); free(Wt); free(E); free(A); free(dWb); free(ak); free(de); free(tmp);
+  }
+}

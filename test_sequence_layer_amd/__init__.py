@@ -1,4 +1,4 @@
-"""MI355X (gfx950) forward pass of the TTT sequence layer -- Python binding.
+"""MI355X (gfx950) TTT sequence layer (forward, and the TTT-Linear backward) -- Python binding.
 
 Thin ctypes layer over libttt.so (C ABI in include/ttt.h).  It only checks and
 marshals arguments: torch supplies device memory and the current HIP stream,
@@ -8,6 +8,8 @@ no CPU or PyTorch fallback: if libttt.so is missing, importing the ops raises.
     import test_sequence_layer_amd as ttt
     z, w_final = ttt.linear_fwd(q, k, v, w0, eta, b=16)
     z, w1_final, w2_final = ttt.mlp_fwd(q, k, v, w1, w2, eta, b=16)
+    z, w_final, e = ttt.linear_fwd_save(q, k, v, w0, eta, b=16)          # training
+    dq, dk, dv, deta, dw0 = ttt.linear_bwd(q, k, eta, w_final, e, dz, b=16)
 
 Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，一夜推翻Transformer"
 (aharts.cn / itmax.cn), part 03 §1-§9 (the TTT layer, mini-batch GD, the dual
@@ -38,6 +40,7 @@ EXPORTS = (
     "ttt_linear_fwd", "ttt_linear_validate", "ttt_linear_kernel_name",
     "ttt_linear_decode", "ttt_linear_decode_validate",
     "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes", "ttt_linear_ln_fwd",
+    "ttt_linear_fwd_save", "ttt_linear_bwd", "ttt_linear_bwd_validate", "ttt_linear_bwd_kernel_name",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name",
     "ttt_status_str", "ttt_abi_version",
 )
@@ -99,6 +102,15 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_ln_fwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, fp, vp, fp,
                                     vp]
     L.ttt_linear_ln_fwd.restype = ctypes.c_int
+    L.ttt_linear_fwd_save.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, vp, fp, fp, vp]
+    L.ttt_linear_fwd_save.restype = ctypes.c_int
+    L.ttt_linear_bwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, vp]
+    L.ttt_linear_bwd.restype = ctypes.c_int
+    L.ttt_linear_bwd_validate.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp,
+                                          fp]
+    L.ttt_linear_bwd_validate.restype = ctypes.c_int
+    L.ttt_linear_bwd_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
+    L.ttt_linear_bwd_kernel_name.restype = ctypes.c_char_p
     L.ttt_linear_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
     L.ttt_linear_kernel_name.restype = ctypes.c_char_p
     L.ttt_mlp_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp, vp]
@@ -222,6 +234,97 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
     if st != TTT_OK:
         raise TTTError(st, "ttt_linear_fwd")
     return z, w_final
+
+
+def linear_fwd_save(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None, e_saved=None,
+                    generic: bool = False, stream=None):
+    """TTT-Linear forward for training: :func:`linear_fwd` plus the saved
+    reconstruction errors E [B, H, T, d] float32 (e_t = W k_t - v_t at the
+    mini-batch-start W) that :func:`linear_bwd` needs.
+
+    returns (Z, W_final, E).
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    if w0.dtype != torch.float32:
+        raise TypeError("w0 must be float32")
+    wstride = _w0_stride(w0, B, H, d)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    if w_final is None:
+        w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    if e_saved is None:
+        e_saved = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    _check_dev(q, k, v, w0, eta_t, z, w_final, e_saved)
+    flags = TTT_FLAG_GENERIC if generic else 0
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, flags)
+    st = lib().ttt_linear_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta_t),
+                                   _ptr(z), _ptr(w_final), _ptr(e_saved), _stream_handle(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_fwd_save")
+    return z, w_final, e_saved
+
+
+def linear_bwd(q, k, eta, w_final, e_saved, dz, b: int, dw_final=None, generic: bool = False, out=None,
+               stream=None):
+    """TTT-Linear backward (dual form).
+
+    q, k     : the forward's [B, H, T, d] inputs (v is not needed)
+    eta      : as given to the forward
+    w_final, e_saved : from :func:`linear_fwd_save`
+    dz       : [B, H, T, d] gradient of the loss with respect to Z (its dtype
+               is the dtype of dq, dk, dv)
+    dw_final : [B, H, d, d] float32 gradient with respect to W_final, or None (zero)
+    out      : optional (dq, dk, dv, deta, dw0) preallocated outputs
+    returns (dq, dk, dv, deta [B, H, T] per token, dw0 [B, H, d, d] per sequence).
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q, k must have the same shape and dtype")
+    if dz.shape != q.shape or tuple(e_saved.shape) != tuple(q.shape) or tuple(w_final.shape) != (B, H, d, d):
+        raise ValueError("dz, e_saved must be [B, H, T, d] and w_final [B, H, d, d]")
+    if e_saved.dtype != torch.float32 or w_final.dtype != torch.float32:
+        raise TypeError("e_saved and w_final must be float32")
+    if dw_final is not None and (tuple(dw_final.shape) != (B, H, d, d) or dw_final.dtype != torch.float32):
+        raise ValueError("dw_final must be [B, H, d, d] float32")
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if out is None:
+        dev = q.device
+        out = (torch.empty((B, H, T, d), dtype=dz.dtype, device=dev),
+               torch.empty((B, H, T, d), dtype=dz.dtype, device=dev),
+               torch.empty((B, H, T, d), dtype=dz.dtype, device=dev),
+               torch.empty((B, H, T), dtype=torch.float32, device=dev),
+               torch.empty((B, H, d, d), dtype=torch.float32, device=dev))
+    dq, dk, dv, deta, dw0 = out
+    _check_dev(q, k, eta_t, w_final, e_saved, dz, dw_final, dq, dk, dv, deta, dw0)
+    flags = TTT_FLAG_GENERIC if generic else 0
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(dz.dtype), 0, est, flags)
+    st = lib().ttt_linear_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(eta_t), _ptr(w_final), _ptr(e_saved),
+                              _ptr(dz), _ptr(dw_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0),
+                              _stream_handle(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_bwd")
+    return dq, dk, dv, deta, dw0
+
+
+def linear_bwd_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),
+                           generic=False) -> Optional[str]:
+    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_GENERIC if generic else 0)
+    name = lib().ttt_linear_bwd_kernel_name(ctypes.byref(desc))
+    return None if name is None else name.decode()
+
+
+def _w0_stride(w0, B, H, d) -> int:
+    if tuple(w0.shape) == (H, d, d):
+        return 0
+    if tuple(w0.shape) == (B, H, d, d):
+        return H * d * d
+    raise ValueError(f"w0 shape {tuple(w0.shape)}: expected [H,d,d] or [B,H,d,d]")
 
 
 def linear_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),

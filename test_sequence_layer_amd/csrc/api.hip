@@ -57,6 +57,7 @@ ttt::LinearArgs make_linear_args(const ttt_linear_desc* d, const void* Q, const 
   a.Z = const_cast<void*>(Z); a.Wf = const_cast<float*>(Wf);
   a.nchunk = 1; a.Tc = d->T; a.Wstart = nullptr; a.maps = nullptr;
   a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
+  a.Esave = nullptr;
   return a;
 }
 
@@ -161,6 +162,80 @@ ttt_status validate_decode(const ttt_linear_desc* d, const void* Q, const void* 
     for (Range in : {rq, rk, rv, re})
       if (overlaps(out, in)) return TTT_ERR_ALIAS;
   if (overlaps(rz, rw) || overlaps(rz, rwb) || overlaps(rw, rwb)) return TTT_ERR_ALIAS;
+  return TTT_OK;
+}
+
+// ----------------------------------------------------------- backward --
+
+enum BwdKernel { KB_NONE, KB_GENERIC, KB_MFMA };
+
+ttt::BwdArgs make_bwd_args(const ttt_linear_desc* d, const void* Q, const void* K, const float* eta,
+                           const float* Wf, const float* E, const void* dZ, const float* dWf, void* dQ, void* dK,
+                           void* dV, float* deta, float* dW0) {
+  ttt::BwdArgs a;
+  a.B = d->B; a.H = d->H; a.T = d->T; a.d = d->d; a.b = d->b;
+  a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype;
+  a.Q = Q; a.K = K;
+  a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
+  a.Wf = Wf; a.E = E; a.dZ = dZ; a.dWf = dWf;
+  a.dQ = dQ; a.dK = dK; a.dV = dV; a.deta = deta; a.dW0 = dW0;
+  return a;
+}
+
+BwdKernel pick_bwd(const ttt::BwdArgs& a, uint32_t flags) {
+  if (!(flags & TTT_FLAG_GENERIC) && ttt::linear_bwd_mfma_supported(a)) return KB_MFMA;
+  if (ttt::linear_bwd_generic_supported(a.d, a.b)) return KB_GENERIC;
+  return KB_NONE;
+}
+
+ttt_status validate_bwd(const ttt_linear_desc* d, const void* Q, const void* K, const float* eta, const float* Wf,
+                        const float* E, const void* dZ, const float* dWf, const void* dQ, const void* dK,
+                        const void* dV, const float* deta, const float* dW0, BwdKernel* which) {
+  if (which) *which = KB_NONE;
+  if (!d) return TTT_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->b < 1) return TTT_ERR_SHAPE;
+  if (d->T % d->b != 0) return TTT_ERR_SHAPE;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
+  if (d->flags & ~static_cast<uint32_t>(TTT_FLAG_GENERIC)) return TTT_ERR_FLAGS;
+  if (d->w0_batch_stride != 0 && d->w0_batch_stride != static_cast<int64_t>(d->H) * d->d * d->d)
+    return TTT_ERR_STRIDE;
+  if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
+  int64_t chains = 1, tok = 1, wel = 1;
+  if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
+  tok = chains;
+  if (!mul_ok(tok, d->T) || !mul_ok(tok, d->d)) return TTT_ERR_SHAPE;
+  wel = chains;
+  if (!mul_ok(wel, d->d) || !mul_ok(wel, d->d)) return TTT_ERR_SHAPE;
+  const ttt::BwdArgs a = make_bwd_args(d, Q, K, eta, Wf, E, dZ, dWf, nullptr, nullptr, nullptr, nullptr, nullptr);
+  const BwdKernel k = pick_bwd(a, d->flags);
+  if (k == KB_NONE) return TTT_ERR_UNSUPPORTED;
+  if (chains == 0) {
+    if (which) *which = k;
+    return TTT_OK;
+  }
+  if (!Wf || !dW0) return TTT_ERR_NULL;
+  if (tok > 0 && (!Q || !K || !eta || !E || !dZ || !dQ || !dK || !dV || !deta)) return TTT_ERR_NULL;
+  if (!aligned(Wf, 16) || !aligned(dW0, 16) || (dWf && !aligned(dWf, 16))) return TTT_ERR_ALIGN;
+  if (tok > 0) {
+    for (const void* p : {Q, K, static_cast<const void*>(E), dZ, dQ, dK, dV})
+      if (!aligned(p, 16)) return TTT_ERR_ALIGN;
+    if (!aligned(eta, 4) || !aligned(deta, 4)) return TTT_ERR_ALIGN;
+  }
+  const int64_t in_b = tok * dtype_size(d->in_dtype);
+  const int64_t g_b = tok * dtype_size(d->out_dtype);
+  const int64_t w_b = wel * 4;
+  const int64_t eta_b =
+      tok > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const int64_t deta_b = tok > 0 ? chains * d->T * 4 : 0;
+  const Range ins[] = {{Q, in_b}, {K, in_b}, {eta, eta_b}, {Wf, w_b}, {E, tok * 4}, {dZ, g_b}, {dWf, w_b}};
+  const Range outs[] = {{dQ, g_b}, {dK, g_b}, {dV, g_b}, {deta, deta_b}, {dW0, w_b}};
+  for (int i = 0; i < 5; ++i) {
+    for (const Range& in : ins)
+      if (overlaps(outs[i], in)) return TTT_ERR_ALIAS;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_ALIAS;
+  }
+  if (which) *which = k;
   return TTT_OK;
 }
 
@@ -287,6 +362,68 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
     e = ttt::launch_linear_primal(make_primal_args_fwd(desc, Q, K, V, W0, eta, Z, W_final), s);
   else
     e = ttt::launch_linear_generic(a, s);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_linear_fwd_save(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                               const float* W0, const float* eta, void* Z, float* W_final, float* E_saved,
+                               void* stream) {
+  Kernel k;
+  const ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
+  if (st != TTT_OK) return st;
+  if (desc->flags & TTT_FLAG_PRIMAL) return TTT_ERR_FLAGS;
+  const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
+  if (chains == 0) return TTT_OK;
+  const int64_t tok = chains * desc->T * desc->d;
+  if (tok > 0) {
+    if (!E_saved) return TTT_ERR_NULL;
+    if (!aligned(E_saved, 16)) return TTT_ERR_ALIGN;
+    const int64_t in_b = tok * dtype_size(desc->in_dtype), z_b = tok * dtype_size(desc->out_dtype);
+    const int64_t hdd = static_cast<int64_t>(desc->H) * desc->d * desc->d;
+    const int64_t w0_b = (desc->w0_batch_stride == 0 ? hdd : chains * desc->d * desc->d) * 4;
+    const int64_t eta_b =
+        eta_extent(desc->B, desc->H, desc->T, desc->eta_stride_b, desc->eta_stride_h, desc->eta_stride_t) * 4;
+    const Range re{E_saved, tok * 4};
+    for (Range r : {Range{Q, in_b}, Range{K, in_b}, Range{V, in_b}, Range{eta, eta_b}, Range{W0, w0_b},
+                    Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
+      if (overlaps(re, r)) return TTT_ERR_ALIAS;
+  }
+  ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
+  a.Esave = tok > 0 ? E_saved : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = k == K_MFMA ? ttt::launch_linear_mfma(a, s) : ttt::launch_linear_generic(a, s);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_linear_bwd_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const float* eta,
+                                   const float* W_final, const float* E_saved, const void* dZ,
+                                   const float* dW_final, const void* dQ, const void* dK, const void* dV,
+                                   const float* deta, const float* dW0) {
+  return validate_bwd(desc, Q, K, eta, W_final, E_saved, dZ, dW_final, dQ, dK, dV, deta, dW0, nullptr);
+}
+
+const char* ttt_linear_bwd_kernel_name(const ttt_linear_desc* d) {
+  if (!d) return nullptr;
+  const ttt::BwdArgs a = make_bwd_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, nullptr, nullptr, nullptr);
+  switch (pick_bwd(a, d->flags)) {
+    case KB_MFMA: return "ttt_linear_bwd_d64b16";
+    case KB_GENERIC: return ttt::linear_bwd_generic_name(a.d);
+    default: return nullptr;
+  }
+}
+
+ttt_status ttt_linear_bwd(const ttt_linear_desc* desc, const void* Q, const void* K, const float* eta,
+                          const float* W_final, const float* E_saved, const void* dZ, const float* dW_final,
+                          void* dQ, void* dK, void* dV, float* deta, float* dW0, void* stream) {
+  BwdKernel k;
+  const ttt_status st =
+      validate_bwd(desc, Q, K, eta, W_final, E_saved, dZ, dW_final, dQ, dK, dV, deta, dW0, &k);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  const ttt::BwdArgs a = make_bwd_args(desc, Q, K, eta, W_final, E_saved, dZ, dW_final, dQ, dK, dV, deta, dW0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = k == KB_MFMA ? ttt::launch_linear_bwd_mfma(a, s) : ttt::launch_linear_bwd_generic(a, s);
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

@@ -9,7 +9,7 @@
 // implementation against which the MFMA kernel is cross-checked.
 //
 // Per mini-batch of b tokens (token-major rows; W row i = output i):
-//   E[t][i]  = sum_c W[i][c] K[t][c] - V[t][i]
+//   E[t][i]  = sum_c W[i][c] K[t][c] - V[t][i]   (also written out when saved for the backward)
 //   L[t][s]  = 2 eta_s (q_t . k_s)           for s <= t, else 0
 //   Z[t][i]  = sum_c W[i][c] Q[t][c] - sum_s L[t][s] E[s][i]
 //   W[i][c] -= sum_s 2 eta_s E[s][i] K[s][c]
@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_generic_kernel(LinearArgs
           pq = fmaf(W[i][c], Qs[t][c], pq);
         }
         Es[t][i] = pk - Es[t][i];
+        if (a.Esave) a.Esave[base + static_cast<size_t>(t0) * D + x] = Es[t][i];
         zq[j] = pq;
       }
     }

@@ -46,16 +46,12 @@
 // stores the tile one step ahead into a double-buffered LDS slot, and issues
 // one barrier.  The update's K^T operand and E's V values are column reads of
 // the row-major tiles with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
-#include "ttt_internal.h"
+#include "mfma_common.h"
 
 namespace ttt {
 namespace {
 
-typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float float4v __attribute__((__vector_size__(4 * sizeof(float))));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace mfma;
 
 constexpr int D = 64;       // head dim
 constexpr int BT = 16;      // mini-batch (tokens)
@@ -70,99 +66,10 @@ struct __align__(16) Slot {
 };
 static_assert(sizeof(Slot) % 16 == 0, "slot size");
 
-__device__ __forceinline__ float4v mfma32(bf16x8 a, bf16x8 b, float4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-typedef short short4v __attribute__((__vector_size__(4 * sizeof(short))));
-
-// Column read of a row-major bf16 tile (row stride ROW): lane l gets
-// X[row0 + 4(l/16) + r][col0 + l%16] for r = 0..3.  ds_read_b64_tr_b16 works on
-// blocks of 16 lanes: output lane i receives element r from the 8-byte chunk
-// addressed by lane 4r + i/4 of its block, position i%4; so lane j of block g
-// addresses row row0 + 4g + j/4, columns col0 + 4(j%4) .. +3.
-__device__ __forceinline__ bf16x4 read_cols(const uint16_t* tile, int row0, int col0, int li, int g) {
-  const uint16_t* p = tile + (row0 + 4 * g + (li >> 2)) * ROW + col0 + 4 * (li & 3);
-  typedef short4v __attribute__((address_space(3))) * lds_short4v_ptr;
-  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v_ptr)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
-typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
-typedef float float2v __attribute__((__vector_size__(2 * sizeof(float))));
-
-// Two fp32 values -> packed bf16 hi pair and lo pair, x ~= hi + lo.  One
-// v_cvt_pk_bf16_f32 rounds both hi values (nearest even); they are widened back
-// with a shift and a mask, and the exact residuals are rounded into lo.
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = __builtin_convertvector(float2v{x0, x1}, bf16x2);
-  hi = __builtin_bit_cast(uint32_t, h);
-  const float h0 = __uint_as_float(hi << 16);
-  const float h1 = __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{x0 - h0, x1 - h1}, bf16x2));
-}
-
-__device__ __forceinline__ void split4(const float x[4], bf16x4& hi, bf16x4& lo) {
-  uint32_t h[2], l[2];
-  split2(x[0], x[1], h[0], l[0]);
-  split2(x[2], x[3], h[1], l[1]);
-  hi = __builtin_bit_cast(bf16x4, h);
-  lo = __builtin_bit_cast(bf16x4, l);
-}
-
-__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-#ifndef TTT_LINEAR_NT
-#define TTT_LINEAR_NT 1
-#endif
-// Q/K/V and Z are touched exactly once: mark them as streaming (non-temporal)
-// so they do not evict each other from the caches (about 15% at the 1.3B shape).
-template <typename T>
-__device__ __forceinline__ T ld_stream(const T* p) {
-  if constexpr (TTT_LINEAR_NT) {
-    return __builtin_nontemporal_load(p);
-  } else {
-    return *p;
-  }
-}
-template <typename T>
-__device__ __forceinline__ void st_stream(T* p, T x) {
-  if constexpr (TTT_LINEAR_NT) {
-    __builtin_nontemporal_store(x, p);
-  } else {
-    *p = x;
-  }
-}
-
-template <typename OutT>
-__device__ __forceinline__ void store_z(OutT* p, float x);
-template <>
-__device__ __forceinline__ void store_z<float>(float* p, float x) { st_stream(p, x); }
-template <>
-__device__ __forceinline__ void store_z<uint16_t>(uint16_t* p, float x) { st_stream(p, f32_to_bf16_bits(x)); }
-
 // ---- layer norm across the row-split waves --------------------------------
 // A token's 64 outputs are spread over the 4 waves (16 each, at lanes l%16 of
-// lane group l/16 = token / 4).  Sums over a wave's 16 outputs use xor
-// shuffles inside the 16-lane group; the 4 wave partials meet in LDS.
-// Data-parallel-primitive (DPP) lane moves inside a 16-lane row: quad_perm
-// [1,0,3,2] and [2,3,0,1] exchange neighbours 1 and 2 apart; row_half_mirror
-// (lane i <-> 7 - i within 8) and row_mirror (i <-> 15 - i) then fold the
-// quads, so after four adds every lane of the row holds the row's sum.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_mov<0x141>(x);  // row_half_mirror
-  x += dpp_mov<0x140>(x);  // row_mirror
-  return x;
-}
-
+// lane group l/16 = token / 4).  Sums over a wave's 16 outputs are DPP
+// reductions inside the 16-lane row (sum16); the 4 wave partials meet in LDS.
 struct LnShared {
   float2 part[3][4][BT];  // [exchange][wave][token]
 };
@@ -203,7 +110,8 @@ __device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs
 // chunked forward -- the state recurrence from I with V = 0 / from 0 with V,
 // over one chunk, with no query path and no Z.
 // LN: f(x) = x + LN(W x) (layer norm and residual inside f; MODE 0 only).
-template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN>
+// SAVE: also write E = W K - V of every token (the backward's input; MODE 0, no LN).
+template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN, bool SAVE = false>
 __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a) {
   __shared__ Slot slots[2];
   __shared__ LnShared lns;
@@ -367,8 +275,8 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
       float mu[4], rs[4], yh[4], gr[4], s1[4], s2[4];
       const float yk[4] = {pk[0], pk[1], pk[2], pk[3]};
       ln_stats(yk, mu, rs, lns.part[0], w, li, g, a.eps);
-      const bf16x4 vc = read_cols(S.v, 0, 16 * w, li, g);   // V[4g + r][16w + li]
-      const bf16x4 kc = read_cols(S.k, 0, 16 * w, li, g);   // K[4g + r][16w + li]
+      const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * w, li, g);   // V[4g + r][16w + li]
+      const bf16x4 kc = read_cols<ROW>(S.k, 0, 16 * w, li, g);   // K[4g + r][16w + li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         yh[r] = (pk[r] - mu[r]) * rs[r];
@@ -399,9 +307,14 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) e[r] = pk[r];  // V = 0
       } else {
-        const bf16x4 vc = read_cols(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
+        const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
 #pragma unroll
         for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
+      }
+      if constexpr (SAVE) {
+        float* ep = a.Esave + (tok0 + static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st_stream(ep + r * D, e[r]);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) gv[r] = -2.f * et[r] * e[r];
@@ -429,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     const bf16x8 gb = cat(bhi, blo);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x4 kt = read_cols(S.k, 0, 16 * t, li, g);  // K[4g + r][16t + li]
+      const bf16x4 kt = read_cols<ROW>(S.k, 0, 16 * t, li, g);  // K[4g + r][16t + li]
       wt[t] = mfma32(cat(kt, kt), gb, wt[t]);
     }
 
@@ -440,14 +353,14 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) zz[r] = z[r];
       ln_stats(zz, mu, rs, lns.part[2], w, li, g, a.eps);
-      const bf16x4 qc = read_cols(S.q, 0, 16 * w, li, g);  // Q[4g + r][16w + li]
+      const bf16x4 qc = read_cols<ROW>(S.q, 0, 16 * w, li, g);  // Q[4g + r][16w + li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qc[r]) + ln_g * (zz[r] - mu[r]) * rs[r] + ln_b;
     }
     if constexpr (MODE == 0) {
       OutT* zp = Zg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) store_z<OutT>(zp + r * D, z[r]);
+      for (int r = 0; r < 4; ++r) store_out<OutT>(zp + r * D, z[r]);
     }
 
     __syncthreads();
@@ -488,6 +401,15 @@ constexpr int kPF = TTT_LINEAR_PF;  // prefetch distance (mini-batches in flight
 template <bool TOK, bool LN>
 hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
   dim3 grid(a.B * a.H * a.nchunk), block(kThreads);
+  if constexpr (!LN) {
+    if (a.Esave) {
+      if (a.out_dtype == 0)
+        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 0, false, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t, 0, false, true>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (a.out_dtype == 0)
     hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 0, LN>), grid, block, 0, s, a);
   else

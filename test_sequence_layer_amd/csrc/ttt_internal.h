@@ -28,7 +28,34 @@ struct LinearArgs {
   const float* gamma;   // [H][d]
   const float* beta;    // [H][d]
   float eps;
+  // Forward for training: also write E[t] = W_{mini-batch start} k_t - v_t
+  // ([chains][T][d] fp32) for the backward; nullptr: not saved.
+  float* Esave;
 };
+
+// Backward of TTT-Linear (plain f(x) = W x) from the saved E and the final state.
+struct BwdArgs {
+  int B, H, T, d, b;
+  int in_dtype, out_dtype;   // Q/K dtype; dZ and dQ/dK/dV dtype
+  const void* Q;
+  const void* K;
+  const float* eta;
+  int64_t esb, esh, est;
+  const float* Wf;           // [chains][d][d] state after the last mini-batch
+  const float* E;            // [chains][T][d] saved by the forward
+  const void* dZ;            // [chains][T][d]
+  const float* dWf;          // [chains][d][d] or nullptr (zero)
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* deta;               // [chains][T]
+  float* dW0;                // [chains][d][d]
+};
+bool linear_bwd_mfma_supported(const BwdArgs& a);
+hipError_t launch_linear_bwd_mfma(const BwdArgs& a, hipStream_t s);
+bool linear_bwd_generic_supported(int d, int b);
+const char* linear_bwd_generic_name(int d);
+hipError_t launch_linear_bwd_generic(const BwdArgs& a, hipStream_t s);
 
 struct MlpArgs {
   int B, H, T, d, dh, b;

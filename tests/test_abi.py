@@ -196,3 +196,58 @@ def test_chunked_workspace_bytes():
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 8) == 64 * (7 * 2 + 8) * 64 * 64 * 4
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 0) == -1
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(None, 4) == -1
+
+
+# ---- backward validation ----------------------------------------------------------
+
+class BwdBufs:
+    """Fake aligned, disjoint device addresses for the backward's 12 tensors."""
+
+    NAMES = ("q", "k", "eta", "wf", "e", "dz", "dwf", "dq", "dk", "dv", "deta", "dw0")
+
+    def __init__(self):
+        for i, n in enumerate(self.NAMES):
+            setattr(self, n, (i + 1) * GB)
+
+    def args(self):
+        return tuple(getattr(self, n) for n in self.NAMES)
+
+
+def _bval(desc, **over):
+    bufs = BwdBufs()
+    for k, v in over.items():
+        setattr(bufs, k, v)
+    return ttt.lib().ttt_linear_bwd_validate(ctypes.byref(desc), *bufs.args())
+
+
+def test_bwd_validation():
+    assert _bval(_desc()) == OK
+    assert _bval(_desc(est=(4 * 64, 64, 1))) == OK
+    assert _bval(_desc(ind=0, d=16, b=4)) == OK
+    assert _bval(_desc(), dwf=None) == OK                     # dW_final is optional
+    assert ttt.lib().ttt_linear_bwd_validate(None, *BwdBufs().args()) == NULL
+    for name in ("q", "k", "eta", "wf", "e", "dz", "dq", "dk", "dv", "deta", "dw0"):
+        assert _bval(_desc(), **{name: None}) == NULL, name
+    assert _bval(_desc(T=60)) == SHAPE
+    assert _bval(_desc(flags=ttt.TTT_FLAG_PRIMAL)) == FLAGS   # no primal backward
+    assert _bval(_desc(d=48)) == UNSUP
+    assert _bval(_desc(d=64, b=32, ind=0)) == UNSUP           # generic backward: d = 64 needs b <= 16
+    assert _bval(_desc(), e=1 * GB + 8) == ALIGN
+    assert _bval(_desc(), dv=1 * GB) == ALIAS                 # output over an input
+    assert _bval(_desc(), dk=8 * GB + 64) == ALIAS            # output over another output
+    assert _bval(_desc(B=0)) == OK
+    assert _bval(_desc(T=0), q=None, k=None, e=None, dz=None, dq=None, dk=None, dv=None, deta=None) == OK
+
+
+def test_bwd_kernel_selection():
+    assert ttt.linear_bwd_kernel_name(16, 32, 8192, 64, 16) == "ttt_linear_bwd_d64b16"
+    assert ttt.linear_bwd_kernel_name(16, 32, 8192, 64, 16, generic=True) == "ttt_linear_bwd_generic_kernel<64>"
+    assert ttt.linear_bwd_kernel_name(1, 1, 64, 16, 4, in_dtype=ttt.TTT_F32) == "ttt_linear_bwd_generic_kernel<16>"
+    assert ttt.linear_bwd_kernel_name(1, 1, 64, 64, 32) is None
+
+
+def test_fwd_save_rejects_primal():
+    desc = _desc(flags=ttt.TTT_FLAG_PRIMAL)
+    b = Bufs()
+    st = ttt.lib().ttt_linear_fwd_save(ctypes.byref(desc), *b.args(), 9 * GB, None)
+    assert st == FLAGS

@@ -73,3 +73,57 @@ def test_dv_of_final_state():
     dwf = np.random.default_rng(8).standard_normal((1, 4, 4))
     _, _, dv, _, _ = oracle.linear_grads(q, k, v, np.zeros((1, 4, 4)), eta, 8, np.zeros((1, 8, 4)), dwf)
     np.testing.assert_allclose(dv[0], 2.0 * eta[0][:, None] * (k[0] @ dwf[0].T), atol=1e-14)
+
+
+# ---- the C reverse pass (used at full size) ----------------------------------------
+
+@pytest.mark.parametrize("n,T,d,b", [(2, 12, 4, 4), (1, 10, 3, 4), (3, 7, 5, 1), (2, 16, 8, 16), (1, 33, 6, 8)])
+def test_c_reverse_pass_matches_autograd(n, T, d, b):
+    q, k, v, w0, eta = _rand(10 + T + b, n, T, d)
+    r = np.random.default_rng(11)
+    dz, dwf = r.standard_normal((n, T, d)), r.standard_normal((n, d, d))
+    a = oracle.linear_grads(q, k, v, w0, eta, b, dz, dwf)
+    c = oracle.linear_primal_grads(q, k, v, w0, eta, b, dz, dwf)
+    for x, y in zip(a, c):
+        np.testing.assert_allclose(y, x, rtol=1e-11, atol=1e-12)
+    a0 = oracle.linear_grads(q, k, v, w0, eta, b, dz)
+    c0 = oracle.linear_primal_grads(q, k, v, w0, eta, b, dz)
+    for x, y in zip(a0, c0):
+        np.testing.assert_allclose(y, x, rtol=1e-11, atol=1e-12)
+
+
+def test_c_reverse_pass_finite_differences():
+    """Central differences of the C forward (oracle_linear_primal), entry by entry."""
+    n, T, d, b = 1, 6, 3, 4
+    q, k, v, w0, eta = _rand(12, n, T, d)
+    r = np.random.default_rng(13)
+    dz, dwf = r.standard_normal((n, T, d)), r.standard_normal((n, d, d))
+
+    def loss(q_, k_, v_, w_, e_):
+        z, wf = oracle.linear_primal(q_, k_, v_, w_, e_, b)
+        return float((z * dz).sum() + (wf * dwf).sum())
+
+    grads = oracle.linear_primal_grads(q, k, v, w0, eta, b, dz, dwf)
+    ins = [q, k, v, eta, w0]
+    h = 1e-6
+    for which, g in enumerate(grads):
+        x = ins[which]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if j == which else ins[j] for j in range(5)]
+            args_m = [xm if j == which else ins[j] for j in range(5)]
+            fd[idx] = (loss(args_p[0], args_p[1], args_p[2], args_p[4], args_p[3]) -
+                       loss(args_m[0], args_m[1], args_m[2], args_m[4], args_m[3])) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_c_reverse_pass_dual_form_single_minibatch():
+    """b = T (one mini-batch), W0 = 0, dZ = 0: E = -V, so W_final = 2 V diag(eta) K^T is
+    linear in V and dV_s = 2 eta_s dWf k_s whatever Q."""
+    q, k, v, _, eta = _rand(14, 2, 8, 5)
+    dwf = np.random.default_rng(15).standard_normal((2, 5, 5))
+    _, _, dv, _, _ = oracle.linear_primal_grads(q, k, v, np.zeros((2, 5, 5)), eta, 8, np.zeros((2, 8, 5)), dwf)
+    np.testing.assert_allclose(dv, 2.0 * eta[:, :, None] * np.einsum("nij,ntj->nti", dwf, k), atol=1e-14)

@@ -25,6 +25,9 @@ Recipe (identical bits on both sides):
   * W0 (or W1, W2) ~ N(0, 0.02^2) per head, fp64 -> fp32.  W0 is [H, d, d],
     row-major, shared by every sequence of the batch; z = W q.
   * eta as listed; per-token g ~ N(0, 1) per chain, eta = fp32(sigmoid(g)/d).
+  * Backward: upstream gradients dZ ~ N(0, 1) per element ([n, T, d], fp32,
+    or rounded to bf16) and dW_final ~ N(0, 1) ([n, d, d], fp32), each chain
+    with its own stream as above.
 
 Layouts: Q, K, V are [B, H, T, d] (token-major).  eta is described by a
 buffer plus element strides (stride_b, stride_h, stride_t).
@@ -38,6 +41,7 @@ import numpy as np
 
 # tensor ids used in the stream keys
 _TID_Q, _TID_K, _TID_V, _TID_W1, _TID_W2, _TID_G = 0, 1, 2, 3, 4, 5
+_TID_DZ, _TID_DWF = 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -185,6 +189,26 @@ def generate(cfg: Config, chains: Optional[Sequence[int]] = None) -> Inputs:
     else:
         raise ValueError(cfg.eta_kind)
     return Inputs(cfg, chains, q, k, v, w1, w2, eta_buf, strides)
+
+
+def upstream_grads(cfg: Config, chains: Optional[Sequence[int]] = None, dtype: str = "fp32",
+                   dwf_scale: float = 1.0):
+    """Seeded gradients of a loss with respect to Z and W_final, for the backward.
+
+    returns (dz [n, T, d] fp32 holding the stored values -- bf16-rounded when
+    dtype == "bf16" --, dwf [n, d, d] fp32 scaled by dwf_scale).
+    """
+    if chains is None:
+        chains = np.arange(cfg.chains)
+    chains = np.asarray(chains, dtype=np.int64)
+    n, T, d = len(chains), cfg.T, cfg.d
+    dz = np.empty((n, T, d), np.float32)
+    dwf = np.empty((n, d, d), np.float32)
+    for i, c in enumerate(chains):
+        x = _rng(cfg.seed, _TID_DZ, int(c)).standard_normal((T, d)).astype(np.float32)
+        dz[i] = bf16_round(x)[0] if dtype == "bf16" else x
+        dwf[i] = (_rng(cfg.seed, _TID_DWF, int(c)).standard_normal((d, d)) * dwf_scale).astype(np.float32)
+    return dz, dwf
 
 
 def sample_chains(cfg: Config, count: int, seed: int = 7) -> np.ndarray:
