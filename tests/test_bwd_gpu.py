@@ -58,10 +58,16 @@ def _oracle(cfg, chains, grad_dtype="fp32", with_dwf=True, dwf_scale=1.0):
     return dict(zip(NAMES, ref))
 
 
+# bf16 outputs (dq, dk, dv when dZ is bf16): rounding to 8 significant bits
+# alone is up to 2^-8 relative, plus the kernel's own error
+BF16_OUT_TOL = 2.0 ** -8 + 2e-4
+
+
 def _compare(got, ref, chains, tol, label):
     errs = {n: max_rel(rows(got[n], chains), ref[n]) for n in NAMES}
     print(f"[bwd {label}] " + " ".join(f"{n}={errs[n]:.2e}" for n in NAMES), flush=True)
-    bad = {n: e for n, e in errs.items() if not e < tol}
+    tols = {n: (BF16_OUT_TOL if got[n].dtype == torch.bfloat16 else tol) for n in NAMES}
+    bad = {n: e for n, e in errs.items() if not e < tols[n]}
     assert not bad, bad
     return errs
 
