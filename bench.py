@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark: TTT-Linear dual-form forward on one MI355X.
+"""Benchmark: TTT-Linear dual-form forward on one MI355X (and, by flag, the other forms and the backward).
 
 One step = one call of the whole hot path (ttt_linear_fwd: every mini-batch of
 every (sequence, head) chain) on inputs already resident in HBM.  Prints one
@@ -7,6 +7,7 @@ JSON line (rank 0) with tokens/s, the HBM roofline of the kernel (live HIP
 event timing) and the fp64 CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--config l1p3b|l125m|long|mlp]
+                    [--generic | --primal | --decode | --ln | --chunks N | --save | --bwd | --train]
 """
 from __future__ import annotations
 
@@ -65,6 +66,25 @@ def algorithmic(cfg: ti.Config, eta_strides):
     return bytes_, flops
 
 
+def algorithmic_bwd(cfg: ti.Config, eta_strides, grad_size: int = 4):
+    """Algorithmic bytes and flops of one backward call (ttt_linear_bwd).
+
+    Bytes: read Q, K (input dtype), the saved E (fp32), dZ (grad_size), eta;
+    write dQ, dK, dV (grad_size) and deta (fp32, per token); read W_final and
+    dW_final, write dW0 (fp32 d x d per chain).
+    Flops per token-head: 14 d^2 for the seven d x d x b products of a
+    mini-batch (rebuilding the start state, A K, W^T dZ, W^T dE, A^T E and the
+    two terms of the adjoint update) plus 10 d b for the five b x b x d ones.
+    """
+    th = cfg.B * cfg.H * cfg.T
+    in_sz = 2 if cfg.dtype == "bf16" else 4
+    d, b = cfg.d, cfg.b
+    eta_b = 4 * th if eta_strides[2] != 0 else 4 * (cfg.H if eta_strides[1] else 1)
+    bytes_ = th * d * (2 * in_sz + 4 + grad_size + 3 * grad_size) + eta_b + 4 * th + 3 * cfg.B * cfg.H * d * d * 4
+    flops = th * (14 * d * d + 10 * d * b)
+    return bytes_, flops
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when the summary is missing or was taken on a different kernel source."""
@@ -97,6 +117,23 @@ def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int):
                       f"fp64 primal form, {dt:.2f} s wall on {threads} threads"}
 
 
+def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int):
+    import oracle
+
+    chains = ti.sample_chains(cfg, sample_chains)
+    sub = ti.Inputs(cfg, chains, inp_full.q[chains], inp_full.k[chains], inp_full.v[chains],
+                    inp_full.w1, inp_full.w2, inp_full.eta_buf, inp_full.eta_strides)
+    dz, dwf = ti.upstream_grads(cfg, chains=chains)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.linear_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(), sub.eta_rows(), cfg.b, dz, dwf, threads=threads)
+    dt = time.perf_counter() - t0
+    tokens = len(chains) * cfg.T / cfg.H
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(chains)} of {cfg.chains} (sequence, head) chains at full T={cfg.T}, "
+                      f"fp64 reverse pass of the primal loop, {dt:.2f} s wall on {threads} threads"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +153,11 @@ def main():
                     help="split each sequence into this many chunks run in parallel (chunked forward)")
     ap.add_argument("--decode", action="store_true",
                     help="time decoding: one token per call for every sequence, state carried in place")
+    ap.add_argument("--save", action="store_true",
+                    help="time the forward for training (also writes E for the backward)")
+    ap.add_argument("--bwd", action="store_true", help="time the TTT-Linear backward (ttt_linear_bwd)")
+    ap.add_argument("--train", action="store_true",
+                    help="time forward-for-training + backward (one training step of the layer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) so profiler "
                          "HBM counters can be scaled to bytes")
@@ -167,7 +209,32 @@ def main():
         kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
                                        inp.eta_strides, args.generic, args.primal)
 
-        if args.ln:
+        if args.save or args.bwd or args.train:
+            e_sv = torch.empty((B, H, T, d), dtype=torch.float32, device="cuda:0")
+            ttt.linear_fwd_save(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf, e_saved=e_sv)
+            gen = torch.Generator(device="cuda:0")
+            gen.manual_seed(cfg.seed)
+            dz = torch.randn((B, H, T, d), generator=gen, device="cuda:0")
+            dwf = torch.randn((B, H, d, d), generator=gen, device="cuda:0")
+            gout = (torch.empty_like(dz), torch.empty_like(dz), torch.empty_like(dz),
+                    torch.empty((B, H, T), dtype=torch.float32, device="cuda:0"), torch.empty_like(dwf))
+            if args.save:
+                def step():
+                    ttt.linear_fwd_save(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf,
+                                        e_saved=e_sv)
+            elif args.bwd:
+                kname = ttt.linear_bwd_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
+                                                   inp.eta_strides, args.generic)
+
+                def step():
+                    ttt.linear_bwd(t["q"], t["k"], t["eta"], wf, e_sv, dz, cfg.b, dw_final=dwf,
+                                   generic=args.generic, out=gout)
+            else:
+                def step():
+                    ttt.linear_fwd_save(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf,
+                                        e_saved=e_sv)
+                    ttt.linear_bwd(t["q"], t["k"], t["eta"], wf, e_sv, dz, cfg.b, dw_final=dwf, out=gout)
+        elif args.ln:
             gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
             bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
 
@@ -206,6 +273,13 @@ def main():
     value = tokens / (ms_per_step / 1e3)
 
     bytes_, flops = algorithmic(cfg, inp.eta_strides)
+    if args.save:
+        bytes_ += B * H * T * d * 4                     # E written
+    elif args.bwd:
+        bytes_, flops = algorithmic_bwd(cfg, inp.eta_strides)
+    elif args.train:
+        b2, f2 = algorithmic_bwd(cfg, inp.eta_strides)
+        bytes_, flops = bytes_ + B * H * T * d * 4 + b2, flops + f2
     if args.decode:
         # per call: read every state twice (W and Wb) and write them, one token of Q/K/V in, Z out
         bytes_ = B * H * (4 * d * d * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
@@ -245,7 +319,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and not args.decode:
         log("bench: timing the fp64 oracle on a sample ...")
-        cpu = cpu_baseline(cfg, inp, args.cpu_sample_chains)
+        if args.bwd:
+            cpu = cpu_baseline_bwd(cfg, inp, args.cpu_sample_chains)
+        else:
+            cpu = cpu_baseline(cfg, inp, args.cpu_sample_chains)
         log(f"bench: cpu baseline {cpu['value']:.3e} tokens/s ({cpu['sample']})")
 
     eta_desc = {(0, 0, 0): "scalar", (0, 1, 0): "per head"}.get(tuple(inp.eta_strides), "per token")
@@ -257,15 +334,25 @@ def main():
     if args.chunks > 1:
         form = f"chunked({args.chunks})"
         roof["note"] = "chunked forward: chunk maps + scan + parallel chunks (4 launches per call)"
-    headline = cfg.name == "l1p3b" and not form
+    direction = "fwd"
+    if args.save:
+        form, direction = "", "fwd (saving E for the backward)"
+    if args.bwd:
+        form, direction = ("generic " if args.generic else ""), "bwd"
+        roof["note"] = "backward: dQ, dK, dV, deta, dW0 from dZ and dW_final, state rebuilt from W_final and E"
+    if args.train:
+        form, direction = "", "fwd+bwd (training step)"
+        roof["note"] = "forward saving E, then backward: two launches per step"
+    headline = cfg.name == "l1p3b" and not form and direction == "fwd"
     rec = {
-        "metric": METRIC if headline else f"{model} {form + ' ' if form else ''}fwd tokens/sec ({cfg.name})",
+        "metric": METRIC if headline else
+        f"{model} {form.strip() + ' ' if form.strip() else ''}{direction} tokens/sec ({cfg.name})",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" and not args.generic else "fp32",
         "data": "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) weights)",
-        "config": {"workload": f"{model} dual-form forward B{B} H{H} d{d}"
+        "config": {"workload": f"{model} dual-form {direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
                                f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
                                f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta",
                    "B": B, "H": H, "d": d, "T": T, "b": cfg.b, "global_batch": B, "seq_len": T,
