@@ -40,6 +40,14 @@
 // Precision: every fp32 operand enters the bf16 matrix cores as a hi + lo
 // pair (|x - hi - lo| <= 2^-16 |x|); products of two fp32 operands take three
 // passes (hi hi, hi lo, lo hi), products with bf16 inputs two.
+//
+// Staging: each 16-token tile is loaded PF mini-batches ahead into registers
+// and, one step ahead, written to a double-buffered LDS slot already split:
+// E and dZ as bf16 hi / lo tiles, and the state-rebuilding term
+// R = 2 diag(eta) E as the negated split of the forward's own -2 eta e, so the
+// rebuilt state subtracts exactly the operands the forward added.  The waves
+// read every operand in the layout its product wants: rows with 8-byte
+// loads, columns with the transposing LDS load (ds_read_b64_tr_b16).
 #include "mfma_common.h"
 
 namespace ttt {
@@ -49,52 +57,66 @@ using namespace mfma;
 
 constexpr int D = 64;       // head dim
 constexpr int BT = 16;      // mini-batch (tokens)
-constexpr int ROW = 72;     // padded LDS row of a bf16 token tile (elements)
-constexpr int ER = 68;      // padded LDS row of an fp32 token tile (elements, 272 B)
+constexpr int ROW = 72;     // padded LDS row of a bf16 token tile (elements, 144 B)
 constexpr int kThreads = 256;
 
+typedef uint16_t Tile[BT * ROW];
+
 struct __align__(16) BSlot {
-  uint16_t q[BT * ROW];
-  uint16_t k[BT * ROW];
-  float e[BT * ER];
-  float dz[BT * ER];
+  Tile q, k;        // inputs (bf16)
+  Tile eh, el;      // E = W K - V, split
+  Tile rh, rl;      // R = 2 diag(eta) E (the negated forward update factor), split
+  Tile zh, zl;      // dZ, split
   float eta[BT];
 };
 static_assert(sizeof(BSlot) % 16 == 0, "slot size");
 
-// dZ tile loads: 4 elements per thread per mini-batch
+// dZ tile loads: 4 elements per thread per mini-batch, widened to fp32
 template <typename GT>
 struct GradLoad;
 template <>
 struct GradLoad<float> {
   typedef u32x4 type;
-  __device__ static void to_lds(float* dst, type x) { *reinterpret_cast<u32x4*>(dst) = x; }
+  __device__ static void get(type x, float v[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(x[i]);
+  }
 };
 template <>
 struct GradLoad<uint16_t> {
   typedef u32x2 type;
-  __device__ static void to_lds(float* dst, type x) {
-    *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
-                                                  __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u));
+  __device__ static void get(type x, float v[4]) {
+    v[0] = __uint_as_float(x[0] << 16);
+    v[1] = __uint_as_float(x[0] & 0xffff0000u);
+    v[2] = __uint_as_float(x[1] << 16);
+    v[3] = __uint_as_float(x[1] & 0xffff0000u);
   }
 };
 
 __device__ __forceinline__ float4v zero4v() { return float4v{0.f, 0.f, 0.f, 0.f}; }
 
-// Rows li of an fp32 LDS tile in the F2 contraction order: block b holds
-// columns 16b + 4g .. 16b + 4g + 3, split into hi / lo.
-__device__ __forceinline__ void rows_split(const float* tile, int li, int g, float scale, bf16x4 hi[4],
-                                           bf16x4 lo[4]) {
+// Raw bits of element r of a bf16x4, taken from its two 32-bit words.  (Stores
+// of bit-cast __bf16 vector elements were compiled as stores of element 0 for
+// every r; the word arithmetic avoids that path.)
+__device__ __forceinline__ uint16_t bf16_bits(bf16x4 x, int r) {
+  const u32x2 w = __builtin_bit_cast(u32x2, x);
+  const uint32_t v = w[r >> 1];
+  return static_cast<uint16_t>((r & 1) ? (v >> 16) : (v & 0xffffu));
+}
+
+__device__ __forceinline__ void put4(uint16_t* tile, int off, bf16x4 x) {
+  *reinterpret_cast<bf16x4*>(tile + off) = x;
+}
+
+// Row li of a bf16 tile in the row-contraction order: block b holds columns
+// 16b + 4g .. 16b + 4g + 3 (the order of an F2 state's rows).
+__device__ __forceinline__ void rows4(const uint16_t* tile, int li, int g, bf16x4 x[4]) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const float4 x = *reinterpret_cast<const float4*>(tile + li * ER + 16 * b + 4 * g);
-    const float v[4] = {scale * x.x, scale * x.y, scale * x.z, scale * x.w};
-    split4(v, hi[b], lo[b]);
-  }
+  for (int b = 0; b < 4; ++b) x[b] = *reinterpret_cast<const bf16x4*>(tile + li * ROW + 16 * b + 4 * g);
 }
 
 // 64-deep contraction over the rows of an F2 state: acc += X[m = li][:] . F2[:][n = li]
-// with X given as rows (rows_split) and the state tiles pre-split; three passes.
+// with X given as split rows (rows4) and the state tiles pre-split; three passes.
 __device__ __forceinline__ float4v rows_x_f2(const bf16x4 xh[4], const bf16x4 xl[4], const bf16x4 sh[4],
                                              const bf16x4 sl[4], float4v acc) {
 #pragma unroll
@@ -108,16 +130,11 @@ __device__ __forceinline__ float4v rows_x_f2(const bf16x4 xh[4], const bf16x4 xl
   return acc;
 }
 
-// Accumulator-layout column block of an fp32 LDS tile: X[4g + r][col0 + li].
-__device__ __forceinline__ void acc_cols(const float* tile, int col0, int li, int g, float x[4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) x[r] = tile[(4 * g + r) * ER + col0 + li];
-}
-
 template <int PF, bool ETA_TOKEN, typename GT>
 __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
+  static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
   __shared__ BSlot slots[2];
-  __shared__ float dEs[BT * ER];
+  __shared__ Tile deh, del;  // dE of all rows, split
   __shared__ float part[4][BT];
 
   const int tid = threadIdx.x;
@@ -144,7 +161,8 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
   const float* eg = a.eta + bi * a.esb + h * a.esh;
 
   // staging roles: 16 B of Q (tid < 128) or K (tid >= 128) at row srow, columns
-  // scol..scol+7; 4 values of E and of dZ at row tid / 16, columns 4 (tid % 16)..+3
+  // scol..scol+7; 4 values of E and of dZ at row frow = tid / 16, columns
+  // fcol..fcol+3, and the step size of token frow
   const int within = tid & 127;
   const u32x4* srcA = (tid < 128 ? Qg : Kg) + within;
   const u32x4* srcE = Eg + tid;
@@ -153,11 +171,14 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
   const int scol = (within & 7) * 8;
   const int frow = tid >> 4;
   const int fcol = (tid & 15) * 4;
-  const float* srcEta = eg + static_cast<int64_t>(tid & 15) * a.est;
+  const float* srcEta = eg + static_cast<int64_t>(frow) * a.est;
 
   u32x4 ra[PF], re[PF];
   GLoad rz[PF];
   float rt[PF];
+
+  float eta_c = 0.f;
+  if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
 
   auto load_step = [&](int n, u32x4& xa, u32x4& xe, GLoad& xz, float& xt) {
     xa = ld_stream(srcA + static_cast<size_t>(n) * (BT * D / 8));
@@ -168,13 +189,27 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
   auto stage = [&](int slot, const u32x4& xa, const u32x4& xe, const GLoad& xz, float xt) {
     BSlot& S = slots[slot];
     *reinterpret_cast<u32x4*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
-    *reinterpret_cast<u32x4*>(&S.e[frow * ER + fcol]) = xe;
-    GradLoad<GT>::to_lds(&S.dz[frow * ER + fcol], xz);
-    if (ETA_TOKEN && tid < BT) S.eta[tid] = xt;
+    const float et = ETA_TOKEN ? xt : eta_c;
+    float e[4], r[4], z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[i] = __uint_as_float(xe[i]);
+      r[i] = -(-2.f * et * e[i]);  // the forward's update factor, negated (exact)
+    }
+    GradLoad<GT>::get(xz, z);
+    const int off = frow * ROW + fcol;
+    bf16x4 hi, lo;
+    split4(e, hi, lo);
+    put4(S.eh, off, hi);
+    put4(S.el, off, lo);
+    split4(r, hi, lo);
+    put4(S.rh, off, hi);
+    put4(S.rl, off, lo);
+    split4(z, hi, lo);
+    put4(S.zh, off, hi);
+    put4(S.zl, off, lo);
+    if (ETA_TOKEN && (tid & 15) == 0) S.eta[frow] = xt;
   };
-
-  float eta_c = 0.f;
-  if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
 
   // state: W (F2) from the final state, A (F1 and F2) from dL/dW_final
   float4v w2[4], a2[4], a1[4];
@@ -249,20 +284,16 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
     }
 
     // ---- Y = E dZ^T (s = 4g+r, t = li), contraction over all 64 outputs ----
-    bf16x4 zh[4], zl[4];
-    rows_split(S.dz, li, g, 1.f, zh, zl);
-    float4v y;
-    {
-      bf16x4 eh[4], el[4];
-      rows_split(S.e, li, g, 1.f, eh, el);
-      y = rows_x_f2(eh, el, zh, zl, zero4v());
-    }
+    bf16x4 erh[4], erl[4], zrh[4], zrl[4];
+    rows4(S.eh, li, g, erh);
+    rows4(S.el, li, g, erl);
+    rows4(S.zh, li, g, zrh);
+    rows4(S.zl, li, g, zrl);
+    const float4v y = rows_x_f2(erh, erl, zrh, zrl, zero4v());
 
     // ---- dE = -2 dZ M^T - 2 P diag(eta), rows i of this wave ----
-    float zw[4];
-    acc_cols(S.dz, 16 * w, li, g, zw);  // dZ[t = 4g+r][16w + li]
-    bf16x4 zwh, zwl;
-    split4(zw, zwh, zwl);
+    const bf16x4 zwh = read_cols<ROW>(S.zh, 0, 16 * w, li, g);  // dZ[t = 4g+r][16w + li]
+    const bf16x4 zwl = read_cols<ROW>(S.zl, 0, 16 * w, li, g);
     float4v mdz;
     {
       // A operand M[s = li][t = 4g+r] from S^T, causal mask s <= t, scale eta_s
@@ -278,22 +309,26 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
     float de[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) de[r] = -2.f * mdz[r] - 2.f * et[r] * p[r];
+    bf16x4 dh, dl;
+    split4(de, dh, dl);
     {
       GT* vp = dVg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         store_out<GT>(vp + r * D, -de[r]);
-        dEs[(4 * g + r) * ER + 16 * w + li] = de[r];
+        const int o = (4 * g + r) * ROW + 16 * w + li;
+        deh[o] = bf16_bits(dh, r);
+        del[o] = bf16_bits(dl, r);
       }
     }
 
     // ---- deta partials: -2 sum_t S Y [s <= t] (wave 0) - 2 sum_i E P (rows of this wave) ----
     {
-      float ew[4];
-      acc_cols(S.e, 16 * w, li, g, ew);
+      const bf16x4 ewh = read_cols<ROW>(S.eh, 0, 16 * w, li, g);  // E[4g + r][16w + li]
+      const bf16x4 ewl = read_cols<ROW>(S.el, 0, 16 * w, li, g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = ew[r] * p[r];
+        float x = (static_cast<float>(ewh[r]) + static_cast<float>(ewl[r])) * p[r];
         if (w == 0) x += (4 * g + r <= li) ? sc[r] * y[r] : 0.f;
         x = sum16(x);
         if (li == 0) part[w][4 * g + r] = -2.f * x;
@@ -320,8 +355,6 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
 
     // ---- A (F1, rows of this wave) += dZ Q^T + dE K^T, after P used it ----
     {
-      bf16x4 dh, dl;
-      split4(de, dh, dl);
       const bf16x8 bz = cat(zwh, zwl), bd = cat(dh, dl);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -332,52 +365,47 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
       }
     }
 
-    // ---- rebuild the mini-batch-start state: W -= G^T K, G = -2 diag(eta) E ----
-    // (the forward's update term, recomputed from the same fp32 values)
+    // ---- rebuild the mini-batch-start state: W += R^T K, R = 2 diag(eta) E ----
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      float ge[4];
-      acc_cols(S.e, 16 * b, li, g, ge);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ge[r] = -(-2.f * et[r] * ge[r]);
-      bf16x4 gh, gl;
-      split4(ge, gh, gl);
-      w2[b] = mfma32(cat(gh, gl), cat(kw, kw), w2[b]);
+      const bf16x4 rh = read_cols<ROW>(S.rh, 0, 16 * b, li, g);  // R[s = 4g+r][16b + li]
+      const bf16x4 rl = read_cols<ROW>(S.rl, 0, 16 * b, li, g);
+      w2[b] = mfma32(cat(rh, rl), cat(kw, kw), w2[b]);
     }
     bf16x4 wh[4], wl[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) split4(w2[b], wh[b], wl[b]);
 
     // ---- dQ += dZ W (contraction over the 64 rows of W) ----
-    dq = rows_x_f2(zh, zl, wh, wl, dq);
+    dq = rows_x_f2(zrh, zrl, wh, wl, dq);
 
-    // ---- dK += G A (A before this mini-batch's update, F2) ----
+    // ---- dK += -2 diag(eta) E A (A before this mini-batch's update, F2) ----
     {
-      bf16x4 gh[4], gl[4], ah[4], al[4];
-      rows_split(S.e, li, g, -2.f * eta_li, gh, gl);
+      bf16x4 ah[4], al[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) split4(a2[b], ah[b], al[b]);
-      dk = rows_x_f2(gh, gl, ah, al, dk);
+      const float4v ea = rows_x_f2(erh, erl, ah, al, zero4v());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dk[r] += -2.f * et[r] * ea[r];
     }
 
     __syncthreads();  // dE of all rows and the deta partials are in LDS
 
     // ---- dK += dE W ----
     {
-      bf16x4 dh[4], dl[4];
-      rows_split(dEs, li, g, 1.f, dh, dl);
-      dk = rows_x_f2(dh, dl, wh, wl, dk);
+      bf16x4 drh[4], drl[4];
+      rows4(deh, li, g, drh);
+      rows4(del, li, g, drl);
+      dk = rows_x_f2(drh, drl, wh, wl, dk);
     }
 
     // ---- A (F2, columns of this wave) += dZ Q^T + dE K^T ----
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      float zb[4], db[4];
-      acc_cols(S.dz, 16 * b, li, g, zb);
-      acc_cols(dEs, 16 * b, li, g, db);
-      bf16x4 zbh, zbl, dbh, dbl;
-      split4(zb, zbh, zbl);
-      split4(db, dbh, dbl);
+      const bf16x4 zbh = read_cols<ROW>(S.zh, 0, 16 * b, li, g);
+      const bf16x4 zbl = read_cols<ROW>(S.zl, 0, 16 * b, li, g);
+      const bf16x4 dbh = read_cols<ROW>(deh, 0, 16 * b, li, g);
+      const bf16x4 dbl = read_cols<ROW>(del, 0, 16 * b, li, g);
       a2[b] = mfma32(cat(zbh, zbl), cat(qw, qw), a2[b]);
       a2[b] = mfma32(cat(dbh, dbl), cat(kw, kw), a2[b]);
     }
@@ -418,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
 }
 
 #ifndef TTT_BWD_PF
-#define TTT_BWD_PF 4
+#define TTT_BWD_PF 3
 #endif
 constexpr int kPF = TTT_BWD_PF;
 

@@ -113,6 +113,7 @@ __device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs
 // SAVE: also write E = W K - V of every token (the backward's input; MODE 0, no LN).
 template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN, bool SAVE = false>
 __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a) {
+  static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
   __shared__ Slot slots[2];
   __shared__ LnShared lns;
 
