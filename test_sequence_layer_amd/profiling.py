@@ -16,6 +16,8 @@ factor = known bytes / counter bytes (per counter).
     python -m test_sequence_layer_amd.profiling --stats D1 --fetch D2 --write D3 \
         --kernel ttt_linear_mfma_d64b16 --workload l1p3b --algorithmic-bytes N \
         --command "..."
+    python -m test_sequence_layer_amd.profiling --counters D --kernel K --workload W \
+        --algorithmic-flops F --command "..."      (SQ counter summary)
 """
 from __future__ import annotations
 
@@ -138,17 +140,54 @@ def summarize(stats_dir, fetch_dir, write_dir, kernel, workload, algorithmic_byt
     return md
 
 
+COUNTER_SET = ("MfmaUtil", "VALUBusy", "LDSBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+
+
+def summarize_counters(pmc_dir, kernel, workload, algorithmic_flops, command, out_dir=PROFILES):
+    """Write profiles/<kernel>__<workload>__counters.md from one rocprofv3 --pmc
+    run of COUNTER_SET: medians per dispatch, and the MFMA work the kernel
+    performed (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts the MFMA's add and multiply
+    operations / 512, so x 512 is flops) against its algorithmic flops."""
+    med = {}
+    for c in COUNTER_SET:
+        v = counter_kib(pmc_dir, kernel, c)
+        med[c] = statistics.median(v)
+    performed = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    md = os.path.join(out_dir, f"{kernel}__{workload}__counters.md")
+    with open(md, "w") as fh:
+        fh.write(f"# {kernel} -- {workload}: SQ counters\n\n")
+        fh.write("Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root):\n\n")
+        for c in command:
+            fh.write(f"    {c}\n")
+        fh.write("\n| counter (median per dispatch) | value |\n|---|---|\n")
+        fh.write(f"| MfmaUtil (MFMA busy / (GPU active x SIMDs)) | {med['MfmaUtil']:.1f} % |\n")
+        fh.write(f"| VALUBusy (VALU instruction cycles / (GPU active x CUs)) | {med['VALUBusy']:.1f} % |\n")
+        fh.write(f"| LDSBankConflict (bank-conflict stall / (GPU active x CUs)) | {med['LDSBankConflict']:.1f} % |\n")
+        fh.write(f"| GRBM_GUI_ACTIVE (summed over the 8 XCDs) | {med['GRBM_GUI_ACTIVE']:.4e} cycles |\n")
+        fh.write(f"| SQ_INSTS_VALU_MFMA_MOPS_BF16 | {med['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4e} |\n")
+        fh.write(f"| bf16 MFMA flops performed (MOPS x 512) | {performed:.4e} |\n")
+        fh.write(f"| algorithmic flops | {algorithmic_flops:.4e} |\n")
+        fh.write(f"| performed / algorithmic (split passes, padding) | {performed / algorithmic_flops:.2f} |\n")
+        fh.write(f"| kernel source hash | {source_hash(kernel)} |\n")
+    return md
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--counters", help="summarise one --pmc run of COUNTER_SET instead")
+    ap.add_argument("--algorithmic-flops", type=float)
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--kernel", required=True)
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--algorithmic-bytes", type=float, required=True)
+    ap.add_argument("--algorithmic-bytes", type=float)
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--timed", type=int, default=200, help="launches in the benchmark's timed region")
     a = ap.parse_args()
+    if a.counters:
+        print(summarize_counters(a.counters, a.kernel, a.workload, a.algorithmic_flops, a.command))
+        return
     print(summarize(a.stats, a.fetch, a.write, a.kernel, a.workload, a.algorithmic_bytes, a.command,
                     timed=a.timed))
 
