@@ -285,7 +285,9 @@ def main():
         bytes_ = B * H * (4 * d * d * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
         flops = B * H * 6 * d * d
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
-    traffic = measured_traffic(kname, cfg.name)
+    # counters are recorded per (kernel, workload); the saving forward and the
+    # two-kernel training step have no record of their own
+    traffic = None if (args.save or args.train) else measured_traffic(kname, cfg.name)
     tflops = flops / (kernel_ms / 1e3) / 1e12
     # the binding roofline: bytes / 8 TB/s vs flops / 2.5 PF/s (bf16 MFMA, which every
     # contraction runs on); TTT-Linear is HBM-bound, TTT-MLP MFMA-bound
