@@ -132,9 +132,13 @@ __device__ __forceinline__ float4v mfma3_16(float4v a, float4v b, float4v c) {
   return c;
 }
 
+// GELU(x) = x Phi(x) and GELU'(x) = Phi(x) + x phi(x), exact erf form, with one
+// erff per pre-activation shared by both.
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
-__device__ __forceinline__ float gelu_prime(float x) {
-  return 0.5f * (1.f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+__device__ __forceinline__ void gelu_and_prime(float x, float& g, float& gp) {
+  const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752f));
+  g = x * cdf;
+  gp = cdf + x * 0.39894228040143268f * expf(-0.5f * x * x);
 }
 
 __device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cast<const float4v*>(p); }
@@ -281,11 +285,12 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     for (int jt = 0; jt < 2; ++jt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = hk[jt][r];
-        ak[jt][r] = gelu(x);
+        float gv, gpv;
+        gelu_and_prime(hk[jt][r], gv, gpv);
+        ak[jt][r] = gv;
         // transpose buffers: [j = 16jt + 4g + r][t = li]
-        akt[(16 * jt + 4 * g + r) * TROW + li] = ak[jt][r];
-        gkt[(16 * jt + 4 * g + r) * TROW + li] = gelu_prime(x);
+        akt[(16 * jt + 4 * g + r) * TROW + li] = gv;
+        gkt[(16 * jt + 4 * g + r) * TROW + li] = gpv;
       }
     }
     const Op8 akop = split8(ak[0], ak[1]);  // A_K with j in the k-slots, t at l%16
@@ -386,20 +391,28 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       }
     }
     // W2[i][j] += sum_s E[i][s] (-eta_s A_K[j][s])   (tile: j = 16jt + 4g + r, i = 16it + li)
-    float4v ga[2];
+    // (each operand split once: -eta A_K per hidden tile, E per output tile)
+    bf16x4 gah[2], gal[2];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      ga[jt] = ld4(&akt[(16 * jt + li) * TROW + 4 * g]);  // A_K[j = 16jt + li][s = 4g + r]
+      float4v ga = ld4(&akt[(16 * jt + li) * TROW + 4 * g]);  // A_K[j = 16jt + li][s = 4g + r]
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ga[jt][r] *= -et[r];
+      for (int r = 0; r < 4; ++r) ga[r] *= -et[r];
+      split4(ga, gah[jt], gal[jt]);
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       float4v es;  // E[i = 16it + li][s = 4g + r]
 #pragma unroll
       for (int r = 0; r < 4; ++r) es[r] = sm.e[(4 * g + r) * PROW + 16 * it + li];
+      bf16x4 eh, el;
+      split4(es, eh, el);
+      const bf16x4 z = {};
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) w2a[it][jt] = mfma3_16(ga[jt], es, w2a[it][jt]);
+      for (int jt = 0; jt < 2; ++jt) {
+        w2a[it][jt] = mfma32(cat(gah[jt], gah[jt]), cat(eh, el), w2a[it][jt]);
+        w2a[it][jt] = mfma32(cat(gal[jt], z), cat(eh, z), w2a[it][jt]);
+      }
     }
     __syncthreads();  // #3: S2 and W2 A_Q partials written
 
