@@ -44,7 +44,8 @@
 // Streaming: a 16-token tile of Q, K, V is 3 x 2 KB contiguous.  Each step
 // loads the tile PF steps ahead into registers (coalesced 16-byte loads),
 // stores the tile one step ahead into a double-buffered LDS slot, and issues
-// one barrier.  The update's K^T operand and E's V values are column reads of
+// one barrier.  Z goes out through a double-buffered LDS tile as whole rows,
+// one step late, so every store instruction writes contiguous 16-byte pieces.  The update's K^T operand and E's V values are column reads of
 // the row-major tiles with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
 #include "mfma_common.h"
 
@@ -57,6 +58,7 @@ constexpr int D = 64;       // head dim
 constexpr int BT = 16;      // mini-batch (tokens)
 constexpr int ROW = 72;     // padded LDS row of a token tile (bf16 elements, 144 B)
 constexpr int kThreads = 256;
+constexpr int ZROW = 68;    // padded fp32 row of the Z staging tile (conflict-free deposits)
 
 struct __align__(16) Slot {
   uint16_t q[BT * ROW];
@@ -116,6 +118,10 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
   __shared__ Slot slots[2];
   __shared__ LnShared lns;
+  // Z of the last two mini-batches, fp32 [token][output] (rows padded to ZROW):
+  // each wave deposits its 16 outputs of every token, and one step later every
+  // thread writes 16 contiguous bytes of whole rows to HBM.
+  __shared__ __align__(16) float zbuf[MODE == 0 ? 2 : 1][MODE == 0 ? BT * ZROW : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,6 +219,21 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // min(n+PF, nb-1) into ring slot j, compute step n, barrier.  The prefetch
   // index is clamped instead of guarded so every step issues the same memory
   // operations and the compiler's wait counts stay exact.
+  // Z rows of mini-batch m from the staging tile to HBM: thread tid writes
+  // token tid / 16, outputs 4 (tid % 16) .. +3
+  auto flush_z = [&](int m) {
+    const float4 x = *reinterpret_cast<const float4*>(&zbuf[m & 1][(tid >> 4) * ZROW + (tid & 15) * 4]);
+    OutT* zp = Zg + (static_cast<size_t>(m) * BT + (tid >> 4)) * D + (tid & 15) * 4;
+    if constexpr (sizeof(OutT) == 4) {
+      st_stream(reinterpret_cast<u32x4*>(zp),
+                u32x4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)});
+    } else {
+      st_stream(reinterpret_cast<u32x2*>(zp),
+                u32x2{static_cast<uint32_t>(f32_to_bf16_bits(x.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.y)) << 16),
+                      static_cast<uint32_t>(f32_to_bf16_bits(x.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.w)) << 16)});
+    }
+  };
+
   auto step = [&](const int n, u32x4& xa, u32x2& xb, float& xe, const u32x4& ya, const u32x2& yb,
                   const float ye) {
     stage((n + 1) & 1, ya, yb, ye);
@@ -359,9 +380,10 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
       for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qc[r]) + ln_g * (zz[r] - mu[r]) * rs[r] + ln_b;
     }
     if constexpr (MODE == 0) {
-      OutT* zp = Zg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
+      if (n > 0) flush_z(n - 1);
+      float* zb = &zbuf[n & 1][(4 * g) * ZROW + 16 * w + li];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) store_out<OutT>(zp + r * D, z[r]);
+      for (int r = 0; r < 4; ++r) zb[r * ZROW] = z[r];
     }
 
     __syncthreads();
@@ -379,6 +401,10 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   for (int j = 0; j < PF; ++j) {
     const int jn = (j + 1) % PF;
     if (nfull + j < nb) step(nfull + j, ra[j], rb[j], re[j], ra[jn], rb[jn], re[jn]);
+  }
+
+  if constexpr (MODE == 0) {
+    if (nb > 0) flush_z(nb - 1);  // the last step's barrier made its tile visible
   }
 
   float* wf;
