@@ -122,6 +122,8 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // each wave deposits its 16 outputs of every token, and one step later every
   // thread writes 16 contiguous bytes of whole rows to HBM.
   __shared__ __align__(16) float zbuf[MODE == 0 ? 2 : 1][MODE == 0 ? BT * ZROW : 4];
+  // E of the last two mini-batches when it is saved for the backward (same scheme)
+  __shared__ __align__(16) float ebuf[SAVE ? 2 : 1][SAVE ? BT * ZROW : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,6 +224,12 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // Z rows of mini-batch m from the staging tile to HBM: thread tid writes
   // token tid / 16, outputs 4 (tid % 16) .. +3
   auto flush_z = [&](int m) {
+    if constexpr (SAVE) {
+      const float4 e4 = *reinterpret_cast<const float4*>(&ebuf[m & 1][(tid >> 4) * ZROW + (tid & 15) * 4]);
+      float* ep = a.Esave + (tok0 + static_cast<size_t>(m) * BT + (tid >> 4)) * D + (tid & 15) * 4;
+      st_stream(reinterpret_cast<u32x4*>(ep),
+                u32x4{__float_as_uint(e4.x), __float_as_uint(e4.y), __float_as_uint(e4.z), __float_as_uint(e4.w)});
+    }
     const float4 x = *reinterpret_cast<const float4*>(&zbuf[m & 1][(tid >> 4) * ZROW + (tid & 15) * 4]);
     OutT* zp = Zg + (static_cast<size_t>(m) * BT + (tid >> 4)) * D + (tid & 15) * 4;
     if constexpr (sizeof(OutT) == 4) {
@@ -334,9 +342,9 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
         for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
       }
       if constexpr (SAVE) {
-        float* ep = a.Esave + (tok0 + static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
+        float* eb = &ebuf[n & 1][(4 * g) * ZROW + 16 * w + li];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st_stream(ep + r * D, e[r]);
+        for (int r = 0; r < 4; ++r) eb[r * ZROW] = e[r];
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) gv[r] = -2.f * et[r] * e[r];
