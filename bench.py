@@ -285,9 +285,12 @@ def main():
         bytes_ = B * H * (4 * d * d * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
         flops = B * H * 6 * d * d
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
-    # counters are recorded per (kernel, workload); the saving forward and the
-    # two-kernel training step have no record of their own
-    traffic = None if (args.save or args.train) else measured_traffic(kname, cfg.name)
+    # counters are recorded per (kernel, workload) for the plain forward and the
+    # backward; the other modes (saving forward, training step, layer norm,
+    # chunked, primal, decode, portable kernel) run other code under related
+    # names and have no record of their own
+    plain = not (args.save or args.train or args.ln or args.chunks > 1 or args.primal or args.decode or args.generic)
+    traffic = measured_traffic(kname, cfg.name) if plain else None
     tflops = flops / (kernel_ms / 1e3) / 1e12
     # the binding roofline: bytes / 8 TB/s vs flops / 2.5 PF/s (bf16 MFMA, which every
     # contraction runs on); TTT-Linear is HBM-bound, TTT-MLP MFMA-bound
