@@ -141,6 +141,65 @@ def test_orthogonal_interpolation(ttt):
     assert np.abs(wk - v[:, :, -b:]).max() / np.abs(v).max() < 1e-4
 
 
+@pytest.mark.parametrize("generic", [False, True])
+def test_batch_gd_is_linear_attention(ttt, generic):
+    """W0 = 0 and one mini-batch (b = T): E = -V, so z_t = 2 sum_{s <= t} eta_s (q_t . k_s) v_s
+    (causal linear attention, [TTT] 03 §8) and W_final = 2 sum_s eta_s v_s k_s^T.
+    Closed form in fp64 on the stored input values."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=3, T=16, eta_kind="token", seed=21)
+    inp = ti.generate(cfg)
+    t = to_device(inp)
+    dev = "cuda:0"
+    w0 = torch.zeros((cfg.H, 64, 64), device=dev)
+    z, wf = ttt.linear_fwd(t["q"], t["k"], t["v"], w0, t["eta"], 16, generic=generic)
+    torch.cuda.synchronize()
+    q, k, v = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v))
+    eta = inp.eta_rows().astype(np.float64)
+    scores = np.einsum("ntc,nsc->nts", q, k) * eta[:, None, :] * np.tril(np.ones((16, 16)))[None]
+    z_ref = 2.0 * np.einsum("nts,nsi->nti", scores, v)
+    w_ref = 2.0 * np.einsum("ns,nsi,nsc->nic", eta, v, k)
+    ez, ew = max_rel(rows(z), z_ref), max_rel(rows(wf), w_ref)
+    print(f"linear attention (generic={generic}): err Z={ez:.3e} W_final={ew:.3e}", flush=True)
+    assert ez < 1e-5 and ew < 1e-5
+
+
+def test_fixed_point_exact(ttt):
+    """V = W* K with W0 = W*: every gradient is zero, so W_final = W* and Z = W* Q.
+    With W* = 1/2 times a permutation, W* K is exact in bf16 and E is exactly zero
+    in the kernel, so both hold bit for bit."""
+    rng = np.random.default_rng(22)
+    B, H, T, d = 2, 3, 64, 64
+    perm = np.stack([rng.permutation(d) for _ in range(H)])
+    wstar = np.zeros((H, d, d), np.float32)
+    for h in range(H):
+        wstar[h, np.arange(d), perm[h]] = 0.5
+    k, _ = ti.bf16_round(rng.standard_normal((B, H, T, d)).astype(np.float32) / 8)
+    q, _ = ti.bf16_round(rng.standard_normal((B, H, T, d)).astype(np.float32) / 8)
+    v = np.einsum("hij,bhtj->bhti", wstar, k).astype(np.float32)   # exact: one term of 0.5 * bf16
+    dev = "cuda:0"
+    bf = lambda x: torch.from_numpy(ti.bf16_round(x)[1].view(np.int16)).view(torch.bfloat16).to(dev)  # noqa
+    eta = torch.full((B, H, T), 0.03, device=dev)
+    z, wf = ttt.linear_fwd(bf(q), bf(k), bf(v), torch.from_numpy(wstar).to(dev), eta, 16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(wf.cpu().numpy(), np.broadcast_to(wstar, (B, H, d, d)))
+    np.testing.assert_array_equal(z.cpu().numpy(), np.einsum("hij,bhtj->bhti", wstar, q))
+
+
+def test_output_row_permutation(ttt):
+    """Permuting the output rows of W0 and V permutes the rows of Z and W_final
+    (rows of the state are independent, [TTT] 03 §9 with f = W x): bit for bit."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=2, T=128, seed=23)
+    inp = ti.generate(cfg)
+    t = to_device(inp)
+    perm = torch.from_numpy(np.random.default_rng(24).permutation(64)).to("cuda:0")
+    z, wf = ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], 16)
+    zp, wfp = ttt.linear_fwd(t["q"], t["k"], t["v"][..., perm].contiguous(), t["w1"][:, perm].contiguous(),
+                             t["eta"], 16)
+    torch.cuda.synchronize()
+    assert torch.equal(zp, z[..., perm])
+    assert torch.equal(wfp, wf[:, :, perm])
+
+
 def test_state_passing_and_inplace_carry(ttt):
     """fwd(T) == fwd(T1) then fwd(T - T1) from W_final (bitwise), with the state
     carried in place (W_final written over a per-sequence W0)."""
