@@ -108,7 +108,7 @@ __device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs
   }
 }
 
-// MODE 0: forward (Z and the final state).  MODE 1 / 2: chunk map P / R of a
+// MODE 0: forward (Z and the final state).  MODE 1: chunk maps P and R of a
 // chunked forward -- the state recurrence from I with V = 0 / from 0 with V,
 // over one chunk, with no query path and no Z.
 // LN: f(x) = x + LN(W x) (layer norm and residual inside f; MODE 0 only).
@@ -131,10 +131,19 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   const int li = lane & 15;
   const int g = lane >> 4;
 
-  // workgroup -> (chain, chunk); a plain forward has one chunk of T tokens
+  // workgroup -> (chain, chunk); a plain forward has one chunk of T tokens.
+  // The maps launch covers both maps: the first half of its grid computes P
+  // (from I, V = 0), the second half R (from 0, with V).
   const int per_chain = MODE == 0 ? a.nchunk : a.nchunk - 1;
-  const int chain = blockIdx.x / per_chain;
-  const int chunk = blockIdx.x - chain * per_chain;
+  int blk = blockIdx.x;
+  bool map_r = false;
+  if constexpr (MODE != 0) {
+    const int half = a.B * a.H * per_chain;
+    map_r = blk >= half;
+    if (map_r) blk -= half;
+  }
+  const int chain = blk / per_chain;
+  const int chunk = blk - chain * per_chain;
   const int bi = chain / a.H;
   const int h = chain - bi * a.H;
   const int nb = a.Tc / BT;
@@ -149,8 +158,10 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // staging roles (every load unconditional, so the ring stays in registers):
   //   16 B of Q (tid < 128) or K (tid >= 128): row srow, columns scol..scol+7
   //   8 B of V: row vrow, columns vcol..vcol+3;  eta of token (tid & 15)
+  // The maps have no query path: there the first 128 threads load 16 B of V
+  // instead of Q and the 8-byte V loads are dropped (4 KB per step, not 6).
   const int within = tid & 127;
-  const u32x4* srcA = (tid < 128 ? Qg : Kg) + within;
+  const u32x4* srcA = (tid < 128 ? (MODE == 0 ? Qg : reinterpret_cast<const u32x4*>(Vg)) : Kg) + within;
   const u32x2* srcB = reinterpret_cast<const u32x2*>(Vg) + tid;
   const int srow = within >> 3;
   const int scol = (within & 7) * 8;
@@ -164,13 +175,17 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 
   auto load_step = [&](int n, u32x4& xa, u32x2& xb, float& xe) {
     xa = ld_stream(srcA + static_cast<size_t>(n) * (BT * D / 8));  // 128 uint4 per tile
-    xb = ld_stream(srcB + static_cast<size_t>(n) * (BT * D / 4));  // 256 uint2 per tile
+    if constexpr (MODE == 0) xb = ld_stream(srcB + static_cast<size_t>(n) * (BT * D / 4));  // 256 uint2 per tile
     xe = ETA_TOKEN ? srcE[static_cast<int64_t>(n) * BT * a.est] : 0.f;
   };
   auto stage = [&](int slot, const u32x4& xa, const u32x2& xb, float xe) {
     Slot& S = slots[slot];
-    *reinterpret_cast<u32x2*>(&S.v[vrow * ROW + vcol]) = xb;
-    *reinterpret_cast<u32x4*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
+    if constexpr (MODE == 0) {
+      *reinterpret_cast<u32x2*>(&S.v[vrow * ROW + vcol]) = xb;
+      *reinterpret_cast<u32x4*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
+    } else {
+      *reinterpret_cast<u32x4*>(tid < 128 ? &S.v[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
+    }
     if (ETA_TOKEN && tid < BT) S.eta[tid] = xe;
   };
 
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        wt[t][r] = (MODE == 1 && 16 * w + li == 16 * t + 4 * g + r) ? 1.f : 0.f;
+        wt[t][r] = (!map_r && 16 * w + li == 16 * t + 4 * g + r) ? 1.f : 0.f;
   }
 
   // Drain the state / eta loads before the ring prologue: otherwise the
@@ -333,13 +348,12 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
       }
     } else {
       float e[4];
-      if constexpr (MODE == 1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e[r] = pk[r];  // V = 0
-      } else {
+      {
         const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
+        // (the P map runs the recurrence with V = 0)
+        const float vs = (MODE != 0 && !map_r) ? 0.f : 1.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
+        for (int r = 0; r < 4; ++r) e[r] = pk[r] - vs * static_cast<float>(vc[r]);
       }
       if constexpr (SAVE) {
         float* eb = &ebuf[n & 1][(4 * g) * ZROW + 16 * w + li];
@@ -420,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     if (chunk != a.nchunk - 1) return;  // only the last chunk holds the final state
     wf = a.Wf + static_cast<int64_t>(chain) * D * D;
   } else {
-    wf = a.maps + ((static_cast<int64_t>(chain) * (a.nchunk - 1) + chunk) * 2 + (MODE - 1)) * D * D;
+    wf = a.maps + ((static_cast<int64_t>(chain) * (a.nchunk - 1) + chunk) * 2 + (map_r ? 1 : 0)) * D * D;
   }
   wf += static_cast<int64_t>(16 * w + li) * D + 4 * g;
 #pragma unroll
@@ -454,9 +468,8 @@ hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
 
 template <bool TOK>
 hipError_t launch_maps_eta(const LinearArgs& a, hipStream_t s) {
-  dim3 grid(a.B * a.H * (a.nchunk - 1)), block(kThreads);
+  dim3 grid(2 * a.B * a.H * (a.nchunk - 1)), block(kThreads);  // P and R maps in one launch
   hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 1, false>), grid, block, 0, s, a);
-  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 2, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
