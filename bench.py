@@ -281,8 +281,10 @@ def main():
         b2, f2 = algorithmic_bwd(cfg, inp.eta_strides)
         bytes_, flops = bytes_ + B * H * T * d * 4 + b2, flops + f2
     if args.decode:
-        # per call: read every state twice (W and Wb) and write them, one token of Q/K/V in, Z out
-        bytes_ = B * H * (4 * d * d * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
+        # per call: read W and write it; read Wb unless the token starts a mini-batch, write
+        # Wb only when it does -- three d x d states on average over b calls -- plus one
+        # token of Q/K/V in and Z out
+        bytes_ = B * H * (3 * d * d * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
         flops = B * H * 6 * d * d
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
     # counters are recorded per (kernel, workload) for the plain forward and the

@@ -51,16 +51,31 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
   const int chain = blockIdx.x;
   const int bi = chain / a.H, h = chain - bi * a.H;
 
+  // The state slice of this thread is 16-byte aligned (CQ is a multiple of 4):
+  // moved with 16-byte accesses.  Wb is read only if the first token does not
+  // start a mini-batch itself (then Wb <- W before any use).
   float W[CQ], Wb[CQ];
   {
-    const float* w = a.W_in + bi * a.w_in_bstride + static_cast<int64_t>(h) * D * D + i * D + qd * CQ;
-    const float* wb = a.Wb_in + bi * a.w_in_bstride + static_cast<int64_t>(h) * D * D + i * D + qd * CQ;
+    const int64_t off = bi * a.w_in_bstride + static_cast<int64_t>(h) * D * D + i * D + qd * CQ;
+    const float4* w = reinterpret_cast<const float4*>(a.W_in + off);
 #pragma unroll
-    for (int c = 0; c < CQ; ++c) {
-      W[c] = w[c];
-      Wb[c] = wb[c];
+    for (int c = 0; c < CQ / 4; ++c) {
+      const float4 x = w[c];
+      W[4 * c] = x.x, W[4 * c + 1] = x.y, W[4 * c + 2] = x.z, W[4 * c + 3] = x.w;
+    }
+    if (a.pos % a.b != 0) {
+      const float4* wb = reinterpret_cast<const float4*>(a.Wb_in + off);
+#pragma unroll
+      for (int c = 0; c < CQ / 4; ++c) {
+        const float4 x = wb[c];
+        Wb[4 * c] = x.x, Wb[4 * c + 1] = x.y, Wb[4 * c + 2] = x.z, Wb[4 * c + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CQ; ++c) Wb[c] = W[c];
     }
   }
+  bool wb_moved = false;  // Wb was re-snapshotted during this call
   const size_t base = static_cast<size_t>(chain) * a.T * D;
   const InT* Qg = static_cast<const InT*>(a.Q) + base;
   const InT* Kg = static_cast<const InT*>(a.K) + base;
@@ -83,6 +98,7 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
       if ((a.pos + t0 + t) % a.b == 0) {
 #pragma unroll
         for (int c = 0; c < CQ; ++c) Wb[c] = W[c];
+        wb_moved = true;
       }
       float e = 0.f;
 #pragma unroll
@@ -105,13 +121,14 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
     for (int x = tid; x < nt * D; x += NT) st_out<OutT>(Zg, static_cast<size_t>(t0) * D + x, zs[x / D][x % D]);
   }
 
-  float* w = a.W_out + static_cast<int64_t>(chain) * D * D + i * D + qd * CQ;
+  float4* w = reinterpret_cast<float4*>(a.W_out + static_cast<int64_t>(chain) * D * D + i * D + qd * CQ);
 #pragma unroll
-  for (int c = 0; c < CQ; ++c) w[c] = W[c];
-  if (a.Wb_out) {
-    float* wb = a.Wb_out + static_cast<int64_t>(chain) * D * D + i * D + qd * CQ;
+  for (int c = 0; c < CQ / 4; ++c) w[c] = make_float4(W[4 * c], W[4 * c + 1], W[4 * c + 2], W[4 * c + 3]);
+  // an in-place Wb that no token re-snapshotted already holds these values
+  if (a.Wb_out && (wb_moved || a.Wb_out != a.Wb_in)) {
+    float4* wb = reinterpret_cast<float4*>(a.Wb_out + static_cast<int64_t>(chain) * D * D + i * D + qd * CQ);
 #pragma unroll
-    for (int c = 0; c < CQ; ++c) wb[c] = Wb[c];
+    for (int c = 0; c < CQ / 4; ++c) wb[c] = make_float4(Wb[4 * c], Wb[4 * c + 1], Wb[4 * c + 2], Wb[4 * c + 3]);
   }
 }
 
