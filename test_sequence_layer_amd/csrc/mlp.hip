@@ -30,21 +30,17 @@
 // keeps the first orientation; the second is made each mini-batch by
 // multiplying the split W2 operand by an identity operand on the matrix cores
 // (D = X I moves X's k-slot index to l%16; bf16 x 1 is exact).  Activations
-// needed in the other orientation (A_K and GELU'(H_K) for the updates and the
-// backward product) go through an LDS transpose buffer.  As in the TTT-Linear kernel, fp32 operands enter as bf16
+// needed in the other orientation (A_K for the W2 update, GELU'(H_K) for the
+// backward product) go through per-wave LDS tiles; A_K is stored already split
+// and read back with transposing loads.  As in the TTT-Linear kernel, fp32 operands enter as bf16
 // hi + lo pairs (3 passes when both are fp32; 16-token contractions put two
 // passes into the 8 k-slots of one instruction).
-#include "ttt_internal.h"
+#include "mfma_common.h"
 
 namespace ttt {
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
-typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float float2v __attribute__((__vector_size__(2 * sizeof(float))));
-typedef float float4v __attribute__((__vector_size__(4 * sizeof(float))));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace mfma;
 
 constexpr int D = 64;       // model dim
 constexpr int DH = 256;     // hidden width
@@ -52,9 +48,11 @@ constexpr int BT = 16;      // mini-batch
 constexpr int NW = 8;       // waves per workgroup
 constexpr int JW = DH / NW; // hidden units per wave (32)
 constexpr int kThreads = NW * 64;
-constexpr int ROW = 72;     // padded bf16 row of a token tile
+constexpr int ROW = 72;     // padded bf16 row of a token tile (row reads conflict-free)
+constexpr int EROW = 80;    // padded bf16 row of the -eta E tiles (column reads conflict-free)
+constexpr int AROW = 48;    // padded bf16 row of the per-wave A_K tiles [t][j] (column reads conflict-free)
 constexpr int KTROW = 20;   // padded bf16 row of the transposed K tile
-constexpr int TROW = 20;    // padded fp32 row of the per-wave transpose buffers [j][t]
+constexpr int TROW = 20;    // padded fp32 row of the per-wave transpose buffer [j][t]
 constexpr int PROW = 68;    // padded fp32 row of [t][i] buffers
 constexpr int SROW = 20;    // padded fp32 row of [s][t] buffers
 
@@ -66,41 +64,23 @@ struct __align__(16) Slot {
   float eta[BT];
 };
 
+// Every fp32 operand that several waves (or several products) use is split into
+// bf16 hi + lo once, where it is made, and kept split: E and -eta E by the
+// threads that form them, A_K by the wave that owns its hidden units.
 struct __align__(16) Smem {
   Slot slots[2];
-  float ak_t[NW][JW * TROW];    // A_K of each wave, [j][t]
+  uint16_t akh[NW][BT * AROW];  // A_K of each wave, bf16 hi, [t][j]
+  uint16_t akl[NW][BT * AROW];  //   and lo
   float gk_t[NW][JW * TROW];    // GELU'(H_K) of each wave, [j][t]
   float part[NW][BT * PROW];    // per-wave partial of W2 A (over the wave's hidden units), [t][i]
   float s2p[NW][BT * SROW];     // per-wave partial of A_K^T A_Q, [s][t]
-  float e[BT * PROW];           // E, [t][i]
+  uint16_t eh[BT * ROW];        // E, bf16 hi, [t][i]
+  uint16_t el[BT * ROW];        //   and lo
+  uint16_t enh[BT * EROW];      // -eta_t E, bf16 hi, [t][i]
+  uint16_t enl[BT * EROW];      //   and lo
   float zr[BT * PROW];          // W2 A_Q summed over waves, [t][i]
   float s2[BT * SROW];          // A_K^T A_Q summed over waves, [s][t]
 };
-
-__device__ __forceinline__ float4v mfma32(bf16x8 a, bf16x8 b, float4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = __builtin_convertvector(float2v{x0, x1}, bf16x2);
-  hi = __builtin_bit_cast(uint32_t, h);
-  const float h0 = __uint_as_float(hi << 16);
-  const float h1 = __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{x0 - h0, x1 - h1}, bf16x2));
-}
-
-// four fp32 -> bf16x4 hi and lo
-__device__ __forceinline__ void split4(float4v x, bf16x4& hi, bf16x4& lo) {
-  uint32_t h[2], l[2];
-  split2(x[0], x[1], h[0], l[0]);
-  split2(x[2], x[3], h[1], l[1]);
-  hi = __builtin_bit_cast(bf16x4, h);
-  lo = __builtin_bit_cast(bf16x4, l);
-}
-
-__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
 
 // a pair of 4-wide tiles split into 8-slot hi and lo operands
 struct Op8 {
@@ -121,11 +101,9 @@ __device__ __forceinline__ float4v mfma3(const Op8& a, const Op8& b, float4v c) 
   return c;
 }
 
-// 16-slot contraction with both operands fp32 (4 values each): 3 passes in 2 instructions
-__device__ __forceinline__ float4v mfma3_16(float4v a, float4v b, float4v c) {
-  bf16x4 ah, al, bh, bl;
-  split4(a, ah, al);
-  split4(b, bh, bl);
+// 16-slot contraction of two split operands (4 values each): the 3 passes
+// hi*hi + hi*lo + lo*hi in 2 instructions
+__device__ __forceinline__ float4v mfma3_16(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, float4v c) {
   const bf16x4 z = {};
   c = mfma32(cat(ah, ah), cat(bh, bl), c);
   c = mfma32(cat(al, z), cat(bh, z), c);
@@ -138,7 +116,8 @@ __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.f + erff(x
 __device__ __forceinline__ void gelu_and_prime(float x, float& g, float& gp) {
   const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752f));
   g = x * cdf;
-  gp = cdf + x * 0.39894228040143268f * expf(-0.5f * x * x);
+  // phi(x) = exp(-x^2 / 2) / sqrt(2 pi), as 2^(-x^2 log2(e) / 2) on the hardware exponential
+  gp = cdf + x * 0.39894228040143268f * __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);
 }
 
 __device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cast<const float4v*>(p); }
@@ -237,7 +216,8 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   }
   __syncthreads();
 
-  float* akt = sm.ak_t[w];
+  uint16_t* akh = sm.akh[w];
+  uint16_t* akl = sm.akl[w];
   float* gkt = sm.gk_t[w];
   float* part = sm.part[w];
 
@@ -288,12 +268,18 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
         float gv, gpv;
         gelu_and_prime(hk[jt][r], gv, gpv);
         ak[jt][r] = gv;
-        // transpose buffers: [j = 16jt + 4g + r][t = li]
-        akt[(16 * jt + 4 * g + r) * TROW + li] = gv;
-        gkt[(16 * jt + 4 * g + r) * TROW + li] = gpv;
+        gkt[(16 * jt + 4 * g + r) * TROW + li] = gpv;  // transposed: [j = 16jt + 4g + r][t = li]
       }
     }
     const Op8 akop = split8(ak[0], ak[1]);  // A_K with j in the k-slots, t at l%16
+    {
+      // the same split values, row t = li of the [t][j] tiles (read back transposed for the W2 update)
+      const u32x4 hv = __builtin_bit_cast(u32x4, akop.hi), lv = __builtin_bit_cast(u32x4, akop.lo);
+      *reinterpret_cast<u32x2*>(&akh[li * AROW + 4 * g]) = u32x2{hv.x, hv.y};
+      *reinterpret_cast<u32x2*>(&akh[li * AROW + 16 + 4 * g]) = u32x2{hv.z, hv.w};
+      *reinterpret_cast<u32x2*>(&akl[li * AROW + 4 * g]) = u32x2{lv.x, lv.y};
+      *reinterpret_cast<u32x2*>(&akl[li * AROW + 16 + 4 * g]) = u32x2{lv.z, lv.w};
+    }
 
     // Y partial[i][t] = sum_{j in J_w} W2[i][j] A_K[j][t]  -> part[t][i]
 #pragma unroll
@@ -304,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     }
     __syncthreads();  // #1: partials written
 
-    // ---- phase 2: E[t][i] = 2 (sum_w part_w[t][i] - V[t][i]) ----
+    // ---- phase 2: E[t][i] = 2 (sum_w part_w[t][i] - V[t][i]), stored split, and -eta_t E ----
     {
       const int e0 = 2 * tid;
       const int t = e0 >> 6, i = e0 & 63;
@@ -315,8 +301,16 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
         y1 += sm.part[ww][t * PROW + i + 1];
       }
       const uint32_t vv = *reinterpret_cast<const uint32_t*>(&S.v[t * ROW + i]);
-      sm.e[t * PROW + i] = 2.f * (y0 - __uint_as_float(vv << 16));
-      sm.e[t * PROW + i + 1] = 2.f * (y1 - __uint_as_float(vv & 0xffff0000u));
+      const float x0 = 2.f * (y0 - __uint_as_float(vv << 16));
+      const float x1 = 2.f * (y1 - __uint_as_float(vv & 0xffff0000u));
+      const float ne = -(ETA_TOKEN ? S.eta[t] : eta_c);
+      uint32_t hi, lo;
+      split2(x0, x1, hi, lo);
+      *reinterpret_cast<uint32_t*>(&sm.eh[t * ROW + i]) = hi;
+      *reinterpret_cast<uint32_t*>(&sm.el[t * ROW + i]) = lo;
+      split2(ne * x0, ne * x1, hi, lo);
+      *reinterpret_cast<uint32_t*>(&sm.enh[t * EROW + i]) = hi;
+      *reinterpret_cast<uint32_t*>(&sm.enl[t * EROW + i]) = lo;
     }
     __syncthreads();  // #2: E ready, partial buffer free
 
@@ -324,15 +318,20 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     // E^T operand: row t = li, i in the k-slots {32m + 16 h + 4g .. +3}
     Op8 eq[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      eq[m] = split8(ld4(&sm.e[li * PROW + 32 * m + 4 * g]), ld4(&sm.e[li * PROW + 32 * m + 16 + 4 * g]));
+    for (int m = 0; m < 2; ++m) {
+      const uint16_t* ph = &sm.eh[li * ROW + 32 * m + 4 * g];
+      const uint16_t* pl = &sm.el[li * ROW + 32 * m + 4 * g];
+      eq[m] = Op8{cat(*reinterpret_cast<const bf16x4*>(ph), *reinterpret_cast<const bf16x4*>(ph + 16)),
+                  cat(*reinterpret_cast<const bf16x4*>(pl), *reinterpret_cast<const bf16x4*>(pl + 16))};
+    }
     // W2 with the hidden unit at l%16 (contraction over i): the split W2 operands
     // times the identity give W2[i = 16it + 4g + r][j = 16jt + li], exact bf16 values.
     Op8 w2s[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) w2s[it] = split8(w2a[it][0], w2a[it][1]);
-    // Dt[t][j] = GELU'(H_K)[j][t] * sum_i E[i][t] W2[i][j]   (t = 4g + r, j = 16jt + li)
-    float4v dt[2];
+    // G[j][s] = -eta_s GELU'(H_K)[j][s] sum_i E[i][s] W2[i][j]   (s = 4g + r, j = 16jt + li),
+    // i.e. -eta_s D[j][s]; split once, it serves the H_Q correction and the W1 gradient
+    bf16x4 gdh[2], gdl[2];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
       float4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -346,17 +345,23 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
         acc = mfma3(eq[m], Op8{cat(h0, h1), cat(l0, l1v)}, acc);
       }
       const float4v gp = ld4(&gkt[(16 * jt + li) * TROW + 4 * g]);
+      float4v gd;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dt[jt][r] = acc[r] * gp[r];
+      for (int r = 0; r < 4; ++r) gd[r] = -et[r] * (acc[r] * gp[r]);
+      split4(gd, gdh[jt], gdl[jt]);
     }
-    // H_Q[j][t] -= sum_s D[j][s] L1[s][t],  L1[s][t] = eta_s S1[s][t] [s <= t]
-    float4v l1;
+    // H_Q[j][t] += sum_s G[j][s] S1[s][t] [s <= t]   (= - D diag(eta) triu(K^T Q))
+    bf16x4 s1h, s1l;
+    {
+      float4v s1m;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) l1[r] = (4 * g + r <= li) ? -et[r] * s1[r] : 0.f;
+      for (int r = 0; r < 4; ++r) s1m[r] = (4 * g + r <= li) ? s1[r] : 0.f;
+      split4(s1m, s1h, s1l);
+    }
     float4v aq[2];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      hq[jt] = mfma3_16(dt[jt], l1, hq[jt]);
+      hq[jt] = mfma3_16(gdh[jt], gdl[jt], s1h, s1l, hq[jt]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) aq[jt][r] = gelu(hq[jt][r]);
     }
@@ -375,44 +380,30 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     }
 
     // ---- state updates (gradients at the mini-batch-start state) ----
-    // W1^T[c][j] += sum_s K[s][c] (-eta_s D[j][s])
+    // W1^T[c][j] += sum_s K[s][c] G[j][s]
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      float4v g1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) g1[r] = -et[r] * dt[jt][r];
-      bf16x4 gh, gl;
-      split4(g1, gh, gl);
-      const bf16x8 gb = cat(gh, gl);
+      const bf16x8 gb = cat(gdh[jt], gdl[jt]);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
         const bf16x4 kt = *reinterpret_cast<const bf16x4*>(&S.kt[(16 * c4 + li) * KTROW + 4 * g]);
         w1[jt][c4] = mfma32(cat(kt, kt), gb, w1[jt][c4]);
       }
     }
-    // W2[i][j] += sum_s E[i][s] (-eta_s A_K[j][s])   (tile: j = 16jt + 4g + r, i = 16it + li)
-    // (each operand split once: -eta A_K per hidden tile, E per output tile)
+    // W2[i][j] += sum_s A_K[j][s] (-eta_s E[i][s])   (tile: j = 16jt + 4g + r, i = 16it + li),
+    // both operands read back split: A_K[j = 16jt + li][s = 4g + r], -eta_s E[i = 16it + li][s = 4g + r]
     bf16x4 gah[2], gal[2];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      float4v ga = ld4(&akt[(16 * jt + li) * TROW + 4 * g]);  // A_K[j = 16jt + li][s = 4g + r]
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ga[r] *= -et[r];
-      split4(ga, gah[jt], gal[jt]);
+      gah[jt] = read_cols<AROW>(akh, 0, 16 * jt, li, g);
+      gal[jt] = read_cols<AROW>(akl, 0, 16 * jt, li, g);
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      float4v es;  // E[i = 16it + li][s = 4g + r]
+      const bf16x4 eh = read_cols<EROW>(sm.enh, 0, 16 * it, li, g);
+      const bf16x4 el = read_cols<EROW>(sm.enl, 0, 16 * it, li, g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) es[r] = sm.e[(4 * g + r) * PROW + 16 * it + li];
-      bf16x4 eh, el;
-      split4(es, eh, el);
-      const bf16x4 z = {};
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        w2a[it][jt] = mfma32(cat(gah[jt], gah[jt]), cat(eh, el), w2a[it][jt]);
-        w2a[it][jt] = mfma32(cat(gal[jt], z), cat(eh, z), w2a[it][jt]);
-      }
+      for (int jt = 0; jt < 2; ++jt) w2a[it][jt] = mfma3_16(gah[jt], gal[jt], eh, el, w2a[it][jt]);
     }
     __syncthreads();  // #3: S2 and W2 A_Q partials written
 
@@ -438,22 +429,25 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     }
     __syncthreads();  // #4
 
-    // ---- phase 5: Z[t][i] = (W2 A_Q)[i][t] - sum_s E[i][s] L2[s][t], waves 0..3 ----
+    // ---- phase 5: Z[t][i] = (W2 A_Q)[i][t] + sum_s (-eta_s E[i][s]) S2[s][t] [s <= t], waves 0..3 ----
     if (w < 4) {
       const int it = w;
-      float4v l2;
+      bf16x4 s2h, s2l;
+      {
+        float4v s2m;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = 4 * g + r;
-        l2[r] = (s <= li) ? -et[r] * sm.s2[s * SROW + li] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int s = 4 * g + r;
+          s2m[r] = (s <= li) ? sm.s2[s * SROW + li] : 0.f;
+        }
+        split4(s2m, s2h, s2l);
       }
-      // A: E[i = 16it + li][s = 4g + r] (E stays valid until the next mini-batch's barrier #1)
-      float4v ez;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ez[r] = sm.e[(4 * g + r) * PROW + 16 * it + li];
+      // A: -eta_s E[i = 16it + li][s = 4g + r] (valid until the next mini-batch's barrier #1)
+      const bf16x4 eh = read_cols<EROW>(sm.enh, 0, 16 * it, li, g);
+      const bf16x4 el = read_cols<EROW>(sm.enl, 0, 16 * it, li, g);
       // C: (W2 A_Q)[i = 16it + 4g + r][t = li]
       float4v z = ld4(&sm.zr[li * PROW + 16 * it + 4 * g]);
-      z = mfma3_16(ez, l2, z);
+      z = mfma3_16(eh, el, s2h, s2l, z);
       float* zp = Zg + (static_cast<size_t>(n) * BT + li) * D + 16 * it + 4 * g;
       __builtin_nontemporal_store(z, reinterpret_cast<float4v*>(zp));
     }
