@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
       GT* vp = dVg + (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        store_out<GT>(vp + r * D, -de[r]);
+        store_merged<GT>(vp + r * D, -de[r]);
         const int o = (4 * g + r) * ROW + 16 * w + li;
         deh[o] = bf16_bits(dh, r);
         del[o] = bf16_bits(dl, r);
@@ -410,13 +410,14 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
       a2[b] = mfma32(cat(dbh, dbl), cat(kw, kw), a2[b]);
     }
 
-    // ---- stores: dQ, dK rows 4g + r, columns 16w + li; deta ----
+    // ---- stores: dQ, dK rows 4g + r, columns 16w + li (64-byte pieces of a row
+    // per wave, merged in the L2); deta ----
     {
       const size_t o = (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        store_out<GT>(dQg + o + r * D, dq[r]);
-        store_out<GT>(dKg + o + r * D, dk[r]);
+        store_merged<GT>(dQg + o + r * D, dq[r]);
+        store_merged<GT>(dKg + o + r * D, dk[r]);
       }
     }
     if (tid < BT) detag[n * BT + tid] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];

@@ -103,6 +103,16 @@ __device__ __forceinline__ void store_out<float>(float* p, float x) { st_stream(
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float x) { st_stream(p, f32_to_bf16_bits(x)); }
 
+// The same through the L2 (no non-temporal hint): outputs written as partial
+// lines by several waves merge there before they reach HBM, where non-temporal
+// partial-line stores were measured to cost 22% extra write traffic.
+template <typename OutT>
+__device__ __forceinline__ void store_merged(OutT* p, float x);
+template <>
+__device__ __forceinline__ void store_merged<float>(float* p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store_merged<uint16_t>(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
+
 // Data-parallel-primitive (DPP) lane moves inside a 16-lane row: quad_perm
 // [1,0,3,2] and [2,3,0,1] exchange neighbours 1 and 2 apart; row_half_mirror
 // (lane i <-> 7 - i within 8) and row_mirror (i <-> 15 - i) then fold the

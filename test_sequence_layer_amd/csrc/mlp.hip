@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       float4v z = ld4(&sm.zr[li * PROW + 16 * it + 4 * g]);
       z = mfma3_16(eh, el, s2h, s2l, z);
       float* zp = Zg + (static_cast<size_t>(n) * BT + li) * D + 16 * it + 4 * g;
-      __builtin_nontemporal_store(z, reinterpret_cast<float4v*>(zp));
+      *reinterpret_cast<float4v*>(zp) = z;  // 64-byte pieces of a row per wave, merged in the L2
     }
   };
 
