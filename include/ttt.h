@@ -71,6 +71,21 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
 #define TTT_FLAG_GENERIC 1u /* force the portable fp32 kernel (testing / cross-check)          */
 #define TTT_FLAG_PRIMAL 2u  /* compute token by token (primal form, [TTT] 03 §7's naive form):  */
                             /* the same result, no dual form; d in {16, 32, 64}, any b          */
+/* Row blocks of the matrix-core forward (d = 64, b = 16, bf16 inputs).  Rows of
+ * W evolve independently ([TTT] 03 §9: row i of the next state and of Z needs
+ * only row i of W and column i of V), so one (sequence, head) can be spread
+ * over 1, 2 or 4 workgroups of 64, 32 or 16 rows (4, 2 or 1 waves).  The
+ * default is one workgroup: its waves already run their rows in parallel, one
+ * per SIMD, so more workgroups add no parallelism and the per-step latency
+ * stays that of one wave (measured on MI355X: 64 sequences x 32,768 tokens
+ * 0.916 -> 0.892 ms with 4 blocks; no gain or a loss on the other shapes).
+ * A flag sets the count (results are identical: each row goes through the
+ * same arithmetic); at most one may be set, not with TTT_FLAG_GENERIC or
+ * TTT_FLAG_PRIMAL (TTT_ERR_FLAGS), and a shape the matrix-core kernel does
+ * not support then returns TTT_ERR_UNSUPPORTED.                              */
+#define TTT_FLAG_ROWS1 4u
+#define TTT_FLAG_ROWS2 8u
+#define TTT_FLAG_ROWS4 16u
 
 /* TTT-Linear problem description. */
 typedef struct {
@@ -104,8 +119,8 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
  * R_n = 2 V diag(eta) K^T; [TTT] 03 §7), so the library (1) composes the map of
  * every chunk but the last in parallel, (2) scans them to get each chunk's
  * start state, (3) runs every chunk's forward in parallel from its start state.
- * Requires the MFMA path (d = 64, b = 16, bf16 inputs, flags = 0) and
- * T % (16 * nchunks) == 0.  workspace: device memory of at least
+ * Requires the MFMA path (d = 64, b = 16, bf16 inputs; flags 0 or one
+ * TTT_FLAG_ROWS*, applied to both parallel passes) and T % (16 * nchunks) == 0.  workspace: device memory of at least
  * ttt_linear_chunked_workspace_bytes(desc, nchunks) bytes, 16-byte aligned,
  * overlapping no argument; contents on return are unspecified.  nchunks = 1
  * is ttt_linear_fwd (the workspace may then be NULL).

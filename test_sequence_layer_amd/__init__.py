@@ -28,6 +28,16 @@ TTT_OK = 0
 TTT_F32, TTT_BF16 = 0, 1
 TTT_FLAG_GENERIC = 1
 TTT_FLAG_PRIMAL = 2
+TTT_FLAG_ROWS = {1: 4, 2: 8, 4: 16}  # row blocks per (sequence, head) -> TTT_FLAG_ROWS1/2/4
+
+
+def _rows_flag(rows) -> int:
+    """flag bits forcing ``rows`` row blocks of the matrix-core forward (None: the library's choice)"""
+    if rows is None:
+        return 0
+    if rows not in TTT_FLAG_ROWS:
+        raise ValueError(f"rows must be None, 1, 2 or 4, not {rows!r}")
+    return TTT_FLAG_ROWS[rows]
 
 STATUS_NAMES = {
     0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE", 4: "TTT_ERR_UNSUPPORTED",
@@ -196,7 +206,7 @@ def linear_desc(B, H, T, d, b, in_dtype, out_dtype, w0_batch_stride, eta_strides
 
 
 def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
-               generic: bool = False, primal: bool = False, stream=None) -> Tuple["object", "object"]:
+               generic: bool = False, primal: bool = False, rows=None, stream=None) -> Tuple["object", "object"]:
     """TTT-Linear forward (dual form) on the GPU.
 
     q, k, v : [B, H, T, d] bfloat16 or float32 (same dtype), contiguous, on the GPU
@@ -206,7 +216,9 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
     returns (Z [B, H, T, d] of out_dtype (default float32), W_final [B, H, d, d] float32).
     ``w_final`` may be ``w0`` itself (in-place carry) when w0 is [B, H, d, d].
     ``generic`` forces the portable fp32 kernel; ``primal`` computes token by
-    token (the primal form) instead of with the dual form.
+    token (the primal form) instead of with the dual form; ``rows`` (1, 2, 4)
+    forces the number of row-block workgroups per sequence and head of the
+    matrix-core kernel (default 1).
     """
     torch = _torch()
     B, H, T, d = q.shape
@@ -227,7 +239,7 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
     if w_final is None:
         w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
     _check_dev(q, k, v, w0, eta_t, z, w_final)
-    flags = (TTT_FLAG_GENERIC if generic else 0) | (TTT_FLAG_PRIMAL if primal else 0)
+    flags = (TTT_FLAG_GENERIC if generic else 0) | (TTT_FLAG_PRIMAL if primal else 0) | _rows_flag(rows)
     desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, flags)
     st = lib().ttt_linear_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta_t),
                               _ptr(z), _ptr(w_final), _stream_handle(stream))
@@ -237,7 +249,7 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
 
 
 def linear_fwd_save(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None, e_saved=None,
-                    generic: bool = False, stream=None):
+                    generic: bool = False, rows=None, stream=None):
     """TTT-Linear forward for training: :func:`linear_fwd` plus the saved
     reconstruction errors E [B, H, T, d] float32 (e_t = W k_t - v_t at the
     mini-batch-start W) that :func:`linear_bwd` needs.
@@ -260,7 +272,7 @@ def linear_fwd_save(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=No
     if e_saved is None:
         e_saved = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
     _check_dev(q, k, v, w0, eta_t, z, w_final, e_saved)
-    flags = TTT_FLAG_GENERIC if generic else 0
+    flags = (TTT_FLAG_GENERIC if generic else 0) | _rows_flag(rows)
     desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, flags)
     st = lib().ttt_linear_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta_t),
                                    _ptr(z), _ptr(w_final), _ptr(e_saved), _stream_handle(stream))
@@ -328,15 +340,15 @@ def _w0_stride(w0, B, H, d) -> int:
 
 
 def linear_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),
-                       generic=False, primal=False) -> Optional[str]:
-    flags = (TTT_FLAG_GENERIC if generic else 0) | (TTT_FLAG_PRIMAL if primal else 0)
+                       generic=False, primal=False, rows=None) -> Optional[str]:
+    flags = (TTT_FLAG_GENERIC if generic else 0) | (TTT_FLAG_PRIMAL if primal else 0) | _rows_flag(rows)
     desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, flags)
     name = lib().ttt_linear_kernel_name(ctypes.byref(desc))
     return None if name is None else name.decode()
 
 
 def linear_fwd_chunked(q, k, v, w0, eta, b: int, nchunks: int, workspace=None, out_dtype=None,
-                       w_final=None, z=None, stream=None):
+                       w_final=None, z=None, rows=None, stream=None):
     """TTT-Linear forward with the sequence split into ``nchunks`` chunks run in parallel.
 
     Same arguments and result as :func:`linear_fwd` (to rounding).  ``workspace``
@@ -357,7 +369,7 @@ def linear_fwd_chunked(q, k, v, w0, eta, b: int, nchunks: int, workspace=None, o
         z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
     if w_final is None:
         w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, 0)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, _rows_flag(rows))
     need = int(lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(desc), int(nchunks)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -39,12 +39,23 @@ int64_t eta_extent(int64_t B, int64_t H, int64_t T, int64_t sb, int64_t sh, int6
 
 enum Kernel { K_NONE, K_GENERIC, K_MFMA, K_PRIMAL };
 
+constexpr uint32_t kRowFlags = TTT_FLAG_ROWS1 | TTT_FLAG_ROWS2 | TTT_FLAG_ROWS4;
+
 Kernel pick_linear(const ttt::LinearArgs& a, uint32_t flags) {
   if (flags & TTT_FLAG_PRIMAL) return ttt::linear_primal_supported(a.d) ? K_PRIMAL : K_NONE;
   if (flags & TTT_FLAG_GENERIC) return ttt::linear_generic_supported(a.d, a.b) ? K_GENERIC : K_NONE;
   if (ttt::linear_mfma_supported(a)) return K_MFMA;
+  if (flags & kRowFlags) return K_NONE;  // row blocks exist only in the matrix-core kernel
   if (ttt::linear_generic_supported(a.d, a.b)) return K_GENERIC;
   return K_NONE;
+}
+
+// Row blocks per (sequence, head, chunk) of the matrix-core forward: the
+// flag's count, else 1 (see TTT_FLAG_ROWS1 in ttt.h for why).
+int row_blocks(uint32_t flags) {
+  if (flags & TTT_FLAG_ROWS4) return 4;
+  if (flags & TTT_FLAG_ROWS2) return 2;
+  return 1;
 }
 
 ttt::LinearArgs make_linear_args(const ttt_linear_desc* d, const void* Q, const void* K, const void* V,
@@ -58,6 +69,7 @@ ttt::LinearArgs make_linear_args(const ttt_linear_desc* d, const void* Q, const 
   a.nchunk = 1; a.Tc = d->T; a.Wstart = nullptr; a.maps = nullptr;
   a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
   a.Esave = nullptr;
+  a.rb = row_blocks(d->flags);
   return a;
 }
 
@@ -69,8 +81,13 @@ ttt_status validate_linear(const ttt_linear_desc* d, const void* Q, const void* 
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->b < 1) return TTT_ERR_SHAPE;
   if (d->T % d->b != 0) return TTT_ERR_SHAPE;
   if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
-  if (d->flags & ~static_cast<uint32_t>(TTT_FLAG_GENERIC | TTT_FLAG_PRIMAL)) return TTT_ERR_FLAGS;
+  if (d->flags & ~(static_cast<uint32_t>(TTT_FLAG_GENERIC | TTT_FLAG_PRIMAL) | kRowFlags)) return TTT_ERR_FLAGS;
   if ((d->flags & TTT_FLAG_GENERIC) && (d->flags & TTT_FLAG_PRIMAL)) return TTT_ERR_FLAGS;
+  {
+    const uint32_t rows = d->flags & kRowFlags;
+    if (rows & (rows - 1)) return TTT_ERR_FLAGS;  // more than one row-block count
+    if (rows && (d->flags & (TTT_FLAG_GENERIC | TTT_FLAG_PRIMAL))) return TTT_ERR_FLAGS;
+  }
   int64_t chains = 1, tok = 1, wel = 1;
   if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
   tok = chains;
@@ -448,6 +465,7 @@ ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const v
   a.gamma = gamma;
   a.beta = beta;
   a.eps = eps;
+  a.rb = 1;
   const hipError_t e = ttt::launch_linear_mfma(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -466,7 +484,7 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
   ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
   if (st != TTT_OK) return st;
   if (nchunks < 1 || desc->T % (16 * nchunks) != 0) return TTT_ERR_SHAPE;
-  if (desc->flags != 0 || k != K_MFMA) return TTT_ERR_UNSUPPORTED;
+  if ((desc->flags & ~kRowFlags) != 0 || k != K_MFMA) return TTT_ERR_UNSUPPORTED;
   if (nchunks == 1) return ttt_linear_fwd(desc, Q, K, V, W0, eta, Z, W_final, stream);
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   if (chains == 0) return TTT_OK;

@@ -7,11 +7,15 @@
 // from matrix products), §9 (TTT-Linear, f(x) = W x).
 //
 // Work decomposition
-//   One workgroup (4 waves) per (sequence, head) walks the T/16 mini-batches
-//   in order.  Rows of W are independent (row i of the next state and of Z
-//   needs only row i of W, column i of V and all of K, Q, eta), so wave w
-//   owns rows [16w, 16w+16) of W and never talks to the other waves except
-//   through the shared input tiles.
+//   The 4 waves of a (sequence, head) walk its T/16 mini-batches in order.
+//   Rows of W are independent (row i of the next state and of Z needs only
+//   row i of W, column i of V and all of K, Q, eta), so wave w owns rows
+//   [16w, 16w+16) of W and never talks to the other waves except through the
+//   shared input tiles.  The 4 waves form one workgroup (RB = 1), or RB = 2 or
+//   4 workgroups of 4 / RB waves (row blocks) when there are too few
+//   sequences x heads to fill the chip; each row block then stages the whole
+//   K and Q tiles itself (they are read from the L2 it shares with the
+//   chain's other row blocks) and only its own columns of V.
 //
 // State layout (the key trick)
 //   Wave w keeps W^T[c][i] (c = 0..63, i = 16w..16w+15) as four 16x16 fp32
@@ -57,7 +61,6 @@ using namespace mfma;
 constexpr int D = 64;       // head dim
 constexpr int BT = 16;      // mini-batch (tokens)
 constexpr int ROW = 72;     // padded LDS row of a token tile (bf16 elements, 144 B)
-constexpr int kThreads = 256;
 constexpr int ZROW = 68;    // padded fp32 row of the Z staging tile (conflict-free deposits)
 
 struct __align__(16) Slot {
@@ -113,9 +116,15 @@ __device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs
 // over one chunk, with no query path and no Z.
 // LN: f(x) = x + LN(W x) (layer norm and residual inside f; MODE 0 only).
 // SAVE: also write E = W K - V of every token (the backward's input; MODE 0, no LN).
-template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN, bool SAVE = false>
-__global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a) {
+// RB: row blocks (workgroups) per (sequence, head, chunk); 1, 2 or 4.
+template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN, bool SAVE, int RB>
+__global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a) {
   static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
+  static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks");
+  static_assert(!LN || RB == 1, "the layer norm needs all 64 outputs of a token in one workgroup");
+  constexpr int NWV = 4 / RB;   // waves per workgroup
+  constexpr int NT = 64 * NWV;  // threads per workgroup
+  constexpr int CA = 256 / NT;  // 16-byte pieces of the Q|K tiles each thread stages per step
   __shared__ Slot slots[2];
   __shared__ LnShared lns;
   // Z of the last two mini-batches, fp32 [token][output] (rows padded to ZROW):
@@ -131,19 +140,32 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   const int li = lane & 15;
   const int g = lane >> 4;
 
-  // workgroup -> (chain, chunk); a plain forward has one chunk of T tokens.
-  // The maps launch covers both maps: the first half of its grid computes P
-  // (from I, V = 0), the second half R (from 0, with V).
+  // workgroup -> (chain, chunk, row block); a plain forward has one chunk of
+  // T tokens.  The maps launch covers both maps: the first half of its grid
+  // computes P (from I, V = 0), the second half R (from 0, with V).
   const int per_chain = MODE == 0 ? a.nchunk : a.nchunk - 1;
+  const int units = a.B * a.H * per_chain;
   int blk = blockIdx.x;
   bool map_r = false;
   if constexpr (MODE != 0) {
-    const int half = a.B * a.H * per_chain;
-    map_r = blk >= half;
-    if (map_r) blk -= half;
+    map_r = blk >= units * RB;
+    if (map_r) blk -= units * RB;
   }
-  const int chain = blk / per_chain;
-  const int chunk = blk - chain * per_chain;
+  // The RB row blocks of a unit are 8 block indices apart, so the round-robin
+  // dispatch of workgroups over the 8 XCDs places them on one XCD (one L2).
+  // A last group of fewer than 8 units is packed the same way with its size.
+  int unit = blk, rblk = 0;
+  if constexpr (RB > 1) {
+    const int full = units / 8;
+    const int grp = blk / (8 * RB);
+    const int in = blk - grp * 8 * RB;
+    const int width = grp < full ? 8 : units - full * 8;  // > 0: blk < units * RB
+    rblk = in / width;
+    unit = grp * 8 + (in - rblk * width);
+  }
+  const int chain = unit / per_chain;
+  const int chunk = unit - chain * per_chain;
+  const int wg = NWV * rblk + w;  // this wave's rows of W: [16 wg, 16 wg + 16)
   const int bi = chain / a.H;
   const int h = chain - bi * a.H;
   const int nb = a.Tc / BT;
@@ -156,35 +178,42 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   const float* eg = a.eta + bi * a.esb + h * a.esh + static_cast<int64_t>(chunk) * a.Tc * a.est;
 
   // staging roles (every load unconditional, so the ring stays in registers):
-  //   16 B of Q (tid < 128) or K (tid >= 128): row srow, columns scol..scol+7
-  //   8 B of V: row vrow, columns vcol..vcol+3;  eta of token (tid & 15)
-  // The maps have no query path: there the first 128 threads load 16 B of V
-  // instead of Q and the 8-byte V loads are dropped (4 KB per step, not 6).
-  const int within = tid & 127;
-  const u32x4* srcA = (tid < 128 ? (MODE == 0 ? Qg : reinterpret_cast<const u32x4*>(Vg)) : Kg) + within;
-  const u32x2* srcB = reinterpret_cast<const u32x2*>(Vg) + tid;
-  const int srow = within >> 3;
-  const int scol = (within & 7) * 8;
-  const int vrow = tid >> 4;
-  const int vcol = (tid & 15) * 4;
+  //   CA 16-byte pieces of the Q|K tiles: piece x = tid + c NT of the 256
+  //   (x < 128: Q, else K) is row (x & 127) / 8, columns 8 (x & 7) .. +7;
+  //   8 B of V in this row block's columns: row vrow, columns vcol .. vcol+3;
+  //   eta of token (tid & 15).
+  // The maps have no query path: there V takes Q's place in the 16-byte
+  // pieces and the 8-byte V loads are dropped (4 KB per step, not 6).
+  const u32x4* tileA = MODE == 0 ? Qg : reinterpret_cast<const u32x4*>(Vg);
+  const u32x4* srcA[CA];
+#pragma unroll
+  for (int c = 0; c < CA; ++c) {
+    const int x = tid + c * NT;
+    srcA[c] = (x < 128 ? tileA : Kg) + (x & 127);
+  }
+  const int vrow = tid / (4 * NWV);
+  const int vcol = 16 * NWV * rblk + (tid % (4 * NWV)) * 4;
+  const u32x2* srcB = reinterpret_cast<const u32x2*>(Vg) + (vrow * D + vcol) / 4;
   const float* srcE = eg + static_cast<int64_t>(tid & 15) * a.est;
 
-  u32x4 ra[PF];
+  u32x4 ra[PF][CA];
   u32x2 rb[PF];
   float re[PF];
 
-  auto load_step = [&](int n, u32x4& xa, u32x2& xb, float& xe) {
-    xa = ld_stream(srcA + static_cast<size_t>(n) * (BT * D / 8));  // 128 uint4 per tile
+  auto load_step = [&](int n, u32x4 (&xa)[CA], u32x2& xb, float& xe) {
+#pragma unroll
+    for (int c = 0; c < CA; ++c) xa[c] = ld_stream(srcA[c] + static_cast<size_t>(n) * (BT * D / 8));  // 128 uint4 per tile
     if constexpr (MODE == 0) xb = ld_stream(srcB + static_cast<size_t>(n) * (BT * D / 4));  // 256 uint2 per tile
     xe = ETA_TOKEN ? srcE[static_cast<int64_t>(n) * BT * a.est] : 0.f;
   };
-  auto stage = [&](int slot, const u32x4& xa, const u32x2& xb, float xe) {
+  auto stage = [&](int slot, const u32x4 (&xa)[CA], const u32x2& xb, float xe) {
     Slot& S = slots[slot];
-    if constexpr (MODE == 0) {
-      *reinterpret_cast<u32x2*>(&S.v[vrow * ROW + vcol]) = xb;
-      *reinterpret_cast<u32x4*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
-    } else {
-      *reinterpret_cast<u32x4*>(tid < 128 ? &S.v[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
+    if constexpr (MODE == 0) *reinterpret_cast<u32x2*>(&S.v[vrow * ROW + vcol]) = xb;
+#pragma unroll
+    for (int c = 0; c < CA; ++c) {
+      const int x = tid + c * NT, within = x & 127;
+      uint16_t* dst = x < 128 ? (MODE == 0 ? S.q : S.v) : S.k;
+      *reinterpret_cast<u32x4*>(&dst[(within >> 3) * ROW + (within & 7) * 8]) = xa[c];
     }
     if (ETA_TOKEN && tid < BT) S.eta[tid] = xe;
   };
@@ -195,8 +224,8 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // LN scale and shift of output 16w + l%16
   float ln_g = 0.f, ln_b = 0.f;
   if constexpr (LN) {
-    ln_g = a.gamma[h * D + 16 * w + li];
-    ln_b = a.beta[h * D + 16 * w + li];
+    ln_g = a.gamma[h * D + 16 * wg + li];
+    ln_b = a.beta[h * D + 16 * wg + li];
   }
 
   // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   if constexpr (MODE == 0) {
     const float* w0 = (a.Wstart ? a.Wstart + (static_cast<int64_t>(chain) * a.nchunk + chunk) * D * D
                                 : a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D) +
-                      static_cast<int64_t>(16 * w + li) * D + 4 * g;
+                      static_cast<int64_t>(16 * wg + li) * D + 4 * g;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float4 x = *reinterpret_cast<const float4*>(w0 + 16 * t);
@@ -216,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        wt[t][r] = (!map_r && 16 * w + li == 16 * t + 4 * g + r) ? 1.f : 0.f;
+        wt[t][r] = (!map_r && 16 * wg + li == 16 * t + 4 * g + r) ? 1.f : 0.f;
   }
 
   // Drain the state / eta loads before the ring prologue: otherwise the
@@ -237,27 +266,39 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   // index is clamped instead of guarded so every step issues the same memory
   // operations and the compiler's wait counts stay exact.
   // Z rows of mini-batch m from the staging tile to HBM: thread tid writes
-  // token tid / 16, outputs 4 (tid % 16) .. +3
+  // token tid / (4 NWV), this row block's outputs fcol .. fcol + 3.  One row
+  // block writes whole 256-byte rows (non-temporal); several write a piece of
+  // every row each, and the pieces merge in the L2 before they reach HBM.
+  const int frow = tid / (4 * NWV);
+  const int fl = (tid % (4 * NWV)) * 4;    // column in the staging tile
+  const int fcol = 16 * NWV * rblk + fl;   // output column
+  auto put = [](auto* p, auto x) {
+    if constexpr (RB == 1) {
+      st_stream(p, x);
+    } else {
+      *p = x;
+    }
+  };
   auto flush_z = [&](int m) {
     if constexpr (SAVE) {
-      const float4 e4 = *reinterpret_cast<const float4*>(&ebuf[m & 1][(tid >> 4) * ZROW + (tid & 15) * 4]);
-      float* ep = a.Esave + (tok0 + static_cast<size_t>(m) * BT + (tid >> 4)) * D + (tid & 15) * 4;
-      st_stream(reinterpret_cast<u32x4*>(ep),
-                u32x4{__float_as_uint(e4.x), __float_as_uint(e4.y), __float_as_uint(e4.z), __float_as_uint(e4.w)});
+      const float4 e4 = *reinterpret_cast<const float4*>(&ebuf[m & 1][frow * ZROW + fl]);
+      float* ep = a.Esave + (tok0 + static_cast<size_t>(m) * BT + frow) * D + fcol;
+      put(reinterpret_cast<u32x4*>(ep),
+          u32x4{__float_as_uint(e4.x), __float_as_uint(e4.y), __float_as_uint(e4.z), __float_as_uint(e4.w)});
     }
-    const float4 x = *reinterpret_cast<const float4*>(&zbuf[m & 1][(tid >> 4) * ZROW + (tid & 15) * 4]);
-    OutT* zp = Zg + (static_cast<size_t>(m) * BT + (tid >> 4)) * D + (tid & 15) * 4;
+    const float4 x = *reinterpret_cast<const float4*>(&zbuf[m & 1][frow * ZROW + fl]);
+    OutT* zp = Zg + (static_cast<size_t>(m) * BT + frow) * D + fcol;
     if constexpr (sizeof(OutT) == 4) {
-      st_stream(reinterpret_cast<u32x4*>(zp),
-                u32x4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)});
+      put(reinterpret_cast<u32x4*>(zp),
+          u32x4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)});
     } else {
-      st_stream(reinterpret_cast<u32x2*>(zp),
-                u32x2{static_cast<uint32_t>(f32_to_bf16_bits(x.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.y)) << 16),
-                      static_cast<uint32_t>(f32_to_bf16_bits(x.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.w)) << 16)});
+      put(reinterpret_cast<u32x2*>(zp),
+          u32x2{static_cast<uint32_t>(f32_to_bf16_bits(x.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.y)) << 16),
+                static_cast<uint32_t>(f32_to_bf16_bits(x.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.w)) << 16)});
     }
   };
 
-  auto step = [&](const int n, u32x4& xa, u32x2& xb, float& xe, const u32x4& ya, const u32x2& yb,
+  auto step = [&](const int n, u32x4 (&xa)[CA], u32x2& xb, float& xe, const u32x4 (&ya)[CA], const u32x2& yb,
                   const float ye) {
     stage((n + 1) & 1, ya, yb, ye);
     load_step(min(n + PF, nb - 1), xa, xb, xe);
@@ -320,8 +361,8 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
       float mu[4], rs[4], yh[4], gr[4], s1[4], s2[4];
       const float yk[4] = {pk[0], pk[1], pk[2], pk[3]};
       ln_stats(yk, mu, rs, lns.part[0], w, li, g, a.eps);
-      const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * w, li, g);   // V[4g + r][16w + li]
-      const bf16x4 kc = read_cols<ROW>(S.k, 0, 16 * w, li, g);   // K[4g + r][16w + li]
+      const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);   // V[4g + r][16wg + li]
+      const bf16x4 kc = read_cols<ROW>(S.k, 0, 16 * wg, li, g);   // K[4g + r][16wg + li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         yh[r] = (pk[r] - mu[r]) * rs[r];
@@ -349,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
     } else {
       float e[4];
       {
-        const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * w, li, g);  // V[4g + r][16w + li]
+        const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);  // V[4g + r][16wg + li]
         // (the P map runs the recurrence with V = 0)
         const float vs = (MODE != 0 && !map_r) ? 0.f : 1.f;
 #pragma unroll
@@ -397,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) zz[r] = z[r];
       ln_stats(zz, mu, rs, lns.part[2], w, li, g, a.eps);
-      const bf16x4 qc = read_cols<ROW>(S.q, 0, 16 * w, li, g);  // Q[4g + r][16w + li]
+      const bf16x4 qc = read_cols<ROW>(S.q, 0, 16 * wg, li, g);  // Q[4g + r][16wg + li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qc[r]) + ln_g * (zz[r] - mu[r]) * rs[r] + ln_b;
     }
@@ -436,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
   } else {
     wf = a.maps + ((static_cast<int64_t>(chain) * (a.nchunk - 1) + chunk) * 2 + (map_r ? 1 : 0)) * D * D;
   }
-  wf += static_cast<int64_t>(16 * w + li) * D + 4 * g;
+  wf += static_cast<int64_t>(16 * wg + li) * D + 4 * g;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     *reinterpret_cast<float4*>(wf + 16 * t) = make_float4(wt[t][0], wt[t][1], wt[t][2], wt[t][3]);
@@ -445,32 +486,60 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_mfma_d64b16(LinearArgs a)
 #ifndef TTT_LINEAR_PF
 #define TTT_LINEAR_PF 8
 #endif
-constexpr int kPF = TTT_LINEAR_PF;  // prefetch distance (mini-batches in flight per thread)
+// Prefetch distance (mini-batches in flight per thread).  A thread of a
+// smaller row block stages more of each tile (CA + 1 loads per step), so its
+// ring is shorter; those launches are latency-bound (few chains), not
+// bandwidth-bound.
+template <int RB>
+constexpr int pf_for() { return RB == 1 ? TTT_LINEAR_PF : 4; }
 
-template <bool TOK, bool LN>
-hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
-  dim3 grid(a.B * a.H * a.nchunk), block(kThreads);
+template <bool TOK, bool LN, int RB>
+hipError_t launch_rb(const LinearArgs& a, hipStream_t s) {
+  constexpr int PF = pf_for<RB>();
+  dim3 grid(a.B * a.H * a.nchunk * RB), block(256 / RB);
   if constexpr (!LN) {
     if (a.Esave) {
       if (a.out_dtype == 0)
-        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 0, false, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, 0, false, true, RB>), grid, block, 0, s, a);
       else
-        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t, 0, false, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, 0, false, true, RB>), grid, block, 0, s, a);
       return hipGetLastError();
     }
   }
   if (a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 0, LN>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, 0, LN, false, RB>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, uint16_t, 0, LN>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, 0, LN, false, RB>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool TOK, bool LN>
+hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
+  if constexpr (LN) {
+    return launch_rb<TOK, true, 1>(a, s);  // the layer norm runs with one row block
+  } else {
+    switch (a.rb) {
+      case 4: return launch_rb<TOK, false, 4>(a, s);
+      case 2: return launch_rb<TOK, false, 2>(a, s);
+      default: return launch_rb<TOK, false, 1>(a, s);
+    }
+  }
+}
+
+template <bool TOK, int RB>
+hipError_t launch_maps_rb(const LinearArgs& a, hipStream_t s) {
+  dim3 grid(2 * a.B * a.H * (a.nchunk - 1) * RB), block(256 / RB);  // P and R maps in one launch
+  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<pf_for<RB>(), TOK, float, 1, false, false, RB>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <bool TOK>
 hipError_t launch_maps_eta(const LinearArgs& a, hipStream_t s) {
-  dim3 grid(2 * a.B * a.H * (a.nchunk - 1)), block(kThreads);  // P and R maps in one launch
-  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<kPF, TOK, float, 1, false>), grid, block, 0, s, a);
-  return hipGetLastError();
+  switch (a.rb) {
+    case 4: return launch_maps_rb<TOK, 4>(a, s);
+    case 2: return launch_maps_rb<TOK, 2>(a, s);
+    default: return launch_maps_rb<TOK, 1>(a, s);
+  }
 }
 
 }  // namespace
@@ -478,7 +547,8 @@ hipError_t launch_maps_eta(const LinearArgs& a, hipStream_t s) {
 bool linear_mfma_supported(const LinearArgs& a) { return a.d == 64 && a.b == 16 && a.in_dtype == 1; }
 
 const char* linear_mfma_name(const LinearArgs& a) {
-  return a.gamma ? "ttt_linear_mfma_d64b16 (layer norm)" : "ttt_linear_mfma_d64b16";
+  if (a.gamma) return "ttt_linear_mfma_d64b16 (layer norm)";
+  return a.rb == 4 ? "ttt_linear_mfma_d64b16_r4" : a.rb == 2 ? "ttt_linear_mfma_d64b16_r2" : "ttt_linear_mfma_d64b16";
 }
 
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {

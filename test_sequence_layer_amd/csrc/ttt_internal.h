@@ -31,6 +31,9 @@ struct LinearArgs {
   // Forward for training: also write E[t] = W_{mini-batch start} k_t - v_t
   // ([chains][T][d] fp32) for the backward; nullptr: not saved.
   float* Esave;
+  // MFMA forward: workgroups (row blocks of 64 / rb rows of W) per
+  // (sequence, head, chunk); 1, 2 or 4 (1 with a layer norm).
+  int rb;
 };
 
 // Backward of TTT-Linear (plain f(x) = W x) from the saved E and the final state.

@@ -95,7 +95,7 @@ def test_linear_shape(kw):
 def test_linear_dtype_flags_stride():
     assert _val(_desc(ind=2)) == DTYPE
     assert _val(_desc(outd=-1)) == DTYPE
-    assert _val(_desc(flags=4)) == FLAGS
+    assert _val(_desc(flags=32)) == FLAGS
     assert _val(_desc(wstride=5)) == STRIDE
     assert _val(_desc(est=(0, -1, 0))) == STRIDE
     assert _val(_desc(wstride=4 * 64 * 64)) == OK
@@ -124,6 +124,30 @@ def test_linear_alias():
     # Z directly after Q (no overlap) is fine: Q is 2*4*64*64*2 bytes
     assert _val(d, z=1 * GB + 2 * 4 * 64 * 64 * 2) == OK
     assert _val(d, z=1 * GB + 2 * 4 * 64 * 64 * 2 - 16) == ALIAS
+
+
+def test_linear_row_block_flags():
+    R1, R2, R4 = (ttt.TTT_FLAG_ROWS[r] for r in (1, 2, 4))
+    for f in (R1, R2, R4):
+        assert _val(_desc(flags=f)) == OK
+    assert _val(_desc(flags=R1 | R2)) == FLAGS                       # at most one count
+    assert _val(_desc(flags=R2 | R4)) == FLAGS
+    assert _val(_desc(flags=R4 | ttt.TTT_FLAG_GENERIC)) == FLAGS
+    assert _val(_desc(flags=R2 | ttt.TTT_FLAG_PRIMAL)) == FLAGS
+    assert _val(_desc(flags=R4, ind=0, d=16, b=4)) == UNSUP           # matrix-core shapes only
+    assert _val(_desc(flags=R2, ind=0)) == UNSUP
+    with pytest.raises(ValueError):
+        ttt.linear_kernel_name(1, 1, 64, 64, 16, rows=3)
+
+
+def test_linear_row_block_choice():
+    # one workgroup per (sequence, head) unless a flag asks for row blocks
+    name = lambda B, H, **kw: ttt.linear_kernel_name(B, H, 8192, 64, 16, **kw)  # noqa: E731
+    for B, H in ((16, 32), (2, 32), (8, 12), (1, 1)):
+        assert name(B, H) == "ttt_linear_mfma_d64b16"
+        assert name(B, H, rows=1) == "ttt_linear_mfma_d64b16"
+        assert name(B, H, rows=2) == "ttt_linear_mfma_d64b16_r2"
+        assert name(B, H, rows=4) == "ttt_linear_mfma_d64b16_r4"
 
 
 def test_linear_kernel_selection():

@@ -58,7 +58,7 @@ def test_tiny_fp32(ttt):
 @pytest.mark.parametrize("eta_kind", ["scalar", "head", "token"])
 def test_bf16_mfma_small(ttt, B, H, T, eta_kind):
     cfg = ti.CONFIGS["l1p3b"].with_(B=B, H=H, T=T, eta_kind=eta_kind, eta_value=1.0 / 64, seed=7 + T)
-    assert ttt.linear_kernel_name(B, H, T, 64, 16) == "ttt_linear_mfma_d64b16"
+    assert ttt.linear_kernel_name(B, H, T, 64, 16).startswith("ttt_linear_mfma_d64b16")
     _check(ttt, cfg, 2e-3, label=f"mfma B{B} H{H} T{T} {eta_kind}")
 
 
