@@ -158,6 +158,9 @@ def main():
     ap.add_argument("--bwd", action="store_true", help="time the TTT-Linear backward (ttt_linear_bwd)")
     ap.add_argument("--train", action="store_true",
                     help="time forward-for-training + backward (one training step of the layer)")
+    ap.add_argument("--no-measured-peak", action="store_true",
+                    help="skip measuring the chip's achievable peak (HBM copy or bf16 MFMA loop) "
+                         "that roofline.frac_measured is stated against")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) so profiler "
                          "HBM counters can be scaled to bytes")
@@ -309,6 +312,22 @@ def main():
             "frac_of_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
     log(f"bench: {kname}: {kernel_ms:.3f} ms/launch, {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM), "
         f"{tflops:.1f} TFLOP/s algorithmic")
+
+    if not args.no_measured_peak:
+        # the chip's achievable peak for the binding resource, measured after the
+        # timed region on the same device: the fraction against it sits beside
+        # the fraction against the published peak
+        from test_sequence_layer_amd import peaks
+
+        if roof["bound"] == "hbm":
+            pm = peaks.measure_hbm_copy()
+            roof.update({"peak_measured": round(pm, 1), "frac_measured": round(achieved / pm, 4),
+                         "peak_measured_by": "2 GiB device copy, 16-byte non-temporal loads/stores"})
+        else:
+            pm = peaks.measure_mfma_bf16()
+            roof.update({"peak_measured": round(pm, 1), "frac_measured": round(tflops / pm, 4),
+                         "peak_measured_by": "bf16 v_mfma_f32_16x16x32 issue loop, 8 chains per wave"})
+        log(f"bench: measured peak {pm:.1f} {roof['unit']} -> {roof['frac_measured']:.1%} of it")
 
     if args.decode or args.primal:
         roof["note"] = ("decode: one token per call, latency-bound" if args.decode

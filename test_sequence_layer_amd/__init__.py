@@ -94,6 +94,15 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it first "
                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    # torch ships its own HIP runtime under the soname libamdhip64.so.7, which
+    # libttt.so also needs.  Loaded after torch, libttt.so binds to torch's
+    # runtime; loaded first, it would bind to the system's and torch would then
+    # load a second runtime whose device memory the first cannot use.  So torch
+    # (when installed) is imported first.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, fp = ctypes.c_void_p, ctypes.c_void_p
     L.ttt_linear_fwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, vp, fp, vp]

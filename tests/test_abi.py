@@ -275,3 +275,16 @@ def test_fwd_save_rejects_primal():
     b = Bufs()
     st = ttt.lib().ttt_linear_fwd_save(ctypes.byref(desc), *b.args(), 9 * GB, None)
     assert st == FLAGS
+
+
+def test_one_hip_runtime_per_process():
+    # torch ships a HIP runtime under the same soname the library needs; the
+    # binding imports torch before it loads libttt.so so that both use that one
+    # runtime (the library loaded first would bind to the system's, and torch
+    # would then bring a second runtime whose memory the first cannot use)
+    code = ("import test_sequence_layer_amd as t; t.lib(); import torch; "
+            "print(sorted(set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l)))")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    runtimes = eval(out.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes
