@@ -90,6 +90,7 @@ ttt_status validate_linear(const ttt_linear_desc* d, const void* Q, const void* 
   }
   int64_t chains = 1, tok = 1, wel = 1;
   if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
+  if (chains * row_blocks(d->flags) > INT_MAX) return TTT_ERR_SHAPE;  // workgroups of one launch
   tok = chains;
   if (!mul_ok(tok, d->T) || !mul_ok(tok, d->d)) return TTT_ERR_SHAPE;
   wel = chains;
@@ -485,6 +486,9 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
   if (st != TTT_OK) return st;
   if (nchunks < 1 || desc->T % (16 * nchunks) != 0) return TTT_ERR_SHAPE;
   if ((desc->flags & ~kRowFlags) != 0 || k != K_MFMA) return TTT_ERR_UNSUPPORTED;
+  // workgroups of the map launch (2 maps per chunk but the last) and of the chunk forward
+  if (static_cast<int64_t>(desc->B) * desc->H * 2 * nchunks * row_blocks(desc->flags) > INT_MAX)
+    return TTT_ERR_SHAPE;
   if (nchunks == 1) return ttt_linear_fwd(desc, Q, K, V, W0, eta, Z, W_final, stream);
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   if (chains == 0) return TTT_OK;

@@ -136,6 +136,8 @@ def test_linear_row_block_flags():
     assert _val(_desc(flags=R2 | ttt.TTT_FLAG_PRIMAL)) == FLAGS
     assert _val(_desc(flags=R4, ind=0, d=16, b=4)) == UNSUP           # matrix-core shapes only
     assert _val(_desc(flags=R2, ind=0)) == UNSUP
+    # 2^29 sequence-heads x 4 row blocks: more workgroups than one launch takes
+    assert _val(_desc(B=1 << 15, H=1 << 14, flags=R4)) == SHAPE
     with pytest.raises(ValueError):
         ttt.linear_kernel_name(1, 1, 64, 64, 16, rows=3)
 
