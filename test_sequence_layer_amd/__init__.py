@@ -161,6 +161,16 @@ def _torch():
     return torch
 
 
+def _done(status: int, what: str) -> None:
+    """Raise on a non-OK status.  With TTT_DEBUG_SYNC=1 in the environment, also
+    wait for the launched work and let torch raise any asynchronous kernel fault
+    here, at the call that caused it, rather than at a later synchronization."""
+    if status != TTT_OK:
+        raise TTTError(status, what)
+    if os.environ.get("TTT_DEBUG_SYNC") == "1":
+        _torch().cuda.synchronize()
+
+
 def _dtype_code(dt) -> int:
     torch = _torch()
     if dt == torch.float32:
@@ -252,8 +262,7 @@ def linear_fwd(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=None,
     desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, flags)
     st = lib().ttt_linear_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta_t),
                               _ptr(z), _ptr(w_final), _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_linear_fwd")
+    _done(st, "ttt_linear_fwd")
     return z, w_final
 
 
@@ -285,8 +294,7 @@ def linear_fwd_save(q, k, v, w0, eta, b: int, out_dtype=None, w_final=None, z=No
     desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, flags)
     st = lib().ttt_linear_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(eta_t),
                                    _ptr(z), _ptr(w_final), _ptr(e_saved), _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_linear_fwd_save")
+    _done(st, "ttt_linear_fwd_save")
     return z, w_final, e_saved
 
 
@@ -328,8 +336,7 @@ def linear_bwd(q, k, eta, w_final, e_saved, dz, b: int, dw_final=None, generic: 
     st = lib().ttt_linear_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(eta_t), _ptr(w_final), _ptr(e_saved),
                               _ptr(dz), _ptr(dw_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0),
                               _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_linear_bwd")
+    _done(st, "ttt_linear_bwd")
     return dq, dk, dv, deta, dw0
 
 
@@ -387,8 +394,7 @@ def linear_fwd_chunked(q, k, v, w0, eta, b: int, nchunks: int, workspace=None, o
     st = lib().ttt_linear_fwd_chunked(ctypes.byref(desc), int(nchunks), _ptr(q), _ptr(k), _ptr(v), _ptr(w0),
                                       _ptr(eta_t), _ptr(z), _ptr(w_final), _ptr(workspace), wbytes,
                                       _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_linear_fwd_chunked")
+    _done(st, "ttt_linear_fwd_chunked")
     return z, w_final
 
 
@@ -418,8 +424,7 @@ def linear_ln_fwd(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, out_
     desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, 0)
     st = lib().ttt_linear_ln_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
                                  _ptr(beta), float(eps), _ptr(eta_t), _ptr(z), _ptr(w_final), _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_linear_ln_fwd")
+    _done(st, "ttt_linear_ln_fwd")
     return z, w_final
 
 
@@ -452,8 +457,7 @@ def linear_decode(q, k, v, eta, w, wb, pos: int, b: int, out_dtype=None, z=None,
     desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), 0, est, 0)
     st = lib().ttt_linear_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(z),
                                  _ptr(w), _ptr(wb), int(pos), _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_linear_decode")
+    _done(st, "ttt_linear_decode")
     return z
 
 
@@ -495,8 +499,7 @@ def mlp_fwd(q, k, v, w1, w2, eta, b: int, out_dtype=None, w1_final=None, w2_fina
     desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est)
     st = lib().ttt_mlp_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(eta_t),
                            _ptr(z), _ptr(w1_final), _ptr(w2_final), _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_mlp_fwd")
+    _done(st, "ttt_mlp_fwd")
     return z, w1_final, w2_final
 
 

@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import ctypes
 
-from . import TTT_OK, TTTError, _ptr, _stream_handle, lib
+from . import _done, _ptr, _stream_handle, lib
 
 PEAK_EXPORTS = ("ttt_peak_copy", "ttt_peak_mfma_bf16", "ttt_peak_mfma_bf16_flops")
 
@@ -32,8 +32,7 @@ def copy(src, dst, stream=None) -> None:
     if dst.numel() * dst.element_size() != n:
         raise ValueError("src and dst differ in size")
     st = _plib().ttt_peak_copy(_ptr(src), _ptr(dst), n, _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_peak_copy")
+    _done(st, "ttt_peak_copy")
 
 
 def mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:
@@ -41,8 +40,7 @@ def mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:
     if out.numel() < blocks * 1024:
         raise ValueError("out too small")
     st = _plib().ttt_peak_mfma_bf16(_ptr(out), int(blocks), int(iters), _stream_handle(stream))
-    if st != TTT_OK:
-        raise TTTError(st, "ttt_peak_mfma_bf16")
+    _done(st, "ttt_peak_mfma_bf16")
 
 
 def mfma_bf16_flops(blocks: int, iters: int) -> int:

@@ -290,3 +290,28 @@ def test_one_hip_runtime_per_process():
     assert out.returncode == 0, out.stderr
     runtimes = eval(out.stdout.strip().splitlines()[-1])
     assert len(runtimes) == 1, runtimes
+
+
+def test_status_check_and_debug_sync(monkeypatch):
+    calls = []
+
+    class FakeCuda:
+        @staticmethod
+        def synchronize():
+            calls.append("sync")
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    monkeypatch.setattr(ttt, "_torch", lambda: FakeTorch)
+    monkeypatch.delenv("TTT_DEBUG_SYNC", raising=False)
+    ttt._done(OK, "ttt_linear_fwd")
+    assert calls == []
+    with pytest.raises(ttt.TTTError, match="TTT_ERR_SHAPE"):
+        ttt._done(SHAPE, "ttt_linear_fwd")
+    monkeypatch.setenv("TTT_DEBUG_SYNC", "1")
+    ttt._done(OK, "ttt_linear_fwd")
+    assert calls == ["sync"]
+    with pytest.raises(ttt.TTTError):
+        ttt._done(ALIGN, "ttt_linear_fwd")
+    assert calls == ["sync"]   # no wait after a rejected call: nothing was launched
