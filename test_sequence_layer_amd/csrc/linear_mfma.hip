@@ -31,7 +31,7 @@
 //   E   = P_K - V               registers (E^T layout: lane = (t = 4g+r, i))
 //   G   = -2 diag(eta) E        registers (same layout as E)
 //   Z   = P_Q + M G,  M[t][s] = S[s][t] [s <= t]
-//                               v_mfma_f32_16x16x32_bf16 x2 (3 split passes)
+//                               v_mfma_f32_16x16x32_bf16 x2 (4 split passes)
 //   W^T += K^T G                v_mfma_f32_16x16x32_bf16, [K^T K^T] x [G_hi G_lo]
 //   Only the native gfx950 K=32 bf16 MFMA is used: a 16-token contraction
 //   puts two split passes into its 8 k-slots per lane group.
@@ -417,10 +417,12 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       bf16x4 mhi, mlo;
       split4(mv, mhi, mlo);
       // The 16x16x32 MFMA sums 8 k-slots per lane group; a 16-token contraction
-      // uses slots 0-3 and 4-7 for two passes at once: [hi, hi] x [hi, lo].
-      const bf16x4 zero4 = {};
-      z = mfma32(cat(mhi, mhi), cat(bhi, blo), z);
-      z = mfma32(cat(mlo, zero4), cat(bhi, zero4), z);
+      // uses slots 0-3 and 4-7 for two passes at once: [Mhi Mhi] x [Ghi Glo] and
+      // [Mlo Mlo] x [Ghi Glo] (the update's own G operand and no zero-padded
+      // halves to build; the extra lo x lo product is below fp32 rounding).
+      const bf16x8 gz = cat(bhi, blo);
+      z = mfma32(cat(mhi, mhi), gz, z);
+      z = mfma32(cat(mlo, mlo), gz, z);
     }
 
     // ---- W^T[c][i] += sum_s K[s][c] G[s][i] ----
