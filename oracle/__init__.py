@@ -80,6 +80,8 @@ def _load():
     lib.oracle_linear_ln_primal.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, dp, i]
     lib.oracle_linear_ln_primal.restype = None
     lib.oracle_linear_primal_grads.argtypes = [i, i, i, i] + [dp] * 12 + [i]
+    lib.oracle_mlp_ln_primal.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, dp,
+                                         dp, i]
     lib.oracle_linear_primal_grads.restype = None
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -176,6 +178,27 @@ def linear_ln_primal(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, t
         _load().oracle_linear_ln_primal(n, T, d, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
                                         _ptr(beta), float(eps), _ptr(eta), _ptr(z), _ptr(wf), int(threads))
     return z, wf
+
+
+def mlp_ln_primal(q, k, v, w1, w2, gamma, beta, eta, b: int, eps: float = 1e-6, threads: int = 0):
+    """TTT-MLP with LN + residual, f(x) = x + LN(W2 GELU(W1 x)), primal form, fp64.
+
+    q, k, v : [n, T, d];  w1 : [n, dh, d];  w2 : [n, d, dh];  gamma, beta : [n, d];
+    eta : [n, T].  returns (z, w1_final, w2_final).
+    """
+    q, k, v, w1, w2, gamma, beta, eta = map(_f64, (q, k, v, w1, w2, gamma, beta, eta))
+    n, T, d = q.shape
+    dh = w1.shape[1]
+    assert w1.shape == (n, dh, d) and w2.shape == (n, d, dh) and eta.shape == (n, T)
+    assert gamma.shape == (n, d) and beta.shape == (n, d)
+    z = np.empty((n, T, d))
+    w1f = np.empty((n, dh, d))
+    w2f = np.empty((n, d, dh))
+    if n:
+        _load().oracle_mlp_ln_primal(n, T, d, dh, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(gamma),
+                                     _ptr(beta), float(eps), _ptr(eta), _ptr(z), _ptr(w1f), _ptr(w2f),
+                                     int(threads))
+    return z, w1f, w2f
 
 
 def run_inputs(inp, threads: int = 0):
@@ -433,6 +456,44 @@ def mlp_dual_f64(q, k, v, w1, w2, eta, b):
             z[c, sl] = (W2 @ AQ - E @ (np.triu(AK.T @ AQ) * et[:, None])).T
             W1 = W1 - (D1 * et[None, :]) @ K.T
             W2 = W2 - (E * et[None, :]) @ AK.T
+        W1f[c], W2f[c] = W1, W2
+    return z, W1f, W2f
+
+
+def mlp_ln_dual_f64(q, k, v, w1, w2, gamma, beta, eta, b, eps=1e-6):
+    """Dual form of TTT-MLP with LN + residual, fp64 (self-check only).
+
+    Per mini-batch (columns = tokens, start weights W1, W2):
+      H_K = W1 K, A_K = gelu(H_K), Y = W2 A_K, LN statistics per column,
+      G = 2 (K + LN(Y) - V) * gamma,  Dl = (G - mean(G) - Yh mean(G Yh)) / s,
+      D1 = (W2^T Dl) * gelu'(H_K),
+      H_Q = W1 Q - D1 (diag(eta) triu(K^T Q)),  A_Q = gelu(H_Q),
+      Z = Q + LN(W2 A_Q - Dl (diag(eta) triu(A_K^T A_Q))),
+      W1 -= D1 diag(eta) K^T,  W2 -= Dl diag(eta) A_K^T.
+    """
+    q, k, v, w1, w2, gamma, beta, eta = map(_f64, (q, k, v, w1, w2, gamma, beta, eta))
+    n, T, d = q.shape
+    z = np.empty((n, T, d))
+    W1f = np.empty_like(w1)
+    W2f = np.empty_like(w2)
+    for c in range(n):
+        W1, W2 = w1[c].copy(), w2[c].copy()
+        for t0 in range(0, T, b):
+            sl = slice(t0, min(t0 + b, T))
+            K, V, Q = k[c, sl].T, v[c, sl].T, q[c, sl].T
+            et = eta[c, sl]
+            HK = W1 @ K
+            AK = gelu(HK)
+            L, Yh, s = _ln_cols(W2 @ AK, gamma[c], beta[c], eps)
+            G = 2.0 * (K + L - V) * gamma[c][:, None]
+            Dl = (G - G.mean(axis=0, keepdims=True) - Yh * (G * Yh).mean(axis=0, keepdims=True)) / s
+            D1 = (W2.T @ Dl) * gelu_prime(HK)
+            HQ = W1 @ Q - D1 @ (np.triu(K.T @ Q) * et[:, None])
+            AQ = gelu(HQ)
+            YQ = W2 @ AQ - Dl @ (np.triu(AK.T @ AQ) * et[:, None])
+            z[c, sl] = (Q + _ln_cols(YQ, gamma[c], beta[c], eps)[0]).T
+            W1 = W1 - (D1 * et[None, :]) @ K.T
+            W2 = W2 - (Dl * et[None, :]) @ AK.T
         W1f[c], W2f[c] = W1, W2
     return z, W1f, W2f
 

@@ -228,6 +228,77 @@ void oracle_linear_ln_primal(int n, int T, int d, int b,
   }
 }
 
+/* TTT-MLP with LN and residual, f(x) = x + LN(W2 GELU(W1 x)), primal form.
+ * gamma, beta : [n, d] (per chain).  The loss |f(k) - v|^2 is pulled back
+ * through LN to y = W2 GELU(W1 k) as for TTT-Linear with LN:
+ *   g = 2 (f(k) - v) * gamma,  delta = (g - mean(g) - yhat * mean(g * yhat)) / s,
+ * and through the two layers as for plain TTT-MLP with delta in place of
+ * 2 (y - v): the W2 gradient is delta a^T and the W1 gradient
+ * ((W2^T delta) * GELU'(h)) k^T, both at the mini-batch-start weights. */
+void oracle_mlp_ln_primal(int n, int T, int d, int dh, int b,
+                          const double* q, const double* k, const double* v,
+                          const double* w1_0, const double* w2_0,
+                          const double* gamma, const double* beta, double eps, const double* eta,
+                          double* z, double* w1f, double* w2f, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int c = 0; c < n; ++c) {
+    const size_t sz = (size_t)dh * d;
+    const double* gm = gamma + (size_t)c * d;
+    const double* bt = beta + (size_t)c * d;
+    double* W1 = (double*)malloc(sz * sizeof(double));
+    double* W2 = (double*)malloc(sz * sizeof(double));
+    double* W1b = (double*)malloc(sz * sizeof(double));
+    double* W2b = (double*)malloc(sz * sizeof(double));
+    double* h = (double*)malloc((size_t)dh * sizeof(double));
+    double* a = (double*)malloc((size_t)dh * sizeof(double));
+    double* g1 = (double*)malloc((size_t)dh * sizeof(double));
+    double* y = (double*)malloc((size_t)d * sizeof(double));
+    double* yh = (double*)malloc((size_t)d * sizeof(double));
+    double* dl = (double*)malloc((size_t)d * sizeof(double));
+    memcpy(W1, w1_0 + c * sz, sz * sizeof(double));
+    memcpy(W2, w2_0 + c * sz, sz * sizeof(double));
+    for (int t0 = 0; t0 < T; t0 += b) {
+      memcpy(W1b, W1, sz * sizeof(double));
+      memcpy(W2b, W2, sz * sizeof(double));
+      int t1 = t0 + b < T ? t0 + b : T;
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        const double et = eta[(size_t)c * T + t];
+        /* reconstruction of v_t from k_t at the mini-batch-start weights */
+        matvec(W1b, k + o, h, dh, d);
+        for (int j = 0; j < dh; ++j) a[j] = gelu(h[j]);
+        matvec(W2b, a, y, d, dh);
+        const double s = ln_normalize(y, yh, d, eps);
+        double mg = 0.0, mgy = 0.0;
+        for (int i = 0; i < d; ++i) {
+          dl[i] = 2.0 * (k[o + i] + gm[i] * yh[i] + bt[i] - v[o + i]) * gm[i];
+          mg += dl[i];
+          mgy += dl[i] * yh[i];
+        }
+        mg /= d;
+        mgy /= d;
+        for (int i = 0; i < d; ++i) dl[i] = (dl[i] - mg - yh[i] * mgy) / s; /* dl/dy */
+        matvec_t(W2b, dl, g1, d, dh);
+        for (int j = 0; j < dh; ++j) g1[j] *= gelu_prime(h[j]);
+        rank1_sub(W2, et, dl, a, d, dh);
+        rank1_sub(W1, et, g1, k + o, dh, d);
+        /* output with the updated weights */
+        matvec(W1, q + o, h, dh, d);
+        for (int j = 0; j < dh; ++j) a[j] = gelu(h[j]);
+        matvec(W2, a, y, d, dh);
+        ln_normalize(y, yh, d, eps);
+        for (int i = 0; i < d; ++i) z[o + i] = q[o + i] + gm[i] * yh[i] + bt[i];
+      }
+    }
+    memcpy(w1f + c * sz, W1, sz * sizeof(double));
+    memcpy(w2f + c * sz, W2, sz * sizeof(double));
+    free(W1); free(W2); free(W1b); free(W2b); free(h); free(a); free(g1); free(y); free(yh); free(dl);
+  }
+}
+
 /* Gradients of TTT-Linear by reverse-mode differentiation of the primal token
  * loop above (fp64), for L = sum(dz * Z) + sum(dwf * W_final):
  *   dq, dk, dv : [n, T, d]   deta : [n, T]   dw0 : [n, d, d]   (dwf may be NULL).

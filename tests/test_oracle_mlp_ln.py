@@ -1,0 +1,157 @@
+"""Pins of the oracle of TTT-MLP with layer norm and residual inside f.
+
+Pages: [TTT] news article, part 03 §9: f always contains layer normalization and
+a residual connection, f(x) = x + LN(f_res(x)); TTT-MLP's f_res is a two-layer
+MLP with hidden width 4d and GELU.  Here f(x) = x + LN(W2 GELU(W1 x)) with
+per-head gamma, beta and a small eps; both layers take their gradient at the
+mini-batch-start weights and the output uses the updated weights.
+"""
+import numpy as np
+import pytest
+from scipy.special import erf
+
+import oracle
+
+
+def _gelu(x):
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def _ln(y, gamma, beta, eps):
+    mu = y.mean()
+    s = np.sqrt(((y - mu) ** 2).mean() + eps)
+    return gamma * (y - mu) / s + beta
+
+
+def _f(W1, W2, x, gamma, beta, eps):
+    return x + _ln(W2 @ _gelu(W1 @ x), gamma, beta, eps)
+
+
+def _rand(seed, n, T, d, dh, eta_scale=0.05):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((n, T, d)) / np.sqrt(d)
+    k = r.standard_normal((n, T, d)) / np.sqrt(d)
+    v = r.standard_normal((n, T, d)) / np.sqrt(d)
+    w1 = r.standard_normal((n, dh, d)) * 0.4
+    w2 = r.standard_normal((n, d, dh)) * 0.4
+    gamma = 1.0 + 0.3 * r.standard_normal((n, d))
+    beta = 0.1 * r.standard_normal((n, d))
+    eta = eta_scale / (1.0 + np.exp(-r.standard_normal((n, T))))
+    return q, k, v, w1, w2, gamma, beta, eta
+
+
+def test_step_is_gradient_fd():
+    """T = b = 1: each layer moves by -eta times the gradient of |f(k) - v|^2,
+    checked against central differences of the loss written out here."""
+    d, dh, eps, eta = 5, 7, 1e-6, 0.01
+    q, k, v, w1, w2, gamma, beta, _ = _rand(1, 1, 1, d, dh)
+    _, w1f, w2f = oracle.mlp_ln_primal(q, k, v, w1, w2, gamma, beta, np.array([[eta]]), 1, eps)
+    x, t, g0, b0 = k[0, 0], v[0, 0], gamma[0], beta[0]
+
+    def loss(A, B):
+        return float(np.sum((_f(A, B, x, g0, b0, eps) - t) ** 2))
+
+    h = 1e-6
+    for W, Wf, which in ((w1[0], w1f[0], 1), (w2[0], w2f[0], 2)):
+        fd = np.zeros_like(W)
+        for idx in np.ndindex(W.shape):
+            P, M = W.copy(), W.copy()
+            P[idx] += h
+            M[idx] -= h
+            if which == 1:
+                fd[idx] = (loss(P, w2[0]) - loss(M, w2[0])) / (2 * h)
+            else:
+                fd[idx] = (loss(w1[0], P) - loss(w1[0], M)) / (2 * h)
+        np.testing.assert_allclose((W - Wf) / eta, fd, rtol=1e-6, atol=1e-7)
+
+
+def test_eta_zero_closed_form():
+    q, k, v, w1, w2, gamma, beta, eta = _rand(2, 2, 20, 6, 12)
+    z, w1f, w2f = oracle.mlp_ln_primal(q, k, v, w1, w2, gamma, beta, np.zeros_like(eta), 4)
+    np.testing.assert_array_equal(w1f, w1)
+    np.testing.assert_array_equal(w2f, w2)
+    for c in range(2):
+        for t in range(20):
+            np.testing.assert_allclose(z[c, t], _f(w1[c], w2[c], q[c, t], gamma[c], beta[c], 1e-6),
+                                       rtol=0, atol=1e-14)
+
+
+def test_zero_gamma_freezes_state():
+    """gamma = 0: f(x) = x + beta does not depend on the weights, so neither layer
+    moves and Z = Q + beta."""
+    q, k, v, w1, w2, gamma, beta, eta = _rand(3, 2, 32, 6, 12)
+    z, w1f, w2f = oracle.mlp_ln_primal(q, k, v, w1, w2, np.zeros_like(gamma), beta, eta, 16)
+    np.testing.assert_array_equal(w1f, w1)
+    np.testing.assert_array_equal(w2f, w2)
+    np.testing.assert_allclose(z, q + beta[:, None, :], rtol=0, atol=1e-15)
+
+
+def test_output_rows_are_normalised():
+    q, k, v, w1, w2, _, _, eta = _rand(4, 2, 32, 16, 24)
+    z, _, _ = oracle.mlp_ln_primal(q, k, v, w1, w2, np.ones((2, 16)), np.zeros((2, 16)), eta, 8)
+    dz = z - q
+    np.testing.assert_allclose(dz.mean(axis=2), 0.0, atol=1e-14)
+    ms = (dz ** 2).mean(axis=2)
+    assert np.all(ms < 1.0) and np.all(ms > 0.99)
+
+
+def test_second_layer_row_shift_invariance():
+    """LN removes the mean over the outputs, and its gradient sums to zero over
+    them.  So adding the same u^T to every row of W2 changes neither Z, nor W1's
+    gradient (W2^T delta gains u * sum(delta) = 0), nor W2's own gradient:
+    Z and W1_final are unchanged and W2_final shifts by exactly 1 u^T."""
+    d, dh = 8, 16
+    q, k, v, w1, w2, gamma, beta, eta = _rand(5, 1, 48, d, dh)
+    u = np.random.default_rng(9).standard_normal(dh)
+    shift = np.outer(np.ones(d), u)[None]
+    z1, a1, b1 = oracle.mlp_ln_primal(q, k, v, w1, w2, gamma, beta, eta, 16)
+    z2, a2, b2 = oracle.mlp_ln_primal(q, k, v, w1, w2 + shift, gamma, beta, eta, 16)
+    np.testing.assert_allclose(z2, z1, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(a2, a1, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(b2 - b1, shift, rtol=0, atol=1e-11)
+
+
+def test_b1_is_online_gd():
+    d, dh, eps = 6, 10, 1e-6
+    q, k, v, w1, w2, gamma, beta, eta = _rand(6, 1, 12, d, dh)
+    z, w1f, w2f = oracle.mlp_ln_primal(q, k, v, w1, w2, gamma, beta, eta, 1, eps)
+    W1, W2 = w1[0].copy(), w2[0].copy()
+    g0, b0 = gamma[0], beta[0]
+    for t in range(12):
+        x = k[0, t]
+        h = W1 @ x
+        a = _gelu(h)
+        y = W2 @ a
+        mu = y.mean()
+        s = np.sqrt(((y - mu) ** 2).mean() + eps)
+        yh = (y - mu) / s
+        gr = 2 * (x + g0 * yh + b0 - v[0, t]) * g0
+        delta = (gr - gr.mean() - yh * (gr * yh).mean()) / s
+        gp = 0.5 * (1 + erf(h / np.sqrt(2))) + h * np.exp(-0.5 * h * h) / np.sqrt(2 * np.pi)
+        W1n = W1 - eta[0, t] * np.outer((W2.T @ delta) * gp, x)
+        W2 = W2 - eta[0, t] * np.outer(delta, a)
+        W1 = W1n
+        np.testing.assert_allclose(z[0, t], _f(W1, W2, q[0, t], g0, b0, eps), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(w1f[0], W1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(w2f[0], W2, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,T,d,dh,b", [(2, 48, 16, 64, 16), (1, 37, 8, 32, 5), (2, 64, 64, 256, 16)])
+def test_dual_equals_primal(n, T, d, dh, b):
+    q, k, v, w1, w2, gamma, beta, eta = _rand(7 + T, n, T, d, dh)
+    w1 *= 0.25
+    w2 *= 0.25
+    got = oracle.mlp_ln_primal(q, k, v, w1, w2, gamma, beta, eta, b)
+    ref = oracle.mlp_ln_dual_f64(q, k, v, w1, w2, gamma, beta, eta, b)
+    for x, r in zip(got, ref):
+        assert oracle.max_rel_err(x, r) < 1e-12
+
+
+def test_state_passing_bitwise():
+    q, k, v, w1, w2, gamma, beta, eta = _rand(8, 2, 64, 8, 16)
+    z, a, b = oracle.mlp_ln_primal(q, k, v, w1, w2, gamma, beta, eta, 16)
+    z1, a1, b1 = oracle.mlp_ln_primal(q[:, :32], k[:, :32], v[:, :32], w1, w2, gamma, beta, eta[:, :32], 16)
+    z2, a2, b2 = oracle.mlp_ln_primal(q[:, 32:], k[:, 32:], v[:, 32:], a1, b1, gamma, beta, eta[:, 32:], 16)
+    np.testing.assert_array_equal(np.concatenate([z1, z2], axis=1), z)
+    np.testing.assert_array_equal(a2, a)
+    np.testing.assert_array_equal(b2, b)
