@@ -101,7 +101,7 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int):
+def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = False):
     import oracle
 
     chains = ti.sample_chains(cfg, sample_chains)
@@ -109,7 +109,16 @@ def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int):
                     inp_full.w1, inp_full.w2, inp_full.eta_buf, inp_full.eta_strides)
     threads = oracle.max_threads()
     t0 = time.perf_counter()
-    oracle.run_inputs(sub, threads=threads)
+    if ln:  # the layer-norm forms, with the benchmark's gamma = 1, beta = 0
+        one, zero = np.ones((len(chains), cfg.d)), np.zeros((len(chains), cfg.d))
+        if cfg.is_mlp:
+            oracle.mlp_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(1), sub.w_rows(2), one, zero, sub.eta_rows(),
+                                 cfg.b, threads=threads)
+        else:
+            oracle.linear_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(1), one, zero, sub.eta_rows(), cfg.b,
+                                    threads=threads)
+    else:
+        oracle.run_inputs(sub, threads=threads)
     dt = time.perf_counter() - t0
     tokens = len(chains) * cfg.T / cfg.H           # token = all H heads of one position
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -188,9 +197,18 @@ def main():
         f1 = torch.empty((B, H, cfg.dh, d), dtype=torch.float32, device="cuda:0")
         f2 = torch.empty((B, H, d, cfg.dh), dtype=torch.float32, device="cuda:0")
         kname = ttt.mlp_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides)
+        if args.ln:
+            kname += " (layer norm)"
+            gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
+            bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
 
-        def step():
-            ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1, w2_final=f2)
+            def step():
+                ttt.mlp_ln_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], gam, bet, t["eta"], cfg.b, z=z,
+                               w1_final=f1, w2_final=f2)
+        else:
+            def step():
+                ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1,
+                            w2_final=f2)
     elif args.decode:
         # one call = one new token for all B*H sequences (T=1), positions advancing
         kname = ttt.linear_kernel_name(B, H, 1, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0, (0, 0, 0),
@@ -348,7 +366,7 @@ def main():
         if args.bwd:
             cpu = cpu_baseline_bwd(cfg, inp, args.cpu_sample_chains)
         else:
-            cpu = cpu_baseline(cfg, inp, args.cpu_sample_chains)
+            cpu = cpu_baseline(cfg, inp, args.cpu_sample_chains, ln=args.ln)
         log(f"bench: cpu baseline {cpu['value']:.3e} tokens/s ({cpu['sample']})")
 
     eta_desc = {(0, 0, 0): "scalar", (0, 1, 0): "per head"}.get(tuple(inp.eta_strides), "per token")
@@ -356,7 +374,8 @@ def main():
     form = "decode" if args.decode else ("primal" if args.primal else ("generic" if args.generic else ""))
     if args.ln:
         form = "layer-norm"
-        roof["note"] = "f(x) = x + LN(W x): layer norm and residual inside f"
+        roof["note"] = ("f(x) = x + LN(W2 GELU(W1 x))" if cfg.is_mlp else "f(x) = x + LN(W x)") + \
+            ": layer norm and residual inside f"
     if args.chunks > 1:
         form = f"chunked({args.chunks})"
         roof["note"] = "chunked forward: chunk maps + scan + parallel chunks (4 launches per call)"

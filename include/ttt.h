@@ -251,6 +251,24 @@ ttt_status ttt_mlp_validate(const ttt_mlp_desc* desc, const void* Q, const void*
 
 const char* ttt_mlp_kernel_name(const ttt_mlp_desc* desc);
 
+/*
+ * TTT-MLP with layer norm and residual inside f ([TTT] 03 §9: f always
+ * contains LN and a residual connection): f(x) = x + LN(W2 GELU(W1 x)), LN over
+ * the d outputs with per-head gamma, beta ([H, d] fp32) and eps as for
+ * ttt_linear_ln_fwd.  The gradient of |f(k) - v|^2 with respect to the
+ * pre-norm output is Delta = J_LN^T (2 (f(k) - v) * gamma), and the dual form
+ * carries over with Delta in place of 2 (W2 GELU(W1 k) - v):
+ * Z = Q + LN(W2 A_Q - Delta (diag(eta) triu(A_K^T A_Q))), both layers updated
+ * from Delta as in ttt_mlp_fwd.  Other arguments, support and errors as for
+ * ttt_mlp_fwd; in addition eps must be finite and >= 0 (TTT_ERR_SHAPE), gamma
+ * and beta non-NULL (TTT_ERR_NULL), 4-byte aligned (TTT_ERR_ALIGN) and not
+ * overlapping Z or the final states (TTT_ERR_ALIAS).
+ */
+ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                          const float* W1_0, const float* W2_0, const float* gamma, const float* beta,
+                          float eps, const float* eta, void* Z, float* W1_final, float* W2_final,
+                          void* stream);
+
 /* Human-readable text of a status code (never NULL). */
 const char* ttt_status_str(int status);
 

@@ -51,7 +51,7 @@ EXPORTS = (
     "ttt_linear_decode", "ttt_linear_decode_validate",
     "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes", "ttt_linear_ln_fwd",
     "ttt_linear_fwd_save", "ttt_linear_bwd", "ttt_linear_bwd_validate", "ttt_linear_bwd_kernel_name",
-    "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name",
+    "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name", "ttt_mlp_ln_fwd",
     "ttt_status_str", "ttt_abi_version",
 )
 
@@ -134,6 +134,9 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_kernel_name.restype = ctypes.c_char_p
     L.ttt_mlp_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp, vp]
     L.ttt_mlp_fwd.restype = ctypes.c_int
+    L.ttt_mlp_ln_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, fp, vp, fp,
+                                 fp, vp]
+    L.ttt_mlp_ln_fwd.restype = ctypes.c_int
     L.ttt_mlp_validate.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp]
     L.ttt_mlp_validate.restype = ctypes.c_int
     L.ttt_mlp_kernel_name.argtypes = [ctypes.POINTER(MlpDesc)]
@@ -474,6 +477,22 @@ def mlp_fwd(q, k, v, w1, w2, eta, b: int, out_dtype=None, w1_final=None, w2_fina
     w1 : [H, dh, d] or [B, H, dh, d] float32;  w2 : [H, d, dh] or [B, H, d, dh] float32
     returns (Z, W1_final [B,H,dh,d], W2_final [B,H,d,dh]).
     """
+    return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream)
+
+
+def mlp_ln_fwd(q, k, v, w1, w2, gamma, beta, eta, b: int, eps: float = 1e-6, out_dtype=None, w1_final=None,
+               w2_final=None, z=None, stream=None):
+    """TTT-MLP with layer norm and residual inside f: f(x) = x + LN(W2 GELU(W1 x)).
+
+    gamma, beta : [H, d] float32 (per head).  Other arguments as :func:`mlp_fwd`.
+    """
+    H, d = q.shape[1], q.shape[3]
+    if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
+        raise ValueError("gamma and beta must be [H, d]")
+    return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=(gamma, beta, eps))
+
+
+def _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=None):
     torch = _torch()
     B, H, T, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -495,11 +514,18 @@ def mlp_fwd(q, k, v, w1, w2, eta, b: int, out_dtype=None, w1_final=None, w2_fina
         w1_final = torch.empty((B, H, dh, d), dtype=torch.float32, device=q.device)
     if w2_final is None:
         w2_final = torch.empty((B, H, d, dh), dtype=torch.float32, device=q.device)
-    _check_dev(q, k, v, w1, w2, eta_t, z, w1_final, w2_final)
+    _check_dev(q, k, v, w1, w2, eta_t, z, w1_final, w2_final, *(ln[:2] if ln else ()))
     desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est)
-    st = lib().ttt_mlp_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(eta_t),
-                           _ptr(z), _ptr(w1_final), _ptr(w2_final), _stream_handle(stream))
-    _done(st, "ttt_mlp_fwd")
+    if ln is None:
+        st = lib().ttt_mlp_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(eta_t),
+                               _ptr(z), _ptr(w1_final), _ptr(w2_final), _stream_handle(stream))
+        _done(st, "ttt_mlp_fwd")
+    else:
+        gamma, beta, eps = ln
+        st = lib().ttt_mlp_ln_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(gamma),
+                                  _ptr(beta), float(eps), _ptr(eta_t), _ptr(z), _ptr(w1_final), _ptr(w2_final),
+                                  _stream_handle(stream))
+        _done(st, "ttt_mlp_ln_fwd")
     return z, w1_final, w2_final
 
 

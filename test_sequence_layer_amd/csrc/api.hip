@@ -267,6 +267,7 @@ ttt::MlpArgs make_mlp_args(const ttt_mlp_desc* d, const void* Q, const void* K, 
   a.Q = Q; a.K = K; a.V = V; a.W1 = W1; a.W2 = W2; a.w_bstride = d->w_batch_stride;
   a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
   a.Z = const_cast<void*>(Z); a.W1f = const_cast<float*>(W1f); a.W2f = const_cast<float*>(W2f);
+  a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
   return a;
 }
 
@@ -561,6 +562,31 @@ ttt_status ttt_mlp_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, c
   if (st != TTT_OK) return st;
   if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
   const ttt::MlpArgs a = make_mlp_args(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final);
+  const hipError_t e = ttt::launch_mlp(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                          const float* W1_0, const float* W2_0, const float* gamma, const float* beta, float eps,
+                          const float* eta, void* Z, float* W1_final, float* W2_final, void* stream) {
+  bool ok;
+  const ttt_status st = validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, &ok);
+  if (st != TTT_OK) return st;
+  if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
+  const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
+  if (chains == 0) return TTT_OK;
+  if (!gamma || !beta) return TTT_ERR_NULL;
+  if (!aligned(gamma, 4) || !aligned(beta, 4)) return TTT_ERR_ALIGN;
+  const int64_t hd_b = static_cast<int64_t>(desc->H) * desc->d * 4;
+  const int64_t z_b = chains * desc->T * desc->d * dtype_size(desc->out_dtype);
+  const int64_t w_b = chains * desc->d * desc->dh * 4;
+  for (Range out : {Range{Z, z_b}, Range{W1_final, w_b}, Range{W2_final, w_b}})
+    for (Range in : {Range{gamma, hd_b}, Range{beta, hd_b}})
+      if (overlaps(out, in)) return TTT_ERR_ALIAS;
+  ttt::MlpArgs a = make_mlp_args(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final);
+  a.gamma = gamma;
+  a.beta = beta;
+  a.eps = eps;
   const hipError_t e = ttt::launch_mlp(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }

@@ -80,6 +80,7 @@ struct __align__(16) Smem {
   uint16_t enl[BT * EROW];      //   and lo
   float zr[BT * PROW];          // W2 A_Q summed over waves, [t][i]
   float s2[BT * SROW];          // A_K^T A_Q summed over waves, [s][t]
+  float2 lnp[4][BT];            // layer norm: (mean, M2) of each output wave's 16 outputs, per token
 };
 
 // a pair of 4-wide tiles split into 8-slot hi and lo operands
@@ -120,10 +121,22 @@ __device__ __forceinline__ void gelu_and_prime(float x, float& g, float& gp) {
   gp = cdf + x * 0.39894228040143268f * __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);
 }
 
+// Sum over the 32 lanes of a half wave (lanes 0-31 or 32-63): DPP inside each
+// 16-lane row, then the neighbouring row.
+__device__ __forceinline__ float sum32(float x) {
+  x = sum16(x);
+  return x + __shfl_xor(x, 16);
+}
+
 __device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cast<const float4v*>(p); }
 __device__ __forceinline__ void st4(float* p, float4v x) { *reinterpret_cast<float4v*>(p) = x; }
 
-template <bool ETA_TOKEN>
+// LN: f(x) = x + LN(W2 GELU(W1 x)) (layer norm over the d outputs, per-head
+// gamma and beta, and a residual).  The loss gradient with respect to the
+// pre-norm output, Delta = J_LN^T (2 (f(k) - v) * gamma), takes the place of
+// E = 2 (W2 A_K - V); everything downstream is unchanged, and the output is
+// Z = Q + LN(W2 A_Q - Delta (diag(eta) triu(A_K^T A_Q))).
+template <bool ETA_TOKEN, bool LN>
 __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -180,6 +193,24 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
 
   float eta_c = 0.f;
   if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
+
+  // layer norm scale and shift: of outputs i, i + 1 for the phase-2 role (token
+  // tid / 32), of outputs 16w + 4g .. +3 for the output role of waves 0..3
+  float lg[2] = {0.f, 0.f}, lb[2] = {0.f, 0.f}, zg[4] = {0.f, 0.f, 0.f, 0.f}, zb[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (LN) {
+    const float* gm = a.gamma + static_cast<int64_t>(h) * D;
+    const float* bt = a.beta + static_cast<int64_t>(h) * D;
+    const int i2 = (2 * tid) & (D - 1);
+    lg[0] = gm[i2]; lg[1] = gm[i2 + 1];
+    lb[0] = bt[i2]; lb[1] = bt[i2 + 1];
+    if (w < 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        zg[r] = gm[16 * w + 4 * g + r];
+        zb[r] = bt[16 * w + 4 * g + r];
+      }
+    }
+  }
 
   // ---- resident state (this wave's hidden units J_w) ----
   // w1[jt][c4]  : W1[j = 32w + 16jt + li][c = 16 c4 + 4g + r]
@@ -301,8 +332,26 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
         y1 += sm.part[ww][t * PROW + i + 1];
       }
       const uint32_t vv = *reinterpret_cast<const uint32_t*>(&S.v[t * ROW + i]);
-      const float x0 = 2.f * (y0 - __uint_as_float(vv << 16));
-      const float x1 = 2.f * (y1 - __uint_as_float(vv & 0xffff0000u));
+      float x0, x1;
+      if constexpr (LN) {
+        // 32 consecutive threads (half a wave) hold token t's 64 outputs
+        const float mu = sum32(y0 + y1) * (1.f / D);
+        const float d0 = y0 - mu, d1 = y1 - mu;
+        const float rs = rsqrtf(sum32(d0 * d0 + d1 * d1) * (1.f / D) + a.eps);
+        const float h0 = d0 * rs, h1 = d1 * rs;
+        const uint32_t kk = *reinterpret_cast<const uint32_t*>(&S.k[t * ROW + i]);
+        // dl/df = 2 (k + gamma yhat + beta - v), times gamma: the gradient at yhat
+        const float g0 = 2.f * (__uint_as_float(kk << 16) + lg[0] * h0 + lb[0] - __uint_as_float(vv << 16)) * lg[0];
+        const float g1 =
+            2.f * (__uint_as_float(kk & 0xffff0000u) + lg[1] * h1 + lb[1] - __uint_as_float(vv & 0xffff0000u)) * lg[1];
+        const float mg = sum32(g0 + g1) * (1.f / D);
+        const float mgy = sum32(g0 * h0 + g1 * h1) * (1.f / D);
+        x0 = (g0 - mg - h0 * mgy) * rs;
+        x1 = (g1 - mg - h1 * mgy) * rs;
+      } else {
+        x0 = 2.f * (y0 - __uint_as_float(vv << 16));
+        x1 = 2.f * (y1 - __uint_as_float(vv & 0xffff0000u));
+      }
       const float ne = -(ETA_TOKEN ? S.eta[t] : eta_c);
       uint32_t hi, lo;
       split2(x0, x1, hi, lo);
@@ -430,6 +479,9 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     __syncthreads();  // #4
 
     // ---- phase 5: Z[t][i] = (W2 A_Q)[i][t] + sum_s (-eta_s E[i][s]) S2[s][t] [s <= t], waves 0..3 ----
+    // (with the layer norm: Z = Q + LN of that, over the 64 outputs of each token)
+    float4v z;
+    bf16x4 qz;
     if (w < 4) {
       const int it = w;
       bf16x4 s2h, s2l;
@@ -446,9 +498,41 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       const bf16x4 eh = read_cols<EROW>(sm.enh, 0, 16 * it, li, g);
       const bf16x4 el = read_cols<EROW>(sm.enl, 0, 16 * it, li, g);
       // C: (W2 A_Q)[i = 16it + 4g + r][t = li]
-      float4v z = ld4(&sm.zr[li * PROW + 16 * it + 4 * g]);
+      z = ld4(&sm.zr[li * PROW + 16 * it + 4 * g]);
       z = mfma3_16(eh, el, s2h, s2l, z);
-      float* zp = Zg + (static_cast<size_t>(n) * BT + li) * D + 16 * it + 4 * g;
+      if constexpr (LN) {
+        // Q[t = li][i = 16it + 4g + r] for the residual, read before the barrier below,
+        // after which the other waves may restage this slot
+        qz = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * it + 4 * g]);
+        // mean and M2 of token li's 16 outputs in this wave (4 here, 4 lane groups)
+        float m = z[0] + z[1] + z[2] + z[3];
+        m += __shfl_xor(m, 16);
+        m += __shfl_xor(m, 32);
+        m *= 1.f / 16.f;
+        float m2 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m2 += (z[r] - m) * (z[r] - m);
+        m2 += __shfl_xor(m2, 16);
+        m2 += __shfl_xor(m2, 32);
+        if (g == 0) sm.lnp[w][li] = make_float2(m, m2);
+      }
+    }
+    if constexpr (LN) __syncthreads();  // #5: every output wave's statistics
+    if (w < 4) {
+      if constexpr (LN) {
+        // combine the 4 waves' (mean, M2) over equal counts exactly
+        float2 p[4];
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) p[ww] = sm.lnp[ww][li];
+        const float mu = 0.25f * (p[0].x + p[1].x + p[2].x + p[3].x);
+        float m2 = p[0].y + p[1].y + p[2].y + p[3].y;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) m2 += 16.f * (p[ww].x - mu) * (p[ww].x - mu);
+        const float rs = rsqrtf(m2 * (1.f / D) + a.eps);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qz[r]) + zg[r] * (z[r] - mu) * rs + zb[r];
+      }
+      float* zp = Zg + (static_cast<size_t>(n) * BT + li) * D + 16 * w + 4 * g;
       *reinterpret_cast<float4v*>(zp) = z;  // 64-byte pieces of a row per wave, merged in the L2
     }
   };
@@ -479,17 +563,17 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   }
 }
 
-template <bool TOK>
+template <bool TOK, bool LN>
 hipError_t launch_tok(const MlpArgs& a, hipStream_t s) {
   const size_t smem = sizeof(Smem);
   static bool attr_set = false;  // benign race: every caller sets the same value
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ttt_mlp_fwd_d64h256b16<TOK>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ttt_mlp_fwd_d64h256b16<TOK, LN>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((ttt_mlp_fwd_d64h256b16<TOK>), dim3(a.B * a.H), dim3(kThreads), smem, s, a);
+  hipLaunchKernelGGL((ttt_mlp_fwd_d64h256b16<TOK, LN>), dim3(a.B * a.H), dim3(kThreads), smem, s, a);
   return hipGetLastError();
 }
 
@@ -500,12 +584,12 @@ bool mlp_supported(const MlpArgs& a) {
 }
 
 const char* mlp_name(const MlpArgs& a) {
-  (void)a;
-  return "ttt_mlp_fwd_d64h256b16";
+  return a.gamma ? "ttt_mlp_fwd_d64h256b16 (layer norm)" : "ttt_mlp_fwd_d64h256b16";
 }
 
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t s) {
-  return a.est != 0 ? launch_tok<true>(a, s) : launch_tok<false>(a, s);
+  if (a.gamma) return a.est != 0 ? launch_tok<true, true>(a, s) : launch_tok<false, true>(a, s);
+  return a.est != 0 ? launch_tok<true, false>(a, s) : launch_tok<false, false>(a, s);
 }
 
 }  // namespace ttt

@@ -74,6 +74,10 @@ struct MlpArgs {
   void* Z;
   float* W1f;
   float* W2f;
+  // Layer norm and residual inside f (f(x) = x + LN(W2 GELU(W1 x))); gamma == nullptr: plain f.
+  const float* gamma;   // [H][d]
+  const float* beta;    // [H][d]
+  float eps;
 };
 
 // Primal form (token by token): full forward and decode.
