@@ -177,7 +177,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
+        print(f"bench.py: the benchmark runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the (sequence, head) chains are independent, so N GPUs would each run this same kernel on "
               "1/N of them with no communication", file=sys.stderr)
         sys.exit(2)
