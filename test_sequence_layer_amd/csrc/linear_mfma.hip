@@ -76,15 +76,19 @@ static_assert(sizeof(Slot) % 16 == 0, "slot size");
 // lane group l/16 = token / 4).  Sums over a wave's 16 outputs are DPP
 // reductions inside the 16-lane row (sum16); the 4 wave partials meet in LDS.
 struct LnShared {
-  float2 part[3][4][BT];  // [exchange][wave][token]
+  float2 part[3][4][BT];  // [exchange][wave][token]: each wave's partials
+  float2 comb[3][4][BT];  // [exchange][wave][token]: the combined values, one copy per wave
 };
 
 // Mean and 1/sqrt(var + eps) over the 64 outputs of the 4 tokens 4g + r this
 // lane holds (x[r] = output 16w + l%16 of token 4g + r).  Each wave's
 // (mean, M2) over its 16 outputs are combined exactly (equal counts), which
-// avoids the cancellation of raw power sums.
-__device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs[4], float2 (*part)[BT], int w,
-                                         int li, int g, float eps) {
+// avoids the cancellation of raw power sums.  The combination is done once per
+// token: lane l%16 of every 16-lane row takes token l%16, the wave stores the
+// results in its own comb slot, and each lane reads back its 4 tokens (one
+// wave's LDS accesses complete in order, so no barrier is needed for that).
+__device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs[4], float2 (*part)[BT],
+                                         float2* comb, int w, int li, int g, float eps) {
   float mw[4], m2[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -97,17 +101,21 @@ __device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs
     for (int r = 0; r < 4; ++r) part[w][4 * g + r] = make_float2(mw[r], m2[r]);
   }
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  {
     float2 p[4];
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) p[ww] = part[ww][4 * g + r];
+    for (int ww = 0; ww < 4; ++ww) p[ww] = part[ww][li];
     const float m = 0.25f * (p[0].x + p[1].x + p[2].x + p[3].x);
     float M2 = p[0].y + p[1].y + p[2].y + p[3].y;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) M2 += 16.f * (p[ww].x - m) * (p[ww].x - m);
-    mu[r] = m;
-    rs[r] = rsqrtf(M2 * (1.f / 64.f) + eps);
+    if (g == 0) comb[li] = make_float2(m, rsqrtf(M2 * (1.f / 64.f) + eps));
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float2 c = comb[4 * g + r];
+    mu[r] = c.x;
+    rs[r] = c.y;
   }
 }
 
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       // y = W k (pk), f(k) = k + LN(y); dl/dy through LN (mini-batch-start state)
       float mu[4], rs[4], yh[4], gr[4], s1[4], s2[4];
       const float yk[4] = {pk[0], pk[1], pk[2], pk[3]};
-      ln_stats(yk, mu, rs, lns.part[0], w, li, g, a.eps);
+      ln_stats(yk, mu, rs, lns.part[0], lns.comb[0][w], w, li, g, a.eps);
       const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);   // V[4g + r][16wg + li]
       const bf16x4 kc = read_cols<ROW>(S.k, 0, 16 * wg, li, g);   // K[4g + r][16wg + li]
 #pragma unroll
@@ -376,16 +384,21 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
         for (int r = 0; r < 4; ++r) lns.part[1][w][4 * g + r] = make_float2(s1[r], s2[r]);
       }
       __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      {
+        // the two means over the 64 outputs, once per token (as in ln_stats)
         float mg = 0.f, mgy = 0.f;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-          const float2 p = lns.part[1][ww][4 * g + r];
+          const float2 p = lns.part[1][ww][li];
           mg += p.x;
           mgy += p.y;
         }
-        gv[r] = -et[r] * (gr[r] - mg * (1.f / 64.f) - yh[r] * mgy * (1.f / 64.f)) * rs[r];
+        if (g == 0) lns.comb[1][w][li] = make_float2(mg * (1.f / 64.f), mgy * (1.f / 64.f));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float2 c = lns.comb[1][w][4 * g + r];
+        gv[r] = -et[r] * (gr[r] - c.x - yh[r] * c.y) * rs[r];
       }
     } else {
       float e[4];
@@ -439,7 +452,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       float zz[4], mu[4], rs[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) zz[r] = z[r];
-      ln_stats(zz, mu, rs, lns.part[2], w, li, g, a.eps);
+      ln_stats(zz, mu, rs, lns.part[2], lns.comb[2][w], w, li, g, a.eps);
       const bf16x4 qc = read_cols<ROW>(S.q, 0, 16 * wg, li, g);  // Q[4g + r][16wg + li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qc[r]) + ln_g * (zz[r] - mu[r]) * rs[r] + ln_b;

@@ -566,13 +566,11 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
 template <bool TOK, bool LN>
 hipError_t launch_tok(const MlpArgs& a, hipStream_t s) {
   const size_t smem = sizeof(Smem);
-  static bool attr_set = false;  // benign race: every caller sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ttt_mlp_fwd_d64h256b16<TOK, LN>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // the dynamic LDS limit is raised on every launch (a host-side attribute, no
+  // stream work), so the library keeps no state between calls
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ttt_mlp_fwd_d64h256b16<TOK, LN>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((ttt_mlp_fwd_d64h256b16<TOK, LN>), dim3(a.B * a.H), dim3(kThreads), smem, s, a);
   return hipGetLastError();
 }
