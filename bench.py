@@ -288,7 +288,7 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps      # one call per step (the chunked form: 4 launches)
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps      # one call per step (the chunked form: 3 launches)
     ms_per_step = max(wall * 1e3 / args.steps, kernel_ms)
     tokens = B * (1 if args.decode else T)
     value = tokens / (ms_per_step / 1e3)
@@ -378,7 +378,7 @@ def main():
             ": layer norm and residual inside f"
     if args.chunks > 1:
         form = f"chunked({args.chunks})"
-        roof["note"] = "chunked forward: chunk maps + scan + parallel chunks (4 launches per call)"
+        roof["note"] = "chunked forward: chunk maps + scan + parallel chunks (3 launches per call)"
     direction = "fwd"
     if args.save:
         form, direction = "", "fwd (saving E for the backward)"

@@ -27,6 +27,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +42,9 @@ KERNEL_SOURCES = {
     "ttt_linear_generic_kernel": ["linear_generic.hip", "ttt_internal.h"],
     "ttt_linear_bwd_d64b16": ["linear_bwd_mfma.hip", "mfma_common.h", "ttt_internal.h"],
     "ttt_linear_bwd_generic_kernel": ["linear_bwd_generic.hip", "ttt_internal.h"],
-    "ttt_mlp_fwd_d64h256b16": ["mlp.hip", "ttt_internal.h"],
+    "ttt_mlp_fwd_d64h256b16": ["mlp.hip", "mfma_common.h", "ttt_internal.h"],
+    "ttt_linear_primal_kernel": ["linear_primal.hip", "ttt_internal.h"],
+    "ttt_linear_chunk_scan": ["linear_chunked.hip", "ttt_internal.h"],
 }
 
 
@@ -90,11 +93,15 @@ def counter_kib(pmc_dir: str, name_substr: str, counter: str):
 
 
 def summarize(stats_dir, fetch_dir, write_dir, kernel, workload, algorithmic_bytes, command, out_dir=PROFILES,
-              timed=0):
-    calls, avg_ns, min_ns, full_name = kernel_stats(stats_dir, kernel)
-    timed_ns, ntimed = last_launches_avg_ns(stats_dir, kernel, timed)
-    fetch = counter_kib(fetch_dir, kernel, "FETCH_SIZE")
-    write = counter_kib(write_dir, kernel, "WRITE_SIZE")
+              timed=0, match=None):
+    """``match``: the substring that picks the kernel's rows in the CSVs (default:
+    ``kernel``), e.g. a template argument list when one run launches several
+    instantiations of one kernel."""
+    match = match or kernel
+    calls, avg_ns, min_ns, full_name = kernel_stats(stats_dir, match)
+    timed_ns, ntimed = last_launches_avg_ns(stats_dir, match, timed)
+    fetch = counter_kib(fetch_dir, match, "FETCH_SIZE")
+    write = counter_kib(write_dir, match, "WRITE_SIZE")
     cf = counter_kib(fetch_dir, COPY_KERNEL, "FETCH_SIZE")
     cw = counter_kib(write_dir, COPY_KERNEL, "WRITE_SIZE")
     f_fetch = COPY_BYTES / (statistics.median(cf) * 1024)
@@ -140,6 +147,55 @@ def summarize(stats_dir, fetch_dir, write_dir, kernel, workload, algorithmic_byt
     return md
 
 
+def _kernel_id(symbol: str) -> str:
+    """The kernel's own name in a demangled symbol (namespaces, template
+    arguments and parameters stripped)."""
+    return re.search(r"(ttt_\w+)", symbol.split("(ttt::")[0].replace("(anonymous namespace)", "")).group(1)
+
+
+def summarize_call(stats_dir, fetch_dir, write_dir, name, parts, algorithmic_bytes, command, out_dir=PROFILES,
+                   timed=0):
+    """profiles/<name>.md for an entry point that launches several kernels per
+    call (``parts``: (label, substring) pairs, one per launch in a call): each
+    launch's average duration and scaled HBM bytes, their sums per call, and the
+    call's algorithmic bytes over the summed time of the timed calls."""
+    cf = counter_kib(fetch_dir, COPY_KERNEL, "FETCH_SIZE")
+    cw = counter_kib(write_dir, COPY_KERNEL, "WRITE_SIZE")
+    f_fetch = COPY_BYTES / (statistics.median(cf) * 1024)
+    f_write = COPY_BYTES / (statistics.median(cw) * 1024)
+    rows, t_sum, rd_sum, wr_sum = [], 0.0, 0.0, 0.0
+    for label, match in parts:
+        calls, avg_ns, _, full_name = kernel_stats(stats_dir, match)
+        timed_ns, ntimed = last_launches_avg_ns(stats_dir, match, timed)
+        rd = statistics.median(counter_kib(fetch_dir, match, "FETCH_SIZE")) * 1024 * f_fetch
+        wr = statistics.median(counter_kib(write_dir, match, "WRITE_SIZE")) * 1024 * f_write
+        rows.append((label, full_name, calls, avg_ns, timed_ns, ntimed, rd, wr))
+        t_sum, rd_sum, wr_sum = t_sum + timed_ns, rd_sum + rd, wr_sum + wr
+    os.makedirs(out_dir, exist_ok=True)
+    md = os.path.join(out_dir, name + ".md")
+    with open(md, "w") as fh:
+        fh.write(f"# {name}\n\n")
+        fh.write("Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root):\n\n")
+        for c in command:
+            fh.write(f"    {c}\n")
+        fh.write(f"\nCopy calibration (1 GiB copy) FETCH / WRITE raw: {statistics.median(cf):.0f} / "
+                 f"{statistics.median(cw):.0f} KiB; scale factors {f_fetch:.4f} / {f_write:.4f}.\n\n")
+        fh.write("| launch | kernel symbol | launches traced | average | average of the timed launches "
+                 "| HBM read | HBM written |\n|---|---|---|---|---|---|---|\n")
+        for label, full_name, calls, avg_ns, timed_ns, ntimed, rd, wr in rows:
+            fh.write(f"| {label} | `{full_name}` | {calls} | {avg_ns / 1e3:.1f} us | {timed_ns / 1e3:.1f} us "
+                     f"(last {ntimed}) | {rd:.4e} B | {wr:.4e} B |\n")
+        fh.write(f"\n| per call | value |\n|---|---|\n")
+        fh.write(f"| summed launch time (timed launches) | {t_sum / 1e3:.1f} us |\n")
+        fh.write(f"| HBM traffic | {rd_sum + wr_sum:.4e} B |\n")
+        fh.write(f"| algorithmic bytes | {algorithmic_bytes:.4e} B |\n")
+        fh.write(f"| traffic / algorithmic | {(rd_sum + wr_sum) / algorithmic_bytes:.4f} |\n")
+        fh.write(f"| achieved (algorithmic bytes / summed launch time) | {algorithmic_bytes / t_sum:.1f} GB/s |\n")
+        kernels = sorted({_kernel_id(r[1]) for r in rows})
+        fh.write(f"| kernel source hashes | {', '.join(f'{k} {source_hash(k)}' for k in kernels)} |\n")
+    return md
+
+
 COUNTER_SET = ("MfmaUtil", "VALUBusy", "LDSBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
 
 
@@ -179,17 +235,27 @@ def main():
     ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
-    ap.add_argument("--kernel", required=True)
-    ap.add_argument("--workload", required=True)
+    ap.add_argument("--kernel")
+    ap.add_argument("--workload")
+    ap.add_argument("--call", help="summarise every launch of one multi-kernel call into profiles/CALL.md")
+    ap.add_argument("--part", action="append", default=[], help="LABEL=SUBSTRING, one per launch of the call")
     ap.add_argument("--algorithmic-bytes", type=float)
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--timed", type=int, default=200, help="launches in the benchmark's timed region")
+    ap.add_argument("--match", help="substring that picks the kernel's rows (default: --kernel)")
     a = ap.parse_args()
+    if a.call:
+        parts = [tuple(p.split("=", 1)) for p in a.part]
+        print(summarize_call(a.stats, a.fetch, a.write, a.call, parts, a.algorithmic_bytes, a.command,
+                             timed=a.timed))
+        return
+    if not a.kernel or not a.workload:
+        ap.error("--kernel and --workload are required")
     if a.counters:
         print(summarize_counters(a.counters, a.kernel, a.workload, a.algorithmic_flops, a.command))
         return
     print(summarize(a.stats, a.fetch, a.write, a.kernel, a.workload, a.algorithmic_bytes, a.command,
-                    timed=a.timed))
+                    timed=a.timed, match=a.match))
 
 
 if __name__ == "__main__":
