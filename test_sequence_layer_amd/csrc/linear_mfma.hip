@@ -72,51 +72,57 @@ struct __align__(16) Slot {
 static_assert(sizeof(Slot) % 16 == 0, "slot size");
 
 // ---- layer norm across the row-split waves --------------------------------
-// A token's 64 outputs are spread over the 4 waves (16 each, at lanes l%16 of
-// lane group l/16 = token / 4).  Sums over a wave's 16 outputs are DPP
-// reductions inside the 16-lane row (sum16); the 4 wave partials meet in LDS.
+// The layer-norm path computes its projections transposed (W as the A operand),
+// so lane l holds token l%16 and outputs 16w + 4(l/16) + r, r = 0..3.  A sum
+// over a wave's 16 outputs of a token is then a lane-local sum of 4 and two
+// lane-group exchanges; the 4 wave partials meet in LDS.
 struct LnShared {
   float2 part[3][4][BT];  // [exchange][wave][token]: each wave's partials
-  float2 comb[3][4][BT];  // [exchange][wave][token]: the combined values, one copy per wave
 };
 
-// Mean and 1/sqrt(var + eps) over the 64 outputs of the 4 tokens 4g + r this
-// lane holds (x[r] = output 16w + l%16 of token 4g + r).  Each wave's
-// (mean, M2) over its 16 outputs are combined exactly (equal counts), which
-// avoids the cancellation of raw power sums.  The combination is done once per
-// token: lane l%16 of every 16-lane row takes token l%16, the wave stores the
-// results in its own comb slot, and each lane reads back its 4 tokens (one
-// wave's LDS accesses complete in order, so no barrier is needed for that).
-__device__ __forceinline__ void ln_stats(const float x[4], float mu[4], float rs[4], float2 (*part)[BT],
-                                         float2* comb, int w, int li, int g, float eps) {
-  float mw[4], m2[4];
+// Sum over the four 16-lane groups: v_permlane16_swap and v_permlane32_swap
+// with both operands x return x of the two rows (halves) of a pair, so the
+// sum of the pair is the same in every lane of it.
+__device__ __forceinline__ float sum_rows(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Mean and 1/sqrt(var + eps) of token l%16 over its 64 outputs (x[r]: output
+// 16w + 4g + r).  Each wave's (mean, M2) over its 16 outputs are combined
+// exactly across the waves (equal counts), which avoids the cancellation of
+// raw power sums.
+__device__ __forceinline__ float2 ln_stats(const float4v& x, float2 (*part)[BT], int w, int li, int g, float eps) {
+  const float mw = sum_rows((x[0] + x[1]) + (x[2] + x[3])) * (1.f / 16.f);
+  float m2 = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    mw[r] = sum16(x[r]) * (1.f / 16.f);
-    const float dv = x[r] - mw[r];
-    m2[r] = sum16(dv * dv);
+    const float dv = x[r] - mw;
+    m2 = fmaf(dv, dv, m2);
   }
-  if (li == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) part[w][4 * g + r] = make_float2(mw[r], m2[r]);
-  }
+  m2 = sum_rows(m2);
+  if (g == 0) part[w][li] = make_float2(mw, m2);
   __syncthreads();
-  {
-    float2 p[4];
+  float2 p[4];
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) p[ww] = part[ww][li];
-    const float m = 0.25f * (p[0].x + p[1].x + p[2].x + p[3].x);
-    float M2 = p[0].y + p[1].y + p[2].y + p[3].y;
+  for (int ww = 0; ww < 4; ++ww) p[ww] = part[ww][li];
+  const float m = 0.25f * ((p[0].x + p[1].x) + (p[2].x + p[3].x));
+  float M2 = (p[0].y + p[1].y) + (p[2].y + p[3].y);
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M2 += 16.f * (p[ww].x - m) * (p[ww].x - m);
-    if (g == 0) comb[li] = make_float2(m, rsqrtf(M2 * (1.f / 64.f) + eps));
+  for (int ww = 0; ww < 4; ++ww) {
+    const float dm = p[ww].x - m;
+    M2 = fmaf(16.f * dm, dm, M2);
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float2 c = comb[4 * g + r];
-    mu[r] = c.x;
-    rs[r] = c.y;
-  }
+  return make_float2(m, rsqrtf(M2 * (1.f / 64.f) + eps));
+}
+
+// Four fp32 values that are bf16 numbers -> packed bf16 (exact)
+__device__ __forceinline__ bf16x4 pack_exact(float4v x) {
+  const bf16x2 a = __builtin_convertvector(float2v{x[0], x[1]}, bf16x2);
+  const bf16x2 b = __builtin_convertvector(float2v{x[2], x[3]}, bf16x2);
+  return bf16x4{a[0], a[1], b[0], b[1]};
 }
 
 // MODE 0: forward (Z and the final state).  MODE 1: chunk maps P and R of a
@@ -130,6 +136,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
   static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks");
   static_assert(!LN || RB == 1, "the layer norm needs all 64 outputs of a token in one workgroup");
+  static_assert(!LN || (MODE == 0 && !SAVE), "the layer norm is a forward-only path");
   constexpr int NWV = 4 / RB;   // waves per workgroup
   constexpr int NT = 64 * NWV;  // threads per workgroup
   constexpr int CA = 256 / NT;  // 16-byte pieces of the Q|K tiles each thread stages per step
@@ -229,11 +236,18 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   // constant eta (scalar or per head)
   float eta_c = 0.f;
   if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
-  // LN scale and shift of output 16w + l%16
-  float ln_g = 0.f, ln_b = 0.f;
+  // LN scale and shift of outputs 16w + 4g + r (the transposed tiles), and the
+  // identity B operand that moves a transposed tile back: lane l holds
+  // B[k = 8g + j][n = l%16] = 1 if n = 4g + j (j < 4), else 0
+  float4v ln_g = {}, ln_b = {};
+  bf16x8 ident = {};
   if constexpr (LN) {
-    ln_g = a.gamma[h * D + 16 * wg + li];
-    ln_b = a.beta[h * D + 16 * wg + li];
+    const float4 gm = *reinterpret_cast<const float4*>(a.gamma + h * D + 16 * wg + 4 * g);
+    const float4 bt = *reinterpret_cast<const float4*>(a.beta + h * D + 16 * wg + 4 * g);
+    ln_g = float4v{gm.x, gm.y, gm.z, gm.w};
+    ln_b = float4v{bt.x, bt.y, bt.z, bt.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ident[j] = static_cast<__bf16>(li == 4 * g + j ? 1.f : 0.f);
   }
 
   // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
@@ -353,54 +367,68 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       const bf16x8 whi = cat(h0, h1), wlo = cat(l0, l1);
       const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
       const bf16x8 aq = cat(qx[2 * m], qx[2 * m + 1]);
-      pk = mfma32(ak, whi, pk);
-      pq = mfma32(aq, whi, pq);
-      sc = mfma32(ak, aq, sc);
-      pk = mfma32(ak, wlo, pk);
-      pq = mfma32(aq, wlo, pq);
+      if constexpr (LN) {
+        // transposed: P_K^T[i = 16w + 4g + r][t = li] (lane li holds token li)
+        pk = mfma32(whi, ak, pk);
+        pq = mfma32(whi, aq, pq);
+        sc = mfma32(ak, aq, sc);
+        pk = mfma32(wlo, ak, pk);
+        pq = mfma32(wlo, aq, pq);
+      } else {
+        pk = mfma32(ak, whi, pk);
+        pq = mfma32(aq, whi, pq);
+        sc = mfma32(ak, aq, sc);
+        pk = mfma32(ak, wlo, pk);
+        pq = mfma32(aq, wlo, pq);
+      }
     }
 
     // ---- E^T[t = 4g+r][i = 16w+li] = P_K - V ----
     // ---- G[s][i] = -eta_s (dl/dy)[s][i]: the gradient factor of the rank-16
     // update, also the operand of the Z correction ----
-    float gv[4];
+    bf16x4 bhi, blo;
     if constexpr (LN) {
-      // y = W k (pk), f(k) = k + LN(y); dl/dy through LN (mini-batch-start state)
-      float mu[4], rs[4], yh[4], gr[4], s1[4], s2[4];
-      const float yk[4] = {pk[0], pk[1], pk[2], pk[3]};
-      ln_stats(yk, mu, rs, lns.part[0], lns.comb[0][w], w, li, g, a.eps);
-      const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);   // V[4g + r][16wg + li]
-      const bf16x4 kc = read_cols<ROW>(S.k, 0, 16 * wg, li, g);   // K[4g + r][16wg + li]
+      // y = W k (pk, transposed: token li, outputs 16w + 4g + r), f(k) = k + LN(y);
+      // dl/dy through LN at the mini-batch-start state
+      const float2 st = ln_stats(pk, lns.part[0], w, li, g, a.eps);  // (mean, 1/std) of token li
+      const bf16x4 kr = *reinterpret_cast<const bf16x4*>(&S.k[li * ROW + 16 * wg + 4 * g]);
+      const bf16x4 vr = *reinterpret_cast<const bf16x4*>(&S.v[li * ROW + 16 * wg + 4 * g]);
+      float yh[4], gr[4], s1 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        yh[r] = (pk[r] - mu[r]) * rs[r];
-        const float res = static_cast<float>(kc[r]) + ln_g * yh[r] + ln_b - static_cast<float>(vc[r]);
-        gr[r] = 2.f * res * ln_g;
-        s1[r] = sum16(gr[r]);
-        s2[r] = sum16(gr[r] * yh[r]);
+        yh[r] = (pk[r] - st.x) * st.y;
+        const float res = static_cast<float>(kr[r]) - static_cast<float>(vr[r]) + ln_b[r] + ln_g[r] * yh[r];
+        gr[r] = 2.f * ln_g[r] * res;
+        s1 += gr[r];
+        s2 = fmaf(gr[r], yh[r], s2);
       }
-      if (li == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lns.part[1][w][4 * g + r] = make_float2(s1[r], s2[r]);
-      }
+      s1 = sum_rows(s1);
+      s2 = sum_rows(s2);
+      if (g == 0) lns.part[1][w][li] = make_float2(s1, s2);
       __syncthreads();
-      {
-        // the two means over the 64 outputs, once per token (as in ln_stats)
-        float mg = 0.f, mgy = 0.f;
+      float c1 = 0.f, c2 = 0.f;  // the two means over the 64 outputs
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          const float2 p = lns.part[1][ww][li];
-          mg += p.x;
-          mgy += p.y;
-        }
-        if (g == 0) lns.comb[1][w][li] = make_float2(mg * (1.f / 64.f), mgy * (1.f / 64.f));
+      for (int ww = 0; ww < 4; ++ww) {
+        const float2 p = lns.part[1][ww][li];
+        c1 += p.x;
+        c2 += p.y;
       }
+      c1 *= 1.f / 64.f;
+      c2 *= 1.f / 64.f;
+      const float sg = -(ETA_TOKEN ? S.eta[li] : eta_c) * st.y;
+      float d[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float2 c = lns.comb[1][w][4 * g + r];
-        gv[r] = -et[r] * (gr[r] - c.x - yh[r] * c.y) * rs[r];
-      }
+      for (int r = 0; r < 4; ++r) d[r] = sg * (gr[r] - c1 - yh[r] * c2);
+      // G[s][i] = d of token s, output i: split, then moved to lane i, slot s by
+      // the identity product (bf16 x 1 summed with zeros: exact)
+      bf16x4 dh, dl;
+      split4(d, dh, dl);
+      const bf16x4 z4 = {};
+      const float4v f0 = {0.f, 0.f, 0.f, 0.f};
+      bhi = pack_exact(mfma32(cat(dh, z4), ident, f0));
+      blo = pack_exact(mfma32(cat(dl, z4), ident, f0));
     } else {
+      float gv[4];
       float e[4];
       {
         const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);  // V[4g + r][16wg + li]
@@ -416,12 +444,11 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) gv[r] = -2.f * et[r] * e[r];
+      split4(gv, bhi, blo);
     }
 
     // ---- Z = P_Q + M G, with M[t][s] = S[s][t] [s <= t] (causal mask, diagonal
     // included), G the operand the update uses too ----
-    bf16x4 bhi, blo;
-    split4(gv, bhi, blo);
     float4v z = pq;
     if constexpr (MODE == 0) {
       float mv[4];
@@ -434,8 +461,14 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       // [Mlo Mlo] x [Ghi Glo] (the update's own G operand and no zero-padded
       // halves to build; the extra lo x lo product is below fp32 rounding).
       const bf16x8 gz = cat(bhi, blo);
-      z = mfma32(cat(mhi, mhi), gz, z);
-      z = mfma32(cat(mlo, mlo), gz, z);
+      if constexpr (LN) {
+        // transposed: Z^T = G^T M^T
+        z = mfma32(gz, cat(mhi, mhi), z);
+        z = mfma32(gz, cat(mlo, mlo), z);
+      } else {
+        z = mfma32(cat(mhi, mhi), gz, z);
+        z = mfma32(cat(mlo, mlo), gz, z);
+      }
     }
 
     // ---- W^T[c][i] += sum_s K[s][c] G[s][i] ----
@@ -446,18 +479,18 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       wt[t] = mfma32(cat(kt, kt), gb, wt[t]);
     }
 
-    // ---- store Z rows t = 4g + r, columns 16w + li ----
     if constexpr (LN) {
-      // z = q + LN(W_t q): normalise the pre-norm output over its 64 entries
-      float zz[4], mu[4], rs[4];
+      // z = q + LN(W_t q), transposed: token li, outputs 16w + 4g + r; the
+      // staging tile takes them as one 16-byte row piece
+      const float2 st = ln_stats(z, lns.part[2], w, li, g, a.eps);
+      const bf16x4 qr = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * wg + 4 * g]);
+      float o[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) zz[r] = z[r];
-      ln_stats(zz, mu, rs, lns.part[2], lns.comb[2][w], w, li, g, a.eps);
-      const bf16x4 qc = read_cols<ROW>(S.q, 0, 16 * wg, li, g);  // Q[4g + r][16wg + li]
-#pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qc[r]) + ln_g * (zz[r] - mu[r]) * rs[r] + ln_b;
-    }
-    if constexpr (MODE == 0) {
+      for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qr[r]) + ln_g[r] * ((z[r] - st.x) * st.y) + ln_b[r];
+      if (n > 0) flush_z(n - 1);
+      *reinterpret_cast<float4*>(&zbuf[n & 1][li * ZROW + 16 * w + 4 * g]) = make_float4(o[0], o[1], o[2], o[3]);
+    } else if constexpr (MODE == 0) {
+      // ---- store Z rows t = 4g + r, columns 16w + li ----
       if (n > 0) flush_z(n - 1);
       float* zb = &zbuf[n & 1][(4 * g) * ZROW + 16 * w + li];
 #pragma unroll
