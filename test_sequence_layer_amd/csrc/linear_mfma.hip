@@ -80,16 +80,6 @@ struct LnShared {
   float2 part[3][4][BT];  // [exchange][wave][token]: each wave's partials
 };
 
-// Sum over the four 16-lane groups: v_permlane16_swap and v_permlane32_swap
-// with both operands x return x of the two rows (halves) of a pair, so the
-// sum of the pair is the same in every lane of it.
-__device__ __forceinline__ float sum_rows(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 // Mean and 1/sqrt(var + eps) of token l%16 over its 64 outputs (x[r]: output
 // 16w + 4g + r).  Each wave's (mean, M2) over its 16 outputs are combined
 // exactly across the waves (equal counts), which avoids the cancellation of

@@ -1,7 +1,7 @@
 // Device helpers shared by the gfx950 matrix-core kernels of TTT-Linear
 // (forward and backward): operand types, the bf16 hi + lo split of fp32
 // values, transposing LDS column reads, streaming loads and stores, and
-// 16-lane sums.
+// sums within and across 16-lane rows.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 lane layouts (lane l, li = l % 16, g = l / 16):
 //   A operand  lane l holds A[m = li][k = 8g + j],  j = 0..7
@@ -117,9 +117,11 @@ __device__ __forceinline__ void store_merged<uint16_t>(uint16_t* p, float x) { *
 // [1,0,3,2] and [2,3,0,1] exchange neighbours 1 and 2 apart; row_half_mirror
 // (lane i <-> 7 - i within 8) and row_mirror (i <-> 15 - i) then fold the
 // quads, so after four adds every lane of the row holds the row's sum.
+// (Every source lane of these patterns lies in the row, so no lane keeps an old
+// value and the move needs no zeroed destination.)
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float sum16(float x) {
   x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
@@ -127,6 +129,20 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_mov<0x141>(x);  // row_half_mirror
   x += dpp_mov<0x140>(x);  // row_mirror
   return x;
+}
+
+// Sums across the 16-lane rows: v_permlane16_swap with both operands x
+// returns x of the two rows of a pair (rows 0, 1 and rows 2, 3), and
+// v_permlane32_swap x of the two halves of the wave, so each pair's sum is the
+// same in every lane of it.
+__device__ __forceinline__ float sum_row_pairs(float x) {  // rows 2p and 2p + 1
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_rows(float x) {  // all four rows
+  x = sum_row_pairs(x);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 }  // namespace mfma

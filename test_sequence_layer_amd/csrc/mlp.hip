@@ -124,8 +124,7 @@ __device__ __forceinline__ void gelu_and_prime(float x, float& g, float& gp) {
 // Sum over the 32 lanes of a half wave (lanes 0-31 or 32-63): DPP inside each
 // 16-lane row, then the neighbouring row.
 __device__ __forceinline__ float sum32(float x) {
-  x = sum16(x);
-  return x + __shfl_xor(x, 16);
+  return sum_row_pairs(sum16(x));
 }
 
 __device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cast<const float4v*>(p); }
@@ -505,15 +504,11 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
         // after which the other waves may restage this slot
         qz = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * it + 4 * g]);
         // mean and M2 of token li's 16 outputs in this wave (4 here, 4 lane groups)
-        float m = z[0] + z[1] + z[2] + z[3];
-        m += __shfl_xor(m, 16);
-        m += __shfl_xor(m, 32);
-        m *= 1.f / 16.f;
+        const float m = sum_rows((z[0] + z[1]) + (z[2] + z[3])) * (1.f / 16.f);
         float m2 = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) m2 += (z[r] - m) * (z[r] - m);
-        m2 += __shfl_xor(m2, 16);
-        m2 += __shfl_xor(m2, 32);
+        m2 = sum_rows(m2);
         if (g == 0) sm.lnp[w][li] = make_float2(m, m2);
       }
     }
