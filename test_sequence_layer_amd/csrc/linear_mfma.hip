@@ -189,7 +189,10 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   //   eta of token (tid & 15).
   // The maps have no query path: there V takes Q's place in the 16-byte
   // pieces and the 8-byte V loads are dropped (4 KB per step, not 6).
-  const u32x4* tileA = MODE == 0 ? Qg : reinterpret_cast<const u32x4*>(Vg);
+  // (The P map runs the recurrence with V = 0, scaling its V tile by zero: its
+  // "V" pieces are read from the K tile, whose lines the K pieces of the same
+  // step fetch anyway, so they cost L2 hits instead of HBM reads.)
+  const u32x4* tileA = MODE == 0 ? Qg : reinterpret_cast<const u32x4*>(map_r ? Vg : Kg);
   const u32x4* srcA[CA];
 #pragma unroll
   for (int c = 0; c < CA; ++c) {
