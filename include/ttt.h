@@ -133,8 +133,8 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
 int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t nchunks);
 
 /*
- * TTT-Linear with layer norm and residual inside f ([TTT] 03 §9: "for
- * stability, f always contains LN and a residual connection"):
+ * TTT-Linear with layer norm and residual inside f ([TTT] 03 §9: the layer's
+ * f carries a layer norm and a residual connection around W x, for stability):
  *     f(x) = x + LN(W x),  LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps) + beta
  * over the d outputs (var = mean of squared deviations), gamma and beta fp32
  * [H, d] per head.  The gradient of |f(k) - v|^2 stays rank one per token,

@@ -235,12 +235,12 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   float4v ln_g = {}, ln_b = {};
   bf16x8 ident = {};
   if constexpr (LN) {
-    const float4 gm = *reinterpret_cast<const float4*>(a.gamma + h * D + 16 * wg + 4 * g);
-    const float4 bt = *reinterpret_cast<const float4*>(a.beta + h * D + 16 * wg + 4 * g);
-    ln_g = float4v{gm.x, gm.y, gm.z, gm.w};
-    ln_b = float4v{bt.x, bt.y, bt.z, bt.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ident[j] = static_cast<__bf16>(li == 4 * g + j ? 1.f : 0.f);
+    for (int j = 0; j < 4; ++j) {  // (gamma and beta are only 4-byte aligned)
+      ln_g[j] = a.gamma[h * D + 16 * wg + 4 * g + j];
+      ln_b[j] = a.beta[h * D + 16 * wg + 4 * g + j];
+      ident[j] = static_cast<__bf16>(li == 4 * g + j ? 1.f : 0.f);
+    }
   }
 
   // resident state: wt[a][r] = W[16w + li][16a + 4g + r]

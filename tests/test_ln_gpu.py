@@ -97,3 +97,72 @@ def test_ln_errors(ttt):
     with pytest.raises(ttt.TTTError) as ei:
         ttt.linear_ln_fwd(x, x, x, w0, g, g, 0.1, 16, eps=-1.0)
     assert ei.value.status == 2
+
+
+def test_ln_bf16_output_is_rounded_fp32(ttt):
+    """bf16 Z: the same kernel arithmetic, rounded to bf16 (nearest even) at the
+    store, so it equals the fp32 output rounded by torch, bit for bit."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=3, T=96, seed=64)
+    t = to_device(ti.generate(cfg))
+    g, b = (torch.from_numpy(x).cuda() for x in _ln_params(3, 64, 8))
+    z32, w32 = ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], g, b, t["eta"], 16)
+    z16, w16 = ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], g, b, t["eta"], 16, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert z16.dtype == torch.bfloat16
+    assert torch.equal(z16, z32.to(torch.bfloat16))
+    assert torch.equal(w16, w32)
+
+
+def test_ln_state_passing_and_in_place_carry(ttt):
+    """fwd(T) == fwd(T1) then fwd(T - T1) from its final state (bitwise: the
+    per-step arithmetic does not depend on the position), here with a
+    per-sequence W0 [B, H, d, d] carried in place (W_final aliasing W0)."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=2, T=128, eta_kind="token", seed=65)
+    inp = ti.generate(cfg)
+    t = to_device(inp)
+    g, b = (torch.from_numpy(x).cuda() for x in _ln_params(2, 64, 9))
+    w0 = t["w1"].unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+    z, wf = ttt.linear_ln_fwd(t["q"], t["k"], t["v"], w0, g, b, t["eta"], 16)
+    h = 48
+    state = w0.clone()
+    parts = []
+    for lo, hi in ((0, h), (h, cfg.T)):
+        sl = lambda x: x[:, :, lo:hi].contiguous()  # noqa: E731
+        zp, _ = ttt.linear_ln_fwd(sl(t["q"]), sl(t["k"]), sl(t["v"]), state, g, b, sl(t["eta"]), 16,
+                                  w_final=state)
+        parts.append(zp)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts, dim=2), z)
+    assert torch.equal(state, wf)
+
+
+def test_ln_eta_zero(ttt):
+    """eta = 0: the state does not move (bitwise) and Z = Q + LN(W0 Q)."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=1, H=2, T=64, seed=66)
+    inp = ti.generate(cfg)
+    t = to_device(inp)
+    gamma, beta = _ln_params(2, 64, 10)
+    z, wf = ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], torch.from_numpy(gamma).cuda(),
+                              torch.from_numpy(beta).cuda(), 0.0, 16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(rows(wf), inp.w_rows())
+    heads = np.arange(cfg.chains) % cfg.H
+    zr, _ = oracle.linear_ln_primal(inp.q, inp.k, inp.v, inp.w_rows(), gamma[heads], beta[heads],
+                                    np.zeros((cfg.chains, cfg.T)), 16, 1e-6)
+    assert max_rel(rows(z), zr) < 2e-3
+
+
+def test_ln_empty(ttt):
+    """B = 0 or T = 0: nothing to do, no launch; W_final = W0 when T = 0."""
+    dev = "cuda:0"
+    g = torch.ones((3, 64), device=dev)
+    b = torch.zeros((3, 64), device=dev)
+    w0 = torch.randn((3, 64, 64), device=dev)
+    e = torch.empty((0, 3, 32, 64), dtype=torch.bfloat16, device=dev)
+    z, wf = ttt.linear_ln_fwd(e, e, e, w0, g, b, 0.1, 16)
+    assert z.shape == (0, 3, 32, 64) and wf.shape == (0, 3, 64, 64)
+    e = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device=dev)
+    z, wf = ttt.linear_ln_fwd(e, e, e, w0, g, b, 0.1, 16)
+    torch.cuda.synchronize()
+    assert z.shape == (2, 3, 0, 64)
+    assert torch.equal(wf, w0.unsqueeze(0).expand(2, -1, -1, -1))
