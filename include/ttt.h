@@ -239,7 +239,8 @@ typedef struct {
  * TTT-MLP forward.  Q, K, V, Z as for TTT-Linear.
  *   W1_0 : [B or 1, H, dh, d] fp32     W2_0 : [B or 1, H, d, dh] fp32
  *   W1_final : [B,H,dh,d] fp32         W2_final : [B,H,d,dh] fp32
- * Supported: d = 64, dh = 256, b = 16, bf16 inputs.
+ * Supported: d = 64, dh = 256, b = 16, bf16 inputs, fp32 Z (anything else:
+ * TTT_ERR_UNSUPPORTED).
  */
 ttt_status ttt_mlp_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
                        const float* W1_0, const float* W2_0, const float* eta, void* Z,

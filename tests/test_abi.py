@@ -162,8 +162,8 @@ def test_linear_kernel_selection():
 
 # ---- TTT-MLP validation ----------------------------------------------------------
 
-def _mdesc(B=2, H=4, T=64, d=64, dh=256, b=16, wstride=0, est=(0, 0, 0)):
-    return ttt.mlp_desc(B, H, T, d, dh, b, 1, 0, wstride, est)
+def _mdesc(B=2, H=4, T=64, d=64, dh=256, b=16, wstride=0, est=(0, 0, 0), in_dtype=1, out_dtype=0):
+    return ttt.mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, wstride, est)
 
 
 def _mval(desc, **over):
@@ -180,6 +180,9 @@ def test_mlp_validation():
     assert _mval(_mdesc()) == OK
     assert _mval(_mdesc(T=40)) == SHAPE
     assert _mval(_mdesc(dh=128)) == UNSUP
+    assert _mval(_mdesc(out_dtype=1)) == UNSUP    # Z is fp32 only
+    assert _mval(_mdesc(in_dtype=0)) == UNSUP     # bf16 inputs only
+    assert _mval(_mdesc(out_dtype=7)) == 3        # no such dtype: TTT_ERR_DTYPE
     assert _mval(_mdesc(), f1=None) == NULL
     assert _mval(_mdesc(), z=1 * GB) == ALIAS
     assert _mval(_mdesc(), f1=4 * GB) == ALIAS
