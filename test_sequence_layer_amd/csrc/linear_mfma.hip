@@ -474,9 +474,13 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
 
     if constexpr (LN) {
       // z = q + LN(W_t q), transposed: token li, outputs 16w + 4g + r; the
-      // staging tile takes them as one 16-byte row piece
-      const float2 st = ln_stats(z, lns.part[2], w, li, g, a.eps);
+      // staging tile takes them as one 16-byte row piece.  Q is read before the
+      // statistics barrier: it is this step's last read of the slot, so past
+      // that barrier the next step may restage the slot, and the step needs no
+      // closing barrier (the staged tile of the next step was made visible by
+      // this step's first barrier, the Z tile by the next step's).
       const bf16x4 qr = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * wg + 4 * g]);
+      const float2 st = ln_stats(z, lns.part[2], w, li, g, a.eps);
       float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qr[r]) + ln_g[r] * ((z[r] - st.x) * st.y) + ln_b[r];
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       for (int r = 0; r < 4; ++r) zb[r * ZROW] = z[r];
     }
 
-    __syncthreads();
+    if constexpr (!LN) __syncthreads();
   };
 
   const int nfull = nb / PF * PF;
@@ -508,6 +512,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   }
 
   if constexpr (MODE == 0) {
+    if constexpr (LN) __syncthreads();  // (the layer-norm step ends without a barrier)
     if (nb > 0) flush_z(nb - 1);  // the last step's barrier made its tile visible
   }
 
