@@ -57,7 +57,7 @@ using namespace mfma;
 
 constexpr int D = 64;       // head dim
 constexpr int BT = 16;      // mini-batch (tokens)
-constexpr int ROW = 72;     // padded LDS row of a bf16 token tile (elements, 144 B)
+constexpr int ROW = 68;     // padded LDS row of a bf16 token tile (elements, 136 B: 8-byte aligned rows)
 constexpr int kThreads = 256;
 
 typedef uint16_t Tile[BT * ROW];
@@ -188,7 +188,12 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
   };
   auto stage = [&](int slot, const u32x4& xa, const u32x4& xe, const GLoad& xz, float xt) {
     BSlot& S = slots[slot];
-    *reinterpret_cast<u32x4*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]) = xa;
+    {
+      // two 8-byte stores: a 136-byte row keeps 8-byte, not 16-byte, alignment
+      u32x2* dst = reinterpret_cast<u32x2*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]);
+      dst[0] = u32x2{xa[0], xa[1]};
+      dst[1] = u32x2{xa[2], xa[3]};
+    }
     const float et = ETA_TOKEN ? xt : eta_c;
     float e[4], r[4], z[4];
 #pragma unroll
