@@ -71,48 +71,31 @@ struct __align__(16) Slot {
 };
 static_assert(sizeof(Slot) % 16 == 0, "slot size");
 
-// ---- layer norm across the row-split waves --------------------------------
-// The layer-norm path computes its projections transposed (W as the A operand),
-// so lane l holds token l%16 and outputs 16w + 4(l/16) + r, r = 0..3.  A sum
-// over a wave's 16 outputs of a token is then a lane-local sum of 4 and two
-// lane-group exchanges; the 4 wave partials meet in LDS.
+// ---- layer norm: tokens split over the waves ------------------------------
+// The row-split waves each hold 16 of a token's 64 outputs.  For the layer
+// norm they swap roles through LDS: each wave deposits its transposed tile
+// (lane l: token l%16, outputs 16w + 4(l/16) + r) as row pieces of a
+// [token][output] tile, and then normalises 4 whole tokens, 4w + l/16, 4 outputs
+// (4(l%16) + r) per lane, so a token's sums are 16-lane DPP reductions.
 struct LnShared {
-  float2 part[3][4][BT];  // [exchange][wave][token]: each wave's partials
+  float yk[BT * ZROW];    // W k of the mini-batch, fp32 [token][output]
+  float yq[BT * ZROW];    // the pre-norm outputs W_t q, fp32 [token][output]
+  uint16_t gh[BT * ROW];  // the update factor G, bf16 hi, [token][output]
+  uint16_t gl[BT * ROW];  //   and lo
 };
 
-// Mean and 1/sqrt(var + eps) of token l%16 over its 64 outputs (x[r]: output
-// 16w + 4g + r).  Each wave's (mean, M2) over its 16 outputs are combined
-// exactly across the waves (equal counts), which avoids the cancellation of
-// raw power sums.
-__device__ __forceinline__ float2 ln_stats(const float4v& x, float2 (*part)[BT], int w, int li, int g, float eps) {
-  const float mw = sum_rows((x[0] + x[1]) + (x[2] + x[3])) * (1.f / 16.f);
+// Mean and centred values of the 64 entries a 16-lane row holds 4 at a time,
+// and 1/sqrt(variance + eps): two passes, no cancellation of raw power sums.
+__device__ __forceinline__ float ln_centre(const float4 y, float dv[4], float eps) {
+  const float mu = sum16((y.x + y.y) + (y.z + y.w)) * (1.f / 64.f);
+  dv[0] = y.x - mu;
+  dv[1] = y.y - mu;
+  dv[2] = y.z - mu;
+  dv[3] = y.w - mu;
   float m2 = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float dv = x[r] - mw;
-    m2 = fmaf(dv, dv, m2);
-  }
-  m2 = sum_rows(m2);
-  if (g == 0) part[w][li] = make_float2(mw, m2);
-  __syncthreads();
-  float2 p[4];
-#pragma unroll
-  for (int ww = 0; ww < 4; ++ww) p[ww] = part[ww][li];
-  const float m = 0.25f * ((p[0].x + p[1].x) + (p[2].x + p[3].x));
-  float M2 = (p[0].y + p[1].y) + (p[2].y + p[3].y);
-#pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
-    const float dm = p[ww].x - m;
-    M2 = fmaf(16.f * dm, dm, M2);
-  }
-  return make_float2(m, rsqrtf(M2 * (1.f / 64.f) + eps));
-}
-
-// Four fp32 values that are bf16 numbers -> packed bf16 (exact)
-__device__ __forceinline__ bf16x4 pack_exact(float4v x) {
-  const bf16x2 a = __builtin_convertvector(float2v{x[0], x[1]}, bf16x2);
-  const bf16x2 b = __builtin_convertvector(float2v{x[2], x[3]}, bf16x2);
-  return bf16x4{a[0], a[1], b[0], b[1]};
+  for (int r = 0; r < 4; ++r) m2 = fmaf(dv[r], dv[r], m2);
+  return rsqrtf(sum16(m2) * (1.f / 64.f) + eps);
 }
 
 // MODE 0: forward (Z and the final state).  MODE 1: chunk maps P and R of a
@@ -135,7 +118,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   // Z of the last two mini-batches, fp32 [token][output] (rows padded to ZROW):
   // each wave deposits its 16 outputs of every token, and one step later every
   // thread writes 16 contiguous bytes of whole rows to HBM.
-  __shared__ __align__(16) float zbuf[MODE == 0 ? 2 : 1][MODE == 0 ? BT * ZROW : 4];
+  __shared__ __align__(16) float zbuf[MODE == 0 && !LN ? 2 : 1][MODE == 0 && !LN ? BT * ZROW : 4];
   // E of the last two mini-batches when it is saved for the backward (same scheme)
   __shared__ __align__(16) float ebuf[SAVE ? 2 : 1][SAVE ? BT * ZROW : 4];
 
@@ -229,19 +212,16 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   // constant eta (scalar or per head)
   float eta_c = 0.f;
   if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
-  // LN scale and shift of outputs 16w + 4g + r (the transposed tiles), and the
-  // identity B operand that moves a transposed tile back: lane l holds
-  // B[k = 8g + j][n = l%16] = 1 if n = 4g + j (j < 4), else 0
+  // LN scale and shift of outputs 4(l%16) + j (the token rows this lane normalises)
   float4v ln_g = {}, ln_b = {};
-  bf16x8 ident = {};
   if constexpr (LN) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // (gamma and beta are only 4-byte aligned)
-      ln_g[j] = a.gamma[h * D + 16 * wg + 4 * g + j];
-      ln_b[j] = a.beta[h * D + 16 * wg + 4 * g + j];
-      ident[j] = static_cast<__bf16>(li == 4 * g + j ? 1.f : 0.f);
+      ln_g[j] = a.gamma[h * D + 4 * li + j];
+      ln_b[j] = a.beta[h * D + 4 * li + j];
     }
   }
+  [[maybe_unused]] const int tk = 4 * w + g;  // the token whose layer norms this lane takes part in
 
   // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
   float4v wt[4];
@@ -328,6 +308,10 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     float et[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) et[r] = ETA_TOKEN ? S.eta[4 * g + r] : eta_c;
+    // (layer norm: the residual's Q row piece of token tk, read now, before the
+    // step's last barrier)
+    bf16x4 qr = {};
+    if constexpr (LN) qr = *reinterpret_cast<const bf16x4*>(&S.q[tk * ROW + 4 * li]);
 
     // ---- P_K = K W^T, P_Q = Q W^T, S = K Q^T ----
     float4v pk = {0.f, 0.f, 0.f, 0.f}, pq = pk, sc = pk;
@@ -381,45 +365,39 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     // update, also the operand of the Z correction ----
     bf16x4 bhi, blo;
     if constexpr (LN) {
-      // y = W k (pk, transposed: token li, outputs 16w + 4g + r), f(k) = k + LN(y);
-      // dl/dy through LN at the mini-batch-start state
-      const float2 st = ln_stats(pk, lns.part[0], w, li, g, a.eps);  // (mean, 1/std) of token li
-      const bf16x4 kr = *reinterpret_cast<const bf16x4*>(&S.k[li * ROW + 16 * wg + 4 * g]);
-      const bf16x4 vr = *reinterpret_cast<const bf16x4*>(&S.v[li * ROW + 16 * wg + 4 * g]);
+      // y = W k, f(k) = k + LN(y); dl/dy back through LN at the mini-batch-start
+      // state.  The wave's transposed tile goes to the [token][output] tile ...
+      *reinterpret_cast<float4*>(&lns.yk[li * ZROW + 16 * w + 4 * g]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
+      __syncthreads();
+      // ... and this lane takes token tk, outputs 4 li .. 4 li + 3
+      float dv[4];
+      const float rs = ln_centre(*reinterpret_cast<const float4*>(&lns.yk[tk * ZROW + 4 * li]), dv, a.eps);
+      const bf16x4 kr = *reinterpret_cast<const bf16x4*>(&S.k[tk * ROW + 4 * li]);
+      const bf16x4 vr = *reinterpret_cast<const bf16x4*>(&S.v[tk * ROW + 4 * li]);
       float yh[4], gr[4], s1 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        yh[r] = (pk[r] - st.x) * st.y;
+        yh[r] = dv[r] * rs;
         const float res = static_cast<float>(kr[r]) - static_cast<float>(vr[r]) + ln_b[r] + ln_g[r] * yh[r];
         gr[r] = 2.f * ln_g[r] * res;
         s1 += gr[r];
         s2 = fmaf(gr[r], yh[r], s2);
       }
-      s1 = sum_rows(s1);
-      s2 = sum_rows(s2);
-      if (g == 0) lns.part[1][w][li] = make_float2(s1, s2);
-      __syncthreads();
-      float c1 = 0.f, c2 = 0.f;  // the two means over the 64 outputs
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float2 p = lns.part[1][ww][li];
-        c1 += p.x;
-        c2 += p.y;
-      }
-      c1 *= 1.f / 64.f;
-      c2 *= 1.f / 64.f;
-      const float sg = -(ETA_TOKEN ? S.eta[li] : eta_c) * st.y;
+      s1 = sum16(s1) * (1.f / 64.f);  // the two means over the 64 outputs
+      s2 = sum16(s2) * (1.f / 64.f);
+      const float sg = -(ETA_TOKEN ? S.eta[tk] : eta_c) * rs;
       float d[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) d[r] = sg * (gr[r] - c1 - yh[r] * c2);
-      // G[s][i] = d of token s, output i: split, then moved to lane i, slot s by
-      // the identity product (bf16 x 1 summed with zeros: exact)
+      for (int r = 0; r < 4; ++r) d[r] = sg * (gr[r] - s1 - yh[r] * s2);
+      // G = -eta delta, split once, as [token][output] rows; read back in the
+      // operand layout (lane = output 16w + l%16, slots = tokens)
       bf16x4 dh, dl;
       split4(d, dh, dl);
-      const bf16x4 z4 = {};
-      const float4v f0 = {0.f, 0.f, 0.f, 0.f};
-      bhi = pack_exact(mfma32(cat(dh, z4), ident, f0));
-      blo = pack_exact(mfma32(cat(dl, z4), ident, f0));
+      *reinterpret_cast<bf16x4*>(&lns.gh[tk * ROW + 4 * li]) = dh;
+      *reinterpret_cast<bf16x4*>(&lns.gl[tk * ROW + 4 * li]) = dl;
+      __syncthreads();
+      bhi = read_cols<ROW>(lns.gh, 0, 16 * w, li, g);
+      blo = read_cols<ROW>(lns.gl, 0, 16 * w, li, g);
     } else {
       float gv[4];
       float e[4];
@@ -473,19 +451,28 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     }
 
     if constexpr (LN) {
-      // z = q + LN(W_t q), transposed: token li, outputs 16w + 4g + r; the
-      // staging tile takes them as one 16-byte row piece.  Q is read before the
-      // statistics barrier: it is this step's last read of the slot, so past
-      // that barrier the next step may restage the slot, and the step needs no
-      // closing barrier (the staged tile of the next step was made visible by
-      // this step's first barrier, the Z tile by the next step's).
-      const bf16x4 qr = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * wg + 4 * g]);
-      const float2 st = ln_stats(z, lns.part[2], w, li, g, a.eps);
+      // z = q + LN(W_t q): the transposed tile through LDS as above; this lane
+      // normalises token tk, outputs 4 li .. 4 li + 3, and writes them to HBM as
+      // a 16-byte piece of the token's row (16 lanes: the whole row).  This
+      // step reads nothing of the slot past the barrier below (qr was read at
+      // its start), so the next step may restage the slot at once and no
+      // closing barrier is needed.
+      *reinterpret_cast<float4*>(&lns.yq[li * ZROW + 16 * w + 4 * g]) = make_float4(z[0], z[1], z[2], z[3]);
+      __syncthreads();
+      float dv[4];
+      const float rs = ln_centre(*reinterpret_cast<const float4*>(&lns.yq[tk * ZROW + 4 * li]), dv, a.eps);
       float o[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qr[r]) + ln_g[r] * ((z[r] - st.x) * st.y) + ln_b[r];
-      if (n > 0) flush_z(n - 1);
-      *reinterpret_cast<float4*>(&zbuf[n & 1][li * ZROW + 16 * w + 4 * g]) = make_float4(o[0], o[1], o[2], o[3]);
+      for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qr[r]) + ln_g[r] * (dv[r] * rs) + ln_b[r];
+      OutT* zp = Zg + (static_cast<size_t>(n) * BT + tk) * D + 4 * li;
+      if constexpr (sizeof(OutT) == 4) {
+        st_stream(reinterpret_cast<u32x4*>(zp),
+                  u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])});
+      } else {
+        st_stream(reinterpret_cast<u32x2*>(zp),
+                  u32x2{static_cast<uint32_t>(f32_to_bf16_bits(o[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16),
+                        static_cast<uint32_t>(f32_to_bf16_bits(o[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[3])) << 16)});
+      }
     } else if constexpr (MODE == 0) {
       // ---- store Z rows t = 4g + r, columns 16w + li ----
       if (n > 0) flush_z(n - 1);
@@ -511,8 +498,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     if (nfull + j < nb) step(nfull + j, ra[j], rb[j], re[j], ra[jn], rb[jn], re[jn]);
   }
 
-  if constexpr (MODE == 0) {
-    if constexpr (LN) __syncthreads();  // (the layer-norm step ends without a barrier)
+  if constexpr (MODE == 0 && !LN) {
     if (nb > 0) flush_z(nb - 1);  // the last step's barrier made its tile visible
   }
 
