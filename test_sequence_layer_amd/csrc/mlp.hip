@@ -80,7 +80,6 @@ struct __align__(16) Smem {
   uint16_t enl[BT * EROW];      //   and lo
   float zr[BT * PROW];          // W2 A_Q summed over waves, [t][i]
   float s2[BT * SROW];          // A_K^T A_Q summed over waves, [s][t]
-  float2 lnp[4][BT];            // layer norm: (mean, M2) of each output wave's 16 outputs, per token
 };
 
 // a pair of 4-wide tiles split into 8-slot hi and lo operands
@@ -193,22 +192,15 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   float eta_c = 0.f;
   if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
 
-  // layer norm scale and shift: of outputs i, i + 1 for the phase-2 role (token
-  // tid / 32), of outputs 16w + 4g .. +3 for the output role of waves 0..3
-  float lg[2] = {0.f, 0.f}, lb[2] = {0.f, 0.f}, zg[4] = {0.f, 0.f, 0.f, 0.f}, zb[4] = {0.f, 0.f, 0.f, 0.f};
+  // layer norm scale and shift of outputs i, i + 1 of token tid / 32: the
+  // thread's role in both layer norms (the phase-2 sums and the output)
+  float lg[2] = {0.f, 0.f}, lb[2] = {0.f, 0.f};
   if constexpr (LN) {
     const float* gm = a.gamma + static_cast<int64_t>(h) * D;
     const float* bt = a.beta + static_cast<int64_t>(h) * D;
     const int i2 = (2 * tid) & (D - 1);
     lg[0] = gm[i2]; lg[1] = gm[i2 + 1];
     lb[0] = bt[i2]; lb[1] = bt[i2 + 1];
-    if (w < 4) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        zg[r] = gm[16 * w + 4 * g + r];
-        zb[r] = bt[16 * w + 4 * g + r];
-      }
-    }
   }
 
   // ---- resident state (this wave's hidden units J_w) ----
@@ -479,8 +471,6 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
 
     // ---- phase 5: Z[t][i] = (W2 A_Q)[i][t] + sum_s (-eta_s E[i][s]) S2[s][t] [s <= t], waves 0..3 ----
     // (with the layer norm: Z = Q + LN of that, over the 64 outputs of each token)
-    float4v z;
-    bf16x4 qz;
     if (w < 4) {
       const int it = w;
       bf16x4 s2h, s2l;
@@ -497,38 +487,31 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       const bf16x4 eh = read_cols<EROW>(sm.enh, 0, 16 * it, li, g);
       const bf16x4 el = read_cols<EROW>(sm.enl, 0, 16 * it, li, g);
       // C: (W2 A_Q)[i = 16it + 4g + r][t = li]
-      z = ld4(&sm.zr[li * PROW + 16 * it + 4 * g]);
+      float4v z = ld4(&sm.zr[li * PROW + 16 * it + 4 * g]);
       z = mfma3_16(eh, el, s2h, s2l, z);
       if constexpr (LN) {
-        // Q[t = li][i = 16it + 4g + r] for the residual, read before the barrier below,
-        // after which the other waves may restage this slot
-        qz = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * it + 4 * g]);
-        // mean and M2 of token li's 16 outputs in this wave (4 here, 4 lane groups)
-        const float m = sum_rows((z[0] + z[1]) + (z[2] + z[3])) * (1.f / 16.f);
-        float m2 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m2 += (z[r] - m) * (z[r] - m);
-        m2 = sum_rows(m2);
-        if (g == 0) sm.lnp[w][li] = make_float2(m, m2);
+        st4(&sm.zr[li * PROW + 16 * it + 4 * g], z);  // back in place: the pre-norm rows for the output LN
+      } else {
+        float* zp = Zg + (static_cast<size_t>(n) * BT + li) * D + 16 * w + 4 * g;
+        *reinterpret_cast<float4v*>(zp) = z;  // 64-byte pieces of a row per wave, merged in the L2
       }
     }
-    if constexpr (LN) __syncthreads();  // #5: every output wave's statistics
-    if (w < 4) {
-      if constexpr (LN) {
-        // combine the 4 waves' (mean, M2) over equal counts exactly
-        float2 p[4];
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) p[ww] = sm.lnp[ww][li];
-        const float mu = 0.25f * (p[0].x + p[1].x + p[2].x + p[3].x);
-        float m2 = p[0].y + p[1].y + p[2].y + p[3].y;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) m2 += 16.f * (p[ww].x - mu) * (p[ww].x - mu);
-        const float rs = rsqrtf(m2 * (1.f / D) + a.eps);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] = static_cast<float>(qz[r]) + zg[r] * (z[r] - mu) * rs + zb[r];
-      }
-      float* zp = Zg + (static_cast<size_t>(n) * BT + li) * D + 16 * w + 4 * g;
-      *reinterpret_cast<float4v*>(zp) = z;  // 64-byte pieces of a row per wave, merged in the L2
+    if constexpr (LN) {
+      // The output layer norm in the phase-2 role: every thread takes token
+      // tid / 32, outputs i, i + 1, so the 64 outputs of a token are in 32
+      // consecutive threads (half-wave sums) and the 32 threads write its whole
+      // Z row.  Q for the residual is read before the barrier, after which
+      // other waves may restage this slot.
+      const int t = tid >> 5, i = (2 * tid) & (D - 1);
+      const uint32_t qq = *reinterpret_cast<const uint32_t*>(&S.q[t * ROW + i]);
+      __syncthreads();  // #5: the pre-norm rows of all output waves
+      const float2 y = *reinterpret_cast<const float2*>(&sm.zr[t * PROW + i]);
+      const float mu = sum32(y.x + y.y) * (1.f / D);
+      const float d0 = y.x - mu, d1 = y.y - mu;
+      const float rs = rsqrtf(sum32(d0 * d0 + d1 * d1) * (1.f / D) + a.eps);
+      const float q0 = __uint_as_float(qq << 16), q1 = __uint_as_float(qq & 0xffff0000u);
+      float* zp = Zg + (static_cast<size_t>(n) * BT + t) * D + i;
+      *reinterpret_cast<float2*>(zp) = make_float2(q0 + lg[0] * (d0 * rs) + lb[0], q1 + lg[1] * (d1 * rs) + lb[1]);
     }
   };
 
