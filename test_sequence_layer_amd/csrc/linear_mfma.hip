@@ -222,6 +222,9 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     }
   }
   [[maybe_unused]] const int tk = 4 * w + g;  // the token whose layer norms this lane takes part in
+  // (layer norm: a step's output norm runs after the next step's first barrier,
+  // which also publishes its pre-norm tile; qp holds that step's Q residual)
+  [[maybe_unused]] bf16x4 qp = {};
 
   // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
   float4v wt[4];
@@ -290,6 +293,26 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       put(reinterpret_cast<u32x2*>(zp),
           u32x2{static_cast<uint32_t>(f32_to_bf16_bits(x.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.y)) << 16),
                 static_cast<uint32_t>(f32_to_bf16_bits(x.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.w)) << 16)});
+    }
+  };
+
+  // z = q + LN(W_t q) of mini-batch m from the pre-norm [token][output] tile:
+  // this lane normalises token tk, outputs 4 li .. 4 li + 3, and writes them to
+  // HBM as a 16-byte piece of the token's row (16 lanes: the whole row)
+  auto ln_out = [&](int m) {
+    float dv[4];
+    const float rs = ln_centre(*reinterpret_cast<const float4*>(&lns.yq[tk * ZROW + 4 * li]), dv, a.eps);
+    float o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qp[r]) + ln_g[r] * (dv[r] * rs) + ln_b[r];
+    OutT* zp = Zg + (static_cast<size_t>(m) * BT + tk) * D + 4 * li;
+    if constexpr (sizeof(OutT) == 4) {
+      st_stream(reinterpret_cast<u32x4*>(zp),
+                u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])});
+    } else {
+      st_stream(reinterpret_cast<u32x2*>(zp),
+                u32x2{static_cast<uint32_t>(f32_to_bf16_bits(o[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16),
+                      static_cast<uint32_t>(f32_to_bf16_bits(o[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[3])) << 16)});
     }
   };
 
@@ -364,11 +387,18 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     // ---- G[s][i] = -eta_s (dl/dy)[s][i]: the gradient factor of the rank-16
     // update, also the operand of the Z correction ----
     bf16x4 bhi, blo;
+    // (layer norm: the update's K column reads are made before the G barrier,
+    // the step's last, so that no read of the slot follows it)
+    [[maybe_unused]] bf16x4 kc[4] = {};
     if constexpr (LN) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kc[t] = read_cols<ROW>(S.k, 0, 16 * t, li, g);
       // y = W k, f(k) = k + LN(y); dl/dy back through LN at the mini-batch-start
       // state.  The wave's transposed tile goes to the [token][output] tile ...
       *reinterpret_cast<float4*>(&lns.yk[li * ZROW + 16 * w + 4 * g]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
       __syncthreads();
+      if (n > 0) ln_out(n - 1);  // the previous step's pre-norm tile is visible too
+      qp = qr;
       // ... and this lane takes token tk, outputs 4 li .. 4 li + 3
       float dv[4];
       const float rs = ln_centre(*reinterpret_cast<const float4*>(&lns.yk[tk * ZROW + 4 * li]), dv, a.eps);
@@ -446,33 +476,17 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     const bf16x8 gb = cat(bhi, blo);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x4 kt = read_cols<ROW>(S.k, 0, 16 * t, li, g);  // K[4g + r][16t + li]
+      const bf16x4 kt = LN ? kc[t] : read_cols<ROW>(S.k, 0, 16 * t, li, g);  // K[4g + r][16t + li]
       wt[t] = mfma32(cat(kt, kt), gb, wt[t]);
     }
 
     if constexpr (LN) {
-      // z = q + LN(W_t q): the transposed tile through LDS as above; this lane
-      // normalises token tk, outputs 4 li .. 4 li + 3, and writes them to HBM as
-      // a 16-byte piece of the token's row (16 lanes: the whole row).  This
-      // step reads nothing of the slot past the barrier below (qr was read at
-      // its start), so the next step may restage the slot at once and no
-      // closing barrier is needed.
+      // the pre-norm z of this step, transposed, as row pieces of the [token][output]
+      // tile: the next step's first barrier (or the one after the last step)
+      // publishes it and ln_out normalises it.  No read of the slot follows the
+      // G barrier (Q and K were read before it), so the next step may restage
+      // the slot at once and the step needs no closing barrier.
       *reinterpret_cast<float4*>(&lns.yq[li * ZROW + 16 * w + 4 * g]) = make_float4(z[0], z[1], z[2], z[3]);
-      __syncthreads();
-      float dv[4];
-      const float rs = ln_centre(*reinterpret_cast<const float4*>(&lns.yq[tk * ZROW + 4 * li]), dv, a.eps);
-      float o[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qr[r]) + ln_g[r] * (dv[r] * rs) + ln_b[r];
-      OutT* zp = Zg + (static_cast<size_t>(n) * BT + tk) * D + 4 * li;
-      if constexpr (sizeof(OutT) == 4) {
-        st_stream(reinterpret_cast<u32x4*>(zp),
-                  u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])});
-      } else {
-        st_stream(reinterpret_cast<u32x2*>(zp),
-                  u32x2{static_cast<uint32_t>(f32_to_bf16_bits(o[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16),
-                        static_cast<uint32_t>(f32_to_bf16_bits(o[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[3])) << 16)});
-      }
     } else if constexpr (MODE == 0) {
       // ---- store Z rows t = 4g + r, columns 16w + li ----
       if (n > 0) flush_z(n - 1);
@@ -500,6 +514,10 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
 
   if constexpr (MODE == 0 && !LN) {
     if (nb > 0) flush_z(nb - 1);  // the last step's barrier made its tile visible
+  }
+  if constexpr (LN) {
+    __syncthreads();  // the last step's pre-norm tile
+    if (nb > 0) ln_out(nb - 1);
   }
 
   float* wf;
