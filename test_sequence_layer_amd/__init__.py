@@ -187,10 +187,23 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream_handle(stream) -> Optional[int]:
+_raw_stream = None
+
+
+def _stream_handle(stream, dev: Optional[int] = None) -> Optional[int]:
+    """hipStream_t of ``stream``, else of torch's current stream on device ``dev``
+    (default: the current device).  torch's raw-stream query is used when it
+    exists: building a Stream object costs ~3 us per call, which matters for
+    one-token decode calls."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    global _raw_stream
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        return _raw_stream(torch.cuda.current_device() if dev is None else dev)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check_dev(*ts):
