@@ -162,6 +162,9 @@ def main():
                     help="split each sequence into this many chunks run in parallel (chunked forward)")
     ap.add_argument("--decode", action="store_true",
                     help="time decoding: one token per call for every sequence, state carried in place")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode: capture one mini-batch of one-token calls (b calls) in a HIP graph and "
+                         "time its replays (no per-call host overhead)")
     ap.add_argument("--save", action="store_true",
                     help="time the forward for training (also writes E for the backward)")
     ap.add_argument("--bwd", action="store_true", help="time the TTT-Linear backward (ttt_linear_bwd)")
@@ -176,6 +179,8 @@ def main():
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.graph and not args.decode:
+        ap.error("--graph applies to --decode")
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the (sequence, head) chains are independent, so N GPUs would each run this same kernel on "
@@ -225,6 +230,28 @@ def main():
             q1, k1, v1, e1 = tok[pos[0] % 64]
             ttt.linear_decode(q1, k1, v1, e1, w, wb, pos[0], cfg.b, z=zt)
             pos[0] += 1
+
+        if args.graph:
+            # b consecutive one-token calls, positions 0 .. b-1 (one mini-batch),
+            # captured once; each replay continues the sequences by b tokens
+            def calls():
+                for i in range(cfg.b):
+                    q1, k1, v1, e1 = tok[i]
+                    ttt.linear_decode(q1, k1, v1, e1, w, wb, i, cfg.b, z=zt)
+
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                calls()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                calls()
+            torch.cuda.synchronize()
+
+            def step():
+                graph.replay()
     else:
         wf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda:0")
         kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
@@ -290,7 +317,9 @@ def main():
     wall = time.perf_counter() - w0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps      # one call per step (the chunked form: 3 launches)
     ms_per_step = max(wall * 1e3 / args.steps, kernel_ms)
-    tokens = B * (1 if args.decode else T)
+    tokens = B * ((cfg.b if args.graph else 1) if args.decode else T)
+    if args.decode and args.graph:
+        kernel_ms /= cfg.b  # per launch: one replay is b decode launches
     value = tokens / (ms_per_step / 1e3)
 
     bytes_, flops = algorithmic(cfg, inp.eta_strides)
@@ -350,6 +379,8 @@ def main():
     if args.decode or args.primal:
         roof["note"] = ("decode: one token per call, latency-bound" if args.decode
                         else "primal (token-by-token) form: the baseline the dual form replaces")
+        if args.decode and args.graph:
+            roof["note"] += f"; timed as replays of a HIP graph of {cfg.b} one-token calls"
 
     if args.copy_calibration:
         n = COPY_BYTES // 4
@@ -371,7 +402,8 @@ def main():
 
     eta_desc = {(0, 0, 0): "scalar", (0, 1, 0): "per head"}.get(tuple(inp.eta_strides), "per token")
     model = "TTT-MLP" if cfg.is_mlp else "TTT-Linear"
-    form = "decode" if args.decode else ("primal" if args.primal else ("generic" if args.generic else ""))
+    form = ("decode (graph)" if args.graph else "decode") if args.decode else (
+        "primal" if args.primal else ("generic" if args.generic else ""))
     if args.ln:
         form = "layer-norm"
         roof["note"] = ("f(x) = x + LN(W2 GELU(W1 x))" if cfg.is_mlp else "f(x) = x + LN(W x)") + \

@@ -1,0 +1,124 @@
+"""The entry points allocate nothing and only launch kernels on the caller's
+stream, so they can be captured in a HIP graph.  Each test captures calls on a
+side stream, replays the graph several times with eager work and
+synchronisations in between, and checks every replay against the eager
+result, bit for bit."""
+import pytest
+
+import ttt_inputs as ti
+from ttt_testutil import to_device
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ttt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import test_sequence_layer_amd as m
+    m.lib()
+    return m
+
+
+def _capture(fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm-up outside the graph (first-call setup)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_forward_graph_replays(ttt):
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=4, T=256, eta_kind="token", seed=130)
+    t = to_device(ti.generate(cfg))
+    z_ref, w_ref = ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], 16)
+    zl_ref, wl_ref = ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], torch.ones((4, 64), device="cuda:0"),
+                                       torch.zeros((4, 64), device="cuda:0"), t["eta"], 16)
+    z, w = torch.empty_like(z_ref), torch.empty_like(w_ref)
+    zl, wl = torch.empty_like(zl_ref), torch.empty_like(wl_ref)
+    g1 = torch.ones((4, 64), device="cuda:0")
+    b1 = torch.zeros((4, 64), device="cuda:0")
+
+    def calls():
+        ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], 16, z=z, w_final=w)
+        ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], g1, b1, t["eta"], 16, z=zl, w_final=wl)
+
+    g = _capture(calls)
+    for i in range(3):
+        for x in (z, w, zl, wl):
+            x.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(z, z_ref) and torch.equal(w, w_ref), f"replay {i}"
+        assert torch.equal(zl, zl_ref) and torch.equal(wl, wl_ref), f"replay {i}"
+
+
+def test_mlp_and_chunked_graph_replays(ttt):
+    cfg = ti.CONFIGS["mlp"].with_(B=1, H=2, T=64, seed=131)
+    t = to_device(ti.generate(cfg))
+    ref = ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], 16)
+    out = [torch.empty_like(x) for x in ref]
+    cfg2 = ti.CONFIGS["l1p3b"].with_(B=1, H=3, T=256, seed=132)
+    t2 = to_device(ti.generate(cfg2))
+    zc_ref, wc_ref = ttt.linear_fwd_chunked(t2["q"], t2["k"], t2["v"], t2["w1"], t2["eta"], 16, 4)
+    ws = torch.empty(ttt.linear_chunked_workspace_bytes(1, 3, 256, 64, 16, 4), dtype=torch.uint8, device="cuda:0")
+    zc, wc = torch.empty_like(zc_ref), torch.empty_like(wc_ref)
+
+    def calls():
+        ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], 16, z=out[0], w1_final=out[1],
+                    w2_final=out[2])
+        ttt.linear_fwd_chunked(t2["q"], t2["k"], t2["v"], t2["w1"], t2["eta"], 16, 4, workspace=ws, z=zc,
+                               w_final=wc)
+
+    g = _capture(calls)
+    for i in range(3):
+        for x in out + [zc, wc, ws]:
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(out, ref)), f"replay {i}"
+        assert torch.equal(zc, zc_ref) and torch.equal(wc, wc_ref), f"replay {i}"
+
+
+def test_decode_graph_replays(ttt):
+    """A graph of one mini-batch of one-token decode calls (positions 0..15),
+    replayed twice, continues the state exactly as the same calls made eagerly
+    twice."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=2, T=16, eta_kind="token", seed=133)
+    t = to_device(ti.generate(cfg))
+    toks = [tuple(x[:, :, i:i + 1].contiguous() for x in (t["q"], t["k"], t["v"], t["eta"])) for i in range(16)]
+    w0 = t["w1"].unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+
+    def calls(w, wb, z):
+        for i in range(16):
+            ttt.linear_decode(*toks[i], w, wb, i, 16, z=z[i])
+
+    w_e, wb_e = w0.clone(), w0.clone()
+    z_e = [torch.empty((2, 2, 1, 64), device="cuda:0") for _ in range(16)]
+    zs = []
+    for _ in range(2):
+        calls(w_e, wb_e, z_e)
+        zs.append(torch.cat(z_e, dim=2))
+    torch.cuda.synchronize()
+
+    w_g, wb_g = w0.clone(), w0.clone()
+    z_g = [torch.empty((2, 2, 1, 64), device="cuda:0") for _ in range(16)]
+    g = _capture(lambda: calls(w_g, wb_g, z_g))
+    # the warm-up inside _capture ran the calls once already: start over
+    w_g.copy_(w0)
+    wb_g.copy_(w0)
+    torch.cuda.synchronize()
+    for r in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(z_g, dim=2), zs[r]), f"replay {r}"
+    assert torch.equal(w_g, w_e) and torch.equal(wb_g, wb_e)
