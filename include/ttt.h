@@ -33,7 +33,9 @@
  *  - The call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Argument errors are detected on the host BEFORE any launch and
  *    nothing is written.  Faults during execution surface at the caller's next
- *    synchronisation.
+ *    synchronisation.  A call only launches kernels on `stream` (no
+ *    allocation, copy, memset or synchronisation), so it can be captured in a
+ *    HIP graph and replayed.
  *  - Alignment: Q, K, V, Z, W0, W_final 16-byte aligned; eta 4-byte aligned.
  *  - Outputs (Z, W_final) must not overlap any input, except that W_final may
  *    be exactly W0 when W0 is per sequence (w0_batch_stride == H*d*d): the
@@ -140,8 +142,12 @@ int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t 
  * [H, d] per head.  The gradient of |f(k) - v|^2 stays rank one per token,
  * delta k^T with delta the loss gradient back-propagated through LN to W k, so
  * the dual form carries over: Y = W Q - Delta (diag(eta) triu(K^T Q)),
- * Z = Q + LN(Y), W <- W - Delta diag(eta) K^T.  Other arguments as for
- * ttt_linear_fwd.  Supported: d = 64, b = 16, bf16 inputs, flags = 0, eps >= 0.
+ * Z = Q + LN(Y), W <- W - Delta diag(eta) K^T.  Other arguments, layouts and
+ * errors as for ttt_linear_fwd (Z fp32 or bf16).  Supported: d = 64, b = 16,
+ * bf16 inputs, flags = 0 (else TTT_ERR_UNSUPPORTED); in addition eps must be
+ * finite and >= 0 (TTT_ERR_SHAPE), gamma and beta non-NULL (TTT_ERR_NULL),
+ * 4-byte aligned (TTT_ERR_ALIGN) and not overlapping Z or W_final
+ * (TTT_ERR_ALIAS).
  */
 ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                              const float* W0, const float* gamma, const float* beta, float eps, const float* eta,
@@ -253,8 +259,8 @@ ttt_status ttt_mlp_validate(const ttt_mlp_desc* desc, const void* Q, const void*
 const char* ttt_mlp_kernel_name(const ttt_mlp_desc* desc);
 
 /*
- * TTT-MLP with layer norm and residual inside f ([TTT] 03 §9: f always
- * contains LN and a residual connection): f(x) = x + LN(W2 GELU(W1 x)), LN over
+ * TTT-MLP with layer norm and residual inside f ([TTT] 03 §9, as for
+ * ttt_linear_ln_fwd): f(x) = x + LN(W2 GELU(W1 x)), LN over
  * the d outputs with per-head gamma, beta ([H, d] fp32) and eps as for
  * ttt_linear_ln_fwd.  The gradient of |f(k) - v|^2 with respect to the
  * pre-norm output is Delta = J_LN^T (2 (f(k) - v) * gamma), and the dual form
