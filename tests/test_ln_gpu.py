@@ -97,6 +97,24 @@ def test_ln_errors(ttt):
     with pytest.raises(ttt.TTTError) as ei:
         ttt.linear_ln_fwd(x, x, x, w0, g, g, 0.1, 16, eps=-1.0)
     assert ei.value.status == 2
+    with pytest.raises(ttt.TTTError) as ei:
+        ttt.linear_ln_fwd(x, x, x, w0, g, g, 0.1, 16, eps=float("nan"))
+    assert ei.value.status == 2
+    z = torch.empty((1, 1, 32, 64), device="cuda:0")
+    with pytest.raises(ttt.TTTError, match="TTT_ERR_ALIAS"):  # gamma inside Z
+        ttt.linear_ln_fwd(x, x, x, w0, z.view(-1)[:64].view(1, 64), g, 0.1, 16, z=z)
+    wf = torch.empty((1, 1, 64, 64), device="cuda:0")
+    with pytest.raises(ttt.TTTError, match="TTT_ERR_ALIAS"):  # beta inside W_final
+        ttt.linear_ln_fwd(x, x, x, w0, g, wf.view(-1)[64:128].view(1, 64), 0.1, 16, w_final=wf)
+    # flags (here a row-block count) are not taken: through the C ABI directly
+    import ctypes
+    desc = ttt.linear_desc(1, 1, 32, 64, 16, 1, 0, 0, (0, 0, 0), ttt.TTT_FLAG_ROWS[2])
+    eta = torch.full((1,), 0.1, device="cuda:0")
+    zz = torch.empty((1, 1, 32, 64), device="cuda:0")
+    st = ttt.lib().ttt_linear_ln_fwd(ctypes.byref(desc), x.data_ptr(), x.data_ptr(), x.data_ptr(), w0.data_ptr(),
+                                     g.data_ptr(), g.data_ptr(), ctypes.c_float(1e-6), eta.data_ptr(),
+                                     zz.data_ptr(), wf.data_ptr(), None)
+    assert st == 4
 
 
 def test_ln_bf16_output_is_rounded_fp32(ttt):
