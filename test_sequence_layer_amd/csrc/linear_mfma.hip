@@ -534,19 +534,30 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
 }
 
 #ifndef TTT_LINEAR_PF
-#define TTT_LINEAR_PF 8
+#define TTT_LINEAR_PF 6
 #endif
-// Prefetch distance (mini-batches in flight per thread).  A thread of a
-// smaller row block stages more of each tile (CA + 1 loads per step), so its
-// ring is shorter; those launches are latency-bound (few chains), not
-// bandwidth-bound.
-template <int RB>
-constexpr int pf_for() { return RB == 1 ? TTT_LINEAR_PF : 4; }
+#ifndef TTT_LINEAR_PF_LONG
+#define TTT_LINEAR_PF_LONG 8
+#endif
+// Prefetch distance (mini-batches in flight per thread).  Measured: the plain
+// forward at the 1.3B shape (512 workgroups, two per CU) runs ~1% faster with 6
+// than with 8 (5 and 7 are slower), but with one workgroup or less per CU (64
+// sequences x 32K tokens) 6 is 7% slower than 8, since no other workgroup hides
+// a wave's memory latency; the layer-norm forward is ~1% faster with 8; the map
+// pass keeps 8.  A thread of a smaller row block stages more of each tile
+// (CA + 1 loads per step), so its ring is shorter; those launches are
+// latency-bound (few chains), not bandwidth-bound.
+template <int RB, bool LONG = false>
+constexpr int pf_for() { return RB != 1 ? 4 : LONG ? TTT_LINEAR_PF_LONG : TTT_LINEAR_PF; }
+constexpr int64_t kShortRingUnits = 512;  // workgroups from which the plain forward takes the short ring
 
-template <bool TOK, bool LN, int RB>
+template <bool TOK, bool LN, int RB, bool LONG = LN>
 hipError_t launch_rb(const LinearArgs& a, hipStream_t s) {
-  constexpr int PF = pf_for<RB>();
+  constexpr int PF = pf_for<RB, LONG>();
   dim3 grid(a.B * a.H * a.nchunk * RB), block(256 / RB);
+  if constexpr (!LN && RB == 1 && !LONG) {
+    if (static_cast<int64_t>(a.B) * a.H * a.nchunk < kShortRingUnits) return launch_rb<TOK, false, 1, true>(a, s);
+  }
   if constexpr (!LN) {
     if (a.Esave) {
       if (a.out_dtype == 0)
@@ -579,7 +590,7 @@ hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
 template <bool TOK, int RB>
 hipError_t launch_maps_rb(const LinearArgs& a, hipStream_t s) {
   dim3 grid(2 * a.B * a.H * (a.nchunk - 1) * RB), block(256 / RB);  // P and R maps in one launch
-  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<pf_for<RB>(), TOK, float, 1, false, false, RB>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<pf_for<RB, true>(), TOK, float, 1, false, false, RB>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
