@@ -451,8 +451,11 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
     *reinterpret_cast<float4*>(dw + 16 * t) = make_float4(a1[t][0], a1[t][1], a1[t][2], a1[t][3]);
 }
 
+// Prefetch ring depth (mini-batches in flight per thread; at least 2): 2
+// measured 1.3% faster than 3 at the 1.3B shape and 4.4% at 64 sequences x 32K
+// tokens (228 against 244 VGPRs), bit-identical results.
 #ifndef TTT_BWD_PF
-#define TTT_BWD_PF 3
+#define TTT_BWD_PF 2
 #endif
 constexpr int kPF = TTT_BWD_PF;
 
