@@ -6,9 +6,11 @@
 // of mini-batches maps it as W -> W P + R.  With the maps P_c, R_c of every
 // chunk but the last (computed in parallel by the MFMA kernel in its map
 // mode), the start state of chunk c+1 is Wstart[c] P_c + R_c; this kernel runs
-// that short sequential scan per chain (fp32 FMA, the maps staged in LDS and
-// fetched one chunk ahead), after which every chunk's outputs are computed in
-// parallel from its start state.
+// that short sequential scan per chain, after which every chunk's outputs are
+// computed in parallel from its start state.  Each 64 x 64 x 64 product runs on
+// the fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32 products and sums, no
+// bf16 splitting): wave w computes rows 16w .. 16w + 15 of W P + R, the four
+// 16 x 16 column tiles accumulating over k in steps of 4.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -16,11 +18,15 @@ namespace {
 
 constexpr int D = 64;
 constexpr int kThreads = 256;
+typedef float float4v __attribute__((__vector_size__(4 * sizeof(float))));
 
 __global__ __launch_bounds__(kThreads) void ttt_linear_chunk_scan(LinearArgs a) {
-  __shared__ float W[D][D + 1];
-  __shared__ float P[D][D + 1];
+  // row strides chosen so that the operand reads (16 rows x 4 columns of W,
+  // 4 rows x 16 columns of P per instruction) hit 64 distinct banks
+  __shared__ float W[D][D + 4];
+  __shared__ float P[D][D + 16];
   const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int chain = blockIdx.x;
   const int bi = chain / a.H, h = chain - bi * a.H;
   const float* w0 = a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D;
@@ -30,52 +36,51 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_chunk_scan(LinearArgs a) 
     W[x / D][x % D] = v;
     ws[x] = v;
   }
-  // Thread tid owns outputs W'[i][j0 .. j0 + 15] and stages the same 16 entries
-  // of P; the next chunk's P and R entries are loaded one step ahead so their
-  // latency overlaps the current product.
-  const int i = tid >> 2, j0 = (tid & 3) * 16;
+  // This thread stages row pr, columns pc .. pc + 15 of the next P, and holds
+  // R in the accumulator layout: acc[b][r] = R[16w + 4g + r][16b + li].  Both
+  // are loaded one chunk ahead so their latency overlaps the current product.
+  const int pr = tid >> 2, pc = (tid & 3) * 16;
   const float* maps = a.maps + static_cast<int64_t>(chain) * (a.nchunk - 1) * 2 * D * D;
-  float4 pn[4], rn[4];
+  float4 pn[4];
+  float4v rn[4];
   auto load_maps = [&](int c) {
-    const float* Pg = maps + static_cast<int64_t>(c) * 2 * D * D + i * D + j0;
+    const float* Pg = maps + static_cast<int64_t>(c) * 2 * D * D;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      pn[q] = *reinterpret_cast<const float4*>(Pg + 4 * q);
-      rn[q] = *reinterpret_cast<const float4*>(Pg + D * D + 4 * q);
-    }
+    for (int q = 0; q < 4; ++q) pn[q] = *reinterpret_cast<const float4*>(Pg + pr * D + pc + 4 * q);
+    const float* Rg = Pg + D * D + (16 * w + 4 * g) * D + li;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rn[b][r] = Rg[r * D + 16 * b];
   };
   if (a.nchunk > 1) load_maps(0);
   for (int c = 0; c + 1 < a.nchunk; ++c) {
     __syncthreads();  // W complete, previous P consumed
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      P[i][j0 + 4 * q + 0] = pn[q].x;
-      P[i][j0 + 4 * q + 1] = pn[q].y;
-      P[i][j0 + 4 * q + 2] = pn[q].z;
-      P[i][j0 + 4 * q + 3] = pn[q].w;
-    }
-    float acc[16];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(&P[pr][pc + 4 * q]) = pn[q];
+    float4v acc[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[4 * q + 0] = rn[q].x;
-      acc[4 * q + 1] = rn[q].y;
-      acc[4 * q + 2] = rn[q].z;
-      acc[4 * q + 3] = rn[q].w;
-    }
+    for (int b = 0; b < 4; ++b) acc[b] = rn[b];
     if (c + 2 < a.nchunk) load_maps(c + 1);
     __syncthreads();
-    for (int k = 0; k < D; ++k) {
-      const float wik = W[i][k];
+    // acc[b] += W[16w + m][k] P[k][16b + n]: A operand W[16w + li][k0 + g],
+    // B operand P[k0 + g][16b + li], k0 = 0, 4, ..., 60
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const float av = W[16 * w + li][k0 + g];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) acc[jj] = fmaf(wik, P[k][j0 + jj], acc[jj]);
+      for (int b = 0; b < 4; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, P[k0 + g][16 * b + li], acc[b], 0, 0, 0);
     }
     __syncthreads();  // every read of W done
-    float* out = ws + static_cast<int64_t>(c + 1) * D * D + i * D + j0;
+    float* out = ws + static_cast<int64_t>(c + 1) * D * D;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) W[i][j0 + jj] = acc[jj];
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(out + 4 * q) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      for (int r = 0; r < 4; ++r) {
+        W[16 * w + 4 * g + r][16 * b + li] = acc[b][r];
+        out[(16 * w + 4 * g + r) * D + 16 * b + li] = acc[b][r];
+      }
   }
 }
 
