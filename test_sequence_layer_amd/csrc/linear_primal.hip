@@ -39,6 +39,16 @@ __device__ __forceinline__ void st_out<float>(float* p, size_t i, float x) { p[i
 template <>
 __device__ __forceinline__ void st_out<uint16_t>(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16_bits(x); }
 
+// Sum over the 4 lanes of a quad (the 4 threads of one state row): two DPP
+// quad_perm moves ([1,0,3,2], then [2,3,0,1]) fused into the adds, instead of
+// shuffles through the LDS crossbar, which sit on the per-token serial chain.
+// Every lane of the quad gets the same (commutative) sums as with the shuffles.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, true));
+  return x;
+}
+
 template <int D, typename InT, typename OutT>
 __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) {
   constexpr int NT = 4 * D;
@@ -103,9 +113,7 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
       float e = 0.f;
 #pragma unroll
       for (int c = 0; c < CQ; ++c) e = fmaf(Wb[c], ks[t][qd * CQ + c], e);
-      e += __shfl_xor(e, 1, 4);
-      e += __shfl_xor(e, 2, 4);
-      e -= vs[t][i];
+      e = quad_sum(e) - vs[t][i];
       const float ge = -2.f * es[t] * e;
       float z = 0.f;
 #pragma unroll
@@ -113,8 +121,7 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
         W[c] = fmaf(ge, ks[t][qd * CQ + c], W[c]);
         z = fmaf(W[c], qs[t][qd * CQ + c], z);
       }
-      z += __shfl_xor(z, 1, 4);
-      z += __shfl_xor(z, 2, 4);
+      z = quad_sum(z);
       if (qd == 0) zs[t][i] = z;
     }
     __syncthreads();
