@@ -13,7 +13,9 @@
 // One workgroup of 4D threads per (sequence, head): thread (i = tid / 4,
 // quarter = tid % 4) owns W[i][quarter*D/4 .. +D/4) and the same slice of Wb in
 // registers; the two dot products per token are finished with a 4-lane
-// shuffle reduction.  Tokens are staged 16 at a time through LDS as fp32.
+// DPP reduction.  Tokens are staged TB at a time through LDS as fp32; while one
+// block is processed, the next full block is already loading into registers
+// (pieces of 4 consecutive elements of K, Q and V per thread).
 //
 // The same kernel serves two entry points: the full forward (state from W0,
 // written to W_final) and decode (state W and Wb read and written in place,
@@ -23,7 +25,12 @@
 namespace ttt {
 namespace {
 
-constexpr int TB = 16;  // tokens staged per block
+#ifndef TTT_PRIMAL_TB
+#define TTT_PRIMAL_TB 32
+#endif
+constexpr int TB = TTT_PRIMAL_TB;  // tokens staged per block
+constexpr int TU = 16;             // tokens per unrolled run piece
+static_assert(TB % TU == 0 && TU % 4 == 0, "block holds whole unrolled pieces");
 
 template <typename T>
 __device__ __forceinline__ float ld_in(const T* p, size_t i);
@@ -31,6 +38,21 @@ template <>
 __device__ __forceinline__ float ld_in<float>(const float* p, size_t i) { return p[i]; }
 template <>
 __device__ __forceinline__ float ld_in<uint16_t>(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
+
+// Four consecutive inputs starting at element i (i a multiple of 4; the
+// sequences are 16-byte aligned, so these are 16- or 8-byte loads).
+template <typename T>
+__device__ __forceinline__ float4 ld_in4(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float4 ld_in4<float>(const float* p, size_t i) {
+  return *reinterpret_cast<const float4*>(p + i);
+}
+template <>
+__device__ __forceinline__ float4 ld_in4<uint16_t>(const uint16_t* p, size_t i) {
+  const uint2 x = *reinterpret_cast<const uint2*>(p + i);
+  return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                     __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+}
 
 template <typename T>
 __device__ __forceinline__ void st_out(T* p, size_t i, float x);
@@ -64,6 +86,10 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
   // The state slice of this thread is 16-byte aligned (CQ is a multiple of 4):
   // moved with 16-byte accesses.  Wb is read only if the first token does not
   // start a mini-batch itself (then Wb <- W before any use).
+  // Position of the next token within its mini-batch, carried as a counter
+  // (a 64-bit modulo per token would cost more than the token's arithmetic).
+  int ph = static_cast<int>(a.pos % a.b);
+
   float W[CQ], Wb[CQ];
   {
     const int64_t off = bi * a.w_in_bstride + static_cast<int64_t>(h) * D * D + i * D + qd * CQ;
@@ -73,7 +99,7 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
       const float4 x = w[c];
       W[4 * c] = x.x, W[4 * c + 1] = x.y, W[4 * c + 2] = x.z, W[4 * c + 3] = x.w;
     }
-    if (a.pos % a.b != 0) {
+    if (ph != 0) {
       const float4* wb = reinterpret_cast<const float4*>(a.Wb_in + off);
 #pragma unroll
       for (int c = 0; c < CQ / 4; ++c) {
@@ -86,6 +112,9 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
     }
   }
   bool wb_moved = false;  // Wb was re-snapshotted during this call
+  // Full blocks go in unrolled TU-token pieces when mini-batch starts fall only
+  // on piece boundaries (then ph stays a multiple of TU at every full block).
+  const bool pieces = a.b % TU == 0 && ph % TU == 0;
   const size_t base = static_cast<size_t>(chain) * a.T * D;
   const InT* Qg = static_cast<const InT*>(a.Q) + base;
   const InT* Kg = static_cast<const InT*>(a.K) + base;
@@ -93,39 +122,126 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
   OutT* Zg = static_cast<OutT*>(a.Z) + base;
   const float* eg = a.eta + bi * a.esb + h * a.esh;
 
-  for (int t0 = 0; t0 < a.T; t0 += TB) {
-    const int nt = min(TB, a.T - t0);
-    __syncthreads();  // previous block's tiles and outputs consumed
+  // A full block is TB*D elements per input, NT = 4D threads: thread tid holds
+  // the 4-element pieces p*NT + tid (p < NP) of it, i.e. element 4 (p NT + tid)
+  // at row 4 (p NT + tid) / D.
+  constexpr int NP = TB * D / (4 * NT);
+  static_assert(NP * 4 * NT == TB * D, "whole 4-element pieces per thread and input");
+  float4 kr[NP], qr[NP], vr[NP];
+  float er = 0.f;
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const size_t g = static_cast<size_t>(t0) * D + 4 * (p * NT + tid);
+      kr[p] = ld_in4<InT>(Kg, g);
+      qr[p] = ld_in4<InT>(Qg, g);
+      vr[p] = ld_in4<InT>(Vg, g);
+    }
+    if (tid < TB) er = eg[static_cast<int64_t>(t0 + tid) * a.est];
+  };
+
+  auto step = [&](int t) {
+    float e = 0.f;
+#pragma unroll
+    for (int c = 0; c < CQ; ++c) e = fmaf(Wb[c], ks[t][qd * CQ + c], e);
+    e = quad_sum(e) - vs[t][i];
+    const float ge = es[t] * e;  // es holds -2 eta (exact scaling)
+    float z = 0.f;
+#pragma unroll
+    for (int c = 0; c < CQ; ++c) {
+      W[c] = fmaf(ge, ks[t][qd * CQ + c], W[c]);
+      z = fmaf(W[c], qs[t][qd * CQ + c], z);
+    }
+    return quad_sum(z);
+  };
+
+  // Tokens [t0, t0 + nt) of a block that is not full: loaded element by element.
+  auto stage_part = [&](int t0, int nt) {
     for (int x = tid; x < nt * D; x += NT) {
       const size_t gidx = static_cast<size_t>(t0) * D + x;
       ks[x / D][x % D] = ld_in<InT>(Kg, gidx);
       qs[x / D][x % D] = ld_in<InT>(Qg, gidx);
       vs[x / D][x % D] = ld_in<InT>(Vg, gidx);
     }
-    if (tid < nt) es[tid] = eg[static_cast<int64_t>(t0 + tid) * a.est];
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-      if ((a.pos + t0 + t) % a.b == 0) {
+    if (tid < nt) es[tid] = -2.f * eg[static_cast<int64_t>(t0 + tid) * a.est];
+  };
+  // Token by token, with the mini-batch-start test at every token.
+  auto tokens_each = [&](int nt) {
+    for (int u = 0; u < nt; ++u) {
+      if (ph == 0) {
 #pragma unroll
-        for (int c = 0; c < CQ; ++c) Wb[c] = W[c];
+        for (int j = 0; j < CQ; ++j) Wb[j] = W[j];
         wb_moved = true;
       }
-      float e = 0.f;
-#pragma unroll
-      for (int c = 0; c < CQ; ++c) e = fmaf(Wb[c], ks[t][qd * CQ + c], e);
-      e = quad_sum(e) - vs[t][i];
-      const float ge = -2.f * es[t] * e;
-      float z = 0.f;
-#pragma unroll
-      for (int c = 0; c < CQ; ++c) {
-        W[c] = fmaf(ge, ks[t][qd * CQ + c], W[c]);
-        z = fmaf(W[c], qs[t][qd * CQ + c], z);
-      }
-      z = quad_sum(z);
-      if (qd == 0) zs[t][i] = z;
+      const float z = step(u);
+      if (qd == 0) zs[u][i] = z;
+      if (++ph == a.b) ph = 0;
     }
-    __syncthreads();
+  };
+  auto store_z = [&](int t0, int nt) {
     for (int x = tid; x < nt * D; x += NT) st_out<OutT>(Zg, static_cast<size_t>(t0) * D + x, zs[x / D][x % D]);
+  };
+
+  if (a.T < TB) {
+    // One short block (decode): no prefetch, and the state loads stay in flight
+    // while the tokens load.
+    stage_part(0, a.T);
+    __syncthreads();
+    tokens_each(a.T);
+    __syncthreads();
+    store_z(0, a.T);
+  } else {
+    // Retire the state loads first (s_waitcnt vmcnt(0)): otherwise the
+    // compiler's wait counting cannot tell them from the prefetch loads and
+    // waits for the whole prefetch at the first token of every block.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    fetch(0);
+    for (int t0 = 0; t0 < a.T; t0 += TB) {
+      const int nt = min(TB, a.T - t0);
+      __syncthreads();  // previous block's tiles and outputs consumed
+      if (nt == TB) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int x = 4 * (p * NT + tid);
+          *reinterpret_cast<float4*>(&ks[x / D][x % D]) = kr[p];
+          *reinterpret_cast<float4*>(&qs[x / D][x % D]) = qr[p];
+          *reinterpret_cast<float4*>(&vs[x / D][x % D]) = vr[p];
+        }
+        if (tid < TB) es[tid] = -2.f * er;
+        if (t0 + 2 * TB <= a.T) fetch(t0 + TB);  // the next block is full too
+      } else {
+        stage_part(t0, nt);
+      }
+      __syncthreads();
+      if (nt == TB && pieces) {
+        // TU-token pieces never straddle a mini-batch start: the snapshot test
+        // is made once per piece, and the unrolled tokens of a piece form one
+        // basic block.  The z of token u is kept by lane qd = u % 4 of its row
+        // (a select, not a masked store).
+#pragma unroll
+        for (int c = 0; c < TB / TU; ++c) {
+          if (ph == 0) {
+#pragma unroll
+            for (int j = 0; j < CQ; ++j) Wb[j] = W[j];
+            wb_moved = true;
+          }
+          float zr[TU / 4];
+#pragma unroll
+          for (int u = 0; u < TU; ++u) {
+            const float z = step(c * TU + u);
+            if (qd == (u & 3)) zr[u >> 2] = z;
+          }
+#pragma unroll
+          for (int j = 0; j < TU / 4; ++j) zs[c * TU + 4 * j + qd][i] = zr[j];
+          ph += TU;
+          if (ph == a.b) ph = 0;
+        }
+      } else {
+        tokens_each(nt);
+      }
+      __syncthreads();
+      store_z(t0, nt);
+    }
   }
 
   float4* w = reinterpret_cast<float4*>(a.W_out + static_cast<int64_t>(chain) * D * D + i * D + qd * CQ);

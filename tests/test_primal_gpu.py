@@ -34,6 +34,8 @@ def _oracle(inp):
     (64, 5, 45, "fp32", "token"),
     (32, 8, 96, "bf16", "scalar"),
     (64, 64, 128, "bf16", "token"),     # b larger than any dual-form kernel takes
+    (16, 16, 80, "fp32", "token"),      # unrolled 16-token pieces at d = 16 and 32
+    (32, 32, 128, "bf16", "head"),
 ])
 def test_primal_vs_oracle(ttt, d, b, T, dtype, eta_kind):
     cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=3, d=d, b=b, T=T, dtype=dtype, eta_kind=eta_kind,
@@ -80,7 +82,7 @@ def _decode_in_chunks(ttt, t, cuts, b, w0_bh):
     return torch.cat(zs, dim=2), w
 
 
-@pytest.mark.parametrize("cuts", [[1] * 48, [5, 11, 16, 3, 13], [48]])
+@pytest.mark.parametrize("cuts", [[1] * 48, [5, 11, 16, 3, 13], [48], [5, 40, 3], [16, 32]])
 def test_decode_matches_forward(ttt, cuts):
     cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=2, T=48, seed=17)
     inp = ti.generate(cfg)
