@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -101,29 +102,65 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+_HOST_THREADS: list = []
+
+
+def _host_threads(oracle) -> int:
+    """OpenMP threads available to the oracle, read once: a call with threads=1
+    lowers what the OpenMP runtime reports from then on."""
+    if not _HOST_THREADS:
+        _HOST_THREADS.append(oracle.max_threads())
+    return _HOST_THREADS[0]
+
+
+def _oracle_subset(cfg: ti.Config, inp_full, chains):
+    return ti.Inputs(cfg, chains, inp_full.q[chains], inp_full.k[chains], inp_full.v[chains],
+                     inp_full.w1, inp_full.w2, inp_full.eta_buf, inp_full.eta_strides)
+
+
 def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = False):
+    """The fp64 oracle timed on all host threads over a sample of chains, and on one
+    thread over a 1/threads share of that sample (about the same wall time)."""
     import oracle
 
-    chains = ti.sample_chains(cfg, sample_chains)
-    sub = ti.Inputs(cfg, chains, inp_full.q[chains], inp_full.k[chains], inp_full.v[chains],
-                    inp_full.w1, inp_full.w2, inp_full.eta_buf, inp_full.eta_strides)
-    threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    if ln:  # the layer-norm forms, with the benchmark's gamma = 1, beta = 0
-        one, zero = np.ones((len(chains), cfg.d)), np.zeros((len(chains), cfg.d))
-        if cfg.is_mlp:
-            oracle.mlp_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(1), sub.w_rows(2), one, zero, sub.eta_rows(),
-                                 cfg.b, threads=threads)
+    def run(sub, threads):
+        t0 = time.perf_counter()
+        if ln:  # the layer-norm forms, with the benchmark's gamma = 1, beta = 0
+            n = len(sub.chains)
+            one, zero = np.ones((n, cfg.d)), np.zeros((n, cfg.d))
+            if cfg.is_mlp:
+                oracle.mlp_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(1), sub.w_rows(2), one, zero, sub.eta_rows(),
+                                     cfg.b, threads=threads)
+            else:
+                oracle.linear_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(1), one, zero, sub.eta_rows(), cfg.b,
+                                        threads=threads)
         else:
-            oracle.linear_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(1), one, zero, sub.eta_rows(), cfg.b,
-                                    threads=threads)
-    else:
-        oracle.run_inputs(sub, threads=threads)
-    dt = time.perf_counter() - t0
-    tokens = len(chains) * cfg.T / cfg.H           # token = all H heads of one position
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            oracle.run_inputs(sub, threads=threads)
+        return time.perf_counter() - t0
+
+    chains = ti.sample_chains(cfg, sample_chains)
+    threads = _host_threads(oracle)
+    dt = run(_oracle_subset(cfg, inp_full, chains), threads)
+    chains1 = chains[:max(1, len(chains) // threads)]
+    dt1 = run(_oracle_subset(cfg, inp_full, chains1), 1)
+    tok = lambda n: n * cfg.T / cfg.H              # noqa: E731  (token = all H heads of one position)
+    return {"value": tok(len(chains)) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(chains)} of {cfg.chains} (sequence, head) chains at full T={cfg.T}, "
-                      f"fp64 primal form, {dt:.2f} s wall on {threads} threads"}
+                      f"fp64 primal form, {dt:.2f} s wall on {threads} threads",
+            "cpu_model": _cpu_model(),
+            "one_thread": {"value": tok(len(chains1)) / dt1, "unit": "tokens/s",
+                           "sample": f"{len(chains1)} chains at full T={cfg.T}, {dt1:.2f} s wall on 1 thread"}}
 
 
 def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int):
@@ -133,7 +170,7 @@ def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int):
     sub = ti.Inputs(cfg, chains, inp_full.q[chains], inp_full.k[chains], inp_full.v[chains],
                     inp_full.w1, inp_full.w2, inp_full.eta_buf, inp_full.eta_strides)
     dz, dwf = ti.upstream_grads(cfg, chains=chains)
-    threads = oracle.max_threads()
+    threads = _host_threads(oracle)
     t0 = time.perf_counter()
     oracle.linear_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(), sub.eta_rows(), cfg.b, dz, dwf, threads=threads)
     dt = time.perf_counter() - t0
