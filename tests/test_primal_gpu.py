@@ -34,7 +34,8 @@ def _oracle(inp):
     (64, 5, 45, "fp32", "token"),
     (32, 8, 96, "bf16", "scalar"),
     (64, 64, 128, "bf16", "token"),     # b larger than any dual-form kernel takes
-    (16, 16, 80, "fp32", "token"),      # unrolled 16-token pieces at d = 16 and 32
+    (16, 16, 80, "fp32", "token"),      # unrolled 16-token pieces at d = 16, 32, 64
+    (64, 16, 112, "fp32", "head"),      # fp32 inputs, three 32-token blocks and a 16-token tail
     (32, 32, 128, "bf16", "head"),
 ])
 def test_primal_vs_oracle(ttt, d, b, T, dtype, eta_kind):
