@@ -83,13 +83,13 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
   const int chain = blockIdx.x;
   const int bi = chain / a.H, h = chain - bi * a.H;
 
-  // The state slice of this thread is 16-byte aligned (CQ is a multiple of 4):
-  // moved with 16-byte accesses.  Wb is read only if the first token does not
-  // start a mini-batch itself (then Wb <- W before any use).
   // Position of the next token within its mini-batch, carried as a counter
   // (a 64-bit modulo per token would cost more than the token's arithmetic).
   int ph = static_cast<int>(a.pos % a.b);
 
+  // The state slice of this thread is 16-byte aligned (CQ is a multiple of 4):
+  // moved with 16-byte accesses.  Wb is read only if the first token does not
+  // start a mini-batch itself (then Wb <- W before any use).
   float W[CQ], Wb[CQ];
   {
     const int64_t off = bi * a.w_in_bstride + static_cast<int64_t>(h) * D * D + i * D + qd * CQ;
