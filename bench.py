@@ -29,7 +29,6 @@ import ttt_inputs as ti  # noqa: E402
 METRIC = "TTT-Linear fwd tokens/sec at B16 H32 d64 T8192 b16; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3       # fp32 matrix
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30           # size of the calibration copy (read and written once each)
 
@@ -103,14 +102,26 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it, with the family/model/stepping
+    numbers and the logical CPU count (some hosts give only a short brand
+    string as the model name)."""
+    fields = {}
+    ncpu = 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    continue
+                key, val = (x.strip() for x in line.split(":", 1))
+                if key == "processor":
+                    ncpu += 1
+                fields.setdefault(key, val)
     except OSError:
-        pass
-    return platform.processor() or "unknown"
+        return platform.processor() or "unknown"
+    name = fields.get("model name", platform.processor() or "unknown")
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model", "stepping") if k in fields)
+    extra = f"; {fields['cpu MHz']} MHz" if "cpu MHz" in fields else ""
+    return f"{name} ({ids}; {ncpu} logical CPUs visible{extra})"
 
 
 _HOST_THREADS: list = []
@@ -180,11 +191,74 @@ def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int):
                       f"fp64 reverse pass of the primal loop, {dt:.2f} s wall on {threads} threads"}
 
 
+def settle(step, stream, min_s: float = 1.0, max_s: float = 6.0, batch_ms: float = 25.0,
+           tol: float = 0.01, patience: int = 3):
+    """Launch ``step`` back to back until the per-launch time stops falling.
+
+    The GPU's clock settles only after some tens of milliseconds of
+    back-to-back work (the first launches of a fresh process run up to 40%
+    slower), so a fixed handful of warm-up launches can leave a short timed
+    region inside the ramp.  Batches of about ``batch_ms`` of GPU work are
+    timed with events on ``stream``; the warm-up ends once at least ``min_s``
+    seconds have passed and ``patience`` batches in a row were no more than
+    ``tol`` faster than the best batch before them (or after ``max_s``).
+    Returns what was run, for the JSON record."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    step()
+    e1.record(stream)
+    e1.synchronize()
+    per = max(e0.elapsed_time(e1), 1e-3)
+    n = max(4, int(batch_ms / per))
+    launches, gpu_ms, best, stale, batches = 1, per, float("inf"), 0, []
+    while True:
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        launches += n
+        gpu_ms += ms
+        batches.append(ms / n)
+        if ms / n < best * (1.0 - tol):
+            best, stale = ms / n, 0
+        else:
+            stale += 1
+        el = time.perf_counter() - t0
+        if (el >= min_s and stale >= patience) or el >= max_s:
+            break
+    return {"launches": launches, "seconds": round(time.perf_counter() - t0, 3), "gpu_ms": round(gpu_ms, 1),
+            "first_batch_ms_per_launch": round(batches[0], 4), "last_batch_ms_per_launch": round(batches[-1], 4),
+            "rule": f"after the requested warm-up, batches of ~{batch_ms:g} ms of launches until >= {min_s:g} s "
+                    f"and {patience} batches in a row within {tol:.0%} of the best (cap {max_s:g} s)"}
+
+
+def measured_mfma_flops(kernel: str, workload: str):
+    """bf16 MFMA flops performed per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+    from the committed counter summary, or None when it is missing or was
+    taken on a different kernel source."""
+    path = os.path.join(PROFILES, "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        db = json.load(fh)
+    from test_sequence_layer_amd.profiling import source_hash
+
+    rec = db.get(f"{kernel}|{workload}")
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("mfma_flops_performed")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU clock settles only after ~50 back-to-back launches (~30 ms at the
-    # 1.3B shape: the first launches run up to 40% slower), so warm up with 100.
+    # whatever --warmup asks, settle() then runs until launch times stop falling
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="l1p3b", choices=sorted(ti.CONFIGS))
@@ -207,6 +281,8 @@ def main():
     ap.add_argument("--bwd", action="store_true", help="time the TTT-Linear backward (ttt_linear_bwd)")
     ap.add_argument("--train", action="store_true",
                     help="time forward-for-training + backward (one training step of the layer)")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the warm-up that runs until launch times stop falling (timing studies of the ramp)")
     ap.add_argument("--no-measured-peak", action="store_true",
                     help="skip measuring the chip's achievable peak (HBM copy or bf16 MFMA loop) "
                          "that roofline.frac_measured is stated against")
@@ -343,6 +419,10 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    settled = None if args.no_settle else settle(step, stream)
+    if settled:
+        log(f"bench: settled after {settled['launches']} more launches ({settled['seconds']} s): "
+            f"{settled['first_batch_ms_per_launch']} -> {settled['last_batch_ms_per_launch']} ms/launch")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -391,9 +471,17 @@ def main():
                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
     roof.update({"algorithmic_bytes": bytes_, "algorithmic_flops": flops, "achieved_gbs": round(achieved, 1),
                  "kernel": kname, "kernel_ms": round(kernel_ms, 4)})
+    # matrix-core work: the algorithmic flops against the dense bf16 peak (every
+    # contraction runs on bf16 MFMA), and the flops the kernel actually issued
+    # (hi/lo split passes, zero-padded k-slots) from the committed counters
     mfma = {"algorithmic_flops": flops, "achieved_tflops": round(tflops, 2),
-            "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
-            "frac_of_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    performed = measured_mfma_flops(kname, cfg.name) if plain else None
+    if performed:
+        ptf = performed / (kernel_ms / 1e3) / 1e12
+        mfma.update({"performed_flops": performed, "performed_over_algorithmic": round(performed / flops, 3),
+                     "performed_tflops": round(ptf, 2), "performed_frac_of_bf16_peak": round(ptf / BF16_PEAK_TFLOPS, 4),
+                     "performed_from": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, profiles/counters.json"})
     log(f"bench: {kname}: {kernel_ms:.3f} ms/launch, {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM), "
         f"{tflops:.1f} TFLOP/s algorithmic")
 
@@ -462,7 +550,8 @@ def main():
         "metric": METRIC if headline else
         f"{model} {form.strip() + ' ' if form.strip() else ''}{direction} tokens/sec ({cfg.name})",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "warmup_settle": settled,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" and not args.generic else "fp32",
         "data": "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) weights)",

@@ -225,7 +225,23 @@ def summarize_counters(pmc_dir, kernel, workload, algorithmic_flops, command, ou
         fh.write(f"| algorithmic flops | {algorithmic_flops:.4e} |\n")
         fh.write(f"| performed / algorithmic (split passes, padding) | {performed / algorithmic_flops:.2f} |\n")
         fh.write(f"| kernel source hash | {source_hash(kernel)} |\n")
+    record_counters(kernel, workload, med, out_dir)
     return md
+
+
+def record_counters(kernel, workload, med, out_dir=PROFILES, source=None):
+    """Keep the medians of one counter run in profiles/counters.json, keyed by
+    kernel|workload with the kernel's source hash (bench.py reports the MFMA
+    flops performed only while that hash is current)."""
+    cj = os.path.join(out_dir, "counters.json")
+    db = json.load(open(cj)) if os.path.exists(cj) else {}
+    db[f"{kernel}|{workload}"] = {"mfma_util_pct": round(med["MfmaUtil"], 2), "valu_busy_pct": round(med["VALUBusy"], 2),
+                                  "lds_bank_conflict_pct": round(med["LDSBankConflict"], 2),
+                                  "grbm_gui_active": round(med["GRBM_GUI_ACTIVE"]),
+                                  "mfma_flops_performed": round(med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512),
+                                  "source_hash": source or source_hash(kernel)}
+    with open(cj, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
 
 
 def main():
