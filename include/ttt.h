@@ -64,7 +64,8 @@ typedef enum {
   TTT_ERR_STRIDE = 8,      /* negative eta stride, or w0 stride not 0 / H*d*d    */
   TTT_ERR_FLAGS = 9,       /* unknown bit set in flags                           */
   TTT_ERR_POS = 10,        /* negative decode position                           */
-  TTT_ERR_WORKSPACE = 11   /* workspace missing, misaligned or too small         */
+  TTT_ERR_WORKSPACE = 11,  /* workspace missing, misaligned or too small         */
+  TTT_ERR_SCRATCH = 12     /* the call needs more than TTT_NOALLOC_SCRATCH_BYTES  */
 } ttt_status;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
@@ -133,6 +134,29 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
 
 /* Workspace bytes ttt_linear_fwd_chunked needs (0 for nchunks = 1; -1 if desc is NULL or nchunks < 1). */
 int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t nchunks);
+
+/*
+ * ttt_linear_fwd_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The chunk maps and start states go to a
+ * static device array of TTT_NOALLOC_SCRATCH_BYTES inside the library: one
+ * copy per GPU, taken when the library's code is first loaded on that GPU and
+ * held until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); on its first call on a GPU it looks
+ * up that GPU's copy (hipGetSymbolAddress, the GPU that owns `stream`).
+ * Arguments, results and errors as ttt_linear_fwd_chunked, except:
+ *   - a call whose ttt_linear_chunked_workspace_bytes exceeds
+ *     TTT_NOALLOC_SCRATCH_BYTES returns TTT_ERR_SCRATCH before any launch;
+ *   - every call on one GPU shares that GPU's scratch, so calls that may run
+ *     at the same time on one GPU (different streams, or graphs replayed
+ *     concurrently) race and give wrong results: order them on one stream.
+ * A failed symbol lookup returns TTT_ERR_HIP.  This entry point keeps global
+ * state (the scratch and the per-GPU addresses), unlike the others.
+ */
+#define TTT_NOALLOC_SCRATCH_BYTES (32ll * 1024 * 1024)
+ttt_status ttt_linear_fwd_chunked_noalloc(const ttt_linear_desc* desc, int32_t nchunks, const void* Q,
+                                          const void* K, const void* V, const float* W0, const float* eta,
+                                          void* Z, float* W_final, void* stream);
 
 /*
  * TTT-Linear with layer norm and residual inside f ([TTT] 03 §9: the layer's

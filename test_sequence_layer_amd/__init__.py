@@ -42,14 +42,16 @@ def _rows_flag(rows) -> int:
 STATUS_NAMES = {
     0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE", 4: "TTT_ERR_UNSUPPORTED",
     5: "TTT_ERR_ALIAS", 6: "TTT_ERR_ALIGN", 7: "TTT_ERR_HIP", 8: "TTT_ERR_STRIDE", 9: "TTT_ERR_FLAGS",
-    10: "TTT_ERR_POS", 11: "TTT_ERR_WORKSPACE",
+    10: "TTT_ERR_POS", 11: "TTT_ERR_WORKSPACE", 12: "TTT_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # TTT_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/ttt.h declares.
 EXPORTS = (
     "ttt_linear_fwd", "ttt_linear_validate", "ttt_linear_kernel_name",
     "ttt_linear_decode", "ttt_linear_decode_validate",
-    "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes", "ttt_linear_ln_fwd",
+    "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes", "ttt_linear_fwd_chunked_noalloc",
+    "ttt_linear_ln_fwd",
     "ttt_linear_fwd_save", "ttt_linear_bwd", "ttt_linear_bwd_validate", "ttt_linear_bwd_kernel_name",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name", "ttt_mlp_ln_fwd",
     "ttt_status_str", "ttt_abi_version",
@@ -116,6 +118,9 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_fwd_chunked.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int32, vp, vp, vp, fp, fp, vp, fp,
                                          vp, ctypes.c_int64, vp]
     L.ttt_linear_fwd_chunked.restype = ctypes.c_int
+    L.ttt_linear_fwd_chunked_noalloc.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int32, vp, vp, vp, fp, fp,
+                                                 vp, fp, vp]
+    L.ttt_linear_fwd_chunked_noalloc.restype = ctypes.c_int
     L.ttt_linear_chunked_workspace_bytes.argtypes = [ctypes.POINTER(LinearDesc), ctypes.c_int32]
     L.ttt_linear_chunked_workspace_bytes.restype = ctypes.c_int64
     L.ttt_linear_ln_fwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, fp, vp, fp,
@@ -411,6 +416,29 @@ def linear_fwd_chunked(q, k, v, w0, eta, b: int, nchunks: int, workspace=None, o
                                       _ptr(eta_t), _ptr(z), _ptr(w_final), _ptr(workspace), wbytes,
                                       _stream_handle(stream))
     _done(st, "ttt_linear_fwd_chunked")
+    return z, w_final
+
+
+def linear_fwd_chunked_noalloc(q, k, v, w0, eta, b: int, nchunks: int, out_dtype=None, w_final=None, z=None,
+                               rows=None, stream=None):
+    """:func:`linear_fwd_chunked` with the library's static scratch in place of a
+    workspace (ttt_linear_fwd_chunked_noalloc: the call allocates no device
+    memory; calls that overlap on one GPU race).  ``z`` and ``w_final`` are
+    allocated here when omitted; pass them to keep the call allocation-free."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    wstride = _w0_stride(w0, B, H, d)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    if w_final is None:
+        w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    _check_dev(q, k, v, w0, eta_t, z, w_final)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, _rows_flag(rows))
+    st = lib().ttt_linear_fwd_chunked_noalloc(ctypes.byref(desc), int(nchunks), _ptr(q), _ptr(k), _ptr(v), _ptr(w0),
+                                              _ptr(eta_t), _ptr(z), _ptr(w_final), _stream_handle(stream))
+    _done(st, "ttt_linear_fwd_chunked_noalloc")
     return z, w_final
 
 

@@ -3,10 +3,48 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/ttt.h"
 #include "ttt_internal.h"
 
+// Scratch of ttt_linear_fwd_chunked_noalloc (chunk maps and start states):
+// one copy per GPU the library runs on, held until the process ends.  In host
+// code this name stands for a host-side shadow, not device memory: host code
+// uses only the per-device address scratch_address() looks up.
+__device__ __align__(256) unsigned char scratch[TTT_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of each GPU's `scratch` (nullptr: not looked up yet)
+
+// The device address of `scratch` on the GPU that owns `stream`, looked up once
+// per device (hipGetSymbolAddress with that device current) and kept.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
 
 struct Range {
   const void* p;
@@ -346,6 +384,9 @@ const char* ttt_status_str(int s) {
     case TTT_ERR_FLAGS: return "unknown flag or non-zero reserved field";
     case TTT_ERR_POS: return "negative decode position";
     case TTT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TTT_ERR_SCRATCH:
+      return "the call needs more than the library's static scratch (TTT_NOALLOC_SCRATCH_BYTES); "
+             "use ttt_linear_fwd_chunked with a workspace, or fewer chunks";
     default: return "unknown status";
   }
 }
@@ -479,9 +520,11 @@ int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t 
   return static_cast<int64_t>(desc->B) * desc->H * per_chain;
 }
 
-ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K,
-                                  const void* V, const float* W0, const float* eta, void* Z, float* W_final,
-                                  void* workspace, int64_t workspace_bytes, void* stream) {
+namespace {
+
+// Argument checks of the chunked forward (everything but the workspace).
+ttt_status validate_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K,
+                            const void* V, const float* W0, const float* eta, const void* Z, const float* W_final) {
   Kernel k;
   ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
   if (st != TTT_OK) return st;
@@ -490,6 +533,22 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
   // workgroups of the map launch (2 maps per chunk but the last) and of the chunk forward
   if (static_cast<int64_t>(desc->B) * desc->H * 2 * nchunks * row_blocks(desc->flags) > INT_MAX)
     return TTT_ERR_SHAPE;
+  return TTT_OK;
+}
+
+// The chunked forward's launches, after validate_chunked, nchunks > 1 and
+// B*H > 0, with a workspace of at least the bytes it needs.
+ttt_status run_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K, const void* V,
+                       const float* W0, const float* eta, void* Z, float* W_final, void* workspace,
+                       void* stream);
+
+}  // namespace
+
+ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K,
+                                  const void* V, const float* W0, const float* eta, void* Z, float* W_final,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+  ttt_status st = validate_chunked(desc, nchunks, Q, K, V, W0, eta, Z, W_final);
+  if (st != TTT_OK) return st;
   if (nchunks == 1) return ttt_linear_fwd(desc, Q, K, V, W0, eta, Z, W_final, stream);
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   if (chains == 0) return TTT_OK;
@@ -507,6 +566,30 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
                     Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
       if (overlaps(rw, r)) return TTT_ERR_ALIAS;
   }
+  return run_chunked(desc, nchunks, Q, K, V, W0, eta, Z, W_final, workspace, stream);
+}
+
+ttt_status ttt_linear_fwd_chunked_noalloc(const ttt_linear_desc* desc, int32_t nchunks, const void* Q,
+                                          const void* K, const void* V, const float* W0, const float* eta,
+                                          void* Z, float* W_final, void* stream) {
+  ttt_status st = validate_chunked(desc, nchunks, Q, K, V, W0, eta, Z, W_final);
+  if (st != TTT_OK) return st;
+  if (nchunks == 1) return ttt_linear_fwd(desc, Q, K, V, W0, eta, Z, W_final, stream);
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  if (ttt_linear_chunked_workspace_bytes(desc, nchunks) > TTT_NOALLOC_SCRATCH_BYTES) return TTT_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_address(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return TTT_ERR_HIP;
+  // (the chunked passes write every map and start state before reading it, so
+  // the scratch needs no clearing between calls)
+  return run_chunked(desc, nchunks, Q, K, V, W0, eta, Z, W_final, ws, stream);
+}
+
+namespace {
+
+ttt_status run_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K, const void* V,
+                       const float* W0, const float* eta, void* Z, float* W_final, void* workspace,
+                       void* stream) {
+  const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
   a.nchunk = nchunks;
   a.Tc = desc->T / nchunks;
@@ -518,6 +601,8 @@ ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, 
   if (e == hipSuccess) e = ttt::launch_linear_mfma(a, s);
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
+
+}  // namespace
 
 ttt_status ttt_linear_decode_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                                       const float* eta, const void* Z, const float* W, const float* Wb,

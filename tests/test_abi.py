@@ -16,7 +16,7 @@ import test_sequence_layer_amd as ttt
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ttt.h")
 
-OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, ALIGN, HIP, STRIDE, FLAGS, POS, WORKSPACE = range(12)
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, ALIGN, HIP, STRIDE, FLAGS, POS, WORKSPACE, SCRATCH = range(13)
 GB = 1 << 30
 
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert ttt.abi_version() == 1
-    for s in range(12):
+    for s in range(13):
         assert ttt.status_str(s) and ttt.status_str(s) != "unknown status"
     assert ttt.status_str(99) == "unknown status"
 
@@ -225,6 +225,33 @@ def test_chunked_workspace_bytes():
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 8) == 64 * (7 * 2 + 8) * 64 * 64 * 4
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 0) == -1
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(None, 4) == -1
+
+
+def test_chunked_noalloc_host_errors():
+    """The allocation-free chunked forward's argument errors return before any
+    HIP call (so they run without a GPU): bad shapes and flags as the chunked
+    forward, and TTT_ERR_SCRATCH when the maps and start states would not fit
+    the static scratch."""
+    f = ttt.lib().ttt_linear_fwd_chunked_noalloc
+
+    def call(desc, nchunks, **over):
+        b = Bufs()
+        for k_, v_ in over.items():
+            setattr(b, k_, v_)
+        return f(ctypes.byref(desc), nchunks, *b.args(), None)
+
+    assert call(_desc(B=2, H=32, T=32768), 0) == SHAPE
+    assert call(_desc(B=2, H=32, T=32768), 3) == SHAPE          # T % (16 * nchunks) != 0
+    assert call(_desc(B=2, H=32, T=32768, ind=0), 4) == UNSUP   # fp32 inputs: no matrix-core path
+    assert call(_desc(B=2, H=32, T=32768, flags=1), 4) == UNSUP
+    assert call(_desc(B=2, H=32, T=32768), 4, q=None) == NULL
+    assert call(_desc(B=2, H=32, T=32768), 4, z=3 * GB) == ALIAS
+    big = _desc(B=16, H=32, T=8192)                              # 512 chains x 4 chunks: 80 MiB of maps
+    need = ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(big), 4)
+    assert need > ttt.NOALLOC_SCRATCH_BYTES
+    assert call(big, 4) == SCRATCH
+    assert "static scratch" in ttt.status_str(SCRATCH)
+    assert f(None, 4, *Bufs().args(), None) == NULL
 
 
 # ---- backward validation ----------------------------------------------------------
