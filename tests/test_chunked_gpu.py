@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import ttt_inputs as ti
-from ttt_testutil import max_rel, rows, to_device
+from ttt_testutil import CONTRACT_BF16, REGRESS_MFMA, max_rel, parity, rows, to_device
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -34,10 +34,9 @@ def test_chunked_small(ttt, nchunks, eta_kind):
     zp, wp = ttt.linear_fwd(t["q"], t["k"], t["v"], t["w1"], t["eta"], 16)
     torch.cuda.synchronize()
     zr, wr = oracle.run_inputs(inp)
-    ez, ew = max_rel(rows(z), zr), max_rel(rows(wf), wr)
-    print(f"chunked n={nchunks} {eta_kind}: Z {ez:.3e} W {ew:.3e}  vs plain Z {max_rel(rows(z), rows(zp)):.3e}",
-          flush=True)
-    assert ez < 2e-3 and ew < 2e-3
+    parity(f"chunked n={nchunks} {eta_kind}", [("Z", rows(z), zr), ("W_final", rows(wf), wr)], CONTRACT_BF16,
+           REGRESS_MFMA)
+    print(f"chunked n={nchunks} {eta_kind}: vs plain Z {max_rel(rows(z), rows(zp)):.3e}", flush=True)
     assert max_rel(rows(z), rows(zp)) < 1e-4 and max_rel(rows(wf), rows(wp)) < 1e-4
 
 
@@ -49,9 +48,8 @@ def test_chunked_long_config(ttt):
     torch.cuda.synchronize()
     ch = ti.sample_chains(cfg, 6)
     zr, wr = oracle.run_inputs(ti.generate(cfg, chains=ch))
-    ez, ew = max_rel(rows(z, ch), zr), max_rel(rows(wf, ch), wr)
-    print(f"chunked long (8 chunks): Z {ez:.3e} W {ew:.3e}", flush=True)
-    assert ez < 2e-3 and ew < 2e-3
+    parity("chunked long (8 chunks)", [("Z", rows(z, ch), zr), ("W_final", rows(wf, ch), wr)], CONTRACT_BF16,
+           REGRESS_MFMA)
 
 
 def test_chunked_inplace_state_and_workspace_reuse(ttt):

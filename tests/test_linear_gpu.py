@@ -1,15 +1,16 @@
 """GPU parity of TTT-Linear (libttt.so through its C ABI) against the fp64 oracle.
 
 Tolerances (max over chains of max|x - ref| / max|ref|): 1e-5 for fp32
-inputs, 2e-3 for bf16 inputs (fp32 Z).  The MFMA kernel's own error budget is
-far below that (hi+lo bf16 operands, fp32 sums); each test prints its error.
+inputs, 2e-3 for bf16 inputs (fp32 Z), and for bf16 inputs also the 5e-5
+regression bound of the hi+lo split-bf16 arithmetic (tests/ttt_testutil.py);
+each test prints the max-norm, elementwise and Frobenius errors.
 """
 import numpy as np
 import pytest
 
 import oracle
 import ttt_inputs as ti
-from ttt_testutil import max_rel, rows, to_device
+from ttt_testutil import CONTRACT_BF16, CONTRACT_FP32, REGRESS_MFMA, max_rel, parity, rows, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -41,17 +42,16 @@ def _check(ttt, cfg, tol, chains=None, generic=False, out_dtype=None, label=""):
         chains = np.arange(cfg.chains)
     sub = ti.generate(cfg, chains=chains)
     zr, wr = oracle.run_inputs(sub)
-    ez = max_rel(rows(z, chains), zr)
-    ew = max_rel(rows(wf, chains), wr)
     name = ttt.linear_kernel_name(cfg.B, cfg.H, cfg.T, cfg.d, cfg.b,
                                   1 if cfg.dtype == "bf16" else 0, 0, full.eta_strides, generic)
-    print(f"[{label or cfg.name}] kernel={name} chains={len(chains)} err Z={ez:.3e} W_final={ew:.3e}", flush=True)
-    assert ez < tol and ew < tol, (ez, ew)
-    return ez, ew
+    e = parity(f"{label or cfg.name} kernel={name} chains={len(chains)}",
+               [("Z", rows(z, chains), zr), ("W_final", rows(wf, chains), wr)], tol,
+               REGRESS_MFMA if cfg.dtype == "bf16" and out_dtype in (None, torch.float32) else None)
+    return e["Z"]["max"], e["W_final"]["max"]
 
 
 def test_tiny_fp32(ttt):
-    _check(ttt, ti.CONFIGS["tiny"], 1e-5)
+    _check(ttt, ti.CONFIGS["tiny"], CONTRACT_FP32)
 
 
 @pytest.mark.parametrize("B,H,T", [(1, 1, 16), (2, 3, 112), (3, 5, 256), (1, 2, 80)])
@@ -59,19 +59,19 @@ def test_tiny_fp32(ttt):
 def test_bf16_mfma_small(ttt, B, H, T, eta_kind):
     cfg = ti.CONFIGS["l1p3b"].with_(B=B, H=H, T=T, eta_kind=eta_kind, eta_value=1.0 / 64, seed=7 + T)
     assert ttt.linear_kernel_name(B, H, T, 64, 16).startswith("ttt_linear_mfma_d64b16")
-    _check(ttt, cfg, 2e-3, label=f"mfma B{B} H{H} T{T} {eta_kind}")
+    _check(ttt, cfg, CONTRACT_BF16, label=f"mfma B{B} H{H} T{T} {eta_kind}")
 
 
 @pytest.mark.parametrize("B,H,T,eta_kind", [(2, 3, 112, "token"), (1, 2, 64, "scalar")])
 def test_bf16_generic_small(ttt, B, H, T, eta_kind):
     cfg = ti.CONFIGS["l1p3b"].with_(B=B, H=H, T=T, eta_kind=eta_kind, eta_value=1.0 / 64, seed=11 + T)
-    _check(ttt, cfg, 2e-3, generic=True, label=f"generic B{B} H{H} T{T} {eta_kind}")
+    _check(ttt, cfg, CONTRACT_BF16, generic=True, label=f"generic B{B} H{H} T{T} {eta_kind}")
 
 
 @pytest.mark.parametrize("d,b,T", [(64, 16, 128), (32, 8, 96), (16, 4, 64), (64, 32, 64), (16, 1, 20)])
 def test_fp32_generic(ttt, d, b, T):
     cfg = ti.CONFIGS["tiny"].with_(B=2, H=3, d=d, b=b, T=T, eta_value=0.05, seed=d * b + T)
-    _check(ttt, cfg, 1e-5, label=f"fp32 d{d} b{b} T{T}")
+    _check(ttt, cfg, CONTRACT_FP32, label=f"fp32 d{d} b{b} T{T}")
 
 
 def test_mfma_vs_generic(ttt):
@@ -88,17 +88,17 @@ def test_mfma_vs_generic(ttt):
 # ---- the workloads at full size, in the launch configuration the benchmark times ----
 
 def test_config_l125m_all_chains(ttt):
-    _check(ttt, ti.CONFIGS["l125m"], 2e-3)
+    _check(ttt, ti.CONFIGS["l125m"], CONTRACT_BF16)
 
 
 def test_config_l1p3b_sampled(ttt):
     cfg = ti.CONFIGS["l1p3b"]
-    _check(ttt, cfg, 2e-3, chains=ti.sample_chains(cfg, 24))
+    _check(ttt, cfg, CONTRACT_BF16, chains=ti.sample_chains(cfg, 24))
 
 
 def test_config_long_sampled(ttt):
     cfg = ti.CONFIGS["long"]
-    _check(ttt, cfg, 2e-3, chains=ti.sample_chains(cfg, 6))
+    _check(ttt, cfg, CONTRACT_BF16, chains=ti.sample_chains(cfg, 6))
 
 
 # ---- pins that need no oracle ----

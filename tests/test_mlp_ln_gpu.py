@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import ttt_inputs as ti
-from ttt_testutil import max_rel, rows, to_device
+from ttt_testutil import CONTRACT_BF16, REGRESS_MFMA, REGRESS_MFMA_LN_MLP, max_rel, parity, rows, to_device
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -55,9 +55,8 @@ def test_small(ttt, B, H, T, eta_kind):
     gamma, beta = _ln_params(H, 64, 5 + T)
     inp, _, z, w1f, w2f = _run(ttt, cfg, gamma, beta)
     zr, w1r, w2r = _oracle(inp, gamma, beta)
-    errs = [max_rel(rows(x), r) for x, r in ((z, zr), (w1f, w1r), (w2f, w2r))]
-    print(f"mlp+ln B{B} H{H} T{T} {eta_kind}: Z {errs[0]:.3e} W1 {errs[1]:.3e} W2 {errs[2]:.3e}", flush=True)
-    assert max(errs) < 2e-3, errs
+    parity(f"mlp+ln B{B} H{H} T{T} {eta_kind}",
+           [("Z", rows(z), zr), ("W1", rows(w1f), w1r), ("W2", rows(w2f), w2r)], CONTRACT_BF16, REGRESS_MFMA_LN_MLP)
 
 
 def test_large_step_and_eps(ttt):
@@ -67,9 +66,8 @@ def test_large_step_and_eps(ttt):
     gamma, beta = _ln_params(2, 64, 11)
     inp, _, z, w1f, w2f = _run(ttt, cfg, gamma, beta, eps=0.05)
     zr, w1r, w2r = _oracle(inp, gamma, beta, eps=0.05)
-    errs = [max_rel(rows(x), r) for x, r in ((z, zr), (w1f, w1r), (w2f, w2r))]
-    print(f"mlp+ln large step, eps 0.05: {errs}", flush=True)
-    assert max(errs) < 2e-3, errs
+    parity("mlp+ln large step, eps 0.05",
+           [("Z", rows(z), zr), ("W1", rows(w1f), w1r), ("W2", rows(w2f), w2r)], CONTRACT_BF16, REGRESS_MFMA_LN_MLP)
 
 
 def test_config_mlp_sampled(ttt):
@@ -98,9 +96,10 @@ def test_config_mlp_sampled(ttt):
     heads = np.asarray(ch) % cfg.H
     zr, w1r, w2r = oracle.mlp_ln_primal(sub.q, sub.k, sub.v, w1[heads], w2[heads], gamma[heads], beta[heads],
                                         sub.eta_rows(), cfg.b, 1e-6)
-    errs = [max_rel(rows(x, ch), r) for x, r in ((z, zr), (w1f, w1r), (w2f, w2r))]
-    print(f"mlp+ln full shape, chains {list(ch)}: {errs}", flush=True)
-    assert max(errs) < 2e-3, errs
+    # well conditioned at this scale: the matrix-core bound of the plain forms
+    parity(f"mlp+ln full shape (W1 x 20, W2 x 5), chains {list(ch)}",
+           [("Z", rows(z, ch), zr), ("W1", rows(w1f, ch), w1r), ("W2", rows(w2f, ch), w2r)], CONTRACT_BF16,
+           REGRESS_MFMA)
 
 
 def test_eta_zero(ttt):
@@ -111,7 +110,23 @@ def test_eta_zero(ttt):
     assert torch.equal(w1f, t["w1"].unsqueeze(0).expand_as(w1f))
     assert torch.equal(w2f, t["w2"].unsqueeze(0).expand_as(w2f))
     zr, _, _ = _oracle(inp, gamma, beta, eta_rows=np.zeros((cfg.chains, cfg.T)))
-    assert max_rel(rows(z), zr) < 2e-3
+    parity("mlp+ln eta=0", [("Z", rows(z), zr)], CONTRACT_BF16, REGRESS_MFMA_LN_MLP)
+
+
+def test_config_mlp_workload_scale_t512(ttt):
+    """The workload's own 0.02-std weights at the full batch and heads (B16 H32),
+    T = 512: the longest of 512/1024/2048 at which fp32 arithmetic itself stays
+    well inside the bar (the fp32 numpy dual form is ~6e-5 off the fp64 oracle
+    here and ~8e-3 at T = 2048, where the layer norm's backward amplifies rounding
+    through the recurrence), so the kernel must meet both bounds."""
+    cfg = ti.CONFIGS["mlp"].with_(T=512)
+    gamma, beta = _ln_params(cfg.H, cfg.d, 12)
+    inp, t, z, w1f, w2f = _run(ttt, cfg, gamma, beta)
+    ch = ti.sample_chains(cfg, 4)
+    zr, w1r, w2r = _oracle(ti.generate(cfg, chains=ch), gamma, beta)
+    parity(f"mlp+ln workload scale T512, chains {list(ch)}",
+           [("Z", rows(z, ch), zr), ("W1", rows(w1f, ch), w1r), ("W2", rows(w2f, ch), w2r)], CONTRACT_BF16,
+           REGRESS_MFMA_LN_MLP)
 
 
 def test_zero_gamma(ttt):

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import ttt_inputs as ti
-from ttt_testutil import max_rel, rows, to_device
+from ttt_testutil import CONTRACT_BF16, REGRESS_MFMA, parity, rows, to_device
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -40,9 +40,7 @@ def _case(ttt, cfg, nchunks):
     assert torch.equal(z, zr) and torch.equal(wf, wr)
     ch = ti.sample_chains(cfg, 4)
     zo, wo = oracle.run_inputs(ti.generate(cfg, chains=ch))
-    ez, ew = max_rel(rows(z, ch), zo), max_rel(rows(wf, ch), wo)
-    print(f"noalloc: vs oracle Z {ez:.3e} W_final {ew:.3e}", flush=True)
-    assert ez < 2e-3 and ew < 2e-3
+    parity("noalloc vs oracle", [("Z", rows(z, ch), zo), ("W_final", rows(wf, ch), wo)], CONTRACT_BF16, REGRESS_MFMA)
 
 
 def test_noalloc_two_calls_second_smaller(ttt):
