@@ -535,7 +535,8 @@ def main():
             ": layer norm and residual inside f"
     if args.chunks > 1:
         form = f"chunked({args.chunks})"
-        roof["note"] = "chunked forward: chunk maps + scan + parallel chunks (3 launches per call)"
+        roof["note"] = ("chunked forward: chunk 0 with the maps of chunks 1..n-2, the scan of the maps, then "
+                        "chunks 1..n-1 in parallel (3 launches per call)")
     direction = "fwd"
     if args.save:
         form, direction = "", "fwd (saving E for the backward)"

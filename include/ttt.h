@@ -119,14 +119,18 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
  * parallel: the same result as ttt_linear_fwd (to rounding), for shapes with
  * few (sequence, head) chains and long sequences.  Each mini-batch maps the
  * state affinely (W -> W P_n + R_n, P_n = I - 2 K diag(eta) K^T,
- * R_n = 2 V diag(eta) K^T; [TTT] 03 §7), so the library (1) composes the map of
- * every chunk but the last in parallel, (2) scans them to get each chunk's
- * start state, (3) runs every chunk's forward in parallel from its start state.
- * Requires the MFMA path (d = 64, b = 16, bf16 inputs; flags 0 or one
- * TTT_FLAG_ROWS*, applied to both parallel passes) and T % (16 * nchunks) == 0.  workspace: device memory of at least
- * ttt_linear_chunked_workspace_bytes(desc, nchunks) bytes, 16-byte aligned,
- * overlapping no argument; contents on return are unspecified.  nchunks = 1
- * is ttt_linear_fwd (the workspace may then be NULL).
+ * R_n = 2 V diag(eta) K^T; [TTT] 03 §7), so a chunk maps it as W -> W P + R.
+ * With nb = T / 16 mini-batches, chunk c holds mini-batches
+ * [c nb / nchunks, (c + 1) nb / nchunks) (integer division).  The library
+ * (1) runs chunk 0 from W0 and, in the same launch, composes the maps of
+ * chunks 1 .. nchunks-2 (the last chunk needs none), (2) scans them to get the
+ * start state of every later chunk, (3) runs chunks 1 .. nchunks-1 in
+ * parallel from their start states.  Requires the MFMA path (d = 64, b = 16,
+ * bf16 inputs; flags 0 or one TTT_FLAG_ROWS*, which applies to pass (3)) and
+ * 1 <= nchunks <= T / 16 (else TTT_ERR_SHAPE).  workspace: device memory of at
+ * least ttt_linear_chunked_workspace_bytes(desc, nchunks) bytes, 16-byte
+ * aligned, overlapping no argument; contents on return are unspecified.
+ * nchunks = 1 is ttt_linear_fwd (the workspace may then be NULL).
  */
 ttt_status ttt_linear_fwd_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void* Q, const void* K,
                                   const void* V, const float* W0, const float* eta, void* Z, float* W_final,

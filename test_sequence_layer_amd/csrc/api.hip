@@ -104,7 +104,7 @@ ttt::LinearArgs make_linear_args(const ttt_linear_desc* d, const void* Q, const 
   a.Q = Q; a.K = K; a.V = V; a.W0 = W0; a.w0_bstride = d->w0_batch_stride;
   a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
   a.Z = const_cast<void*>(Z); a.Wf = const_cast<float*>(Wf);
-  a.nchunk = 1; a.Tc = d->T; a.Wstart = nullptr; a.maps = nullptr;
+  a.nchunk = 1; a.Wstart = nullptr; a.maps = nullptr;
   a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
   a.Esave = nullptr;
   a.rb = row_blocks(d->flags);
@@ -516,7 +516,8 @@ ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const v
 int64_t ttt_linear_chunked_workspace_bytes(const ttt_linear_desc* desc, int32_t nchunks) {
   if (!desc || nchunks < 1 || desc->B < 0 || desc->H < 0 || desc->d < 1) return -1;
   if (nchunks == 1) return 0;
-  const int64_t per_chain = (static_cast<int64_t>(nchunks - 1) * 2 + nchunks) * desc->d * desc->d * 4;
+  // maps (P, R) of chunks 1 .. n-2 and start states of chunks 1 .. n-1
+  const int64_t per_chain = (static_cast<int64_t>(nchunks - 2) * 2 + (nchunks - 1)) * desc->d * desc->d * 4;
   return static_cast<int64_t>(desc->B) * desc->H * per_chain;
 }
 
@@ -528,10 +529,12 @@ ttt_status validate_chunked(const ttt_linear_desc* desc, int32_t nchunks, const 
   Kernel k;
   ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
   if (st != TTT_OK) return st;
-  if (nchunks < 1 || desc->T % (16 * nchunks) != 0) return TTT_ERR_SHAPE;
+  if (nchunks < 1 || nchunks > desc->T / 16) {  // every chunk holds at least one mini-batch
+    if (!(nchunks == 1 && desc->T == 0)) return TTT_ERR_SHAPE;
+  }
   if ((desc->flags & ~kRowFlags) != 0 || k != K_MFMA) return TTT_ERR_UNSUPPORTED;
-  // workgroups of the map launch (2 maps per chunk but the last) and of the chunk forward
-  if (static_cast<int64_t>(desc->B) * desc->H * 2 * nchunks * row_blocks(desc->flags) > INT_MAX)
+  // workgroups of the launches (nchunks - 1 units per chain, row blocks in the last)
+  if (static_cast<int64_t>(desc->B) * desc->H * nchunks * row_blocks(desc->flags) > INT_MAX)
     return TTT_ERR_SHAPE;
   return TTT_OK;
 }
@@ -592,12 +595,14 @@ ttt_status run_chunked(const ttt_linear_desc* desc, int32_t nchunks, const void*
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
   a.nchunk = nchunks;
-  a.Tc = desc->T / nchunks;
   a.maps = static_cast<float*>(workspace);
-  a.Wstart = a.maps + chains * (nchunks - 1) * 2 * desc->d * desc->d;
+  a.Wstart = a.maps + chains * (nchunks - 2) * 2 * desc->d * desc->d;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = ttt::launch_linear_mfma_maps(a, s);
-  if (e == hipSuccess) e = ttt::launch_linear_chunk_scan(a, s);
+  // chunk 0 and the maps of chunks 1 .. n-2 (row blocks: one workgroup per unit)
+  ttt::LinearArgs a1 = a;
+  a1.rb = 1;
+  hipError_t e = ttt::launch_linear_mfma_head_maps(a1, s);
+  if (e == hipSuccess && nchunks > 2) e = ttt::launch_linear_chunk_scan(a, s);
   if (e == hipSuccess) e = ttt::launch_linear_mfma(a, s);
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }

@@ -3,11 +3,12 @@
 // Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，一夜推翻Transformer"
 // (aharts.cn / itmax.cn), part 03 §6-§7.  Each mini-batch of TTT-Linear maps the
 // state affinely, W -> W (I - 2 K diag(eta) K^T) + 2 V diag(eta) K^T, so a chunk
-// of mini-batches maps it as W -> W P + R.  With the maps P_c, R_c of every
-// chunk but the last (computed in parallel by the MFMA kernel in its map
-// mode), the start state of chunk c+1 is Wstart[c] P_c + R_c; this kernel runs
-// that short sequential scan per chain, after which every chunk's outputs are
-// computed in parallel from its start state.  Each 64 x 64 x 64 product runs on
+// of mini-batches maps it as W -> W P + R.  The first pass of a chunked forward
+// runs chunk 0 from W0 (so the start state of chunk 1 is known) and computes
+// the maps P_c, R_c of chunks 1 .. n-2 in parallel; the start state of chunk
+// c+1 is then Wstart[c] P_c + R_c, and this kernel runs that short sequential
+// scan per chain, after which chunks 1 .. n-1 are computed in parallel from
+// their start states.  Each 64 x 64 x 64 product runs on
 // the fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32 products and sums, no
 // bf16 splitting): wave w computes rows 16w .. 16w + 15 of W P + R, the four
 // 16 x 16 column tiles accumulating over k in steps of 4.
@@ -28,19 +29,15 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_chunk_scan(LinearArgs a) 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int chain = blockIdx.x;
-  const int bi = chain / a.H, h = chain - bi * a.H;
-  const float* w0 = a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D;
-  float* ws = a.Wstart + static_cast<int64_t>(chain) * a.nchunk * D * D;
-  for (int x = tid; x < D * D; x += kThreads) {
-    const float v = w0[x];
-    W[x / D][x % D] = v;
-    ws[x] = v;
-  }
+  // ws[c - 1]: start state of chunk c = 1 .. n-1; ws[0] was written by the first pass
+  float* ws = a.Wstart + static_cast<int64_t>(chain) * (a.nchunk - 1) * D * D;
+  for (int x = tid; x < D * D; x += kThreads) W[x / D][x % D] = ws[x];
   // This thread stages row pr, columns pc .. pc + 15 of the next P, and holds
   // R in the accumulator layout: acc[b][r] = R[16w + 4g + r][16b + li].  Both
   // are loaded one chunk ahead so their latency overlaps the current product.
   const int pr = tid >> 2, pc = (tid & 3) * 16;
-  const float* maps = a.maps + static_cast<int64_t>(chain) * (a.nchunk - 1) * 2 * D * D;
+  // maps[c - 1]: P, R of chunk c = 1 .. n-2
+  const float* maps = a.maps + static_cast<int64_t>(chain) * (a.nchunk - 2) * 2 * D * D;
   float4 pn[4];
   float4v rn[4];
   auto load_maps = [&](int c) {
@@ -53,15 +50,15 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_chunk_scan(LinearArgs a) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) rn[b][r] = Rg[r * D + 16 * b];
   };
-  if (a.nchunk > 1) load_maps(0);
-  for (int c = 0; c + 1 < a.nchunk; ++c) {
+  if (a.nchunk > 2) load_maps(0);
+  for (int c = 0; c + 2 < a.nchunk; ++c) {  // chunk c + 1's map: Wstart of chunk c + 2
     __syncthreads();  // W complete, previous P consumed
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(&P[pr][pc + 4 * q]) = pn[q];
     float4v acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = rn[b];
-    if (c + 2 < a.nchunk) load_maps(c + 1);
+    if (c + 3 < a.nchunk) load_maps(c + 1);
     __syncthreads();
     // acc[b] += W[16w + m][k] P[k][16b + n]: A operand W[16w + li][k0 + g],
     // B operand P[k0 + g][16b + li], k0 = 0, 4, ..., 60

@@ -98,29 +98,55 @@ __device__ __forceinline__ float ln_centre(const float4 y, float dv[4], float ep
   return rsqrtf(sum16(m2) * (1.f / 64.f) + eps);
 }
 
-// MODE 0: forward (Z and the final state).  MODE 1: chunk maps P and R of a
-// chunked forward -- the state recurrence from I with V = 0 / from 0 with V,
-// over one chunk, with no query path and no Z.
+// LDS of one workgroup, declared as separate arrays by each kernel (measured:
+// one struct holding them made the latency-bound forward 3% slower) and handed
+// to the body by reference: the double-buffered input slots, the layer norm's
+// exchange tiles, and for the forward the staging tiles of Z (and of E when it
+// is saved): each wave deposits its 16 outputs of every token, fp32
+// [token][output] with rows padded to ZROW, and one step later every thread
+// writes 16 contiguous bytes of whole rows.
+template <bool ZB, bool SAVE>
+struct Shm {
+  Slot (&slots)[2];
+  LnShared& lns;
+  float (&zbuf)[ZB ? 2 : 1][ZB ? BT * ZROW : 4];
+  float (&ebuf)[SAVE ? 2 : 1][SAVE ? BT * ZROW : 4];
+};
+
+// The stretch of one (sequence, head) chain a workgroup walks, and where its
+// state starts and ends.
+struct Unit {
+  int chain;
+  int rblk;              // row block (rows 64 / RB * rblk ..)
+  int64_t mb0;           // first mini-batch
+  int nb;                // mini-batches
+  const float* w_start;  // MODE 0: start state, row-major d x d (z = W q)
+  float* w_end;          // MODE 0: end state (nullptr: not kept); MODE 1: P
+  float* w_end2;         // MODE 1: R
+};
+
+// First mini-batch of chunk c when nb mini-batches are split into n chunks.
+__device__ __forceinline__ int64_t chunk_begin(int64_t c, int64_t nb, int64_t n) { return c * nb / n; }
+
+// MODE 0: forward (Z and the end state).  MODE 1: the two maps of one chunk of
+// a chunked forward, W_end = W_start P + R: P is the state recurrence run from I
+// with V = 0 and R the recurrence run from 0 with V, over the chunk, with no
+// query path and no Z; every wave holds its 16 rows of both (they share the
+// staged K and V tiles).
 // LN: f(x) = x + LN(W x) (layer norm and residual inside f; MODE 0 only).
 // SAVE: also write E = W K - V of every token (the backward's input; MODE 0, no LN).
 // RB: row blocks (workgroups) per (sequence, head, chunk); 1, 2 or 4.
-template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN, bool SAVE, int RB>
-__global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a) {
+template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN, bool SAVE, int RB, typename SH>
+__device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const Unit& u) {
   static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
   static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks");
   static_assert(!LN || RB == 1, "the layer norm needs all 64 outputs of a token in one workgroup");
   static_assert(!LN || (MODE == 0 && !SAVE), "the layer norm is a forward-only path");
+  static_assert(MODE == 0 || (RB == 1 && !SAVE), "the maps run in whole workgroups");
   constexpr int NWV = 4 / RB;   // waves per workgroup
   constexpr int NT = 64 * NWV;  // threads per workgroup
   constexpr int CA = 256 / NT;  // 16-byte pieces of the Q|K tiles each thread stages per step
-  __shared__ Slot slots[2];
-  __shared__ LnShared lns;
-  // Z of the last two mini-batches, fp32 [token][output] (rows padded to ZROW):
-  // each wave deposits its 16 outputs of every token, and one step later every
-  // thread writes 16 contiguous bytes of whole rows to HBM.
-  __shared__ __align__(16) float zbuf[MODE == 0 && !LN ? 2 : 1][MODE == 0 && !LN ? BT * ZROW : 4];
-  // E of the last two mini-batches when it is saved for the backward (same scheme)
-  __shared__ __align__(16) float ebuf[SAVE ? 2 : 1][SAVE ? BT * ZROW : 4];
+  auto& slots = sh.slots;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,42 +154,19 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   const int li = lane & 15;
   const int g = lane >> 4;
 
-  // workgroup -> (chain, chunk, row block); a plain forward has one chunk of
-  // T tokens.  The maps launch covers both maps: the first half of its grid
-  // computes P (from I, V = 0), the second half R (from 0, with V).
-  const int per_chain = MODE == 0 ? a.nchunk : a.nchunk - 1;
-  const int units = a.B * a.H * per_chain;
-  int blk = blockIdx.x;
-  bool map_r = false;
-  if constexpr (MODE != 0) {
-    map_r = blk >= units * RB;
-    if (map_r) blk -= units * RB;
-  }
-  // The RB row blocks of a unit are 8 block indices apart, so the round-robin
-  // dispatch of workgroups over the 8 XCDs places them on one XCD (one L2).
-  // A last group of fewer than 8 units is packed the same way with its size.
-  int unit = blk, rblk = 0;
-  if constexpr (RB > 1) {
-    const int full = units / 8;
-    const int grp = blk / (8 * RB);
-    const int in = blk - grp * 8 * RB;
-    const int width = grp < full ? 8 : units - full * 8;  // > 0: blk < units * RB
-    rblk = in / width;
-    unit = grp * 8 + (in - rblk * width);
-  }
-  const int chain = unit / per_chain;
-  const int chunk = unit - chain * per_chain;
+  const int chain = u.chain;
+  const int rblk = u.rblk;
   const int wg = NWV * rblk + w;  // this wave's rows of W: [16 wg, 16 wg + 16)
   const int bi = chain / a.H;
   const int h = chain - bi * a.H;
-  const int nb = a.Tc / BT;
+  const int nb = u.nb;
 
-  const size_t tok0 = static_cast<size_t>(chain) * a.T + static_cast<size_t>(chunk) * a.Tc;
+  const size_t tok0 = static_cast<size_t>(chain) * a.T + static_cast<size_t>(u.mb0) * BT;
   const u32x4* Qg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.Q) + tok0 * D);
   const u32x4* Kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.K) + tok0 * D);
   const u32x4* Vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.V) + tok0 * D);
   OutT* Zg = static_cast<OutT*>(a.Z) + tok0 * D;
-  const float* eg = a.eta + bi * a.esb + h * a.esh + static_cast<int64_t>(chunk) * a.Tc * a.est;
+  const float* eg = a.eta + bi * a.esb + h * a.esh + u.mb0 * BT * a.est;
 
   // staging roles (every load unconditional, so the ring stays in registers):
   //   CA 16-byte pieces of the Q|K tiles: piece x = tid + c NT of the 256
@@ -172,10 +175,7 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   //   eta of token (tid & 15).
   // The maps have no query path: there V takes Q's place in the 16-byte
   // pieces and the 8-byte V loads are dropped (4 KB per step, not 6).
-  // (The P map runs the recurrence with V = 0, scaling its V tile by zero: its
-  // "V" pieces are read from the K tile, whose lines the K pieces of the same
-  // step fetch anyway, so they cost L2 hits instead of HBM reads.)
-  const u32x4* tileA = MODE == 0 ? Qg : reinterpret_cast<const u32x4*>(map_r ? Vg : Kg);
+  const u32x4* tileA = MODE == 0 ? Qg : Vg;
   const u32x4* srcA[CA];
 #pragma unroll
   for (int c = 0; c < CA; ++c) {
@@ -226,30 +226,38 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   // which also publishes its pre-norm tile; qp holds that step's Q residual)
   [[maybe_unused]] bf16x4 qp = {};
 
-  // resident state: wt[a][r] = W[16w + li][16a + 4g + r]
+  // resident state: wt[a][r] = W[16w + li][16a + 4g + r] (the maps: P in wt, R in wr)
   float4v wt[4];
+  [[maybe_unused]] float4v wr[4];
   if constexpr (MODE == 0) {
-    const float* w0 = (a.Wstart ? a.Wstart + (static_cast<int64_t>(chain) * a.nchunk + chunk) * D * D
-                                : a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D) +
-                      static_cast<int64_t>(16 * wg + li) * D + 4 * g;
+    const float* w0 = u.w_start + static_cast<int64_t>(16 * wg + li) * D + 4 * g;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float4 x = *reinterpret_cast<const float4*>(w0 + 16 * t);
       wt[t] = float4v{x.x, x.y, x.z, x.w};
     }
   } else {
-    // P map starts from the identity, R map from zero
+    // P starts from the identity, R from zero
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        wt[t][r] = (!map_r && 16 * wg + li == 16 * t + 4 * g + r) ? 1.f : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        wt[t][r] = (16 * wg + li == 16 * t + 4 * g + r) ? 1.f : 0.f;
+        wr[t][r] = 0.f;
+      }
   }
 
   // Drain the state / eta loads before the ring prologue: otherwise the
   // compiler's wait analysis sees them pending at the loop header and makes
-  // every step wait for all outstanding loads (vmcnt(0)), which serialises the
-  // prefetch ring.  (s_waitcnt immediate: vmcnt = 0, expcnt = 7, lgkmcnt = 15.)
+  // every step wait for them, i.e. for most of the prefetch ring, which
+  // serialises it.  The empty asm statements read the loaded state registers,
+  // so the loads cannot sink below this point (a bare s_waitcnt does not stop
+  // that) and their wait is placed here, once.  (s_waitcnt immediate: vmcnt =
+  // 0, expcnt = 7, lgkmcnt = 15.)
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(wt[t]));
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   if (nb > 0) {
@@ -279,12 +287,12 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   };
   auto flush_z = [&](int m) {
     if constexpr (SAVE) {
-      const float4 e4 = *reinterpret_cast<const float4*>(&ebuf[m & 1][frow * ZROW + fl]);
+      const float4 e4 = *reinterpret_cast<const float4*>(&sh.ebuf[m & 1][frow * ZROW + fl]);
       float* ep = a.Esave + (tok0 + static_cast<size_t>(m) * BT + frow) * D + fcol;
       put(reinterpret_cast<u32x4*>(ep),
           u32x4{__float_as_uint(e4.x), __float_as_uint(e4.y), __float_as_uint(e4.z), __float_as_uint(e4.w)});
     }
-    const float4 x = *reinterpret_cast<const float4*>(&zbuf[m & 1][frow * ZROW + fl]);
+    const float4 x = *reinterpret_cast<const float4*>(&sh.zbuf[m & 1][frow * ZROW + fl]);
     OutT* zp = Zg + (static_cast<size_t>(m) * BT + frow) * D + fcol;
     if constexpr (sizeof(OutT) == 4) {
       put(reinterpret_cast<u32x4*>(zp),
@@ -300,19 +308,21 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   // this lane normalises token tk, outputs 4 li .. 4 li + 3, and writes them to
   // HBM as a 16-byte piece of the token's row (16 lanes: the whole row)
   auto ln_out = [&](int m) {
-    float dv[4];
-    const float rs = ln_centre(*reinterpret_cast<const float4*>(&lns.yq[tk * ZROW + 4 * li]), dv, a.eps);
-    float o[4];
+    if constexpr (LN) {
+      float dv[4];
+      const float rs = ln_centre(*reinterpret_cast<const float4*>(&sh.lns.yq[tk * ZROW + 4 * li]), dv, a.eps);
+      float o[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qp[r]) + ln_g[r] * (dv[r] * rs) + ln_b[r];
-    OutT* zp = Zg + (static_cast<size_t>(m) * BT + tk) * D + 4 * li;
-    if constexpr (sizeof(OutT) == 4) {
-      st_stream(reinterpret_cast<u32x4*>(zp),
-                u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])});
-    } else {
-      st_stream(reinterpret_cast<u32x2*>(zp),
-                u32x2{static_cast<uint32_t>(f32_to_bf16_bits(o[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16),
-                      static_cast<uint32_t>(f32_to_bf16_bits(o[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[3])) << 16)});
+      for (int r = 0; r < 4; ++r) o[r] = static_cast<float>(qp[r]) + ln_g[r] * (dv[r] * rs) + ln_b[r];
+      OutT* zp = Zg + (static_cast<size_t>(m) * BT + tk) * D + 4 * li;
+      if constexpr (sizeof(OutT) == 4) {
+        st_stream(reinterpret_cast<u32x4*>(zp),
+                  u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])});
+      } else {
+        st_stream(reinterpret_cast<u32x2*>(zp),
+                  u32x2{static_cast<uint32_t>(f32_to_bf16_bits(o[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[1])) << 16),
+                        static_cast<uint32_t>(f32_to_bf16_bits(o[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(o[3])) << 16)});
+      }
     }
   };
 
@@ -326,11 +336,57 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       kx[t] = *reinterpret_cast<const bf16x4*>(&S.k[li * ROW + 16 * t + 4 * g]);
-      qx[t] = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * t + 4 * g]);
+      if constexpr (MODE == 0) qx[t] = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * t + 4 * g]);
     }
     float et[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) et[r] = ETA_TOKEN ? S.eta[4 * g + r] : eta_c;
+
+    if constexpr (MODE != 0) {
+      // ---- the maps: E_X = K X^T - V_X for X = P (V_P = 0) and R (V_R = V), and
+      // X^T += K^T G_X, G_X = -2 diag(eta) E_X, on the shared K and V tiles ----
+      float4v pp = {0.f, 0.f, 0.f, 0.f}, pr = pp;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
+        float p8[8], r8[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p8[r] = wt[2 * m][r];
+          p8[4 + r] = wt[2 * m + 1][r];
+          r8[r] = wr[2 * m][r];
+          r8[4 + r] = wr[2 * m + 1][r];
+        }
+        bf16x4 h0, l0, h1, l1;
+        split4(p8, h0, l0);
+        split4(p8 + 4, h1, l1);
+        pp = mfma32(ak, cat(h0, h1), pp);
+        pp = mfma32(ak, cat(l0, l1), pp);
+        split4(r8, h0, l0);
+        split4(r8 + 4, h1, l1);
+        pr = mfma32(ak, cat(h0, h1), pr);
+        pr = mfma32(ak, cat(l0, l1), pr);
+      }
+      const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);  // V[4g + r][16wg + li]
+      float gp[4], gr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        gp[r] = -2.f * et[r] * pp[r];
+        gr[r] = -2.f * et[r] * (pr[r] - static_cast<float>(vc[r]));
+      }
+      bf16x4 ph, pl, rh, rl;
+      split4(gp, ph, pl);
+      split4(gr, rh, rl);
+      const bf16x8 gpb = cat(ph, pl), grb = cat(rh, rl);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x4 kt = read_cols<ROW>(S.k, 0, 16 * t, li, g);  // K[4g + r][16t + li]
+        wt[t] = mfma32(cat(kt, kt), gpb, wt[t]);
+        wr[t] = mfma32(cat(kt, kt), grb, wr[t]);
+      }
+      __syncthreads();
+      return;
+    }
     // (layer norm: the residual's Q row piece of token tk, read now, before the
     // step's last barrier)
     bf16x4 qr = {};
@@ -340,21 +396,6 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     float4v pk = {0.f, 0.f, 0.f, 0.f}, pq = pk, sc = pk;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      if constexpr (MODE != 0) {
-        float w8[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          w8[r] = wt[2 * m][r];
-          w8[4 + r] = wt[2 * m + 1][r];
-        }
-        bf16x4 h0, l0, h1, l1;
-        split4(w8, h0, l0);
-        split4(w8 + 4, h1, l1);
-        const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
-        pk = mfma32(ak, cat(h0, h1), pk);
-        pk = mfma32(ak, cat(l0, l1), pk);
-        continue;
-      }
       float w8[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -395,13 +436,13 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       for (int t = 0; t < 4; ++t) kc[t] = read_cols<ROW>(S.k, 0, 16 * t, li, g);
       // y = W k, f(k) = k + LN(y); dl/dy back through LN at the mini-batch-start
       // state.  The wave's transposed tile goes to the [token][output] tile ...
-      *reinterpret_cast<float4*>(&lns.yk[li * ZROW + 16 * w + 4 * g]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
+      *reinterpret_cast<float4*>(&sh.lns.yk[li * ZROW + 16 * w + 4 * g]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
       __syncthreads();
       if (n > 0) ln_out(n - 1);  // the previous step's pre-norm tile is visible too
       qp = qr;
       // ... and this lane takes token tk, outputs 4 li .. 4 li + 3
       float dv[4];
-      const float rs = ln_centre(*reinterpret_cast<const float4*>(&lns.yk[tk * ZROW + 4 * li]), dv, a.eps);
+      const float rs = ln_centre(*reinterpret_cast<const float4*>(&sh.lns.yk[tk * ZROW + 4 * li]), dv, a.eps);
       const bf16x4 kr = *reinterpret_cast<const bf16x4*>(&S.k[tk * ROW + 4 * li]);
       const bf16x4 vr = *reinterpret_cast<const bf16x4*>(&S.v[tk * ROW + 4 * li]);
       float yh[4], gr[4], s1 = 0.f, s2 = 0.f;
@@ -423,23 +464,21 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       // operand layout (lane = output 16w + l%16, slots = tokens)
       bf16x4 dh, dl;
       split4(d, dh, dl);
-      *reinterpret_cast<bf16x4*>(&lns.gh[tk * ROW + 4 * li]) = dh;
-      *reinterpret_cast<bf16x4*>(&lns.gl[tk * ROW + 4 * li]) = dl;
+      *reinterpret_cast<bf16x4*>(&sh.lns.gh[tk * ROW + 4 * li]) = dh;
+      *reinterpret_cast<bf16x4*>(&sh.lns.gl[tk * ROW + 4 * li]) = dl;
       __syncthreads();
-      bhi = read_cols<ROW>(lns.gh, 0, 16 * w, li, g);
-      blo = read_cols<ROW>(lns.gl, 0, 16 * w, li, g);
+      bhi = read_cols<ROW>(sh.lns.gh, 0, 16 * w, li, g);
+      blo = read_cols<ROW>(sh.lns.gl, 0, 16 * w, li, g);
     } else {
       float gv[4];
       float e[4];
       {
         const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);  // V[4g + r][16wg + li]
-        // (the P map runs the recurrence with V = 0)
-        const float vs = (MODE != 0 && !map_r) ? 0.f : 1.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) e[r] = pk[r] - vs * static_cast<float>(vc[r]);
+        for (int r = 0; r < 4; ++r) e[r] = pk[r] - static_cast<float>(vc[r]);
       }
       if constexpr (SAVE) {
-        float* eb = &ebuf[n & 1][(4 * g) * ZROW + 16 * w + li];
+        float* eb = &sh.ebuf[n & 1][(4 * g) * ZROW + 16 * w + li];
 #pragma unroll
         for (int r = 0; r < 4; ++r) eb[r * ZROW] = e[r];
       }
@@ -486,11 +525,11 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
       // publishes it and ln_out normalises it.  No read of the slot follows the
       // G barrier (Q and K were read before it), so the next step may restage
       // the slot at once and the step needs no closing barrier.
-      *reinterpret_cast<float4*>(&lns.yq[li * ZROW + 16 * w + 4 * g]) = make_float4(z[0], z[1], z[2], z[3]);
+      *reinterpret_cast<float4*>(&sh.lns.yq[li * ZROW + 16 * w + 4 * g]) = make_float4(z[0], z[1], z[2], z[3]);
     } else if constexpr (MODE == 0) {
       // ---- store Z rows t = 4g + r, columns 16w + li ----
       if (n > 0) flush_z(n - 1);
-      float* zb = &zbuf[n & 1][(4 * g) * ZROW + 16 * w + li];
+      float* zb = &sh.zbuf[n & 1][(4 * g) * ZROW + 16 * w + li];
 #pragma unroll
       for (int r = 0; r < 4; ++r) zb[r * ZROW] = z[r];
     }
@@ -520,17 +559,101 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
     if (nb > 0) ln_out(nb - 1);
   }
 
-  float* wf;
-  if constexpr (MODE == 0) {
-    if (chunk != a.nchunk - 1) return;  // only the last chunk holds the final state
-    wf = a.Wf + static_cast<int64_t>(chain) * D * D;
-  } else {
-    wf = a.maps + ((static_cast<int64_t>(chain) * (a.nchunk - 1) + chunk) * 2 + (map_r ? 1 : 0)) * D * D;
-  }
-  wf += static_cast<int64_t>(16 * wg + li) * D + 4 * g;
+  // end state (a chunk that is not the sequence's last keeps none) / the maps
+  const int64_t off = static_cast<int64_t>(16 * wg + li) * D + 4 * g;
+  if (u.w_end) {
+    float* wf = u.w_end + off;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    *reinterpret_cast<float4*>(wf + 16 * t) = make_float4(wt[t][0], wt[t][1], wt[t][2], wt[t][3]);
+    for (int t = 0; t < 4; ++t)
+      *reinterpret_cast<float4*>(wf + 16 * t) = make_float4(wt[t][0], wt[t][1], wt[t][2], wt[t][3]);
+  }
+  if constexpr (MODE != 0) {
+    float* wf = u.w_end2 + off;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      *reinterpret_cast<float4*>(wf + 16 * t) = make_float4(wr[t][0], wr[t][1], wr[t][2], wr[t][3]);
+  }
+}
+
+// The plain forward (one unit per chain, the whole sequence from W0) and the
+// last pass of a chunked forward (a.nchunk > 1: one unit per chain and chunk
+// 1 .. nchunk - 1, each from its start state in a.Wstart; the last chunk writes
+// W_final).
+template <int PF, bool ETA_TOKEN, typename OutT, bool LN, bool SAVE, int RB>
+__global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a) {
+  __shared__ Slot slots[2];
+  __shared__ LnShared lns;
+  __shared__ __align__(16) float zbuf[!LN ? 2 : 1][!LN ? BT * ZROW : 4];
+  __shared__ __align__(16) float ebuf[SAVE ? 2 : 1][SAVE ? BT * ZROW : 4];
+  Shm<!LN, SAVE> sh{slots, lns, zbuf, ebuf};
+  const int per_chain = a.nchunk > 1 ? a.nchunk - 1 : 1;
+  const int units = a.B * a.H * per_chain;
+  // The RB row blocks of a unit are 8 block indices apart, so the round-robin
+  // dispatch of workgroups over the 8 XCDs places them on one XCD (one L2).
+  // A last group of fewer than 8 units is packed the same way with its size.
+  int unit = blockIdx.x, rblk = 0;
+  if constexpr (RB > 1) {
+    const int full = units / 8;
+    const int grp = unit / (8 * RB);
+    const int in = unit - grp * 8 * RB;
+    const int width = grp < full ? 8 : units - full * 8;  // > 0: blockIdx.x < units * RB
+    rblk = in / width;
+    unit = grp * 8 + (in - rblk * width);
+  }
+  Unit u;
+  u.chain = unit / per_chain;
+  u.rblk = rblk;
+  u.w_end2 = nullptr;
+  const int64_t nbt = a.T / BT;
+  if (a.nchunk > 1) {
+    const int c = 1 + (unit - u.chain * per_chain);
+    u.mb0 = chunk_begin(c, nbt, a.nchunk);
+    u.nb = static_cast<int>(chunk_begin(c + 1, nbt, a.nchunk) - u.mb0);
+    u.w_start = a.Wstart + (static_cast<int64_t>(u.chain) * (a.nchunk - 1) + (c - 1)) * D * D;
+    u.w_end = c == a.nchunk - 1 ? a.Wf + static_cast<int64_t>(u.chain) * D * D : nullptr;
+  } else {
+    const int bi = u.chain / a.H, h = u.chain - bi * a.H;
+    u.mb0 = 0;
+    u.nb = static_cast<int>(nbt);
+    u.w_start = a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D;
+    u.w_end = a.Wf + static_cast<int64_t>(u.chain) * D * D;
+  }
+  linear_body<PF, ETA_TOKEN, OutT, 0, LN, SAVE, RB>(a, sh, u);
+}
+
+// The first pass of a chunked forward: per chain, nchunk - 1 units.  Unit 0
+// runs the forward of chunk 0 from W0 (Z of its tokens, and its end state =
+// the start state of chunk 1, a.Wstart[chain][0]); unit c = 1 .. nchunk - 2
+// computes the maps P_c, R_c of chunk c (a.maps[chain][c - 1]).  The last
+// chunk needs no map: the scan only has to reach its start state.
+template <int PF, bool ETA_TOKEN, typename OutT>
+__global__ __launch_bounds__(256) void ttt_linear_mfma_head_maps(LinearArgs a) {
+  __shared__ Slot slots[2];
+  __shared__ LnShared lns;  // (unused: no layer norm here)
+  __shared__ __align__(16) float zbuf[2][BT * ZROW];
+  __shared__ __align__(16) float ebuf[1][4];
+  Shm<true, false> sh{slots, lns, zbuf, ebuf};
+  const int per_chain = a.nchunk - 1;
+  Unit u;
+  u.chain = blockIdx.x / per_chain;
+  const int c = blockIdx.x - u.chain * per_chain;
+  u.rblk = 0;
+  const int64_t nbt = a.T / BT;
+  u.mb0 = chunk_begin(c, nbt, a.nchunk);
+  u.nb = static_cast<int>(chunk_begin(c + 1, nbt, a.nchunk) - u.mb0);
+  if (c == 0) {
+    const int bi = u.chain / a.H, h = u.chain - bi * a.H;
+    u.w_start = a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D;
+    u.w_end = a.Wstart + static_cast<int64_t>(u.chain) * (a.nchunk - 1) * D * D;
+    u.w_end2 = nullptr;
+    linear_body<PF, ETA_TOKEN, OutT, 0, false, false, 1>(a, sh, u);
+  } else {
+    float* m = a.maps + (static_cast<int64_t>(u.chain) * (a.nchunk - 2) + (c - 1)) * 2 * D * D;
+    u.w_start = nullptr;
+    u.w_end = m;
+    u.w_end2 = m + D * D;
+    linear_body<PF, ETA_TOKEN, OutT, 1, false, false, 1>(a, sh, u);
+  }
 }
 
 #ifndef TTT_LINEAR_PF
@@ -554,23 +677,24 @@ constexpr int64_t kShortRingUnits = 512;  // workgroups from which the plain for
 template <bool TOK, bool LN, int RB, bool LONG = LN>
 hipError_t launch_rb(const LinearArgs& a, hipStream_t s) {
   constexpr int PF = pf_for<RB, LONG>();
-  dim3 grid(a.B * a.H * a.nchunk * RB), block(256 / RB);
+  const int64_t units = static_cast<int64_t>(a.B) * a.H * (a.nchunk > 1 ? a.nchunk - 1 : 1);
+  dim3 grid(units * RB), block(256 / RB);
   if constexpr (!LN && RB == 1 && !LONG) {
-    if (static_cast<int64_t>(a.B) * a.H * a.nchunk < kShortRingUnits) return launch_rb<TOK, false, 1, true>(a, s);
+    if (units < kShortRingUnits) return launch_rb<TOK, false, 1, true>(a, s);
   }
   if constexpr (!LN) {
     if (a.Esave) {
       if (a.out_dtype == 0)
-        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, 0, false, true, RB>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, false, true, RB>), grid, block, 0, s, a);
       else
-        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, 0, false, true, RB>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, false, true, RB>), grid, block, 0, s, a);
       return hipGetLastError();
     }
   }
   if (a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, 0, LN, false, RB>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, LN, false, RB>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, 0, LN, false, RB>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, LN, false, RB>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -587,20 +711,14 @@ hipError_t launch_eta(const LinearArgs& a, hipStream_t s) {
   }
 }
 
-template <bool TOK, int RB>
-hipError_t launch_maps_rb(const LinearArgs& a, hipStream_t s) {
-  dim3 grid(2 * a.B * a.H * (a.nchunk - 1) * RB), block(256 / RB);  // P and R maps in one launch
-  hipLaunchKernelGGL((ttt_linear_mfma_d64b16<pf_for<RB, true>(), TOK, float, 1, false, false, RB>), grid, block, 0, s, a);
-  return hipGetLastError();
-}
-
 template <bool TOK>
-hipError_t launch_maps_eta(const LinearArgs& a, hipStream_t s) {
-  switch (a.rb) {
-    case 4: return launch_maps_rb<TOK, 4>(a, s);
-    case 2: return launch_maps_rb<TOK, 2>(a, s);
-    default: return launch_maps_rb<TOK, 1>(a, s);
-  }
+hipError_t launch_head_maps_eta(const LinearArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.H * (a.nchunk - 1)), block(256);
+  if (a.out_dtype == 0)
+    hipLaunchKernelGGL((ttt_linear_mfma_head_maps<pf_for<1, true>(), TOK, float>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((ttt_linear_mfma_head_maps<pf_for<1, true>(), TOK, uint16_t>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -617,8 +735,8 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
   return a.est != 0 ? launch_eta<true, false>(a, s) : launch_eta<false, false>(a, s);
 }
 
-hipError_t launch_linear_mfma_maps(const LinearArgs& a, hipStream_t s) {
-  return a.est != 0 ? launch_maps_eta<true>(a, s) : launch_maps_eta<false>(a, s);
+hipError_t launch_linear_mfma_head_maps(const LinearArgs& a, hipStream_t s) {
+  return a.est != 0 ? launch_head_maps_eta<true>(a, s) : launch_head_maps_eta<false>(a, s);
 }
 
 }  // namespace ttt

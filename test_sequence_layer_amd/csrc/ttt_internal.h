@@ -19,11 +19,12 @@ struct LinearArgs {
   int64_t esb, esh, est;  // eta strides (elements)
   void* Z;
   float* Wf;
-  // Chunked execution: the sequence is split into nchunk chunks of Tc tokens
-  // (nchunk = 1, Tc = T, Wstart = maps = nullptr for a plain forward).
-  int nchunk, Tc;
-  float* Wstart;        // [chains][nchunk][d][d] start state of every chunk
-  float* maps;          // [chains][nchunk-1][2][d][d] chunk maps (P, R)
+  // Chunked execution: the sequence's T / 16 mini-batches are split into
+  // nchunk chunks, chunk c starting at mini-batch c * (T / 16) / nchunk
+  // (nchunk = 1, Wstart = maps = nullptr for a plain forward).
+  int nchunk;
+  float* Wstart;        // [chains][nchunk-1][d][d] start states of chunks 1 .. nchunk-1
+  float* maps;          // [chains][nchunk-2][2][d][d] maps (P, R) of chunks 1 .. nchunk-2
   // Layer norm and residual inside f (f(x) = x + LN(W x)); gamma == nullptr: plain f(x) = W x.
   const float* gamma;   // [H][d]
   const float* beta;    // [H][d]
@@ -110,11 +111,13 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(const LinearArgs& a);
 const char* linear_mfma_name(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
-// The chunk maps of a chunked forward: for every chain and every chunk but the
-// last, P = the product of the chunk's (I - 2 K diag(eta) K^T) and R = the
-// state the chunk reaches from zero, so that W_end = W_start P + R.
-hipError_t launch_linear_mfma_maps(const LinearArgs& a, hipStream_t s);
-// Chunk start states: Wstart[c+1] = Wstart[c] P_c + R_c, Wstart[0] = W0.
+// First pass of a chunked forward: for every chain, the forward of chunk 0
+// from W0 (its Z, and its end state = the start state of chunk 1), and the
+// maps of chunks 1 .. nchunk-2: P = the product of the chunk's
+// (I - 2 K diag(eta) K^T) and R = the state the chunk reaches from zero, so
+// that W_end = W_start P + R.
+hipError_t launch_linear_mfma_head_maps(const LinearArgs& a, hipStream_t s);
+// Chunk start states: Wstart of chunk c+1 = (that of chunk c) P_c + R_c, c = 1 .. nchunk-2.
 hipError_t launch_linear_chunk_scan(const LinearArgs& a, hipStream_t s);
 
 // TTT-MLP kernel: d = 64, dh = 256, b = 16, bf16 Q/K/V.

@@ -39,6 +39,7 @@ COPY_BYTES = 1 << 30
 # source files that define each kernel (a change to any of them invalidates its counters)
 KERNEL_SOURCES = {
     "ttt_linear_mfma_d64b16": ["linear_mfma.hip", "mfma_common.h", "ttt_internal.h"],
+    "ttt_linear_mfma_head_maps": ["linear_mfma.hip", "mfma_common.h", "ttt_internal.h"],
     "ttt_linear_generic_kernel": ["linear_generic.hip", "ttt_internal.h"],
     "ttt_linear_bwd_d64b16": ["linear_bwd_mfma.hip", "mfma_common.h", "ttt_internal.h"],
     "ttt_linear_bwd_generic_kernel": ["linear_bwd_generic.hip", "ttt_internal.h"],

@@ -222,7 +222,9 @@ def test_primal_flag():
 def test_chunked_workspace_bytes():
     d = _desc(B=2, H=32, T=32768)
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 1) == 0
-    assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 8) == 64 * (7 * 2 + 8) * 64 * 64 * 4
+    # maps (P, R) of chunks 1 .. 6 and start states of chunks 1 .. 7
+    assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 8) == 64 * (6 * 2 + 7) * 64 * 64 * 4
+    assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 2) == 64 * 1 * 64 * 64 * 4
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(d), 0) == -1
     assert ttt.lib().ttt_linear_chunked_workspace_bytes(None, 4) == -1
 
@@ -241,12 +243,12 @@ def test_chunked_noalloc_host_errors():
         return f(ctypes.byref(desc), nchunks, *b.args(), None)
 
     assert call(_desc(B=2, H=32, T=32768), 0) == SHAPE
-    assert call(_desc(B=2, H=32, T=32768), 3) == SHAPE          # T % (16 * nchunks) != 0
+    assert call(_desc(B=2, H=32, T=64), 5) == SHAPE             # more chunks than mini-batches
     assert call(_desc(B=2, H=32, T=32768, ind=0), 4) == UNSUP   # fp32 inputs: no matrix-core path
     assert call(_desc(B=2, H=32, T=32768, flags=1), 4) == UNSUP
     assert call(_desc(B=2, H=32, T=32768), 4, q=None) == NULL
     assert call(_desc(B=2, H=32, T=32768), 4, z=3 * GB) == ALIAS
-    big = _desc(B=16, H=32, T=8192)                              # 512 chains x 4 chunks: 80 MiB of maps
+    big = _desc(B=16, H=32, T=8192)                              # 512 chains x 4 chunks: 56 MiB of maps
     need = ttt.lib().ttt_linear_chunked_workspace_bytes(ctypes.byref(big), 4)
     assert need > ttt.NOALLOC_SCRATCH_BYTES
     assert call(big, 4) == SCRATCH

@@ -24,7 +24,9 @@ def ttt():
     return m
 
 
-@pytest.mark.parametrize("nchunks", [2, 4, 8, 16])
+# 16 mini-batches: equal chunks (2, 4, 8, 16) and unequal ones (3, 5, 7: chunk c
+# starts at mini-batch c * 16 // n)
+@pytest.mark.parametrize("nchunks", [2, 3, 4, 5, 7, 8, 16])
 @pytest.mark.parametrize("eta_kind", ["scalar", "head", "token"])
 def test_chunked_small(ttt, nchunks, eta_kind):
     cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=3, T=256, eta_kind=eta_kind, eta_value=1.0 / 64, seed=40 + nchunks)
@@ -41,15 +43,19 @@ def test_chunked_small(ttt, nchunks, eta_kind):
 
 
 def test_chunked_long_config(ttt):
+    """The long workload (64 chains x 2,048 mini-batches) with 5 chunks (409 or
+    410 mini-batches each, the benchmark's split) and 8, against the oracle on
+    sampled chains."""
     cfg = ti.CONFIGS["long"]
     inp = ti.generate(cfg)
     t = to_device(inp)
-    z, wf = ttt.linear_fwd_chunked(t["q"], t["k"], t["v"], t["w1"], t["eta"], 16, 8)
-    torch.cuda.synchronize()
     ch = ti.sample_chains(cfg, 6)
     zr, wr = oracle.run_inputs(ti.generate(cfg, chains=ch))
-    parity("chunked long (8 chunks)", [("Z", rows(z, ch), zr), ("W_final", rows(wf, ch), wr)], CONTRACT_BF16,
-           REGRESS_MFMA)
+    for n in (5, 8):
+        z, wf = ttt.linear_fwd_chunked(t["q"], t["k"], t["v"], t["w1"], t["eta"], 16, n)
+        torch.cuda.synchronize()
+        parity(f"chunked long ({n} chunks)", [("Z", rows(z, ch), zr), ("W_final", rows(wf, ch), wr)],
+               CONTRACT_BF16, REGRESS_MFMA)
 
 
 def test_chunked_inplace_state_and_workspace_reuse(ttt):
@@ -68,7 +74,7 @@ def test_chunked_inplace_state_and_workspace_reuse(ttt):
 def test_chunked_errors(ttt):
     x = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device="cuda:0")
     w0 = torch.zeros((2, 64, 64), device="cuda:0")
-    with pytest.raises(ttt.TTTError) as ei:                      # 64 % (16 * 8) != 0
+    with pytest.raises(ttt.TTTError) as ei:                      # 8 chunks, 4 mini-batches
         ttt.linear_fwd_chunked(x, x, x, w0, 0.1, 16, 8)
     assert ei.value.status == 2
     small = torch.empty(16, dtype=torch.uint8, device="cuda:0")
