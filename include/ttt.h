@@ -120,8 +120,9 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
  * few (sequence, head) chains and long sequences.  Each mini-batch maps the
  * state affinely (W -> W P_n + R_n, P_n = I - 2 K diag(eta) K^T,
  * R_n = 2 V diag(eta) K^T; [TTT] 03 §7), so a chunk maps it as W -> W P + R.
- * With nb = T / 16 mini-batches, chunk c holds mini-batches
- * [c nb / nchunks, (c + 1) nb / nchunks) (integer division).  The library
+ * With nb = T / 16 mini-batches, chunk 0 holds about 1.1 / (nchunks - 1 + 1.1)
+ * of them (half for nchunks = 2) and the other chunks share the rest evenly.
+ * The library
  * (1) runs chunk 0 from W0 and, in the same launch, composes the maps of
  * chunks 1 .. nchunks-2 (the last chunk needs none), (2) scans them to get the
  * start state of every later chunk, (3) runs chunks 1 .. nchunks-1 in

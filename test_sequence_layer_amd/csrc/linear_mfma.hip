@@ -125,8 +125,11 @@ struct Unit {
   float* w_end2;         // MODE 1: R
 };
 
-// First mini-batch of chunk c when nb mini-batches are split into n chunks.
-__device__ __forceinline__ int64_t chunk_begin(int64_t c, int64_t nb, int64_t n) { return c * nb / n; }
+// First mini-batch of chunk c when nb mini-batches are split into n chunks,
+// chunk 0 holding mb1 of them and the rest shared evenly (c = n: nb).
+__device__ __forceinline__ int64_t chunk_begin(int64_t c, int64_t nb, int64_t n, int64_t mb1) {
+  return c == 0 ? 0 : mb1 + (c - 1) * (nb - mb1) / (n - 1);
+}
 
 // MODE 0: forward (Z and the end state).  MODE 1: the two maps of one chunk of
 // a chunked forward, W_end = W_start P + R: P is the state recurrence run from I
@@ -607,8 +610,8 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   const int64_t nbt = a.T / BT;
   if (a.nchunk > 1) {
     const int c = 1 + (unit - u.chain * per_chain);
-    u.mb0 = chunk_begin(c, nbt, a.nchunk);
-    u.nb = static_cast<int>(chunk_begin(c + 1, nbt, a.nchunk) - u.mb0);
+    u.mb0 = chunk_begin(c, nbt, a.nchunk, a.mb1);
+    u.nb = static_cast<int>(chunk_begin(c + 1, nbt, a.nchunk, a.mb1) - u.mb0);
     u.w_start = a.Wstart + (static_cast<int64_t>(u.chain) * (a.nchunk - 1) + (c - 1)) * D * D;
     u.w_end = c == a.nchunk - 1 ? a.Wf + static_cast<int64_t>(u.chain) * D * D : nullptr;
   } else {
@@ -639,8 +642,8 @@ __global__ __launch_bounds__(256) void ttt_linear_mfma_head_maps(LinearArgs a) {
   const int c = blockIdx.x - u.chain * per_chain;
   u.rblk = 0;
   const int64_t nbt = a.T / BT;
-  u.mb0 = chunk_begin(c, nbt, a.nchunk);
-  u.nb = static_cast<int>(chunk_begin(c + 1, nbt, a.nchunk) - u.mb0);
+  u.mb0 = chunk_begin(c, nbt, a.nchunk, a.mb1);
+  u.nb = static_cast<int>(chunk_begin(c + 1, nbt, a.nchunk, a.mb1) - u.mb0);
   if (c == 0) {
     const int bi = u.chain / a.H, h = u.chain - bi * a.H;
     u.w_start = a.W0 + bi * a.w0_bstride + static_cast<int64_t>(h) * D * D;

@@ -19,10 +19,12 @@ struct LinearArgs {
   int64_t esb, esh, est;  // eta strides (elements)
   void* Z;
   float* Wf;
-  // Chunked execution: the sequence's T / 16 mini-batches are split into
-  // nchunk chunks, chunk c starting at mini-batch c * (T / 16) / nchunk
+  // Chunked execution: the sequence's nb = T / 16 mini-batches are split into
+  // nchunk chunks: chunk 0 holds mb1 of them, and chunk c >= 1 starts at
+  // mini-batch mb1 + (c - 1) (nb - mb1) / (nchunk - 1)
   // (nchunk = 1, Wstart = maps = nullptr for a plain forward).
   int nchunk;
+  int64_t mb1;
   float* Wstart;        // [chains][nchunk-1][d][d] start states of chunks 1 .. nchunk-1
   float* maps;          // [chains][nchunk-2][2][d][d] maps (P, R) of chunks 1 .. nchunk-2
   // Layer norm and residual inside f (f(x) = x + LN(W x)); gamma == nullptr: plain f(x) = W x.
