@@ -83,6 +83,9 @@ def _load():
     lib.oracle_mlp_ln_primal.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, dp,
                                          dp, i]
     lib.oracle_linear_primal_grads.restype = None
+    lib.oracle_linear_ln_primal_grads.argtypes = ([i, i, i, i] + [dp] * 6 + [ctypes.c_double] + [dp] * 3 + [dp] * 7
+                                                  + [i])
+    lib.oracle_linear_ln_primal_grads.restype = None
     lib.oracle_max_threads.restype = i
     _lib = lib
     return lib
@@ -142,6 +145,35 @@ def linear_primal_grads(q, k, v, w0, eta, b: int, dz, dwf=None, threads: int = 0
                                            _ptr(dz), dwf_p, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0),
                                            int(threads))
     return dq, dk, dv, deta, dw0
+
+
+def linear_ln_primal_grads(q, k, v, w0, gamma, beta, eta, b: int, dz, dwf=None, eps: float = 1e-6,
+                           threads: int = 0):
+    """Gradients of  sum(dz * Z) + sum(dwf * W_final)  of TTT-Linear with LN +
+    residual inside f (linear_ln_primal), by reverse-mode differentiation of the
+    primal token loop, fp64, in C.  gamma, beta : [n, d] per chain.
+
+    returns (dq, dk, dv, deta [n, T], dw0 [n, d, d], dgamma [n, d], dbeta [n, d]).
+    """
+    q, k, v, w0, gamma, beta, eta, dz = map(_f64, (q, k, v, w0, gamma, beta, eta, dz))
+    n, T, d = q.shape
+    assert k.shape == v.shape == dz.shape == (n, T, d) and w0.shape == (n, d, d) and eta.shape == (n, T)
+    assert gamma.shape == beta.shape == (n, d) and b >= 1
+    dwf_p = None
+    if dwf is not None:
+        dwf = _f64(dwf)
+        assert dwf.shape == (n, d, d)
+        dwf_p = _ptr(dwf)
+    dq, dk, dv = (np.empty((n, T, d)) for _ in range(3))
+    deta = np.empty((n, T))
+    dw0 = np.empty((n, d, d))
+    dgamma, dbeta = np.empty((n, d)), np.empty((n, d))
+    if n:
+        _load().oracle_linear_ln_primal_grads(n, T, d, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
+                                              _ptr(beta), float(eps), _ptr(eta), _ptr(dz), dwf_p, _ptr(dq),
+                                              _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0), _ptr(dgamma), _ptr(dbeta),
+                                              int(threads))
+    return dq, dk, dv, deta, dw0, dgamma, dbeta
 
 
 def mlp_primal(q, k, v, w1, w2, eta, b: int, threads: int = 0):
@@ -389,6 +421,62 @@ def linear_grads(q, k, v, w0, eta, b, dz, dwf=None):
         loss = loss + (wf * torch.tensor(np.asarray(dwf, np.float64))).sum()
     loss.backward()
     return tuple(x.grad.numpy() for x in (q_, k_, v_, e_, w_))
+
+
+def linear_ln_primal_torch(q, k, v, w0, gamma, beta, eta, b, eps=1e-6):
+    """The primal TTT-Linear loop with LN + residual inside f, f(x) = x + LN(W x)
+    (03 §9), on torch CPU tensors, any dtype; differentiable.
+
+    Token t of a mini-batch: y = Wb k_t (Wb: the state before the mini-batch),
+    loss |k_t + LN(y) - v_t|^2, whose gradient with respect to W is delta k_t^T
+    with delta the loss gradient pulled back through LN to y (autograd is not
+    used for it: it is written out, as the forward computes it);
+    W_t = W_{t-1} - eta_t delta k_t^T;  z_t = q_t + LN(W_t q_t).
+    LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps) + beta over the d entries.
+    Shapes: q, k, v [n, T, d]; w0 [n, d, d]; gamma, beta [n, d]; eta [n, T].
+    """
+    import torch
+
+    def ln_stats(y):
+        mu = y.mean(dim=1, keepdim=True)
+        dv = y - mu
+        s = torch.sqrt((dv * dv).mean(dim=1, keepdim=True) + eps)
+        return dv / s, s
+
+    n, T, d = q.shape
+    W = w0.clone()
+    zs = []
+    for t0 in range(0, T, b):
+        Wb = W
+        for t in range(t0, min(t0 + b, T)):
+            yh, s = ln_stats(torch.einsum("nij,nj->ni", Wb, k[:, t]))
+            g = 2.0 * (k[:, t] + gamma * yh + beta - v[:, t]) * gamma
+            delta = (g - g.mean(dim=1, keepdim=True) - yh * (g * yh).mean(dim=1, keepdim=True)) / s
+            W = W - eta[:, t][:, None, None] * delta[:, :, None] * k[:, t][:, None, :]
+            uh, _ = ln_stats(torch.einsum("nij,nj->ni", W, q[:, t]))
+            zs.append(q[:, t] + gamma * uh + beta)
+    return torch.stack(zs, dim=1), W
+
+
+def linear_ln_grads(q, k, v, w0, gamma, beta, eta, b, dz, dwf=None, eps=1e-6):
+    """Gradients of  sum(dz * Z) + sum(dwf * W_final)  of TTT-Linear with LN +
+    residual inside f, fp64 autograd through linear_ln_primal_torch.
+    w0 : [n, d, d], gamma, beta : [n, d], eta : [n, T] (all per chain).
+
+    returns (dq, dk, dv, deta [n, T], dw0 [n, d, d], dgamma [n, d], dbeta [n, d]).
+    """
+    import torch
+
+    def t(x):
+        return torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True)
+
+    q_, k_, v_, w_, g_, b_, e_ = t(q), t(k), t(v), t(w0), t(gamma), t(beta), t(eta)
+    z, wf = linear_ln_primal_torch(q_, k_, v_, w_, g_, b_, e_, b, eps)
+    loss = (z * torch.tensor(np.asarray(dz, np.float64))).sum()
+    if dwf is not None:
+        loss = loss + (wf * torch.tensor(np.asarray(dwf, np.float64))).sum()
+    loss.backward()
+    return tuple(x.grad.numpy() for x in (q_, k_, v_, e_, w_, g_, b_))
 
 
 def gelu(x):

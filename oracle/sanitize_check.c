@@ -23,6 +23,11 @@ void oracle_linear_ln_primal(int n, int T, int d, int b, const double* q, const 
 void oracle_linear_primal_grads(int n, int T, int d, int b, const double* q, const double* k, const double* v,
                                 const double* w0, const double* eta, const double* dz, const double* dwf,
                                 double* dq, double* dk, double* dv, double* deta, double* dw0, int nthreads);
+void oracle_linear_ln_primal_grads(int n, int T, int d, int b, const double* q, const double* k, const double* v,
+                                   const double* w0, const double* gamma, const double* beta, double eps,
+                                   const double* eta, const double* dz, const double* dwf, double* dq, double* dk,
+                                   double* dv, double* deta, double* dw0, double* dgamma, double* dbeta,
+                                   int nthreads);
 
 static uint64_t state = 0x9E3779B97F4A7C15ull;
 
@@ -76,6 +81,16 @@ int main(void) {
            !finite_all(dw0, dd);
     oracle_linear_primal_grads(n, T, d, b, q, k, v, w0, eta, dz, NULL, dq, dk, dv, deta, dw0, 2);
     bad |= !finite_all(dw0, dd);
+
+    double *dgamma = buf((size_t)n * d, 0), *dbeta = buf((size_t)n * d, 0);
+    oracle_linear_ln_primal_grads(n, T, d, b, q, k, v, w0, gamma, beta, 1e-5, eta, dz, dwf, dq, dk, dv, deta, dw0,
+                                  dgamma, dbeta, 2);
+    bad |= !finite_all(dq, tok) || !finite_all(dk, tok) || !finite_all(dv, tok) || !finite_all(deta, nt) ||
+           !finite_all(dw0, dd) || !finite_all(dgamma, (size_t)n * d) || !finite_all(dbeta, (size_t)n * d);
+    oracle_linear_ln_primal_grads(n, T, d, b, q, k, v, w0, gamma, beta, 1e-5, eta, dz, NULL, dq, dk, dv, deta, dw0,
+                                  dgamma, dbeta, 2);
+    bad |= !finite_all(dw0, dd) || !finite_all(dgamma, (size_t)n * d);
+    free(dgamma); free(dbeta);
 
     free(q); free(k); free(v); free(w0); free(eta); free(z); free(wf); free(gamma); free(beta);
     free(w1); free(w2); free(w1f); free(w2f);

@@ -393,3 +393,199 @@ void oracle_linear_primal_grads(int n, int T, int d, int b,
     free(Wst); free(W); free(Wt); free(E); free(A); free(dWb); free(ak); free(de); free(tmp);
   }
 }
+
+/* Gradients of TTT-Linear with LN and residual inside f (oracle_linear_ln_primal)
+ * by reverse-mode differentiation of its primal token loop (fp64), for
+ * L = sum(dz * Z) + sum(dwf * W_final):
+ *   dq, dk, dv : [n, T, d]   deta : [n, T]   dw0 : [n, d, d]
+ *   dgamma, dbeta : [n, d]   (per chain; dwf may be NULL).
+ * Token t of the loop (Wb: the state before t's mini-batch):
+ *   y = Wb k,  yhat = (y - mean y) / s,  r = k + gamma yhat + beta - v,
+ *   g = 2 r gamma,  c = mean(g yhat),  delta = (g - mean g - yhat c) / s,
+ *   W_t = W_{t-1} - eta_t delta k^T,  u = W_t q,  z = q + gamma uhat + beta.
+ * Walking back with A = dL/dW_t (the LN backward of a vector x with adjoint
+ * h is  (h - mean h - xhat mean(h xhat)) / s_x):
+ *   dq = dz;  dgamma += dz uhat;  dbeta += dz;  du = LNback(u, gamma dz)
+ *   A += du q^T;  dq += W_t^T du
+ *   a = -eta_t A k;  dk = -eta_t A^T delta;  deta_t = delta . (A k) * -1
+ *   dg = LNback-projection of a (P a / s, P = I - 11^T/d - yhat yhat^T/d);
+ *   dy = -(a . delta) yhat / (s d) - c (P a) / s^2 - (a . yhat) delta / (s d)
+ *        (the derivative of delta in y at fixed g)
+ *   dr = 2 gamma dg;  dgamma += 2 r dg + dr yhat;  dbeta += dr;  dk += dr;
+ *   dv = -dr;  dy += LNback(y, gamma dr)
+ *   dWb += dy k^T;  dk += Wb^T dy
+ * and at the mini-batch start A += dWb. */
+static void ln_back(const double* h, const double* xh, double s, double* out, int d) {
+  double m = 0.0, mh = 0.0;
+  for (int i = 0; i < d; ++i) {
+    m += h[i];
+    mh += h[i] * xh[i];
+  }
+  m /= d;
+  mh /= d;
+  for (int i = 0; i < d; ++i) out[i] = (h[i] - m - xh[i] * mh) / s;
+}
+
+void oracle_linear_ln_primal_grads(int n, int T, int d, int b,
+                                   const double* q, const double* k, const double* v,
+                                   const double* w0, const double* gamma, const double* beta, double eps,
+                                   const double* eta, const double* dz, const double* dwf,
+                                   double* dq, double* dk, double* dv, double* deta, double* dw0,
+                                   double* dgamma, double* dbeta, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int c = 0; c < n; ++c) {
+    const size_t dd = (size_t)d * d;
+    const int nb = (T + b - 1) / b;
+    const double* gm = gamma + (size_t)c * d;
+    const double* bt = beta + (size_t)c * d;
+    double* dgm = dgamma + (size_t)c * d;
+    double* dbt = dbeta + (size_t)c * d;
+    double* Wst = (double*)malloc((size_t)(nb > 0 ? nb : 1) * dd * sizeof(double));
+    double* W = (double*)malloc(dd * sizeof(double));
+    double* Wt = (double*)malloc((size_t)b * dd * sizeof(double));
+    /* per token of the mini-batch: yhat, s_y, r, delta, c, uhat, s_u */
+    double* YH = (double*)malloc((size_t)b * d * sizeof(double));
+    double* R = (double*)malloc((size_t)b * d * sizeof(double));
+    double* DL = (double*)malloc((size_t)b * d * sizeof(double));
+    double* UH = (double*)malloc((size_t)b * d * sizeof(double));
+    double* sy = (double*)malloc((size_t)b * sizeof(double));
+    double* su = (double*)malloc((size_t)b * sizeof(double));
+    double* cc = (double*)malloc((size_t)b * sizeof(double));
+    double* A = (double*)malloc(dd * sizeof(double));
+    double* dWb = (double*)malloc(dd * sizeof(double));
+    double* y = (double*)malloc((size_t)d * sizeof(double));
+    double* h = (double*)malloc((size_t)d * sizeof(double));
+    double* du = (double*)malloc((size_t)d * sizeof(double));
+    double* ak = (double*)malloc((size_t)d * sizeof(double));
+    double* a = (double*)malloc((size_t)d * sizeof(double));
+    double* pa = (double*)malloc((size_t)d * sizeof(double));
+    double* dy = (double*)malloc((size_t)d * sizeof(double));
+    double* dr = (double*)malloc((size_t)d * sizeof(double));
+    double* tmp = (double*)malloc((size_t)d * sizeof(double));
+    const double* et = eta + (size_t)c * T;
+    for (int i = 0; i < d; ++i) dgm[i] = dbt[i] = 0.0;
+
+    /* forward: the state at every mini-batch start */
+    memcpy(W, w0 + c * dd, dd * sizeof(double));
+    for (int mb = 0; mb < nb; ++mb) {
+      double* Wb = Wst + (size_t)mb * dd;
+      memcpy(Wb, W, dd * sizeof(double));
+      const int t0 = mb * b, t1 = t0 + b < T ? t0 + b : T;
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        matvec(Wb, k + o, y, d, d);
+        double* yh = YH;  /* scratch */
+        const double s = ln_normalize(y, yh, d, eps);
+        double mg = 0.0, mgy = 0.0;
+        for (int i = 0; i < d; ++i) {
+          h[i] = 2.0 * (k[o + i] + gm[i] * yh[i] + bt[i] - v[o + i]) * gm[i];
+          mg += h[i];
+          mgy += h[i] * yh[i];
+        }
+        mg /= d;
+        mgy /= d;
+        for (int i = 0; i < d; ++i) h[i] = (h[i] - mg - yh[i] * mgy) / s;
+        rank1_sub(W, et[t], h, k + o, d, d);
+      }
+    }
+
+    /* backward */
+    if (dwf) memcpy(A, dwf + c * dd, dd * sizeof(double));
+    else memset(A, 0, dd * sizeof(double));
+    for (int mb = nb - 1; mb >= 0; --mb) {
+      const double* Wb = Wst + (size_t)mb * dd;
+      const int t0 = mb * b, t1 = t0 + b < T ? t0 + b : T;
+      /* recompute the mini-batch */
+      memcpy(W, Wb, dd * sizeof(double));
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        const int j = t - t0;
+        double* yh = YH + (size_t)j * d;
+        double* r = R + (size_t)j * d;
+        double* dl = DL + (size_t)j * d;
+        matvec(Wb, k + o, y, d, d);
+        sy[j] = ln_normalize(y, yh, d, eps);
+        double mg = 0.0, mgy = 0.0;
+        for (int i = 0; i < d; ++i) {
+          r[i] = k[o + i] + gm[i] * yh[i] + bt[i] - v[o + i];
+          h[i] = 2.0 * r[i] * gm[i];
+          mg += h[i];
+          mgy += h[i] * yh[i];
+        }
+        mg /= d;
+        mgy /= d;
+        cc[j] = mgy;
+        for (int i = 0; i < d; ++i) dl[i] = (h[i] - mg - yh[i] * mgy) / sy[j];
+        rank1_sub(W, et[t], dl, k + o, d, d);
+        memcpy(Wt + (size_t)j * dd, W, dd * sizeof(double));
+        matvec(W, q + o, y, d, d);
+        su[j] = ln_normalize(y, UH + (size_t)j * d, d, eps);
+      }
+      memset(dWb, 0, dd * sizeof(double));
+      for (int t = t1 - 1; t >= t0; --t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        const int j = t - t0;
+        const double* yh = YH + (size_t)j * d;
+        const double* r = R + (size_t)j * d;
+        const double* dl = DL + (size_t)j * d;
+        const double* uh = UH + (size_t)j * d;
+        const double s = sy[j];
+        /* output: z = q + gamma uhat + beta */
+        for (int i = 0; i < d; ++i) {
+          dgm[i] += dz[o + i] * uh[i];
+          dbt[i] += dz[o + i];
+          h[i] = gm[i] * dz[o + i];
+        }
+        ln_back(h, uh, su[j], du, d);
+        const double* Wc = Wt + (size_t)j * dd;
+        matvec_t(Wc, du, tmp, d, d);                      /* W_t^T du          */
+        for (int i = 0; i < d; ++i) dq[o + i] = dz[o + i] + tmp[i];
+        rank1_sub(A, -1.0, du, q + o, d, d);              /* A += du q^T       */
+        /* W_t = W_{t-1} - eta delta k^T */
+        matvec(A, k + o, ak, d, d);
+        double sd = 0.0;
+        for (int i = 0; i < d; ++i) {
+          a[i] = -et[t] * ak[i];
+          sd += dl[i] * ak[i];
+        }
+        deta[(size_t)c * T + t] = -sd;
+        matvec_t(A, dl, tmp, d, d);                       /* A^T delta         */
+        for (int i = 0; i < d; ++i) dk[o + i] = -et[t] * tmp[i];
+        /* delta = P g / s: dg = P a / s, and its derivative in y at fixed g */
+        double ma = 0.0, ay = 0.0, ad = 0.0;
+        for (int i = 0; i < d; ++i) {
+          ma += a[i];
+          ay += a[i] * yh[i];
+          ad += a[i] * dl[i];
+        }
+        ma /= d;
+        for (int i = 0; i < d; ++i) pa[i] = a[i] - ma - yh[i] * ay / d;
+        for (int i = 0; i < d; ++i)
+          dy[i] = -ad * yh[i] / (s * d) - cc[j] * pa[i] / (s * s) - ay * dl[i] / (s * d);
+        /* g = 2 r gamma, r = k + gamma yhat + beta - v */
+        for (int i = 0; i < d; ++i) {
+          const double dg = pa[i] / s;
+          dr[i] = 2.0 * gm[i] * dg;
+          dgm[i] += 2.0 * r[i] * dg + dr[i] * yh[i];
+          dbt[i] += dr[i];
+          dk[o + i] += dr[i];
+          dv[o + i] = -dr[i];
+          h[i] = gm[i] * dr[i];
+        }
+        ln_back(h, yh, s, tmp, d);
+        for (int i = 0; i < d; ++i) dy[i] += tmp[i];
+        /* y = Wb k */
+        rank1_sub(dWb, -1.0, dy, k + o, d, d);            /* dWb += dy k^T     */
+        matvec_t(Wb, dy, tmp, d, d);
+        for (int i = 0; i < d; ++i) dk[o + i] += tmp[i];
+      }
+      for (size_t x = 0; x < dd; ++x) A[x] += dWb[x];
+    }
+    memcpy(dw0 + c * dd, A, dd * sizeof(double));
+    free(Wst); free(W); free(Wt); free(YH); free(R); free(DL); free(UH); free(sy); free(su); free(cc);
+    free(A); free(dWb); free(y); free(h); free(du); free(ak); free(a); free(pa); free(dy); free(dr); free(tmp);
+  }
+}
