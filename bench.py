@@ -85,6 +85,30 @@ def algorithmic_bwd(cfg: ti.Config, eta_strides, grad_size: int = 4):
     return bytes_, flops
 
 
+def algorithmic_ln_bwd(cfg: ti.Config, eta_strides, grad_size: int = 4):
+    """Algorithmic bytes and flops of one layer-norm backward (ttt_linear_ln_bwd).
+
+    Bytes: read Q, K, V (input dtype), the saved update factors G (fp32), dZ (grad_size),
+    eta, gamma and beta; write dQ, dK, dV (grad_size), deta (fp32 per token);
+    read W_final and dW_final, write dW0 (fp32 d x d per chain) and dgamma,
+    dbeta (fp32 d per chain).
+    Flops per token-head: 18 d^2 for the nine d x d x b products of a
+    mini-batch (the rebuild, W K, W Q, A K, W^T dU, W^T dY, A^T G and the
+    two terms of the adjoint update) plus 12 d b for the six b x b x d ones
+    (K^T Q, G S, G^T dU, dU S^T, K dS, Q dS^T); the layer norms'
+    elementwise work is not counted.
+    """
+    th = cfg.B * cfg.H * cfg.T
+    in_sz = 2 if cfg.dtype == "bf16" else 4
+    d, b = cfg.d, cfg.b
+    chains = cfg.B * cfg.H
+    eta_b = 4 * th if eta_strides[2] != 0 else 4 * (cfg.H if eta_strides[1] else 1)
+    bytes_ = (th * d * (3 * in_sz + 4 + grad_size + 3 * grad_size) + eta_b + 4 * th + 3 * chains * d * d * 4
+              + 2 * chains * d * 4 + 2 * cfg.H * d * 4)
+    flops = th * (18 * d * d + 12 * d * b)
+    return bytes_, flops
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when the summary is missing or was taken on a different kernel source."""
@@ -174,7 +198,7 @@ def cpu_baseline(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = False)
                            "sample": f"{len(chains1)} chains at full T={cfg.T}, {dt1:.2f} s wall on 1 thread"}}
 
 
-def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int):
+def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = False):
     import oracle
 
     chains = ti.sample_chains(cfg, sample_chains)
@@ -183,7 +207,13 @@ def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int):
     dz, dwf = ti.upstream_grads(cfg, chains=chains)
     threads = _host_threads(oracle)
     t0 = time.perf_counter()
-    oracle.linear_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(), sub.eta_rows(), cfg.b, dz, dwf, threads=threads)
+    if ln:  # the benchmark's gamma = 1, beta = 0
+        n = len(chains)
+        oracle.linear_ln_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(), np.ones((n, cfg.d)), np.zeros((n, cfg.d)),
+                                      sub.eta_rows(), cfg.b, dz, dwf, threads=threads)
+    else:
+        oracle.linear_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(), sub.eta_rows(), cfg.b, dz, dwf,
+                                   threads=threads)
     dt = time.perf_counter() - t0
     tokens = len(chains) * cfg.T / cfg.H
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -370,7 +400,40 @@ def main():
         kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
                                        inp.eta_strides, args.generic, args.primal)
 
-        if args.save or args.bwd or args.train:
+        if args.ln and (args.save or args.bwd or args.train):
+            gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
+            bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
+            dl_sv = torch.empty((B, H, T, d), dtype=torch.float32, device="cuda:0")
+
+            def fwd_save():
+                ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], gam, bet, t["eta"], cfg.b, z=z, w_final=wf,
+                                  g_saved=dl_sv)
+
+            fwd_save()
+            gen = torch.Generator(device="cuda:0")
+            gen.manual_seed(cfg.seed)
+            dz = torch.randn((B, H, T, d), generator=gen, device="cuda:0")
+            dwf = torch.randn((B, H, d, d), generator=gen, device="cuda:0")
+            gout = (torch.empty_like(dz), torch.empty_like(dz), torch.empty_like(dz),
+                    torch.empty((B, H, T), dtype=torch.float32, device="cuda:0"), torch.empty_like(dwf),
+                    torch.empty((B, H, d), dtype=torch.float32, device="cuda:0"),
+                    torch.empty((B, H, d), dtype=torch.float32, device="cuda:0"))
+
+            def bwd():
+                ttt.linear_ln_bwd(t["q"], t["k"], t["v"], t["eta"], gam, bet, wf, dl_sv, dz, cfg.b, dw_final=dwf,
+                                  out=gout)
+
+            if args.save:
+                kname = "ttt_linear_mfma_d64b16 (layer norm)"
+                step = fwd_save
+            elif args.bwd:
+                kname = ttt.linear_ln_bwd_kernel_name(B, H, T, d, cfg.b, 1, 0, inp.eta_strides)
+                step = bwd
+            else:
+                def step():
+                    fwd_save()
+                    bwd()
+        elif args.save or args.bwd or args.train:
             e_sv = torch.empty((B, H, T, d), dtype=torch.float32, device="cuda:0")
             ttt.linear_fwd_save(t["q"], t["k"], t["v"], t["w1"], t["eta"], cfg.b, z=z, w_final=wf, e_saved=e_sv)
             gen = torch.Generator(device="cuda:0")
@@ -443,9 +506,9 @@ def main():
     if args.save:
         bytes_ += B * H * T * d * 4                     # E written
     elif args.bwd:
-        bytes_, flops = algorithmic_bwd(cfg, inp.eta_strides)
+        bytes_, flops = (algorithmic_ln_bwd if args.ln else algorithmic_bwd)(cfg, inp.eta_strides)
     elif args.train:
-        b2, f2 = algorithmic_bwd(cfg, inp.eta_strides)
+        b2, f2 = (algorithmic_ln_bwd if args.ln else algorithmic_bwd)(cfg, inp.eta_strides)
         bytes_, flops = bytes_ + B * H * T * d * 4 + b2, flops + f2
     if args.decode:
         # per call: read W and write it; read Wb unless the token starts a mini-batch, write
@@ -520,7 +583,7 @@ def main():
     if not args.no_cpu_baseline and not args.decode:
         log("bench: timing the fp64 oracle on a sample ...")
         if args.bwd:
-            cpu = cpu_baseline_bwd(cfg, inp, args.cpu_sample_chains)
+            cpu = cpu_baseline_bwd(cfg, inp, args.cpu_sample_chains, ln=args.ln)
         else:
             cpu = cpu_baseline(cfg, inp, args.cpu_sample_chains, ln=args.ln)
         log(f"bench: cpu baseline {cpu['value']:.3e} tokens/s ({cpu['sample']})")
@@ -538,14 +601,17 @@ def main():
         roof["note"] = ("chunked forward: chunk 0 with the maps of chunks 1..n-2, the scan of the maps, then "
                         "chunks 1..n-1 in parallel (3 launches per call)")
     direction = "fwd"
+    ln_pre = "layer-norm " if args.ln else ""
+    saved = "G" if args.ln else "E"
     if args.save:
-        form, direction = "", "fwd (saving E for the backward)"
+        form, direction = ln_pre, f"fwd (saving {saved} for the backward)"
     if args.bwd:
-        form, direction = ("generic " if args.generic else ""), "bwd"
-        roof["note"] = "backward: dQ, dK, dV, deta, dW0 from dZ and dW_final, state rebuilt from W_final and E"
+        form, direction = ln_pre + ("generic " if args.generic else ""), "bwd"
+        roof["note"] = (f"backward: dQ, dK, dV, deta, dW0{', dgamma, dbeta' if args.ln else ''} from dZ and "
+                        f"dW_final, state rebuilt from W_final and {saved}")
     if args.train:
-        form, direction = "", "fwd+bwd (training step)"
-        roof["note"] = "forward saving E, then backward: two launches per step"
+        form, direction = ln_pre, "fwd+bwd (training step)"
+        roof["note"] = f"forward saving {saved}, then backward: two launches per step"
     headline = cfg.name == "l1p3b" and not form and direction == "fwd"
     rec = {
         "metric": METRIC if headline else
@@ -556,7 +622,8 @@ def main():
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" and not args.generic else "fp32",
         "data": "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) weights)",
-        "config": {"workload": f"{model} dual-form {direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
+        "config": {"workload": f"{model} {'layer-norm ' if args.ln else ''}dual-form "
+                               f"{direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
                                f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
                                f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta",
                    "B": B, "H": H, "d": d, "T": T, "b": cfg.b, "global_batch": B, "seq_len": T,

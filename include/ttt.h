@@ -183,6 +183,65 @@ ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const v
                              void* Z, float* W_final, void* stream);
 
 /*
+ * TTT-Linear with layer norm, forward for training: ttt_linear_ln_fwd, and also
+ *   G_saved : [B,H,T,d] fp32, g_t = -eta_t delta_t, the update factor of
+ *             token t exactly as the forward applied it to the state
+ *             (W <- W + sum_t g_t k_t^T over each mini-batch), with delta_t
+ *             the gradient of |f(k_t) - v_t|^2 with respect to y_t = W k_t at
+ *             the mini-batch-start W.  With it and W_final, ttt_linear_ln_bwd
+ *             undoes the forward's own steps.  Must overlap no other argument
+ *             (TTT_ERR_ALIAS); 16-byte aligned (TTT_ERR_ALIGN); non-NULL when
+ *             B*H*T > 0 (TTT_ERR_NULL).
+ * Same support and other errors as ttt_linear_ln_fwd; Z and W_final are
+ * bit-identical to those of ttt_linear_ln_fwd.
+ */
+ttt_status ttt_linear_ln_fwd_save(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                  const float* W0, const float* gamma, const float* beta, float eps,
+                                  const float* eta, void* Z, float* W_final, float* G_saved, void* stream);
+
+/*
+ * TTT-Linear with layer norm, backward ([TTT] 03 §4: the layer is trained end
+ * to end; 03 §9: f(x) = x + LN(W x)).  With L any scalar whose gradients with
+ * respect to Z and W_final are dZ and dW_final, it returns the gradients of L
+ * with respect to every input of ttt_linear_ln_fwd:
+ *   in : Q, K, V      [B,H,T,d] bf16 (as given to the forward)
+ *        eta          strided as for the forward
+ *        gamma, beta  [H,d] fp32, eps (as given to the forward)
+ *        W_final      [B,H,d,d] fp32 from ttt_linear_ln_fwd_save
+ *        G_saved      [B,H,T,d] fp32 from ttt_linear_ln_fwd_save
+ *        dZ           [B,H,T,d] out_dtype
+ *        dW_final     [B,H,d,d] fp32, or NULL for zero
+ *   out: dQ, dK, dV   [B,H,T,d] out_dtype
+ *        deta         [B,H,T] fp32 per token (sum it where tokens share an eta)
+ *        dW0          [B,H,d,d] fp32 per sequence (sum over B for a shared W0)
+ *        dgamma, dbeta [B,H,d] fp32 per sequence (sum over B for the [H,d] parameters)
+ * The mini-batch-start states are rebuilt backward from W_final and G_saved
+ * (W = W' - sum_t g_t k_t^T); everything else the backward needs (delta,
+ * both layer norms and their statistics) is recomputed from the inputs.
+ * Outputs overlap no input and no other output (TTT_ERR_ALIAS).
+ * Supported: d = 64, b = 16, bf16 inputs, flags = 0 (else TTT_ERR_UNSUPPORTED),
+ * on one fp32 kernel (ttt_linear_ln_bwd_fp32, one workgroup per sequence and
+ * head).  eps must be finite and >= 0 (TTT_ERR_SHAPE); other errors as for
+ * ttt_linear_bwd.
+ */
+ttt_status ttt_linear_ln_bwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* eta, const float* gamma, const float* beta, float eps,
+                             const float* W_final, const float* G_saved, const void* dZ, const float* dW_final,
+                             void* dQ, void* dK, void* dV, float* deta, float* dW0, float* dgamma, float* dbeta,
+                             void* stream);
+
+/* Runs every host-side check of ttt_linear_ln_bwd and launches nothing. */
+ttt_status ttt_linear_ln_bwd_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                      const float* eta, const float* gamma, const float* beta, float eps,
+                                      const float* W_final, const float* G_saved, const void* dZ,
+                                      const float* dW_final, const void* dQ, const void* dK, const void* dV,
+                                      const float* deta, const float* dW0, const float* dgamma,
+                                      const float* dbeta);
+
+/* Name of the kernel ttt_linear_ln_bwd would launch for desc, or NULL if unsupported. */
+const char* ttt_linear_ln_bwd_kernel_name(const ttt_linear_desc* desc);
+
+/*
  * TTT-Linear decode ([TTT] 04 §3: generation is sequential and uses the primal
  * form).  Continues B*H sequences by desc->T new tokens (often 1), all at
  * absolute positions pos, pos+1, ..., carrying the state in place:

@@ -51,7 +51,8 @@ EXPORTS = (
     "ttt_linear_fwd", "ttt_linear_validate", "ttt_linear_kernel_name",
     "ttt_linear_decode", "ttt_linear_decode_validate",
     "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes", "ttt_linear_fwd_chunked_noalloc",
-    "ttt_linear_ln_fwd",
+    "ttt_linear_ln_fwd", "ttt_linear_ln_fwd_save", "ttt_linear_ln_bwd", "ttt_linear_ln_bwd_validate",
+    "ttt_linear_ln_bwd_kernel_name",
     "ttt_linear_fwd_save", "ttt_linear_bwd", "ttt_linear_bwd_validate", "ttt_linear_bwd_kernel_name",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name", "ttt_mlp_ln_fwd",
     "ttt_status_str", "ttt_abi_version",
@@ -126,6 +127,17 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_ln_fwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, fp, vp, fp,
                                     vp]
     L.ttt_linear_ln_fwd.restype = ctypes.c_int
+    L.ttt_linear_ln_fwd_save.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, fp, vp,
+                                         fp, fp, vp]
+    L.ttt_linear_ln_fwd_save.restype = ctypes.c_int
+    L.ttt_linear_ln_bwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, fp, fp, vp,
+                                    fp, vp, vp, vp, fp, fp, fp, fp, vp]
+    L.ttt_linear_ln_bwd.restype = ctypes.c_int
+    L.ttt_linear_ln_bwd_validate.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float,
+                                             fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, fp]
+    L.ttt_linear_ln_bwd_validate.restype = ctypes.c_int
+    L.ttt_linear_ln_bwd_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
+    L.ttt_linear_ln_bwd_kernel_name.restype = ctypes.c_char_p
     L.ttt_linear_fwd_save.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, vp, fp, fp, vp]
     L.ttt_linear_fwd_save.restype = ctypes.c_int
     L.ttt_linear_bwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, vp]
@@ -443,33 +455,93 @@ def linear_fwd_chunked_noalloc(q, k, v, w0, eta, b: int, nchunks: int, out_dtype
 
 
 def linear_ln_fwd(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, out_dtype=None, w_final=None,
-                  z=None, stream=None):
+                  z=None, stream=None, g_saved=None, save: bool = False):
     """TTT-Linear with layer norm and residual inside f: f(x) = x + LN(W x).
 
     gamma, beta : [H, d] float32 (per head).  Other arguments as :func:`linear_fwd`.
+    save / g_saved : also write G [B, H, T, d] float32, each token's update
+    factor -eta delta as the forward applied it (delta the gradient of the
+    token's loss with respect to W k at its mini-batch-start W), the input of
+    :func:`linear_ln_bwd`; then returns (Z, W_final, G).
     """
     torch = _torch()
     B, H, T, d = q.shape
     if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
         raise ValueError("gamma and beta must be [H, d]")
-    if tuple(w0.shape) == (H, d, d):
-        wstride = 0
-    elif tuple(w0.shape) == (B, H, d, d):
-        wstride = H * d * d
-    else:
-        raise ValueError(f"w0 shape {tuple(w0.shape)}: expected [H,d,d] or [B,H,d,d]")
+    wstride = _w0_stride(w0, B, H, d)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     eta_t, est = eta_layout(eta, B, H, T, q.device)
     if z is None:
         z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
     if w_final is None:
         w_final = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-    _check_dev(q, k, v, w0, gamma, beta, eta_t, z, w_final)
+    save = save or g_saved is not None
+    if save and g_saved is None:
+        g_saved = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    _check_dev(q, k, v, w0, gamma, beta, eta_t, z, w_final, g_saved)
     desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, 0)
+    if save:
+        st = lib().ttt_linear_ln_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
+                                          _ptr(beta), float(eps), _ptr(eta_t), _ptr(z), _ptr(w_final),
+                                          _ptr(g_saved), _stream_handle(stream))
+        _done(st, "ttt_linear_ln_fwd_save")
+        return z, w_final, g_saved
     st = lib().ttt_linear_ln_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
                                  _ptr(beta), float(eps), _ptr(eta_t), _ptr(z), _ptr(w_final), _stream_handle(stream))
     _done(st, "ttt_linear_ln_fwd")
     return z, w_final
+
+
+def linear_ln_bwd(q, k, v, eta, gamma, beta, w_final, g_saved, dz, b: int, eps: float = 1e-6,
+                  dw_final=None, out=None, stream=None):
+    """Backward of :func:`linear_ln_fwd`.
+
+    q, k, v, eta, gamma, beta, eps : as given to the forward
+    w_final, g_saved : from :func:`linear_ln_fwd` with save=True
+    dz       : [B, H, T, d] gradient with respect to Z (its dtype is that of dq, dk, dv)
+    dw_final : [B, H, d, d] float32 gradient with respect to W_final, or None (zero)
+    out      : optional (dq, dk, dv, deta, dw0, dgamma, dbeta) preallocated outputs
+    returns (dq, dk, dv, deta [B, H, T], dw0 [B, H, d, d], dgamma [B, H, d], dbeta [B, H, d]),
+    the last three per sequence.
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
+        raise ValueError("gamma and beta must be [H, d]")
+    if dz.shape != q.shape or tuple(g_saved.shape) != tuple(q.shape) or tuple(w_final.shape) != (B, H, d, d):
+        raise ValueError("dz, g_saved must be [B, H, T, d] and w_final [B, H, d, d]")
+    if g_saved.dtype != torch.float32 or w_final.dtype != torch.float32:
+        raise TypeError("g_saved and w_final must be float32")
+    if dw_final is not None and (tuple(dw_final.shape) != (B, H, d, d) or dw_final.dtype != torch.float32):
+        raise ValueError("dw_final must be [B, H, d, d] float32")
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if out is None:
+        dev = q.device
+        out = (torch.empty((B, H, T, d), dtype=dz.dtype, device=dev),
+               torch.empty((B, H, T, d), dtype=dz.dtype, device=dev),
+               torch.empty((B, H, T, d), dtype=dz.dtype, device=dev),
+               torch.empty((B, H, T), dtype=torch.float32, device=dev),
+               torch.empty((B, H, d, d), dtype=torch.float32, device=dev),
+               torch.empty((B, H, d), dtype=torch.float32, device=dev),
+               torch.empty((B, H, d), dtype=torch.float32, device=dev))
+    dq, dk, dv, deta, dw0, dgamma, dbeta = out
+    _check_dev(q, k, v, eta_t, gamma, beta, w_final, g_saved, dz, dw_final, *out)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(dz.dtype), 0, est, 0)
+    st = lib().ttt_linear_ln_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(gamma),
+                                 _ptr(beta), float(eps), _ptr(w_final), _ptr(g_saved), _ptr(dz),
+                                 _ptr(dw_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0),
+                                 _ptr(dgamma), _ptr(dbeta), _stream_handle(stream))
+    _done(st, "ttt_linear_ln_bwd")
+    return dq, dk, dv, deta, dw0, dgamma, dbeta
+
+
+def linear_ln_bwd_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32,
+                              eta_strides=(0, 0, 0)) -> Optional[str]:
+    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, 0)
+    name = lib().ttt_linear_ln_bwd_kernel_name(ctypes.byref(desc))
+    return None if name is None else name.decode()
 
 
 def linear_chunked_workspace_bytes(B, H, T, d, b, nchunks) -> int:

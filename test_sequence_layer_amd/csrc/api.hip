@@ -235,6 +235,7 @@ ttt::BwdArgs make_bwd_args(const ttt_linear_desc* d, const void* Q, const void* 
   a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
   a.Wf = Wf; a.E = E; a.dZ = dZ; a.dWf = dWf;
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.deta = deta; a.dW0 = dW0;
+  a.V = nullptr; a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f; a.dgamma = nullptr; a.dbeta = nullptr;
   return a;
 }
 
@@ -425,29 +426,43 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+namespace {
+
+// Checks of a forward's saved-for-backward buffer (fp32, one value per token
+// and output): non-NULL, 16-byte aligned, overlapping no input or output.
+ttt_status check_saved(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V, const float* W0,
+                       const float* eta, const void* Z, const float* W_final, const float* saved) {
+  const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
+  const int64_t tok = chains * desc->T * desc->d;
+  if (tok == 0) return TTT_OK;
+  if (!saved) return TTT_ERR_NULL;
+  if (!aligned(saved, 16)) return TTT_ERR_ALIGN;
+  const int64_t in_b = tok * dtype_size(desc->in_dtype), z_b = tok * dtype_size(desc->out_dtype);
+  const int64_t hdd = static_cast<int64_t>(desc->H) * desc->d * desc->d;
+  const int64_t w0_b = (desc->w0_batch_stride == 0 ? hdd : chains * desc->d * desc->d) * 4;
+  const int64_t eta_b =
+      eta_extent(desc->B, desc->H, desc->T, desc->eta_stride_b, desc->eta_stride_h, desc->eta_stride_t) * 4;
+  const Range re{saved, tok * 4};
+  for (Range r : {Range{Q, in_b}, Range{K, in_b}, Range{V, in_b}, Range{eta, eta_b}, Range{W0, w0_b},
+                  Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
+    if (overlaps(re, r)) return TTT_ERR_ALIAS;
+  return TTT_OK;
+}
+
+}  // namespace
+
 ttt_status ttt_linear_fwd_save(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                                const float* W0, const float* eta, void* Z, float* W_final, float* E_saved,
                                void* stream) {
   Kernel k;
-  const ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
+  ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
   if (st != TTT_OK) return st;
   if (desc->flags & TTT_FLAG_PRIMAL) return TTT_ERR_FLAGS;
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   if (chains == 0) return TTT_OK;
+  st = check_saved(desc, Q, K, V, W0, eta, Z, W_final, E_saved);
+  if (st != TTT_OK) return st;
   const int64_t tok = chains * desc->T * desc->d;
-  if (tok > 0) {
-    if (!E_saved) return TTT_ERR_NULL;
-    if (!aligned(E_saved, 16)) return TTT_ERR_ALIGN;
-    const int64_t in_b = tok * dtype_size(desc->in_dtype), z_b = tok * dtype_size(desc->out_dtype);
-    const int64_t hdd = static_cast<int64_t>(desc->H) * desc->d * desc->d;
-    const int64_t w0_b = (desc->w0_batch_stride == 0 ? hdd : chains * desc->d * desc->d) * 4;
-    const int64_t eta_b =
-        eta_extent(desc->B, desc->H, desc->T, desc->eta_stride_b, desc->eta_stride_h, desc->eta_stride_t) * 4;
-    const Range re{E_saved, tok * 4};
-    for (Range r : {Range{Q, in_b}, Range{K, in_b}, Range{V, in_b}, Range{eta, eta_b}, Range{W0, w0_b},
-                    Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
-      if (overlaps(re, r)) return TTT_ERR_ALIAS;
-  }
   ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
   a.Esave = tok > 0 ? E_saved : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -487,9 +502,12 @@ ttt_status ttt_linear_bwd(const ttt_linear_desc* desc, const void* Q, const void
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
-ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
-                             const float* W0, const float* gamma, const float* beta, float eps, const float* eta,
-                             void* Z, float* W_final, void* stream) {
+namespace {
+
+// Every check of the layer-norm forward (the plain forward's, then its own).
+ttt_status validate_ln(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V, const float* W0,
+                       const float* gamma, const float* beta, float eps, const float* eta, const void* Z,
+                       const float* W_final) {
   Kernel k;
   const ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
   if (st != TTT_OK) return st;
@@ -504,12 +522,125 @@ ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const v
   for (Range out : {Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
     for (Range in : {Range{gamma, hd_b}, Range{beta, hd_b}})
       if (overlaps(out, in)) return TTT_ERR_ALIAS;
+  return TTT_OK;
+}
+
+hipError_t launch_ln(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V, const float* W0,
+                     const float* gamma, const float* beta, float eps, const float* eta, void* Z, float* W_final,
+                     float* saved, void* stream) {
   ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
   a.gamma = gamma;
   a.beta = beta;
   a.eps = eps;
   a.rb = 1;
-  const hipError_t e = ttt::launch_linear_mfma(a, static_cast<hipStream_t>(stream));
+  a.Esave = saved;
+  return ttt::launch_linear_mfma(a, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* W0, const float* gamma, const float* beta, float eps, const float* eta,
+                             void* Z, float* W_final, void* stream) {
+  const ttt_status st = validate_ln(desc, Q, K, V, W0, gamma, beta, eps, eta, Z, W_final);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  const hipError_t e = launch_ln(desc, Q, K, V, W0, gamma, beta, eps, eta, Z, W_final, nullptr, stream);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_linear_ln_fwd_save(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                  const float* W0, const float* gamma, const float* beta, float eps,
+                                  const float* eta, void* Z, float* W_final, float* G_saved, void* stream) {
+  ttt_status st = validate_ln(desc, Q, K, V, W0, gamma, beta, eps, eta, Z, W_final);
+  if (st != TTT_OK) return st;
+  const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
+  if (chains == 0) return TTT_OK;
+  st = check_saved(desc, Q, K, V, W0, eta, Z, W_final, G_saved);
+  if (st != TTT_OK) return st;
+  const int64_t hd_b = static_cast<int64_t>(desc->H) * desc->d * 4;
+  const Range rd{G_saved, chains * desc->T * desc->d * 4};
+  if (overlaps(rd, Range{gamma, hd_b}) || overlaps(rd, Range{beta, hd_b})) return TTT_ERR_ALIAS;
+  const bool any = chains * desc->T > 0;
+  const hipError_t e =
+      launch_ln(desc, Q, K, V, W0, gamma, beta, eps, eta, Z, W_final, any ? G_saved : nullptr, stream);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+namespace {
+
+// Every check of the layer-norm backward: the plain backward's (with the saved
+// delta in E's place), then V, gamma, beta, eps and the two extra outputs.
+ttt_status validate_ln_bwd(const ttt_linear_desc* d, const void* Q, const void* K, const void* V, const float* eta,
+                           const float* gamma, const float* beta, float eps, const float* Wf, const float* Ds,
+                           const void* dZ, const float* dWf, const void* dQ, const void* dK, const void* dV,
+                           const float* deta, const float* dW0, const float* dgamma, const float* dbeta) {
+  BwdKernel k;
+  const ttt_status st = validate_bwd(d, Q, K, eta, Wf, Ds, dZ, dWf, dQ, dK, dV, deta, dW0, &k);
+  if (st != TTT_OK) return st;
+  ttt::BwdArgs a = make_bwd_args(d, Q, K, eta, Wf, Ds, dZ, dWf, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (d->flags != 0 || !ttt::linear_ln_bwd_supported(a)) return TTT_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
+  const int64_t chains = static_cast<int64_t>(d->B) * d->H;
+  if (chains == 0) return TTT_OK;
+  const int64_t tok = chains * d->T * d->d;
+  if (!gamma || !beta || !dgamma || !dbeta || (tok > 0 && !V)) return TTT_ERR_NULL;
+  if (!aligned(gamma, 4) || !aligned(beta, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4)) return TTT_ERR_ALIGN;
+  if (tok > 0 && !aligned(V, 16)) return TTT_ERR_ALIGN;
+  const int64_t in_b = tok * dtype_size(d->in_dtype), g_b = tok * dtype_size(d->out_dtype);
+  const int64_t hd_b = static_cast<int64_t>(d->H) * d->d * 4, cd_b = chains * d->d * 4;
+  const int64_t w_b = chains * d->d * d->d * 4;
+  const int64_t eta_b = tok > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const Range ins[] = {{Q, in_b}, {K, in_b}, {V, in_b}, {eta, eta_b}, {gamma, hd_b}, {beta, hd_b}, {Wf, w_b},
+                       {Ds, tok * 4}, {dZ, g_b}, {dWf, w_b}};
+  const Range outs[] = {{dQ, g_b}, {dK, g_b}, {dV, g_b}, {deta, tok > 0 ? chains * d->T * 4 : 0}, {dW0, w_b},
+                        {dgamma, cd_b}, {dbeta, cd_b}};
+  for (int i = 0; i < 7; ++i) {
+    for (const Range& in : ins)
+      if (overlaps(outs[i], in)) return TTT_ERR_ALIAS;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_ALIAS;
+  }
+  return TTT_OK;
+}
+
+}  // namespace
+
+ttt_status ttt_linear_ln_bwd_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                      const float* eta, const float* gamma, const float* beta, float eps,
+                                      const float* W_final, const float* G_saved, const void* dZ,
+                                      const float* dW_final, const void* dQ, const void* dK, const void* dV,
+                                      const float* deta, const float* dW0, const float* dgamma,
+                                      const float* dbeta) {
+  return validate_ln_bwd(desc, Q, K, V, eta, gamma, beta, eps, W_final, G_saved, dZ, dW_final, dQ, dK, dV,
+                         deta, dW0, dgamma, dbeta);
+}
+
+const char* ttt_linear_ln_bwd_kernel_name(const ttt_linear_desc* d) {
+  if (!d || d->flags != 0) return nullptr;
+  const ttt::BwdArgs a = make_bwd_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, nullptr, nullptr, nullptr);
+  return ttt::linear_ln_bwd_supported(a) ? "ttt_linear_ln_bwd_fp32" : nullptr;
+}
+
+ttt_status ttt_linear_ln_bwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* eta, const float* gamma, const float* beta, float eps,
+                             const float* W_final, const float* G_saved, const void* dZ, const float* dW_final,
+                             void* dQ, void* dK, void* dV, float* deta, float* dW0, float* dgamma, float* dbeta,
+                             void* stream) {
+  const ttt_status st = validate_ln_bwd(desc, Q, K, V, eta, gamma, beta, eps, W_final, G_saved, dZ, dW_final,
+                                        dQ, dK, dV, deta, dW0, dgamma, dbeta);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  ttt::BwdArgs a =
+      make_bwd_args(desc, Q, K, eta, W_final, G_saved, dZ, dW_final, dQ, dK, dV, deta, dW0);
+  a.V = V;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.eps = eps;
+  a.dgamma = dgamma;
+  a.dbeta = dbeta;
+  const hipError_t e = ttt::launch_linear_ln_bwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

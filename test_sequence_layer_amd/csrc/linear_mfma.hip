@@ -137,14 +137,16 @@ __device__ __forceinline__ int64_t chunk_begin(int64_t c, int64_t nb, int64_t n,
 // query path and no Z; every wave holds its 16 rows of both (they share the
 // staged K and V tiles).
 // LN: f(x) = x + LN(W x) (layer norm and residual inside f; MODE 0 only).
-// SAVE: also write E = W K - V of every token (the backward's input; MODE 0, no LN).
+// SAVE: also write the backward's input of every token (MODE 0): E = W K - V,
+// or with LN the update factor G = -eta delta as applied (delta the gradient
+// of the token's loss with respect to W k).
 // RB: row blocks (workgroups) per (sequence, head, chunk); 1, 2 or 4.
 template <int PF, bool ETA_TOKEN, typename OutT, int MODE, bool LN, bool SAVE, int RB, typename SH>
 __device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const Unit& u) {
   static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
   static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks");
   static_assert(!LN || RB == 1, "the layer norm needs all 64 outputs of a token in one workgroup");
-  static_assert(!LN || (MODE == 0 && !SAVE), "the layer norm is a forward-only path");
+  static_assert(!LN || MODE == 0, "the maps have no layer norm");
   static_assert(MODE == 0 || (RB == 1 && !SAVE), "the maps run in whole workgroups");
   constexpr int NWV = 4 / RB;   // waves per workgroup
   constexpr int NT = 64 * NWV;  // threads per workgroup
@@ -289,7 +291,7 @@ __device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const U
     }
   };
   auto flush_z = [&](int m) {
-    if constexpr (SAVE) {
+    if constexpr (SAVE && !LN) {
       const float4 e4 = *reinterpret_cast<const float4*>(&sh.ebuf[m & 1][frow * ZROW + fl]);
       float* ep = a.Esave + (tok0 + static_cast<size_t>(m) * BT + frow) * D + fcol;
       put(reinterpret_cast<u32x4*>(ep),
@@ -467,6 +469,16 @@ __device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const U
       // operand layout (lane = output 16w + l%16, slots = tokens)
       bf16x4 dh, dl;
       split4(d, dh, dl);
+      if constexpr (SAVE) {
+        // G exactly as the update applies it (hi + lo is exact in fp32), 16
+        // lanes writing the token's row
+        float* ep = a.Esave + (tok0 + static_cast<size_t>(n) * BT + tk) * D + 4 * li;
+        float gs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gs[r] = static_cast<float>(dh[r]) + static_cast<float>(dl[r]);
+        st_stream(reinterpret_cast<u32x4*>(ep),
+                  u32x4{__float_as_uint(gs[0]), __float_as_uint(gs[1]), __float_as_uint(gs[2]), __float_as_uint(gs[3])});
+      }
       *reinterpret_cast<bf16x4*>(&sh.lns.gh[tk * ROW + 4 * li]) = dh;
       *reinterpret_cast<bf16x4*>(&sh.lns.gl[tk * ROW + 4 * li]) = dl;
       __syncthreads();
@@ -587,8 +599,9 @@ __global__ __launch_bounds__(256 / RB) void ttt_linear_mfma_d64b16(LinearArgs a)
   __shared__ Slot slots[2];
   __shared__ LnShared lns;
   __shared__ __align__(16) float zbuf[!LN ? 2 : 1][!LN ? BT * ZROW : 4];
-  __shared__ __align__(16) float ebuf[SAVE ? 2 : 1][SAVE ? BT * ZROW : 4];
-  Shm<!LN, SAVE> sh{slots, lns, zbuf, ebuf};
+  constexpr bool EB = SAVE && !LN;  // E staged like Z (the layer norm writes delta directly)
+  __shared__ __align__(16) float ebuf[EB ? 2 : 1][EB ? BT * ZROW : 4];
+  Shm<!LN, EB> sh{slots, lns, zbuf, ebuf};
   const int per_chain = a.nchunk > 1 ? a.nchunk - 1 : 1;
   const int units = a.B * a.H * per_chain;
   // The RB row blocks of a unit are 8 block indices apart, so the round-robin
@@ -685,14 +698,12 @@ hipError_t launch_rb(const LinearArgs& a, hipStream_t s) {
   if constexpr (!LN && RB == 1 && !LONG) {
     if (units < kShortRingUnits) return launch_rb<TOK, false, 1, true>(a, s);
   }
-  if constexpr (!LN) {
-    if (a.Esave) {
-      if (a.out_dtype == 0)
-        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, false, true, RB>), grid, block, 0, s, a);
-      else
-        hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, false, true, RB>), grid, block, 0, s, a);
-      return hipGetLastError();
-    }
+  if (a.Esave) {
+    if (a.out_dtype == 0)
+      hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, LN, true, RB>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, uint16_t, LN, true, RB>), grid, block, 0, s, a);
+    return hipGetLastError();
   }
   if (a.out_dtype == 0)
     hipLaunchKernelGGL((ttt_linear_mfma_d64b16<PF, TOK, float, LN, false, RB>), grid, block, 0, s, a);

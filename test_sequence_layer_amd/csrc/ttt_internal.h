@@ -32,6 +32,7 @@ struct LinearArgs {
   const float* beta;    // [H][d]
   float eps;
   // Forward for training: also write E[t] = W_{mini-batch start} k_t - v_t
+  // (with the layer norm: the update factor G[t] = -eta_t delta_t as applied)
   // ([chains][T][d] fp32) for the backward; nullptr: not saved.
   float* Esave;
   // MFMA forward: workgroups (row blocks of 64 / rb rows of W) per
@@ -56,12 +57,25 @@ struct BwdArgs {
   void* dV;
   float* deta;               // [chains][T]
   float* dW0;                // [chains][d][d]
+  // Layer norm and residual inside f (gamma != nullptr): E holds the saved
+  // update factors G = -eta delta (delta the loss gradient at W k) as the
+  // forward applied them, V the values; the gradients of the per-head scale
+  // and shift come out per chain.
+  const void* V;             // [chains][T][d] in_dtype
+  const float* gamma;        // [H][d]
+  const float* beta;         // [H][d]
+  float eps;
+  float* dgamma;             // [chains][d]
+  float* dbeta;              // [chains][d]
 };
 bool linear_bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_linear_bwd_mfma(const BwdArgs& a, hipStream_t s);
 bool linear_bwd_generic_supported(int d, int b);
 const char* linear_bwd_generic_name(int d);
 hipError_t launch_linear_bwd_generic(const BwdArgs& a, hipStream_t s);
+// Backward of TTT-Linear with the layer norm (fp32 arithmetic): d = 64, b = 16.
+bool linear_ln_bwd_supported(const BwdArgs& a);
+hipError_t launch_linear_ln_bwd(const BwdArgs& a, hipStream_t s);
 
 struct MlpArgs {
   int B, H, T, d, dh, b;

@@ -311,6 +311,72 @@ def test_fwd_save_rejects_primal():
     assert st == FLAGS
 
 
+# ---- layer-norm backward validation -------------------------------------------
+
+class LnBwdBufs:
+    """Fake aligned, disjoint device addresses for the layer-norm backward."""
+
+    NAMES = ("q", "k", "v", "eta", "gamma", "beta", "wf", "dl", "dz", "dwf", "dq", "dk", "dv", "deta", "dw0",
+             "dgamma", "dbeta")
+
+    def __init__(self):
+        for i, n in enumerate(self.NAMES):
+            setattr(self, n, (i + 1) * GB)
+
+    def args(self, eps):
+        a = [getattr(self, n) for n in self.NAMES]
+        return (*a[:6], ctypes.c_float(eps), *a[6:])
+
+
+def _lbval(desc, eps=1e-6, **over):
+    bufs = LnBwdBufs()
+    for k, v in over.items():
+        setattr(bufs, k, v)
+    return ttt.lib().ttt_linear_ln_bwd_validate(ctypes.byref(desc), *bufs.args(eps))
+
+
+def test_ln_bwd_validation():
+    assert _lbval(_desc()) == OK
+    assert _lbval(_desc(outd=1, est=(4 * 64, 64, 1))) == OK
+    assert _lbval(_desc(), dwf=None) == OK
+    assert ttt.lib().ttt_linear_ln_bwd_validate(None, *LnBwdBufs().args(1e-6)) == NULL
+    for name in LnBwdBufs.NAMES:
+        if name != "dwf":
+            assert _lbval(_desc(), **{name: None}) == NULL, name
+    assert _lbval(_desc(), eps=-1.0) == SHAPE
+    assert _lbval(_desc(), eps=float("nan")) == SHAPE
+    assert _lbval(_desc(ind=0)) == UNSUP                      # bf16 inputs only
+    assert _lbval(_desc(b=8)) == UNSUP
+    assert _lbval(_desc(flags=ttt.TTT_FLAG_GENERIC)) == UNSUP
+    assert _lbval(_desc(), v=3 * GB + 8) == ALIGN
+    assert _lbval(_desc(), gamma=5 * GB + 2) == ALIGN
+    assert _lbval(_desc(), dgamma=1 * GB) == ALIAS            # output over an input
+    assert _lbval(_desc(), dbeta=16 * GB + 64) == ALIAS       # output over another output
+    assert _lbval(_desc(), dq=5 * GB) == ALIAS                # dq over gamma
+    assert _lbval(_desc(B=0)) == OK
+    assert _lbval(_desc(T=0), q=None, k=None, v=None, dl=None, dz=None, dq=None, dk=None, dv=None,
+                  deta=None) == OK
+    assert ttt.linear_ln_bwd_kernel_name(16, 32, 8192, 64, 16) == "ttt_linear_ln_bwd_fp32"
+    assert ttt.linear_ln_bwd_kernel_name(1, 1, 64, 64, 16, in_dtype=ttt.TTT_F32) is None
+
+
+def test_ln_fwd_save_host_errors():
+    desc = _desc()
+    b = Bufs()
+    f = ttt.lib().ttt_linear_ln_fwd_save
+    gam, bet = 8 * GB, 9 * GB
+    assert f(ctypes.byref(desc), b.q, b.k, b.v, b.w0, gam, bet, ctypes.c_float(1e-6), b.eta, b.z, b.wf,
+             None, None) == NULL
+    assert f(ctypes.byref(desc), b.q, b.k, b.v, b.w0, gam, bet, ctypes.c_float(1e-6), b.eta, b.z, b.wf,
+             b.z, None) == ALIAS
+    assert f(ctypes.byref(desc), b.q, b.k, b.v, b.w0, gam, bet, ctypes.c_float(1e-6), b.eta, b.z, b.wf,
+             gam, None) == ALIAS
+    assert f(ctypes.byref(desc), b.q, b.k, b.v, b.w0, gam, bet, ctypes.c_float(1e-6), b.eta, b.z, b.wf,
+             10 * GB + 4, None) == ALIGN
+    assert f(ctypes.byref(_desc(ind=0)), b.q, b.k, b.v, b.w0, gam, bet, ctypes.c_float(1e-6), b.eta, b.z, b.wf,
+             10 * GB, None) == UNSUP
+
+
 def test_one_hip_runtime_per_process():
     # torch ships a HIP runtime under the same soname the library needs; the
     # binding imports torch before it loads libttt.so so that both use that one
