@@ -303,6 +303,9 @@ def main():
                     help="split each sequence into this many chunks run in parallel (chunked forward)")
     ap.add_argument("--decode", action="store_true",
                     help="time decoding: one token per call for every sequence, state carried in place")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="with --decode: the number of sequences B (the pages' generation benchmark uses 512); "
+                         "the inputs then hold 64 tokens per sequence, which the calls cycle through")
     ap.add_argument("--graph", action="store_true",
                     help="with --decode: capture one mini-batch of one-token calls (b calls) in a HIP graph and "
                          "time its replays (no per-call host overhead)")
@@ -324,6 +327,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.graph and not args.decode:
         ap.error("--graph applies to --decode")
+    if args.batch is not None and not args.decode:
+        ap.error("--batch applies to --decode")
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the (sequence, head) chains are independent, so N GPUs would each run this same kernel on "
@@ -334,6 +339,8 @@ def main():
     import test_sequence_layer_amd as ttt
 
     cfg = ti.CONFIGS[args.config]
+    if args.batch is not None:
+        cfg = cfg.with_(name=f"{cfg.name}-B{args.batch}", B=args.batch, T=64)
     log(f"bench: generating {cfg.name} inputs ...")
     t0 = time.perf_counter()
     inp = ti.generate(cfg)
@@ -341,37 +348,34 @@ def main():
     log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
     B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
     z = torch.empty((B, H, T, d), dtype=torch.float32, device="cuda:0")
-    if cfg.is_mlp:
-        f1 = torch.empty((B, H, cfg.dh, d), dtype=torch.float32, device="cuda:0")
-        f2 = torch.empty((B, H, d, cfg.dh), dtype=torch.float32, device="cuda:0")
-        kname = ttt.mlp_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides)
-        if args.ln:
-            kname += " (layer norm)"
-            gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
-            bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
-
-            def step():
-                ttt.mlp_ln_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], gam, bet, t["eta"], cfg.b, z=z,
-                               w1_final=f1, w2_final=f2)
-        else:
-            def step():
-                ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1,
-                            w2_final=f2)
-    elif args.decode:
+    if args.decode:
         # one call = one new token for all B*H sequences (T=1), positions advancing
-        kname = ttt.linear_kernel_name(B, H, 1, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0, (0, 0, 0),
-                                       primal=True)
-        w = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
-        wb = w.clone()
+        in_code = 1 if cfg.dtype == "bf16" else 0
         zt = torch.empty((B, H, 1, d), dtype=torch.float32, device="cuda:0")
         tok = [(t["q"][:, :, i:i + 1].contiguous(), t["k"][:, :, i:i + 1].contiguous(),
                 t["v"][:, :, i:i + 1].contiguous(),
                 t["eta"][:, :, i:i + 1].contiguous() if t["eta"].dim() == 3 else t["eta"]) for i in range(64)]
+        if cfg.is_mlp:
+            kname = ttt.mlp_kernel_name(B, H, 1, d, cfg.dh, cfg.b, in_code, 0, (0, 0, 0), primal=True)
+            w1 = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
+            w2 = t["w2"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
+            w1b, w2b = w1.clone(), w2.clone()
+
+            def call(i, p):
+                q1, k1, v1, e1 = tok[i]
+                ttt.mlp_decode(q1, k1, v1, e1, w1, w2, w1b, w2b, p, cfg.b, z=zt)
+        else:
+            kname = ttt.linear_kernel_name(B, H, 1, d, cfg.b, in_code, 0, (0, 0, 0), primal=True)
+            w = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
+            wb = w.clone()
+
+            def call(i, p):
+                q1, k1, v1, e1 = tok[i]
+                ttt.linear_decode(q1, k1, v1, e1, w, wb, p, cfg.b, z=zt)
         pos = [0]
 
         def step():
-            q1, k1, v1, e1 = tok[pos[0] % 64]
-            ttt.linear_decode(q1, k1, v1, e1, w, wb, pos[0], cfg.b, z=zt)
+            call(pos[0] % 64, pos[0])
             pos[0] += 1
 
         if args.graph:
@@ -379,8 +383,7 @@ def main():
             # captured once; each replay continues the sequences by b tokens
             def calls():
                 for i in range(cfg.b):
-                    q1, k1, v1, e1 = tok[i]
-                    ttt.linear_decode(q1, k1, v1, e1, w, wb, i, cfg.b, z=zt)
+                    call(i, i)
 
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -395,6 +398,22 @@ def main():
 
             def step():
                 graph.replay()
+    elif cfg.is_mlp:
+        f1 = torch.empty((B, H, cfg.dh, d), dtype=torch.float32, device="cuda:0")
+        f2 = torch.empty((B, H, d, cfg.dh), dtype=torch.float32, device="cuda:0")
+        kname = ttt.mlp_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides, primal=args.primal)
+        if args.ln:
+            kname += " (layer norm)"
+            gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
+            bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
+
+            def step():
+                ttt.mlp_ln_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], gam, bet, t["eta"], cfg.b, z=z,
+                               w1_final=f1, w2_final=f2)
+        else:
+            def step():
+                ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1,
+                            w2_final=f2, primal=args.primal)
     else:
         wf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda:0")
         kname = ttt.linear_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
@@ -511,11 +530,14 @@ def main():
         b2, f2 = (algorithmic_ln_bwd if args.ln else algorithmic_bwd)(cfg, inp.eta_strides)
         bytes_, flops = bytes_ + B * H * T * d * 4 + b2, flops + f2
     if args.decode:
-        # per call: read W and write it; read Wb unless the token starts a mini-batch, write
-        # Wb only when it does -- three d x d states on average over b calls -- plus one
-        # token of Q/K/V in and Z out
-        bytes_ = B * H * (3 * d * d * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
-        flops = B * H * 6 * d * d
+        # per call: read the state and write it; read the mini-batch-start state unless
+        # the token starts a mini-batch, write it only when it does -- three states on
+        # average over b calls (TTT-MLP: each state is W1 and W2, 2 d dh floats) --
+        # plus one token of Q/K/V in and Z out
+        state = 2 * d * cfg.dh if cfg.is_mlp else d * d
+        bytes_ = B * H * (3 * state * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
+        # TTT-MLP per token: W1b k, W1 q, W2b a, W2b^T e, the two rank-one steps, W2 a' (7 d dh MACs)
+        flops = B * H * (14 * d * cfg.dh if cfg.is_mlp else 6 * d * d)
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
     # counters are recorded per (kernel, workload) for the plain forward and the
     # backward; the other modes (saving forward, training step, layer norm,
@@ -613,6 +635,16 @@ def main():
         form, direction = ln_pre, "fwd+bwd (training step)"
         roof["note"] = f"forward saving {saved}, then backward: two launches per step"
     headline = cfg.name == "l1p3b" and not form and direction == "fwd"
+    if args.decode:
+        workload = (f"{model} decode (primal form, one token per call"
+                    f"{f', replays of a HIP graph of {cfg.b} calls' if args.graph else ''}) "
+                    f"B{B} H{H} d{d} b{cfg.b}: {B * H} (sequence, head) states, {cfg.dtype} Q/K/V, fp32 state "
+                    f"and Z, {eta_desc} eta")
+    else:
+        workload = (f"{model} {'layer-norm ' if args.ln else ''}dual-form "
+                    f"{direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
+                    f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
+                    f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta")
     rec = {
         "metric": METRIC if headline else
         f"{model} {form.strip() + ' ' if form.strip() else ''}{direction} tokens/sec ({cfg.name})",
@@ -622,10 +654,7 @@ def main():
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" and not args.generic else "fp32",
         "data": "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) weights)",
-        "config": {"workload": f"{model} {'layer-norm ' if args.ln else ''}dual-form "
-                               f"{direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
-                               f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
-                               f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta",
+        "config": {"workload": workload,
                    "B": B, "H": H, "d": d, "T": T, "b": cfg.b, "global_batch": B, "seq_len": T,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,

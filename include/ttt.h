@@ -333,12 +333,45 @@ typedef struct {
  * TTT-MLP forward.  Q, K, V, Z as for TTT-Linear.
  *   W1_0 : [B or 1, H, dh, d] fp32     W2_0 : [B or 1, H, d, dh] fp32
  *   W1_final : [B,H,dh,d] fp32         W2_final : [B,H,d,dh] fp32
- * Supported: d = 64, dh = 256, b = 16, bf16 inputs, fp32 Z (anything else:
- * TTT_ERR_UNSUPPORTED).
+ * flags: 0 (the dual form) or TTT_FLAG_PRIMAL (token by token, [TTT] 03 §7's
+ * naive form, on ttt_mlp_primal_d64h256: d = 64, dh = 256, any b >= 1, fp32
+ * or bf16 inputs and Z; T % b == 0 still required); other bits TTT_ERR_FLAGS.
+ * Supported without the flag: d = 64, dh = 256, b = 16, bf16 inputs, fp32 Z
+ * (anything else: TTT_ERR_UNSUPPORTED).
  */
 ttt_status ttt_mlp_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
                        const float* W1_0, const float* W2_0, const float* eta, void* Z,
                        float* W1_final, float* W2_final, void* stream);
+
+/*
+ * TTT-MLP decode ([TTT] 04 §3: generation is sequential and uses the primal
+ * form; Fig 15 compares TTT-MLP generation with TTT-Linear).  Continues B*H
+ * sequences by desc->T new tokens (often 1) at absolute positions pos, pos+1,
+ * ..., carrying the state in place:
+ *   W1, W2   : [B,H,dh,d] and [B,H,d,dh] fp32, the state after the pos tokens
+ *              seen so far (read, then overwritten with the state after the
+ *              new tokens)
+ *   W1b, W2b : the same shapes, the state at the start of the current
+ *              mini-batch (read and overwritten likewise).  A token at
+ *              position p with p % b == 0 starts a mini-batch: W1b, W2b <- W1, W2
+ *              before its gradient is taken.
+ *   Q, K, V, Z : [B,H,T,d]; eta strides index the new tokens (t = 0..T-1).
+ * Per token: h = W1b k, e = 2 (W2b GELU(h) - v), W2 -= eta e GELU(h)^T,
+ * W1 -= eta ((W2b^T e) * GELU'(h)) k^T, z = W2 GELU(W1 q).
+ * desc->w_batch_stride, desc->flags and desc->reserved must be 0; T need not
+ * be a multiple of b; pos < 0 is TTT_ERR_POS.  Decoding T tokens from pos = 0
+ * with W = Wb = W0 gives the same Z and state as ttt_mlp_fwd (to rounding).
+ * The five outputs (Z and the four states) overlap no input and each other
+ * (TTT_ERR_ALIAS).  Supported: d = 64, dh = 256, any b >= 1, fp32/bf16 inputs
+ * and Z.
+ */
+ttt_status ttt_mlp_decode(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* eta,
+                          void* Z, float* W1, float* W2, float* W1b, float* W2b, int64_t pos, void* stream);
+
+/* Runs every host-side check of ttt_mlp_decode and launches nothing. */
+ttt_status ttt_mlp_decode_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                   const float* eta, const void* Z, const float* W1, const float* W2,
+                                   const float* W1b, const float* W2b, int64_t pos);
 
 ttt_status ttt_mlp_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
                             const float* W1_0, const float* W2_0, const float* eta, const void* Z,

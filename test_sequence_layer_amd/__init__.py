@@ -55,6 +55,7 @@ EXPORTS = (
     "ttt_linear_ln_bwd_kernel_name",
     "ttt_linear_fwd_save", "ttt_linear_bwd", "ttt_linear_bwd_validate", "ttt_linear_bwd_kernel_name",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name", "ttt_mlp_ln_fwd",
+    "ttt_mlp_decode", "ttt_mlp_decode_validate",
     "ttt_status_str", "ttt_abi_version",
 )
 
@@ -150,6 +151,11 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
     L.ttt_linear_kernel_name.restype = ctypes.c_char_p
     L.ttt_mlp_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, vp, fp, fp, vp]
+    L.ttt_mlp_decode.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, vp, fp, fp, fp, fp, ctypes.c_int64, vp]
+    L.ttt_mlp_decode.restype = ctypes.c_int
+    L.ttt_mlp_decode_validate.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, vp, fp, fp, fp, fp,
+                                          ctypes.c_int64]
+    L.ttt_mlp_decode_validate.restype = ctypes.c_int
     L.ttt_mlp_fwd.restype = ctypes.c_int
     L.ttt_mlp_ln_fwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, fp, vp, fp,
                                  fp, vp]
@@ -579,18 +585,20 @@ def linear_decode(q, k, v, eta, w, wb, pos: int, b: int, out_dtype=None, z=None,
 
 # ---------------------------------------------------------------- TTT-MLP --
 
-def mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, w_batch_stride, eta_strides) -> MlpDesc:
-    return MlpDesc(B, H, T, d, dh, b, in_dtype, out_dtype, 0, 0, w_batch_stride, *eta_strides)
+def mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, w_batch_stride, eta_strides, flags=0) -> MlpDesc:
+    return MlpDesc(B, H, T, d, dh, b, in_dtype, out_dtype, flags, 0, w_batch_stride, *eta_strides)
 
 
 def mlp_fwd(q, k, v, w1, w2, eta, b: int, out_dtype=None, w1_final=None, w2_final=None, z=None,
-            stream=None):
+            stream=None, primal: bool = False):
     """TTT-MLP forward: f(x) = W2 GELU(W1 x).
 
     w1 : [H, dh, d] or [B, H, dh, d] float32;  w2 : [H, d, dh] or [B, H, d, dh] float32
+    primal : compute token by token (the primal form) instead of the dual form
     returns (Z, W1_final [B,H,dh,d], W2_final [B,H,d,dh]).
     """
-    return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream)
+    return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream,
+                     flags=TTT_FLAG_PRIMAL if primal else 0)
 
 
 def mlp_ln_fwd(q, k, v, w1, w2, gamma, beta, eta, b: int, eps: float = 1e-6, out_dtype=None, w1_final=None,
@@ -605,7 +613,7 @@ def mlp_ln_fwd(q, k, v, w1, w2, gamma, beta, eta, b: int, eps: float = 1e-6, out
     return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=(gamma, beta, eps))
 
 
-def _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=None):
+def _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=None, flags=0):
     torch = _torch()
     B, H, T, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -628,7 +636,7 @@ def _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream,
     if w2_final is None:
         w2_final = torch.empty((B, H, d, dh), dtype=torch.float32, device=q.device)
     _check_dev(q, k, v, w1, w2, eta_t, z, w1_final, w2_final, *(ln[:2] if ln else ()))
-    desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est)
+    desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, flags)
     if ln is None:
         st = lib().ttt_mlp_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(eta_t),
                                _ptr(z), _ptr(w1_final), _ptr(w2_final), _stream_handle(stream))
@@ -642,7 +650,38 @@ def _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream,
     return z, w1_final, w2_final
 
 
-def mlp_kernel_name(B, H, T, d, dh, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0)):
-    desc = mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, 0, eta_strides)
+def mlp_kernel_name(B, H, T, d, dh, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),
+                    primal: bool = False):
+    desc = mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_PRIMAL if primal else 0)
     name = lib().ttt_mlp_kernel_name(ctypes.byref(desc))
     return None if name is None else name.decode()
+
+
+def mlp_decode(q, k, v, eta, w1, w2, w1b, w2b, pos: int, b: int, out_dtype=None, z=None, stream=None):
+    """Continue B*H TTT-MLP sequences by T new tokens (primal form), state carried in place.
+
+    q, k, v : [B, H, T, d];  w1, w1b : [B, H, dh, d], w2, w2b : [B, H, d, dh]
+    float32 -- the state and the mini-batch-start state after ``pos`` tokens,
+    all updated in place.  eta : float, [H] or [B, H, T] (indexed by the new tokens).
+    returns Z [B, H, T, d].
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    dh = w1.shape[-2]
+    if (tuple(w1.shape) != (B, H, dh, d) or tuple(w1b.shape) != (B, H, dh, d) or
+            tuple(w2.shape) != (B, H, d, dh) or tuple(w2b.shape) != (B, H, d, dh)):
+        raise ValueError("w1, w1b must be [B, H, dh, d] and w2, w2b [B, H, d, dh]")
+    if any(x.dtype != torch.float32 for x in (w1, w2, w1b, w2b)):
+        raise TypeError("the states must be float32")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    _check_dev(q, k, v, eta_t, z, w1, w2, w1b, w2b)
+    desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), _dtype_code(z.dtype), 0, est)
+    st = lib().ttt_mlp_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(z), _ptr(w1),
+                              _ptr(w2), _ptr(w1b), _ptr(w2b), int(pos), _stream_handle(stream))
+    _done(st, "ttt_mlp_decode")
+    return z

@@ -318,7 +318,7 @@ ttt_status validate_mlp(const ttt_mlp_desc* d, const void* Q, const void* K, con
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->dh < 1 || d->b < 1) return TTT_ERR_SHAPE;
   if (d->T % d->b != 0) return TTT_ERR_SHAPE;
   if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
-  if (d->flags != 0 || d->reserved != 0) return TTT_ERR_FLAGS;
+  if ((d->flags & ~static_cast<uint32_t>(TTT_FLAG_PRIMAL)) != 0 || d->reserved != 0) return TTT_ERR_FLAGS;
   int64_t chains = 1, tok = 1, wel = 1;
   if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
   tok = chains;
@@ -329,7 +329,9 @@ ttt_status validate_mlp(const ttt_mlp_desc* d, const void* Q, const void* K, con
   if (d->w_batch_stride != 0 && d->w_batch_stride != hw) return TTT_ERR_STRIDE;
   if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
   ttt::MlpArgs a = make_mlp_args(d, Q, K, V, W1, W2, eta, Z, W1f, W2f);
-  if (!ttt::mlp_supported(a)) return TTT_ERR_UNSUPPORTED;
+  const bool supported =
+      (d->flags & TTT_FLAG_PRIMAL) ? ttt::mlp_primal_supported(d->d, d->dh) : ttt::mlp_supported(a);
+  if (!supported) return TTT_ERR_UNSUPPORTED;
   if (chains == 0) {
     if (ok_kernel) *ok_kernel = true;
     return TTT_OK;
@@ -785,9 +787,91 @@ ttt_status ttt_mlp_validate(const ttt_mlp_desc* desc, const void* Q, const void*
 
 const char* ttt_mlp_kernel_name(const ttt_mlp_desc* d) {
   if (!d) return nullptr;
+  if (d->flags & TTT_FLAG_PRIMAL) return ttt::mlp_primal_supported(d->d, d->dh) ? "ttt_mlp_primal_d64h256" : nullptr;
   ttt::MlpArgs a = make_mlp_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                  nullptr);
   return ttt::mlp_supported(a) ? ttt::mlp_name(a) : nullptr;
+}
+
+namespace {
+
+ttt::MlpPrimalArgs make_mlp_primal_args(const ttt_mlp_desc* d, const void* Q, const void* K, const void* V,
+                                        const float* eta, void* Z) {
+  ttt::MlpPrimalArgs a;
+  a.B = d->B; a.H = d->H; a.T = d->T; a.d = d->d; a.dh = d->dh; a.b = d->b;
+  a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype;
+  a.Q = Q; a.K = K; a.V = V;
+  a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
+  a.Z = Z;
+  a.W1_in = a.W2_in = a.W1b_in = a.W2b_in = nullptr;
+  a.W1_out = a.W2_out = a.W1b_out = a.W2b_out = nullptr;
+  a.w_in_bstride = 0;
+  a.pos = 0;
+  return a;
+}
+
+ttt_status validate_mlp_decode(const ttt_mlp_desc* d, const void* Q, const void* K, const void* V,
+                               const float* eta, const void* Z, const float* W1, const float* W2, const float* W1b,
+                               const float* W2b, int64_t pos) {
+  if (!d) return TTT_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->dh < 1 || d->b < 1) return TTT_ERR_SHAPE;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
+  if (d->flags != 0 || d->reserved != 0) return TTT_ERR_FLAGS;
+  if (pos < 0) return TTT_ERR_POS;
+  if (d->w_batch_stride != 0) return TTT_ERR_STRIDE;
+  if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
+  int64_t chains = 1, tok = 1, wel = 1;
+  if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
+  tok = chains;
+  if (!mul_ok(tok, d->T) || !mul_ok(tok, d->d)) return TTT_ERR_SHAPE;
+  wel = chains;
+  if (!mul_ok(wel, d->d) || !mul_ok(wel, d->dh)) return TTT_ERR_SHAPE;
+  if (!ttt::mlp_primal_supported(d->d, d->dh)) return TTT_ERR_UNSUPPORTED;
+  if (chains == 0) return TTT_OK;
+  if (!W1 || !W2 || !W1b || !W2b) return TTT_ERR_NULL;
+  if (tok > 0 && (!Q || !K || !V || !Z || !eta)) return TTT_ERR_NULL;
+  for (const float* p : {W1, W2, W1b, W2b})
+    if (!aligned(p, 16)) return TTT_ERR_ALIGN;
+  if (tok > 0 && (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(Z, 16) || !aligned(eta, 4)))
+    return TTT_ERR_ALIGN;
+  const int64_t in_b = tok * dtype_size(d->in_dtype);
+  const int64_t z_b = tok * dtype_size(d->out_dtype);
+  const int64_t w_b = wel * 4;
+  const int64_t eta_b =
+      tok > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const Range ins[] = {{Q, in_b}, {K, in_b}, {V, in_b}, {eta, eta_b}};
+  const Range outs[] = {{Z, z_b}, {W1, w_b}, {W2, w_b}, {W1b, w_b}, {W2b, w_b}};
+  for (int i = 0; i < 5; ++i) {
+    for (const Range& in : ins)
+      if (overlaps(outs[i], in)) return TTT_ERR_ALIAS;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_ALIAS;
+  }
+  return TTT_OK;
+}
+
+}  // namespace
+
+ttt_status ttt_mlp_decode_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                   const float* eta, const void* Z, const float* W1, const float* W2,
+                                   const float* W1b, const float* W2b, int64_t pos) {
+  return validate_mlp_decode(desc, Q, K, V, eta, Z, W1, W2, W1b, W2b, pos);
+}
+
+ttt_status ttt_mlp_decode(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* eta,
+                          void* Z, float* W1, float* W2, float* W1b, float* W2b, int64_t pos, void* stream) {
+  const ttt_status st = validate_mlp_decode(desc, Q, K, V, eta, Z, W1, W2, W1b, W2b, pos);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  ttt::MlpPrimalArgs a = make_mlp_primal_args(desc, Q, K, V, eta, Z);
+  a.W1_in = a.W1_out = W1;
+  a.W2_in = a.W2_out = W2;
+  a.W1b_in = a.W1b_out = W1b;
+  a.W2b_in = a.W2b_out = W2b;
+  a.w_in_bstride = static_cast<int64_t>(desc->H) * desc->d * desc->dh;
+  a.pos = pos;
+  const hipError_t e = ttt::launch_mlp_primal(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
 ttt_status ttt_mlp_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* W1_0,
@@ -797,6 +881,18 @@ ttt_status ttt_mlp_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, c
   const ttt_status st = validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, &ok);
   if (st != TTT_OK) return st;
   if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  if (desc->flags & TTT_FLAG_PRIMAL) {
+    // token by token from W0 (the first token starts a mini-batch, so no
+    // mini-batch-start state is read)
+    ttt::MlpPrimalArgs p = make_mlp_primal_args(desc, Q, K, V, eta, Z);
+    p.W1_in = p.W1b_in = W1_0;
+    p.W2_in = p.W2b_in = W2_0;
+    p.w_in_bstride = desc->w_batch_stride;
+    p.W1_out = W1_final;
+    p.W2_out = W2_final;
+    const hipError_t e = ttt::launch_mlp_primal(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+  }
   const ttt::MlpArgs a = make_mlp_args(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final);
   const hipError_t e = ttt::launch_mlp(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
@@ -808,6 +904,7 @@ ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K
   bool ok;
   const ttt_status st = validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, &ok);
   if (st != TTT_OK) return st;
+  if (desc->flags != 0) return TTT_ERR_FLAGS;  // no primal form with the layer norm
   if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   if (chains == 0) return TTT_OK;

@@ -136,6 +136,30 @@ hipError_t launch_linear_mfma_head_maps(const LinearArgs& a, hipStream_t s);
 // Chunk start states: Wstart of chunk c+1 = (that of chunk c) P_c + R_c, c = 1 .. nchunk-2.
 hipError_t launch_linear_chunk_scan(const LinearArgs& a, hipStream_t s);
 
+// TTT-MLP primal form (token by token): full forward and decode, d = 64, dh = 256.
+struct MlpPrimalArgs {
+  int B, H, T, d, dh, b;
+  int in_dtype, out_dtype;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* W1_in;   // state at position pos: W1 [dh][d], W2 [d][dh]
+  const float* W2_in;
+  const float* W1b_in;  // mini-batch-start state at position pos
+  const float* W2b_in;
+  int64_t w_in_bstride; // elements between sequences' input states (0: shared over B)
+  const float* eta;
+  int64_t esb, esh, est;
+  void* Z;
+  float* W1_out;        // [B, H, dh, d]
+  float* W2_out;        // [B, H, d, dh]
+  float* W1b_out;       // [B, H, dh, d] or nullptr
+  float* W2b_out;       // [B, H, d, dh] or nullptr
+  int64_t pos;          // tokens already processed
+};
+bool mlp_primal_supported(int d, int dh);
+hipError_t launch_mlp_primal(const MlpPrimalArgs& a, hipStream_t s);
+
 // TTT-MLP kernel: d = 64, dh = 256, b = 16, bf16 Q/K/V.
 bool mlp_supported(const MlpArgs& a);
 const char* mlp_name(const MlpArgs& a);

@@ -190,6 +190,54 @@ def test_mlp_validation():
     assert _mval(_mdesc(), f2=9 * GB + 8) == ALIGN
 
 
+def test_mlp_primal_flag_validation():
+    P = ttt.TTT_FLAG_PRIMAL
+
+    def d(T=64, dh=256, b=16, ind=1, outd=0, flags=P):
+        return ttt.mlp_desc(2, 4, T, 64, dh, b, ind, outd, 0, (0, 0, 0), flags)
+
+    assert _mval(d()) == OK
+    assert _mval(d(b=1)) == OK and _mval(d(b=64)) == OK       # any mini-batch size
+    assert _mval(d(ind=0, outd=1)) == OK                       # fp32 inputs, bf16 Z
+    assert _mval(d(T=40)) == SHAPE                              # T % b != 0
+    assert _mval(d(dh=128)) == UNSUP
+    assert _mval(d(flags=P | 1)) == FLAGS
+    assert ttt.mlp_kernel_name(2, 4, 64, 64, 256, 5, primal=True) == "ttt_mlp_primal_d64h256"
+    assert ttt.mlp_kernel_name(2, 4, 64, 64, 128, 16, primal=True) is None
+
+
+class MlpDecBufs:
+    NAMES = ("q", "k", "v", "eta", "z", "w1", "w2", "w1b", "w2b")
+
+    def __init__(self):
+        for i, n in enumerate(self.NAMES):
+            setattr(self, n, (i + 1) * GB)
+
+
+def _mdval(desc, pos=0, **over):
+    b = MlpDecBufs()
+    for k, v in over.items():
+        setattr(b, k, v)
+    return ttt.lib().ttt_mlp_decode_validate(ctypes.byref(desc), *(getattr(b, n) for n in MlpDecBufs.NAMES),
+                                             ctypes.c_int64(pos))
+
+
+def test_mlp_decode_validation():
+    assert _mdval(_mdesc(T=1)) == OK
+    assert _mdval(_mdesc(T=37, b=16, in_dtype=0, out_dtype=1, est=(4 * 37, 37, 1)), pos=5) == OK  # ragged T
+    assert ttt.lib().ttt_mlp_decode_validate(None, *(0,) * 9, ctypes.c_int64(0)) == NULL
+    for name in MlpDecBufs.NAMES:
+        assert _mdval(_mdesc(T=1), **{name: None}) == NULL, name
+    assert _mdval(_mdesc(T=1), pos=-1) == POS
+    assert _mdval(_mdesc(T=1, wstride=4 * 64 * 256)) == STRIDE
+    assert _mdval(_mdesc(T=1, dh=128)) == UNSUP
+    assert _mdval(_mdesc(T=1), w1b=6 * GB + 16) == ALIAS          # W1b inside W1
+    assert _mdval(_mdesc(T=1), z=2 * GB) == ALIAS                 # Z over K
+    assert _mdval(_mdesc(T=1), w2=7 * GB + 4) == ALIGN
+    assert _mdval(_mdesc(B=0, T=1)) == OK
+    assert _mdval(_mdesc(T=0), q=None, k=None, v=None, z=None, eta=None) == OK
+
+
 # ---- decode validation -------------------------------------------------------------
 
 def _dval(desc, pos=0, **over):

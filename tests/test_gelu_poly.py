@@ -1,5 +1,5 @@
-"""Accuracy of the TTT-MLP kernel's polynomial normal CDF (phi_poly in
-csrc/mlp.hip), read from the kernel source and evaluated in float32 the way
+"""Accuracy of the TTT-MLP kernels' polynomial normal CDF (phi_poly in
+csrc/gelu.h), read from the kernel source and evaluated in float32 the way
 the kernel does (Horner with fused multiply-adds), against scipy's exact CDF.
 The kernel takes this path only while every |x| in the wave is below sqrt 2;
 elsewhere it uses the library erff."""
@@ -12,7 +12,7 @@ import pytest
 scipy_special = pytest.importorskip("scipy.special")
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "test_sequence_layer_amd", "csrc", "mlp.hip")
+                   "test_sequence_layer_amd", "csrc", "gelu.h")
 
 
 def _coefficients():

@@ -99,6 +99,23 @@ def test_decode_matches_forward(ttt, cuts):
     assert max_rel(rows(z), rows(zf)) < 1e-4 and max_rel(rows(w), rows(wf)) < 1e-4
 
 
+def test_decode_batch_512(ttt):
+    """Generation at the pages' batch (512 sequences x 32 heads = 16,384 chains,
+    [TTT] 04 §3), one token per call with positions advancing over a mini-batch
+    boundary, against the oracle on sampled chains."""
+    cfg = ti.CONFIGS["l1p3b"].with_(B=512, H=32, T=20, seed=23)
+    inp = ti.generate(cfg)
+    t = to_device(inp)
+    w0 = t["w1"].unsqueeze(0).expand(cfg.B, -1, -1, -1).contiguous()
+    z, w = _decode_in_chunks(ttt, t, [1] * 20, 16, w0)
+    torch.cuda.synchronize()
+    ch = ti.sample_chains(cfg, 16)
+    zr, wr = _oracle(ti.generate(cfg, chains=ch))
+    ez, ew = max_rel(rows(z, ch), zr), max_rel(rows(w, ch), wr)
+    print(f"decode batch 512: vs oracle Z {ez:.3e} W {ew:.3e}", flush=True)
+    assert ez < 1e-5 and ew < 1e-5
+
+
 def test_decode_ragged_length(ttt):
     """37 tokens with b = 16: the last mini-batch is short (the oracle's reading of a
     ragged tail); the dual-form forward rejects T % b != 0, decode does not."""
