@@ -440,13 +440,13 @@ def main():
 
             def bwd():
                 ttt.linear_ln_bwd(t["q"], t["k"], t["v"], t["eta"], gam, bet, wf, dl_sv, dz, cfg.b, dw_final=dwf,
-                                  out=gout)
+                                  out=gout, generic=args.generic)
 
             if args.save:
                 kname = "ttt_linear_mfma_d64b16 (layer norm)"
                 step = fwd_save
             elif args.bwd:
-                kname = ttt.linear_ln_bwd_kernel_name(B, H, T, d, cfg.b, 1, 0, inp.eta_strides)
+                kname = ttt.linear_ln_bwd_kernel_name(B, H, T, d, cfg.b, 1, 0, inp.eta_strides, args.generic)
                 step = bwd
             else:
                 def step():

@@ -219,9 +219,10 @@ ttt_status ttt_linear_ln_fwd_save(const ttt_linear_desc* desc, const void* Q, co
  * (W = W' - sum_t g_t k_t^T); everything else the backward needs (delta,
  * both layer norms and their statistics) is recomputed from the inputs.
  * Outputs overlap no input and no other output (TTT_ERR_ALIAS).
- * Supported: d = 64, b = 16, bf16 inputs, flags = 0 (else TTT_ERR_UNSUPPORTED),
- * on one fp32 kernel (ttt_linear_ln_bwd_fp32, one workgroup per sequence and
- * head).  eps must be finite and >= 0 (TTT_ERR_SHAPE); other errors as for
+ * Supported: d = 64, b = 16, bf16 inputs; flags 0 (the matrix-core kernel
+ * ttt_linear_ln_bwd_d64b16) or TTT_FLAG_GENERIC (the fp32 kernel
+ * ttt_linear_ln_bwd_fp32, the cross-check); anything else TTT_ERR_UNSUPPORTED.
+ * eps must be finite and >= 0 (TTT_ERR_SHAPE); other errors as for
  * ttt_linear_bwd.
  */
 ttt_status ttt_linear_ln_bwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,

@@ -499,7 +499,7 @@ def linear_ln_fwd(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, out_
 
 
 def linear_ln_bwd(q, k, v, eta, gamma, beta, w_final, g_saved, dz, b: int, eps: float = 1e-6,
-                  dw_final=None, out=None, stream=None):
+                  dw_final=None, out=None, stream=None, generic: bool = False):
     """Backward of :func:`linear_ln_fwd`.
 
     q, k, v, eta, gamma, beta, eps : as given to the forward
@@ -507,6 +507,7 @@ def linear_ln_bwd(q, k, v, eta, gamma, beta, w_final, g_saved, dz, b: int, eps: 
     dz       : [B, H, T, d] gradient with respect to Z (its dtype is that of dq, dk, dv)
     dw_final : [B, H, d, d] float32 gradient with respect to W_final, or None (zero)
     out      : optional (dq, dk, dv, deta, dw0, dgamma, dbeta) preallocated outputs
+    generic  : run the fp32 kernel (the cross-check) instead of the matrix-core one
     returns (dq, dk, dv, deta [B, H, T], dw0 [B, H, d, d], dgamma [B, H, d], dbeta [B, H, d]),
     the last three per sequence.
     """
@@ -534,7 +535,8 @@ def linear_ln_bwd(q, k, v, eta, gamma, beta, w_final, g_saved, dz, b: int, eps: 
                torch.empty((B, H, d), dtype=torch.float32, device=dev))
     dq, dk, dv, deta, dw0, dgamma, dbeta = out
     _check_dev(q, k, v, eta_t, gamma, beta, w_final, g_saved, dz, dw_final, *out)
-    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(dz.dtype), 0, est, 0)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(dz.dtype), 0, est,
+                       TTT_FLAG_GENERIC if generic else 0)
     st = lib().ttt_linear_ln_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(gamma),
                                  _ptr(beta), float(eps), _ptr(w_final), _ptr(g_saved), _ptr(dz),
                                  _ptr(dw_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0),
@@ -544,8 +546,8 @@ def linear_ln_bwd(q, k, v, eta, gamma, beta, w_final, g_saved, dz, b: int, eps: 
 
 
 def linear_ln_bwd_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32,
-                              eta_strides=(0, 0, 0)) -> Optional[str]:
-    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, 0)
+                              eta_strides=(0, 0, 0), generic: bool = False) -> Optional[str]:
+    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_GENERIC if generic else 0)
     name = lib().ttt_linear_ln_bwd_kernel_name(ctypes.byref(desc))
     return None if name is None else name.decode()
 

@@ -581,7 +581,8 @@ ttt_status validate_ln_bwd(const ttt_linear_desc* d, const void* Q, const void* 
   const ttt_status st = validate_bwd(d, Q, K, eta, Wf, Ds, dZ, dWf, dQ, dK, dV, deta, dW0, &k);
   if (st != TTT_OK) return st;
   ttt::BwdArgs a = make_bwd_args(d, Q, K, eta, Wf, Ds, dZ, dWf, nullptr, nullptr, nullptr, nullptr, nullptr);
-  if (d->flags != 0 || !ttt::linear_ln_bwd_supported(a)) return TTT_ERR_UNSUPPORTED;
+  if ((d->flags & ~static_cast<uint32_t>(TTT_FLAG_GENERIC)) != 0 || !ttt::linear_ln_bwd_supported(a))
+    return TTT_ERR_UNSUPPORTED;
   if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
   const int64_t chains = static_cast<int64_t>(d->B) * d->H;
   if (chains == 0) return TTT_OK;
@@ -619,10 +620,11 @@ ttt_status ttt_linear_ln_bwd_validate(const ttt_linear_desc* desc, const void* Q
 }
 
 const char* ttt_linear_ln_bwd_kernel_name(const ttt_linear_desc* d) {
-  if (!d || d->flags != 0) return nullptr;
+  if (!d || (d->flags & ~static_cast<uint32_t>(TTT_FLAG_GENERIC)) != 0) return nullptr;
   const ttt::BwdArgs a = make_bwd_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                        nullptr, nullptr, nullptr, nullptr);
-  return ttt::linear_ln_bwd_supported(a) ? "ttt_linear_ln_bwd_fp32" : nullptr;
+  if (!ttt::linear_ln_bwd_supported(a)) return nullptr;
+  return (d->flags & TTT_FLAG_GENERIC) ? "ttt_linear_ln_bwd_fp32" : "ttt_linear_ln_bwd_d64b16";
 }
 
 ttt_status ttt_linear_ln_bwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
@@ -642,7 +644,9 @@ ttt_status ttt_linear_ln_bwd(const ttt_linear_desc* desc, const void* Q, const v
   a.eps = eps;
   a.dgamma = dgamma;
   a.dbeta = dbeta;
-  const hipError_t e = ttt::launch_linear_ln_bwd(a, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      (desc->flags & TTT_FLAG_GENERIC) ? ttt::launch_linear_ln_bwd(a, s) : ttt::launch_linear_ln_bwd_mfma(a, s);
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

@@ -71,65 +71,6 @@ struct __align__(16) BSlot {
 };
 static_assert(sizeof(BSlot) % 16 == 0, "slot size");
 
-// dZ tile loads: 4 elements per thread per mini-batch, widened to fp32
-template <typename GT>
-struct GradLoad;
-template <>
-struct GradLoad<float> {
-  typedef u32x4 type;
-  __device__ static void get(type x, float v[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(x[i]);
-  }
-};
-template <>
-struct GradLoad<uint16_t> {
-  typedef u32x2 type;
-  __device__ static void get(type x, float v[4]) {
-    v[0] = __uint_as_float(x[0] << 16);
-    v[1] = __uint_as_float(x[0] & 0xffff0000u);
-    v[2] = __uint_as_float(x[1] << 16);
-    v[3] = __uint_as_float(x[1] & 0xffff0000u);
-  }
-};
-
-__device__ __forceinline__ float4v zero4v() { return float4v{0.f, 0.f, 0.f, 0.f}; }
-
-// Raw bits of element r of a bf16x4, taken from its two 32-bit words.  (Stores
-// of bit-cast __bf16 vector elements were compiled as stores of element 0 for
-// every r; the word arithmetic avoids that path.)
-__device__ __forceinline__ uint16_t bf16_bits(bf16x4 x, int r) {
-  const u32x2 w = __builtin_bit_cast(u32x2, x);
-  const uint32_t v = w[r >> 1];
-  return static_cast<uint16_t>((r & 1) ? (v >> 16) : (v & 0xffffu));
-}
-
-__device__ __forceinline__ void put4(uint16_t* tile, int off, bf16x4 x) {
-  *reinterpret_cast<bf16x4*>(tile + off) = x;
-}
-
-// Row li of a bf16 tile in the row-contraction order: block b holds columns
-// 16b + 4g .. 16b + 4g + 3 (the order of an F2 state's rows).
-__device__ __forceinline__ void rows4(const uint16_t* tile, int li, int g, bf16x4 x[4]) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) x[b] = *reinterpret_cast<const bf16x4*>(tile + li * ROW + 16 * b + 4 * g);
-}
-
-// 64-deep contraction over the rows of an F2 state: acc += X[m = li][:] . F2[:][n = li]
-// with X given as split rows (rows4) and the state tiles pre-split; three passes.
-__device__ __forceinline__ float4v rows_x_f2(const bf16x4 xh[4], const bf16x4 xl[4], const bf16x4 sh[4],
-                                             const bf16x4 sl[4], float4v acc) {
-#pragma unroll
-  for (int p = 0; p < 4; p += 2) {
-    const bf16x8 ah = cat(xh[p], xh[p + 1]), al = cat(xl[p], xl[p + 1]);
-    const bf16x8 bh = cat(sh[p], sh[p + 1]), bl = cat(sl[p], sl[p + 1]);
-    acc = mfma32(ah, bh, acc);
-    acc = mfma32(ah, bl, acc);
-    acc = mfma32(al, bh, acc);
-  }
-  return acc;
-}
-
 template <int PF, bool ETA_TOKEN, typename GT>
 __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
   static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
@@ -290,10 +231,10 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
 
     // ---- Y = E dZ^T (s = 4g+r, t = li), contraction over all 64 outputs ----
     bf16x4 erh[4], erl[4], zrh[4], zrl[4];
-    rows4(S.eh, li, g, erh);
-    rows4(S.el, li, g, erl);
-    rows4(S.zh, li, g, zrh);
-    rows4(S.zl, li, g, zrl);
+    rows4<ROW>(S.eh, li, g, erh);
+    rows4<ROW>(S.el, li, g, erl);
+    rows4<ROW>(S.zh, li, g, zrh);
+    rows4<ROW>(S.zl, li, g, zrl);
     const float4v y = rows_x_f2(erh, erl, zrh, zrl, zero4v());
 
     // ---- dE = -2 dZ M^T - 2 P diag(eta), rows i of this wave ----
@@ -399,8 +340,8 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
     // ---- dK += dE W ----
     {
       bf16x4 drh[4], drl[4];
-      rows4(deh, li, g, drh);
-      rows4(del, li, g, drl);
+      rows4<ROW>(deh, li, g, drh);
+      rows4<ROW>(del, li, g, drl);
       dk = rows_x_f2(drh, drl, wh, wl, dk);
     }
 

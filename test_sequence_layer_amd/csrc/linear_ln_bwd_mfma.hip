@@ -1,0 +1,525 @@
+// TTT-Linear backward with layer norm and residual inside f, on CDNA4 matrix
+// cores: d = 64, b = 16, bf16 Q/K/V.
+//
+// Pages: [TTT] = news article "大模型最强架构TTT问世！斯坦福UCSD等5年磨一剑，一夜推翻Transformer"
+// (aharts.cn / itmax.cn), part 03 §4 (the layer is trained end to end), §7
+// (the dual form serves the backward too), §9 (f(x) = x + LN(W x)).
+//
+// The forward of one mini-batch (token-major rows; W the mini-batch-start
+// state, W row i = output i; G_s = -eta_s delta_s the update factor the
+// forward saved, exactly as it applied it):
+//   y_s = W k_s,  u_t = W q_t + sum_{s <= t} S[s][t] G_s,  S = K Q^T,
+//   z_t = q_t + gamma uh_t + beta,   W' = W + sum_s G_s k_s^T.
+// Its backward, given dz and A = dL/dW' (the same steps as the fp32 kernel,
+// ttt_linear_ln_bwd_fp32):
+//   W  = W' - G^T K                                         (the state rebuilt)
+//   du_t = LNback_u(gamma dz_t);  dS[s][t] = G_s . du_t (s <= t)
+//   dG_s = P_s + sum_{t >= s} S[s][t] du_t,  P = K A^T;  lambda_s = -eta_s dG_s
+//   delta_s recomputed from y_s;  deta_s = -delta_s . dG_s
+//   dg, dy: the layer norm's double backward of lambda;  dv = -2 gamma dg
+//   dQ = dZ + dU W + dS'^T K;  dK = dY W + G A + dS' Q + 2 gamma dg   (dS' masked)
+//   A <- A + dU^T Q + dY^T K
+//
+// Work decomposition (one 256-thread workgroup per (sequence, head), the
+// mini-batches last to first, as the plain backward): W and A are each held
+// in both MFMA layouts, F1 (wave w owns rows 16w..16w+15; the B operand of a
+// contraction over W's columns: W K, W Q, A K) and F2 (wave w owns columns
+// 16w..16w+15; the B operand of a contraction over its rows: dU W, dY W,
+// G A).  Both copies of W are rebuilt by subtracting exactly the split
+// operands the forward added.  The layer norms' per-token statistics need all
+// 64 outputs of a token, so Y = W K, U and P = K A^T cross once through LDS
+// into a token layout (lane: token 4w + l/16, outputs 4(l%16) .. +3; a token's
+// sums are 16-lane DPP row sums), where delta, du, lambda, dg and dy are
+// formed in fp32; du and dy come back through LDS as bf16 hi/lo tiles for the
+// matrix cores.  Four barriers per mini-batch.
+//
+// Precision: fp32 operands enter the matrix cores as hi + lo pairs (products
+// of two fp32 operands: three passes; with a bf16 input: two), the layer-norm
+// arithmetic is fp32, and the state rebuild undoes the forward's own steps.
+#include "mfma_common.h"
+
+namespace ttt {
+namespace {
+
+using namespace mfma;
+
+constexpr int D = 64;
+constexpr int BT = 16;
+constexpr int ROW = 68;  // padded LDS row of a bf16 token tile (elements)
+constexpr int ZR = 68;   // padded LDS row of an fp32 token tile (floats, 16-byte multiple)
+constexpr int kThreads = 256;
+
+typedef uint16_t Tile[BT * ROW];
+typedef float FTile[BT * ZR];
+
+struct __align__(16) LSlot {
+  Tile q, k, v;  // inputs (bf16)
+  Tile gh, gl;   // G, split
+  FTile dz;      // dZ (fp32)
+  float eta[BT];
+};
+static_assert(sizeof(LSlot) % 16 == 0, "slot size");
+
+__device__ __forceinline__ bf16x4 neg4(bf16x4 x) {
+  return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, x) ^ u32x2{0x80008000u, 0x80008000u});
+}
+
+__device__ __forceinline__ float4 bf16x4_to_f4(const uint16_t* p) {
+  const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+  return make_float4(__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u), __uint_as_float(x[1] << 16),
+                     __uint_as_float(x[1] & 0xffff0000u));
+}
+
+__device__ __forceinline__ float sum4(float4 x) { return (x.x + x.y) + (x.z + x.w); }
+
+template <typename GT>
+__device__ __forceinline__ void store4(GT* p, float4 x);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 x) {
+  *reinterpret_cast<float4*>(p) = x;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float4 x) {
+  *reinterpret_cast<u32x2*>(p) =
+      u32x2{static_cast<uint32_t>(f32_to_bf16_bits(x.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.y)) << 16),
+            static_cast<uint32_t>(f32_to_bf16_bits(x.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.w)) << 16)};
+}
+
+template <int PF, bool ETA_TOKEN, typename GT>
+__global__ __launch_bounds__(kThreads) void ttt_linear_ln_bwd_d64b16(BwdArgs a) {
+  static_assert(PF >= 2, "a step stages its successor before it issues its own prefetch");
+  __shared__ LSlot slots[2];
+  __shared__ __align__(16) FTile yk;    // W k, [token][output]
+  __shared__ __align__(16) FTile yq;    // u
+  __shared__ __align__(16) FTile pk;    // P = K A^T
+  __shared__ __align__(16) FTile du32;  // du (fp32)
+  __shared__ __align__(16) FTile dgt;   // dg (fp32)
+  __shared__ __align__(16) Tile duh, dul, dyh, dyl;
+  __shared__ float sS[BT][BT + 1];      // S = K Q^T
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int li = lane & 15;
+  const int g = lane >> 4;
+  const int tk = 4 * w + g;  // the token this lane takes in the token layout
+
+  const int chain = blockIdx.x;
+  const int bi = chain / a.H;
+  const int h = chain - bi * a.H;
+  const int nb = a.T / BT;
+  const size_t tok0 = static_cast<size_t>(chain) * a.T;
+
+  typedef typename GradLoad<GT>::type GLoad;
+  const u32x4* Qg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.Q) + tok0 * D);
+  const u32x4* Kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.K) + tok0 * D);
+  const u32x2* Vg = reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.V) + tok0 * D);
+  const u32x4* Gg = reinterpret_cast<const u32x4*>(a.E + tok0 * D);
+  const GLoad* Zg = reinterpret_cast<const GLoad*>(static_cast<const GT*>(a.dZ) + tok0 * D);
+  GT* dQg = static_cast<GT*>(a.dQ) + tok0 * D;
+  GT* dKg = static_cast<GT*>(a.dK) + tok0 * D;
+  GT* dVg = static_cast<GT*>(a.dV) + tok0 * D;
+  float* detag = a.deta + tok0;
+  const float* eg = a.eta + bi * a.esb + h * a.esh;
+
+  // staging roles: 16 B of Q (tid < 128) or K (tid >= 128) at row srow,
+  // columns scol..scol+7; 4 values of V, G and dZ at row frow = tid / 16,
+  // columns fcol..fcol+3; the step size of token frow
+  const int within = tid & 127;
+  const u32x4* srcA = (tid < 128 ? Qg : Kg) + within;
+  const u32x2* srcV = Vg + tid;
+  const u32x4* srcG = Gg + tid;
+  const GLoad* srcZ = Zg + tid;
+  const int srow = within >> 3;
+  const int scol = (within & 7) * 8;
+  const int frow = tid >> 4;
+  const int fcol = (tid & 15) * 4;
+  const float* srcEta = eg + static_cast<int64_t>(frow) * a.est;
+
+  u32x4 ra[PF], rg[PF];
+  u32x2 rv[PF];
+  GLoad rz[PF];
+  float rt[PF];
+
+  float eta_c = 0.f;
+  if (!ETA_TOKEN && nb > 0) eta_c = eg[0];
+
+  auto load_step = [&](int n, u32x4& xa, u32x2& xv, u32x4& xg, GLoad& xz, float& xt) {
+    xa = ld_stream(srcA + static_cast<size_t>(n) * (BT * D / 8));
+    xv = ld_stream(srcV + static_cast<size_t>(n) * (BT * D / 4));
+    xg = ld_stream(srcG + static_cast<size_t>(n) * (BT * D / 4));
+    xz = ld_stream(srcZ + static_cast<size_t>(n) * (BT * D / 4));
+    xt = ETA_TOKEN ? srcEta[static_cast<int64_t>(n) * BT * a.est] : 0.f;
+  };
+  auto stage = [&](int slot, const u32x4& xa, const u32x2& xv, const u32x4& xg, const GLoad& xz, float xt) {
+    LSlot& S = slots[slot];
+    {
+      u32x2* dst = reinterpret_cast<u32x2*>(tid < 128 ? &S.q[srow * ROW + scol] : &S.k[srow * ROW + scol]);
+      dst[0] = u32x2{xa[0], xa[1]};
+      dst[1] = u32x2{xa[2], xa[3]};
+    }
+    const int off = frow * ROW + fcol;
+    *reinterpret_cast<u32x2*>(&S.v[off]) = xv;
+    float gv[4], z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gv[i] = __uint_as_float(xg[i]);
+    bf16x4 hi, lo;
+    split4(gv, hi, lo);
+    put4(S.gh, off, hi);
+    put4(S.gl, off, lo);
+    GradLoad<GT>::get(xz, z);
+    *reinterpret_cast<float4*>(&S.dz[frow * ZR + fcol]) = make_float4(z[0], z[1], z[2], z[3]);
+    if (ETA_TOKEN && (tid & 15) == 0) S.eta[frow] = xt;
+  };
+
+  // state: W (F1 and F2) from the final state, A (F1 and F2) from dL/dW_final
+  float4v w1[4], w2[4], a1[4], a2[4];
+  {
+    const float* wf = a.Wf + static_cast<int64_t>(chain) * D * D;
+    const float* af = a.dWf ? a.dWf + static_cast<int64_t>(chain) * D * D : nullptr;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int o = (16 * b + 4 * g + r) * D + 16 * w + li;
+        w2[b][r] = wf[o];
+        a2[b][r] = af ? af[o] : 0.f;
+      }
+      const float4 x = *reinterpret_cast<const float4*>(wf + (16 * w + li) * D + 16 * b + 4 * g);
+      w1[b] = float4v{x.x, x.y, x.z, x.w};
+      if (af) {
+        const float4 y = *reinterpret_cast<const float4*>(af + (16 * w + li) * D + 16 * b + 4 * g);
+        a1[b] = float4v{y.x, y.y, y.z, y.w};
+      } else {
+        a1[b] = zero4v();
+      }
+    }
+  }
+  // layer-norm parameters: outputs 4 li .. 4 li + 3 (token layout) and 16 w + li
+  // (column-owned outputs of dK)
+  float4 gam4, bet4;
+  gam4.x = a.gamma[h * D + 4 * li];
+  gam4.y = a.gamma[h * D + 4 * li + 1];
+  gam4.z = a.gamma[h * D + 4 * li + 2];
+  gam4.w = a.gamma[h * D + 4 * li + 3];
+  bet4.x = a.beta[h * D + 4 * li];
+  bet4.y = a.beta[h * D + 4 * li + 1];
+  bet4.z = a.beta[h * D + 4 * li + 2];
+  bet4.w = a.beta[h * D + 4 * li + 3];
+  const float gam_c = a.gamma[h * D + 16 * w + li];
+  const float eps = a.eps;
+  float4 dgam = make_float4(0.f, 0.f, 0.f, 0.f), dbet = dgam;
+
+  bf16x8 ident;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ident[j] = (4 * g + (j & 3) == li) ? static_cast<__bf16>(1.f) : static_cast<__bf16>(0.f);
+
+#pragma unroll
+  for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(w1[t]), "+v"(a1[t]));
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the state loads retired before the ring prologue
+
+  if (nb > 0) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load_step(max(nb - 1 - j, 0), ra[j], rv[j], rg[j], rz[j], rt[j]);
+    stage(0, ra[0], rv[0], rg[0], rz[0], rt[0]);
+  }
+  __syncthreads();
+
+  auto step = [&](const int j, u32x4& xa, u32x2& xv, u32x4& xg, GLoad& xz, float& xt, const u32x4& ya,
+                  const u32x2& yv, const u32x4& yg, const GLoad& yz, const float yt) {
+    const int n = nb - 1 - j;
+    stage((j + 1) & 1, ya, yv, yg, yz, yt);
+    load_step(max(n - PF, 0), xa, xv, xg, xz, xt);
+    const LSlot& S = slots[j & 1];
+
+    // ================= phase 1: matrix cores, per wave =================
+    bf16x4 kx[4], qx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      kx[t] = *reinterpret_cast<const bf16x4*>(&S.k[li * ROW + 16 * t + 4 * g]);
+      qx[t] = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * t + 4 * g]);
+    }
+    const bf16x4 kw = read_cols<ROW>(S.k, 0, 16 * w, li, g);    // K[4g + r][16w + li]
+    const bf16x4 qw = read_cols<ROW>(S.q, 0, 16 * w, li, g);    // Q[4g + r][16w + li]
+    const bf16x4 gwh = read_cols<ROW>(S.gh, 0, 16 * w, li, g);  // G[4g + r][16w + li]
+    const bf16x4 gwl = read_cols<ROW>(S.gl, 0, 16 * w, li, g);
+
+    // ---- rebuild the mini-batch-start state in both layouts: W -= G^T K ----
+    {
+      const bf16x8 ngw = cat(neg4(gwh), neg4(gwl));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x4 kt = read_cols<ROW>(S.k, 0, 16 * t, li, g);  // K[4g + r][16t + li]
+        w1[t] = mfma32(cat(kt, kt), ngw, w1[t]);
+        const bf16x4 gbh = read_cols<ROW>(S.gh, 0, 16 * t, li, g);
+        const bf16x4 gbl = read_cols<ROW>(S.gl, 0, 16 * t, li, g);
+        w2[t] = mfma32(cat(neg4(gbh), neg4(gbl)), cat(kw, kw), w2[t]);
+      }
+    }
+
+    // ---- S = K Q^T (s = 4g+r, t = li) and S^T; y = W k, W q, P = A k (rows of this wave) ----
+    float4v sc = zero4v(), st = zero4v(), y = zero4v(), u = zero4v(), p = zero4v();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
+      const bf16x8 aq = cat(qx[2 * m], qx[2 * m + 1]);
+      sc = mfma32(ak, aq, sc);
+      st = mfma32(aq, ak, st);
+      bf16x4 h0, l0, h1, l1;
+      split4(w1[2 * m], h0, l0);
+      split4(w1[2 * m + 1], h1, l1);
+      const bf16x8 whi = cat(h0, h1), wlo = cat(l0, l1);
+      y = mfma32(ak, whi, y);
+      y = mfma32(ak, wlo, y);
+      u = mfma32(aq, whi, u);
+      u = mfma32(aq, wlo, u);
+      split4(a1[2 * m], h0, l0);
+      split4(a1[2 * m + 1], h1, l1);
+      p = mfma32(ak, cat(h0, h1), p);
+      p = mfma32(ak, cat(l0, l1), p);
+    }
+    // ---- u += M G, M[t][s] = S[s][t] (s <= t) ----
+    {
+      float mv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mv[r] = (4 * g + r <= li) ? sc[r] : 0.f;
+      bf16x4 mh, ml;
+      split4(mv, mh, ml);
+      const bf16x8 gz = cat(gwh, gwl);
+      u = mfma32(cat(mh, mh), gz, u);
+      u = mfma32(cat(ml, ml), gz, u);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = (4 * g + r) * ZR + 16 * w + li;
+      yk[o] = y[r];
+      yq[o] = u[r];
+      pk[o] = p[r];
+    }
+    if (w == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sS[4 * g + r][li] = sc[r];
+    }
+    __syncthreads();  // B1: y, u, P, S in LDS
+
+    // ================= phase 2: token layout =================
+    const float inv_d = 1.f / D;
+    const float4 k4 = bf16x4_to_f4(&S.k[tk * ROW + 4 * li]);
+    const float4 v4 = bf16x4_to_f4(&S.v[tk * ROW + 4 * li]);
+    float4 yh, res, dl;
+    float rsy, cg;
+    {
+      const float4 y4 = *reinterpret_cast<const float4*>(&yk[tk * ZR + 4 * li]);
+      const float my = sum16(sum4(y4)) * inv_d;
+      const float4 yc = make_float4(y4.x - my, y4.y - my, y4.z - my, y4.w - my);
+      rsy = rsqrtf(sum16(yc.x * yc.x + yc.y * yc.y + yc.z * yc.z + yc.w * yc.w) * inv_d + eps);
+      yh = make_float4(yc.x * rsy, yc.y * rsy, yc.z * rsy, yc.w * rsy);
+      res = make_float4(k4.x + gam4.x * yh.x + bet4.x - v4.x, k4.y + gam4.y * yh.y + bet4.y - v4.y,
+                        k4.z + gam4.z * yh.z + bet4.z - v4.z, k4.w + gam4.w * yh.w + bet4.w - v4.w);
+      const float4 gg = make_float4(2.f * gam4.x * res.x, 2.f * gam4.y * res.y, 2.f * gam4.z * res.z,
+                                    2.f * gam4.w * res.w);
+      const float mg = sum16(sum4(gg)) * inv_d;
+      cg = sum16(gg.x * yh.x + gg.y * yh.y + gg.z * yh.z + gg.w * yh.w) * inv_d;
+      dl = make_float4(rsy * (gg.x - mg - yh.x * cg), rsy * (gg.y - mg - yh.y * cg), rsy * (gg.z - mg - yh.z * cg),
+                       rsy * (gg.w - mg - yh.w * cg));
+    }
+    {
+      const float4 u4 = *reinterpret_cast<const float4*>(&yq[tk * ZR + 4 * li]);
+      const float mu = sum16(sum4(u4)) * inv_d;
+      const float4 uc = make_float4(u4.x - mu, u4.y - mu, u4.z - mu, u4.w - mu);
+      const float rsu = rsqrtf(sum16(uc.x * uc.x + uc.y * uc.y + uc.z * uc.z + uc.w * uc.w) * inv_d + eps);
+      const float4 uh = make_float4(uc.x * rsu, uc.y * rsu, uc.z * rsu, uc.w * rsu);
+      const float4 dz4 = *reinterpret_cast<const float4*>(&S.dz[tk * ZR + 4 * li]);
+      const float4 hh = make_float4(gam4.x * dz4.x, gam4.y * dz4.y, gam4.z * dz4.z, gam4.w * dz4.w);
+      const float mh = sum16(sum4(hh)) * inv_d;
+      const float mhu = sum16(hh.x * uh.x + hh.y * uh.y + hh.z * uh.z + hh.w * uh.w) * inv_d;
+      const float du[4] = {rsu * (hh.x - mh - uh.x * mhu), rsu * (hh.y - mh - uh.y * mhu),
+                           rsu * (hh.z - mh - uh.z * mhu), rsu * (hh.w - mh - uh.w * mhu)};
+      dgam = make_float4(fmaf(dz4.x, uh.x, dgam.x), fmaf(dz4.y, uh.y, dgam.y), fmaf(dz4.z, uh.z, dgam.z),
+                         fmaf(dz4.w, uh.w, dgam.w));
+      dbet = make_float4(dbet.x + dz4.x, dbet.y + dz4.y, dbet.z + dz4.z, dbet.w + dz4.w);
+      *reinterpret_cast<float4*>(&du32[tk * ZR + 4 * li]) = make_float4(du[0], du[1], du[2], du[3]);
+      bf16x4 hi, lo;
+      split4(du, hi, lo);
+      put4(duh, tk * ROW + 4 * li, hi);
+      put4(dul, tk * ROW + 4 * li, lo);
+    }
+    __syncthreads();  // B2: du in LDS
+
+    // ================= phase 3: token layout, then matrix cores =================
+    {
+      const float4 p4 = *reinterpret_cast<const float4*>(&pk[tk * ZR + 4 * li]);
+      float4 acc = p4;  // dG of token tk
+#pragma unroll
+      for (int t = 0; t < BT; ++t) {
+        const float sv = t >= tk ? sS[tk][t] : 0.f;  // S[s][t], t >= s
+        const float4 d4 = *reinterpret_cast<const float4*>(&du32[t * ZR + 4 * li]);
+        acc = make_float4(fmaf(sv, d4.x, acc.x), fmaf(sv, d4.y, acc.y), fmaf(sv, d4.z, acc.z),
+                          fmaf(sv, d4.w, acc.w));
+      }
+      const float et = ETA_TOKEN ? S.eta[tk] : eta_c;
+      const float de = sum16(dl.x * acc.x + dl.y * acc.y + dl.z * acc.z + dl.w * acc.w);
+      if (li == 0) detag[n * BT + tk] = -de;
+      const float4 lam = make_float4(-et * acc.x, -et * acc.y, -et * acc.z, -et * acc.w);
+      const float ml = sum16(sum4(lam)) * inv_d;
+      const float mly = sum16(lam.x * yh.x + lam.y * yh.y + lam.z * yh.z + lam.w * yh.w) * inv_d;
+      const float mld = sum16(lam.x * dl.x + lam.y * dl.y + lam.z * dl.z + lam.w * dl.w) * inv_d;
+      const float4 dg = make_float4(rsy * (lam.x - ml - yh.x * mly), rsy * (lam.y - ml - yh.y * mly),
+                                    rsy * (lam.z - ml - yh.z * mly), rsy * (lam.w - ml - yh.w * mly));
+      const float4 h2 = make_float4(2.f * gam4.x * gam4.x * dg.x, 2.f * gam4.y * gam4.y * dg.y,
+                                    2.f * gam4.z * gam4.z * dg.z, 2.f * gam4.w * gam4.w * dg.w);
+      const float mh2 = sum16(sum4(h2)) * inv_d;
+      const float mh2y = sum16(h2.x * yh.x + h2.y * yh.y + h2.z * yh.z + h2.w * yh.w) * inv_d;
+      const float dy[4] = {
+          -cg * rsy * dg.x - rsy * (mly * dl.x + mld * yh.x) + rsy * (h2.x - mh2 - yh.x * mh2y),
+          -cg * rsy * dg.y - rsy * (mly * dl.y + mld * yh.y) + rsy * (h2.y - mh2 - yh.y * mh2y),
+          -cg * rsy * dg.z - rsy * (mly * dl.z + mld * yh.z) + rsy * (h2.z - mh2 - yh.z * mh2y),
+          -cg * rsy * dg.w - rsy * (mly * dl.w + mld * yh.w) + rsy * (h2.w - mh2 - yh.w * mh2y)};
+      store4<GT>(dVg + (static_cast<size_t>(n) * BT + tk) * D + 4 * li,
+                 make_float4(-2.f * gam4.x * dg.x, -2.f * gam4.y * dg.y, -2.f * gam4.z * dg.z, -2.f * gam4.w * dg.w));
+      dgam = make_float4(fmaf(2.f * dg.x, res.x + gam4.x * yh.x, dgam.x), fmaf(2.f * dg.y, res.y + gam4.y * yh.y, dgam.y),
+                         fmaf(2.f * dg.z, res.z + gam4.z * yh.z, dgam.z), fmaf(2.f * dg.w, res.w + gam4.w * yh.w, dgam.w));
+      dbet = make_float4(fmaf(2.f * gam4.x, dg.x, dbet.x), fmaf(2.f * gam4.y, dg.y, dbet.y),
+                         fmaf(2.f * gam4.z, dg.z, dbet.z), fmaf(2.f * gam4.w, dg.w, dbet.w));
+      *reinterpret_cast<float4*>(&dgt[tk * ZR + 4 * li]) = dg;
+      bf16x4 hi, lo;
+      split4(dy, hi, lo);
+      put4(dyh, tk * ROW + 4 * li, hi);
+      put4(dyl, tk * ROW + 4 * li, lo);
+    }
+
+    // the state tiles split once for the row contractions (W: F2, the rebuilt state)
+    bf16x4 wh[4], wl[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) split4(w2[b], wh[b], wl[b]);
+    bf16x4 grh[4], grl[4], durh[4], durl[4];
+    rows4<ROW>(S.gh, li, g, grh);
+    rows4<ROW>(S.gl, li, g, grl);
+    rows4<ROW>(duh, li, g, durh);
+    rows4<ROW>(dul, li, g, durl);
+    // dS[s = 4g+r][t = li] = G_s . du_t; dU W (dQ part); G A (dK part, A before this step's update)
+    const float4v ds = rows_x_f2(grh, grl, durh, durl, zero4v());
+    float4v dq = rows_x_f2(durh, durl, wh, wl, zero4v());
+    float4v dk;
+    {
+      bf16x4 ah[4], al[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) split4(a2[b], ah[b], al[b]);
+      dk = rows_x_f2(grh, grl, ah, al, zero4v());
+    }
+    // A += dU^T Q (F1 and F2)
+    {
+      const bf16x4 duwh = read_cols<ROW>(duh, 0, 16 * w, li, g);  // du[4g + r][16w + li]
+      const bf16x4 duwl = read_cols<ROW>(dul, 0, 16 * w, li, g);
+      const bf16x8 bu = cat(duwh, duwl);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x4 qt = read_cols<ROW>(S.q, 0, 16 * t, li, g);
+        a1[t] = mfma32(cat(qt, qt), bu, a1[t]);
+        const bf16x4 dbh = read_cols<ROW>(duh, 0, 16 * t, li, g);
+        const bf16x4 dbl = read_cols<ROW>(dul, 0, 16 * t, li, g);
+        a2[t] = mfma32(cat(dbh, dbl), cat(qw, qw), a2[t]);
+      }
+    }
+    __syncthreads();  // B3: dy and dg in LDS
+
+    // ================= phase 4: matrix cores, column-owned outputs =================
+    {
+      float yp[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yp[r] = (4 * g + r <= li) ? ds[r] : 0.f;
+      bf16x4 yh4, yl4;
+      split4(yp, yh4, yl4);
+      const bf16x8 ya8 = cat(yh4, yl4);
+      dq = mfma32(ya8, cat(kw, kw), dq);
+      const float4v ypt = mfma32(ya8, ident, zero4v());  // dS'^T (t = 4g+r, s = li)
+      bf16x4 th, tl;
+      split4(ypt, th, tl);
+      dk = mfma32(cat(th, tl), cat(qw, qw), dk);
+    }
+    {
+      bf16x4 dyrh[4], dyrl[4];
+      rows4<ROW>(dyh, li, g, dyrh);
+      rows4<ROW>(dyl, li, g, dyrl);
+      dk = rows_x_f2(dyrh, dyrl, wh, wl, dk);
+    }
+    // A += dY^T K (F1 and F2)
+    {
+      const bf16x4 dywh = read_cols<ROW>(dyh, 0, 16 * w, li, g);
+      const bf16x4 dywl = read_cols<ROW>(dyl, 0, 16 * w, li, g);
+      const bf16x8 bd = cat(dywh, dywl);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x4 kt = read_cols<ROW>(S.k, 0, 16 * t, li, g);
+        a1[t] = mfma32(cat(kt, kt), bd, a1[t]);
+        const bf16x4 dbh = read_cols<ROW>(dyh, 0, 16 * t, li, g);
+        const bf16x4 dbl = read_cols<ROW>(dyl, 0, 16 * t, li, g);
+        a2[t] = mfma32(cat(dbh, dbl), cat(kw, kw), a2[t]);
+      }
+    }
+    {
+      const size_t o = (static_cast<size_t>(n) * BT + 4 * g) * D + 16 * w + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lo = (4 * g + r) * ZR + 16 * w + li;
+        store_merged<GT>(dQg + o + r * D, dq[r] + S.dz[lo]);
+        store_merged<GT>(dKg + o + r * D, fmaf(2.f * gam_c, dgt[lo], dk[r]));
+      }
+    }
+    __syncthreads();  // B4: the step's tiles are consumed
+  };
+
+  const int nfull = nb / PF * PF;
+  for (int j0 = 0; j0 < nfull; j0 += PF) {
+#pragma unroll
+    for (int jj = 0; jj < PF; ++jj) {
+      const int jn = (jj + 1) % PF;
+      step(j0 + jj, ra[jj], rv[jj], rg[jj], rz[jj], rt[jj], ra[jn], rv[jn], rg[jn], rz[jn], rt[jn]);
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < PF; ++jj) {
+    const int jn = (jj + 1) % PF;
+    if (nfull + jj < nb) step(nfull + jj, ra[jj], rv[jj], rg[jj], rz[jj], rt[jj], ra[jn], rv[jn], rg[jn], rz[jn], rt[jn]);
+  }
+
+  // dL/dW0 (F1 copy); dgamma, dbeta: the 16 token lanes of each output summed through LDS
+  float* dw = a.dW0 + static_cast<int64_t>(chain) * D * D + static_cast<int64_t>(16 * w + li) * D + 4 * g;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    *reinterpret_cast<float4*>(dw + 16 * t) = make_float4(a1[t][0], a1[t][1], a1[t][2], a1[t][3]);
+  *reinterpret_cast<float4*>(&yk[tk * ZR + 4 * li]) = dgam;
+  *reinterpret_cast<float4*>(&yq[tk * ZR + 4 * li]) = dbet;
+  __syncthreads();
+  if (tid < D) {
+    float sg = 0.f, sb = 0.f;
+    for (int t = 0; t < BT; ++t) {
+      sg += yk[t * ZR + tid];
+      sb += yq[t * ZR + tid];
+    }
+    a.dgamma[static_cast<int64_t>(chain) * D + tid] = sg;
+    a.dbeta[static_cast<int64_t>(chain) * D + tid] = sb;
+  }
+}
+
+#ifndef TTT_LN_BWD_PF
+#define TTT_LN_BWD_PF 2
+#endif
+
+template <bool TOK>
+hipError_t launch_tok(const BwdArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.H), block(kThreads);
+  if (a.out_dtype == 0)
+    hipLaunchKernelGGL((ttt_linear_ln_bwd_d64b16<TTT_LN_BWD_PF, TOK, float>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((ttt_linear_ln_bwd_d64b16<TTT_LN_BWD_PF, TOK, uint16_t>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_ln_bwd_mfma(const BwdArgs& a, hipStream_t s) {
+  return a.est != 0 ? launch_tok<true>(a, s) : launch_tok<false>(a, s);
+}
+
+}  // namespace ttt

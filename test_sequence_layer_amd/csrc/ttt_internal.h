@@ -73,9 +73,11 @@ hipError_t launch_linear_bwd_mfma(const BwdArgs& a, hipStream_t s);
 bool linear_bwd_generic_supported(int d, int b);
 const char* linear_bwd_generic_name(int d);
 hipError_t launch_linear_bwd_generic(const BwdArgs& a, hipStream_t s);
-// Backward of TTT-Linear with the layer norm (fp32 arithmetic): d = 64, b = 16.
+// Backward of TTT-Linear with the layer norm: d = 64, b = 16, bf16 inputs; the
+// matrix-core kernel and the fp32 one (the cross-check).
 bool linear_ln_bwd_supported(const BwdArgs& a);
 hipError_t launch_linear_ln_bwd(const BwdArgs& a, hipStream_t s);
+hipError_t launch_linear_ln_bwd_mfma(const BwdArgs& a, hipStream_t s);
 
 struct MlpArgs {
   int B, H, T, d, dh, b;

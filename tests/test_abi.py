@@ -395,7 +395,8 @@ def test_ln_bwd_validation():
     assert _lbval(_desc(), eps=float("nan")) == SHAPE
     assert _lbval(_desc(ind=0)) == UNSUP                      # bf16 inputs only
     assert _lbval(_desc(b=8)) == UNSUP
-    assert _lbval(_desc(flags=ttt.TTT_FLAG_GENERIC)) == UNSUP
+    assert _lbval(_desc(flags=ttt.TTT_FLAG_GENERIC)) == OK
+    assert _lbval(_desc(flags=ttt.TTT_FLAG_PRIMAL)) == FLAGS
     assert _lbval(_desc(), v=3 * GB + 8) == ALIGN
     assert _lbval(_desc(), gamma=5 * GB + 2) == ALIGN
     assert _lbval(_desc(), dgamma=1 * GB) == ALIAS            # output over an input
@@ -404,7 +405,8 @@ def test_ln_bwd_validation():
     assert _lbval(_desc(B=0)) == OK
     assert _lbval(_desc(T=0), q=None, k=None, v=None, dl=None, dz=None, dq=None, dk=None, dv=None,
                   deta=None) == OK
-    assert ttt.linear_ln_bwd_kernel_name(16, 32, 8192, 64, 16) == "ttt_linear_ln_bwd_fp32"
+    assert ttt.linear_ln_bwd_kernel_name(16, 32, 8192, 64, 16) == "ttt_linear_ln_bwd_d64b16"
+    assert ttt.linear_ln_bwd_kernel_name(16, 32, 8192, 64, 16, generic=True) == "ttt_linear_ln_bwd_fp32"
     assert ttt.linear_ln_bwd_kernel_name(1, 1, 64, 64, 16, in_dtype=ttt.TTT_F32) is None
 
 
