@@ -303,6 +303,8 @@ def main():
                     help="split each sequence into this many chunks run in parallel (chunked forward)")
     ap.add_argument("--decode", action="store_true",
                     help="time decoding: one token per call for every sequence, state carried in place")
+    ap.add_argument("--dtype", choices=("bf16", "fp32"), default=None,
+                    help="storage dtype of Q, K, V (default: the config's; the headline is bf16)")
     ap.add_argument("--batch", type=int, default=None,
                     help="with --decode: the number of sequences B (the pages' generation benchmark uses 512); "
                          "the inputs then hold 64 tokens per sequence, which the calls cycle through")
@@ -341,6 +343,8 @@ def main():
     cfg = ti.CONFIGS[args.config]
     if args.batch is not None:
         cfg = cfg.with_(name=f"{cfg.name}-B{args.batch}", B=args.batch, T=64)
+    if args.dtype is not None and args.dtype != cfg.dtype:
+        cfg = cfg.with_(name=f"{cfg.name}-{args.dtype}", dtype=args.dtype)
     log(f"bench: generating {cfg.name} inputs ...")
     t0 = time.perf_counter()
     inp = ti.generate(cfg)

@@ -75,7 +75,7 @@ int64_t eta_extent(int64_t B, int64_t H, int64_t T, int64_t sb, int64_t sh, int6
   return (B - 1) * sb + (H - 1) * sh + (T - 1) * st + 1;
 }
 
-enum Kernel { K_NONE, K_GENERIC, K_MFMA, K_PRIMAL };
+enum Kernel { K_NONE, K_GENERIC, K_MFMA, K_MFMA32, K_PRIMAL };
 
 constexpr uint32_t kRowFlags = TTT_FLAG_ROWS1 | TTT_FLAG_ROWS2 | TTT_FLAG_ROWS4;
 
@@ -83,7 +83,8 @@ Kernel pick_linear(const ttt::LinearArgs& a, uint32_t flags) {
   if (flags & TTT_FLAG_PRIMAL) return ttt::linear_primal_supported(a.d) ? K_PRIMAL : K_NONE;
   if (flags & TTT_FLAG_GENERIC) return ttt::linear_generic_supported(a.d, a.b) ? K_GENERIC : K_NONE;
   if (ttt::linear_mfma_supported(a)) return K_MFMA;
-  if (flags & kRowFlags) return K_NONE;  // row blocks exist only in the matrix-core kernel
+  if (flags & kRowFlags) return K_NONE;  // row blocks exist only in the bf16 matrix-core kernel
+  if (ttt::linear_mfma_f32_supported(a)) return K_MFMA32;
   if (ttt::linear_generic_supported(a.d, a.b)) return K_GENERIC;
   return K_NONE;
 }
@@ -404,6 +405,7 @@ const char* ttt_linear_kernel_name(const ttt_linear_desc* d) {
   ttt::LinearArgs a = make_linear_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
   switch (pick_linear(a, d->flags)) {
     case K_MFMA: return ttt::linear_mfma_name(a);
+    case K_MFMA32: return "ttt_linear_mfma_f32_d64b16";
     case K_GENERIC: return ttt::linear_generic_name(a.d);
     case K_PRIMAL: return ttt::linear_primal_name(a.d);
     default: return nullptr;
@@ -421,6 +423,8 @@ ttt_status ttt_linear_fwd(const ttt_linear_desc* desc, const void* Q, const void
   hipError_t e;
   if (k == K_MFMA)
     e = ttt::launch_linear_mfma(a, s);
+  else if (k == K_MFMA32)
+    e = ttt::launch_linear_mfma_f32(a, s);
   else if (k == K_PRIMAL)
     e = ttt::launch_linear_primal(make_primal_args_fwd(desc, Q, K, V, W0, eta, Z, W_final), s);
   else

@@ -129,6 +129,10 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(const LinearArgs& a);
 const char* linear_mfma_name(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
+// MFMA kernel for fp32 Q/K/V: d = 64, b = 16, plain forward (no layer norm, no
+// saved E, not chunked).
+bool linear_mfma_f32_supported(const LinearArgs& a);
+hipError_t launch_linear_mfma_f32(const LinearArgs& a, hipStream_t s);
 // First pass of a chunked forward: for every chain, the forward of chunk 0
 // from W0 (its Z, and its end state = the start state of chunk 1), and the
 // maps of chunks 1 .. nchunk-2: P = the product of the chunk's

@@ -156,7 +156,9 @@ def test_linear_kernel_selection():
     assert ttt.linear_kernel_name(16, 32, 8192, 64, 16) == "ttt_linear_mfma_d64b16"
     assert ttt.linear_kernel_name(16, 32, 8192, 64, 16, generic=True) == "ttt_linear_generic_kernel<64>"
     assert ttt.linear_kernel_name(1, 1, 64, 16, 4, in_dtype=0) == "ttt_linear_generic_kernel<16>"
-    assert ttt.linear_kernel_name(1, 1, 64, 64, 16, in_dtype=0) == "ttt_linear_generic_kernel<64>"
+    assert ttt.linear_kernel_name(1, 1, 64, 64, 16, in_dtype=0) == "ttt_linear_mfma_f32_d64b16"   # fp32 Q/K/V
+    assert ttt.linear_kernel_name(1, 1, 64, 64, 16, in_dtype=0, generic=True) == "ttt_linear_generic_kernel<64>"
+    assert ttt.linear_kernel_name(1, 1, 64, 64, 8, in_dtype=0) == "ttt_linear_generic_kernel<64>"
     assert ttt.linear_kernel_name(1, 1, 64, 48, 16) is None
 
 

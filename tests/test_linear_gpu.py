@@ -71,7 +71,38 @@ def test_bf16_generic_small(ttt, B, H, T, eta_kind):
 @pytest.mark.parametrize("d,b,T", [(64, 16, 128), (32, 8, 96), (16, 4, 64), (64, 32, 64), (16, 1, 20)])
 def test_fp32_generic(ttt, d, b, T):
     cfg = ti.CONFIGS["tiny"].with_(B=2, H=3, d=d, b=b, T=T, eta_value=0.05, seed=d * b + T)
-    _check(ttt, cfg, CONTRACT_FP32, label=f"fp32 d{d} b{b} T{T}")
+    _check(ttt, cfg, CONTRACT_FP32, generic=True, label=f"fp32 d{d} b{b} T{T}")
+
+
+# ---- fp32 Q/K/V on the matrix cores (d = 64, b = 16) ----------------------------------
+
+@pytest.mark.parametrize("B,H,T", [(1, 1, 16), (2, 3, 112), (1, 2, 256)])
+@pytest.mark.parametrize("eta_kind", ["scalar", "head", "token"])
+def test_fp32_mfma_small(ttt, B, H, T, eta_kind):
+    cfg = ti.CONFIGS["l1p3b"].with_(B=B, H=H, T=T, dtype="fp32", eta_kind=eta_kind, eta_value=1.0 / 64,
+                                   seed=300 + T)
+    assert ttt.linear_kernel_name(B, H, T, 64, 16, in_dtype=0) == "ttt_linear_mfma_f32_d64b16"
+    _check(ttt, cfg, CONTRACT_FP32, label=f"fp32 mfma B{B} H{H} T{T} {eta_kind}")
+
+
+@pytest.mark.parametrize("name,sample", [("l125m", 12), ("l1p3b", 6), ("long", 3)])
+def test_fp32_mfma_workloads(ttt, name, sample):
+    """The 125M, 1.3B and long workload shapes with fp32 Q/K/V (the support
+    matrix's fp32 rows), against the oracle on sampled chains at the fp32 bar."""
+    cfg = ti.CONFIGS[name].with_(dtype="fp32")
+    _check(ttt, cfg, CONTRACT_FP32, chains=ti.sample_chains(cfg, sample), label=f"fp32 {name}")
+
+
+def test_fp32_mfma_vs_generic_and_bf16_output(ttt):
+    cfg = ti.CONFIGS["l1p3b"].with_(B=2, H=3, T=192, dtype="fp32", seed=310)
+    inp = ti.generate(cfg)
+    z1, w1, _ = _run(ttt, inp)
+    z2, w2, _ = _run(ttt, inp, generic=True)
+    zb, wb, _ = _run(ttt, inp, out_dtype=torch.bfloat16)
+    e = max(max_rel(rows(z1), rows(z2)), max_rel(rows(w1), rows(w2)))
+    print(f"fp32 mfma vs generic: {e:.2e}", flush=True)
+    assert e < 1e-5
+    assert torch.equal(zb, z1.to(torch.bfloat16)) and torch.equal(wb, w1)
 
 
 def test_mfma_vs_generic(ttt):
