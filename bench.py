@@ -543,12 +543,15 @@ def main():
         # TTT-MLP per token: W1b k, W1 q, W2b a, W2b^T e, the two rank-one steps, W2 a' (7 d dh MACs)
         flops = B * H * (14 * d * cfg.dh if cfg.is_mlp else 6 * d * d)
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
-    # counters are recorded per (kernel, workload) for the plain forward and the
-    # backward; the other modes (saving forward, training step, layer norm,
-    # chunked, primal, decode, portable kernel) run other code under related
-    # names and have no record of their own
-    plain = not (args.save or args.train or args.ln or args.chunks > 1 or args.primal or args.decode or args.generic)
-    traffic = measured_traffic(kname, cfg.name) if plain else None
+    # counters are recorded per (kernel, workload) for every mode that launches
+    # one kernel per step; the saving forward, the training step and the chunked
+    # call launch several (or another instantiation) and have no record of
+    # their own.  Workload keys: the config's name, "-ln" for the layer-norm
+    # forward, "-decode" for decoding.
+    single = not (args.save or args.train or args.chunks > 1)
+    prof_workload = cfg.name + ("-ln" if args.ln and not args.bwd else "") + ("-decode" if args.decode else "")
+    kid = kname.split(" ")[0]
+    traffic = measured_traffic(kid, prof_workload) if single else None
     tflops = flops / (kernel_ms / 1e3) / 1e12
     # the binding roofline: bytes / 8 TB/s vs flops / 2.5 PF/s (bf16 MFMA, which every
     # contraction runs on); TTT-Linear is HBM-bound, TTT-MLP MFMA-bound
@@ -565,7 +568,7 @@ def main():
     # (hi/lo split passes, zero-padded k-slots) from the committed counters
     mfma = {"algorithmic_flops": flops, "achieved_tflops": round(tflops, 2),
             "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
-    performed = measured_mfma_flops(kname, cfg.name) if plain else None
+    performed = measured_mfma_flops(kid, prof_workload) if single else None
     if performed:
         ptf = performed / (kernel_ms / 1e3) / 1e12
         mfma.update({"performed_flops": performed, "performed_over_algorithmic": round(performed / flops, 3),
