@@ -331,6 +331,10 @@ def main():
         ap.error("--graph applies to --decode")
     if args.batch is not None and not args.decode:
         ap.error("--batch applies to --decode")
+    if args.ln and (args.decode or args.primal) and ti.CONFIGS[args.config].is_mlp:
+        ap.error("the TTT-MLP layer-norm path has the dual form only (no --primal / --decode)")
+    if args.ln and args.primal and (args.save or args.bwd or args.train):
+        ap.error("--primal with --ln times the forward only")
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the (sequence, head) chains are independent, so N GPUs would each run this same kernel on "
@@ -368,6 +372,16 @@ def main():
             def call(i, p):
                 q1, k1, v1, e1 = tok[i]
                 ttt.mlp_decode(q1, k1, v1, e1, w1, w2, w1b, w2b, p, cfg.b, z=zt)
+        elif args.ln:
+            kname = ttt.linear_ln_kernel_name(B, H, 1, d, cfg.b, in_code, 0, (0, 0, 0), primal=True)
+            w = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
+            wb = w.clone()
+            gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
+            bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
+
+            def call(i, p):
+                q1, k1, v1, e1 = tok[i]
+                ttt.linear_ln_decode(q1, k1, v1, e1, gam, bet, w, wb, p, cfg.b, z=zt)
         else:
             kname = ttt.linear_kernel_name(B, H, 1, d, cfg.b, in_code, 0, (0, 0, 0), primal=True)
             w = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
@@ -484,9 +498,13 @@ def main():
         elif args.ln:
             gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
             bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
+            if args.primal:
+                kname = ttt.linear_ln_kernel_name(B, H, T, d, cfg.b, 1 if cfg.dtype == "bf16" else 0, 0,
+                                                  inp.eta_strides, primal=True)
 
             def step():
-                ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], gam, bet, t["eta"], cfg.b, z=z, w_final=wf)
+                ttt.linear_ln_fwd(t["q"], t["k"], t["v"], t["w1"], gam, bet, t["eta"], cfg.b, z=z, w_final=wf,
+                                  primal=args.primal)
         elif args.chunks > 1:
             kname = "ttt_linear_mfma_d64b16"
             ws = torch.empty(ttt.linear_chunked_workspace_bytes(B, H, T, d, cfg.b, args.chunks),
@@ -540,6 +558,8 @@ def main():
         # plus one token of Q/K/V in and Z out
         state = 2 * d * cfg.dh if cfg.is_mlp else d * d
         bytes_ = B * H * (3 * state * 4 + d * (3 * (2 if cfg.dtype == "bf16" else 4) + 4))
+        if args.ln:
+            bytes_ += H * 2 * d * 4                     # gamma, beta
         # TTT-MLP per token: W1b k, W1 q, W2b a, W2b^T e, the two rank-one steps, W2 a' (7 d dh MACs)
         flops = B * H * (14 * d * cfg.dh if cfg.is_mlp else 6 * d * d)
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
@@ -622,9 +642,14 @@ def main():
     form = ("decode (graph)" if args.graph else "decode") if args.decode else (
         "primal" if args.primal else ("generic" if args.generic else ""))
     if args.ln:
-        form = "layer-norm"
-        roof["note"] = ("f(x) = x + LN(W2 GELU(W1 x))" if cfg.is_mlp else "f(x) = x + LN(W x)") + \
+        ln_note = ("f(x) = x + LN(W2 GELU(W1 x))" if cfg.is_mlp else "f(x) = x + LN(W x)") + \
             ": layer norm and residual inside f"
+        if args.decode or args.primal:
+            form = "layer-norm " + form
+            roof["note"] = ln_note + "; " + roof["note"]
+        else:
+            form = "layer-norm"
+            roof["note"] = ln_note
     if args.chunks > 1:
         form = f"chunked({args.chunks})"
         roof["note"] = ("chunked forward: chunk 0 with the maps of chunks 1..n-2, the scan of the maps, then "
@@ -643,12 +668,12 @@ def main():
         roof["note"] = f"forward saving {saved}, then backward: two launches per step"
     headline = cfg.name == "l1p3b" and not form and direction == "fwd"
     if args.decode:
-        workload = (f"{model} decode (primal form, one token per call"
+        workload = (f"{model} {'layer-norm ' if args.ln else ''}decode (primal form, one token per call"
                     f"{f', replays of a HIP graph of {cfg.b} calls' if args.graph else ''}) "
                     f"B{B} H{H} d{d} b{cfg.b}: {B * H} (sequence, head) states, {cfg.dtype} Q/K/V, fp32 state "
                     f"and Z, {eta_desc} eta")
     else:
-        workload = (f"{model} {'layer-norm ' if args.ln else ''}dual-form "
+        workload = (f"{model} {'layer-norm ' if args.ln else ''}{'primal' if args.primal else 'dual'}-form "
                     f"{direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
                     f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
                     f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta")

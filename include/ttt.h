@@ -172,15 +172,19 @@ ttt_status ttt_linear_fwd_chunked_noalloc(const ttt_linear_desc* desc, int32_t n
  * delta k^T with delta the loss gradient back-propagated through LN to W k, so
  * the dual form carries over: Y = W Q - Delta (diag(eta) triu(K^T Q)),
  * Z = Q + LN(Y), W <- W - Delta diag(eta) K^T.  Other arguments, layouts and
- * errors as for ttt_linear_fwd (Z fp32 or bf16).  Supported: d = 64, b = 16,
- * bf16 inputs, flags = 0 (else TTT_ERR_UNSUPPORTED); in addition eps must be
- * finite and >= 0 (TTT_ERR_SHAPE), gamma and beta non-NULL (TTT_ERR_NULL),
- * 4-byte aligned (TTT_ERR_ALIGN) and not overlapping Z or W_final
- * (TTT_ERR_ALIAS).
+ * errors as for ttt_linear_fwd (Z fp32 or bf16).  Supported: flags = 0, the
+ * dual form, at d = 64, b = 16, bf16 inputs; flags = TTT_FLAG_PRIMAL, token by
+ * token ([TTT] 03 §7), at d in {16, 32, 64}, any b, fp32 or bf16 inputs;
+ * anything else TTT_ERR_UNSUPPORTED.  In addition eps must be finite and >= 0
+ * (TTT_ERR_SHAPE), gamma and beta non-NULL (TTT_ERR_NULL), 4-byte aligned
+ * (TTT_ERR_ALIGN) and not overlapping Z or W_final (TTT_ERR_ALIAS).
  */
 ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                              const float* W0, const float* gamma, const float* beta, float eps, const float* eta,
                              void* Z, float* W_final, void* stream);
+
+/* Name of the kernel ttt_linear_ln_fwd would launch for desc, or NULL if unsupported. */
+const char* ttt_linear_ln_kernel_name(const ttt_linear_desc* desc);
 
 /*
  * TTT-Linear with layer norm, forward for training: ttt_linear_ln_fwd, and also
@@ -192,8 +196,9 @@ ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const v
  *             undoes the forward's own steps.  Must overlap no other argument
  *             (TTT_ERR_ALIAS); 16-byte aligned (TTT_ERR_ALIGN); non-NULL when
  *             B*H*T > 0 (TTT_ERR_NULL).
- * Same support and other errors as ttt_linear_ln_fwd; Z and W_final are
- * bit-identical to those of ttt_linear_ln_fwd.
+ * Same support and other errors as ttt_linear_ln_fwd with flags = 0 (any
+ * other flags: TTT_ERR_UNSUPPORTED); Z and W_final are bit-identical to those
+ * of ttt_linear_ln_fwd.
  */
 ttt_status ttt_linear_ln_fwd_save(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                                   const float* W0, const float* gamma, const float* beta, float eps,
@@ -258,6 +263,28 @@ const char* ttt_linear_ln_bwd_kernel_name(const ttt_linear_desc* desc);
  */
 ttt_status ttt_linear_decode(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                              const float* eta, void* Z, float* W, float* Wb, int64_t pos, void* stream);
+
+/*
+ * TTT-Linear decode with layer norm and residual inside f ([TTT] 03 §9 and 04
+ * §3: generation with the layer's own f(x) = x + LN(W x)).  Per new token t at
+ * position p, with Wb the mini-batch-start state:
+ *   y = Wb k_t;  delta = the gradient of |k_t + LN(y) - v_t|^2 with respect to y;
+ *   W <- W - eta_t delta k_t^T;  z_t = q_t + LN(W q_t)
+ * (LN, gamma, beta [H, d] fp32 and eps as for ttt_linear_ln_fwd).  Arguments,
+ * state carry, support and errors as ttt_linear_decode, plus the layer-norm
+ * checks of ttt_linear_ln_fwd (eps: TTT_ERR_SHAPE; gamma, beta: TTT_ERR_NULL,
+ * TTT_ERR_ALIGN, and TTT_ERR_ALIAS when they overlap Z, W or Wb).  Decoding T
+ * tokens from pos = 0 with W = Wb = W0 gives the Z and W of ttt_linear_ln_fwd
+ * (to rounding).
+ */
+ttt_status ttt_linear_ln_decode(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                const float* eta, const float* gamma, const float* beta, float eps, void* Z,
+                                float* W, float* Wb, int64_t pos, void* stream);
+
+/* Runs every host-side check of ttt_linear_ln_decode and launches nothing. */
+ttt_status ttt_linear_ln_decode_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                         const float* eta, const float* gamma, const float* beta, float eps,
+                                         const void* Z, const float* W, const float* Wb, int64_t pos);
 
 /*
  * TTT-Linear forward for training: ttt_linear_fwd, and also

@@ -52,7 +52,8 @@ EXPORTS = (
     "ttt_linear_decode", "ttt_linear_decode_validate",
     "ttt_linear_fwd_chunked", "ttt_linear_chunked_workspace_bytes", "ttt_linear_fwd_chunked_noalloc",
     "ttt_linear_ln_fwd", "ttt_linear_ln_fwd_save", "ttt_linear_ln_bwd", "ttt_linear_ln_bwd_validate",
-    "ttt_linear_ln_bwd_kernel_name",
+    "ttt_linear_ln_bwd_kernel_name", "ttt_linear_ln_kernel_name", "ttt_linear_ln_decode",
+    "ttt_linear_ln_decode_validate",
     "ttt_linear_fwd_save", "ttt_linear_bwd", "ttt_linear_bwd_validate", "ttt_linear_bwd_kernel_name",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name", "ttt_mlp_ln_fwd",
     "ttt_mlp_decode", "ttt_mlp_decode_validate",
@@ -139,6 +140,14 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_ln_bwd_validate.restype = ctypes.c_int
     L.ttt_linear_ln_bwd_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
     L.ttt_linear_ln_bwd_kernel_name.restype = ctypes.c_char_p
+    L.ttt_linear_ln_kernel_name.argtypes = [ctypes.POINTER(LinearDesc)]
+    L.ttt_linear_ln_kernel_name.restype = ctypes.c_char_p
+    L.ttt_linear_ln_decode.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, vp, fp,
+                                       fp, ctypes.c_int64, vp]
+    L.ttt_linear_ln_decode.restype = ctypes.c_int
+    L.ttt_linear_ln_decode_validate.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float,
+                                                vp, fp, fp, ctypes.c_int64]
+    L.ttt_linear_ln_decode_validate.restype = ctypes.c_int
     L.ttt_linear_fwd_save.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, vp, fp, fp, vp, fp, fp, vp]
     L.ttt_linear_fwd_save.restype = ctypes.c_int
     L.ttt_linear_bwd.argtypes = [ctypes.POINTER(LinearDesc), vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, vp]
@@ -461,7 +470,7 @@ def linear_fwd_chunked_noalloc(q, k, v, w0, eta, b: int, nchunks: int, out_dtype
 
 
 def linear_ln_fwd(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, out_dtype=None, w_final=None,
-                  z=None, stream=None, g_saved=None, save: bool = False):
+                  z=None, stream=None, g_saved=None, save: bool = False, primal: bool = False):
     """TTT-Linear with layer norm and residual inside f: f(x) = x + LN(W x).
 
     gamma, beta : [H, d] float32 (per head).  Other arguments as :func:`linear_fwd`.
@@ -469,11 +478,14 @@ def linear_ln_fwd(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, out_
     factor -eta delta as the forward applied it (delta the gradient of the
     token's loss with respect to W k at its mini-batch-start W), the input of
     :func:`linear_ln_bwd`; then returns (Z, W_final, G).
+    primal : compute token by token (the primal form; any b, d in {16, 32, 64}).
     """
     torch = _torch()
     B, H, T, d = q.shape
     if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
         raise ValueError("gamma and beta must be [H, d]")
+    if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("gamma and beta must be float32")
     wstride = _w0_stride(w0, B, H, d)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     eta_t, est = eta_layout(eta, B, H, T, q.device)
@@ -485,7 +497,8 @@ def linear_ln_fwd(q, k, v, w0, gamma, beta, eta, b: int, eps: float = 1e-6, out_
     if save and g_saved is None:
         g_saved = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
     _check_dev(q, k, v, w0, gamma, beta, eta_t, z, w_final, g_saved)
-    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est, 0)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), wstride, est,
+                       TTT_FLAG_PRIMAL if primal else 0)
     if save:
         st = lib().ttt_linear_ln_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w0), _ptr(gamma),
                                           _ptr(beta), float(eps), _ptr(eta_t), _ptr(z), _ptr(w_final),
@@ -517,6 +530,8 @@ def linear_ln_bwd(q, k, v, eta, gamma, beta, w_final, g_saved, dz, b: int, eps: 
         raise ValueError("q, k, v must have the same shape and dtype")
     if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
         raise ValueError("gamma and beta must be [H, d]")
+    if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("gamma and beta must be float32")
     if dz.shape != q.shape or tuple(g_saved.shape) != tuple(q.shape) or tuple(w_final.shape) != (B, H, d, d):
         raise ValueError("dz, g_saved must be [B, H, T, d] and w_final [B, H, d, d]")
     if g_saved.dtype != torch.float32 or w_final.dtype != torch.float32:
@@ -549,6 +564,13 @@ def linear_ln_bwd_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F3
                               eta_strides=(0, 0, 0), generic: bool = False) -> Optional[str]:
     desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_GENERIC if generic else 0)
     name = lib().ttt_linear_ln_bwd_kernel_name(ctypes.byref(desc))
+    return None if name is None else name.decode()
+
+
+def linear_ln_kernel_name(B, H, T, d, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),
+                          primal: bool = False) -> Optional[str]:
+    desc = linear_desc(B, H, T, d, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_PRIMAL if primal else 0)
+    name = lib().ttt_linear_ln_kernel_name(ctypes.byref(desc))
     return None if name is None else name.decode()
 
 
@@ -585,6 +607,34 @@ def linear_decode(q, k, v, eta, w, wb, pos: int, b: int, out_dtype=None, z=None,
     return z
 
 
+def linear_ln_decode(q, k, v, eta, gamma, beta, w, wb, pos: int, b: int, eps: float = 1e-6, out_dtype=None,
+                     z=None, stream=None):
+    """:func:`linear_decode` with f(x) = x + LN(W x); gamma, beta [H, d] float32."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    if tuple(w.shape) != (B, H, d, d) or tuple(wb.shape) != (B, H, d, d):
+        raise ValueError("w and wb must be [B, H, d, d]")
+    if w.dtype != torch.float32 or wb.dtype != torch.float32:
+        raise TypeError("w and wb must be float32")
+    if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
+        raise ValueError("gamma and beta must be [H, d]")
+    if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("gamma and beta must be float32")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
+    _check_dev(q, k, v, eta_t, gamma, beta, z, w, wb)
+    desc = linear_desc(B, H, T, d, b, _dtype_code(q.dtype), _dtype_code(z.dtype), 0, est, 0)
+    st = lib().ttt_linear_ln_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(gamma),
+                                    _ptr(beta), float(eps), _ptr(z), _ptr(w), _ptr(wb), int(pos),
+                                    _stream_handle(stream))
+    _done(st, "ttt_linear_ln_decode")
+    return z
+
+
 # ---------------------------------------------------------------- TTT-MLP --
 
 def mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, w_batch_stride, eta_strides, flags=0) -> MlpDesc:
@@ -609,9 +659,12 @@ def mlp_ln_fwd(q, k, v, w1, w2, gamma, beta, eta, b: int, eps: float = 1e-6, out
 
     gamma, beta : [H, d] float32 (per head).  Other arguments as :func:`mlp_fwd`.
     """
+    torch = _torch()
     H, d = q.shape[1], q.shape[3]
     if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
         raise ValueError("gamma and beta must be [H, d]")
+    if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("gamma and beta must be float32")
     return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=(gamma, beta, eps))
 
 

@@ -3,6 +3,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/ttt.h"
@@ -184,6 +185,7 @@ ttt::PrimalArgs make_primal_args_fwd(const ttt_linear_desc* d, const void* Q, co
   a.W_in = W0; a.Wb_in = W0; a.w_in_bstride = d->w0_batch_stride;
   a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
   a.Z = Z; a.W_out = Wf; a.Wb_out = nullptr; a.pos = 0;
+  a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
   return a;
 }
 
@@ -220,6 +222,45 @@ ttt_status validate_decode(const ttt_linear_desc* d, const void* Q, const void* 
       if (overlaps(out, in)) return TTT_ERR_ALIAS;
   if (overlaps(rz, rw) || overlaps(rz, rwb) || overlaps(rw, rwb)) return TTT_ERR_ALIAS;
   return TTT_OK;
+}
+
+// Layer-norm parameters: finite eps >= 0, gamma and beta [H, d] fp32, non-NULL,
+// 4-byte aligned, overlapping none of the outputs.
+ttt_status check_ln_params(const ttt_linear_desc* d, const float* gamma, const float* beta, float eps,
+                           std::initializer_list<Range> outs) {
+  if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
+  if (static_cast<int64_t>(d->B) * d->H == 0) return TTT_OK;
+  if (!gamma || !beta) return TTT_ERR_NULL;
+  if (!aligned(gamma, 4) || !aligned(beta, 4)) return TTT_ERR_ALIGN;
+  const int64_t hd_b = static_cast<int64_t>(d->H) * d->d * 4;
+  for (Range out : outs)
+    for (Range in : {Range{gamma, hd_b}, Range{beta, hd_b}})
+      if (overlaps(out, in)) return TTT_ERR_ALIAS;
+  return TTT_OK;
+}
+
+ttt_status validate_ln_decode(const ttt_linear_desc* d, const void* Q, const void* K, const void* V,
+                              const float* eta, const float* gamma, const float* beta, float eps, const void* Z,
+                              const float* W, const float* Wb, int64_t pos) {
+  const ttt_status st = validate_decode(d, Q, K, V, eta, Z, W, Wb, pos);
+  if (st != TTT_OK) return st;
+  const int64_t chains = static_cast<int64_t>(d->B) * d->H;
+  const int64_t w_b = chains * d->d * d->d * 4;
+  return check_ln_params(d, gamma, beta, eps,
+                         {Range{Z, chains * d->T * d->d * dtype_size(d->out_dtype)}, Range{W, w_b}, Range{Wb, w_b}});
+}
+
+ttt::PrimalArgs make_decode_args(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                 const float* eta, void* Z, float* W, float* Wb, int64_t pos) {
+  ttt::PrimalArgs a;
+  a.B = desc->B; a.H = desc->H; a.T = desc->T; a.d = desc->d; a.b = desc->b;
+  a.in_dtype = desc->in_dtype; a.out_dtype = desc->out_dtype;
+  a.Q = Q; a.K = K; a.V = V;
+  a.W_in = W; a.Wb_in = Wb; a.w_in_bstride = static_cast<int64_t>(desc->H) * desc->d * desc->d;
+  a.eta = eta; a.esb = desc->eta_stride_b; a.esh = desc->eta_stride_h; a.est = desc->eta_stride_t;
+  a.Z = Z; a.W_out = W; a.Wb_out = Wb; a.pos = pos;
+  a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
+  return a;
 }
 
 // ----------------------------------------------------------- backward --
@@ -517,23 +558,21 @@ ttt_status validate_ln(const ttt_linear_desc* desc, const void* Q, const void* K
   Kernel k;
   const ttt_status st = validate_linear(desc, Q, K, V, W0, eta, Z, W_final, &k);
   if (st != TTT_OK) return st;
-  if (desc->flags != 0 || k != K_MFMA) return TTT_ERR_UNSUPPORTED;
-  if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
+  const bool ok = (desc->flags == 0 && k == K_MFMA) || (desc->flags == TTT_FLAG_PRIMAL && k == K_PRIMAL);
+  if (!ok) return TTT_ERR_UNSUPPORTED;
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
-  if (chains == 0) return TTT_OK;
-  if (!gamma || !beta) return TTT_ERR_NULL;
-  if (!aligned(gamma, 4) || !aligned(beta, 4)) return TTT_ERR_ALIGN;
-  const int64_t hd_b = static_cast<int64_t>(desc->H) * desc->d * 4;
   const int64_t z_b = chains * desc->T * desc->d * dtype_size(desc->out_dtype);
-  for (Range out : {Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}})
-    for (Range in : {Range{gamma, hd_b}, Range{beta, hd_b}})
-      if (overlaps(out, in)) return TTT_ERR_ALIAS;
-  return TTT_OK;
+  return check_ln_params(desc, gamma, beta, eps, {Range{Z, z_b}, Range{W_final, chains * desc->d * desc->d * 4}});
 }
 
 hipError_t launch_ln(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V, const float* W0,
                      const float* gamma, const float* beta, float eps, const float* eta, void* Z, float* W_final,
                      float* saved, void* stream) {
+  if (desc->flags & TTT_FLAG_PRIMAL) {
+    ttt::PrimalArgs p = make_primal_args_fwd(desc, Q, K, V, W0, eta, Z, W_final);
+    p.gamma = gamma; p.beta = beta; p.eps = eps;
+    return ttt::launch_linear_primal(p, static_cast<hipStream_t>(stream));
+  }
   ttt::LinearArgs a = make_linear_args(desc, Q, K, V, W0, eta, Z, W_final);
   a.gamma = gamma;
   a.beta = beta;
@@ -544,6 +583,15 @@ hipError_t launch_ln(const ttt_linear_desc* desc, const void* Q, const void* K, 
 }
 
 }  // namespace
+
+const char* ttt_linear_ln_kernel_name(const ttt_linear_desc* d) {
+  if (!d) return nullptr;
+  ttt::LinearArgs a = make_linear_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  const Kernel k = pick_linear(a, d->flags);
+  if (d->flags == 0 && k == K_MFMA) return "ttt_linear_mfma_d64b16 (layer norm)";
+  if (d->flags == TTT_FLAG_PRIMAL && k == K_PRIMAL) return ttt::linear_primal_name(a.d, true);
+  return nullptr;
+}
 
 ttt_status ttt_linear_ln_fwd(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
                              const float* W0, const float* gamma, const float* beta, float eps, const float* eta,
@@ -560,6 +608,7 @@ ttt_status ttt_linear_ln_fwd_save(const ttt_linear_desc* desc, const void* Q, co
                                   const float* eta, void* Z, float* W_final, float* G_saved, void* stream) {
   ttt_status st = validate_ln(desc, Q, K, V, W0, gamma, beta, eps, eta, Z, W_final);
   if (st != TTT_OK) return st;
+  if (desc->flags != 0) return TTT_ERR_UNSUPPORTED;  // the primal kernel saves nothing
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
   if (chains == 0) return TTT_OK;
   st = check_saved(desc, Q, K, V, W0, eta, Z, W_final, G_saved);
@@ -776,13 +825,25 @@ ttt_status ttt_linear_decode(const ttt_linear_desc* desc, const void* Q, const v
   const ttt_status st = validate_decode(desc, Q, K, V, eta, Z, W, Wb, pos);
   if (st != TTT_OK) return st;
   if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
-  ttt::PrimalArgs a;
-  a.B = desc->B; a.H = desc->H; a.T = desc->T; a.d = desc->d; a.b = desc->b;
-  a.in_dtype = desc->in_dtype; a.out_dtype = desc->out_dtype;
-  a.Q = Q; a.K = K; a.V = V;
-  a.W_in = W; a.Wb_in = Wb; a.w_in_bstride = static_cast<int64_t>(desc->H) * desc->d * desc->d;
-  a.eta = eta; a.esb = desc->eta_stride_b; a.esh = desc->eta_stride_h; a.est = desc->eta_stride_t;
-  a.Z = Z; a.W_out = W; a.Wb_out = Wb; a.pos = pos;
+  const hipError_t e =
+      ttt::launch_linear_primal(make_decode_args(desc, Q, K, V, eta, Z, W, Wb, pos), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_linear_ln_decode_validate(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                         const float* eta, const float* gamma, const float* beta, float eps,
+                                         const void* Z, const float* W, const float* Wb, int64_t pos) {
+  return validate_ln_decode(desc, Q, K, V, eta, gamma, beta, eps, Z, W, Wb, pos);
+}
+
+ttt_status ttt_linear_ln_decode(const ttt_linear_desc* desc, const void* Q, const void* K, const void* V,
+                                const float* eta, const float* gamma, const float* beta, float eps, void* Z,
+                                float* W, float* Wb, int64_t pos, void* stream) {
+  const ttt_status st = validate_ln_decode(desc, Q, K, V, eta, gamma, beta, eps, Z, W, Wb, pos);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  ttt::PrimalArgs a = make_decode_args(desc, Q, K, V, eta, Z, W, Wb, pos);
+  a.gamma = gamma; a.beta = beta; a.eps = eps;
   const hipError_t e = ttt::launch_linear_primal(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }

@@ -20,6 +20,19 @@
 // The same kernel serves two entry points: the full forward (state from W0,
 // written to W_final) and decode (state W and Wb read and written in place,
 // continuing from position `pos`).
+//
+// With layer norm and residual inside f (part 03 §9: f(x) = x + LN(W x), LN
+// over the d outputs with per-head gamma, beta), ttt_linear_ln_primal_kernel
+// takes per token
+//   y = Wb k_t,  yh = (y - mean y) / sqrt(var y + eps),  g = gamma (k_t + gamma yh + beta - v_t)
+//   delta = (g - mean g - yh mean(g yh)) / sqrt(var y + eps)   (half the gradient at y)
+//   W <- W - 2 eta_t delta k_t^T
+//   z_t = q_t + LN(W q_t)
+// The means run over the whole workgroup: each row's value goes to LDS, and
+// after one barrier every thread sums the quarter of the d values matching its
+// state columns and finishes with the quad sum (mean and centred variance in
+// two passes over the same registers).  Three barriers per token: the
+// statistics of Wb k, the two sums of the LN backward, the statistics of W q.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -31,6 +44,12 @@ namespace {
 constexpr int TB = TTT_PRIMAL_TB;  // tokens staged per block
 constexpr int TU = 16;             // tokens per unrolled run piece
 static_assert(TB % TU == 0 && TU % 4 == 0, "block holds whole unrolled pieces");
+// Calls of at most TS tokens (decode) take an instantiation of their own with
+// TS-token tiles and no prefetch path: fewer registers and less LDS per
+// workgroup, so more of the state loads of different sequences are in flight
+// per CU.  Its arithmetic is that of the short branch of the full kernel.
+constexpr int TS = 8;
+static_assert(TS < TB, "short calls are a special case of the short branch");
 
 template <typename T>
 __device__ __forceinline__ float ld_in(const T* p, size_t i);
@@ -71,17 +90,22 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-template <int D, typename InT, typename OutT>
-__global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) {
+template <int D, bool LN, bool SHORT, typename InT, typename OutT>
+__device__ __forceinline__ void primal_body(const PrimalArgs& a) {
   constexpr int NT = 4 * D;
   constexpr int CQ = D / 4;  // columns per thread
-  __shared__ float ks[TB][D], qs[TB][D], vs[TB][D], zs[TB][D + 1];
-  __shared__ float es[TB];
-
+  constexpr int TK = SHORT ? TS : TB;  // tokens per tile
+  __shared__ float ks[TK][D], qs[TK][D], vs[TK][D], zs[TK][D + 1];
+  __shared__ float es[TK];
+  // layer-norm exchange: one value (ys, ys2) or pair (pr) per state row
+  __shared__ __align__(16) float ys[D], ys2[D];
+  __shared__ __align__(16) float2 pr[D];
   const int tid = threadIdx.x;
   const int i = tid >> 2, qd = tid & 3;
   const int chain = blockIdx.x;
   const int bi = chain / a.H, h = chain - bi * a.H;
+  float gam = 0.f, bet = 0.f;
+  if constexpr (LN) gam = a.gamma[h * D + i], bet = a.beta[h * D + i];
 
   // Position of the next token within its mini-batch, carried as a counter
   // (a 64-bit modulo per token would cost more than the token's arithmetic).
@@ -140,11 +164,55 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
     if (tid < TB) er = eg[static_cast<int64_t>(t0 + tid) * a.est];
   };
 
+  // Mean and 1/sqrt(var + eps) of the d values in y[] (written by the rows
+  // before a barrier): thread (i, qd) sums y[qd CQ .. qd CQ + CQ), the quad
+  // sum completes it; the variance is centred, from the same registers.
+  auto stats = [&](const float* y, float& mu, float& rs) {
+    float r[CQ];
+#pragma unroll
+    for (int c = 0; c < CQ / 4; ++c) {
+      const float4 x = *reinterpret_cast<const float4*>(y + qd * CQ + 4 * c);
+      r[4 * c] = x.x, r[4 * c + 1] = x.y, r[4 * c + 2] = x.z, r[4 * c + 3] = x.w;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < CQ; ++c) s += r[c];
+    mu = quad_sum(s) * (1.f / D);
+    float s2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < CQ; ++c) {
+      const float u = r[c] - mu;
+      s2 = fmaf(u, u, s2);
+    }
+    rs = rsqrtf(fmaf(quad_sum(s2), 1.f / D, a.eps));
+  };
+
   auto step = [&](int t) {
     float e = 0.f;
 #pragma unroll
     for (int c = 0; c < CQ; ++c) e = fmaf(Wb[c], ks[t][qd * CQ + c], e);
-    e = quad_sum(e) - vs[t][i];
+    e = quad_sum(e);
+    if constexpr (LN) {
+      if (qd == 0) ys[i] = e;
+      __syncthreads();
+      float mu, rs;
+      stats(ys, mu, rs);
+      const float yh = (e - mu) * rs;
+      const float g = gam * (fmaf(gam, yh, bet) + ks[t][i] - vs[t][i]);
+      if (qd == 0) pr[i] = make_float2(g, g * yh);
+      __syncthreads();
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CQ / 2; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(pr + qd * CQ + 2 * c);
+        s1 += x.x + x.z;
+        s2 += x.y + x.w;
+      }
+      const float m1 = quad_sum(s1) * (1.f / D), m2 = quad_sum(s2) * (1.f / D);
+      e = rs * (g - m1 - yh * m2);
+    } else {
+      e -= vs[t][i];
+    }
     const float ge = es[t] * e;  // es holds -2 eta (exact scaling)
     float z = 0.f;
 #pragma unroll
@@ -152,7 +220,15 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
       W[c] = fmaf(ge, ks[t][qd * CQ + c], W[c]);
       z = fmaf(W[c], qs[t][qd * CQ + c], z);
     }
-    return quad_sum(z);
+    z = quad_sum(z);
+    if constexpr (LN) {
+      if (qd == 0) ys2[i] = z;
+      __syncthreads();
+      float mu, rs;
+      stats(ys2, mu, rs);
+      z = qs[t][i] + fmaf(gam, (z - mu) * rs, bet);
+    }
+    return z;
   };
 
   // Tokens [t0, t0 + nt) of a block that is not full: loaded element by element.
@@ -182,7 +258,7 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
     for (int x = tid; x < nt * D; x += NT) st_out<OutT>(Zg, static_cast<size_t>(t0) * D + x, zs[x / D][x % D]);
   };
 
-  if (a.T < TB) {
+  if (SHORT || a.T < TB) {
     // One short block (decode): no prefetch, and the state loads stay in flight
     // while the tokens load.
     stage_part(0, a.T);
@@ -190,7 +266,7 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
     tokens_each(a.T);
     __syncthreads();
     store_z(0, a.T);
-  } else {
+  } else if constexpr (!SHORT) {
     // Retire the state loads first (s_waitcnt vmcnt(0)): otherwise the
     // compiler's wait counting cannot tell them from the prefetch loads and
     // waits for the whole prefetch at the first token of every block.
@@ -255,38 +331,69 @@ __global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) 
   }
 }
 
-template <int D>
-hipError_t launch_d(const PrimalArgs& a, hipStream_t s) {
+template <int D, bool SHORT, typename InT, typename OutT>
+__global__ __launch_bounds__(4 * D) void ttt_linear_primal_kernel(PrimalArgs a) {
+  primal_body<D, false, SHORT, InT, OutT>(a);
+}
+
+template <int D, bool SHORT, typename InT, typename OutT>
+__global__ __launch_bounds__(4 * D) void ttt_linear_ln_primal_kernel(PrimalArgs a) {
+  primal_body<D, true, SHORT, InT, OutT>(a);
+}
+
+template <int D, bool LN, bool SHORT, typename InT, typename OutT>
+void launch_s(const PrimalArgs& a, hipStream_t s) {
   dim3 grid(a.B * a.H), block(4 * D);
-  if (a.in_dtype == 0 && a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_linear_primal_kernel<D, float, float>), grid, block, 0, s, a);
-  else if (a.in_dtype == 0)
-    hipLaunchKernelGGL((ttt_linear_primal_kernel<D, float, uint16_t>), grid, block, 0, s, a);
-  else if (a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_linear_primal_kernel<D, uint16_t, float>), grid, block, 0, s, a);
+  if constexpr (LN)
+    hipLaunchKernelGGL((ttt_linear_ln_primal_kernel<D, SHORT, InT, OutT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((ttt_linear_primal_kernel<D, uint16_t, uint16_t>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_primal_kernel<D, SHORT, InT, OutT>), grid, block, 0, s, a);
+}
+
+template <int D, bool LN, typename InT, typename OutT>
+void launch_t(const PrimalArgs& a, hipStream_t s) {
+  if (a.T <= TS)
+    launch_s<D, LN, true, InT, OutT>(a, s);
+  else
+    launch_s<D, LN, false, InT, OutT>(a, s);
+}
+
+template <int D, bool LN>
+hipError_t launch_d(const PrimalArgs& a, hipStream_t s) {
+  if (a.in_dtype == 0 && a.out_dtype == 0)
+    launch_t<D, LN, float, float>(a, s);
+  else if (a.in_dtype == 0)
+    launch_t<D, LN, float, uint16_t>(a, s);
+  else if (a.out_dtype == 0)
+    launch_t<D, LN, uint16_t, float>(a, s);
+  else
+    launch_t<D, LN, uint16_t, uint16_t>(a, s);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dl(const PrimalArgs& a, hipStream_t s) {
+  return a.gamma ? launch_d<D, true>(a, s) : launch_d<D, false>(a, s);
 }
 
 }  // namespace
 
 bool linear_primal_supported(int d) { return d == 16 || d == 32 || d == 64; }
 
-const char* linear_primal_name(int d) {
+const char* linear_primal_name(int d, bool ln) {
   switch (d) {
-    case 16: return "ttt_linear_primal_kernel<16>";
-    case 32: return "ttt_linear_primal_kernel<32>";
-    case 64: return "ttt_linear_primal_kernel<64>";
+    case 16: return ln ? "ttt_linear_ln_primal_kernel<16>" : "ttt_linear_primal_kernel<16>";
+    case 32: return ln ? "ttt_linear_ln_primal_kernel<32>" : "ttt_linear_primal_kernel<32>";
+    case 64: return ln ? "ttt_linear_ln_primal_kernel<64>" : "ttt_linear_primal_kernel<64>";
     default: return nullptr;
   }
 }
 
 hipError_t launch_linear_primal(const PrimalArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 16: return launch_d<16>(a, s);
-    case 32: return launch_d<32>(a, s);
-    case 64: return launch_d<64>(a, s);
+    case 16: return launch_dl<16>(a, s);
+    case 32: return launch_dl<32>(a, s);
+    case 64: return launch_dl<64>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

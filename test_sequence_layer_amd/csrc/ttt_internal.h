@@ -115,9 +115,12 @@ struct PrimalArgs {
   float* W_out;        // [B, H, d, d]
   float* Wb_out;       // [B, H, d, d] or nullptr
   int64_t pos;         // tokens already processed
+  const float* gamma;  // [H, d] layer-norm scale, or nullptr for f(x) = W x
+  const float* beta;   // [H, d] layer-norm shift (with gamma)
+  float eps;
 };
 bool linear_primal_supported(int d);
-const char* linear_primal_name(int d);
+const char* linear_primal_name(int d, bool ln = false);
 hipError_t launch_linear_primal(const PrimalArgs& a, hipStream_t s);
 
 // Portable fp32 kernel (any supported d/b/dtype).

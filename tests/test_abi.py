@@ -429,6 +429,55 @@ def test_ln_fwd_save_host_errors():
              10 * GB, None) == UNSUP
 
 
+def _lnd(desc, pos=0, eps=1e-6, **over):
+    p = dict(q=1 * GB, k=2 * GB, v=3 * GB, eta=5 * GB, gamma=10 * GB, beta=11 * GB, z=6 * GB, w=7 * GB, wb=8 * GB)
+    p.update(over)
+    return ttt.lib().ttt_linear_ln_decode_validate(ctypes.byref(desc), p["q"], p["k"], p["v"], p["eta"], p["gamma"],
+                                                   p["beta"], ctypes.c_float(eps), p["z"], p["w"], p["wb"], pos)
+
+
+def test_ln_decode_validation():
+    POS = 10
+    assert _lnd(_desc(T=1)) == OK
+    assert _lnd(_desc(T=37, d=32, b=5, ind=0)) == OK     # any b, ragged T, fp32 inputs
+    assert _lnd(_desc(T=1), pos=-1) == POS
+    assert _lnd(_desc(T=1, flags=2)) == FLAGS
+    assert _lnd(_desc(T=1, d=48)) == UNSUP
+    assert _lnd(_desc(T=1), eps=-1.0) == SHAPE
+    assert _lnd(_desc(T=1), eps=float("nan")) == SHAPE
+    assert _lnd(_desc(T=1), gamma=None) == NULL
+    assert _lnd(_desc(T=1), beta=None) == NULL
+    assert _lnd(_desc(T=0), q=None, k=None, v=None, z=None, eta=None, gamma=None) == NULL  # the kernel reads gamma
+    assert _lnd(_desc(B=0), gamma=None, beta=None) == OK
+    assert _lnd(_desc(T=1), gamma=10 * GB + 2) == ALIGN
+    assert _lnd(_desc(T=1), gamma=7 * GB + 64) == ALIAS   # gamma inside W
+    assert _lnd(_desc(T=1), beta=6 * GB) == ALIAS         # beta over Z
+    assert _lnd(_desc(T=1), wb=7 * GB) == ALIAS           # the plain decode checks still hold
+
+
+def test_ln_fwd_primal_flag_host_errors():
+    b = Bufs()
+    f = ttt.lib().ttt_linear_ln_fwd
+    gam, bet = 8 * GB, 9 * GB
+
+    def call(desc, eps=1e-6, g=gam):
+        return f(ctypes.byref(desc), b.q, b.k, b.v, b.w0, g, bet, ctypes.c_float(eps), b.eta, b.z, b.wf, None)
+    assert call(_desc(flags=2, d=48)) == UNSUP
+    assert call(_desc(flags=3)) == FLAGS
+    assert call(_desc(flags=2, b=5, T=63)) == SHAPE      # T a multiple of b, as for ttt_linear_fwd
+    assert call(_desc(flags=2), eps=-1.0) == SHAPE
+    assert call(_desc(flags=2), g=None) == NULL
+    assert call(_desc(flags=2), g=6 * GB) == ALIAS        # gamma over Z
+    save = ttt.lib().ttt_linear_ln_fwd_save             # the primal kernel saves nothing
+    assert save(ctypes.byref(_desc(flags=2)), b.q, b.k, b.v, b.w0, gam, bet, ctypes.c_float(1e-6), b.eta, b.z,
+                b.wf, 10 * GB, None) == UNSUP
+    assert ttt.linear_ln_kernel_name(2, 4, 64, 64, 16) == "ttt_linear_mfma_d64b16 (layer norm)"
+    assert ttt.linear_ln_kernel_name(2, 4, 64, 64, 16, primal=True) == "ttt_linear_ln_primal_kernel<64>"
+    assert ttt.linear_ln_kernel_name(2, 4, 60, 32, 5, primal=True) == "ttt_linear_ln_primal_kernel<32>"
+    assert ttt.linear_ln_kernel_name(2, 4, 64, 48, 16, primal=True) is None
+    assert ttt.linear_ln_kernel_name(2, 4, 64, 64, 16, in_dtype=ttt.TTT_F32) is None
+
+
 def test_one_hip_runtime_per_process():
     # torch ships a HIP runtime under the same soname the library needs; the
     # binding imports torch before it loads libttt.so so that both use that one
