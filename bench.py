@@ -331,8 +331,6 @@ def main():
         ap.error("--graph applies to --decode")
     if args.batch is not None and not args.decode:
         ap.error("--batch applies to --decode")
-    if args.ln and (args.decode or args.primal) and ti.CONFIGS[args.config].is_mlp:
-        ap.error("the TTT-MLP layer-norm path has the dual form only (no --primal / --decode)")
     if args.ln and args.primal and (args.save or args.bwd or args.train):
         ap.error("--primal with --ln times the forward only")
     if args.gpus != 1 or world != 1:
@@ -364,14 +362,19 @@ def main():
                 t["v"][:, :, i:i + 1].contiguous(),
                 t["eta"][:, :, i:i + 1].contiguous() if t["eta"].dim() == 3 else t["eta"]) for i in range(64)]
         if cfg.is_mlp:
-            kname = ttt.mlp_kernel_name(B, H, 1, d, cfg.dh, cfg.b, in_code, 0, (0, 0, 0), primal=True)
+            kname = (ttt.mlp_ln_kernel_name if args.ln else ttt.mlp_kernel_name)(B, H, 1, d, cfg.dh, cfg.b, in_code, 0,
+                                                                               (0, 0, 0), primal=True)
             w1 = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
             w2 = t["w2"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
             w1b, w2b = w1.clone(), w2.clone()
+            ln = None
+            if args.ln:
+                ln = (torch.ones((H, d), dtype=torch.float32, device="cuda:0"),
+                      torch.zeros((H, d), dtype=torch.float32, device="cuda:0"), 1e-6)
 
             def call(i, p):
                 q1, k1, v1, e1 = tok[i]
-                ttt.mlp_decode(q1, k1, v1, e1, w1, w2, w1b, w2b, p, cfg.b, z=zt)
+                ttt.mlp_decode(q1, k1, v1, e1, w1, w2, w1b, w2b, p, cfg.b, z=zt, ln=ln)
         elif args.ln:
             kname = ttt.linear_ln_kernel_name(B, H, 1, d, cfg.b, in_code, 0, (0, 0, 0), primal=True)
             w = t["w1"].unsqueeze(0).expand(B, -1, -1, -1).contiguous()
@@ -421,13 +424,13 @@ def main():
         f2 = torch.empty((B, H, d, cfg.dh), dtype=torch.float32, device="cuda:0")
         kname = ttt.mlp_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides, primal=args.primal)
         if args.ln:
-            kname += " (layer norm)"
+            kname = ttt.mlp_ln_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides, primal=args.primal)
             gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
             bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
 
             def step():
                 ttt.mlp_ln_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], gam, bet, t["eta"], cfg.b, z=z,
-                               w1_final=f1, w2_final=f2)
+                               w1_final=f1, w2_final=f2, primal=args.primal)
         else:
             def step():
                 ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1,

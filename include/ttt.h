@@ -416,20 +416,48 @@ const char* ttt_mlp_kernel_name(const ttt_mlp_desc* desc);
  * carries over with Delta in place of 2 (W2 GELU(W1 k) - v):
  * Z = Q + LN(W2 A_Q - Delta (diag(eta) triu(A_K^T A_Q))), both layers updated
  * from Delta as in ttt_mlp_fwd.  Other arguments, support and errors as for
- * ttt_mlp_fwd; in addition eps must be finite and >= 0 (TTT_ERR_SHAPE), gamma
- * and beta non-NULL (TTT_ERR_NULL), 4-byte aligned (TTT_ERR_ALIGN) and not
- * overlapping Z or the final states (TTT_ERR_ALIAS).
+ * ttt_mlp_fwd (flags 0: the dual form; TTT_FLAG_PRIMAL: token by token, in
+ * fp32 throughout); in addition eps must be finite and >= 0 (TTT_ERR_SHAPE),
+ * gamma and beta non-NULL (TTT_ERR_NULL), 4-byte aligned (TTT_ERR_ALIGN) and
+ * not overlapping Z or the final states (TTT_ERR_ALIAS).
  * Accuracy limit: with small weights (std 0.02 for W1 and W2) the pre-norm
  * output's variance is only ~10x eps, the layer norm's backward divides by
  * that small scale and the recurrence amplifies rounding: against an fp64
- * reference Z is ~2.4e-4 off at T = 512 and ~5e-3 at T = 2048 (fp32
- * arithmetic itself: up to ~1e-3 at T = 2048).  With larger weights (e.g.
- * std 0.4 / 0.1) it stays at ~1e-5 over the full length.
+ * reference the dual form's Z is ~2.4e-4 off at T = 512 and ~5e-3 at
+ * T = 2048 (fp32 arithmetic itself, as in the primal form: up to ~1e-3 at
+ * T = 2048).  With larger weights (e.g. std 0.4 / 0.1) it stays at ~1e-5
+ * over the full length.
  */
 ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
                           const float* W1_0, const float* W2_0, const float* gamma, const float* beta,
                           float eps, const float* eta, void* Z, float* W1_final, float* W2_final,
                           void* stream);
+
+/* Name of the kernel ttt_mlp_ln_fwd would launch for desc, or NULL if unsupported. */
+const char* ttt_mlp_ln_kernel_name(const ttt_mlp_desc* desc);
+
+/*
+ * TTT-MLP decode with layer norm and residual inside f ([TTT] 03 §9 and 04
+ * §3: generation with the layer's own f(x) = x + LN(W2 GELU(W1 x))).  Per new
+ * token, with W1b, W2b the mini-batch-start state: y = W2b GELU(W1b k);
+ * Delta = the gradient of |k + LN(y) - v|^2 with respect to y; both layers
+ * stepped from Delta as in ttt_mlp_decode; z = q + LN(W2 GELU(W1 q)) with the
+ * updated state (LN, gamma, beta [H, d] fp32 and eps as for ttt_mlp_ln_fwd).
+ * Arguments, state carry, support and errors as ttt_mlp_decode, plus the
+ * layer-norm checks of ttt_mlp_ln_fwd (eps: TTT_ERR_SHAPE; gamma, beta:
+ * TTT_ERR_NULL, TTT_ERR_ALIGN, and TTT_ERR_ALIAS when they overlap Z or a
+ * state).  Decoding T tokens from pos = 0 with W1 = W1b = W1_0, W2 = W2b = W2_0
+ * gives the Z and states of ttt_mlp_ln_fwd (to rounding).
+ */
+ttt_status ttt_mlp_ln_decode(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* eta, const float* gamma, const float* beta, float eps, void* Z, float* W1,
+                             float* W2, float* W1b, float* W2b, int64_t pos, void* stream);
+
+/* Runs every host-side check of ttt_mlp_ln_decode and launches nothing. */
+ttt_status ttt_mlp_ln_decode_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                      const float* eta, const float* gamma, const float* beta, float eps,
+                                      const void* Z, const float* W1, const float* W2, const float* W1b,
+                                      const float* W2b, int64_t pos);
 
 /* Human-readable text of a status code (never NULL). */
 const char* ttt_status_str(int status);

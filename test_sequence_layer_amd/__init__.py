@@ -56,7 +56,8 @@ EXPORTS = (
     "ttt_linear_ln_decode_validate",
     "ttt_linear_fwd_save", "ttt_linear_bwd", "ttt_linear_bwd_validate", "ttt_linear_bwd_kernel_name",
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name", "ttt_mlp_ln_fwd",
-    "ttt_mlp_decode", "ttt_mlp_decode_validate",
+    "ttt_mlp_decode", "ttt_mlp_decode_validate", "ttt_mlp_ln_decode", "ttt_mlp_ln_decode_validate",
+    "ttt_mlp_ln_kernel_name",
     "ttt_status_str", "ttt_abi_version",
 )
 
@@ -173,6 +174,14 @@ def lib() -> ctypes.CDLL:
     L.ttt_mlp_validate.restype = ctypes.c_int
     L.ttt_mlp_kernel_name.argtypes = [ctypes.POINTER(MlpDesc)]
     L.ttt_mlp_kernel_name.restype = ctypes.c_char_p
+    L.ttt_mlp_ln_kernel_name.argtypes = [ctypes.POINTER(MlpDesc)]
+    L.ttt_mlp_ln_kernel_name.restype = ctypes.c_char_p
+    L.ttt_mlp_ln_decode.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, vp, fp, fp, fp,
+                                    fp, ctypes.c_int64, vp]
+    L.ttt_mlp_ln_decode.restype = ctypes.c_int
+    L.ttt_mlp_ln_decode_validate.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, vp,
+                                             fp, fp, fp, fp, ctypes.c_int64]
+    L.ttt_mlp_ln_decode_validate.restype = ctypes.c_int
     L.ttt_status_str.argtypes = [ctypes.c_int]
     L.ttt_status_str.restype = ctypes.c_char_p
     L.ttt_abi_version.argtypes = []
@@ -654,10 +663,11 @@ def mlp_fwd(q, k, v, w1, w2, eta, b: int, out_dtype=None, w1_final=None, w2_fina
 
 
 def mlp_ln_fwd(q, k, v, w1, w2, gamma, beta, eta, b: int, eps: float = 1e-6, out_dtype=None, w1_final=None,
-               w2_final=None, z=None, stream=None):
+               w2_final=None, z=None, stream=None, primal: bool = False):
     """TTT-MLP with layer norm and residual inside f: f(x) = x + LN(W2 GELU(W1 x)).
 
     gamma, beta : [H, d] float32 (per head).  Other arguments as :func:`mlp_fwd`.
+    primal : compute token by token (the primal form) instead of the dual form.
     """
     torch = _torch()
     H, d = q.shape[1], q.shape[3]
@@ -665,7 +675,8 @@ def mlp_ln_fwd(q, k, v, w1, w2, gamma, beta, eta, b: int, eps: float = 1e-6, out
         raise ValueError("gamma and beta must be [H, d]")
     if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
         raise TypeError("gamma and beta must be float32")
-    return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=(gamma, beta, eps))
+    return _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=(gamma, beta, eps),
+                     flags=TTT_FLAG_PRIMAL if primal else 0)
 
 
 def _mlp_call(q, k, v, w1, w2, eta, b, out_dtype, w1_final, w2_final, z, stream, ln=None, flags=0):
@@ -712,12 +723,21 @@ def mlp_kernel_name(B, H, T, d, dh, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta
     return None if name is None else name.decode()
 
 
-def mlp_decode(q, k, v, eta, w1, w2, w1b, w2b, pos: int, b: int, out_dtype=None, z=None, stream=None):
+def mlp_ln_kernel_name(B, H, T, d, dh, b, in_dtype=TTT_BF16, out_dtype=TTT_F32, eta_strides=(0, 0, 0),
+                       primal: bool = False):
+    desc = mlp_desc(B, H, T, d, dh, b, in_dtype, out_dtype, 0, eta_strides, TTT_FLAG_PRIMAL if primal else 0)
+    name = lib().ttt_mlp_ln_kernel_name(ctypes.byref(desc))
+    return None if name is None else name.decode()
+
+
+def mlp_decode(q, k, v, eta, w1, w2, w1b, w2b, pos: int, b: int, out_dtype=None, z=None, stream=None, ln=None):
     """Continue B*H TTT-MLP sequences by T new tokens (primal form), state carried in place.
 
     q, k, v : [B, H, T, d];  w1, w1b : [B, H, dh, d], w2, w2b : [B, H, d, dh]
     float32 -- the state and the mini-batch-start state after ``pos`` tokens,
     all updated in place.  eta : float, [H] or [B, H, T] (indexed by the new tokens).
+    ln : (gamma, beta, eps) for f(x) = x + LN(W2 GELU(W1 x)) (ttt_mlp_ln_decode),
+    gamma and beta [H, d] float32.
     returns Z [B, H, T, d].
     """
     torch = _torch()
@@ -734,8 +754,20 @@ def mlp_decode(q, k, v, eta, w1, w2, w1b, w2b, pos: int, b: int, out_dtype=None,
     eta_t, est = eta_layout(eta, B, H, T, q.device)
     if z is None:
         z = torch.empty((B, H, T, d), dtype=out_dtype, device=q.device)
-    _check_dev(q, k, v, eta_t, z, w1, w2, w1b, w2b)
     desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), _dtype_code(z.dtype), 0, est)
+    if ln is not None:
+        gamma, beta, eps = ln
+        if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
+            raise ValueError("gamma and beta must be [H, d]")
+        if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+            raise TypeError("gamma and beta must be float32")
+        _check_dev(q, k, v, eta_t, z, w1, w2, w1b, w2b, gamma, beta)
+        st = lib().ttt_mlp_ln_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(gamma),
+                                     _ptr(beta), float(eps), _ptr(z), _ptr(w1), _ptr(w2), _ptr(w1b), _ptr(w2b),
+                                     int(pos), _stream_handle(stream))
+        _done(st, "ttt_mlp_ln_decode")
+        return z
+    _check_dev(q, k, v, eta_t, z, w1, w2, w1b, w2b)
     st = lib().ttt_mlp_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(eta_t), _ptr(z), _ptr(w1),
                               _ptr(w2), _ptr(w1b), _ptr(w2b), int(pos), _stream_handle(stream))
     _done(st, "ttt_mlp_decode")

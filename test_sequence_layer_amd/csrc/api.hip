@@ -226,17 +226,22 @@ ttt_status validate_decode(const ttt_linear_desc* d, const void* Q, const void* 
 
 // Layer-norm parameters: finite eps >= 0, gamma and beta [H, d] fp32, non-NULL,
 // 4-byte aligned, overlapping none of the outputs.
-ttt_status check_ln_params(const ttt_linear_desc* d, const float* gamma, const float* beta, float eps,
-                           std::initializer_list<Range> outs) {
+ttt_status check_ln(int64_t chains, int64_t H, int64_t d, const float* gamma, const float* beta, float eps,
+                    std::initializer_list<Range> outs) {
   if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
-  if (static_cast<int64_t>(d->B) * d->H == 0) return TTT_OK;
+  if (chains == 0) return TTT_OK;
   if (!gamma || !beta) return TTT_ERR_NULL;
   if (!aligned(gamma, 4) || !aligned(beta, 4)) return TTT_ERR_ALIGN;
-  const int64_t hd_b = static_cast<int64_t>(d->H) * d->d * 4;
+  const int64_t hd_b = H * d * 4;
   for (Range out : outs)
     for (Range in : {Range{gamma, hd_b}, Range{beta, hd_b}})
       if (overlaps(out, in)) return TTT_ERR_ALIAS;
   return TTT_OK;
+}
+
+ttt_status check_ln_params(const ttt_linear_desc* d, const float* gamma, const float* beta, float eps,
+                           std::initializer_list<Range> outs) {
+  return check_ln(static_cast<int64_t>(d->B) * d->H, d->H, d->d, gamma, beta, eps, outs);
 }
 
 ttt_status validate_ln_decode(const ttt_linear_desc* d, const void* Q, const void* K, const void* V,
@@ -854,6 +859,15 @@ ttt_status ttt_mlp_validate(const ttt_mlp_desc* desc, const void* Q, const void*
   return validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, nullptr);
 }
 
+const char* ttt_mlp_ln_kernel_name(const ttt_mlp_desc* d) {
+  if (!d) return nullptr;
+  if (d->flags & TTT_FLAG_PRIMAL)
+    return ttt::mlp_primal_supported(d->d, d->dh) ? "ttt_mlp_ln_primal_d64h256" : nullptr;
+  ttt::MlpArgs a = make_mlp_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr);
+  return ttt::mlp_supported(a) ? "ttt_mlp_fwd_d64h256b16 (layer norm)" : nullptr;
+}
+
 const char* ttt_mlp_kernel_name(const ttt_mlp_desc* d) {
   if (!d) return nullptr;
   if (d->flags & TTT_FLAG_PRIMAL) return ttt::mlp_primal_supported(d->d, d->dh) ? "ttt_mlp_primal_d64h256" : nullptr;
@@ -876,6 +890,7 @@ ttt::MlpPrimalArgs make_mlp_primal_args(const ttt_mlp_desc* d, const void* Q, co
   a.W1_out = a.W2_out = a.W1b_out = a.W2b_out = nullptr;
   a.w_in_bstride = 0;
   a.pos = 0;
+  a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
   return a;
 }
 
@@ -919,6 +934,32 @@ ttt_status validate_mlp_decode(const ttt_mlp_desc* d, const void* Q, const void*
   return TTT_OK;
 }
 
+ttt_status validate_mlp_ln_decode(const ttt_mlp_desc* d, const void* Q, const void* K, const void* V,
+                                  const float* eta, const float* gamma, const float* beta, float eps, const void* Z,
+                                  const float* W1, const float* W2, const float* W1b, const float* W2b,
+                                  int64_t pos) {
+  const ttt_status st = validate_mlp_decode(d, Q, K, V, eta, Z, W1, W2, W1b, W2b, pos);
+  if (st != TTT_OK) return st;
+  const int64_t chains = static_cast<int64_t>(d->B) * d->H;
+  const int64_t w_b = chains * d->d * d->dh * 4;
+  return check_ln(chains, d->H, d->d, gamma, beta, eps,
+                  {Range{Z, chains * d->T * d->d * dtype_size(d->out_dtype)}, Range{W1, w_b}, Range{W2, w_b},
+                   Range{W1b, w_b}, Range{W2b, w_b}});
+}
+
+ttt::MlpPrimalArgs make_mlp_decode_args(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                        const float* eta, void* Z, float* W1, float* W2, float* W1b, float* W2b,
+                                        int64_t pos) {
+  ttt::MlpPrimalArgs a = make_mlp_primal_args(desc, Q, K, V, eta, Z);
+  a.W1_in = a.W1_out = W1;
+  a.W2_in = a.W2_out = W2;
+  a.W1b_in = a.W1b_out = W1b;
+  a.W2b_in = a.W2b_out = W2b;
+  a.w_in_bstride = static_cast<int64_t>(desc->H) * desc->d * desc->dh;
+  a.pos = pos;
+  return a;
+}
+
 }  // namespace
 
 ttt_status ttt_mlp_decode_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
@@ -932,13 +973,26 @@ ttt_status ttt_mlp_decode(const ttt_mlp_desc* desc, const void* Q, const void* K
   const ttt_status st = validate_mlp_decode(desc, Q, K, V, eta, Z, W1, W2, W1b, W2b, pos);
   if (st != TTT_OK) return st;
   if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
-  ttt::MlpPrimalArgs a = make_mlp_primal_args(desc, Q, K, V, eta, Z);
-  a.W1_in = a.W1_out = W1;
-  a.W2_in = a.W2_out = W2;
-  a.W1b_in = a.W1b_out = W1b;
-  a.W2b_in = a.W2b_out = W2b;
-  a.w_in_bstride = static_cast<int64_t>(desc->H) * desc->d * desc->dh;
-  a.pos = pos;
+  const hipError_t e = ttt::launch_mlp_primal(make_mlp_decode_args(desc, Q, K, V, eta, Z, W1, W2, W1b, W2b, pos),
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+ttt_status ttt_mlp_ln_decode_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                      const float* eta, const float* gamma, const float* beta, float eps,
+                                      const void* Z, const float* W1, const float* W2, const float* W1b,
+                                      const float* W2b, int64_t pos) {
+  return validate_mlp_ln_decode(desc, Q, K, V, eta, gamma, beta, eps, Z, W1, W2, W1b, W2b, pos);
+}
+
+ttt_status ttt_mlp_ln_decode(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                             const float* eta, const float* gamma, const float* beta, float eps, void* Z, float* W1,
+                             float* W2, float* W1b, float* W2b, int64_t pos, void* stream) {
+  const ttt_status st = validate_mlp_ln_decode(desc, Q, K, V, eta, gamma, beta, eps, Z, W1, W2, W1b, W2b, pos);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  ttt::MlpPrimalArgs a = make_mlp_decode_args(desc, Q, K, V, eta, Z, W1, W2, W1b, W2b, pos);
+  a.gamma = gamma; a.beta = beta; a.eps = eps;
   const hipError_t e = ttt::launch_mlp_primal(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -971,20 +1025,25 @@ ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K
                           const float* W1_0, const float* W2_0, const float* gamma, const float* beta, float eps,
                           const float* eta, void* Z, float* W1_final, float* W2_final, void* stream) {
   bool ok;
-  const ttt_status st = validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, &ok);
+  ttt_status st = validate_mlp(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final, &ok);
   if (st != TTT_OK) return st;
-  if (desc->flags != 0) return TTT_ERR_FLAGS;  // no primal form with the layer norm
-  if (!(eps >= 0.f) || eps > 1e30f) return TTT_ERR_SHAPE;
   const int64_t chains = static_cast<int64_t>(desc->B) * desc->H;
-  if (chains == 0) return TTT_OK;
-  if (!gamma || !beta) return TTT_ERR_NULL;
-  if (!aligned(gamma, 4) || !aligned(beta, 4)) return TTT_ERR_ALIGN;
-  const int64_t hd_b = static_cast<int64_t>(desc->H) * desc->d * 4;
   const int64_t z_b = chains * desc->T * desc->d * dtype_size(desc->out_dtype);
   const int64_t w_b = chains * desc->d * desc->dh * 4;
-  for (Range out : {Range{Z, z_b}, Range{W1_final, w_b}, Range{W2_final, w_b}})
-    for (Range in : {Range{gamma, hd_b}, Range{beta, hd_b}})
-      if (overlaps(out, in)) return TTT_ERR_ALIAS;
+  st = check_ln(chains, desc->H, desc->d, gamma, beta, eps,
+                {Range{Z, z_b}, Range{W1_final, w_b}, Range{W2_final, w_b}});
+  if (st != TTT_OK || chains == 0) return st;
+  if (desc->flags & TTT_FLAG_PRIMAL) {
+    ttt::MlpPrimalArgs p = make_mlp_primal_args(desc, Q, K, V, eta, Z);
+    p.W1_in = p.W1b_in = W1_0;
+    p.W2_in = p.W2b_in = W2_0;
+    p.w_in_bstride = desc->w_batch_stride;
+    p.W1_out = W1_final;
+    p.W2_out = W2_final;
+    p.gamma = gamma; p.beta = beta; p.eps = eps;
+    const hipError_t e = ttt::launch_mlp_primal(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+  }
   ttt::MlpArgs a = make_mlp_args(desc, Q, K, V, W1_0, W2_0, eta, Z, W1_final, W2_final);
   a.gamma = gamma;
   a.beta = beta;

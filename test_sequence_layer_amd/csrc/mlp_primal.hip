@@ -29,6 +29,17 @@
 // through LDS (sp): three barriers per token.  W1 q of the updated state is
 // taken as W1 q - eta delta (k . q), from the W1 q of the state before the
 // step, which the W1 pass computes together with W1b k.
+//
+// With layer norm and residual inside f (part 03 §9: f(x) = x + LN(W2 GELU(W1 x)),
+// LN over the d outputs with per-head gamma, beta), ttt_mlp_ln_primal_d64h256
+// replaces e by the loss gradient at the pre-norm output y = W2b a:
+//   yh = (y - mean y) / sqrt(var y + eps),  g = gamma (k + gamma yh + beta - v)
+//   e = 2 (g - mean g - yh mean(g yh)) / sqrt(var y + eps)
+// and writes z = q + LN(W2 GELU(W1 q)).  Each wave's 8 pre-norm outputs go
+// to LDS; after one barrier every wave holds all 64, one per lane, takes the
+// statistics and the two LN-backward means as wave sums, and reads the e of
+// its own 8 rows from the lanes that hold them.  The output's pre-norm values
+// take the same way, and wave 0 normalises them: five barriers per token.
 #include "gelu.h"
 #include "mfma_common.h"
 #include "ttt_internal.h"
@@ -67,19 +78,34 @@ __device__ __forceinline__ float4 sub_scaled(float4 x, float c, float4 y) {
   return make_float4(fmaf(-c, y.x, x.x), fmaf(-c, y.y, x.y), fmaf(-c, y.z, x.z), fmaf(-c, y.w, x.w));
 }
 
-template <typename InT, typename OutT>
-__global__ __launch_bounds__(NT) void ttt_mlp_primal_d64h256(MlpPrimalArgs a) {
+// The sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum(float x) { return sum_rows(sum16(x)); }
+
+// Mean and 1/sqrt(var + eps) of the 64 values x (one per lane), centred.
+__device__ __forceinline__ void wave_stats(float x, float eps, float& mu, float& rs) {
+  mu = wave_sum(x) * (1.f / D);
+  const float dv = x - mu;
+  rs = rsqrtf(fmaf(wave_sum(dv * dv), 1.f / D, eps));
+}
+
+template <bool LN, typename InT, typename OutT>
+__device__ __forceinline__ void mlp_primal_body(const MlpPrimalArgs& a) {
   __shared__ float ks[TB][D], qs[TB][D], vs[TB][D];
   __shared__ float es[TB];
   __shared__ float zs[TB][D];
   __shared__ __align__(16) float ak[DH];  // GELU(W1b k)
   __shared__ __align__(16) float aq[DH];  // GELU(W1 q) of the updated state
   __shared__ __align__(16) float sp[NW][DH];
+  __shared__ float lny[D];                // layer norm: a token's 64 pre-norm outputs
 
   const int tid = threadIdx.x;
-  const int l = tid & 63, w = tid >> 6, g = l >> 4, li = l & 15;
+  // (the layer norm's lane reads need the wave index in a scalar register)
+  const int l = tid & 63, w = LN ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6, g = l >> 4, li = l & 15;
   const int chain = blockIdx.x;
   const int bi = chain / a.H, h = chain - bi * a.H;
+  // layer norm: lane l handles output l
+  float gam = 0.f, bet = 0.f;
+  if constexpr (LN) gam = a.gamma[h * D + l], bet = a.beta[h * D + l];
 
   // position of the next token within its mini-batch
   int ph = static_cast<int>(a.pos % a.b);
@@ -161,12 +187,34 @@ __global__ __launch_bounds__(NT) void ttt_mlp_primal_d64h256(MlpPrimalArgs a) {
       // W2b^T e, and the W2 step
       const float4 a4 = *reinterpret_cast<const float4*>(&ak[4 * l]);
       float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (LN) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float y = sum_rows(sum16(dot4(w2b[m], a4)));
-        const float e = 2.f * (y - vs[u][8 * w + m]);
-        s4 = sub_scaled(s4, -e, w2b[m]);
-        w2[m] = sub_scaled(w2[m], et * e, a4);
+        for (int m = 0; m < 8; ++m) {
+          const float y = wave_sum(dot4(w2b[m], a4));
+          if (l == m) lny[8 * w + m] = y;
+        }
+        __syncthreads();
+        float mu, rs;
+        const float yl = lny[l];
+        wave_stats(yl, a.eps, mu, rs);
+        const float yh = (yl - mu) * rs;
+        const float gl = gam * (fmaf(gam, yh, bet) + ks[u][l] - vs[u][l]);
+        const float m1 = wave_sum(gl) * (1.f / D), m2 = wave_sum(gl * yh) * (1.f / D);
+        const float el = 2.f * rs * (gl - m1 - yh * m2);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(el), 8 * w + m));
+          s4 = sub_scaled(s4, -e, w2b[m]);
+          w2[m] = sub_scaled(w2[m], et * e, a4);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float y = sum_rows(sum16(dot4(w2b[m], a4)));
+          const float e = 2.f * (y - vs[u][8 * w + m]);
+          s4 = sub_scaled(s4, -e, w2b[m]);
+          w2[m] = sub_scaled(w2[m], et * e, a4);
+        }
       }
       *reinterpret_cast<float4*>(&sp[w][4 * l]) = s4;
       __syncthreads();
@@ -190,7 +238,22 @@ __global__ __launch_bounds__(NT) void ttt_mlp_primal_d64h256(MlpPrimalArgs a) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const float z = sum_rows(sum16(dot4(w2[m], a4q)));
-        if (l == m) zs[u][8 * w + m] = z;
+        if (l == m) {
+          if constexpr (LN)
+            lny[8 * w + m] = z;
+          else
+            zs[u][8 * w + m] = z;
+        }
+      }
+      if constexpr (LN) {
+        // lny's pre-norm values of W2 b were read before the sp barrier
+        __syncthreads();
+        if (w == 0) {
+          float mu, rs;
+          const float zl = lny[l];
+          wave_stats(zl, a.eps, mu, rs);
+          zs[u][l] = qs[u][l] + fmaf(gam, (zl - mu) * rs, bet);
+        }
       }
       if (++ph == a.b) ph = 0;
     }
@@ -214,20 +277,38 @@ __global__ __launch_bounds__(NT) void ttt_mlp_primal_d64h256(MlpPrimalArgs a) {
   }
 }
 
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(NT) void ttt_mlp_primal_d64h256(MlpPrimalArgs a) {
+  mlp_primal_body<false, InT, OutT>(a);
+}
+
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(NT) void ttt_mlp_ln_primal_d64h256(MlpPrimalArgs a) {
+  mlp_primal_body<true, InT, OutT>(a);
+}
+
+template <typename InT, typename OutT>
+void launch_io(const MlpPrimalArgs& a, hipStream_t s) {
+  dim3 grid(a.B * a.H), block(NT);
+  if (a.gamma)
+    hipLaunchKernelGGL((ttt_mlp_ln_primal_d64h256<InT, OutT>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((ttt_mlp_primal_d64h256<InT, OutT>), grid, block, 0, s, a);
+}
+
 }  // namespace
 
 bool mlp_primal_supported(int d, int dh) { return d == D && dh == DH; }
 
 hipError_t launch_mlp_primal(const MlpPrimalArgs& a, hipStream_t s) {
-  dim3 grid(a.B * a.H), block(NT);
   if (a.in_dtype == 0 && a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_mlp_primal_d64h256<float, float>), grid, block, 0, s, a);
+    launch_io<float, float>(a, s);
   else if (a.in_dtype == 0)
-    hipLaunchKernelGGL((ttt_mlp_primal_d64h256<float, uint16_t>), grid, block, 0, s, a);
+    launch_io<float, uint16_t>(a, s);
   else if (a.out_dtype == 0)
-    hipLaunchKernelGGL((ttt_mlp_primal_d64h256<uint16_t, float>), grid, block, 0, s, a);
+    launch_io<uint16_t, float>(a, s);
   else
-    hipLaunchKernelGGL((ttt_mlp_primal_d64h256<uint16_t, uint16_t>), grid, block, 0, s, a);
+    launch_io<uint16_t, uint16_t>(a, s);
   return hipGetLastError();
 }
 

@@ -165,6 +165,9 @@ struct MlpPrimalArgs {
   float* W1b_out;       // [B, H, dh, d] or nullptr
   float* W2b_out;       // [B, H, d, dh] or nullptr
   int64_t pos;          // tokens already processed
+  const float* gamma;   // [H, d] layer-norm scale, or nullptr for f(x) = W2 GELU(W1 x)
+  const float* beta;    // [H, d] layer-norm shift (with gamma)
+  float eps;
 };
 bool mlp_primal_supported(int d, int dh);
 hipError_t launch_mlp_primal(const MlpPrimalArgs& a, hipStream_t s);

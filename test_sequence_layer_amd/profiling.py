@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "ttt_linear_ln_bwd_fp32": ["linear_ln_bwd.hip", "ttt_internal.h"],
     "ttt_mlp_fwd_d64h256b16": ["mlp.hip", "gelu.h", "mfma_common.h", "ttt_internal.h"],
     "ttt_mlp_primal_d64h256": ["mlp_primal.hip", "gelu.h", "mfma_common.h", "ttt_internal.h"],
+    "ttt_mlp_ln_primal_d64h256": ["mlp_primal.hip", "gelu.h", "mfma_common.h", "ttt_internal.h"],
     "ttt_linear_primal_kernel": ["linear_primal.hip", "ttt_internal.h"],
     "ttt_linear_ln_primal_kernel": ["linear_primal.hip", "ttt_internal.h"],
     "ttt_linear_chunk_scan": ["linear_chunked.hip", "ttt_internal.h"],

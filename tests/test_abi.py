@@ -240,6 +240,51 @@ def test_mlp_decode_validation():
     assert _mdval(_mdesc(T=0), q=None, k=None, v=None, z=None, eta=None) == OK
 
 
+def _mlndval(desc, pos=0, eps=1e-6, gamma=10 * GB, beta=11 * GB, **over):
+    b = MlpDecBufs()
+    for k, v in over.items():
+        setattr(b, k, v)
+    q, k, v, eta, z, w1, w2, w1b, w2b = (getattr(b, n) for n in MlpDecBufs.NAMES)
+    return ttt.lib().ttt_mlp_ln_decode_validate(ctypes.byref(desc), q, k, v, eta, gamma, beta, ctypes.c_float(eps),
+                                                z, w1, w2, w1b, w2b, ctypes.c_int64(pos))
+
+
+def test_mlp_ln_decode_validation():
+    assert _mlndval(_mdesc(T=1)) == OK
+    assert _mlndval(_mdesc(T=37, b=5, in_dtype=0, out_dtype=1)) == OK     # any b, ragged T
+    assert _mlndval(_mdesc(T=1), pos=-1) == POS
+    assert _mlndval(_mdesc(T=1, dh=128)) == UNSUP
+    assert _mlndval(_mdesc(T=1), eps=-1.0) == SHAPE
+    assert _mlndval(_mdesc(T=1), gamma=None) == NULL
+    assert _mlndval(_mdesc(T=0), q=None, k=None, v=None, z=None, eta=None, beta=None) == NULL
+    assert _mlndval(_mdesc(B=0), gamma=None, beta=None) == OK
+    assert _mlndval(_mdesc(T=1), beta=11 * GB + 2) == ALIGN
+    assert _mlndval(_mdesc(T=1), gamma=6 * GB + 64) == ALIAS             # gamma inside W1
+    assert _mlndval(_mdesc(T=1), beta=9 * GB) == ALIAS                   # beta over W2b
+    assert _mlndval(_mdesc(T=1), w1b=6 * GB + 16) == ALIAS               # the plain decode checks still hold
+
+
+def test_mlp_ln_fwd_primal_flag_host_errors():
+    P = ttt.TTT_FLAG_PRIMAL
+    f = ttt.lib().ttt_mlp_ln_fwd
+
+    def call(desc, eps=1e-6, gamma=10 * GB):
+        return f(ctypes.byref(desc), 1 * GB, 2 * GB, 3 * GB, 4 * GB, 5 * GB, gamma, 11 * GB, ctypes.c_float(eps),
+                 6 * GB, 7 * GB, 8 * GB, 9 * GB, None)
+
+    def d(dh=256, b=16, T=64, flags=P):
+        return ttt.mlp_desc(2, 4, T, 64, dh, b, 1, 0, 0, (0, 0, 0), flags)
+    assert call(d(dh=128)) == UNSUP
+    assert call(d(flags=P | 1)) == FLAGS
+    assert call(d(b=5, T=63)) == SHAPE
+    assert call(d(), eps=-1.0) == SHAPE
+    assert call(d(), gamma=None) == NULL
+    assert call(d(), gamma=7 * GB) == ALIAS                             # gamma over Z
+    assert ttt.mlp_ln_kernel_name(2, 4, 64, 64, 256, 16) == "ttt_mlp_fwd_d64h256b16 (layer norm)"
+    assert ttt.mlp_ln_kernel_name(2, 4, 60, 64, 256, 5, primal=True) == "ttt_mlp_ln_primal_d64h256"
+    assert ttt.mlp_ln_kernel_name(2, 4, 64, 64, 128, 16, primal=True) is None
+
+
 # ---- decode validation -------------------------------------------------------------
 
 def _dval(desc, pos=0, **over):

@@ -155,3 +155,31 @@ def test_state_passing_bitwise():
     np.testing.assert_array_equal(np.concatenate([z1, z2], axis=1), z)
     np.testing.assert_array_equal(a2, a)
     np.testing.assert_array_equal(b2, b)
+
+
+def test_conditioning_depends_on_gamma_beta():
+    """The TTT-MLP workload's weights (std 0.02), T = 512, b = 16, scalar eta
+    1/64: with random gamma, beta (1 + 0.2 N(0,1), 0.1 N(0,1)) the recurrence
+    turns a relative change of K by 1e-7 into a change of the exact Z of up to
+    ~1e-3 on some chains; with gamma = 1, beta = 0 (the usual initialisation)
+    the change stays near the perturbation on the same chains.  Measured on
+    these chains: 4.8e-5 .. 1.3e-3 (random) and 1.9e-7 .. 2.8e-7 (unit)."""
+    import ttt_inputs as ti
+
+    cfg = ti.CONFIGS["mlp"].with_(T=512)
+    rr = np.random.default_rng(12)
+    g = 1.0 + 0.2 * rr.standard_normal((cfg.H, 64))
+    be = 0.1 * rr.standard_normal((cfg.H, 64))
+    ch = np.array([54, 95, 173, 186])
+    sub = ti.generate(cfg, chains=ch)
+    hd = ch % cfg.H
+    kp = sub.k * (1 + 1e-7 * np.random.default_rng(5).standard_normal(sub.k.shape))
+    moved = {}
+    for name, gg, bb in (("random", g, be), ("unit", np.ones_like(g), np.zeros_like(be))):
+        z0, _, _ = oracle.mlp_ln_primal(sub.q, sub.k, sub.v, sub.w_rows(1), sub.w_rows(2), gg[hd], bb[hd],
+                                        sub.eta_rows(), 16, 1e-6)
+        z1, _, _ = oracle.mlp_ln_primal(sub.q, kp, sub.v, sub.w_rows(1), sub.w_rows(2), gg[hd], bb[hd],
+                                        sub.eta_rows(), 16, 1e-6)
+        moved[name] = max(np.abs(z1[i] - z0[i]).max() / np.abs(z0[i]).max() for i in range(len(ch)))
+    assert moved["random"] > 3e-4
+    assert moved["unit"] < 2e-6
