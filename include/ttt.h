@@ -420,13 +420,14 @@ const char* ttt_mlp_kernel_name(const ttt_mlp_desc* desc);
  * fp32 throughout); in addition eps must be finite and >= 0 (TTT_ERR_SHAPE),
  * gamma and beta non-NULL (TTT_ERR_NULL), 4-byte aligned (TTT_ERR_ALIGN) and
  * not overlapping Z or the final states (TTT_ERR_ALIAS).
- * Accuracy limit: with small weights (std 0.02 for W1 and W2) the pre-norm
- * output's variance is only ~10x eps, the layer norm's backward divides by
- * that small scale and the recurrence amplifies rounding: against an fp64
- * reference the dual form's Z is ~2.4e-4 off at T = 512 and ~5e-3 at
- * T = 2048 (fp32 arithmetic itself, as in the primal form: up to ~1e-3 at
- * T = 2048).  With larger weights (e.g. std 0.4 / 0.1) it stays at ~1e-5
- * over the full length.
+ * Accuracy limit: it depends on gamma and beta.  With gamma = 1, beta = 0
+ * the recurrence is well conditioned at the full workload length (std 0.02
+ * weights, T = 2048: the dual form's Z within 2.4e-5 of an fp64 reference,
+ * the primal form's within 3.4e-6).  With random gamma, beta (e.g.
+ * 1 + 0.2 N(0,1), 0.1 N(0,1)) some sequences are chaotic: a 1e-7 relative
+ * change of K moves the exact Z by up to 8e-4 at T = 512, and the dual
+ * form's Z is then up to 6.5e-3 off on a few of 512 sequences (fp32
+ * arithmetic, as in the primal form: up to 2.5e-4).
  */
 ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
                           const float* W1_0, const float* W2_0, const float* gamma, const float* beta,
