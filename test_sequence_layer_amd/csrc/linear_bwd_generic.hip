@@ -17,7 +17,7 @@
 //   dK[s][c] = sum_i (dE[s][i] W[i][c] - 2 eta_s E[s][i] A[i][c]) + eta_s sum_t Y[s][t] Q[t][c]
 //   deta_s   = sum_t Y[s][t] S[s][t] - 2 sum_i E[s][i] P[s][i]
 //   A[i][c] += sum_t dZ[t][i] Q[t][c] + sum_s dE[s][i] K[s][c]
-#include "ttt_internal.h"
+#include "args_bwd.h"
 
 namespace ttt {
 namespace {

@@ -48,6 +48,7 @@
 // rebuilt state subtracts exactly the operands the forward added.  The waves
 // read every operand in the layout its product wants: rows with 8-byte
 // loads, columns with the transposing LDS load (ds_read_b64_tr_b16).
+#include "args_bwd.h"
 #include "mfma_common.h"
 
 namespace ttt {

@@ -12,7 +12,7 @@
 // the fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32 products and sums, no
 // bf16 splitting): wave w computes rows 16w .. 16w + 15 of W P + R, the four
 // 16 x 16 column tiles accumulating over k in steps of 4.
-#include "ttt_internal.h"
+#include "args_linear.h"
 
 namespace ttt {
 namespace {

@@ -13,7 +13,7 @@
 //   L[t][s]  = 2 eta_s (q_t . k_s)           for s <= t, else 0
 //   Z[t][i]  = sum_c W[i][c] Q[t][c] - sum_s L[t][s] E[s][i]
 //   W[i][c] -= sum_s 2 eta_s E[s][i] K[s][c]
-#include "ttt_internal.h"
+#include "args_linear.h"
 
 namespace ttt {
 namespace {

@@ -33,7 +33,7 @@
 // last to first with W and A in LDS.  Products are plain fp32 FMA loops over
 // LDS tiles; the per-token layer-norm statistics are wave reductions, a
 // token's 64 outputs on the 64 lanes of one wave.
-#include "ttt_internal.h"
+#include "args_bwd.h"
 
 namespace ttt {
 namespace {

@@ -36,6 +36,7 @@
 // Precision: fp32 operands enter the matrix cores as hi + lo pairs (products
 // of two fp32 operands: three passes; with a bf16 input: two), the layer-norm
 // arithmetic is fp32, and the state rebuild undoes the forward's own steps.
+#include "args_bwd.h"
 #include "mfma_common.h"
 
 namespace ttt {

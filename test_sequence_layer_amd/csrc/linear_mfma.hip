@@ -51,6 +51,7 @@
 // one barrier.  Z goes out through a double-buffered LDS tile as whole rows,
 // one step late, so every store instruction writes contiguous 16-byte pieces.  The update's K^T operand and E's V values are column reads of
 // the row-major tiles with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
+#include "args_linear.h"
 #include "mfma_common.h"
 
 namespace ttt {

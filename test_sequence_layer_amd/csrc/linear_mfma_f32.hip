@@ -22,6 +22,7 @@
 // loaded PF mini-batches ahead into registers (one 16-byte piece of each per
 // thread), staged one step ahead into a double-buffered LDS slot; Z leaves
 // through a double-buffered LDS tile as whole rows, one step late.
+#include "args_linear.h"
 #include "mfma_common.h"
 
 namespace ttt {

@@ -33,7 +33,7 @@
 // state columns and finishes with the quad sum (mean and centred variance in
 // two passes over the same registers).  Three barriers per token: the
 // statistics of Wb k, the two sums of the LN backward, the statistics of W q.
-#include "ttt_internal.h"
+#include "args_primal.h"
 
 namespace ttt {
 namespace {

@@ -13,7 +13,7 @@
 // slots 4..7 take the same rows again for a second split pass.
 #pragma once
 
-#include "ttt_internal.h"
+#include "ttt_common.h"
 
 namespace ttt {
 namespace mfma {

@@ -36,6 +36,7 @@
 // hi + lo pairs (3 passes when both are fp32; 16-token contractions put two
 // passes into the 8 k-slots of one instruction).
 #include "gelu.h"
+#include "args_mlp.h"
 #include "mfma_common.h"
 
 namespace ttt {

@@ -41,8 +41,8 @@
 // its own 8 rows from the lanes that hold them.  The output's pre-norm values
 // take the same way, and wave 0 normalises them: five barriers per token.
 #include "gelu.h"
+#include "args_primal.h"
 #include "mfma_common.h"
-#include "ttt_internal.h"
 
 namespace ttt {
 namespace {
