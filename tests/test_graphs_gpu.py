@@ -122,3 +122,52 @@ def test_decode_graph_replays(ttt):
         torch.cuda.synchronize()
         assert torch.equal(torch.cat(z_g, dim=2), zs[r]), f"replay {r}"
     assert torch.equal(w_g, w_e) and torch.equal(wb_g, wb_e)
+
+
+def test_layer_norm_decode_graph_replays(ttt):
+    """The same for the layer-norm decode entry points of TTT-Linear and
+    TTT-MLP, captured together in one graph of 16 one-token calls each."""
+    dev = "cuda:0"
+    cl = ti.CONFIGS["l1p3b"].with_(B=2, H=2, T=16, eta_kind="token", seed=134)
+    cm = ti.CONFIGS["mlp"].with_(B=2, H=2, T=16, seed=135)
+    tl, tm = to_device(ti.generate(cl)), to_device(ti.generate(cm))
+    g = torch.Generator(device="cpu").manual_seed(7)
+    gam = (1.0 + 0.2 * torch.randn((2, 64), generator=g)).to(dev)
+    bet = (0.1 * torch.randn((2, 64), generator=g)).to(dev)
+    lt = [tuple(x[:, :, i:i + 1].contiguous() for x in (tl["q"], tl["k"], tl["v"], tl["eta"])) for i in range(16)]
+    mt = [tuple(x[:, :, i:i + 1].contiguous() for x in (tm["q"], tm["k"], tm["v"])) for i in range(16)]
+    w0 = tl["w1"].unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+    m1 = tm["w1"].unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+    m2 = tm["w2"].unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+
+    def calls(s, zl, zm):
+        w, wb, a1, a2, a1b, a2b = s
+        for i in range(16):
+            ttt.linear_ln_decode(*lt[i], gam, bet, w, wb, i, 16, z=zl[i])
+            ttt.mlp_decode(*mt[i], tm["eta"], a1, a2, a1b, a2b, i, 16, z=zm[i], ln=(gam, bet, 1e-6))
+
+    def fresh():
+        return [w0.clone(), w0.clone(), m1.clone(), m2.clone(), m1.clone(), m2.clone()]
+
+    def outs():
+        return ([torch.empty((2, 2, 1, 64), device=dev) for _ in range(16)],
+                [torch.empty((2, 2, 1, 64), device=dev) for _ in range(16)])
+
+    s_e, (zl_e, zm_e) = fresh(), outs()
+    ref = []
+    for _ in range(2):
+        calls(s_e, zl_e, zm_e)
+        ref.append((torch.cat(zl_e, dim=2), torch.cat(zm_e, dim=2)))
+    torch.cuda.synchronize()
+
+    s_g, (zl_g, zm_g) = fresh(), outs()
+    graph = _capture(lambda: calls(s_g, zl_g, zm_g))
+    for x, x0 in zip(s_g, fresh()):   # the warm-up inside _capture ran the calls once: start over
+        x.copy_(x0)
+    torch.cuda.synchronize()
+    for r in range(2):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(zl_g, dim=2), ref[r][0]), f"linear, replay {r}"
+        assert torch.equal(torch.cat(zm_g, dim=2), ref[r][1]), f"mlp, replay {r}"
+    assert all(torch.equal(a, b) for a, b in zip(s_g, s_e))

@@ -217,3 +217,22 @@ def test_ln_decode_errors(ttt):
     assert ei.value.status == 2
     with pytest.raises(TypeError):
         ttt.linear_ln_decode(x, x, x, 0.1, g.double(), g.clone(), w, w.clone(), 0, 16)
+
+
+def test_ln_decode_zero_tokens_keeps_state(ttt):
+    """A call with T = 0 launches, reads the state and writes it back unchanged
+    (both layer-norm decode entry points)."""
+    dev = "cuda:0"
+    x = torch.zeros((2, 3, 0, 64), dtype=torch.bfloat16, device=dev)
+    g, b = torch.ones((3, 64), device=dev), torch.zeros((3, 64), device=dev)
+    w, wb = torch.randn((2, 3, 64, 64), device=dev), torch.randn((2, 3, 64, 64), device=dev)
+    w_ref, wb_ref = w.clone(), wb.clone()
+    z = ttt.linear_ln_decode(x, x, x, 0.1, g, b, w, wb, 5, 16)
+    a1, a2 = torch.randn((2, 3, 256, 64), device=dev), torch.randn((2, 3, 64, 256), device=dev)
+    a1b, a2b = torch.randn_like(a1), torch.randn_like(a2)
+    refs = [t.clone() for t in (a1, a2, a1b, a2b)]
+    zm = ttt.mlp_decode(x, x, x, 0.1, a1, a2, a1b, a2b, 5, 16, ln=(g, b, 1e-6))
+    torch.cuda.synchronize()
+    assert z.shape == (2, 3, 0, 64) and zm.shape == (2, 3, 0, 64)
+    assert torch.equal(w, w_ref) and torch.equal(wb, wb_ref)
+    assert all(torch.equal(t, r) for t, r in zip((a1, a2, a1b, a2b), refs))
