@@ -27,6 +27,11 @@ Contents
   linear_primal_grads          the same gradients by a hand-written reverse
                                pass of the primal loop in C (fast; pinned by
                                finite differences and against linear_grads).
+  mlp_grads                    gradients of TTT-MLP: torch fp64 autograd
+                               through mlp_primal_torch.
+  mlp_primal_grads             the same by a hand-written reverse pass of the
+                               TTT-MLP primal loop in C (pinned by finite
+                               differences, against mlp_grads, eta = 0).
   linear_dual_f64, mlp_dual_f64, linear_naive_f64, mlp_primal_np,
   linear_ln_dual_f64
                                numpy fp64 forms used only to check the oracle.
@@ -83,6 +88,8 @@ def _load():
     lib.oracle_mlp_ln_primal.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, ctypes.c_double, dp, dp, dp,
                                          dp, i]
     lib.oracle_linear_primal_grads.restype = None
+    lib.oracle_mlp_primal_grads.argtypes = [i, i, i, i, i] + [dp] * 15 + [i]
+    lib.oracle_mlp_primal_grads.restype = None
     lib.oracle_linear_ln_primal_grads.argtypes = ([i, i, i, i] + [dp] * 6 + [ctypes.c_double] + [dp] * 3 + [dp] * 7
                                                   + [i])
     lib.oracle_linear_ln_primal_grads.restype = None
@@ -145,6 +152,40 @@ def linear_primal_grads(q, k, v, w0, eta, b: int, dz, dwf=None, threads: int = 0
                                            _ptr(dz), dwf_p, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0),
                                            int(threads))
     return dq, dk, dv, deta, dw0
+
+
+def mlp_primal_grads(q, k, v, w1, w2, eta, b: int, dz, dw1f=None, dw2f=None, threads: int = 0):
+    """Gradients of  sum(dz * Z) + sum(dw1f * W1_final) + sum(dw2f * W2_final)
+    of TTT-MLP, by reverse-mode differentiation of the primal token loop
+    (mlp_primal), fp64, in C.
+
+    Shapes as mlp_primal; dz : [n, T, d], dw1f : [n, dh, d] or None,
+    dw2f : [n, d, dh] or None.
+    returns (dq, dk, dv, deta [n, T], dw1 [n, dh, d], dw2 [n, d, dh]).
+    """
+    q, k, v, w1, w2, eta, dz = map(_f64, (q, k, v, w1, w2, eta, dz))
+    n, T, d = q.shape
+    dh = w1.shape[1]
+    assert k.shape == v.shape == dz.shape == (n, T, d) and eta.shape == (n, T)
+    assert w1.shape == (n, dh, d) and w2.shape == (n, d, dh) and b >= 1
+    ptrs = []
+    for x, shape in ((dw1f, (n, dh, d)), (dw2f, (n, d, dh))):
+        if x is None:
+            ptrs.append(None)
+        else:
+            x = _f64(x)
+            assert x.shape == shape
+            ptrs.append(x)
+    dq, dk, dv = (np.empty((n, T, d)) for _ in range(3))
+    deta = np.empty((n, T))
+    dw1 = np.empty((n, dh, d))
+    dw2 = np.empty((n, d, dh))
+    if n:
+        _load().oracle_mlp_primal_grads(n, T, d, dh, b, _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(eta),
+                                        _ptr(dz), None if ptrs[0] is None else _ptr(ptrs[0]),
+                                        None if ptrs[1] is None else _ptr(ptrs[1]), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        _ptr(deta), _ptr(dw1), _ptr(dw2), int(threads))
+    return dq, dk, dv, deta, dw1, dw2
 
 
 def linear_ln_primal_grads(q, k, v, w0, gamma, beta, eta, b: int, dz, dwf=None, eps: float = 1e-6,
@@ -512,6 +553,63 @@ def mlp_primal_np(q, k, v, w1, w2, eta, b):
                 z[c, t] = W2 @ gelu(W1 @ q[c, t])
         W1f[c], W2f[c] = W1, W2
     return z, W1f, W2f
+
+
+def mlp_primal_torch(q, k, v, w1, w2, eta, b):
+    """The primal TTT-MLP loop (03 §6, §9) on torch CPU tensors, any dtype:
+    per token h = W1b k, e = 2 (W2b GELU(h) - v), W2 -= eta e GELU(h)^T,
+    W1 -= eta ((W2b^T e) * GELU'(h)) k^T, z = W2 GELU(W1 q).  Differentiable
+    (GELU' is written out, so autograd also takes its derivative), so torch
+    autograd of this loop is the reference gradient of the layer.
+    """
+    import torch
+
+    def phi_cdf(x):
+        return 0.5 * (1.0 + torch.erf(x / 2.0 ** 0.5))
+
+    def gelu_t(x):
+        return x * phi_cdf(x)
+
+    def gelu_prime_t(x):
+        return phi_cdf(x) + x * torch.exp(-0.5 * x * x) / (2.0 * np.pi) ** 0.5
+
+    n, T, d = q.shape
+    W1, W2 = w1.clone(), w2.clone()
+    zs = []
+    for t0 in range(0, T, b):
+        W1b, W2b = W1, W2
+        for t in range(t0, min(t0 + b, T)):
+            h = torch.einsum("nij,nj->ni", W1b, k[:, t])
+            a = gelu_t(h)
+            e = 2.0 * (torch.einsum("nij,nj->ni", W2b, a) - v[:, t])
+            g = torch.einsum("nij,ni->nj", W2b, e) * gelu_prime_t(h)
+            et = eta[:, t][:, None, None]
+            W2 = W2 - et * e[:, :, None] * a[:, None, :]
+            W1 = W1 - et * g[:, :, None] * k[:, t][:, None, :]
+            zs.append(torch.einsum("nij,nj->ni", W2, gelu_t(torch.einsum("nij,nj->ni", W1, q[:, t]))))
+    return torch.stack(zs, dim=1), W1, W2
+
+
+def mlp_grads(q, k, v, w1, w2, eta, b, dz, dw1f=None, dw2f=None):
+    """Gradients of  sum(dz * Z) + sum(dw1f * W1_final) + sum(dw2f * W2_final)  of
+    TTT-MLP, fp64 autograd through mlp_primal_torch.
+
+    returns (dq, dk, dv, deta [n, T], dw1 [n, dh, d], dw2 [n, d, dh]) as numpy fp64.
+    """
+    import torch
+
+    def t(x):
+        return torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True)
+
+    q_, k_, v_, w1_, w2_, e_ = t(q), t(k), t(v), t(w1), t(w2), t(eta)
+    z, f1, f2 = mlp_primal_torch(q_, k_, v_, w1_, w2_, e_, b)
+    loss = (z * torch.tensor(np.asarray(dz, np.float64))).sum()
+    if dw1f is not None:
+        loss = loss + (f1 * torch.tensor(np.asarray(dw1f, np.float64))).sum()
+    if dw2f is not None:
+        loss = loss + (f2 * torch.tensor(np.asarray(dw2f, np.float64))).sum()
+    loss.backward()
+    return tuple(x.grad.numpy() for x in (q_, k_, v_, e_, w1_, w2_))
 
 
 def mlp_dual_f64(q, k, v, w1, w2, eta, b):

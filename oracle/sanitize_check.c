@@ -20,6 +20,10 @@ void oracle_mlp_primal(int n, int T, int d, int dh, int b, const double* q, cons
 void oracle_linear_ln_primal(int n, int T, int d, int b, const double* q, const double* k, const double* v,
                              const double* w0, const double* gamma, const double* beta, double eps,
                              const double* eta, double* z, double* wf, int nthreads);
+void oracle_mlp_primal_grads(int n, int T, int d, int dh, int b, const double* q, const double* k, const double* v,
+                             const double* w1_0, const double* w2_0, const double* eta, const double* dz,
+                             const double* dw1f, const double* dw2f, double* dq, double* dk, double* dv,
+                             double* deta, double* dw1, double* dw2, int nthreads);
 void oracle_linear_primal_grads(int n, int T, int d, int b, const double* q, const double* k, const double* v,
                                 const double* w0, const double* eta, const double* dz, const double* dwf,
                                 double* dq, double* dk, double* dv, double* deta, double* dw0, int nthreads);
@@ -73,6 +77,17 @@ int main(void) {
     double *w1 = buf(hd, 0.1), *w2 = buf(hd, 0.1), *w1f = buf(hd, 0), *w2f = buf(hd, 0);
     oracle_mlp_primal(n, T, d, dh, b, q, k, v, w1, w2, eta, z, w1f, w2f, 2);
     bad |= !finite_all(z, tok) || !finite_all(w1f, hd) || !finite_all(w2f, hd);
+    {
+      double *mdz = buf(tok, 1.0), *m1 = buf(hd, 1.0), *m2 = buf(hd, 1.0);
+      double *gq = buf(tok, 0), *gk = buf(tok, 0), *gv = buf(tok, 0), *ge = buf(nt, 0), *g1 = buf(hd, 0),
+             *g2 = buf(hd, 0);
+      oracle_mlp_primal_grads(n, T, d, dh, b, q, k, v, w1, w2, eta, mdz, m1, m2, gq, gk, gv, ge, g1, g2, 2);
+      bad |= !finite_all(gq, tok) || !finite_all(gk, tok) || !finite_all(gv, tok) || !finite_all(ge, nt) ||
+             !finite_all(g1, hd) || !finite_all(g2, hd);
+      oracle_mlp_primal_grads(n, T, d, dh, b, q, k, v, w1, w2, eta, mdz, NULL, NULL, gq, gk, gv, ge, g1, g2, 2);
+      bad |= !finite_all(g1, hd) || !finite_all(g2, hd);
+      free(mdz); free(m1); free(m2); free(gq); free(gk); free(gv); free(ge); free(g1); free(g2);
+    }
 
     double *dz = buf(tok, 1.0), *dwf = buf(dd, 1.0);
     double *dq = buf(tok, 0), *dk = buf(tok, 0), *dv = buf(tok, 0), *deta = buf(nt, 0), *dw0 = buf(dd, 0);

@@ -589,3 +589,180 @@ void oracle_linear_ln_primal_grads(int n, int T, int d, int b,
     free(A); free(dWb); free(y); free(h); free(du); free(ak); free(a); free(pa); free(dy); free(dr); free(tmp);
   }
 }
+
+static double gelu_second(double x) {
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  return inv_sqrt_2pi * exp(-0.5 * x * x) * (2.0 - x * x);  /* d/dx (Phi + x phi) = phi (2 - x^2) */
+}
+
+/* Gradients of TTT-MLP by reverse-mode differentiation of its primal token loop
+ * (oracle_mlp_primal, fp64), for L = sum(dz * Z) + sum(dw1f * W1_final) +
+ * sum(dw2f * W2_final):
+ *   dq, dk, dv : [n, T, d]   deta : [n, T]   dw1 : [n, dh, d]   dw2 : [n, d, dh]
+ * (dw1f, dw2f may be NULL).  Token t of the loop (W1b, W2b: the state before
+ * t's mini-batch; W1_t, W2_t after t's step):
+ *   h = W1b k,  a = GELU(h),  e = 2 (W2b a - v),  s = W2b^T e,  g = s * GELU'(h),
+ *   W2_t = W2_{t-1} - eta e a^T,  W1_t = W1_{t-1} - eta g k^T,
+ *   u = W1_t q,  c = GELU(u),  z = W2_t c.
+ * Walking back with A1 = dL/dW1_t, A2 = dL/dW2_t:
+ *   A2 += dz c^T;  du = (W2_t^T dz) * GELU'(u);  A1 += du q^T;  dq = W1_t^T du
+ *   dg = -eta A1 k;  de = -eta A2 a;  da = -eta A2^T e;  dk = -eta A1^T g
+ *   deta = -(e . A2 a) - (g . A1 k)
+ *   ds = dg * GELU'(h);  dh = dg * s * GELU''(h);  de += W2b ds;  dW2b += e ds^T
+ *   dy = 2 de;  dv = -dy;  da += W2b^T dy;  dW2b += dy a^T
+ *   dh += da * GELU'(h);  dW1b += dh k^T;  dk += W1b^T dh
+ * and at the mini-batch start A1 += dW1b, A2 += dW2b. */
+void oracle_mlp_primal_grads(int n, int T, int d, int dh, int b,
+                             const double* q, const double* k, const double* v,
+                             const double* w1_0, const double* w2_0, const double* eta,
+                             const double* dz, const double* dw1f, const double* dw2f,
+                             double* dq, double* dk, double* dv, double* deta, double* dw1, double* dw2,
+                             int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int c = 0; c < n; ++c) {
+    const size_t sz = (size_t)dh * d;
+    const int nb = (T + b - 1) / b;
+    const size_t nbs = (size_t)(nb > 0 ? nb : 1);
+    double* S1 = (double*)malloc(nbs * sz * sizeof(double)); /* W1 at every mini-batch start */
+    double* S2 = (double*)malloc(nbs * sz * sizeof(double));
+    double* W1 = (double*)malloc(sz * sizeof(double));
+    double* W2 = (double*)malloc(sz * sizeof(double));
+    double* W1t = (double*)malloc((size_t)b * sz * sizeof(double)); /* W1_t, W2_t of the mini-batch */
+    double* W2t = (double*)malloc((size_t)b * sz * sizeof(double));
+    double* A1 = (double*)malloc(sz * sizeof(double));
+    double* A2 = (double*)malloc(sz * sizeof(double));
+    double* G1 = (double*)malloc(sz * sizeof(double));  /* dL/dW1b, dL/dW2b of the mini-batch */
+    double* G2 = (double*)malloc(sz * sizeof(double));
+    double* H = (double*)malloc((size_t)b * dh * sizeof(double));   /* h, a, s, g, e per token */
+    double* Aa = (double*)malloc((size_t)b * dh * sizeof(double));
+    double* Sv = (double*)malloc((size_t)b * dh * sizeof(double));
+    double* Gv = (double*)malloc((size_t)b * dh * sizeof(double));
+    double* Ev = (double*)malloc((size_t)b * d * sizeof(double));
+    double* u = (double*)malloc((size_t)dh * sizeof(double));
+    double* cv = (double*)malloc((size_t)dh * sizeof(double));
+    double* du = (double*)malloc((size_t)dh * sizeof(double));
+    double* vd = (double*)malloc((size_t)dh * sizeof(double));   /* scratch of size dh */
+    double* vd2 = (double*)malloc((size_t)dh * sizeof(double));
+    double* vd3 = (double*)malloc((size_t)dh * sizeof(double));
+    double* x1 = (double*)malloc((size_t)d * sizeof(double));    /* scratch of size d */
+    double* x2 = (double*)malloc((size_t)d * sizeof(double));
+    double* x3 = (double*)malloc((size_t)d * sizeof(double));
+    const double* et = eta + (size_t)c * T;
+
+    /* forward: the state at every mini-batch start */
+    memcpy(W1, w1_0 + c * sz, sz * sizeof(double));
+    memcpy(W2, w2_0 + c * sz, sz * sizeof(double));
+    for (int mb = 0; mb < nb; ++mb) {
+      double* W1b = S1 + (size_t)mb * sz;
+      double* W2b = S2 + (size_t)mb * sz;
+      memcpy(W1b, W1, sz * sizeof(double));
+      memcpy(W2b, W2, sz * sizeof(double));
+      const int t0 = mb * b, t1 = t0 + b < T ? t0 + b : T;
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        matvec(W1b, k + o, vd, dh, d);
+        for (int j = 0; j < dh; ++j) vd2[j] = gelu(vd[j]);
+        matvec(W2b, vd2, x1, d, dh);
+        for (int i = 0; i < d; ++i) x1[i] = 2.0 * (x1[i] - v[o + i]);
+        matvec_t(W2b, x1, vd3, d, dh);
+        for (int j = 0; j < dh; ++j) vd3[j] *= gelu_prime(vd[j]);
+        rank1_sub(W2, et[t], x1, vd2, d, dh);
+        rank1_sub(W1, et[t], vd3, k + o, dh, d);
+      }
+    }
+
+    /* backward */
+    if (dw1f) memcpy(A1, dw1f + c * sz, sz * sizeof(double));
+    else memset(A1, 0, sz * sizeof(double));
+    if (dw2f) memcpy(A2, dw2f + c * sz, sz * sizeof(double));
+    else memset(A2, 0, sz * sizeof(double));
+    for (int mb = nb - 1; mb >= 0; --mb) {
+      const double* W1b = S1 + (size_t)mb * sz;
+      const double* W2b = S2 + (size_t)mb * sz;
+      const int t0 = mb * b, t1 = t0 + b < T ? t0 + b : T;
+      /* recompute the mini-batch: h, a, e, s, g and the states after each token */
+      memcpy(W1, W1b, sz * sizeof(double));
+      memcpy(W2, W2b, sz * sizeof(double));
+      for (int t = t0; t < t1; ++t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        const int r = t - t0;
+        double *h = H + (size_t)r * dh, *a = Aa + (size_t)r * dh, *s = Sv + (size_t)r * dh;
+        double *g = Gv + (size_t)r * dh, *e = Ev + (size_t)r * d;
+        matvec(W1b, k + o, h, dh, d);
+        for (int j = 0; j < dh; ++j) a[j] = gelu(h[j]);
+        matvec(W2b, a, e, d, dh);
+        for (int i = 0; i < d; ++i) e[i] = 2.0 * (e[i] - v[o + i]);
+        matvec_t(W2b, e, s, d, dh);
+        for (int j = 0; j < dh; ++j) g[j] = s[j] * gelu_prime(h[j]);
+        rank1_sub(W2, et[t], e, a, d, dh);
+        rank1_sub(W1, et[t], g, k + o, dh, d);
+        memcpy(W1t + (size_t)r * sz, W1, sz * sizeof(double));
+        memcpy(W2t + (size_t)r * sz, W2, sz * sizeof(double));
+      }
+      memset(G1, 0, sz * sizeof(double));
+      memset(G2, 0, sz * sizeof(double));
+      for (int t = t1 - 1; t >= t0; --t) {
+        const size_t o = ((size_t)c * T + t) * d;
+        const int r = t - t0;
+        const double *h = H + (size_t)r * dh, *a = Aa + (size_t)r * dh, *s = Sv + (size_t)r * dh;
+        const double *g = Gv + (size_t)r * dh, *e = Ev + (size_t)r * d;
+        const double* W1c = W1t + (size_t)r * sz;
+        const double* W2c = W2t + (size_t)r * sz;
+        /* the output z_t = W2_t GELU(W1_t q_t) */
+        matvec(W1c, q + o, u, dh, d);
+        for (int j = 0; j < dh; ++j) cv[j] = gelu(u[j]);
+        rank1_sub(A2, -1.0, dz + o, cv, d, dh);               /* A2 += dz c^T */
+        matvec_t(W2c, dz + o, du, d, dh);
+        for (int j = 0; j < dh; ++j) du[j] *= gelu_prime(u[j]);
+        rank1_sub(A1, -1.0, du, q + o, dh, d);                /* A1 += du q^T */
+        matvec_t(W1c, du, dq + o, dh, d);                     /* dq = W1_t^T du */
+        /* the two rank-one steps */
+        matvec(A1, k + o, vd, dh, d);                         /* A1 k */
+        matvec(A2, a, x1, d, dh);                             /* A2 a */
+        double se = 0.0, sg = 0.0;
+        for (int i = 0; i < d; ++i) se += e[i] * x1[i];
+        for (int j = 0; j < dh; ++j) sg += g[j] * vd[j];
+        deta[(size_t)c * T + t] = -se - sg;
+        for (int i = 0; i < d; ++i) x2[i] = -et[t] * x1[i];  /* de from the W2 step */
+        matvec_t(A2, e, vd2, d, dh);                          /* A2^T e */
+        for (int j = 0; j < dh; ++j) vd2[j] *= -et[t];        /* da from the W2 step */
+        matvec_t(A1, g, dk + o, dh, d);                       /* A1^T g */
+        for (int i = 0; i < d; ++i) dk[o + i] *= -et[t];
+        /* g = s * GELU'(h), s = W2b^T e; vd = dg */
+        for (int j = 0; j < dh; ++j) vd[j] *= -et[t];
+        for (int j = 0; j < dh; ++j) {
+          const double ds = vd[j] * gelu_prime(h[j]);
+          vd3[j] = vd[j] * s[j] * gelu_second(h[j]);        /* dh, first part */
+          vd[j] = ds;
+        }
+        matvec(W2b, vd, x3, d, dh);                           /* W2b ds */
+        for (int i = 0; i < d; ++i) x2[i] += x3[i];
+        rank1_sub(G2, -1.0, e, vd, d, dh);                    /* dW2b += e ds^T */
+        /* e = 2 (W2b a - v) */
+        for (int i = 0; i < d; ++i) {
+          x2[i] *= 2.0;                                       /* dy */
+          dv[o + i] = -x2[i];
+        }
+        matvec_t(W2b, x2, vd, d, dh);                         /* W2b^T dy (into vd) */
+        for (int j = 0; j < dh; ++j) vd2[j] += vd[j];         /* da */
+        rank1_sub(G2, -1.0, x2, a, d, dh);                    /* dW2b += dy a^T */
+        for (int j = 0; j < dh; ++j) vd3[j] += vd2[j] * gelu_prime(h[j]);  /* dh */
+        rank1_sub(G1, -1.0, vd3, k + o, dh, d);               /* dW1b += dh k^T */
+        matvec_t(W1b, vd3, x3, dh, d);                        /* W1b^T dh */
+        for (int i = 0; i < d; ++i) dk[o + i] += x3[i];
+      }
+      for (size_t x = 0; x < sz; ++x) {
+        A1[x] += G1[x];
+        A2[x] += G2[x];
+      }
+    }
+    memcpy(dw1 + c * sz, A1, sz * sizeof(double));
+    memcpy(dw2 + c * sz, A2, sz * sizeof(double));
+    free(S1); free(S2); free(W1); free(W2); free(W1t); free(W2t); free(A1); free(A2); free(G1); free(G2);
+    free(H); free(Aa); free(Sv); free(Gv); free(Ev); free(u); free(cv); free(du); free(vd); free(vd2); free(vd3);
+    free(x1); free(x2); free(x3);
+  }
+}
