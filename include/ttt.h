@@ -434,6 +434,46 @@ ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K
                           float eps, const float* eta, void* Z, float* W1_final, float* W2_final,
                           void* stream);
 
+/*
+ * TTT-MLP backward ([TTT] 03 §4: the layer is trained end to end; 03 §9:
+ * f(x) = W2 GELU(W1 x)).  With L any scalar whose gradients with respect to Z,
+ * W1_final and W2_final (of ttt_mlp_fwd on the same inputs) are dZ, dW1_final
+ * and dW2_final, it returns the gradients of L with respect to every input:
+ *   in : Q, K, V [B,H,T,d] in_dtype; W1_0, W2_0 and eta as for ttt_mlp_fwd
+ *        (w_batch_stride 0 or H*d*dh); dZ [B,H,T,d] fp32;
+ *        dW1_final [B,H,dh,d], dW2_final [B,H,d,dh] fp32, each NULL for zero
+ *   out: dQ, dK, dV [B,H,T,d] fp32; deta [B,H,T] fp32 per token (sum it where
+ *        tokens share an eta); dW1_0 [B,H,dh,d], dW2_0 [B,H,d,dh] fp32 per
+ *        sequence (sum over B for a shared initial state)
+ *   workspace: device memory of at least ttt_mlp_bwd_workspace_bytes(desc)
+ *        bytes, 16-byte aligned: the state at every mini-batch start, written
+ *        by a forward pass inside the call; contents on return unspecified.
+ * The call differentiates the token loop (the primal form, 03 §7) in reverse,
+ * in fp32, one workgroup per (sequence, head); T need not be a multiple of b.
+ * Outputs and the workspace overlap no input and no other output
+ * (TTT_ERR_ALIAS).  flags must be 0 (TTT_ERR_FLAGS).  Supported: d = 64,
+ * dh = 256, 1 <= b <= 16, out_dtype TTT_F32 (dZ and the gradients fp32);
+ * anything else TTT_ERR_UNSUPPORTED.  dQ, dK, W1_0, W2_0, the gradient
+ * states and the workspace 16-byte aligned (TTT_ERR_ALIGN / _WORKSPACE).
+ */
+ttt_status ttt_mlp_bwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* W1_0,
+                       const float* W2_0, const float* eta, const float* dZ, const float* dW1_final,
+                       const float* dW2_final, void* workspace, int64_t workspace_bytes, float* dQ, float* dK,
+                       float* dV, float* deta, float* dW1_0, float* dW2_0, void* stream);
+
+/* Runs every host-side check of ttt_mlp_bwd and launches nothing. */
+ttt_status ttt_mlp_bwd_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                const float* W1_0, const float* W2_0, const float* eta, const float* dZ,
+                                const float* dW1_final, const float* dW2_final, const void* workspace,
+                                int64_t workspace_bytes, const float* dQ, const float* dK, const float* dV,
+                                const float* deta, const float* dW1_0, const float* dW2_0);
+
+/* Bytes of workspace ttt_mlp_bwd needs for desc (B*H*ceil(T/b)*2*d*dh*4), or -1 for an invalid desc. */
+int64_t ttt_mlp_bwd_workspace_bytes(const ttt_mlp_desc* desc);
+
+/* Name of the kernel ttt_mlp_bwd would launch for desc, or NULL if unsupported. */
+const char* ttt_mlp_bwd_kernel_name(const ttt_mlp_desc* desc);
+
 /* Name of the kernel ttt_mlp_ln_fwd would launch for desc, or NULL if unsupported. */
 const char* ttt_mlp_ln_kernel_name(const ttt_mlp_desc* desc);
 

@@ -1052,4 +1052,103 @@ ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+int64_t ttt_mlp_bwd_workspace_bytes(const ttt_mlp_desc* d) {
+  if (!d || d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->dh < 1 || d->b < 1) return -1;
+  int64_t n = 1;
+  const int64_t nb = (static_cast<int64_t>(d->T) + d->b - 1) / d->b;
+  for (int64_t f : {static_cast<int64_t>(d->B), static_cast<int64_t>(d->H), nb, int64_t{2},
+                    static_cast<int64_t>(d->d), static_cast<int64_t>(d->dh), int64_t{4}})
+    if (!mul_ok(n, f)) return -1;
+  return n;
+}
+
+namespace {
+
+// Every host-side check of the TTT-MLP backward.
+ttt_status validate_mlp_bwd(const ttt_mlp_desc* d, const void* Q, const void* K, const void* V, const float* W1_0,
+                            const float* W2_0, const float* eta, const float* dZ, const float* dW1f,
+                            const float* dW2f, const void* ws, int64_t ws_bytes, const float* dQ, const float* dK,
+                            const float* dV, const float* deta, const float* dW1, const float* dW2) {
+  if (!d) return TTT_ERR_NULL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->dh < 1 || d->b < 1) return TTT_ERR_SHAPE;
+  if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
+  if (d->flags != 0 || d->reserved != 0) return TTT_ERR_FLAGS;
+  const int64_t hs = static_cast<int64_t>(d->H) * d->d * d->dh;
+  if (d->w_batch_stride != 0 && d->w_batch_stride != hs) return TTT_ERR_STRIDE;
+  if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
+  int64_t chains = 1, tok = 1, wel = 1;
+  if (!mul_ok(chains, d->B) || !mul_ok(chains, d->H) || chains > INT_MAX) return TTT_ERR_SHAPE;
+  tok = chains;
+  if (!mul_ok(tok, d->T) || !mul_ok(tok, d->d)) return TTT_ERR_SHAPE;
+  wel = chains;
+  if (!mul_ok(wel, d->d) || !mul_ok(wel, d->dh)) return TTT_ERR_SHAPE;
+  const int64_t need = ttt_mlp_bwd_workspace_bytes(d);
+  if (need < 0) return TTT_ERR_SHAPE;
+  // dZ and every gradient are fp32; the Q/K/V dtype is in_dtype
+  if (d->out_dtype != TTT_F32 || !ttt::mlp_bwd_supported(d->d, d->dh, d->b)) return TTT_ERR_UNSUPPORTED;
+  if (chains == 0) return TTT_OK;
+  if (!W1_0 || !W2_0 || !dW1 || !dW2) return TTT_ERR_NULL;
+  if (tok > 0 && (!Q || !K || !V || !eta || !dZ || !dQ || !dK || !dV || !deta)) return TTT_ERR_NULL;
+  for (const float* p : {W1_0, W2_0, dW1, dW2}) if (!aligned(p, 16)) return TTT_ERR_ALIGN;
+  for (const float* p : {dW1f, dW2f}) if (p && !aligned(p, 16)) return TTT_ERR_ALIGN;
+  if (tok > 0) {
+    for (const void* p : {Q, K, V}) if (!aligned(p, static_cast<int>(dtype_size(d->in_dtype)))) return TTT_ERR_ALIGN;
+    for (const float* p : {dQ, dK}) if (!aligned(p, 16)) return TTT_ERR_ALIGN;
+    for (const float* p : {dZ, dV, deta, eta}) if (!aligned(p, 4)) return TTT_ERR_ALIGN;
+  }
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return TTT_ERR_WORKSPACE;
+  const int64_t in_b = tok * dtype_size(d->in_dtype), f_b = tok * 4;
+  const int64_t w0_b = (d->w_batch_stride == 0 ? hs : wel) * 4, w_b = wel * 4;
+  const int64_t eta_b =
+      tok > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const Range ins[] = {{Q, in_b}, {K, in_b}, {V, in_b}, {W1_0, w0_b}, {W2_0, w0_b}, {eta, eta_b},
+                       {dZ, f_b}, {dW1f, dW1f ? w_b : 0}, {dW2f, dW2f ? w_b : 0}};
+  const Range outs[] = {{dQ, f_b}, {dK, f_b}, {dV, f_b}, {deta, chains * d->T * 4}, {dW1, w_b}, {dW2, w_b},
+                        {ws, need}};
+  for (int i = 0; i < 7; ++i) {
+    for (const Range& in : ins)
+      if (overlaps(outs[i], in)) return TTT_ERR_ALIAS;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_ALIAS;
+  }
+  return TTT_OK;
+}
+
+}  // namespace
+
+ttt_status ttt_mlp_bwd_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                const float* W1_0, const float* W2_0, const float* eta, const float* dZ,
+                                const float* dW1_final, const float* dW2_final, const void* workspace,
+                                int64_t workspace_bytes, const float* dQ, const float* dK, const float* dV,
+                                const float* deta, const float* dW1_0, const float* dW2_0) {
+  return validate_mlp_bwd(desc, Q, K, V, W1_0, W2_0, eta, dZ, dW1_final, dW2_final, workspace, workspace_bytes, dQ,
+                          dK, dV, deta, dW1_0, dW2_0);
+}
+
+ttt_status ttt_mlp_bwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* W1_0,
+                       const float* W2_0, const float* eta, const float* dZ, const float* dW1_final,
+                       const float* dW2_final, void* workspace, int64_t workspace_bytes, float* dQ, float* dK,
+                       float* dV, float* deta, float* dW1_0, float* dW2_0, void* stream) {
+  const ttt_status st = validate_mlp_bwd(desc, Q, K, V, W1_0, W2_0, eta, dZ, dW1_final, dW2_final, workspace,
+                                         workspace_bytes, dQ, dK, dV, deta, dW1_0, dW2_0);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  ttt::MlpBwdArgs a;
+  a.B = desc->B; a.H = desc->H; a.T = desc->T; a.d = desc->d; a.dh = desc->dh; a.b = desc->b;
+  a.in_dtype = desc->in_dtype;
+  a.Q = Q; a.K = K; a.V = V;
+  a.W1_in = W1_0; a.W2_in = W2_0; a.w_in_bstride = desc->w_batch_stride;
+  a.eta = eta; a.esb = desc->eta_stride_b; a.esh = desc->eta_stride_h; a.est = desc->eta_stride_t;
+  a.dZ = dZ; a.dW1f = dW1_final; a.dW2f = dW2_final;
+  a.ws = static_cast<float*>(workspace);
+  a.dQ = dQ; a.dK = dK; a.dV = dV; a.deta = deta; a.dW1 = dW1_0; a.dW2 = dW2_0;
+  const hipError_t e = ttt::launch_mlp_bwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+const char* ttt_mlp_bwd_kernel_name(const ttt_mlp_desc* d) {
+  if (!d) return nullptr;
+  return ttt::mlp_bwd_supported(d->d, d->dh, d->b) && d->out_dtype == TTT_F32 ? "ttt_mlp_bwd_d64h256" : nullptr;
+}
+
 }  // extern "C"

@@ -1,0 +1,35 @@
+// TTT-MLP backward launches (primal form, token by token in reverse).
+#pragma once
+#include "ttt_common.h"
+
+namespace ttt {
+
+// Backward of TTT-MLP (f(x) = W2 GELU(W1 x)) from the inputs and the initial
+// state; the mini-batch-start states are written to the workspace by a
+// forward pass in the same launch and read back in reverse order.
+struct MlpBwdArgs {
+  int B, H, T, d, dh, b;
+  int in_dtype;            // Q, K, V: 0 fp32, 1 bf16 (dZ and every output fp32)
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* W1_in;      // [H or B*H, dh, d]
+  const float* W2_in;      // [H or B*H, d, dh]
+  int64_t w_in_bstride;    // elements between sequences' initial states (0: shared over B)
+  const float* eta;
+  int64_t esb, esh, est;
+  const float* dZ;         // [B, H, T, d]
+  const float* dW1f;       // [B, H, dh, d] or nullptr (zero)
+  const float* dW2f;       // [B, H, d, dh] or nullptr (zero)
+  float* ws;               // [B*H][ceil(T/b)][2][dh*d]
+  float* dQ;
+  float* dK;
+  float* dV;               // [B, H, T, d]
+  float* deta;             // [B, H, T]
+  float* dW1;              // [B, H, dh, d]
+  float* dW2;              // [B, H, d, dh]
+};
+bool mlp_bwd_supported(int d, int dh, int b);
+hipError_t launch_mlp_bwd(const MlpBwdArgs& a, hipStream_t s);
+
+}  // namespace ttt

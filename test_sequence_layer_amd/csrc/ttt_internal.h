@@ -4,5 +4,6 @@
 #include "args_bwd.h"
 #include "args_linear.h"
 #include "args_mlp.h"
+#include "args_mlp_bwd.h"
 #include "args_primal.h"
 #include "ttt_common.h"

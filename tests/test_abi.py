@@ -285,6 +285,53 @@ def test_mlp_ln_fwd_primal_flag_host_errors():
     assert ttt.mlp_ln_kernel_name(2, 4, 64, 64, 128, 16, primal=True) is None
 
 
+class MlpBwdBufs:
+    NAMES = ("q", "k", "v", "w1", "w2", "eta", "dz", "d1f", "d2f", "ws", "dq", "dk", "dv", "deta", "d1", "d2")
+
+    def __init__(self):
+        for i, n in enumerate(self.NAMES):
+            setattr(self, n, (i + 1) * GB)
+
+
+def _mbval(desc, ws_bytes=None, **over):
+    b = MlpBwdBufs()
+    for k, v in over.items():
+        setattr(b, k, v)
+    if ws_bytes is None:
+        ws_bytes = max(ttt.lib().ttt_mlp_bwd_workspace_bytes(ctypes.byref(desc)), 0)
+    v = [getattr(b, n) for n in MlpBwdBufs.NAMES]
+    return ttt.lib().ttt_mlp_bwd_validate(ctypes.byref(desc), *v[:10], ctypes.c_int64(ws_bytes), *v[10:])
+
+
+def test_mlp_bwd_validation():
+    d = _mdesc(T=64, in_dtype=1, out_dtype=0)
+    assert _mbval(d) == OK
+    assert _mbval(_mdesc(T=37, b=5, in_dtype=0)) == OK                 # ragged T, any b <= 16
+    assert _mbval(d, d1f=None, d2f=None) == OK                         # zero final-state gradients
+    assert ttt.lib().ttt_mlp_bwd_validate(None, *(0,) * 10, ctypes.c_int64(0), *(0,) * 6) == NULL
+    for name in ("q", "k", "v", "w1", "w2", "eta", "dz", "dq", "dk", "dv", "deta", "d1", "d2"):
+        assert _mbval(d, **{name: None}) == NULL, name
+    assert _mbval(d, ws=None) == WORKSPACE
+    assert _mbval(d, ws_bytes=1024) == WORKSPACE
+    assert _mbval(d, ws=10 * GB + 8) == WORKSPACE                       # misaligned
+    assert _mbval(_mdesc(T=64, b=32)) == UNSUP
+    assert _mbval(_mdesc(T=64, dh=128)) == UNSUP
+    assert _mbval(_mdesc(T=64, out_dtype=1)) == UNSUP                  # dZ and gradients fp32 only
+    assert _mbval(_mdesc(T=64, wstride=7)) == STRIDE
+    assert _mbval(ttt.mlp_desc(2, 4, 64, 64, 256, 16, 1, 0, 0, (0, 0, 0), ttt.TTT_FLAG_PRIMAL)) == FLAGS
+    assert _mbval(d, dq=11 * GB + 8) == ALIGN
+    assert _mbval(d, d1=1 * GB) == ALIAS                               # dW1 over Q
+    assert _mbval(d, dk=11 * GB) == ALIAS                              # dK over dQ
+    assert _mbval(d, ws=16 * GB) == ALIAS                              # workspace over dW2
+    assert _mbval(_mdesc(B=0, T=64), ws=None, ws_bytes=0) == OK
+    assert _mbval(_mdesc(T=0), q=None, k=None, v=None, eta=None, dz=None, dq=None, dk=None, dv=None, deta=None,
+                  ws=None, ws_bytes=0) == OK
+    assert ttt.mlp_bwd_workspace_bytes(2, 4, 64, 64, 256, 16) == 2 * 4 * 4 * 2 * 64 * 256 * 4
+    assert ttt.mlp_bwd_workspace_bytes(1, 1, 37, 64, 256, 16) == 3 * 2 * 64 * 256 * 4
+    assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 16) == "ttt_mlp_bwd_d64h256"
+    assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 32) is None
+
+
 # ---- decode validation -------------------------------------------------------------
 
 def _dval(desc, pos=0, **over):
