@@ -29,6 +29,7 @@ import ttt_inputs as ti  # noqa: E402
 METRIC = "TTT-Linear fwd tokens/sec at B16 H32 d64 T8192 b16; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # fp32 vector (packed); unpacked v_fma_f32 gives half
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30           # size of the calibration copy (read and written once each)
 
@@ -106,6 +107,32 @@ def algorithmic_ln_bwd(cfg: ti.Config, eta_strides, grad_size: int = 4):
     bytes_ = (th * d * (3 * in_sz + 4 + grad_size + 3 * grad_size) + eta_b + 4 * th + 3 * chains * d * d * 4
               + 2 * chains * d * 4 + 2 * cfg.H * d * 4)
     flops = th * (18 * d * d + 12 * d * b)
+    return bytes_, flops
+
+
+def algorithmic_mlp_bwd(cfg: ti.Config, eta_strides):
+    """Algorithmic bytes and flops of one TTT-MLP backward (ttt_mlp_bwd).
+
+    Bytes: read Q, K, V (input dtype), dZ (fp32) and eta; write dQ, dK, dV and
+    deta (fp32); read W1_0, W2_0 (per head) and dW1_final, dW2_final, write
+    dW1_0, dW2_0 (fp32, 2 d dh per chain).  The mini-batch-start states the
+    kernel checkpoints (written once, read once: 2 d dh fp32 per mini-batch)
+    are traffic of this design, not of the method, and are not counted.
+    Flops per token-head: 40 d dh for twenty d x dh multiply-adds -- the
+    forward's h = W1b k, W2b a, s = W2b^T e and its two rank-one steps (which
+    rebuild the start states); u = W1_t q and W2_t^T dz; the adjoint updates
+    dz c^T and du q^T; A1 k, A1^T g, A2 a, A2^T e; W1b^T du, W2b ds, W2b^T dy,
+    W1b^T dh; the three rank-one terms of the mini-batch-start adjoint -- plus
+    3 (d + dh)(b + 1) for the corrections by the earlier tokens of the
+    mini-batch ((b + 1) / 2 on average, three d- and three dh-long products each).
+    """
+    th = cfg.B * cfg.H * cfg.T
+    in_sz = 2 if cfg.dtype == "bf16" else 4
+    d, dh, b = cfg.d, cfg.dh, cfg.b
+    st = 2 * d * dh * 4
+    eta_b = 4 * th if eta_strides[2] != 0 else 4 * (cfg.H if eta_strides[1] else 1)
+    bytes_ = th * d * (3 * in_sz + 4 + 3 * 4) + eta_b + 4 * th + cfg.H * st + 2 * cfg.B * cfg.H * st
+    flops = th * (40 * d * dh + 3 * (d + dh) * (b + 1))
     return bytes_, flops
 
 
@@ -207,7 +234,10 @@ def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = Fa
     dz, dwf = ti.upstream_grads(cfg, chains=chains)
     threads = _host_threads(oracle)
     t0 = time.perf_counter()
-    if ln:  # the benchmark's gamma = 1, beta = 0
+    if cfg.is_mlp:  # dW_final = 0: the same work
+        oracle.mlp_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(1), sub.w_rows(2), sub.eta_rows(), cfg.b, dz,
+                                threads=threads)
+    elif ln:  # the benchmark's gamma = 1, beta = 0
         n = len(chains)
         oracle.linear_ln_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(), np.ones((n, cfg.d)), np.zeros((n, cfg.d)),
                                       sub.eta_rows(), cfg.b, dz, dwf, threads=threads)
@@ -218,7 +248,8 @@ def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = Fa
     tokens = len(chains) * cfg.T / cfg.H
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(chains)} of {cfg.chains} (sequence, head) chains at full T={cfg.T}, "
-                      f"fp64 reverse pass of the primal loop, {dt:.2f} s wall on {threads} threads"}
+                      f"fp64 reverse pass of the primal loop{', dW_final = 0' if cfg.is_mlp else ''}, "
+                      f"{dt:.2f} s wall on {threads} threads"}
 
 
 def settle(step, stream, min_s: float = 1.0, max_s: float = 6.0, batch_ms: float = 25.0,
@@ -313,7 +344,9 @@ def main():
                          "time its replays (no per-call host overhead)")
     ap.add_argument("--save", action="store_true",
                     help="time the forward for training (also writes E for the backward)")
-    ap.add_argument("--bwd", action="store_true", help="time the TTT-Linear backward (ttt_linear_bwd)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward (ttt_linear_bwd; ttt_linear_ln_bwd with --ln; ttt_mlp_bwd with "
+                         "--config mlp)")
     ap.add_argument("--train", action="store_true",
                     help="time forward-for-training + backward (one training step of the layer)")
     ap.add_argument("--no-settle", action="store_true",
@@ -333,6 +366,9 @@ def main():
         ap.error("--batch applies to --decode")
     if args.ln and args.primal and (args.save or args.bwd or args.train):
         ap.error("--primal with --ln times the forward only")
+    if ti.CONFIGS[args.config].is_mlp and (args.save or ((args.bwd or args.train) and (args.ln or args.primal))):
+        ap.error("TTT-MLP: --bwd and --train take neither --ln nor --primal, and --save does not apply "
+                 "(the backward rebuilds its states from the inputs)")
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the (sequence, head) chains are independent, so N GPUs would each run this same kernel on "
@@ -423,7 +459,31 @@ def main():
         f1 = torch.empty((B, H, cfg.dh, d), dtype=torch.float32, device="cuda:0")
         f2 = torch.empty((B, H, d, cfg.dh), dtype=torch.float32, device="cuda:0")
         kname = ttt.mlp_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides, primal=args.primal)
-        if args.ln:
+        if args.bwd or args.train:
+            gen = torch.Generator(device="cuda:0")
+            gen.manual_seed(cfg.seed)
+            dz = torch.randn((B, H, T, d), generator=gen, device="cuda:0")
+            dw1f = torch.randn((B, H, cfg.dh, d), generator=gen, device="cuda:0")
+            dw2f = torch.randn((B, H, d, cfg.dh), generator=gen, device="cuda:0")
+            mws = torch.empty(ttt.mlp_bwd_workspace_bytes(B, H, T, d, cfg.dh, cfg.b), dtype=torch.uint8,
+                              device="cuda:0")
+            gout = (torch.empty_like(dz), torch.empty_like(dz), torch.empty_like(dz),
+                    torch.empty((B, H, T), dtype=torch.float32, device="cuda:0"), torch.empty_like(dw1f),
+                    torch.empty_like(dw2f))
+
+            def mlp_bwd():
+                ttt.mlp_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, dz, dw1f, dw2f,
+                            workspace=mws, out=gout)
+
+            if args.bwd:
+                kname = ttt.mlp_bwd_kernel_name(B, H, T, d, cfg.dh, cfg.b)
+                step = mlp_bwd
+            else:
+                def step():
+                    ttt.mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, z=z, w1_final=f1,
+                                w2_final=f2)
+                    mlp_bwd()
+        elif args.ln:
             kname = ttt.mlp_ln_kernel_name(B, H, T, d, cfg.dh, cfg.b, eta_strides=inp.eta_strides, primal=args.primal)
             gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
             bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
@@ -547,7 +607,10 @@ def main():
     value = tokens / (ms_per_step / 1e3)
 
     bytes_, flops = algorithmic(cfg, inp.eta_strides)
-    if args.save:
+    if cfg.is_mlp and (args.bwd or args.train):
+        b2, f2 = algorithmic_mlp_bwd(cfg, inp.eta_strides)
+        bytes_, flops = (b2, f2) if args.bwd else (bytes_ + b2, flops + f2)
+    elif args.save:
         bytes_ += B * H * T * d * 4                     # E written
     elif args.bwd:
         bytes_, flops = (algorithmic_ln_bwd if args.ln else algorithmic_bwd)(cfg, inp.eta_strides)
@@ -578,7 +641,11 @@ def main():
     tflops = flops / (kernel_ms / 1e3) / 1e12
     # the binding roofline: bytes / 8 TB/s vs flops / 2.5 PF/s (bf16 MFMA, which every
     # contraction runs on); TTT-Linear is HBM-bound, TTT-MLP MFMA-bound
-    if bytes_ / HBM_PEAK_GBS >= flops / BF16_PEAK_TFLOPS / 1e3:
+    if cfg.is_mlp and (args.bwd or args.train):
+        # the TTT-MLP backward runs its products on the fp32 vector units
+        roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic}
+    elif bytes_ / HBM_PEAK_GBS >= flops / BF16_PEAK_TFLOPS / 1e3:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
@@ -610,6 +677,11 @@ def main():
             pm = peaks.measure_hbm_copy()
             roof.update({"peak_measured": round(pm, 1), "frac_measured": round(achieved / pm, 4),
                          "peak_measured_by": "2 GiB device copy, 16-byte non-temporal loads/stores"})
+        elif roof["bound"] == "alu":
+            pm = peaks.measure_valu_f32()
+            roof.update({"peak_measured": round(pm, 1), "frac_measured": round(tflops / pm, 4),
+                         "peak_measured_by": "fp32 v_fma_f32 issue loop (unpacked, as the library is built), "
+                                             "16 chains per thread"})
         else:
             pm = peaks.measure_mfma_bf16()
             roof.update({"peak_measured": round(pm, 1), "frac_measured": round(tflops / pm, 4),
@@ -662,11 +734,20 @@ def main():
     saved = "G" if args.ln else "E"
     if args.save:
         form, direction = ln_pre, f"fwd (saving {saved} for the backward)"
-    if args.bwd:
+    if args.bwd and cfg.is_mlp:
+        form, direction = "", "bwd"
+        roof["note"] = ("backward: dQ, dK, dV, deta, dW1_0, dW2_0 from dZ, dW1_final and dW2_final; a forward from "
+                        "W0 in the same launch checkpoints every mini-batch-start state, then the tokens run in "
+                        "reverse (primal form, fp32 on the vector units)")
+    elif args.bwd:
         form, direction = ln_pre + ("generic " if args.generic else ""), "bwd"
         roof["note"] = (f"backward: dQ, dK, dV, deta, dW0{', dgamma, dbeta' if args.ln else ''} from dZ and "
                         f"dW_final, state rebuilt from W_final and {saved}")
-    if args.train:
+    if args.train and cfg.is_mlp:
+        form, direction = "", "fwd+bwd (training step)"
+        roof["note"] = ("dual-form forward (bf16 matrix cores), then the backward (fp32 vector units): two "
+                        "launches per step, both calls' flops against the fp32 vector peak")
+    elif args.train:
         form, direction = ln_pre, "fwd+bwd (training step)"
         roof["note"] = f"forward saving {saved}, then backward: two launches per step"
     headline = cfg.name == "l1p3b" and not form and direction == "fwd"
@@ -676,7 +757,8 @@ def main():
                     f"B{B} H{H} d{d} b{cfg.b}: {B * H} (sequence, head) states, {cfg.dtype} Q/K/V, fp32 state "
                     f"and Z, {eta_desc} eta")
     else:
-        workload = (f"{model} {'layer-norm ' if args.ln else ''}{'primal' if args.primal else 'dual'}-form "
+        workload = (f"{model} {'layer-norm ' if args.ln else ''}"
+                    f"{'primal' if args.primal or (cfg.is_mlp and args.bwd) else 'dual'}-form "
                     f"{direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
                     f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
                     f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta")

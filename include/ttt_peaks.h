@@ -1,6 +1,8 @@
 /*
  * Achievable-peak measurements for gfx950 (MI355X), beside the published
- * peaks (HBM 8 TB/s; dense bf16 matrix 2.5 PFLOP/s).  They let a roofline
+ * peaks (HBM 8 TB/s; dense bf16 matrix 2.5 PFLOP/s; fp32 vector 157.3 TFLOP/s,
+ * a rate that needs packed fp32 instructions -- one v_fma_f32 per lane per
+ * clock gives half of it).  They let a roofline
  * fraction be stated against what the chip really sustains as well as against
  * its specification.  Both calls are asynchronous on `stream` (hipStream_t,
  * NULL = the default stream); the caller times them (e.g. with HIP events) and
@@ -43,6 +45,21 @@ ttt_status ttt_peak_mfma_bf16(float* out, int32_t blocks, int32_t iters, void* s
 
 /* Flops one ttt_peak_mfma_bf16(out, blocks, iters) call performs (-1 for bad arguments). */
 int64_t ttt_peak_mfma_bf16_flops(int32_t blocks, int32_t iters);
+
+/*
+ * fp32 vector issue loop: `blocks` workgroups of 256 threads, each thread
+ * running 16 independent chains of `iters` unpacked v_fma_f32
+ * (acc_j <- acc_j * 1 + c, the 1 passed at run time), for
+ * ttt_peak_valu_f32_flops() flops in all.  Chain j starts from j and
+ * c = (t mod 4) for thread t, so thread t of block q writes the exact value
+ *   out[256 q + t] = 120 + 16 * iters * (t mod 4).
+ * out: blocks * 256 floats, 4-byte aligned.  blocks >= 1 and
+ * 0 <= iters <= 300000 (the exactness bound), else TTT_ERR_SHAPE.
+ */
+ttt_status ttt_peak_valu_f32(float* out, int32_t blocks, int32_t iters, void* stream);
+
+/* Flops one ttt_peak_valu_f32(out, blocks, iters) call performs (2 per fma; -1 for bad arguments). */
+int64_t ttt_peak_valu_f32_flops(int32_t blocks, int32_t iters);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,6 @@
 """Achievable peaks of the chip (include/ttt_peaks.h), measured beside its
-published ones: an HBM copy with 16-byte non-temporal accesses and a bf16
-matrix-core issue loop.  Thin ctypes binding plus the timing helpers that
+published ones: an HBM copy with 16-byte non-temporal accesses, a bf16
+matrix-core issue loop and an fp32 vector (v_fma_f32) issue loop.  Thin ctypes binding plus the timing helpers that
 ``bench.py`` uses to state a roofline fraction against both.
 """
 from __future__ import annotations
@@ -9,7 +9,8 @@ import ctypes
 
 from . import _done, _ptr, _stream_handle, lib
 
-PEAK_EXPORTS = ("ttt_peak_copy", "ttt_peak_mfma_bf16", "ttt_peak_mfma_bf16_flops")
+PEAK_EXPORTS = ("ttt_peak_copy", "ttt_peak_mfma_bf16", "ttt_peak_mfma_bf16_flops", "ttt_peak_valu_f32",
+                "ttt_peak_valu_f32_flops")
 
 
 def _plib() -> ctypes.CDLL:
@@ -22,6 +23,10 @@ def _plib() -> ctypes.CDLL:
         L.ttt_peak_mfma_bf16.restype = ctypes.c_int
         L.ttt_peak_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
         L.ttt_peak_mfma_bf16_flops.restype = ctypes.c_int64
+        L.ttt_peak_valu_f32.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
+        L.ttt_peak_valu_f32.restype = ctypes.c_int
+        L.ttt_peak_valu_f32_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.ttt_peak_valu_f32_flops.restype = ctypes.c_int64
         L._peaks_typed = True
     return L
 
@@ -45,6 +50,18 @@ def mfma_bf16(out, blocks: int, iters: int, stream=None) -> None:
 
 def mfma_bf16_flops(blocks: int, iters: int) -> int:
     return int(_plib().ttt_peak_mfma_bf16_flops(int(blocks), int(iters)))
+
+
+def valu_f32(out, blocks: int, iters: int, stream=None) -> None:
+    """The fp32 vector issue loop; out: float32 device tensor of blocks * 256 elements."""
+    if out.numel() < blocks * 256:
+        raise ValueError("out too small")
+    st = _plib().ttt_peak_valu_f32(_ptr(out), int(blocks), int(iters), _stream_handle(stream))
+    _done(st, "ttt_peak_valu_f32")
+
+
+def valu_f32_flops(blocks: int, iters: int) -> int:
+    return int(_plib().ttt_peak_valu_f32_flops(int(blocks), int(iters)))
 
 
 def _time(fn, warmup: int, reps: int) -> float:
@@ -81,3 +98,12 @@ def measure_mfma_bf16(blocks: int = 512, iters: int = 20000, warmup: int = 2, re
     out = torch.empty(blocks * 1024, dtype=torch.float32, device="cuda:0")
     sec = _time(lambda: mfma_bf16(out, blocks, iters), warmup, reps)
     return mfma_bf16_flops(blocks, iters) / sec / 1e12
+
+
+def measure_valu_f32(blocks: int = 2048, iters: int = 50000, warmup: int = 2, reps: int = 5) -> float:
+    """Sustained unpacked fp32 vector-FMA rate of the issue loop, TFLOP/s."""
+    import torch
+
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    sec = _time(lambda: valu_f32(out, blocks, iters), warmup, reps)
+    return valu_f32_flops(blocks, iters) / sec / 1e12

@@ -5,7 +5,8 @@ errors return their status before any launch.  On the GPU: the copy is exact,
 and the matrix-core issue loop returns the exact integer result its header
 documents -- which also pins the v_mfma_f32_16x16x32_bf16 lane layout (A at
 [l%16][8(l/16)+s], B at [8(l/16)+s][l%16], D at [4(l/16)+r][l%16]) that every
-matrix-core kernel here relies on.
+matrix-core kernel here relies on; the fp32 vector loop returns its exact
+documented sums.
 """
 import ctypes
 import os
@@ -46,6 +47,13 @@ def test_argument_errors_before_launch():
     assert L.ttt_peak_mfma_bf16(GB + 4, 4, 10, None) == ALIGN
     assert peaks.mfma_bf16_flops(512, 20000) == 512 * 4 * 20000 * 8 * 2 * 16 * 16 * 32
     assert peaks.mfma_bf16_flops(0, 1) == -1
+    assert L.ttt_peak_valu_f32(GB, 0, 10, None) == SHAPE
+    assert L.ttt_peak_valu_f32(GB, 4, -1, None) == SHAPE
+    assert L.ttt_peak_valu_f32(GB, 4, 300001, None) == SHAPE     # past the exactness bound
+    assert L.ttt_peak_valu_f32(None, 4, 10, None) == NULL
+    assert L.ttt_peak_valu_f32(GB + 2, 4, 10, None) == ALIGN
+    assert peaks.valu_f32_flops(2048, 50000) == 2048 * 256 * 50000 * 16 * 2
+    assert peaks.valu_f32_flops(1, -1) == -1
 
 
 def _expected_mfma(blocks, iters):
@@ -98,6 +106,21 @@ def test_measurements_are_plausible():
         pytest.skip("no GPU")
     bw = peaks.measure_hbm_copy(nbytes=256 << 20, warmup=3, reps=5)
     tf = peaks.measure_mfma_bf16(blocks=512, iters=2000, warmup=1, reps=2)
-    print(f"copy {bw:.0f} GB/s, bf16 MFMA {tf:.0f} TFLOP/s", flush=True)
+    vf = peaks.measure_valu_f32(blocks=1024, iters=5000, warmup=1, reps=2)
+    print(f"copy {bw:.0f} GB/s, bf16 MFMA {tf:.0f} TFLOP/s, fp32 v_fma {vf:.1f} TFLOP/s", flush=True)
     assert 1000 < bw < 8000 * 1.05
     assert 300 < tf < 2517 * 1.05
+    assert 10 < vf < 157.3 * 1.05
+
+
+@pytest.mark.gpu
+def test_valu_loop_is_exact():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    for blocks, iters in ((3, 0), (5, 1000), (2, 300000)):
+        out = torch.full((blocks * 256,), -1.0, dtype=torch.float32, device="cuda:0")
+        peaks.valu_f32(out, blocks, iters)
+        torch.cuda.synchronize()
+        t = np.arange(blocks * 256) % 256
+        assert np.array_equal(out.cpu().numpy(), (120 + 16 * iters * (t % 4)).astype(np.float32)), (blocks, iters)
