@@ -366,8 +366,9 @@ def main():
         ap.error("--batch applies to --decode")
     if args.ln and args.primal and (args.save or args.bwd or args.train):
         ap.error("--primal with --ln times the forward only")
-    if ti.CONFIGS[args.config].is_mlp and (args.save or ((args.bwd or args.train) and (args.ln or args.primal))):
-        ap.error("TTT-MLP: --bwd and --train take neither --ln nor --primal, and --save does not apply "
+    if ti.CONFIGS[args.config].is_mlp and (args.save or ((args.bwd or args.train) and args.ln)
+                                           or (args.train and args.primal)):
+        ap.error("TTT-MLP: --bwd and --train do not take --ln, --train not --primal, and --save does not apply "
                  "(the backward rebuilds its states from the inputs)")
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -473,10 +474,11 @@ def main():
 
             def mlp_bwd():
                 ttt.mlp_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, dz, dw1f, dw2f,
-                            workspace=mws, out=gout)
+                            workspace=mws, out=gout, primal=args.primal)
 
             if args.bwd:
-                kname = ttt.mlp_bwd_kernel_name(B, H, T, d, cfg.dh, cfg.b)
+                kname = ttt.mlp_bwd_kernel_name(B, H, T, d, cfg.dh, cfg.b, 1 if cfg.dtype == "bf16" else 0,
+                                                primal=args.primal)
                 step = mlp_bwd
             else:
                 def step():
@@ -641,8 +643,8 @@ def main():
     tflops = flops / (kernel_ms / 1e3) / 1e12
     # the binding roofline: bytes / 8 TB/s vs flops / 2.5 PF/s (bf16 MFMA, which every
     # contraction runs on); TTT-Linear is HBM-bound, TTT-MLP MFMA-bound
-    if cfg.is_mlp and (args.bwd or args.train):
-        # the TTT-MLP backward runs its products on the fp32 vector units
+    if cfg.is_mlp and args.bwd and args.primal:
+        # the primal-form TTT-MLP backward runs its products on the fp32 vector units
         roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic}
     elif bytes_ / HBM_PEAK_GBS >= flops / BF16_PEAK_TFLOPS / 1e3:
@@ -735,18 +737,21 @@ def main():
     if args.save:
         form, direction = ln_pre, f"fwd (saving {saved} for the backward)"
     if args.bwd and cfg.is_mlp:
-        form, direction = "", "bwd"
-        roof["note"] = ("backward: dQ, dK, dV, deta, dW1_0, dW2_0 from dZ, dW1_final and dW2_final; a forward from "
-                        "W0 in the same launch checkpoints every mini-batch-start state, then the tokens run in "
-                        "reverse (primal form, fp32 on the vector units)")
+        form, direction = ("primal " if args.primal else ""), "bwd"
+        roof["note"] = ("backward: dQ, dK, dV, deta, dW1_0, dW2_0 from dZ, dW1_final and dW2_final; " +
+                        ("a forward from W0 in the same launch checkpoints every mini-batch-start state, then the "
+                         "tokens run in reverse (primal form, fp32 on the vector units)" if args.primal else
+                         "two launches: the forward kernel writes every mini-batch-start state, then the "
+                         "mini-batches run last to first as b x d x dh products on the matrix cores (dual form, "
+                         "fp32 operands split into bf16 hi + lo); achieved = algorithmic flops / time of the call"))
     elif args.bwd:
         form, direction = ln_pre + ("generic " if args.generic else ""), "bwd"
         roof["note"] = (f"backward: dQ, dK, dV, deta, dW0{', dgamma, dbeta' if args.ln else ''} from dZ and "
                         f"dW_final, state rebuilt from W_final and {saved}")
     if args.train and cfg.is_mlp:
         form, direction = "", "fwd+bwd (training step)"
-        roof["note"] = ("dual-form forward (bf16 matrix cores), then the backward (fp32 vector units): two "
-                        "launches per step, both calls' flops against the fp32 vector peak")
+        roof["note"] = ("dual-form forward, then the dual-form backward (its checkpointing forward and its "
+                        "reverse pass): three launches per step, all on the matrix cores")
     elif args.train:
         form, direction = ln_pre, "fwd+bwd (training step)"
         roof["note"] = f"forward saving {saved}, then backward: two launches per step"
@@ -758,7 +763,7 @@ def main():
                     f"and Z, {eta_desc} eta")
     else:
         workload = (f"{model} {'layer-norm ' if args.ln else ''}"
-                    f"{'primal' if args.primal or (cfg.is_mlp and args.bwd) else 'dual'}-form "
+                    f"{'primal' if args.primal else 'dual'}-form "
                     f"{direction if direction != 'fwd' else 'forward'} B{B} H{H} d{d}"
                     f"{(' dh' + str(cfg.dh)) if cfg.is_mlp else ''} T{T} b{cfg.b}, "
                     f"{cfg.dtype} Q/K/V, fp32 state and Z, {eta_desc} eta")

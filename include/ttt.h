@@ -448,13 +448,20 @@ ttt_status ttt_mlp_ln_fwd(const ttt_mlp_desc* desc, const void* Q, const void* K
  *   workspace: device memory of at least ttt_mlp_bwd_workspace_bytes(desc)
  *        bytes, 16-byte aligned: the state at every mini-batch start, written
  *        by a forward pass inside the call; contents on return unspecified.
- * The call differentiates the token loop (the primal form, 03 §7) in reverse,
- * in fp32, one workgroup per (sequence, head); T need not be a multiple of b.
- * Outputs and the workspace overlap no input and no other output
- * (TTT_ERR_ALIAS).  flags must be 0 (TTT_ERR_FLAGS).  Supported: d = 64,
- * dh = 256, 1 <= b <= 16, out_dtype TTT_F32 (dZ and the gradients fp32);
- * anything else TTT_ERR_UNSUPPORTED.  dQ, dK, W1_0, W2_0, the gradient
- * states and the workspace 16-byte aligned (TTT_ERR_ALIGN / _WORKSPACE).
+ * Two forms, by desc:
+ *   - the dual form (03 §7: every mini-batch as b x d x dh matrix products,
+ *     on the matrix cores with fp32 operands split into bf16 hi + lo): b = 16,
+ *     T a multiple of 16, bf16 inputs, flags 0, and Q, K, V, dZ, dQ, dK, dV
+ *     16-byte aligned.  Two launches: the forward kernel writing the
+ *     mini-batch-start states, then the mini-batches last to first.
+ *   - otherwise, or with flags = TTT_FLAG_PRIMAL, the token loop (the primal
+ *     form) differentiated in reverse in fp32; T need not be a multiple of b.
+ * One workgroup per (sequence, head) in either.  Outputs and the workspace
+ * overlap no input and no other output (TTT_ERR_ALIAS).  flags 0 or
+ * TTT_FLAG_PRIMAL (TTT_ERR_FLAGS).  Supported: d = 64, dh = 256,
+ * 1 <= b <= 16, out_dtype TTT_F32 (dZ and the gradients fp32); anything else
+ * TTT_ERR_UNSUPPORTED.  dQ, dK, W1_0, W2_0, the gradient states and the
+ * workspace 16-byte aligned (TTT_ERR_ALIGN / _WORKSPACE).
  */
 ttt_status ttt_mlp_bwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* W1_0,
                        const float* W2_0, const float* eta, const float* dZ, const float* dW1_final,
@@ -471,7 +478,9 @@ ttt_status ttt_mlp_bwd_validate(const ttt_mlp_desc* desc, const void* Q, const v
 /* Bytes of workspace ttt_mlp_bwd needs for desc (B*H*ceil(T/b)*2*d*dh*4), or -1 for an invalid desc. */
 int64_t ttt_mlp_bwd_workspace_bytes(const ttt_mlp_desc* desc);
 
-/* Name of the kernel ttt_mlp_bwd would launch for desc, or NULL if unsupported. */
+/* Name of the kernel ttt_mlp_bwd would launch for desc (ttt_mlp_bwd_d64h256b16:
+ * the dual form, given 16-byte aligned tensors; ttt_mlp_bwd_d64h256: the primal
+ * form), or NULL if unsupported. */
 const char* ttt_mlp_bwd_kernel_name(const ttt_mlp_desc* desc);
 
 /* Name of the kernel ttt_mlp_ln_fwd would launch for desc, or NULL if unsupported. */

@@ -746,16 +746,20 @@ def mlp_bwd_workspace_bytes(B, H, T, d, dh, b) -> int:
                                                                          (0, 0, 0)))))
 
 
-def mlp_bwd_kernel_name(B, H, T, d, dh, b) -> Optional[str]:
-    name = lib().ttt_mlp_bwd_kernel_name(ctypes.byref(mlp_desc(B, H, T, d, dh, b, TTT_BF16, TTT_F32, 0, (0, 0, 0))))
+def mlp_bwd_kernel_name(B, H, T, d, dh, b, in_dtype=TTT_BF16, primal: bool = False) -> Optional[str]:
+    """ttt_mlp_bwd_d64h256b16 (dual form, matrix cores) or ttt_mlp_bwd_d64h256 (primal form)."""
+    desc = mlp_desc(B, H, T, d, dh, b, in_dtype, TTT_F32, 0, (0, 0, 0), TTT_FLAG_PRIMAL if primal else 0)
+    name = lib().ttt_mlp_bwd_kernel_name(ctypes.byref(desc))
     return None if name is None else name.decode()
 
 
 def mlp_bwd(q, k, v, w1, w2, eta, b: int, dz, dw1_final=None, dw2_final=None, workspace=None, out=None,
-            stream=None):
+            stream=None, primal: bool = False):
     """Backward of :func:`mlp_fwd`: the gradients of L with respect to every
     input, given dz = dL/dZ and dw1_final, dw2_final = dL/dW1_final, dL/dW2_final
-    (None for zero).  dz and the gradients are float32.
+    (None for zero).  dz and the gradients are float32.  The dual form on the
+    matrix cores runs where it applies (b = 16, T a multiple of 16, bf16
+    inputs); primal=True, or any other shape, runs the primal form.
 
     workspace : uint8 device tensor of at least mlp_bwd_workspace_bytes bytes
     (allocated when omitted).  out : optional preallocated
@@ -781,7 +785,8 @@ def mlp_bwd(q, k, v, w1, w2, eta, b: int, dz, dw1_final=None, dw2_final=None, wo
         if x is not None and (tuple(x.shape) != shape or x.dtype != torch.float32):
             raise ValueError(f"final-state gradients must be float32 {shape}")
     eta_t, est = eta_layout(eta, B, H, T, q.device)
-    desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), TTT_F32, wstride, est)
+    desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), TTT_F32, wstride, est,
+                    TTT_FLAG_PRIMAL if primal else 0)
     need = int(lib().ttt_mlp_bwd_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -354,6 +354,7 @@ ttt::MlpArgs make_mlp_args(const ttt_mlp_desc* d, const void* Q, const void* K, 
   a.eta = eta; a.esb = d->eta_stride_b; a.esh = d->eta_stride_h; a.est = d->eta_stride_t;
   a.Z = const_cast<void*>(Z); a.W1f = const_cast<float*>(W1f); a.W2f = const_cast<float*>(W2f);
   a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f;
+  a.ckpt = nullptr;
   return a;
 }
 
@@ -1072,7 +1073,7 @@ ttt_status validate_mlp_bwd(const ttt_mlp_desc* d, const void* Q, const void* K,
   if (!d) return TTT_ERR_NULL;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->d < 1 || d->dh < 1 || d->b < 1) return TTT_ERR_SHAPE;
   if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return TTT_ERR_DTYPE;
-  if (d->flags != 0 || d->reserved != 0) return TTT_ERR_FLAGS;
+  if ((d->flags & ~static_cast<uint32_t>(TTT_FLAG_PRIMAL)) != 0 || d->reserved != 0) return TTT_ERR_FLAGS;
   const int64_t hs = static_cast<int64_t>(d->H) * d->d * d->dh;
   if (d->w_batch_stride != 0 && d->w_batch_stride != hs) return TTT_ERR_STRIDE;
   if (d->eta_stride_b < 0 || d->eta_stride_h < 0 || d->eta_stride_t < 0) return TTT_ERR_STRIDE;
@@ -1114,6 +1115,13 @@ ttt_status validate_mlp_bwd(const ttt_mlp_desc* d, const void* Q, const void* K,
   return TTT_OK;
 }
 
+// The matrix-core (dual-form) backward takes the shape it supports with
+// 16-byte aligned token and gradient tensors; everything else, and
+// TTT_FLAG_PRIMAL, runs the primal kernel.
+bool mlp_bwd_dual_shape(const ttt_mlp_desc* d) {
+  return !(d->flags & TTT_FLAG_PRIMAL) && ttt::mlp_bwd_mfma_supported(d->d, d->dh, d->b, d->in_dtype, d->T);
+}
+
 }  // namespace
 
 ttt_status ttt_mlp_bwd_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
@@ -1142,13 +1150,31 @@ ttt_status ttt_mlp_bwd(const ttt_mlp_desc* desc, const void* Q, const void* K, c
   a.dZ = dZ; a.dW1f = dW1_final; a.dW2f = dW2_final;
   a.ws = static_cast<float*>(workspace);
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.deta = deta; a.dW1 = dW1_0; a.dW2 = dW2_0;
-  const hipError_t e = ttt::launch_mlp_bwd(a, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  bool dual = mlp_bwd_dual_shape(desc);
+  if (desc->T > 0)
+    for (const void* p : {Q, K, V, static_cast<const void*>(dZ), static_cast<const void*>(dQ),
+                          static_cast<const void*>(dK), static_cast<const void*>(dV)})
+      dual = dual && aligned(p, 16);
+  if (!dual) {
+    const hipError_t e = ttt::launch_mlp_bwd(a, s);
+    return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+  }
+  if (desc->T > 0) {
+    // pass 1: the forward kernel writes the state at every mini-batch start
+    ttt::MlpArgs f = make_mlp_args(desc, Q, K, V, W1_0, W2_0, eta, nullptr, nullptr, nullptr);
+    f.ckpt = a.ws;
+    const hipError_t e1 = ttt::launch_mlp_ckpt(f, s);
+    if (e1 != hipSuccess) return TTT_ERR_HIP;
+  }
+  const hipError_t e = ttt::launch_mlp_bwd_mfma(a, s);
   return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
 const char* ttt_mlp_bwd_kernel_name(const ttt_mlp_desc* d) {
   if (!d) return nullptr;
-  return ttt::mlp_bwd_supported(d->d, d->dh, d->b) && d->out_dtype == TTT_F32 ? "ttt_mlp_bwd_d64h256" : nullptr;
+  if (!ttt::mlp_bwd_supported(d->d, d->dh, d->b) || d->out_dtype != TTT_F32) return nullptr;
+  return mlp_bwd_dual_shape(d) ? "ttt_mlp_bwd_d64h256b16" : "ttt_mlp_bwd_d64h256";
 }
 
 }  // extern "C"

@@ -22,11 +22,17 @@ struct MlpArgs {
   const float* gamma;   // [H][d]
   const float* beta;    // [H][d]
   float eps;
+  // Checkpoint mode (the first pass of the backward): the state at every
+  // mini-batch start is written to ckpt ([B*H][T/b][W1 dh x d, W2 d x dh],
+  // row-major fp32) and nothing else is written (Z, W1f, W2f unused).
+  float* ckpt;
 };
 
 // TTT-MLP kernel: d = 64, dh = 256, b = 16, bf16 Q/K/V.
 bool mlp_supported(const MlpArgs& a);
 const char* mlp_name(const MlpArgs& a);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t s);
+// The same kernel in checkpoint mode (plain f, a.ckpt set).
+hipError_t launch_mlp_ckpt(const MlpArgs& a, hipStream_t s);
 
 }  // namespace ttt

@@ -29,7 +29,14 @@ struct MlpBwdArgs {
   float* dW1;              // [B, H, dh, d]
   float* dW2;              // [B, H, d, dh]
 };
+// Primal form (token by token, fp32 vector units): d = 64, dh = 256, b <= 16,
+// any T, fp32 or bf16 inputs; the workspace holds the mini-batch-start states.
 bool mlp_bwd_supported(int d, int dh, int b);
 hipError_t launch_mlp_bwd(const MlpBwdArgs& a, hipStream_t s);
+// Dual form on the matrix cores: d = 64, dh = 256, b = 16, T % 16 == 0, bf16
+// inputs.  The states come from the forward kernel in checkpoint mode, which
+// the caller launches first with the same workspace.
+bool mlp_bwd_mfma_supported(int d, int dh, int b, int in_dtype, int T);
+hipError_t launch_mlp_bwd_mfma(const MlpBwdArgs& a, hipStream_t s);
 
 }  // namespace ttt

@@ -120,13 +120,19 @@ __device__ __forceinline__ float sum32(float x) {
 
 __device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cast<const float4v*>(p); }
 __device__ __forceinline__ void st4(float* p, float4v x) { *reinterpret_cast<float4v*>(p) = x; }
+// checkpoints are read back only after the whole forward: keep them out of the caches
+__device__ __forceinline__ void st4nt(float* p, float4v x) { __builtin_nontemporal_store(x, reinterpret_cast<float4v*>(p)); }
 
 // LN: f(x) = x + LN(W2 GELU(W1 x)) (layer norm over the d outputs, per-head
 // gamma and beta, and a residual).  The loss gradient with respect to the
 // pre-norm output, Delta = J_LN^T (2 (f(k) - v) * gamma), takes the place of
 // E = 2 (W2 A_K - V); everything downstream is unchanged, and the output is
 // Z = Q + LN(W2 A_Q - Delta (diag(eta) triu(A_K^T A_Q))).
-template <bool ETA_TOKEN, bool LN>
+//
+// CKPT: the first pass of the backward.  The state at the start of every
+// mini-batch goes to a.ckpt (W1 then W2, row-major fp32, per chain and
+// mini-batch) and the output side (H_Q, A_Q, Z, the final state) is skipped.
+template <bool ETA_TOKEN, bool LN, bool CKPT>
 __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -240,6 +246,16 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     stage((n + 1) & 1, ya, yb, ye);
     load_step(min(n + PF, nb - 1), xa, xb, xe);
     const Slot& S = sm.slots[n & 1];
+    if constexpr (CKPT) {
+      float* ck = a.ckpt + (static_cast<int64_t>(chain) * nb + n) * (2 * DH * D);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) st4nt(ck + (32 * w + 16 * jt + li) * D + 16 * c4 + 4 * g, w1[jt][c4]);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) st4nt(ck + DH * D + (16 * it + li) * DH + 32 * w + 16 * jt + 4 * g, w2a[it][jt]);
+      }
+    }
 
     // token-row operands of K and Q: row li, columns {16 c4 + 4g .. +3}
     bf16x4 kx[4], qx[4];
@@ -266,13 +282,17 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
         const bf16x8 qb = cat(qx[2 * m], qx[2 * m + 1]);
         hk[jt] = mfma32(wj.hi, kb, hk[jt]);
         hk[jt] = mfma32(wj.lo, kb, hk[jt]);
-        hq[jt] = mfma32(wj.hi, qb, hq[jt]);
-        hq[jt] = mfma32(wj.lo, qb, hq[jt]);
+        if constexpr (!CKPT) {
+          hq[jt] = mfma32(wj.hi, qb, hq[jt]);
+          hq[jt] = mfma32(wj.lo, qb, hq[jt]);
+        }
       }
     }
+    if constexpr (!CKPT) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      s1 = mfma32(cat(kx[2 * m], kx[2 * m + 1]), cat(qx[2 * m], qx[2 * m + 1]), s1);
+      for (int m = 0; m < 2; ++m)
+        s1 = mfma32(cat(kx[2 * m], kx[2 * m + 1]), cat(qx[2 * m], qx[2 * m + 1]), s1);
+    }
 
     float4v ak[2];
     {
@@ -387,6 +407,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       split4(gd, gdh[jt], gdl[jt]);
     }
     // H_Q[j][t] += sum_s G[j][s] S1[s][t] [s <= t]   (= - D diag(eta) triu(K^T Q))
+    if constexpr (!CKPT) {
     bf16x4 s1h, s1l;
     {
       float4v s1m;
@@ -418,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       const float4v y = mfma3(w2s[it], aqop, float4v{0.f, 0.f, 0.f, 0.f});
       st4(&part[li * PROW + 16 * it + 4 * g], y);
     }
+    }  // !CKPT
 
     // ---- state updates (gradients at the mini-batch-start state) ----
     // W1^T[c][j] += sum_s K[s][c] G[j][s]
@@ -446,6 +468,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       for (int jt = 0; jt < 2; ++jt) w2a[it][jt] = mfma3_16(gah[jt], gal[jt], eh, el, w2a[it][jt]);
     }
     __syncthreads();  // #3: S2 and W2 A_Q partials written
+    if constexpr (CKPT) return;  // (the next mini-batch may restage this slot only after #3)
 
     // ---- phase 4: sum the partials ----
     if (tid < BT * BT) {
@@ -530,6 +553,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   }
 
   // ---- final state ----
+  if constexpr (CKPT) return;
   float* W1f = a.W1f + static_cast<int64_t>(chain) * DH * D;
   float* W2f = a.W2f + static_cast<int64_t>(chain) * D * DH;
 #pragma unroll
@@ -541,15 +565,15 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   }
 }
 
-template <bool TOK, bool LN>
+template <bool TOK, bool LN, bool CKPT = false>
 hipError_t launch_tok(const MlpArgs& a, hipStream_t s) {
   const size_t smem = sizeof(Smem);
   // the dynamic LDS limit is raised on every launch (a host-side attribute, no
   // stream work), so the library keeps no state between calls
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ttt_mlp_fwd_d64h256b16<TOK, LN>),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ttt_mlp_fwd_d64h256b16<TOK, LN, CKPT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ttt_mlp_fwd_d64h256b16<TOK, LN>), dim3(a.B * a.H), dim3(kThreads), smem, s, a);
+  hipLaunchKernelGGL((ttt_mlp_fwd_d64h256b16<TOK, LN, CKPT>), dim3(a.B * a.H), dim3(kThreads), smem, s, a);
   return hipGetLastError();
 }
 
@@ -566,6 +590,10 @@ const char* mlp_name(const MlpArgs& a) {
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t s) {
   if (a.gamma) return a.est != 0 ? launch_tok<true, true>(a, s) : launch_tok<false, true>(a, s);
   return a.est != 0 ? launch_tok<true, false>(a, s) : launch_tok<false, false>(a, s);
+}
+
+hipError_t launch_mlp_ckpt(const MlpArgs& a, hipStream_t s) {
+  return a.est != 0 ? launch_tok<true, false, true>(a, s) : launch_tok<false, false, true>(a, s);
 }
 
 }  // namespace ttt

@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
     "ttt_mlp_primal_d64h256": ["mlp_primal.hip", "gelu.h", "mfma_common.h", "args_primal.h", "ttt_common.h"],
     "ttt_mlp_ln_primal_d64h256": ["mlp_primal.hip", "gelu.h", "mfma_common.h", "args_primal.h", "ttt_common.h"],
     "ttt_mlp_bwd_d64h256": ["mlp_bwd.hip", "mfma_common.h", "args_mlp_bwd.h", "ttt_common.h"],
+    "ttt_mlp_bwd_d64h256b16": ["mlp_bwd_mfma.hip", "mfma_common.h", "args_mlp_bwd.h", "ttt_common.h"],
     "ttt_linear_primal_kernel": ["linear_primal.hip", "args_primal.h", "ttt_common.h"],
     "ttt_linear_ln_primal_kernel": ["linear_primal.hip", "args_primal.h", "ttt_common.h"],
     "ttt_linear_chunk_scan": ["linear_chunked.hip", "args_linear.h", "ttt_common.h"],

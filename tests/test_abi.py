@@ -318,7 +318,8 @@ def test_mlp_bwd_validation():
     assert _mbval(_mdesc(T=64, dh=128)) == UNSUP
     assert _mbval(_mdesc(T=64, out_dtype=1)) == UNSUP                  # dZ and gradients fp32 only
     assert _mbval(_mdesc(T=64, wstride=7)) == STRIDE
-    assert _mbval(ttt.mlp_desc(2, 4, 64, 64, 256, 16, 1, 0, 0, (0, 0, 0), ttt.TTT_FLAG_PRIMAL)) == FLAGS
+    assert _mbval(ttt.mlp_desc(2, 4, 64, 64, 256, 16, 1, 0, 0, (0, 0, 0), ttt.TTT_FLAG_PRIMAL)) == OK
+    assert _mbval(ttt.mlp_desc(2, 4, 64, 64, 256, 16, 1, 0, 0, (0, 0, 0), ttt.TTT_FLAG_GENERIC)) == FLAGS
     assert _mbval(d, dq=11 * GB + 8) == ALIGN
     assert _mbval(d, d1=1 * GB) == ALIAS                               # dW1 over Q
     assert _mbval(d, dk=11 * GB) == ALIAS                              # dK over dQ
@@ -328,7 +329,11 @@ def test_mlp_bwd_validation():
                   ws=None, ws_bytes=0) == OK
     assert ttt.mlp_bwd_workspace_bytes(2, 4, 64, 64, 256, 16) == 2 * 4 * 4 * 2 * 64 * 256 * 4
     assert ttt.mlp_bwd_workspace_bytes(1, 1, 37, 64, 256, 16) == 3 * 2 * 64 * 256 * 4
-    assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 16) == "ttt_mlp_bwd_d64h256"
+    assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 16) == "ttt_mlp_bwd_d64h256b16"           # dual form
+    assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 16, primal=True) == "ttt_mlp_bwd_d64h256"
+    assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 16, in_dtype=0) == "ttt_mlp_bwd_d64h256"  # fp32 inputs
+    assert ttt.mlp_bwd_kernel_name(16, 32, 2040, 64, 256, 8) == "ttt_mlp_bwd_d64h256"
+    assert ttt.mlp_bwd_kernel_name(1, 1, 37, 64, 256, 16) == "ttt_mlp_bwd_d64h256"                  # ragged T
     assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 32) is None
 
 

@@ -7,8 +7,10 @@ Pages: [TTT] news article, part 03 §4 (the layer is trained end to end), §6
 (mini-batch GD), §9 (TTT-MLP).  The kernel computes in fp32 throughout; every
 gradient is compared per chain (max|x - ref| / max|ref|, max over chains)
 against the 2e-3 contract and the regression bound below, and the errors are
-printed.  Measured on MI355X: at most 9.4e-7 on the small shapes and 4.7e-6
-(dW1) on the TTT-MLP workload's sampled chains; the bound is 2e-5.
+printed.  Measured on MI355X, the primal form (fp32 throughout): at most
+9.4e-7 on the small shapes and 4.7e-6 (dW1) on the TTT-MLP workload's sampled
+chains, bound 2e-5; the dual form (matrix-core products of split bf16
+operands): at most 1.02e-5 (deta, T = 16) and 6.5e-6 on the workload, bound 5e-5.
 """
 import numpy as np
 import pytest
@@ -22,7 +24,8 @@ torch = pytest.importorskip("torch")
 
 DEV = "cuda:0"
 NAMES = ("dq", "dk", "dv", "deta", "dw1", "dw2")
-REGRESS_MLP_BWD = 2e-5
+REGRESS_MLP_BWD = 2e-5   # the primal form (fp32 throughout)
+REGRESS_DUAL = 5e-5      # the dual form (matrix cores, split bf16 operands)
 
 
 @pytest.fixture(scope="module")
@@ -42,7 +45,7 @@ def _upstream(cfg, seed, with_dwf=True):
     return dz, d1, d2
 
 
-def _run(ttt, cfg, seed=0, with_dwf=True, scale=None, chains=None, eta_override=None):
+def _run(ttt, cfg, seed=0, with_dwf=True, scale=None, chains=None, eta_override=None, primal=False):
     inp = ti.generate(cfg)
     t = to_device(inp)
     w1, w2 = inp.w1, inp.w2
@@ -51,7 +54,8 @@ def _run(ttt, cfg, seed=0, with_dwf=True, scale=None, chains=None, eta_override=
     dz, d1, d2 = _upstream(cfg, seed, with_dwf)
     dev = lambda x: None if x is None else torch.from_numpy(x).to(DEV)  # noqa: E731
     eta = t["eta"] if eta_override is None else eta_override
-    got = ttt.mlp_bwd(t["q"], t["k"], t["v"], dev(w1), dev(w2), eta, cfg.b, dev(dz), dev(d1), dev(d2))
+    got = ttt.mlp_bwd(t["q"], t["k"], t["v"], dev(w1), dev(w2), eta, cfg.b, dev(dz), dev(d1), dev(d2),
+                      primal=primal)
     torch.cuda.synchronize()
     got = dict(zip(NAMES, got))
     chains = np.arange(cfg.chains) if chains is None else np.asarray(chains)
@@ -85,15 +89,22 @@ def _check(label, got, ref, chains, regress=REGRESS_MLP_BWD):
 def test_mlp_bwd_vs_oracle(ttt, b, T, dtype, eta_kind):
     cfg = ti.CONFIGS["mlp"].with_(B=2, H=3, T=T, b=b, dtype=dtype, eta_kind=eta_kind, eta_value=1.0 / 64,
                                   seed=500 + b + T)
-    assert ttt.mlp_bwd_kernel_name(2, 3, T, 64, 256, b) == "ttt_mlp_bwd_d64h256"
+    dual = b == 16 and T % 16 == 0 and dtype == "bf16"
+    assert ttt.mlp_bwd_kernel_name(2, 3, T, 64, 256, b, in_dtype=1 if dtype == "bf16" else 0) == \
+        ("ttt_mlp_bwd_d64h256b16" if dual else "ttt_mlp_bwd_d64h256")
     got, ref, ch = _run(ttt, cfg, seed=T)
-    _check(f"b{b} T{T} {dtype} {eta_kind}", got, ref, ch)
+    _check(f"b{b} T{T} {dtype} {eta_kind}", got, ref, ch, REGRESS_DUAL if dual else REGRESS_MLP_BWD)
+    if dual:  # the same call in the primal form
+        got_p, _, _ = _run(ttt, cfg, seed=T, primal=True)
+        _check(f"b{b} T{T} {dtype} {eta_kind} primal", got_p, ref, ch)
 
 
-def test_mlp_bwd_no_final_gradients_and_large_step(ttt):
+@pytest.mark.parametrize("primal", [False, True])
+def test_mlp_bwd_no_final_gradients_and_large_step(ttt, primal):
     cfg = ti.CONFIGS["mlp"].with_(B=1, H=2, T=64, eta_value=8.0 / 64, seed=510)
-    got, ref, ch = _run(ttt, cfg, seed=1, with_dwf=False)
-    _check("dW_final = 0, eta 8/64", got, ref, ch)
+    got, ref, ch = _run(ttt, cfg, seed=1, with_dwf=False, primal=primal)
+    _check(f"dW_final = 0, eta 8/64{' primal' if primal else ''}", got, ref, ch,
+           REGRESS_MLP_BWD if primal else REGRESS_DUAL)
 
 
 def test_mlp_bwd_per_sequence_initial_state(ttt):
@@ -111,19 +122,40 @@ def test_mlp_bwd_per_sequence_initial_state(ttt):
     ref = oracle.mlp_primal_grads(inp.q, inp.k, inp.v, w1.reshape(4, 256, 64), w2.reshape(4, 64, 256),
                                   inp.eta_rows(), 16, dz.reshape(4, 32, 64), d1.reshape(4, 256, 64),
                                   d2.reshape(4, 64, 256))
-    _check("per-sequence W0", dict(zip(NAMES, got)), dict(zip(NAMES, ref)), np.arange(4))
+    _check("per-sequence W0", dict(zip(NAMES, got)), dict(zip(NAMES, ref)), np.arange(4), REGRESS_DUAL)
 
 
-def test_mlp_bwd_eta_zero(ttt):
+@pytest.mark.parametrize("primal", [False, True])
+def test_mlp_bwd_eta_zero(ttt, primal):
     """eta = 0: every path into K and V carries eta, so dK = dV = 0 exactly."""
     cfg = ti.CONFIGS["mlp"].with_(B=1, H=2, T=32, seed=512)
-    got, ref, ch = _run(ttt, cfg, seed=2, eta_override=torch.zeros((1,), device=DEV))
+    got, ref, ch = _run(ttt, cfg, seed=2, eta_override=torch.zeros((1,), device=DEV), primal=primal)
     assert float(got["dk"].abs().max()) == 0.0 and float(got["dv"].abs().max()) == 0.0
-    _check("eta = 0", got, ref, ch)
+    _check(f"eta = 0{' primal' if primal else ''}", got, ref, ch, REGRESS_MLP_BWD if primal else REGRESS_DUAL)
 
 
-def test_mlp_bwd_full_shape_sampled(ttt):
+def test_mlp_bwd_dual_short_and_empty(ttt):
+    """One mini-batch (T = 16), and T = 0 (the gradients of W0 are the final-state ones)."""
+    cfg = ti.CONFIGS["mlp"].with_(B=2, H=2, T=16, seed=513)
+    got, ref, ch = _run(ttt, cfg, seed=3)
+    _check("T = 16", got, ref, ch, REGRESS_DUAL)
+    q = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    w1 = torch.randn((2, 256, 64), device=DEV) * 0.02
+    w2 = torch.randn((2, 64, 256), device=DEV) * 0.02
+    d1 = torch.randn((1, 2, 256, 64), device=DEV)
+    d2 = torch.randn((1, 2, 64, 256), device=DEV)
+    out = ttt.mlp_bwd(q, q, q, w1, w2, torch.full((1,), 1 / 64, device=DEV), 16,
+                      torch.zeros((1, 2, 0, 64), device=DEV), d1, d2)
+    torch.cuda.synchronize()
+    assert torch.equal(out[4], d1) and torch.equal(out[5], d2)
+
+
+@pytest.mark.parametrize("primal", [False, True])
+def test_mlp_bwd_full_shape_sampled(ttt, primal):
     """The TTT-MLP workload (B16 H32 T2048, scalar eta 1/64), sampled chains."""
     cfg = ti.CONFIGS["mlp"]
-    got, ref, ch = _run(ttt, cfg, seed=5, chains=ti.sample_chains(cfg, 6))
-    _check("TTT-MLP workload", got, ref, ch)
+    assert ttt.mlp_bwd_kernel_name(cfg.B, cfg.H, cfg.T, 64, 256, 16, primal=primal) == \
+        ("ttt_mlp_bwd_d64h256" if primal else "ttt_mlp_bwd_d64h256b16")
+    got, ref, ch = _run(ttt, cfg, seed=5, chains=ti.sample_chains(cfg, 6), primal=primal)
+    _check(f"TTT-MLP workload {'primal' if primal else 'dual'}", got, ref, ch,
+           REGRESS_MLP_BWD if primal else REGRESS_DUAL)
