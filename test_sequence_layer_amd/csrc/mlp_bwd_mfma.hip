@@ -45,6 +45,7 @@
 // index is transposed on the matrix cores (its split tiles times an identity
 // operand: exact), a dh x b activation through a per-wave LDS buffer.
 #include "args_mlp_bwd.h"
+#include "gelu.h"
 #include "mfma_common.h"
 
 namespace ttt {
@@ -113,13 +114,24 @@ __device__ __forceinline__ float4v ld4nt(const float* p) {
 }
 __device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
-// GELU(x) = x Phi(x), GELU'(x) = Phi(x) + x phi(x), GELU''(x) = phi(x) (2 - x^2)
-__device__ __forceinline__ void gelu3(float x, float& g, float& gp, float& gpp) {
-  const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752f));
-  const float pdf = 0.39894228040143268f * __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);
-  g = x * cdf;
-  gp = fmaf(x, pdf, cdf);
-  gpp = pdf * (2.f - x * x);
+// GELU(x) = x Phi(x), GELU'(x) = Phi(x) + x phi(x), GELU''(x) = phi(x) (2 - x^2) of
+// the 8 values of two tiles.  Phi comes from phi_poly (the CDF polynomial of
+// the forward kernels) while every |x| in the wave is below sqrt 2, else from
+// erff for all 8 (a wave-uniform test); phi(x) = exp(-x^2 / 2) / sqrt(2 pi).
+__device__ __forceinline__ void gelu_tiles(const float4v x[2], float4v g[2], float4v gp[2], float4v gpp[2]) {
+  bool big = false;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) big |= !(x[k >> 2][k & 3] * x[k >> 2][k & 3] < 2.f);
+  const bool poly = __builtin_amdgcn_ballot_w64(big) == 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float v = x[k >> 2][k & 3], u = v * v;
+    const float cdf = poly ? phi_poly(v, u) : 0.5f * (1.f + erff(v * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * __builtin_amdgcn_exp2f(u * -0.72134752044448170f);
+    g[k >> 2][k & 3] = v * cdf;
+    gp[k >> 2][k & 3] = fmaf(v, pdf, cdf);
+    gpp[k >> 2][k & 3] = pdf * (2.f - u);
+  }
 }
 
 // The transposes (as bf16 hi and lo, exact) of the two tiles x0, x1: out[q]
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar address parts
   const int li = lane & 15;
   const int g = lane >> 4;
   const int chain = blockIdx.x;
@@ -200,6 +212,21 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
     for (int jt = 0; jt < 2; ++jt) y[jt] = ld4(&xs[(16 * jt + li) * XR + 4 * g]);
   };
 
+  // The state at the start of mini-batch n (the checkpoint):
+  // W1 tile (jt, c4) : W1[j = 32w + 16jt + li][c = 16c4 + 4g + r]   (tile rows c, columns j)
+  // W2 tile (it, jt) : W2[i = 16it + li][j = 32w + 16jt + 4g + r]   (tile rows j, columns i)
+  float4v w1t[2][4], w2n[4][2];
+  auto load_state = [&](int n) {
+    const float* ck = a.ws + (static_cast<int64_t>(chain) * nb + n) * (2 * ST);
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) w1t[jt][c4] = ld4(ck + (32 * w + 16 * jt + li) * D + 16 * c4 + 4 * g);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) w2n[it][jt] = ld4(ck + ST + (16 * it + li) * DH + 32 * w + 16 * jt + 4 * g);
+    }
+  };
+
   for (int n = nb - 1; n >= 0; --n) {
     const int t0 = n * BT;
     __syncthreads();  // the previous mini-batch's LDS reads are done
@@ -222,24 +249,13 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
           __builtin_nontemporal_load(reinterpret_cast<const float2v*>(DZg + static_cast<size_t>(t0 + vr) * D + vc));
       if (tid < BT) sm.eta[tid] = eg[static_cast<int64_t>(t0 + tid) * a.est];
     }
-    // ---- the state at the mini-batch start (the checkpoint; read again, from the caches, where a
-    // transpose is needed) ----
-    // W1 tile (jt, c4) : W1[j = 32w + 16jt + li][c = 16c4 + 4g + r]   (tile rows c, columns j)
-    // W2 tile (it, jt) : W2[i = 16it + li][j = 32w + 16jt + 4g + r]   (tile rows j, columns i)
+    // the state tiles again (from the caches) where a transpose is needed
     const float* ck = a.ws + (static_cast<int64_t>(chain) * nb + n) * (2 * ST);
     auto w1_tile = [&](int jt, int c4) { return ld4(ck + (32 * w + 16 * jt + li) * D + 16 * c4 + 4 * g); };
     auto w2_tile = [&](int it, int jt) { return ld4(ck + ST + (16 * it + li) * DH + 32 * w + 16 * jt + 4 * g); };
-    float4v w2n[4][2];
     float4v hk[2], hq[2], s1 = zero4v(), s1t = zero4v();
+    load_state(n);
     {
-      float4v w1t[2][4];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) w1t[jt][c4] = w1_tile(jt, c4);
-#pragma unroll
-        for (int it = 0; it < 4; ++it) w2n[it][jt] = w2_tile(it, jt);
-      }
       __syncthreads();
 
       // token rows: kx[c4] = K[t = li][16c4 + 4g .. +3] (tile rows c, columns t)
@@ -279,21 +295,14 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
 
     // ---- A1 (cont.): GELU, partials of W2 A_K ----
     float4v ak[2], gk1[2], gk2[2];
+    gelu_tiles(hk, ak, gk1, gk2);
+    {
+      const Op8 akop = split8(ak[0], ak[1]);
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x0, x1, x2;
-        gelu3(hk[jt][r], x0, x1, x2);
-        ak[jt][r] = x0;
-        gk1[jt][r] = x1;
-        gk2[jt][r] = x2;
+      for (int it = 0; it < 4; ++it) {
+        const float4v y = mfma3(split8(w2n[it][0], w2n[it][1]), akop, zero4v());  // [i = 16it + 4g + r][t = li]
+        st4(&sm.pa[w][li * PROW + 16 * it + 4 * g], y);
       }
-    const Op8 akop = split8(ak[0], ak[1]);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const float4v y = mfma3(split8(w2n[it][0], w2n[it][1]), akop, zero4v());  // [i = 16it + 4g + r][t = li]
-      st4(&sm.pa[w][li * PROW + 16 * it + 4 * g], y);
     }
     if (w == 0) {
 #pragma unroll
@@ -317,27 +326,38 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
     __syncthreads();  // #2
 
     // ---- A3 ----
-    // e_i[it], dz_i[it] : E, dZ [i = 16it + 4g + r][t = li]   (tile rows i, columns t)
-    float4v e_i[4], dz_i[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      e_i[it] = ld4(&sm.e[li * PROW + 16 * it + 4 * g]);
-      dz_i[it] = ld4(&sm.dz[li * PROW + 16 * it + 4 * g]);
-    }
-    // S = W2^T E and W2^T dZ ([j][t]); W2 transposed: w2i[it][jt] = W2[16it + 4g + r][32w + 16jt + li]
+    // E, dZ tiles of a pair of i blocks: [i = 32m + 16hf + 4g + r][t = li]   (tile rows i, columns t)
+    auto e_tile = [&](int it) { return ld4(&sm.e[li * PROW + 16 * it + 4 * g]); };
+    auto dz_tile = [&](int it) { return ld4(&sm.dz[li * PROW + 16 * it + 4 * g]); };
+    // S = W2^T E and W2^T dZ ([j][t]), ED = E^T dZ ([s][t]) and its transpose
     float4v sv[2] = {zero4v(), zero4v()}, wz[2] = {zero4v(), zero4v()};
+    float4v m2, m2t;  // M2 [s = 4g + r][t = li] and M2 [s = li][t = 4g + r]
+    {
+      float4v ed = zero4v(), edt = zero4v();
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      // th[hf][jt] = W2[16(2m + hf) + 4g + r][32w + 16jt + li]
-      bf16x4 th[2][2], tl[2][2];
-      transpose2(w2n[2 * m][0], w2n[2 * m][1], ident, th[0], tl[0]);
-      transpose2(w2n[2 * m + 1][0], w2n[2 * m + 1][1], ident, th[1], tl[1]);
-      const Op8 eo = split8(e_i[2 * m], e_i[2 * m + 1]), zo = split8(dz_i[2 * m], dz_i[2 * m + 1]);
+      for (int m = 0; m < 2; ++m) {
+        // th[hf][jt] = W2[16(2m + hf) + 4g + r][32w + 16jt + li]
+        bf16x4 th[2][2], tl[2][2];
+        transpose2(w2n[2 * m][0], w2n[2 * m][1], ident, th[0], tl[0]);
+        transpose2(w2n[2 * m + 1][0], w2n[2 * m + 1][1], ident, th[1], tl[1]);
+        const Op8 eo = split8(e_tile(2 * m), e_tile(2 * m + 1)), zo = split8(dz_tile(2 * m), dz_tile(2 * m + 1));
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const Op8 A{cat(th[0][jt], th[1][jt]), cat(tl[0][jt], tl[1][jt])};
-        sv[jt] = mfma3(A, eo, sv[jt]);
-        wz[jt] = mfma3(A, zo, wz[jt]);
+        for (int jt = 0; jt < 2; ++jt) {
+          const Op8 A{cat(th[0][jt], th[1][jt]), cat(tl[0][jt], tl[1][jt])};
+          sv[jt] = mfma3(A, eo, sv[jt]);
+          wz[jt] = mfma3(A, zo, wz[jt]);
+        }
+        ed = mfma3(eo, zo, ed);    // [s = 4g + r][t = li]
+        edt = mfma3(zo, eo, edt);  // [t = 4g + r][s = li]
+      }
+      if (w == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.ed[(4 * g + r) * SROW + li] = ed[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        m2[r] = (4 * g + r <= li) ? -et_row[r] * ed[r] : 0.f;
+        m2t[r] = (li <= 4 * g + r) ? -et_col * edt[r] : 0.f;
       }
     }
     float4v gg[2];  // G [j][t]
@@ -353,44 +373,19 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
       float4v nl1;  // -L1 [s = 4g + r][t = li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) nl1[r] = (4 * g + r <= li) ? -et_row[r] * s1[r] : 0.f;
+      float4v u[2], unused[2];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const float4v u = mfma3_16(ggt[jt], nl1, hq[jt]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x0, x1, unused;
-          gelu3(u[r], x0, x1, unused);
-          cq[jt][r] = x0;
-          gu1[jt][r] = x1;
-        }
-      }
+      for (int jt = 0; jt < 2; ++jt) u[jt] = mfma3_16(ggt[jt], nl1, hq[jt]);
+      gelu_tiles(u, cq, gu1, unused);
     }
     // P partial = A_K^T C over this wave's hidden units
     {
-      const float4v pv = mfma3(akop, split8(cq[0], cq[1]), zero4v());  // [s = 4g + r][t = li]
+      const float4v pv = mfma3(split8(ak[0], ak[1]), split8(cq[0], cq[1]), zero4v());  // [s = 4g + r][t = li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.pp[w][(4 * g + r) * SROW + li] = pv[r];
     }
-    // ED = E^T dZ and its transpose (every wave)
-    float4v ed = zero4v(), edt = zero4v();
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const Op8 eo = split8(e_i[2 * m], e_i[2 * m + 1]), zo = split8(dz_i[2 * m], dz_i[2 * m + 1]);
-      ed = mfma3(eo, zo, ed);    // [s = 4g + r][t = li]
-      edt = mfma3(zo, eo, edt);  // [t = 4g + r][s = li]
-    }
-    if (w == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.ed[(4 * g + r) * SROW + li] = ed[r];
-    }
-    float4v m2, m2t;  // M2 [s = 4g + r][t = li] and M2 [s = li][t = 4g + r]
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m2[r] = (4 * g + r <= li) ? -et_row[r] * ed[r] : 0.f;
-      m2t[r] = (li <= 4 * g + r) ? -et_col * edt[r] : 0.f;
-    }
     // dH_Q = (W2^T dZ + A_K M2) * GELU'(U)
-    float4v akt[2], dhq[2], dhqt[2];
+    float4v akt[2], dhq[2];
     jt2tj(ak, akt);
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
@@ -398,10 +393,11 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dhq[jt][r] = dc[r] * gu1[jt][r];
     }
-    jt2tj(dhq, dhqt);
     // dG = -(dH_Q triu(S1)^T + A1 K) diag(eta); the deta part -g_s . (A1 k_s)
     float4v dg[2];
     {
+      float4v dhqt[2];
+      jt2tj(dhq, dhqt);
       float4v s1m;  // S1[s = li][t = 4g + r], s <= t
 #pragma unroll
       for (int r = 0; r < 4; ++r) s1m[r] = (li <= 4 * g + r) ? s1t[r] : 0.f;
@@ -444,22 +440,98 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
       }
     // dE partial = W2 dS - (A2 A_K) diag(eta), [s][i]; the deta part -e_s . (A2 a_s)
     {
-      const Op8 dso = split8(ds[0], ds[1]);
+      const Op8 dso = split8(ds[0], ds[1]), ako = split8(ak[0], ak[1]);
       float pe = 0.f;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const float4v wd = mfma3(split8(w2n[it][0], w2n[it][1]), dso, zero4v());
-        const float4v aa = mfma3(split8(a2[it][0], a2[it][1]), akop, zero4v());
+        const float4v wd = mfma3(split8(w2_tile(it, 0), w2_tile(it, 1)), dso, zero4v());
+        const float4v aa = mfma3(split8(a2[it][0], a2[it][1]), ako, zero4v());
+        const float4v ev = e_tile(it);
         float4v pv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pv[r] = wd[r] - et_col * aa[r];
-          pe = fmaf(e_i[it][r], aa[r], pe);
+          pe = fmaf(ev[r], aa[r], pe);
         }
         st4(&sm.pa[w][li * PROW + 16 * it + 4 * g], pv);
       }
       pe = sum_rows(pe);
       if (g == 0) sm.de2[w][li] = -pe;
+    }
+    // dA_K so far: C M2^T - (A2^T E) diag(eta)  (W2^T dY is added once dY is known)
+    float4v dak[2];
+    float4v cqt[2], dst[2];
+    jt2tj(cq, cqt);
+    jt2tj(ds, dst);
+    {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) dak[jt] = mfma3_16(cqt[jt], m2t, zero4v());
+      float4v ae[2] = {zero4v(), zero4v()};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        // A2 transposed: ah[hf][jt] = A2[16(2m + hf) + 4g + r][32w + 16jt + li]
+        bf16x4 ah[2][2], al[2][2];
+        transpose2(a2[2 * m][0], a2[2 * m][1], ident, ah[0], al[0]);
+        transpose2(a2[2 * m + 1][0], a2[2 * m + 1][1], ident, ah[1], al[1]);
+        const Op8 eo = split8(e_tile(2 * m), e_tile(2 * m + 1));
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) ae[jt] = mfma3(Op8{cat(ah[0][jt], ah[1][jt]), cat(al[0][jt], al[1][jt])}, eo, ae[jt]);
+      }
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dak[jt][r] -= et_col * ae[jt][r];
+    }
+    // the dK partial's -(A1^T G) diag(eta) ([c][t] tiles, to pb; W1^T dH_K is added later)
+    {
+      const Op8 go = split8(gg[0], gg[1]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        bf16x4 a1jh[2][2], a1jl[2][2];  // [jt][q] = A1[32w + 16jt + 4g + r][16(2m + q) + li]
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) transpose2(a1[jt][2 * m], a1[jt][2 * m + 1], ident, a1jh[jt], a1jl[jt]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float4v ag = mfma3(Op8{cat(a1jh[0][q], a1jh[1][q]), cat(a1jl[0][q], a1jl[1][q])}, go, zero4v());
+          float4v kv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) kv[r] = -et_col * ag[r];
+          st4(&sm.pb[w][li * PROW + 16 * (2 * m + q) + 4 * g], kv);
+        }
+      }
+    }
+    // A1 and A2 are no longer read as the incoming adjoints: the first terms of
+    // the mini-batch-start adjoints, A1 += dH_Q Q^T, A2 += dZ C^T + E dS^T
+    {
+      float4v dhqt[2];
+      jt2tj(dhq, dhqt);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        bf16x4 qh, ql;
+        split4(dhqt[jt], qh, ql);
+        const bf16x8 qb = cat(qh, ql);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const bf16x4 qt4 = *reinterpret_cast<const bf16x4*>(&sm.qt[(16 * c4 + li) * KTROW + 4 * g]);
+          a1[jt][c4] = mfma32(cat(qt4, qt4), qb, a1[jt][c4]);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        float4v zt, et4;  // [t = 4g + r][i = 16it + li]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          zt[r] = sm.dz[(4 * g + r) * PROW + 16 * it + li];
+          et4[r] = sm.e[(4 * g + r) * PROW + 16 * it + li];
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          float4v x = a2[it][jt];
+          x = mfma3_16(cqt[jt], zt, x);
+          x = mfma3_16(dst[jt], et4, x);
+          a2[it][jt] = x;
+        }
+      }
     }
     __syncthreads();  // #3
 
@@ -479,29 +551,26 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
     }
     __syncthreads();  // #4
 
-    // ---- R-B: dE -> dY (LDS) and dV; deta ----
-    {
-      const int e0 = 2 * tid, s = e0 >> 6, i = e0 & 63;
-      float y0 = 0.f, y1 = 0.f;
+    // ---- R-B: dE = (the partials) - (dZ triu(P)^T) diag(eta) -> dY (LDS), dV; deta ----
+    if (w < 4) {
+      const int it = w;  // outputs i = 16it .. 16it + 15
+      // dZ [t = 4g + r][i = 16it + li] and P'[s = li][t = 4g + r] = eta_s P[s][t] (t >= s)
+      float4v zt, pt;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        y0 += sm.pa[ww][s * PROW + i];
-        y1 += sm.pa[ww][s * PROW + i + 1];
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * g + r;
+        zt[r] = sm.dz[t * PROW + 16 * it + li];
+        pt[r] = (t >= li) ? et_col * sm.p[li * SROW + t] : 0.f;
       }
-      float c0 = 0.f, c1 = 0.f;
-      for (int t = s; t < BT; ++t) {
-        const float pv = sm.p[s * SROW + t];
-        c0 = fmaf(sm.dz[t * PROW + i], pv, c0);
-        c1 = fmaf(sm.dz[t * PROW + i + 1], pv, c1);
-      }
-      const float es = sm.eta[s];
-      const float dy0 = 2.f * (y0 - es * c0), dy1 = 2.f * (y1 - es * c1);
-      sm.dy[s * PROW + i] = dy0;
-      sm.dy[s * PROW + i + 1] = dy1;
-      *reinterpret_cast<float2*>(dVg + static_cast<size_t>(t0 + s) * D + i) = make_float2(-dy0, -dy1);
-    }
-    if (tid < BT) {
-      const int s = tid;
+      float4v acc = mfma3_16(zt, pt, zero4v());  // [i = 16it + 4g + r][s = li] = sum_t dZ[t][i] P'[s][t]
+      float4v sum = zero4v();
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) sum += ld4(&sm.pa[ww][li * PROW + 16 * it + 4 * g]);
+      const float4v dy = 2.f * (sum - acc);
+      st4(&sm.dy[li * PROW + 16 * it + 4 * g], dy);
+      *reinterpret_cast<float4v*>(dVg + static_cast<size_t>(t0 + li) * D + 16 * it + 4 * g) = -dy;
+    } else if (w == 4 && lane < BT) {
+      const int s = lane;
       float acc = 0.f;
       for (int t = s; t < BT; ++t)
         acc += sm.ed[s * SROW + t] * sm.p[s * SROW + t] + sm.gq[s * SROW + t] * sm.s1[s * SROW + t];
@@ -513,128 +582,91 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
     __syncthreads();  // #5
 
     // ---- A5: dA_K, dH_K, partials of dQ and dK ----
-    float4v dhk[2], dhkt[2], cqt[2];
+    float4v dhk[2];
     {
-      float4v dy_i[4];  // dY [i = 16it + 4g + r][s = li]
+      // dA_K += W2^T dY
+      float4v wy[2] = {zero4v(), zero4v()};
 #pragma unroll
-      for (int it = 0; it < 4; ++it) dy_i[it] = ld4(&sm.dy[li * PROW + 16 * it + 4 * g]);
-      jt2tj(cq, cqt);
-      float4v dak[2];
+      for (int m = 0; m < 2; ++m) {
+        bf16x4 th[2][2], tl[2][2];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) dak[jt] = mfma3_16(cqt[jt], m2t, zero4v());  // C M2^T
-      {
-        float4v wy[2] = {zero4v(), zero4v()}, ae[2] = {zero4v(), zero4v()};
+        for (int hf = 0; hf < 2; ++hf) transpose2(w2_tile(2 * m + hf, 0), w2_tile(2 * m + hf, 1), ident, th[hf], tl[hf]);
+        // dY [i = 32m + 16hf + 4g + r][s = li]
+        const Op8 yo = split8(ld4(&sm.dy[li * PROW + 32 * m + 4 * g]), ld4(&sm.dy[li * PROW + 32 * m + 16 + 4 * g]));
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          bf16x4 th[2][2], tl[2][2], ah[2][2], al[2][2];
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int it = 2 * m + hf;
-            transpose2(w2_tile(it, 0), w2_tile(it, 1), ident, th[hf], tl[hf]);
-            transpose2(a2[it][0], a2[it][1], ident, ah[hf], al[hf]);
-          }
-          const Op8 yo = split8(dy_i[2 * m], dy_i[2 * m + 1]);
-          const Op8 eo = split8(ld4(&sm.e[li * PROW + 32 * m + 4 * g]), ld4(&sm.e[li * PROW + 32 * m + 16 + 4 * g]));
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            wy[jt] = mfma3(Op8{cat(th[0][jt], th[1][jt]), cat(tl[0][jt], tl[1][jt])}, yo, wy[jt]);
-            ae[jt] = mfma3(Op8{cat(ah[0][jt], ah[1][jt]), cat(al[0][jt], al[1][jt])}, eo, ae[jt]);
-          }
-        }
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dak[jt][r] += wy[jt][r] - et_col * ae[jt][r];
+        for (int jt = 0; jt < 2; ++jt) wy[jt] = mfma3(Op8{cat(th[0][jt], th[1][jt]), cat(tl[0][jt], tl[1][jt])}, yo, wy[jt]);
       }
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dhk[jt][r] = fmaf(dak[jt][r], gk1[jt][r], dhk1[jt][r]);
-      jt2tj(dhk, dhkt);
-      // dQ partial = W1^T dH_Q, dK partial = W1^T dH_K - (A1^T G) diag(eta)   ([c][t] tiles)
-      const Op8 dqo = split8(dhq[0], dhq[1]), dko = split8(dhk[0], dhk[1]), go = split8(gg[0], gg[1]);
+        for (int r = 0; r < 4; ++r) dhk[jt][r] = fmaf(dak[jt][r] + wy[jt][r], gk1[jt][r], dhk1[jt][r]);
+      // dQ partial = W1^T dH_Q (to pa), dK partial += W1^T dH_K (pb)   ([c][t] tiles)
+      const Op8 dqo = split8(dhq[0], dhq[1]), dko = split8(dhk[0], dhk[1]);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        // w1j[jt][q] = W1[32w + 16jt + 4g + r][16(2m + q) + li], a1j likewise
-        bf16x4 w1jh[2][2], w1jl[2][2], a1jh[2][2], a1jl[2][2];
+        bf16x4 w1jh[2][2], w1jl[2][2];  // [jt][q] = W1[32w + 16jt + 4g + r][16(2m + q) + li]
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
+        for (int jt = 0; jt < 2; ++jt)
           transpose2(w1_tile(jt, 2 * m), w1_tile(jt, 2 * m + 1), ident, w1jh[jt], w1jl[jt]);
-          transpose2(a1[jt][2 * m], a1[jt][2 * m + 1], ident, a1jh[jt], a1jl[jt]);
-        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int c4 = 2 * m + q;
           const Op8 W{cat(w1jh[0][q], w1jh[1][q]), cat(w1jl[0][q], w1jl[1][q])};
-          const Op8 A{cat(a1jh[0][q], a1jh[1][q]), cat(a1jl[0][q], a1jl[1][q])};
           const float4v pq = mfma3(W, dqo, zero4v());  // [c = 16c4 + 4g + r][t = li]
-          const float4v pk = mfma3(W, dko, zero4v());
-          const float4v ag = mfma3(A, go, zero4v());
-          float4v kv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) kv[r] = pk[r] - et_col * ag[r];
+          float* kp = &sm.pb[w][li * PROW + 16 * c4 + 4 * g];
+          const float4v pk = mfma3(W, dko, ld4(kp));
           st4(&sm.pa[w][li * PROW + 16 * c4 + 4 * g], pq);
-          st4(&sm.pb[w][li * PROW + 16 * c4 + 4 * g], kv);
+          st4(kp, pk);
         }
       }
     }
     __syncthreads();  // #6
 
-    // ---- R-C: dQ = sum + K M1, dK = sum + Q M1^T ----
-    for (int e = tid; e < 2 * BT * D; e += NT) {
-      const int which = e >> 10, rem = e & 1023, t = rem >> 6, c = rem & 63;
-      float acc = 0.f;
-      if (which == 0) {  // dQ[t][c]
+
+    // ---- R-C: dQ = (the partials) + K M1, dK = (the partials) + Q M1^T; waves 0-3 dQ, 4-7 dK ----
+    {
+      const bool isq = w < 4;
+      const int c4 = w & 3;  // columns c = 16c4 .. 16c4 + 15
+      // M1[s][t] = -eta_s GQ[s][t] (s <= t): dQ takes it with rows s (lane: s = 4g + r, t = li),
+      // dK with rows t (lane: s = li, t = 4g + r)
+      float4v m1;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) acc += sm.pa[ww][t * PROW + c];
-        for (int s = 0; s <= t; ++s) acc = fmaf(-sm.eta[s] * sm.gq[s * SROW + t], bf(sm.k[s * ROW + c]), acc);
-        dQg[static_cast<size_t>(t0 + t) * D + c] = acc;
-      } else {  // dK[s = t][c]
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) acc += sm.pb[ww][t * PROW + c];
-        const float es = -sm.eta[t];
-        for (int u = t; u < BT; ++u) acc = fmaf(es * sm.gq[t * SROW + u], bf(sm.q[u * ROW + c]), acc);
-        dKg[static_cast<size_t>(t0 + t) * D + c] = acc;
+      for (int r = 0; r < 4; ++r) {
+        const int s = isq ? 4 * g + r : li, t = isq ? li : 4 * g + r;
+        m1[r] = (s <= t) ? -sm.eta[s] * sm.gq[s * SROW + t] : 0.f;
       }
+      bf16x4 mh, ml;
+      split4(m1, mh, ml);
+      // K [s = 4g + r][c = 16c4 + li] or Q [t = 4g + r][c]: bf16, exact
+      const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(&(isq ? sm.kt : sm.qt)[(16 * c4 + li) * KTROW + 4 * g]);
+      float4v acc = mfma32(cat(x4, x4), cat(mh, ml), zero4v());  // [c = 16c4 + 4g + r][t = li]
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) acc += ld4(&(isq ? sm.pa[ww] : sm.pb[ww])[li * PROW + 16 * c4 + 4 * g]);
+      *reinterpret_cast<float4v*>((isq ? dQg : dKg) + static_cast<size_t>(t0 + li) * D + 16 * c4 + 4 * g) = acc;
     }
 
-    // ---- A6: the adjoints at the mini-batch start ----
-    // A1[j][c] += sum_t dH_Q[j][t] Q[t][c] + dH_K[j][t] K[t][c]
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      bf16x4 qh, ql, kh, kl;
-      split4(dhqt[jt], qh, ql);
-      split4(dhkt[jt], kh, kl);
-      const bf16x8 qb = cat(qh, ql), kb = cat(kh, kl);
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const bf16x4 qt4 = *reinterpret_cast<const bf16x4*>(&sm.qt[(16 * c4 + li) * KTROW + 4 * g]);
-        const bf16x4 kt4 = *reinterpret_cast<const bf16x4*>(&sm.kt[(16 * c4 + li) * KTROW + 4 * g]);
-        a1[jt][c4] = mfma32(cat(qt4, qt4), qb, a1[jt][c4]);
-        a1[jt][c4] = mfma32(cat(kt4, kt4), kb, a1[jt][c4]);
-      }
-    }
-    // A2[i][j] += sum_t dZ[i][t] C[j][t] + E[i][t] dS[j][t] + dY[i][t] A_K[j][t]
+    // ---- A6: the rest of the mini-batch-start adjoints: A1 += dH_K K^T, A2 += dY A_K^T ----
     {
-      float4v dst[2];
-      jt2tj(ds, dst);
+      float4v dhkt[2];
+      jt2tj(dhk, dhkt);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        bf16x4 kh, kl;
+        split4(dhkt[jt], kh, kl);
+        const bf16x8 kb = cat(kh, kl);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const bf16x4 kt4 = *reinterpret_cast<const bf16x4*>(&sm.kt[(16 * c4 + li) * KTROW + 4 * g]);
+          a1[jt][c4] = mfma32(cat(kt4, kt4), kb, a1[jt][c4]);
+        }
+      }
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        float4v zt, et4, yt;  // [t = 4g + r][i = 16it + li]
+        float4v yt;  // dY [t = 4g + r][i = 16it + li]
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          zt[r] = sm.dz[(4 * g + r) * PROW + 16 * it + li];
-          et4[r] = sm.e[(4 * g + r) * PROW + 16 * it + li];
-          yt[r] = sm.dy[(4 * g + r) * PROW + 16 * it + li];
-        }
+        for (int r = 0; r < 4; ++r) yt[r] = sm.dy[(4 * g + r) * PROW + 16 * it + li];
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          float4v x = a2[it][jt];
-          x = mfma3_16(cqt[jt], zt, x);
-          x = mfma3_16(dst[jt], et4, x);
-          x = mfma3_16(akt[jt], yt, x);
-          a2[it][jt] = x;
-        }
+        for (int jt = 0; jt < 2; ++jt) a2[it][jt] = mfma3_16(akt[jt], yt, a2[it][jt]);
       }
     }
   }
