@@ -135,18 +135,9 @@ __device__ __forceinline__ void gelu_tiles(const float4v x[2], float4v g[2], flo
 }
 
 // The transposes (as bf16 hi and lo, exact) of the two tiles x0, x1: out[q]
-// holds x_q^T, i.e. lane l gets x_q[li][4g + r].  The split tiles (k-slots =
-// the rows of x0, then of x1) times the identity operand ident[q] (1 where the
-// slot's row is 16q + l%16) give tile q with its rows and columns exchanged;
-// bf16 x 1 is exact.  The operand is rebuilt here rather than kept live.
-__device__ __forceinline__ void transpose2(float4v x0, float4v x1, bf16x4 oh[2], bf16x4 ol[2]) {
-  const int l = threadIdx.x & 63;
-  bf16x8 ident[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int sl = 0; sl < 8; ++sl)
-      ident[q][sl] = static_cast<__bf16>((sl / 4 == q && 4 * (l >> 4) + (sl & 3) == (l & 15)) ? 1.f : 0.f);
+// holds x_q^T, i.e. lane l gets x_q[li][4g + r].
+__device__ __forceinline__ void transpose2(float4v x0, float4v x1, const bf16x8 ident[2], bf16x4 oh[2],
+                                           bf16x4 ol[2]) {
   const Op8 x = split8(x0, x1);
   const float4v z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -180,6 +171,15 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
   float* dVg = a.dV + base;
   float* detag = a.deta + static_cast<size_t>(chain) * T;
   const float* eg = a.eta + bi * a.esb + h * a.esh;
+
+  // identity operands: split tiles (k-slots = the rows of two tiles) times
+  // ident[q] give tile q transposed
+  bf16x8 ident[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+      ident[q][sl] = static_cast<__bf16>((sl / 4 == q && 4 * g + (sl & 3) == li) ? 1.f : 0.f);
 
   // adjoints; layouts as the states below:
   // a1[jt][c4] : A1[j = 32w + 16jt + li][c = 16c4 + 4g + r]   (tile rows c, columns j)
@@ -338,8 +338,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
       for (int m = 0; m < 2; ++m) {
         // th[hf][jt] = W2[16(2m + hf) + 4g + r][32w + 16jt + li]
         bf16x4 th[2][2], tl[2][2];
-        transpose2(w2n[2 * m][0], w2n[2 * m][1], th[0], tl[0]);
-        transpose2(w2n[2 * m + 1][0], w2n[2 * m + 1][1], th[1], tl[1]);
+        transpose2(w2n[2 * m][0], w2n[2 * m][1], ident, th[0], tl[0]);
+        transpose2(w2n[2 * m + 1][0], w2n[2 * m + 1][1], ident, th[1], tl[1]);
         const Op8 eo = split8(e_tile(2 * m), e_tile(2 * m + 1)), zo = split8(dz_tile(2 * m), dz_tile(2 * m + 1));
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
       for (int m = 0; m < 2; ++m) {
         // A2 transposed: ah[hf][jt] = A2[16(2m + hf) + 4g + r][32w + 16jt + li]
         bf16x4 ah[2][2], al[2][2];
-        transpose2(a2[2 * m][0], a2[2 * m][1], ah[0], al[0]);
-        transpose2(a2[2 * m + 1][0], a2[2 * m + 1][1], ah[1], al[1]);
+        transpose2(a2[2 * m][0], a2[2 * m][1], ident, ah[0], al[0]);
+        transpose2(a2[2 * m + 1][0], a2[2 * m + 1][1], ident, ah[1], al[1]);
         const Op8 eo = split8(e_tile(2 * m), e_tile(2 * m + 1));
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) ae[jt] = mfma3(Op8{cat(ah[0][jt], ah[1][jt]), cat(al[0][jt], al[1][jt])}, eo, ae[jt]);
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
       for (int m = 0; m < 2; ++m) {
         bf16x4 a1jh[2][2], a1jl[2][2];  // [jt][q] = A1[32w + 16jt + 4g + r][16(2m + q) + li]
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) transpose2(a1[jt][2 * m], a1[jt][2 * m + 1], a1jh[jt], a1jl[jt]);
+        for (int jt = 0; jt < 2; ++jt) transpose2(a1[jt][2 * m], a1[jt][2 * m + 1], ident, a1jh[jt], a1jl[jt]);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const float4v ag = mfma3(Op8{cat(a1jh[0][q], a1jh[1][q]), cat(a1jl[0][q], a1jl[1][q])}, go, zero4v());
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
       for (int m = 0; m < 2; ++m) {
         bf16x4 th[2][2], tl[2][2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) transpose2(w2_tile(2 * m + hf, 0), w2_tile(2 * m + hf, 1), th[hf], tl[hf]);
+        for (int hf = 0; hf < 2; ++hf) transpose2(w2_tile(2 * m + hf, 0), w2_tile(2 * m + hf, 1), ident, th[hf], tl[hf]);
         // dY [i = 32m + 16hf + 4g + r][s = li]
         const Op8 yo = split8(ld4(&sm.dy[li * PROW + 32 * m + 4 * g]), ld4(&sm.dy[li * PROW + 32 * m + 16 + 4 * g]));
 #pragma unroll
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256b16(MlpBwdArgs a) {
         bf16x4 w1jh[2][2], w1jl[2][2];  // [jt][q] = W1[32w + 16jt + 4g + r][16(2m + q) + li]
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
-          transpose2(w1_tile(jt, 2 * m), w1_tile(jt, 2 * m + 1), w1jh[jt], w1jl[jt]);
+          transpose2(w1_tile(jt, 2 * m), w1_tile(jt, 2 * m + 1), ident, w1jh[jt], w1jl[jt]);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int c4 = 2 * m + q;
