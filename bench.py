@@ -632,11 +632,11 @@ def main():
         flops = B * H * (14 * d * cfg.dh if cfg.is_mlp else 6 * d * d)
     achieved = bytes_ / (kernel_ms / 1e3) / 1e9
     # counters are recorded per (kernel, workload) for every mode that launches
-    # one kernel per step; the saving forward, the training step and the chunked
-    # call launch several (or another instantiation) and have no record of
-    # their own.  Workload keys: the config's name, "-ln" for the layer-norm
+    # one kernel per step; the saving forward, the training step, the chunked
+    # call and the dual-form TTT-MLP backward launch several (or another
+    # instantiation) and have no record of their own.  Workload keys: the config's name, "-ln" for the layer-norm
     # forward, "-decode" for decoding.
-    single = not (args.save or args.train or args.chunks > 1)
+    single = not (args.save or args.train or args.chunks > 1 or (cfg.is_mlp and args.bwd and not args.primal))
     prof_workload = cfg.name + ("-ln" if args.ln and not args.bwd else "") + ("-decode" if args.decode else "")
     kid = kname.split(" ")[0]
     traffic = measured_traffic(kid, prof_workload) if single else None
