@@ -171,3 +171,36 @@ def test_layer_norm_decode_graph_replays(ttt):
         assert torch.equal(torch.cat(zl_g, dim=2), ref[r][0]), f"linear, replay {r}"
         assert torch.equal(torch.cat(zm_g, dim=2), ref[r][1]), f"mlp, replay {r}"
     assert all(torch.equal(a, b) for a, b in zip(s_g, s_e))
+
+
+@pytest.mark.parametrize("primal", [False, True])
+def test_mlp_backward_graph_replays(ttt, primal):
+    """ttt_mlp_bwd: the dual form's two launches (checkpointing forward, reverse
+    pass) and the primal form's one, with the caller's workspace."""
+    cfg = ti.CONFIGS["mlp"].with_(B=2, H=2, T=64, eta_kind="token", seed=140)
+    t = to_device(ti.generate(cfg))
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(141)
+    dz = torch.randn((2, 2, 64, 64), generator=gen, device="cuda:0")
+    d1 = torch.randn((2, 2, 256, 64), generator=gen, device="cuda:0")
+    d2 = torch.randn((2, 2, 64, 256), generator=gen, device="cuda:0")
+    ws = torch.empty(ttt.mlp_bwd_workspace_bytes(2, 2, 64, 64, 256, 16), dtype=torch.uint8, device="cuda:0")
+    ref = ttt.mlp_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], 16, dz, d1, d2, workspace=ws,
+                      primal=primal)
+    torch.cuda.synchronize()
+    out = tuple(torch.empty_like(x) for x in ref)
+
+    def calls():
+        ttt.mlp_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], 16, dz, d1, d2, workspace=ws, out=out,
+                    primal=primal)
+
+    g = _capture(calls)
+    for i in range(3):
+        for x in out:
+            x.fill_(float("nan"))
+        ws.fill_(255)  # the workspace holds nothing between calls
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(("dq", "dk", "dv", "deta", "dw1", "dw2"), out, ref):
+            assert torch.equal(x, r), f"replay {i}: {name}"

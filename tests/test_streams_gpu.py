@@ -91,3 +91,21 @@ def test_decode_on_side_stream(ttt):
     z1, w1 = run(s)
     s.synchronize()
     assert torch.equal(z0, z1) and torch.equal(w0, w1)
+
+
+def test_mlp_backward_on_side_stream(ttt):
+    """ttt_mlp_bwd (dual form: two launches) on a side stream, after inputs made on it."""
+    cfg = ti.CONFIGS["mlp"].with_(B=2, H=2, T=32, seed=150)
+    t = to_device(ti.generate(cfg))
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(151)
+    dz = torch.randn((2, 2, 32, 64), generator=gen, device="cuda:0")
+    ref = ttt.mlp_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], 16, dz)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(s):
+        dz2 = dz.clone()
+        got = ttt.mlp_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], 16, dz2)
+    s.synchronize()
+    for x, r in zip(got, ref):
+        assert torch.equal(x, r)
