@@ -32,6 +32,11 @@ Contents
   mlp_primal_grads             the same by a hand-written reverse pass of the
                                TTT-MLP primal loop in C (pinned by finite
                                differences, against mlp_grads, eta = 0).
+  mlp_ln_grads                 gradients of TTT-MLP with layer norm and
+                               residual inside f (dgamma, dbeta included):
+                               torch fp64 autograd through mlp_ln_primal_torch
+                               (pinned against the C forward oracle
+                               mlp_ln_primal, by gradcheck and by eta = 0).
   linear_dual_f64, mlp_dual_f64, linear_naive_f64, mlp_primal_np,
   linear_ln_dual_f64
                                numpy fp64 forms used only to check the oracle.
@@ -610,6 +615,79 @@ def mlp_grads(q, k, v, w1, w2, eta, b, dz, dw1f=None, dw2f=None):
         loss = loss + (f2 * torch.tensor(np.asarray(dw2f, np.float64))).sum()
     loss.backward()
     return tuple(x.grad.numpy() for x in (q_, k_, v_, e_, w1_, w2_))
+
+
+def mlp_ln_primal_torch(q, k, v, w1, w2, gamma, beta, eta, b, eps=1e-6):
+    """The primal TTT-MLP loop with LN + residual inside f,
+    f(x) = x + LN(W2 GELU(W1 x)) (03 §9; the update rule of 03 §6), on torch CPU
+    tensors, any dtype; differentiable.
+
+    Token t of a mini-batch (W1b, W2b: the state before the mini-batch):
+    h = W1b k_t, a = GELU(h), y = W2b a, loss |k_t + LN(y) - v_t|^2; its gradient
+    pulled back through LN to y is delta (written out, as the forward computes
+    it), so the step is W2 -= eta_t delta a^T, W1 -= eta_t ((W2b^T delta) * GELU'(h)) k_t^T;
+    z_t = q_t + LN(W2_t GELU(W1_t q_t)).
+    LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps) + beta over the d entries.
+    Shapes: q, k, v [n, T, d]; w1 [n, dh, d]; w2 [n, d, dh]; gamma, beta [n, d]; eta [n, T].
+    """
+    import torch
+
+    def phi_cdf(x):
+        return 0.5 * (1.0 + torch.erf(x / 2.0 ** 0.5))
+
+    def gelu_t(x):
+        return x * phi_cdf(x)
+
+    def gelu_prime_t(x):
+        return phi_cdf(x) + x * torch.exp(-0.5 * x * x) / (2.0 * np.pi) ** 0.5
+
+    def ln_stats(y):
+        mu = y.mean(dim=1, keepdim=True)
+        dv = y - mu
+        s = torch.sqrt((dv * dv).mean(dim=1, keepdim=True) + eps)
+        return dv / s, s
+
+    n, T, d = q.shape
+    W1, W2 = w1.clone(), w2.clone()
+    zs = []
+    for t0 in range(0, T, b):
+        W1b, W2b = W1, W2
+        for t in range(t0, min(t0 + b, T)):
+            h = torch.einsum("nij,nj->ni", W1b, k[:, t])
+            a = gelu_t(h)
+            yh, s = ln_stats(torch.einsum("nij,nj->ni", W2b, a))
+            g = 2.0 * (k[:, t] + gamma * yh + beta - v[:, t]) * gamma
+            delta = (g - g.mean(dim=1, keepdim=True) - yh * (g * yh).mean(dim=1, keepdim=True)) / s
+            g1 = torch.einsum("nij,ni->nj", W2b, delta) * gelu_prime_t(h)
+            et = eta[:, t][:, None, None]
+            W2 = W2 - et * delta[:, :, None] * a[:, None, :]
+            W1 = W1 - et * g1[:, :, None] * k[:, t][:, None, :]
+            uh, _ = ln_stats(torch.einsum("nij,nj->ni", W2, gelu_t(torch.einsum("nij,nj->ni", W1, q[:, t]))))
+            zs.append(q[:, t] + gamma * uh + beta)
+    return torch.stack(zs, dim=1), W1, W2
+
+
+def mlp_ln_grads(q, k, v, w1, w2, gamma, beta, eta, b, dz, dw1f=None, dw2f=None, eps=1e-6):
+    """Gradients of  sum(dz * Z) + sum(dw1f * W1_final) + sum(dw2f * W2_final)  of
+    TTT-MLP with LN + residual, fp64 autograd through mlp_ln_primal_torch.
+
+    returns (dq, dk, dv, deta [n, T], dw1 [n, dh, d], dw2 [n, d, dh], dgamma [n, d],
+    dbeta [n, d]) as numpy fp64.
+    """
+    import torch
+
+    def t(x):
+        return torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True)
+
+    q_, k_, v_, w1_, w2_, g_, b_, e_ = t(q), t(k), t(v), t(w1), t(w2), t(gamma), t(beta), t(eta)
+    z, f1, f2 = mlp_ln_primal_torch(q_, k_, v_, w1_, w2_, g_, b_, e_, b, eps)
+    loss = (z * torch.tensor(np.asarray(dz, np.float64))).sum()
+    if dw1f is not None:
+        loss = loss + (f1 * torch.tensor(np.asarray(dw1f, np.float64))).sum()
+    if dw2f is not None:
+        loss = loss + (f2 * torch.tensor(np.asarray(dw2f, np.float64))).sum()
+    loss.backward()
+    return tuple(x.grad.numpy() for x in (q_, k_, v_, e_, w1_, w2_, g_, b_))
 
 
 def mlp_dual_f64(q, k, v, w1, w2, eta, b):
