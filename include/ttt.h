@@ -483,6 +483,42 @@ int64_t ttt_mlp_bwd_workspace_bytes(const ttt_mlp_desc* desc);
  * form), or NULL if unsupported. */
 const char* ttt_mlp_bwd_kernel_name(const ttt_mlp_desc* desc);
 
+/*
+ * Backward of ttt_mlp_ln_fwd ([TTT] 03 §4: the layer is trained end to end;
+ * 03 §9: f(x) = x + LN(W2 GELU(W1 x)), the layer norm over the d outputs with
+ * per-head gamma, beta and eps).  As ttt_mlp_bwd, with gamma, beta [H, d] fp32
+ * and eps the forward's, and two more outputs: dgamma, dbeta [B, H, d] fp32
+ * per sequence (sum over B for the shared per-head parameters).
+ * The loss gradient pulled back through the layer norm, Delta, takes the place
+ * of 2 (W2 GELU(W1 k) - v); the backward differentiates Delta itself through
+ * the layer norm (its statistics included), and z = q + LN(...) adds dZ to dQ.
+ * Computed in the primal form (the token loop in reverse, fp32, one workgroup
+ * per (sequence, head); the same workspace and support as ttt_mlp_bwd's primal
+ * form: any b <= 16, ragged T, fp32 or bf16 inputs; flags 0 or
+ * TTT_FLAG_PRIMAL).  In addition eps must be finite and >= 0 (TTT_ERR_SHAPE),
+ * gamma, beta, dgamma, dbeta non-NULL when B*H > 0 (TTT_ERR_NULL), 4-byte
+ * aligned (TTT_ERR_ALIGN), and dgamma, dbeta overlap no input and no other
+ * output, nor gamma, beta any output (TTT_ERR_ALIAS).
+ * Accuracy: as the forward's, it depends on gamma and beta (see
+ * ttt_mlp_ln_fwd): well conditioned with gamma = 1, beta = 0.
+ */
+ttt_status ttt_mlp_ln_bwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                          const float* W1_0, const float* W2_0, const float* gamma, const float* beta, float eps,
+                          const float* eta, const float* dZ, const float* dW1_final, const float* dW2_final,
+                          void* workspace, int64_t workspace_bytes, float* dQ, float* dK, float* dV, float* deta,
+                          float* dW1_0, float* dW2_0, float* dgamma, float* dbeta, void* stream);
+
+/* Runs every host-side check of ttt_mlp_ln_bwd and launches nothing. */
+ttt_status ttt_mlp_ln_bwd_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                   const float* W1_0, const float* W2_0, const float* gamma, const float* beta,
+                                   float eps, const float* eta, const float* dZ, const float* dW1_final,
+                                   const float* dW2_final, const void* workspace, int64_t workspace_bytes,
+                                   const float* dQ, const float* dK, const float* dV, const float* deta,
+                                   const float* dW1_0, const float* dW2_0, const float* dgamma, const float* dbeta);
+
+/* Name of the kernel ttt_mlp_ln_bwd would launch for desc, or NULL if unsupported. */
+const char* ttt_mlp_ln_bwd_kernel_name(const ttt_mlp_desc* desc);
+
 /* Name of the kernel ttt_mlp_ln_fwd would launch for desc, or NULL if unsupported. */
 const char* ttt_mlp_ln_kernel_name(const ttt_mlp_desc* desc);
 

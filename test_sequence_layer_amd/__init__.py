@@ -58,7 +58,7 @@ EXPORTS = (
     "ttt_mlp_fwd", "ttt_mlp_validate", "ttt_mlp_kernel_name", "ttt_mlp_ln_fwd",
     "ttt_mlp_decode", "ttt_mlp_decode_validate", "ttt_mlp_ln_decode", "ttt_mlp_ln_decode_validate",
     "ttt_mlp_ln_kernel_name", "ttt_mlp_bwd", "ttt_mlp_bwd_validate", "ttt_mlp_bwd_workspace_bytes",
-    "ttt_mlp_bwd_kernel_name",
+    "ttt_mlp_bwd_kernel_name", "ttt_mlp_ln_bwd", "ttt_mlp_ln_bwd_validate", "ttt_mlp_ln_bwd_kernel_name",
     "ttt_status_str", "ttt_abi_version",
 )
 
@@ -187,6 +187,14 @@ def lib() -> ctypes.CDLL:
     L.ttt_mlp_bwd_workspace_bytes.restype = ctypes.c_int64
     L.ttt_mlp_bwd_kernel_name.argtypes = [ctypes.POINTER(MlpDesc)]
     L.ttt_mlp_bwd_kernel_name.restype = ctypes.c_char_p
+    L.ttt_mlp_ln_bwd.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, fp, fp, fp, fp,
+                                 vp, ctypes.c_int64, fp, fp, fp, fp, fp, fp, fp, fp, vp]
+    L.ttt_mlp_ln_bwd.restype = ctypes.c_int
+    L.ttt_mlp_ln_bwd_validate.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, fp,
+                                          fp, fp, fp, vp, ctypes.c_int64, fp, fp, fp, fp, fp, fp, fp, fp]
+    L.ttt_mlp_ln_bwd_validate.restype = ctypes.c_int
+    L.ttt_mlp_ln_bwd_kernel_name.argtypes = [ctypes.POINTER(MlpDesc)]
+    L.ttt_mlp_ln_bwd_kernel_name.restype = ctypes.c_char_p
     L.ttt_mlp_ln_decode.argtypes = [ctypes.POINTER(MlpDesc), vp, vp, vp, fp, fp, fp, ctypes.c_float, vp, fp, fp, fp,
                                     fp, ctypes.c_int64, vp]
     L.ttt_mlp_ln_decode.restype = ctypes.c_int
@@ -801,6 +809,60 @@ def mlp_bwd(q, k, v, w1, w2, eta, b: int, dz, dw1_final=None, dw2_final=None, wo
                            _ptr(dv), _ptr(deta), _ptr(dw1), _ptr(dw2), _stream_handle(stream))
     _done(st, "ttt_mlp_bwd")
     return dq, dk, dv, deta, dw1, dw2
+
+
+def mlp_ln_bwd_kernel_name(B, H, T, d, dh, b, in_dtype=TTT_BF16) -> Optional[str]:
+    name = lib().ttt_mlp_ln_bwd_kernel_name(ctypes.byref(mlp_desc(B, H, T, d, dh, b, in_dtype, TTT_F32, 0, (0, 0, 0))))
+    return None if name is None else name.decode()
+
+
+def mlp_ln_bwd(q, k, v, w1, w2, gamma, beta, eps: float, eta, b: int, dz, dw1_final=None, dw2_final=None,
+               workspace=None, out=None, stream=None):
+    """Backward of :func:`mlp_ln_fwd` (f(x) = x + LN(W2 GELU(W1 x))): as
+    :func:`mlp_bwd`, with gamma, beta [H, d] float32 and eps the forward's.
+    out : optional preallocated (dq, dk, dv, deta, dw1, dw2, dgamma, dbeta).
+    returns (dq, dk, dv, deta, dw1, dw2, dgamma [B,H,d], dbeta [B,H,d]).
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    if tuple(dz.shape) != (B, H, T, d) or dz.dtype != torch.float32:
+        raise ValueError("dz must be float32 [B, H, T, d]")
+    dh = w1.shape[-2]
+    if w1.dtype != torch.float32 or w2.dtype != torch.float32:
+        raise TypeError("w1, w2 must be float32")
+    if tuple(w1.shape) == (H, dh, d) and tuple(w2.shape) == (H, d, dh):
+        wstride = 0
+    elif tuple(w1.shape) == (B, H, dh, d) and tuple(w2.shape) == (B, H, d, dh):
+        wstride = H * dh * d
+    else:
+        raise ValueError("w1/w2 shapes: expected [H,dh,d]/[H,d,dh] or [B,H,dh,d]/[B,H,d,dh]")
+    if tuple(gamma.shape) != (H, d) or tuple(beta.shape) != (H, d):
+        raise ValueError("gamma and beta must be [H, d]")
+    if gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("gamma and beta must be float32")
+    for x, shape in ((dw1_final, (B, H, dh, d)), (dw2_final, (B, H, d, dh))):
+        if x is not None and (tuple(x.shape) != shape or x.dtype != torch.float32):
+            raise ValueError(f"final-state gradients must be float32 {shape}")
+    eta_t, est = eta_layout(eta, B, H, T, q.device)
+    desc = mlp_desc(B, H, T, d, dh, b, _dtype_code(q.dtype), TTT_F32, wstride, est)
+    need = int(lib().ttt_mlp_bwd_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        f = dict(dtype=torch.float32, device=q.device)
+        out = (torch.empty((B, H, T, d), **f), torch.empty((B, H, T, d), **f), torch.empty((B, H, T, d), **f),
+               torch.empty((B, H, T), **f), torch.empty((B, H, dh, d), **f), torch.empty((B, H, d, dh), **f),
+               torch.empty((B, H, d), **f), torch.empty((B, H, d), **f))
+    dq, dk, dv, deta, dw1, dw2, dg, db = out
+    _check_dev(q, k, v, w1, w2, gamma, beta, eta_t, dz, dw1_final, dw2_final, workspace, *out)
+    st = lib().ttt_mlp_ln_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w1), _ptr(w2), _ptr(gamma),
+                              _ptr(beta), float(eps), _ptr(eta_t), _ptr(dz), _ptr(dw1_final), _ptr(dw2_final),
+                              _ptr(workspace), workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
+                              _ptr(dw1), _ptr(dw2), _ptr(dg), _ptr(db), _stream_handle(stream))
+    _done(st, "ttt_mlp_ln_bwd")
+    return dq, dk, dv, deta, dw1, dw2, dg, db
 
 
 def mlp_decode(q, k, v, eta, w1, w2, w1b, w2b, pos: int, b: int, out_dtype=None, z=None, stream=None, ln=None):

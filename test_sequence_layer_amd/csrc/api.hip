@@ -1150,6 +1150,7 @@ ttt_status ttt_mlp_bwd(const ttt_mlp_desc* desc, const void* Q, const void* K, c
   a.dZ = dZ; a.dW1f = dW1_final; a.dW2f = dW2_final;
   a.ws = static_cast<float*>(workspace);
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.deta = deta; a.dW1 = dW1_0; a.dW2 = dW2_0;
+  a.gamma = nullptr; a.beta = nullptr; a.eps = 0.f; a.dgamma = nullptr; a.dbeta = nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   bool dual = mlp_bwd_dual_shape(desc);
   if (desc->T > 0)
@@ -1175,6 +1176,94 @@ const char* ttt_mlp_bwd_kernel_name(const ttt_mlp_desc* d) {
   if (!d) return nullptr;
   if (!ttt::mlp_bwd_supported(d->d, d->dh, d->b) || d->out_dtype != TTT_F32) return nullptr;
   return mlp_bwd_dual_shape(d) ? "ttt_mlp_bwd_d64h256b16" : "ttt_mlp_bwd_d64h256";
+}
+
+}  // extern "C"
+
+namespace {
+
+// ttt_mlp_bwd's checks, then the layer-norm parameters and their gradients:
+// gamma, beta [H, d] and dgamma, dbeta [B, H, d] fp32, 4-byte aligned, the
+// latter two outputs overlapping no input and no other output.
+ttt_status validate_mlp_ln_bwd(const ttt_mlp_desc* d, const void* Q, const void* K, const void* V, const float* W1_0,
+                               const float* W2_0, const float* gamma, const float* beta, float eps, const float* eta,
+                               const float* dZ, const float* dW1f, const float* dW2f, const void* ws,
+                               int64_t ws_bytes, const float* dQ, const float* dK, const float* dV, const float* deta,
+                               const float* dW1, const float* dW2, const float* dgamma, const float* dbeta) {
+  const ttt_status st = validate_mlp_bwd(d, Q, K, V, W1_0, W2_0, eta, dZ, dW1f, dW2f, ws, ws_bytes, dQ, dK, dV, deta,
+                                         dW1, dW2);
+  if (st != TTT_OK) return st;
+  const int64_t chains = static_cast<int64_t>(d->B) * d->H;
+  const int64_t tok = chains * d->T * d->d * 4, w_b = chains * d->d * d->dh * 4, cd_b = chains * d->d * 4;
+  const int64_t need = ttt_mlp_bwd_workspace_bytes(d);
+  const std::initializer_list<Range> all_outs = {{dQ, tok}, {dK, tok}, {dV, tok}, {deta, chains * d->T * 4},
+                                                 {dW1, w_b}, {dW2, w_b}, {ws, need}, {dgamma, cd_b}, {dbeta, cd_b}};
+  const ttt_status sl = check_ln(chains, d->H, d->d, gamma, beta, eps, all_outs);
+  if (sl != TTT_OK) return sl;
+  if (chains == 0) return TTT_OK;
+  if (!dgamma || !dbeta) return TTT_ERR_NULL;
+  if (!aligned(dgamma, 4) || !aligned(dbeta, 4)) return TTT_ERR_ALIGN;
+  const int64_t in_b = tok / 4 * dtype_size(d->in_dtype);
+  const int64_t w0_b = (d->w_batch_stride == 0 ? static_cast<int64_t>(d->H) * d->d * d->dh * 4 : w_b);
+  const int64_t eta_b =
+      d->T > 0 ? eta_extent(d->B, d->H, d->T, d->eta_stride_b, d->eta_stride_h, d->eta_stride_t) * 4 : 0;
+  const Range ins[] = {{Q, in_b}, {K, in_b}, {V, in_b}, {W1_0, w0_b}, {W2_0, w0_b}, {eta, eta_b}, {dZ, tok},
+                       {dW1f, dW1f ? w_b : 0}, {dW2f, dW2f ? w_b : 0}};
+  // dgamma and dbeta are the last two outputs: each against every input and
+  // every output before it (ttt_mlp_bwd's checks covered the others)
+  const Range* outs = all_outs.begin();
+  const int n_out = static_cast<int>(all_outs.size());
+  for (int i = n_out - 2; i < n_out; ++i) {
+    for (const Range& in : ins)
+      if (overlaps(outs[i], in)) return TTT_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_ALIAS;
+  }
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status ttt_mlp_ln_bwd_validate(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V,
+                                   const float* W1_0, const float* W2_0, const float* gamma, const float* beta,
+                                   float eps, const float* eta, const float* dZ, const float* dW1_final,
+                                   const float* dW2_final, const void* workspace, int64_t workspace_bytes,
+                                   const float* dQ, const float* dK, const float* dV, const float* deta,
+                                   const float* dW1_0, const float* dW2_0, const float* dgamma, const float* dbeta) {
+  return validate_mlp_ln_bwd(desc, Q, K, V, W1_0, W2_0, gamma, beta, eps, eta, dZ, dW1_final, dW2_final, workspace,
+                             workspace_bytes, dQ, dK, dV, deta, dW1_0, dW2_0, dgamma, dbeta);
+}
+
+ttt_status ttt_mlp_ln_bwd(const ttt_mlp_desc* desc, const void* Q, const void* K, const void* V, const float* W1_0,
+                          const float* W2_0, const float* gamma, const float* beta, float eps, const float* eta,
+                          const float* dZ, const float* dW1_final, const float* dW2_final, void* workspace,
+                          int64_t workspace_bytes, float* dQ, float* dK, float* dV, float* deta, float* dW1_0,
+                          float* dW2_0, float* dgamma, float* dbeta, void* stream) {
+  const ttt_status st = validate_mlp_ln_bwd(desc, Q, K, V, W1_0, W2_0, gamma, beta, eps, eta, dZ, dW1_final,
+                                            dW2_final, workspace, workspace_bytes, dQ, dK, dV, deta, dW1_0, dW2_0,
+                                            dgamma, dbeta);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(desc->B) * desc->H == 0) return TTT_OK;
+  ttt::MlpBwdArgs a;
+  a.B = desc->B; a.H = desc->H; a.T = desc->T; a.d = desc->d; a.dh = desc->dh; a.b = desc->b;
+  a.in_dtype = desc->in_dtype;
+  a.Q = Q; a.K = K; a.V = V;
+  a.W1_in = W1_0; a.W2_in = W2_0; a.w_in_bstride = desc->w_batch_stride;
+  a.eta = eta; a.esb = desc->eta_stride_b; a.esh = desc->eta_stride_h; a.est = desc->eta_stride_t;
+  a.dZ = dZ; a.dW1f = dW1_final; a.dW2f = dW2_final;
+  a.ws = static_cast<float*>(workspace);
+  a.dQ = dQ; a.dK = dK; a.dV = dV; a.deta = deta; a.dW1 = dW1_0; a.dW2 = dW2_0;
+  a.gamma = gamma; a.beta = beta; a.eps = eps; a.dgamma = dgamma; a.dbeta = dbeta;
+  const hipError_t e = ttt::launch_mlp_bwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+const char* ttt_mlp_ln_bwd_kernel_name(const ttt_mlp_desc* d) {
+  if (!d) return nullptr;
+  if (!ttt::mlp_bwd_supported(d->d, d->dh, d->b) || d->out_dtype != TTT_F32) return nullptr;
+  return "ttt_mlp_bwd_d64h256 (layer norm)";
 }
 
 }  // extern "C"

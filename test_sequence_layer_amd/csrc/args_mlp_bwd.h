@@ -28,9 +28,17 @@ struct MlpBwdArgs {
   float* deta;             // [B, H, T]
   float* dW1;              // [B, H, dh, d]
   float* dW2;              // [B, H, d, dh]
+  // Layer norm and residual inside f (f(x) = x + LN(W2 GELU(W1 x))); gamma ==
+  // nullptr: plain f.  Primal form only.
+  const float* gamma;      // [H][d]
+  const float* beta;       // [H][d]
+  float eps;
+  float* dgamma;           // [B, H, d]
+  float* dbeta;            // [B, H, d]
 };
 // Primal form (token by token, fp32 vector units): d = 64, dh = 256, b <= 16,
 // any T, fp32 or bf16 inputs; the workspace holds the mini-batch-start states.
+// With a.gamma set, f carries the layer norm and residual.
 bool mlp_bwd_supported(int d, int dh, int b);
 hipError_t launch_mlp_bwd(const MlpBwdArgs& a, hipStream_t s);
 // Dual form on the matrix cores: d = 64, dh = 256, b = 16, T % 16 == 0, bf16

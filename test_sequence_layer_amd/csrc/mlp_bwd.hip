@@ -91,9 +91,35 @@ struct Tiles {
   float CV[DH], CPV[DH], DU[DH], DA[DH], DH1[DH];
   float GD[BT];
   float reta[2][NW];
+  // layer norm: per token of the mini-batch the normalised pre-norm output, the
+  // loss gradient at it (gamma-scaled) and the standard deviation; a 64-vector
+  // exchange buffer, the gradient of Delta, the residual part of dk, and
+  // e_s . dy_z of the token being reversed
+  float YH[BT][D], GF[BT][D];
+  float SIG[BT];
+  float YB[D], DEB[D], DKR[D];
+  float EDT[BT];
 };
 
-template <typename InT>
+__device__ __forceinline__ float readlane(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// LN: f(x) = x + LN(W2 GELU(W1 x)), LN(y) = gamma (y - mean y) / sqrt(var y + eps) + beta
+// over the d outputs.  The loss gradient at the pre-norm output, Delta =
+// (G - mean G - yh mean(G yh)) / sigma with G = 2 (k + LN(y) - v) * gamma, takes
+// the place of e = 2 (y - v); z = q + LN(W2_t GELU(W1_t q)).  Each layer norm
+// runs in every wave with output i in lane i (its 64 outputs, wave-wide sums),
+// after the 8 waves have put their 8 rows of the 64-vector in LDS.  Backward:
+//   output side: dy_z = (gamma dz - mean(gamma dz) - yh_z mean(gamma dz yh_z)) / sigma_z,
+//     dq += dz, dgamma += dz yh_z, dbeta += dz;
+//   K side, from dDelta: dG = P(dDelta) / sigma (P(x) = x - mean x - yh mean(x yh)),
+//     dyh = -(mean(G yh) dDelta + mean(dDelta yh) G) / sigma + 2 gamma^2 dG,
+//     dsigma = -(dDelta . Delta) / sigma,
+//     dy = (dyh - mean dyh - yh mean(dyh yh)) / sigma + dsigma yh / d,
+//     dk += 2 gamma dG, dv = -2 gamma dG, dgamma += dG (2 (k + gamma yh + beta - v) + 2 gamma yh),
+//     dbeta += 2 gamma dG.
+template <typename InT, bool LN>
 __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
   __shared__ __align__(16) Tiles S_;
   Tiles& L = S_;
@@ -124,6 +150,13 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
   const InT* Vg = static_cast<const InT*>(a.V) + base;
   const float* DZg = a.dZ + base;
   const float* eg = a.eta + bi * a.esb + h * a.esh;
+  // layer norm: gamma, beta of output l, and its dgamma, dbeta sums (wave 0)
+  float gam = 0.f, bet = 0.f, dgam = 0.f, dbet = 0.f;
+  if constexpr (LN) {
+    gam = a.gamma[static_cast<int64_t>(h) * D + l];
+    bet = a.beta[static_cast<int64_t>(h) * D + l];
+  }
+  constexpr float RD = 1.f / D;
 
   auto stage = [&](int t0, int nt) {
     for (int x = tid; x < nt * D; x += NT) {
@@ -156,12 +189,39 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
     const float et = L.ET[u];
     const float4 av4 = ld4(&L.A[u][4 * l]);
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (LN) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float e = 2.f * (wave_sum(dot4(w2b[m], av4)) - L.V[u][8 * w + m]);
-      if (l == m) L.E[u][8 * w + m] = e;
-      s4 = axpy(s4, e, w2b[m]);
-      if (step) a2[m] = axpy(a2[m], -et * e, av4);
+      for (int m = 0; m < 8; ++m) {
+        const float y = wave_sum(dot4(w2b[m], av4));
+        if (l == m) L.YB[8 * w + m] = y;
+      }
+      __syncthreads();
+      const float y = L.YB[l];
+      const float dv = y - wave_sum(y) * RD;
+      const float sg = sqrtf(wave_sum(dv * dv) * RD + a.eps);
+      const float yh = dv / sg;
+      const float gf = 2.f * (L.K[u][l] + gam * yh + bet - L.V[u][l]) * gam;
+      const float el = (gf - wave_sum(gf) * RD - yh * (wave_sum(gf * yh) * RD)) / sg;
+      if (w == 0) {
+        L.YH[u][l] = yh;
+        L.GF[u][l] = gf;
+        L.E[u][l] = el;
+        if (l == 0) L.SIG[u] = sg;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float e = readlane(el, 8 * w + m);
+        s4 = axpy(s4, e, w2b[m]);
+        if (step) a2[m] = axpy(a2[m], -et * e, av4);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float e = 2.f * (wave_sum(dot4(w2b[m], av4)) - L.V[u][8 * w + m]);
+        if (l == m) L.E[u][8 * w + m] = e;
+        s4 = axpy(s4, e, w2b[m]);
+        if (step) a2[m] = axpy(a2[m], -et * e, av4);
+      }
     }
     st4(&L.red1[w][4 * l], s4);
     __syncthreads();
@@ -250,13 +310,46 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
         }
       }
       __syncthreads();
-      // 2. A2 += dz c^T; partials of W2b^T dz
+      // LN, output side: y_z = W2_t c (rows 8w + m), then the gradient at it
+      // (dz_l in lane l) and e_s . dy_z for the W2_t^T correction
+      float dzl = 0.f;
+      if constexpr (LN) {
+        const float4 c4 = ld4(&L.CV[4 * l]);
+        float yz[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) yz[m] = wave_sum(dot4(w2b[m], c4));
+        for (int s = 0; s <= t; ++s) {
+          const float f = -L.ET[s] * wave_sum(dot4(ld4(&L.A[s][4 * l]), c4));
+#pragma unroll
+          for (int m = 0; m < 8; ++m) yz[m] = fmaf(f, L.E[s][8 * w + m], yz[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          if (l == m) L.YB[8 * w + m] = yz[m];
+        __syncthreads();
+        const float y = L.YB[l];
+        const float dv = y - wave_sum(y) * RD;
+        const float sg = sqrtf(wave_sum(dv * dv) * RD + a.eps);
+        const float yh = dv / sg;
+        const float dz = L.DZ[t][l];
+        const float dyh = dz * gam;
+        dzl = (dyh - wave_sum(dyh) * RD - yh * (wave_sum(dyh * yh) * RD)) / sg;
+        if (w == 0) {
+          dgam = fmaf(dz, yh, dgam);
+          dbet += dz;
+        }
+        for (int s = 0; s <= t; ++s) {
+          const float v = wave_sum(L.E[s][l] * dzl);
+          if (w == 0 && l == 0) L.EDT[s] = v;
+        }
+      }
+      // 2. A2 += dz c^T; partials of W2b^T dz   (LN: dy_z for dz)
       {
         const float4 c4 = ld4(&L.CV[4 * l]);
         float4 p4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const float dzv = L.DZ[t][8 * w + m];
+          const float dzv = LN ? readlane(dzl, 8 * w + m) : L.DZ[t][8 * w + m];
           a2[m] = axpy(a2[m], dzv, c4);
           p4 = axpy(p4, dzv, w2b[m]);
         }
@@ -272,7 +365,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
           float wz = 0.f;
 #pragma unroll
           for (int v = 0; v < NW; ++v) wz += L.red1[v][c];
-          for (int s = 0; s <= t; ++s) wz = fmaf(-L.ET[s] * L.ED[s][t], L.A[s][c], wz);
+          for (int s = 0; s <= t; ++s) wz = fmaf(-L.ET[s] * (LN ? L.EDT[s] : L.ED[s][t]), L.A[s][c], wz);
           du[x] = wz * L.CPV[c];
         }
         st4(&L.DU[4 * l], make_float4(du[0], du[1], du[2], du[3]));
@@ -337,6 +430,10 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
           dq = make_float4(dq.x + x.x, dq.y + x.y, dq.z + x.z, dq.w + x.w);
         }
         for (int s = 0; s <= t; ++s) dq = axpy(dq, -L.ET[s] * L.GD[s], ld4(&L.K[s][4 * li]));
+        if constexpr (LN) {  // the residual of z = q + LN(...)
+          const float4 r = ld4(&L.DZ[t][4 * li]);
+          dq = make_float4(dq.x + r.x, dq.y + r.y, dq.z + r.z, dq.w + r.w);
+        }
         st4(a.dQ + base + o + 4 * li, dq);
       }
       if (tid == 0) {
@@ -344,7 +441,34 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
         for (int v = 0; v < NW; ++v) sum += L.reta[0][v] + L.reta[1][v];
         a.deta[static_cast<size_t>(chain) * T + t0 + t] = -sum;
       }
-      {
+      if constexpr (LN) {
+        const float4 ds4 = ld4(&L.DS[t][4 * l]);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float de = de1[m] + wave_sum(dot4(w2b[m], ds4));
+          if (l == m) L.DEB[8 * w + m] = de;
+        }
+        __syncthreads();
+        // the K side's layer norm backward, output l in lane l
+        const float del = L.DEB[l], yh = L.YH[t][l], gf = L.GF[t][l], sg = L.SIG[t];
+        const float mdey = wave_sum(del * yh) * RD;
+        const float dgl = (del - wave_sum(del) * RD - yh * mdey) / sg;
+        const float dyh = fmaf(2.f * gam * gam, dgl, -(wave_sum(gf * yh) * RD * del + mdey * gf) / sg);
+        const float dsg = -wave_sum(del * L.E[t][l]) / sg;
+        const float dyl = (dyh - wave_sum(dyh) * RD - yh * (wave_sum(dyh * yh) * RD)) / sg + dsg * RD * yh;
+        if (w == 0) {
+          L.DY[t][l] = dyl;
+          a.dV[base + o + l] = -2.f * gam * dgl;
+          L.DKR[l] = 2.f * gam * dgl;
+          const float fv = L.K[t][l] + gam * yh + bet - L.V[t][l];
+          dgam = fmaf(dgl, 2.f * fv + 2.f * gam * yh, dgam);
+          dbet = fmaf(2.f * gam, dgl, dbet);
+        }
+        float4 q4b = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) q4b = axpy(q4b, readlane(dyl, 8 * w + m), w2b[m]);  // W2b^T dy
+        st4(&L.red1[w][4 * l], q4b);
+      } else {
         const float4 ds4 = ld4(&L.DS[t][4 * l]);
         float4 q4b = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -402,6 +526,10 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
           dk = make_float4(fmaf(-et, x.x, dk.x + y.x), fmaf(-et, x.y, dk.y + y.y), fmaf(-et, x.z, dk.z + y.z),
                            fmaf(-et, x.w, dk.w + y.w));
         }
+        if constexpr (LN) {  // k's own part of f(k) = k + LN(...) in the loss
+          const float4 r = ld4(&L.DKR[4 * li]);
+          dk = make_float4(dk.x + r.x, dk.y + r.y, dk.z + r.z, dk.w + r.w);
+        }
         st4(a.dK + base + o + 4 * li, dk);
       }
     }
@@ -424,6 +552,12 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_d64h256(MlpBwdArgs a) {
     st4(a.dW1 + static_cast<int64_t>(chain) * st_sz + off1(r), a1[r]);
     st4(a.dW2 + static_cast<int64_t>(chain) * st_sz + off2(r), a2[r]);
   }
+  if constexpr (LN) {
+    if (w == 0) {
+      a.dgamma[static_cast<int64_t>(chain) * D + l] = dgam;
+      a.dbeta[static_cast<int64_t>(chain) * D + l] = dbet;
+    }
+  }
 }
 
 }  // namespace
@@ -432,10 +566,16 @@ bool mlp_bwd_supported(int d, int dh, int b) { return d == D && dh == DH && b >=
 
 hipError_t launch_mlp_bwd(const MlpBwdArgs& a, hipStream_t s) {
   dim3 grid(a.B * a.H), block(NT);
-  if (a.in_dtype == 0)
-    hipLaunchKernelGGL((ttt_mlp_bwd_d64h256<float>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((ttt_mlp_bwd_d64h256<uint16_t>), grid, block, 0, s, a);
+  if (a.gamma) {
+    if (a.in_dtype == 0)
+      hipLaunchKernelGGL((ttt_mlp_bwd_d64h256<float, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((ttt_mlp_bwd_d64h256<uint16_t, true>), grid, block, 0, s, a);
+  } else if (a.in_dtype == 0) {
+    hipLaunchKernelGGL((ttt_mlp_bwd_d64h256<float, false>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((ttt_mlp_bwd_d64h256<uint16_t, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -337,6 +337,46 @@ def test_mlp_bwd_validation():
     assert ttt.mlp_bwd_kernel_name(16, 32, 2048, 64, 256, 32) is None
 
 
+
+def _mlnval(desc, eps=1e-6, ws_bytes=None, **over):
+    """ttt_mlp_ln_bwd_validate with fake pointers: MlpBwdBufs plus gamma, beta,
+    dgamma, dbeta at 17-20 GB."""
+    b = MlpBwdBufs()
+    extra = dict(gamma=17 * GB, beta=18 * GB, dg=19 * GB, db=20 * GB)
+    for k, v in over.items():
+        if k in extra:
+            extra[k] = v
+        else:
+            setattr(b, k, v)
+    if ws_bytes is None:
+        ws_bytes = max(ttt.lib().ttt_mlp_bwd_workspace_bytes(ctypes.byref(desc)), 0)
+    v = [getattr(b, n) for n in MlpBwdBufs.NAMES]
+    return ttt.lib().ttt_mlp_ln_bwd_validate(ctypes.byref(desc), *v[:5], extra["gamma"], extra["beta"],
+                                             ctypes.c_float(eps), *v[5:10], ctypes.c_int64(ws_bytes), *v[10:],
+                                             extra["dg"], extra["db"])
+
+
+def test_mlp_ln_bwd_validation():
+    d = _mdesc(T=64, in_dtype=1, out_dtype=0)
+    assert _mlnval(d) == OK
+    assert _mlnval(_mdesc(T=37, b=5, in_dtype=0)) == OK                 # ragged T, any b <= 16
+    assert _mlnval(d, d1f=None, d2f=None) == OK
+    assert _mlnval(d, eps=-1.0) == SHAPE
+    assert _mlnval(d, eps=float("nan")) == SHAPE
+    for name in ("gamma", "beta", "dg", "db", "dq", "ws"):
+        assert _mlnval(d, **{name: None}) in (NULL, WORKSPACE), name
+    assert _mlnval(d, gamma=17 * GB + 2) == ALIGN
+    assert _mlnval(d, dg=19 * GB + 2) == ALIGN
+    assert _mlnval(d, gamma=11 * GB) == ALIAS                          # gamma over dQ
+    assert _mlnval(d, dg=1 * GB) == ALIAS                              # dgamma over Q
+    assert _mlnval(d, dg=11 * GB) == ALIAS                             # dgamma over dQ
+    assert _mlnval(d, db=19 * GB) == ALIAS                             # dbeta over dgamma
+    assert _mlnval(_mdesc(T=64, dh=128)) == UNSUP
+    assert _mlnval(_mdesc(B=0, T=64), ws=None, ws_bytes=0, gamma=None, beta=None, dg=None, db=None) == OK
+    assert ttt.mlp_ln_bwd_kernel_name(16, 32, 2048, 64, 256, 16) == "ttt_mlp_bwd_d64h256 (layer norm)"
+    assert ttt.mlp_ln_bwd_kernel_name(16, 32, 2048, 64, 256, 32) is None
+
+
 # ---- decode validation -------------------------------------------------------------
 
 def _dval(desc, pos=0, **over):
