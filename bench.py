@@ -110,8 +110,9 @@ def algorithmic_ln_bwd(cfg: ti.Config, eta_strides, grad_size: int = 4):
     return bytes_, flops
 
 
-def algorithmic_mlp_bwd(cfg: ti.Config, eta_strides):
-    """Algorithmic bytes and flops of one TTT-MLP backward (ttt_mlp_bwd).
+def algorithmic_mlp_bwd(cfg: ti.Config, eta_strides, ln: bool = False):
+    """Algorithmic bytes and flops of one TTT-MLP backward (ttt_mlp_bwd; with
+    ln, ttt_mlp_ln_bwd).
 
     Bytes: read Q, K, V (input dtype), dZ (fp32) and eta; write dQ, dK, dV and
     deta (fp32); read W1_0, W2_0 (per head) and dW1_final, dW2_final, write
@@ -125,6 +126,9 @@ def algorithmic_mlp_bwd(cfg: ti.Config, eta_strides):
     W1b^T dh; the three rank-one terms of the mini-batch-start adjoint -- plus
     3 (d + dh)(b + 1) for the corrections by the earlier tokens of the
     mini-batch ((b + 1) / 2 on average, three d- and three dh-long products each).
+    With ln: gamma, beta read (per head) and dgamma, dbeta written (per chain);
+    the layer norms' O(d) vector work per token (under 1% of the 40 d dh) is
+    not counted.
     """
     th = cfg.B * cfg.H * cfg.T
     in_sz = 2 if cfg.dtype == "bf16" else 4
@@ -133,6 +137,8 @@ def algorithmic_mlp_bwd(cfg: ti.Config, eta_strides):
     eta_b = 4 * th if eta_strides[2] != 0 else 4 * (cfg.H if eta_strides[1] else 1)
     bytes_ = th * d * (3 * in_sz + 4 + 3 * 4) + eta_b + 4 * th + cfg.H * st + 2 * cfg.B * cfg.H * st
     flops = th * (40 * d * dh + 3 * (d + dh) * (b + 1))
+    if ln:
+        bytes_ += cfg.H * 2 * d * 4 + cfg.B * cfg.H * 2 * d * 4
     return bytes_, flops
 
 
@@ -234,7 +240,20 @@ def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = Fa
     dz, dwf = ti.upstream_grads(cfg, chains=chains)
     threads = _host_threads(oracle)
     t0 = time.perf_counter()
-    if cfg.is_mlp:  # dW_final = 0: the same work
+    if cfg.is_mlp and ln:
+        # torch fp64 autograd of the primal loop (the benchmark's gamma = 1, beta = 0,
+        # dW_final = 0): about 4 s per chain at full T, so a few chains
+        import torch
+
+        chains = chains[:max(1, min(len(chains), 4))]
+        sub = ti.Inputs(cfg, chains, inp_full.q[chains], inp_full.k[chains], inp_full.v[chains],
+                        inp_full.w1, inp_full.w2, inp_full.eta_buf, inp_full.eta_strides)
+        n = len(chains)
+        t0 = time.perf_counter()
+        oracle.mlp_ln_grads(sub.q, sub.k, sub.v, sub.w_rows(1), sub.w_rows(2), np.ones((n, cfg.d)),
+                            np.zeros((n, cfg.d)), sub.eta_rows(), cfg.b, dz[:n])
+        threads = torch.get_num_threads()
+    elif cfg.is_mlp:  # dW_final = 0: the same work
         oracle.mlp_primal_grads(sub.q, sub.k, sub.v, sub.w_rows(1), sub.w_rows(2), sub.eta_rows(), cfg.b, dz,
                                 threads=threads)
     elif ln:  # the benchmark's gamma = 1, beta = 0
@@ -248,7 +267,8 @@ def cpu_baseline_bwd(cfg: ti.Config, inp_full, sample_chains: int, ln: bool = Fa
     tokens = len(chains) * cfg.T / cfg.H
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(chains)} of {cfg.chains} (sequence, head) chains at full T={cfg.T}, "
-                      f"fp64 reverse pass of the primal loop{', dW_final = 0' if cfg.is_mlp else ''}, "
+                      f"fp64 reverse pass of the primal loop{', dW_final = 0' if cfg.is_mlp else ''}"
+                      f"{' (torch autograd)' if cfg.is_mlp and ln else ''}, "
                       f"{dt:.2f} s wall on {threads} threads"}
 
 
@@ -346,7 +366,7 @@ def main():
                     help="time the forward for training (also writes E for the backward)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward (ttt_linear_bwd; ttt_linear_ln_bwd with --ln; ttt_mlp_bwd with "
-                         "--config mlp)")
+                         "--config mlp; ttt_mlp_ln_bwd, primal form, with --config mlp --ln)")
     ap.add_argument("--train", action="store_true",
                     help="time forward-for-training + backward (one training step of the layer)")
     ap.add_argument("--no-settle", action="store_true",
@@ -364,12 +384,14 @@ def main():
         ap.error("--graph applies to --decode")
     if args.batch is not None and not args.decode:
         ap.error("--batch applies to --decode")
-    if args.ln and args.primal and (args.save or args.bwd or args.train):
+    is_mlp = ti.CONFIGS[args.config].is_mlp
+    if args.ln and args.primal and (args.save or args.bwd or args.train) and not is_mlp:
         ap.error("--primal with --ln times the forward only")
-    if ti.CONFIGS[args.config].is_mlp and (args.save or ((args.bwd or args.train) and args.ln)
-                                           or (args.train and args.primal)):
-        ap.error("TTT-MLP: --bwd and --train do not take --ln, --train not --primal, and --save does not apply "
+    if is_mlp and (args.save or (args.train and (args.ln or args.primal))):
+        ap.error("TTT-MLP: --train takes neither --ln nor --primal, and --save does not apply "
                  "(the backward rebuilds its states from the inputs)")
+    if is_mlp and args.bwd and args.ln:
+        args.primal = True  # the layer-norm TTT-MLP backward exists in the primal form only
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU (got --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the (sequence, head) chains are independent, so N GPUs would each run this same kernel on "
@@ -476,7 +498,17 @@ def main():
                 ttt.mlp_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], cfg.b, dz, dw1f, dw2f,
                             workspace=mws, out=gout, primal=args.primal)
 
-            if args.bwd:
+            if args.bwd and args.ln:
+                gam = torch.ones((H, d), dtype=torch.float32, device="cuda:0")
+                bet = torch.zeros((H, d), dtype=torch.float32, device="cuda:0")
+                lout = gout + (torch.empty((B, H, d), dtype=torch.float32, device="cuda:0"),
+                               torch.empty((B, H, d), dtype=torch.float32, device="cuda:0"))
+                kname = ttt.mlp_ln_bwd_kernel_name(B, H, T, d, cfg.dh, cfg.b, 1 if cfg.dtype == "bf16" else 0)
+
+                def step():
+                    ttt.mlp_ln_bwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], gam, bet, 1e-6, t["eta"], cfg.b, dz,
+                                   dw1f, dw2f, workspace=mws, out=lout)
+            elif args.bwd:
                 kname = ttt.mlp_bwd_kernel_name(B, H, T, d, cfg.dh, cfg.b, 1 if cfg.dtype == "bf16" else 0,
                                                 primal=args.primal)
                 step = mlp_bwd
@@ -610,7 +642,7 @@ def main():
 
     bytes_, flops = algorithmic(cfg, inp.eta_strides)
     if cfg.is_mlp and (args.bwd or args.train):
-        b2, f2 = algorithmic_mlp_bwd(cfg, inp.eta_strides)
+        b2, f2 = algorithmic_mlp_bwd(cfg, inp.eta_strides, ln=args.ln)
         bytes_, flops = (b2, f2) if args.bwd else (bytes_ + b2, flops + f2)
     elif args.save:
         bytes_ += B * H * T * d * 4                     # E written
@@ -637,7 +669,8 @@ def main():
     # instantiation) and have no record of their own.  Workload keys: the config's name, "-ln" for the layer-norm
     # forward, "-decode" for decoding.
     single = not (args.save or args.train or args.chunks > 1 or (cfg.is_mlp and args.bwd and not args.primal))
-    prof_workload = cfg.name + ("-ln" if args.ln and not args.bwd else "") + ("-decode" if args.decode else "")
+    prof_workload = cfg.name + ("-ln" if args.ln and (cfg.is_mlp or not args.bwd) else "") + \
+        ("-primal" if cfg.is_mlp and args.bwd and args.primal else "") + ("-decode" if args.decode else "")
     kid = kname.split(" ")[0]
     traffic = measured_traffic(kid, prof_workload) if single else None
     tflops = flops / (kernel_ms / 1e3) / 1e12
@@ -737,8 +770,10 @@ def main():
     if args.save:
         form, direction = ln_pre, f"fwd (saving {saved} for the backward)"
     if args.bwd and cfg.is_mlp:
-        form, direction = ("primal " if args.primal else ""), "bwd"
-        roof["note"] = ("backward: dQ, dK, dV, deta, dW1_0, dW2_0 from dZ, dW1_final and dW2_final; " +
+        form, direction = ln_pre + ("primal " if args.primal else ""), "bwd"
+        roof["note"] = ((ln_note + "; " if args.ln else "") +
+                        f"backward: dQ, dK, dV, deta, dW1_0, dW2_0{', dgamma, dbeta' if args.ln else ''} from dZ, "
+                        "dW1_final and dW2_final; " +
                         ("a forward from W0 in the same launch checkpoints every mini-batch-start state, then the "
                          "tokens run in reverse (primal form, fp32 on the vector units)" if args.primal else
                          "two launches: the forward kernel writes every mini-batch-start state, then the "
