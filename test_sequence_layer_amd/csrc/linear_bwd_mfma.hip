@@ -50,6 +50,7 @@
 // loads, columns with the transposing LDS load (ds_read_b64_tr_b16).
 #include "args_bwd.h"
 #include "mfma_common.h"
+#include "wave_prio.h"
 
 namespace ttt {
 namespace {
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
       qx[t] = *reinterpret_cast<const bf16x4*>(&S.q[li * ROW + 16 * t + 4 * g]);
     }
     float4v sc = zero4v(), st = zero4v(), p = zero4v();
+    prio_mfma();  // the step's first run of matrix-core work: -1.0% at the 1.3B shape (raised for the later runs too: no gain)
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_bwd_d64b16(BwdArgs a) {
     rows4<ROW>(S.zh, li, g, zrh);
     rows4<ROW>(S.zl, li, g, zrl);
     const float4v y = rows_x_f2(erh, erl, zrh, zrl, zero4v());
+    prio_valu();
 
     // ---- dE = -2 dZ M^T - 2 P diag(eta), rows i of this wave ----
     const bf16x4 zwh = read_cols<ROW>(S.zh, 0, 16 * w, li, g);  // dZ[t = 4g+r][16w + li]

@@ -53,6 +53,7 @@
 // the row-major tiles with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
 #include "args_linear.h"
 #include "mfma_common.h"
+#include "wave_prio.h"
 
 namespace ttt {
 namespace {
@@ -352,6 +353,7 @@ __device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const U
       // ---- the maps: E_X = K X^T - V_X for X = P (V_P = 0) and R (V_R = V), and
       // X^T += K^T G_X, G_X = -2 diag(eta) E_X, on the shared K and V tiles ----
       float4v pp = {0.f, 0.f, 0.f, 0.f}, pr = pp;
+      prio_mfma();  // -1.0% for the 5-chunk long workload
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const bf16x8 ak = cat(kx[2 * m], kx[2 * m + 1]);
@@ -373,6 +375,7 @@ __device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const U
         pr = mfma32(ak, cat(h0, h1), pr);
         pr = mfma32(ak, cat(l0, l1), pr);
       }
+      prio_valu();
       const bf16x4 vc = read_cols<ROW>(S.v, 0, 16 * wg, li, g);  // V[4g + r][16wg + li]
       float gp[4], gr[4];
 #pragma unroll
@@ -400,6 +403,7 @@ __device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const U
 
     // ---- P_K = K W^T, P_Q = Q W^T, S = K Q^T ----
     float4v pk = {0.f, 0.f, 0.f, 0.f}, pq = pk, sc = pk;
+    prio_mfma();  // the step's long run of matrix-core work: -2.2% at the 1.3B shape, -1.9% with the layer norm
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       float w8[8];
@@ -430,6 +434,7 @@ __device__ __forceinline__ void linear_body(const LinearArgs& a, SH& sh, const U
       }
     }
 
+    prio_valu();
     // ---- E^T[t = 4g+r][i = 16w+li] = P_K - V ----
     // ---- G[s][i] = -eta_s (dl/dy)[s][i]: the gradient factor of the rank-16
     // update, also the operand of the Z correction ----

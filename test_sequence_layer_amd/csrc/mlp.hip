@@ -32,12 +32,15 @@
 // (D = X I moves X's k-slot index to l%16; bf16 x 1 is exact).  Activations
 // needed in the other orientation (A_K for the W2 update, GELU'(H_K) for the
 // backward product) go through per-wave LDS tiles; A_K is stored already split
-// and read back with transposing loads.  As in the TTT-Linear kernel, fp32 operands enter as bf16
+// and read back with transposing loads.  Every run of matrix-core instructions
+// is issued at raised wave priority (wave_prio.h): -3.6% at the TTT-MLP shape,
+// -9.3% with the layer norm.  As in the TTT-Linear kernel, fp32 operands enter as bf16
 // hi + lo pairs (3 passes when both are fp32; 16-token contractions put two
 // passes into the 8 k-slots of one instruction).
 #include "gelu.h"
 #include "args_mlp.h"
 #include "mfma_common.h"
+#include "wave_prio.h"
 
 namespace ttt {
 namespace {
@@ -271,6 +274,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     // ---- phase 1: H_K, W1 Q (layout [j][t]), S1 = K Q^T, GELU ----
     float4v hk[2], hq[2];
     float4v s1 = {0.f, 0.f, 0.f, 0.f};
+    prio_mfma();
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
       hk[jt] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -293,6 +297,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       for (int m = 0; m < 2; ++m)
         s1 = mfma32(cat(kx[2 * m], kx[2 * m + 1]), cat(qx[2 * m], qx[2 * m + 1]), s1);
     }
+    prio_valu();
 
     float4v ak[2];
     {
@@ -320,12 +325,14 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     }
 
     // Y partial[i][t] = sum_{j in J_w} W2[i][j] A_K[j][t]  -> part[t][i]
+    prio_mfma();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const float4v y = mfma3(split8(w2a[it][0], w2a[it][1]), akop, float4v{0.f, 0.f, 0.f, 0.f});
       // lane holds Y[i = 16it + 4g + r][t = li]
       st4(&part[li * PROW + 16 * it + 4 * g], y);
     }
+    prio_valu();
     __syncthreads();  // #1: partials written
 
     // ---- phase 2: E[t][i] = 2 (sum_w part_w[t][i] - V[t][i]), stored split, and -eta_t E ----
@@ -388,6 +395,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     // G[j][s] = -eta_s GELU'(H_K)[j][s] sum_i E[i][s] W2[i][j]   (s = 4g + r, j = 16jt + li),
     // i.e. -eta_s D[j][s]; split once, it serves the H_Q correction and the W1 gradient
     bf16x4 gdh[2], gdl[2];
+    prio_mfma();
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
       float4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -406,6 +414,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       for (int r = 0; r < 4; ++r) gd[r] = -et[r] * (acc[r] * gp[r]);
       split4(gd, gdh[jt], gdl[jt]);
     }
+    prio_valu();
     // H_Q[j][t] += sum_s G[j][s] S1[s][t] [s <= t]   (= - D diag(eta) triu(K^T Q))
     if constexpr (!CKPT) {
     bf16x4 s1h, s1l;
@@ -428,6 +437,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
     }
     const Op8 aqop = split8(aq[0], aq[1]);
     // S2 partial[s][t] = sum_{j in J_w} A_K[j][s] A_Q[j][t]   (s = 4g + r, t = li)
+    prio_mfma();
     {
       const float4v s2 = mfma3(akop, aqop, float4v{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -439,10 +449,12 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
       const float4v y = mfma3(w2s[it], aqop, float4v{0.f, 0.f, 0.f, 0.f});
       st4(&part[li * PROW + 16 * it + 4 * g], y);
     }
+    prio_valu();
     }  // !CKPT
 
     // ---- state updates (gradients at the mini-batch-start state) ----
     // W1^T[c][j] += sum_s K[s][c] G[j][s]
+    prio_mfma();
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
       const bf16x8 gb = cat(gdh[jt], gdl[jt]);
@@ -467,6 +479,7 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) w2a[it][jt] = mfma3_16(gah[jt], gal[jt], eh, el, w2a[it][jt]);
     }
+    prio_valu();
     __syncthreads();  // #3: S2 and W2 A_Q partials written
     if constexpr (CKPT) return;  // (the next mini-batch may restage this slot only after #3)
 

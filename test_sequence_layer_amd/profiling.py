@@ -38,15 +38,15 @@ COPY_BYTES = 1 << 30
 
 # source files that define each kernel (a change to any of them invalidates its counters)
 KERNEL_SOURCES = {
-    "ttt_linear_mfma_d64b16": ["linear_mfma.hip", "mfma_common.h", "args_linear.h", "ttt_common.h"],
-    "ttt_linear_mfma_head_maps": ["linear_mfma.hip", "mfma_common.h", "args_linear.h", "ttt_common.h"],
+    "ttt_linear_mfma_d64b16": ["linear_mfma.hip", "mfma_common.h", "wave_prio.h", "args_linear.h", "ttt_common.h"],
+    "ttt_linear_mfma_head_maps": ["linear_mfma.hip", "mfma_common.h", "wave_prio.h", "args_linear.h", "ttt_common.h"],
     "ttt_linear_mfma_f32_d64b16": ["linear_mfma_f32.hip", "mfma_common.h", "args_linear.h", "ttt_common.h"],
     "ttt_linear_generic_kernel": ["linear_generic.hip", "args_linear.h", "ttt_common.h"],
-    "ttt_linear_bwd_d64b16": ["linear_bwd_mfma.hip", "mfma_common.h", "args_bwd.h", "ttt_common.h"],
+    "ttt_linear_bwd_d64b16": ["linear_bwd_mfma.hip", "mfma_common.h", "wave_prio.h", "args_bwd.h", "ttt_common.h"],
     "ttt_linear_bwd_generic_kernel": ["linear_bwd_generic.hip", "args_bwd.h", "ttt_common.h"],
-    "ttt_linear_ln_bwd_d64b16": ["linear_ln_bwd_mfma.hip", "mfma_common.h", "args_bwd.h", "ttt_common.h"],
+    "ttt_linear_ln_bwd_d64b16": ["linear_ln_bwd_mfma.hip", "mfma_common.h", "wave_prio.h", "args_bwd.h", "ttt_common.h"],
     "ttt_linear_ln_bwd_fp32": ["linear_ln_bwd.hip", "args_bwd.h", "ttt_common.h"],
-    "ttt_mlp_fwd_d64h256b16": ["mlp.hip", "gelu.h", "mfma_common.h", "args_mlp.h", "ttt_common.h"],
+    "ttt_mlp_fwd_d64h256b16": ["mlp.hip", "gelu.h", "mfma_common.h", "wave_prio.h", "args_mlp.h", "ttt_common.h"],
     "ttt_mlp_primal_d64h256": ["mlp_primal.hip", "gelu.h", "mfma_common.h", "args_primal.h", "ttt_common.h"],
     "ttt_mlp_ln_primal_d64h256": ["mlp_primal.hip", "gelu.h", "mfma_common.h", "args_primal.h", "ttt_common.h"],
     "ttt_mlp_bwd_d64h256": ["mlp_bwd.hip", "mfma_common.h", "args_mlp_bwd.h", "ttt_common.h"],
