@@ -166,7 +166,12 @@ __global__ __launch_bounds__(kThreads) void ttt_mlp_fwd_d64h256b16(MlpArgs a) {
   const int vrow = tid >> 5, vcol = (tid & 31) * 2;
   const float* srcE = eg + static_cast<int64_t>(tid & 15) * a.est;
 
-  constexpr int PF = 2;  // compute-bound: one mini-batch of look-ahead hides the load latency
+  // Mini-batches of look-ahead in the load ring.  Measured at the TTT-MLP shape:
+  // the plain scalar-eta form runs 1.055 / 1.013 / 1.010 / 1.180 ms with 2 / 3 /
+  // 4 / 6 (6 spills inside the loop); the layer-norm form is fastest with 2
+  // (1.144 ms against 1.148 with 3 or 4), and with 4 the per-token-eta forms
+  // spill 81-121 registers, so they keep 2.
+  constexpr int PF = (ETA_TOKEN || LN) ? 2 : 4;
   u32x2 ra[PF];
   uint32_t rb[PF];
   float re[PF];
