@@ -281,6 +281,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_ln_bwd_d64b16(BwdArgs a) 
       p = mfma32(ak, cat(l0, l1), p);
     }
     // ---- u += M G, M[t][s] = S[s][t] (s <= t) ----
+    prio_mfma();  // -1.4% (raised for the rebuild or the projections above too: slower)
     {
       float mv[4];
 #pragma unroll
@@ -291,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void ttt_linear_ln_bwd_d64b16(BwdArgs a) 
       u = mfma32(cat(mh, mh), gz, u);
       u = mfma32(cat(ml, ml), gz, u);
     }
+    prio_valu();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int o = (4 * g + r) * ZR + 16 * w + li;
